@@ -1,0 +1,157 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, the MI355X (gfx950) Gated DeltaNet token mixer.
+ *
+ * The gated delta rule (source: "On the Design of Qwen3.8-Next Architecture",
+ * picx.dev summary page, section "Theoretical foundations", eqs (1)-(4)): per
+ * (sequence, head), with state S in R^{Dk x Dv}, decay alpha_t and write
+ * strength beta_t,
+ *
+ *     S~ = alpha_t S_{t-1};  e_t = v_t - S~^T k_t;
+ *     S_t = S~ + beta_t k_t e_t^T;  y_t = S_t^T q_t.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer on the current HIP device, to a
+ *   dense row-major (last index fastest) buffer, 16-byte aligned.
+ * - The caller allocates and frees every buffer; the library keeps no device
+ *   memory and no global mutable state other than a thread-local error string.
+ *   It is reentrant.
+ * - Calls enqueue work on `stream` and return without synchronising.  A device
+ *   fault shows up at the caller's next synchronisation.
+ * - Arguments are validated on the host before any HIP call: on a non-OK
+ *   status nothing has been launched and no output has been touched.
+ *   gdn_last_error() then holds a one-line description.
+ * - Value domains are preconditions, not checked on the device:
+ *   alpha in (0, 1] (the pages give the open interval (0,1); alpha = 1 is
+ *   accepted as an exact identity decay), beta in [0, 1], all inputs finite.
+ * - Outputs y, out and final_state are always float32.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_API __attribute__((visibility("default")))
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    GDN_ERR_SHAPE = 2,       /* a size is negative or the sizes overflow        */
+    GDN_ERR_UNSUPPORTED = 3, /* a size/dtype/chunk outside the compiled set     */
+    GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    GDN_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
+    GDN_ERR_HIP = 7          /* a HIP runtime call failed (see gdn_last_error)  */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/*
+ * gdn_prefill_fwd -- whole sequences through eqs (1)-(4), computed chunk by
+ * chunk (C tokens at a time) with the state carried across chunks.
+ *
+ *   q, k          [B, T, H, Dk]  dtype (GDN_F32: float, GDN_BF16: bf16 bits)
+ *   v             [B, T, H, Dv]  dtype
+ *   alpha, beta   [B, T, H]      float32 (eq (1) decay, eq (3) write strength)
+ *   initial_state [B, H, Dk, Dv] float32, or NULL for S_0 = 0
+ *   y             [B, T, H, Dv]  float32 output, y_t of eq (4)
+ *   final_state   [B, H, Dk, Dv] float32 output S_T, or NULL if not wanted;
+ *                 may be the same pointer as initial_state (in-place resume),
+ *                 must not overlap it otherwise.
+ *   chunk         C in {16, 32, 64}; Dk, Dv in {16, 32, 64, 128}.
+ *   B, H, T >= 0; B*H == 0 or T == 0 launch nothing except, for T == 0,
+ *   final_state = initial_state (or zeros).  Any T is accepted: a ragged last
+ *   chunk is padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
+ *   workspace     unused by the current kernels (gdn_prefill_workspace_bytes
+ *                 returns 0); may be NULL.
+ * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
+ */
+GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta,
+                           const float *initial_state,
+                           float *y, float *final_state,
+                           int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                           int64_t chunk, gdn_dtype dtype,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+GDN_API size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                   int64_t Dv, int64_t chunk, gdn_dtype dtype);
+
+/*
+ * gdn_decode_step -- one new token for each of N independent sequences: the
+ * single-token form of eqs (1)-(4) applied to a stored state, updated in place
+ * (the fixed-size state that summarises the prefix).
+ *
+ *   q, k         [N, H, Dk]      dtype
+ *   v            [N, H, Dv]      dtype
+ *   alpha, beta  [N, H]          float32
+ *   state        [N, H, Dk, Dv]  float32, read and overwritten in place
+ *   y            [N, H, Dv]      float32 output
+ *   Dk, Dv in {16, 32, 64, 128}; N, H >= 0 (N*H == 0 launches nothing).
+ * y must not overlap any input or the state.
+ */
+GDN_API gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta,
+                           float *state, float *y,
+                           int64_t N, int64_t H, int64_t Dk, int64_t Dv,
+                           gdn_dtype dtype, hipStream_t stream);
+
+/*
+ * gdn_layer_fwd -- the GDN token-mixing layer around the core (picx.dev
+ * summary, "1. GDN Hybrid Token Mixing": short causal convolution, L2-normalised
+ * queries and keys, eq (9) beta, eq (10) alpha, eq (11) sigmoid-gated
+ * zero-centred RMSNorm and output projection):
+ *
+ *   [q|k|v] = conv(x W_qkv^T);  a = x W_a^T;  b = x W_b^T;  z = x W_gate^T
+ *   q, k <- q / sqrt(|q|^2 + 1e-6) per (token, head)
+ *   alpha = exp(-exp(A) softplus(a + b_alpha));  beta = sigmoid(b)
+ *   y = core(q, k, v, alpha, beta; initial_state)
+ *   out = (sigmoid(z) * y / sqrt(mean(y^2) + 1e-6) * (1 + norm_gamma)) W_o^T
+ *
+ * conv is depthwise and causal over the H*(2Dk+Dv) q|k|v channels,
+ * out[t,c] = sum_j conv_w[c,j] * in[t-(conv_k-1)+j, c] (zero history, no bias,
+ * no activation).  RMSNorm runs per (token, head) over Dv.
+ *
+ *   x     [B, T, hidden] bf16;  out [B, T, hidden] float32
+ *   initial_state / final_state as in gdn_prefill_fwd (NULL allowed).
+ *   hidden % 64 == 0; conv_k in [1, 4]; Dk, Dv, chunk as in gdn_prefill_fwd.
+ *   workspace: at least gdn_layer_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+typedef struct {
+    const void  *W_qkv;      /* [H*(2Dk+Dv), hidden] bf16; rows q | k | v, head-major */
+    const void  *conv_w;     /* [H*(2Dk+Dv), conv_k] bf16; tap conv_k-1 = current token */
+    const void  *W_ab;       /* [2H, hidden] bf16; rows a (eq (10)) | b (eq (9))        */
+    const float *A;          /* [H] eq (10) log-scale of the decay rate                 */
+    const float *b_alpha;    /* [H] eq (10) bias                                        */
+    const void  *W_gate;     /* [H*Dv, hidden] bf16 (W_z of eq (11))                    */
+    const float *norm_gamma; /* [Dv] zero-centred RMSNorm gain: scale = 1 + gamma       */
+    const void  *W_o;        /* [hidden, H*Dv] bf16                                     */
+} gdn_layer_params;
+
+GDN_API gdn_status gdn_layer_fwd(const void *x, const gdn_layer_params *p,
+                         const float *initial_state, float *final_state, float *out,
+                         int64_t B, int64_t T, int64_t hidden, int64_t H,
+                         int64_t Dk, int64_t Dv, int64_t conv_k, int64_t chunk,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+GDN_API size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H,
+                                 int64_t Dk, int64_t Dv, int64_t conv_k, int64_t chunk);
+
+/* Static description of a status code. */
+GDN_API const char *gdn_status_str(gdn_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+GDN_API const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

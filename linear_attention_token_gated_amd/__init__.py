@@ -1,5 +1,186 @@
 """MI355X-native Gated DeltaNet token mixer (gfx950).
 
-The compute lives in ``libgdn.so`` (hand-written HIP kernels behind a C ABI);
-this package only marshals arguments to it.
+The compute lives in ``libgdn.so`` (hand-written HIP kernels behind the C ABI
+declared in ``include/gdn.h``).  This module only marshals torch tensors to it:
+torch provides device memory and the current stream, nothing else.  If the
+library is missing every entry point raises; there is no CPU fallback.
+
+Entry points (same names as the C ABI):
+
+* ``prefill(q, k, v, alpha, beta, initial_state=None, chunk=64)``
+  -> ``(y, final_state)``: whole sequences through eqs (1)-(4) of the picx.dev
+  summary of "On the Design of Qwen3.8-Next Architecture" ("Theoretical
+  foundations"), chunk by chunk.
+* ``decode_step(q, k, v, alpha, beta, state)`` -> ``y``; ``state`` is updated
+  in place.
+* ``layer_fwd(x, params, H, Dk, Dv, initial_state=None, chunk=64)``
+  -> ``(out, final_state)``: the token-mixing layer ("1. GDN Hybrid Token
+  Mixing", eqs (9)-(11)).
 """
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+                4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
+EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_layer_fwd",
+            "gdn_layer_workspace_bytes", "gdn_status_str", "gdn_last_error")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class gdn_layer_params(ctypes.Structure):
+    _fields_ = [("W_qkv", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("W_ab", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("b_alpha", ctypes.c_void_p), ("W_gate", ctypes.c_void_p),
+                ("norm_gamma", ctypes.c_void_p), ("W_o", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m linear_attention_token_gated_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.gdn_prefill_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_int, vp, sz, vp]
+    L.gdn_prefill_fwd.restype = ctypes.c_int
+    L.gdn_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    L.gdn_prefill_workspace_bytes.restype = sz
+    L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
+    L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_layer_fwd.argtypes = [vp, ctypes.POINTER(gdn_layer_params), vp, vp, vp, i64, i64, i64, i64,
+                                i64, i64, i64, i64, vp, sz, vp]
+    L.gdn_layer_fwd.restype = ctypes.c_int
+    L.gdn_layer_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64]
+    L.gdn_layer_workspace_bytes.restype = sz
+    L.gdn_status_str.argtypes = [ctypes.c_int]
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_last_error.argtypes = []
+    L.gdn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _need(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_final_state: bool = True,
+            y=None, final_state=None):
+    """Chunked prefill.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (float32 or bfloat16);
+    alpha, beta: [B,T,H] float32; initial_state: [B,H,Dk,Dv] float32 or None.
+    Returns (y [B,T,H,Dv] float32, final_state or None)."""
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n in ((alpha, "alpha"), (beta, "beta"), (initial_state, "initial_state")):
+        _need(t, n, torch.float32)
+    if y is None:
+        y = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _need(y, "y", torch.float32)
+    _need(final_state, "final_state", torch.float32)
+    _check(lib().gdn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+                                 _ptr(y), _ptr(final_state), B, T, H, Dk, Dv, int(chunk), _dtype_code(q),
+                                 None, 0, _stream(q.device)))
+    return y, final_state
+
+
+def decode_step(q, k, v, alpha, beta, state, y=None):
+    """One token per sequence.  q, k: [N,H,Dk]; v: [N,H,Dv]; alpha, beta: [N,H];
+    state: [N,H,Dk,Dv] float32, updated in place.  Returns y [N,H,Dv] float32."""
+    import torch
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n in ((alpha, "alpha"), (beta, "beta"), (state, "state")):
+        _need(t, n, torch.float32)
+    if y is None:
+        y = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
+    _need(y, "y", torch.float32)
+    _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
+                                 N, H, Dk, Dv, _dtype_code(q), _stream(q.device)))
+    return y
+
+
+def layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k=4, chunk=64) -> int:
+    return int(lib().gdn_layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k, chunk))
+
+
+def layer_fwd(x, params: dict, H: int, Dk: int, Dv: int, initial_state=None, chunk: int = 64,
+              return_final_state: bool = True, out=None, final_state=None, workspace=None):
+    """GDN layer.  x: [B,T,hidden] bfloat16; params: W_qkv, conv_w, W_ab, W_gate,
+    W_o (bfloat16), A, b_alpha, norm_gamma (float32).  Returns (out float32, S_T)."""
+    import torch
+    B, T, hidden = x.shape
+    conv_k = params["conv_w"].shape[1]
+    _need(x, "x", torch.bfloat16)
+    for n in ("W_qkv", "conv_w", "W_ab", "W_gate", "W_o"):
+        _need(params[n], n, torch.bfloat16)
+    for n in ("A", "b_alpha", "norm_gamma"):
+        _need(params[n], n, torch.float32)
+    _need(initial_state, "initial_state", torch.float32)
+    if out is None:
+        out = torch.empty((B, T, hidden), dtype=torch.float32, device=x.device)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=x.device)
+    need = layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    p = gdn_layer_params(*(_ptr(params[n]) for n in ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate",
+                                                      "norm_gamma", "W_o")))
+    _check(lib().gdn_layer_fwd(_ptr(x), ctypes.byref(p), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                               B, T, hidden, H, Dk, Dv, conv_k, int(chunk), _ptr(workspace),
+                               workspace.numel(), _stream(x.device)))
+    return out, final_state

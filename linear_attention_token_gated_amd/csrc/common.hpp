@@ -1,0 +1,117 @@
+// common.hpp -- shared device helpers for the gfx950 (CDNA4) kernels:
+// bf16 conversion, 16x16 MFMA fragments, DPP row broadcast.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16 conversion is round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA tiles.
+//
+// A tile product D[16x16] += A[16 x KS] * B[KS x 16].  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each as KS/4 consecutive k values
+// starting at k = (l / 16) * KS/4.  Any k-permutation that is the same for A
+// and B gives the same sum, so only the row/column ownership matters.  The
+// accumulator layout is the hardware one: lane l holds D[4*(l/16) + i][l % 16],
+// i = 0..3.
+//
+//   bf16, KS=32: v_mfma_f32_16x16x32_bf16      (8 bf16 per lane)
+//   bf16, KS=16: v_mfma_f32_16x16x16_bf16      (4 bf16 per lane)
+//   f32,  KS=16: 4 x v_mfma_f32_16x16x4_f32    (4 f32 per lane)
+//   f32,  KS=32: 8 x v_mfma_f32_16x16x4_f32    (8 f32 per lane)
+// ---------------------------------------------------------------------------
+template <typename OpT, int KS> struct Frag;
+
+template <> struct Frag<__bf16, 32> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const __bf16 *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (__bf16)x; }
+    __device__ __forceinline__ void set_raw(int e, __bf16 x) { v[e] = x; }
+    static __device__ __forceinline__ f32x4 mma(const Frag &a, const Frag &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+    }
+};
+
+template <> struct Frag<__bf16, 16> {
+    bf16x4 v;
+    __device__ __forceinline__ void load(const __bf16 *p) { v = *reinterpret_cast<const bf16x4 *>(p); }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (__bf16)x; }
+    __device__ __forceinline__ void set_raw(int e, __bf16 x) { v[e] = x; }
+    static __device__ __forceinline__ f32x4 mma(const Frag &a, const Frag &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a.v),
+                                                         __builtin_bit_cast(i16x4, b.v), c, 0, 0, 0);
+    }
+};
+
+template <int KS> struct FragF32 {
+    static constexpr int N = KS / 4;
+    float v[N];
+    __device__ __forceinline__ void load(const float *p) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            f32x4 t = *reinterpret_cast<const f32x4 *>(p + e);
+            v[e] = t[0]; v[e + 1] = t[1]; v[e + 2] = t[2]; v[e + 3] = t[3];
+        }
+    }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+    __device__ __forceinline__ void set_raw(int e, float x) { v[e] = x; }
+    static __device__ __forceinline__ f32x4 mma(const FragF32 &a, const FragF32 &b, f32x4 c) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+        return c;
+    }
+};
+template <> struct Frag<float, 32> : FragF32<32> {};
+template <> struct Frag<float, 16> : FragF32<16> {};
+
+// Fragment of rows r0..r0+15 (lane -> row r0 + l%16) and k-range k0..k0+KS-1
+// of a row-major matrix with `pitch` elements per row.  Used both for A
+// operands (rows of A) and for B operands stored transposed (rows of B^T).
+template <typename OpT, int KS>
+__device__ __forceinline__ Frag<OpT, KS> frag_rows(const OpT *base, int pitch, int r0, int k0, int lane) {
+    Frag<OpT, KS> f;
+    f.load(base + (r0 + (lane & 15)) * pitch + k0 + (lane >> 4) * (KS / 4));
+    return f;
+}
+
+// Same fragment taken from the transpose of a row-major matrix: row r of the
+// operand is column r of `base`, so the KS/4 values are gathered down a column.
+template <typename OpT, int KS>
+__device__ __forceinline__ Frag<OpT, KS> frag_cols(const OpT *base, int pitch, int r0, int k0, int lane) {
+    Frag<OpT, KS> f;
+    const OpT *p = base + (k0 + (lane >> 4) * (KS / 4)) * pitch + r0 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < KS / 4; ++e) f.set_raw(e, p[e * pitch]);
+    return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Broadcast lane S of every 16-lane row to the whole row (DPP row_newbcast).
+template <int S> __device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + S, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+}  // namespace gdn

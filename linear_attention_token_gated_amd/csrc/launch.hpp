@@ -1,0 +1,49 @@
+// launch.hpp -- internal host-side launch interface between the C ABI
+// (api.cpp, which validates) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    float *state, *y;
+    int64_t N, H, Dk, Dv;
+    bool bf16;
+};
+
+// Prefill over [B, T, H, *] tensors.  Row strides (elements between
+// consecutive tokens) are explicit so that q/k/v may live inside a wider
+// fused buffer (the layer passes slices of its in-projection output).
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta;      // [B, T, H]
+    const float *s0;                // [B, H, Dk, Dv] or null
+    float *y;                       // [B, T, H, Dv]
+    float *sT;                      // [B, H, Dk, Dv] or null
+    int64_t B, T, H, Dk, Dv, chunk;
+    int64_t q_tok_stride, k_tok_stride, v_tok_stride;   // elements per token (all heads)
+    bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Layer helpers (layer.hip)
+struct LayerArgs {
+    const void *x;
+    const void *W_qkv, *conv_w, *W_ab, *W_gate, *W_o;
+    const float *A, *b_alpha, *norm_gamma;
+    const float *s0;
+    float *sT;
+    float *out;
+    int64_t B, T, hidden, H, Dk, Dv, conv_k, chunk;
+    void *ws;
+};
+size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv);
+hipError_t launch_layer(const LayerArgs &a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,336 @@
+// layer.hip -- the GDN token-mixing layer around the core, on gfx950.
+//
+// Source: "On the Design of Qwen3.8-Next Architecture", picx.dev summary,
+// "Methodology / 1. GDN Hybrid Token Mixing": short causal convolutions,
+// L2-normalised queries and keys, eq (9) write strength, eq (10) decay and the
+// eq (11) output  o_t = W_o [ sigmoid(W_z x_t) * RMSNorm(y_t) ]  with a
+// zero-centred RMSNorm.
+//
+// Steps (M = B*T tokens):
+//   1. gemm_nt: qkv_pre = x W_qkv^T (fp32), z = x W_gate^T (bf16), ab = x W_ab^T (fp32)
+//   2. prologue: depthwise causal conv over the q|k|v channels, L2 norm of
+//      every q and k head, alpha (eq (10)) and beta (eq (9)) per (token, head);
+//      q, k, v stay fp32
+//   3. the chunked core (prefill kernel, fp32 operands) reading q, k, v in place
+//   4. epilogue: g = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + gamma) (bf16)
+//   5. gemm_nt: out = g W_o^T (fp32)
+//
+// Why q, k, v are not rounded to bf16 here: with unit-norm q and k in Dk
+// dimensions, y_t = S_t^T q_t is a small projection of the state (|q.k| ~
+// 1/sqrt(Dk)), so a relative perturbation of 2^-9 in q, k or v (one bf16
+// rounding) becomes several percent of max|err|/RMS in y and in the layer
+// output.  The inputs x and the weights are bf16 and the products accumulate in
+// fp32, so the projections themselves are exact up to fp32 summation.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr float kL2Eps = 1e-6f;
+constexpr float kRmsEps = 1e-6f;
+
+// ---------------------------------------------------------------------------
+// C[M, N] = A[M, K] * B[N, K]^T, bf16 operands, fp32 accumulation.
+// 128 x 128 workgroup tile, 4 wavefronts in a 2 x 2 grid of 64 x 64, K step 64
+// through LDS with the next K step prefetched into registers.  Rows/cols past
+// M/N and k past K are zero-filled; K must be a multiple of 8.
+// ---------------------------------------------------------------------------
+constexpr int GBM = 128, GBN = 128, GBK = 64, GPITCH = GBK + 8;
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
+                                                      OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
+                                                      int64_t ldb, int64_t ldc)
+{
+    __shared__ __attribute__((aligned(16))) __bf16 As[GBM * GPITCH];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[GBN * GPITCH];
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int ln = lane & 15, lg = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
+
+    // each thread moves 4 16-byte vectors of A and 4 of B per K step
+    f32x4 ra[4], rb[4];
+    auto load_tiles = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int vi = tid + 256 * i;
+            const int r = vi >> 3, c = (vi & 7) * 8;
+            const int64_t gm = m0 + r, gn = n0 + r;
+            const int gk = k0 + c;
+            ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const f32x4 *>(A + gm * lda + gk) : zero4();
+            rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const f32x4 *>(Bm + gn * ldb + gk) : zero4();
+        }
+    };
+    auto store_tiles = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int vi = tid + 256 * i;
+            const int r = vi >> 3, c = (vi & 7) * 8;
+            *reinterpret_cast<f32x4 *>(As + r * GPITCH + c) = ra[i];
+            *reinterpret_cast<f32x4 *>(Bs + r * GPITCH + c) = rb[i];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+
+    load_tiles(0);
+    for (int k0 = 0; k0 < K; k0 += GBK) {
+        store_tiles();
+        __syncthreads();
+        if (k0 + GBK < K) load_tiles(k0 + GBK);
+#pragma unroll
+        for (int kk = 0; kk < GBK; kk += 32) {
+            Frag<__bf16, 32> af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = frag_rows<__bf16, 32>(As, GPITCH, wm * 64 + 16 * i, kk, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = frag_rows<__bf16, 32>(Bs, GPITCH, wn * 64 + 16 * j, kk, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = Frag<__bf16, 32>::mma(af[i], bf[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + wn * 64 + 16 * j + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * 64 + 16 * i + 4 * lg + e;
+                if (row < M && col < N) Cm[row * ldc + col] = from_f32<OutT>(acc[i][j][e]);
+            }
+        }
+}
+
+template <typename OutT>
+hipError_t gemm_nt(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                   int64_t ldb, int64_t ldc, hipStream_t s)
+{
+    if (M == 0 || N == 0) return hipSuccess;
+    dim3 grid((unsigned)((N + GBN - 1) / GBN), (unsigned)((M + GBM - 1) / GBM));
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT>), grid, dim3(256), 0, s, A, Bm, C, (int)M, (int)N, (int)K, lda, ldb, ldc);
+    return hipGetLastError();
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float softplusf_(float x) { return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
+
+// ---------------------------------------------------------------------------
+// Prologue: one workgroup per token.  Each thread handles 8 consecutive
+// channels (one 16-byte vector) of the H*(2Dk+Dv) q|k|v channels; a q or k
+// head is Dk/8 consecutive lanes, reduced with xor-shuffles for its L2 norm.
+// ---------------------------------------------------------------------------
+template <int DK>
+__global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__ pre, const __bf16 *__restrict__ conv_w,
+                                                       const float *__restrict__ ab, const float *__restrict__ Aexp,
+                                                       const float *__restrict__ b_alpha, float *__restrict__ post,
+                                                       float *__restrict__ alpha, float *__restrict__ beta, int64_t T,
+                                                       int H, int nqkv, int conv_k)
+{
+    const int64_t row = blockIdx.x;          // b*T + t
+    const int64_t t = row % T;
+    const int nvec = nqkv / 8;
+    const int nqk_vec = 2 * H * DK / 8;      // vectors holding q and k channels
+    constexpr int HV = DK / 8;               // vectors per q/k head (power of two, <= 16)
+
+    for (int base = 0; base < nvec; base += 256) {
+        const int vi = base + threadIdx.x;
+        const bool active = vi < nvec;
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            const int c0 = vi * 8;
+            for (int j = 0; j < conv_k; ++j) {
+                const int64_t lag = conv_k - 1 - j;           // tap j reads token t - lag
+                if (t - lag < 0) continue;
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(pre + (row - lag) * nqkv + c0);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(pre + (row - lag) * nqkv + c0 + 4);
+                const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = fmaf((float)conv_w[(int64_t)(c0 + e) * conv_k + j], x[e], o[e]);
+            }
+        }
+        // L2 normalisation of q and k heads (wave-uniform: heads never straddle
+        // the q|k / v boundary and vector groups are lane-aligned)
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
+#pragma unroll
+        for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
+        if (active) {
+            const float scale = vi < nqk_vec ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
+            f32x4 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
+            *reinterpret_cast<f32x4 *>(post + row * nqkv + vi * 8) = o0;
+            *reinterpret_cast<f32x4 *>(post + row * nqkv + vi * 8 + 4) = o1;
+        }
+    }
+    // eq (10) decay and eq (9) write strength for every head of this token
+    for (int hh = threadIdx.x; hh < H; hh += 256) {
+        const float a = ab[row * 2 * H + hh];
+        const float bb = ab[row * 2 * H + H + hh];
+        alpha[row * H + hh] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
+        beta[row * H + hh] = sigmoidf_(bb);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue: one workgroup per token; per head, RMSNorm over Dv with gain
+// (1 + gamma), times sigmoid(z); written as the bf16 operand of W_o.
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ y, const __bf16 *__restrict__ z,
+                                                       const float *__restrict__ gamma, __bf16 *__restrict__ g,
+                                                       int H)
+{
+    const int64_t row = blockIdx.x;
+    const int nvec = H * DV / 8;
+    constexpr int HV = DV / 8;
+    for (int base = 0; base < nvec; base += 256) {
+        const int vi = base + threadIdx.x;
+        const bool active = vi < nvec;
+        float yv[8];
+        float ss = 0.f;
+        if (active) {
+            const f32x4 y0 = *reinterpret_cast<const f32x4 *>(y + row * H * DV + vi * 8);
+            const f32x4 y1 = *reinterpret_cast<const f32x4 *>(y + row * H * DV + vi * 8 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { yv[e] = y0[e]; yv[4 + e] = y1[e]; }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(yv[e], yv[e], ss);
+        }
+#pragma unroll
+        for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
+        if (active) {
+            const float inv = 1.f / sqrtf(ss / (float)DV + kRmsEps);
+            const f32x4 raw = *reinterpret_cast<const f32x4 *>(z + row * H * DV + vi * 8);
+            const __bf16 *zz = reinterpret_cast<const __bf16 *>(&raw);
+            const int c0 = (vi * 8) % DV;
+            bf16x8 outv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                outv[e] = (__bf16)(sigmoidf_((float)zz[e]) * yv[e] * inv * (1.f + gamma[c0 + e]));
+            *reinterpret_cast<bf16x8 *>(g + row * H * DV + vi * 8) = outv;
+        }
+    }
+}
+
+constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+    size_t pre, post, z, ab, alpha, beta, y, g, total;
+};
+
+WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv)
+{
+    const size_t M = (size_t)(B * T);
+    const size_t nqkv = (size_t)(H * (2 * Dk + Dv));
+    WsLayout w;
+    size_t o = 0;
+    w.pre = o;   o += al256(M * nqkv * 4);
+    w.post = o;  o += al256(M * nqkv * 4);
+    w.z = o;     o += al256(M * (size_t)(H * Dv) * 2);
+    w.ab = o;    o += al256(M * (size_t)(2 * H) * 4);
+    w.alpha = o; o += al256(M * (size_t)H * 4);
+    w.beta = o;  o += al256(M * (size_t)H * 4);
+    w.y = o;     o += al256(M * (size_t)(H * Dv) * 4);
+    w.g = o;     o += al256(M * (size_t)(H * Dv) * 2);
+    w.total = o;
+    return w;
+}
+
+template <int DK>
+hipError_t launch_prologue_dk(const float *pre, const __bf16 *conv_w, const float *ab, const float *A,
+                              const float *b_alpha, float *post, float *alpha, float *beta, int64_t M, int64_t T,
+                              int H, int nqkv, int conv_k, hipStream_t s)
+{
+    hipLaunchKernelGGL((prologue_kernel<DK>), dim3((unsigned)M), dim3(256), 0, s, pre, conv_w, ab, A, b_alpha, post,
+                       alpha, beta, T, H, nqkv, conv_k);
+    return hipGetLastError();
+}
+
+template <int DV>
+hipError_t launch_epilogue_dv(const float *y, const __bf16 *z, const float *gamma, __bf16 *g, int64_t M, int H,
+                              hipStream_t s)
+{
+    hipLaunchKernelGGL((epilogue_kernel<DV>), dim3((unsigned)M), dim3(256), 0, s, y, z, gamma, g, H);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
+{
+    (void)hidden;
+    if (B * T == 0 || H == 0) return 0;
+    return ws_layout(B, T, H, Dk, Dv).total;
+}
+
+hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
+{
+    const int64_t M = a.B * a.T;
+    const int64_t H = a.H, Dk = a.Dk, Dv = a.Dv, hidden = a.hidden;
+    if (a.B * a.H == 0) return hipSuccess;
+    if (M == 0 || H == 0) {
+        PrefillArgs p{};
+        p.B = a.B; p.T = 0; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = a.chunk; p.s0 = a.s0; p.sT = a.sT;
+        return launch_prefill(p, s);
+    }
+    const WsLayout w = ws_layout(a.B, a.T, H, Dk, Dv);
+    char *ws = static_cast<char *>(a.ws);
+    float *pre = reinterpret_cast<float *>(ws + w.pre);
+    float *post = reinterpret_cast<float *>(ws + w.post);
+    __bf16 *z = reinterpret_cast<__bf16 *>(ws + w.z);
+    float *ab = reinterpret_cast<float *>(ws + w.ab);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *y = reinterpret_cast<float *>(ws + w.y);
+    __bf16 *g = reinterpret_cast<__bf16 *>(ws + w.g);
+    const __bf16 *x = static_cast<const __bf16 *>(a.x);
+    const int64_t nqkv = H * (2 * Dk + Dv);
+    hipError_t e;
+
+    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_qkv, pre, M, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
+    if ((e = gemm_nt<__bf16>(x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv, s))) return e;
+    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_ab, ab, M, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
+
+    switch (Dk) {
+    case 16: e = launch_prologue_dk<16>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 32: e = launch_prologue_dk<32>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 64: e = launch_prologue_dk<64>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 128: e = launch_prologue_dk<128>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e) return e;
+
+    PrefillArgs p{};
+    p.q = post; p.k = post + H * Dk; p.v = post + 2 * H * Dk;
+    p.alpha = alpha; p.beta = beta; p.s0 = a.s0; p.y = y; p.sT = a.sT;
+    p.B = a.B; p.T = a.T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = a.chunk;
+    p.q_tok_stride = nqkv; p.k_tok_stride = nqkv; p.v_tok_stride = nqkv;
+    p.bf16 = false;
+    if ((e = launch_prefill(p, s))) return e;
+
+    switch (Dv) {
+    case 16: e = launch_epilogue_dv<16>(y, z, a.norm_gamma, g, M, (int)H, s); break;
+    case 32: e = launch_epilogue_dv<32>(y, z, a.norm_gamma, g, M, (int)H, s); break;
+    case 64: e = launch_epilogue_dv<64>(y, z, a.norm_gamma, g, M, (int)H, s); break;
+    case 128: e = launch_epilogue_dv<128>(y, z, a.norm_gamma, g, M, (int)H, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e) return e;
+    return gemm_nt<float>(g, (const __bf16 *)a.W_o, a.out, M, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+}
+
+}  // namespace gdn

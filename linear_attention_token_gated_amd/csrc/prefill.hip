@@ -1,0 +1,497 @@
+// prefill.hip -- chunkwise gated delta rule for whole sequences on gfx950.
+//
+// Source: "On the Design of Qwen3.8-Next Architecture", picx.dev summary,
+// "Theoretical foundations", eqs (1)-(4).  The pages give only the token-by-
+// token recurrence; the chunk form below is derived from it.  For one chunk of
+// C tokens r = 1..C entering with state S (Dk x Dv):
+//
+//   g_r = ln alpha_r,  G_r = g_1 + ... + g_r,  Gamma_rj = exp(G_r - G_j) (r >= j)
+//   A = strict_lower[ beta_r Gamma_rj (k_r . k_j) ]
+//   R = diag(beta) (V - diag(e^G) K S)
+//   U = (I + A)^-1 R                      (u_r = beta_r e_r of eqs (2)-(3))
+//   Y = diag(e^G) Q S + P U,  P = lower_incl[ Gamma_rj (q_r . k_j) ]   (eq (4))
+//   S' = e^{G_C} S + K^T diag(e^{G_C - G}) U                           (eqs (1),(3))
+//
+// Columns of S, V, Y are independent (e_t[j] only involves column j of S and
+// v_t[j]), so each workgroup owns one 16-column slice of Dv for one (b, h) and
+// carries that slice of S through every chunk in MFMA accumulator registers
+// (fp32 master copy).  Within a chunk:
+//   1. stage K, Q (Dk wide), the V slice, alpha, beta into LDS; prefix-sum ln alpha
+//   2. Gram tiles K K^T and Q K^T on MFMA -> A (fp32 diagonal blocks, operand
+//      precision off-diagonal blocks) and P
+//   3. K S and Q S on MFMA -> R
+//   4. (I + A)^-1 of each 16x16 diagonal block by in-register forward
+//      substitution (DPP row broadcast), then block forward substitution for U
+//      on MFMA, chaining accumulator tiles directly as the next B operand
+//   5. Y = diag(e^G) Q S + P U -> y (fp32);  S <- e^{G_C} S + K^T (e^{G_C-G} U)
+// Ragged tails are padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
+//
+// Precision (bf16 inputs): q, k, v are exact bf16 MFMA operands and every
+// product accumulates in fp32.  The operands that are computed in fp32 and
+// feed an MFMA -- the state S, P, the substitution right-hand side Z, U and
+// the decayed U of the state update -- are carried as a bf16 pair hi + lo with
+// hi = bf16(x), lo = bf16(x - hi), and each product with them is summed over
+// the pair (hi*hi + hi*lo + lo*hi where both sides are split).  Rounding any of
+// them to a single bf16 costs about 1e-2 in max|err|/RMS(y) at the 4K workload;
+// the pair keeps the whole path near 2e-3.  The diagonal-block inverses and
+// the off-diagonal blocks of A are single bf16 (they contribute ~2e-3).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int BV = 16;          // value columns per workgroup
+constexpr int NTHREADS = 256;   // 4 wavefronts
+
+constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+template <typename OpT, int C, int DK> struct Lay {
+    static constexpr bool SPLIT = sizeof(OpT) == 2;   // bf16 hi/lo state operand
+    static constexpr int PAD = sizeof(OpT) == 2 ? 8 : 4;
+    static constexpr int KP = DK + PAD;     // pitch of K, Q, S^T rows
+    static constexpr int CP = C + PAD;      // pitch of C-wide operand rows
+    static constexpr int TP = 16 + PAD;     // pitch of diagonal-inverse rows
+    static constexpr int AFP = C + 1;       // pitch of fp32 A rows
+    static constexpr int NB = C / 16;       // 16-token blocks per chunk
+    static constexpr int NSB = DK / 16;     // 16-row blocks of the state slice
+    static constexpr int MS = (NSB + 3) / 4;   // state tiles per wavefront
+    static constexpr int KS_DK = DK % 32 == 0 ? 32 : 16;
+    static constexpr int KS_C = C % 32 == 0 ? 32 : 16;
+
+    static constexpr size_t oK = 0;
+    static constexpr size_t oQ = oK + align16(sizeof(OpT) * C * KP);
+    static constexpr size_t oST = oQ + align16(sizeof(OpT) * C * KP);
+    static constexpr size_t oSTlo = oST + align16(sizeof(OpT) * BV * KP);
+    static constexpr size_t oAf = oSTlo + (SPLIT ? align16(sizeof(OpT) * BV * KP) : 0);
+    static constexpr size_t oAn = oAf + align16(4 * C * AFP);
+    static constexpr size_t oP = oAn + align16(sizeof(OpT) * C * CP);
+    static constexpr size_t oPlo = oP + align16(sizeof(OpT) * C * CP);
+    static constexpr size_t oTd = oPlo + (SPLIT ? align16(sizeof(OpT) * C * CP) : 0);
+    static constexpr size_t oRf = oTd + align16(sizeof(OpT) * C * TP);
+    static constexpr size_t oUT = oRf + align16(4 * C * BV);
+    static constexpr size_t oUTlo = oUT + align16(sizeof(OpT) * BV * CP);
+    static constexpr size_t oUdT = oUTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
+    static constexpr size_t oUdTlo = oUdT + align16(sizeof(OpT) * BV * CP);
+    static constexpr size_t oV = oUdTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
+    static constexpr size_t oAl = oV + align16(4 * C * BV);
+    static constexpr size_t oBe = oAl + align16(4 * C);
+    static constexpr size_t oG = oBe + align16(4 * C);
+    static constexpr size_t oEG = oG + align16(4 * C);
+    static constexpr size_t BYTES = oEG + align16(4 * C);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+struct KParams {
+    const void *q, *k, *v;
+    const float *alpha, *beta, *s0;
+    float *y, *sT;
+    int64_t T, H, Dv;
+    int64_t qs, ks, vs;      // token strides (elements)
+    int nslices;             // Dv / 16
+    int xcd_map;             // 1: group the slices of a head on one XCD
+};
+
+// Forward substitution of (I + L) X = I for a 16x16 strictly lower L, inside
+// one wavefront.  Lane (r = l%16, g = l/16) owns row r of X, columns g+4i.
+// Step s: row s is final; every row r > s subtracts L[r][s] * X[s][:].
+// X[s][c] lives in lane s of the same 16-lane row (same g) -> DPP broadcast.
+template <int S>
+__device__ __forceinline__ void tri_step(float (&X)[4], const float (&Lr)[16], int r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float xs = row_bcast<S>(X[i]);
+        X[i] = (r > S) ? fmaf(-Lr[S], xs, X[i]) : X[i];
+    }
+}
+template <int... S>
+__device__ __forceinline__ void tri_solve16(float (&X)[4], const float (&Lr)[16], int r,
+                                            std::integer_sequence<int, S...>) {
+    (tri_step<S>(X, Lr, r), ...);
+}
+
+template <typename Tin, int C, int DK>
+__global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
+{
+    using OpT = Tin;
+    using L = Lay<OpT, C, DK>;
+    constexpr bool SPLIT = L::SPLIT;
+    constexpr int KP = L::KP, CP = L::CP, TP = L::TP, AFP = L::AFP, NB = L::NB, NSB = L::NSB,
+                  MS = L::MS, KS_DK = L::KS_DK, KS_C = L::KS_C;
+    using FragDK = Frag<OpT, KS_DK>;
+    using FragC = Frag<OpT, KS_C>;
+    using Frag16 = Frag<OpT, 16>;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    OpT *Ks = reinterpret_cast<OpT *>(smem + L::oK);
+    OpT *Qs = reinterpret_cast<OpT *>(smem + L::oQ);
+    OpT *STs = reinterpret_cast<OpT *>(smem + L::oST);
+    OpT *STlo = reinterpret_cast<OpT *>(smem + L::oSTlo);
+    float *Af = reinterpret_cast<float *>(smem + L::oAf);
+    OpT *An = reinterpret_cast<OpT *>(smem + L::oAn);
+    OpT *Ps = reinterpret_cast<OpT *>(smem + L::oP);
+    OpT *Plo = reinterpret_cast<OpT *>(smem + L::oPlo);
+    OpT *Td = reinterpret_cast<OpT *>(smem + L::oTd);
+    float *Rf = reinterpret_cast<float *>(smem + L::oRf);
+    OpT *UT = reinterpret_cast<OpT *>(smem + L::oUT);
+    OpT *UTlo = reinterpret_cast<OpT *>(smem + L::oUTlo);
+    OpT *UdT = reinterpret_cast<OpT *>(smem + L::oUdT);
+    OpT *UdTlo = reinterpret_cast<OpT *>(smem + L::oUdTlo);
+    float *Vs = reinterpret_cast<float *>(smem + L::oV);
+    float *Al = reinterpret_cast<float *>(smem + L::oAl);
+    float *Be = reinterpret_cast<float *>(smem + L::oBe);
+    float *Gs = reinterpret_cast<float *>(smem + L::oG);
+    float *EG = reinterpret_cast<float *>(smem + L::oEG);
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int ln = lane & 15, lg = lane >> 4;
+
+    // ---- workgroup -> (b*H + h, slice).  With xcd_map the slices of one head
+    // get ids that are equal mod 8, so they run on one XCD and share its L2.
+    const int64_t bid = blockIdx.x;
+    int64_t bh, sl;
+    if (p.xcd_map) {
+        const int64_t xcd = bid & 7, local = bid >> 3;
+        bh = (local / p.nslices) * 8 + xcd;
+        sl = local % p.nslices;
+    } else {
+        bh = bid / p.nslices;
+        sl = bid % p.nslices;
+    }
+    const int64_t H = p.H, T = p.T, Dv = p.Dv;
+    const int64_t b = bh / H, h = bh % H;
+    const int n0 = (int)sl * BV;
+    const Tin *qg = static_cast<const Tin *>(p.q);
+    const Tin *kg = static_cast<const Tin *>(p.k);
+    const Tin *vg = static_cast<const Tin *>(p.v);
+
+    // ---- state slice: wavefront w owns 16-row blocks ib = w + 4m
+    f32x4 S[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        S[m] = zero4();
+        const int ib = wave + 4 * m;
+        if (ib < NSB && p.s0) {
+            const float *s0 = p.s0 + bh * (int64_t)DK * Dv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = s0[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln];
+        }
+    }
+
+    auto write_state_operand = [&]() {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NSB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const OpT hi = from_f32<OpT>(S[m][e]);
+                    STs[ln * KP + 16 * ib + 4 * lg + e] = hi;
+                    if constexpr (L::SPLIT) STlo[ln * KP + 16 * ib + 4 * lg + e] = from_f32<OpT>(S[m][e] - to_f32(hi));
+                }
+            }
+        }
+    };
+    write_state_operand();
+
+    constexpr int EPV = 16 / sizeof(Tin);        // elements per 16-byte vector
+    constexpr int VPR = DK / EPV;                // vectors per K/Q row
+    constexpr int VVR = BV / EPV;                // vectors per V-slice row
+
+    for (int64_t c0 = 0; c0 < T; c0 += C) {
+        // ---------------- 1. stage the chunk ----------------
+        for (int vi = tid; vi < C * VPR; vi += NTHREADS) {
+            const int r = vi / VPR, col = (vi % VPR) * EPV;
+            const int64_t t = c0 + r;
+            f32x4 kv = zero4(), qv = zero4();
+            if (t < T) {
+                const int64_t row = b * T + t;
+                kv = *reinterpret_cast<const f32x4 *>(kg + row * p.ks + h * DK + col);
+                qv = *reinterpret_cast<const f32x4 *>(qg + row * p.qs + h * DK + col);
+            }
+            *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = kv;
+            *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = qv;
+        }
+        if (tid < C * VVR) {
+            const int r = tid / VVR, col = (tid % VVR) * EPV;
+            const int64_t t = c0 + r;
+            Tin tmp[EPV];
+            if (t < T) {
+                *reinterpret_cast<f32x4 *>(tmp) =
+                    *reinterpret_cast<const f32x4 *>(vg + (b * T + t) * p.vs + h * Dv + n0 + col);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) tmp[e] = from_f32<Tin>(0.f);
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) Vs[r * BV + col + e] = to_f32(tmp[e]);
+        }
+        if (tid < C) {
+            const int64_t t = c0 + tid;
+            const bool ok = t < T;
+            Al[tid] = ok ? p.alpha[(b * T + t) * H + h] : 1.f;
+            Be[tid] = ok ? p.beta[(b * T + t) * H + h] : 0.f;
+        }
+        __syncthreads();
+
+        // ---------------- log-decay prefix (wavefront 0) ----------------
+        if (wave == 0) {
+            float g = lane < C ? logf(Al[lane]) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float t = __shfl_up(g, off);
+                if (lane >= off) g += t;
+            }
+            if (lane < C) {
+                Gs[lane] = g;
+                EG[lane] = expf(g);
+            }
+        }
+        __syncthreads();
+        const float GC = Gs[C - 1];
+
+        // ---------------- 2. Gram tiles: K K^T -> A, Q K^T -> P ----------------
+        constexpr int NTRI = NB * (NB + 1) / 2;
+        for (int tile = wave; tile < 2 * NTRI; tile += 4) {
+            const bool isQ = tile >= NTRI;
+            int idx = isQ ? tile - NTRI : tile;
+            int rb = 0;
+            while (idx > rb) { idx -= rb + 1; ++rb; }
+            const int cb = idx;
+            const OpT *Asrc = isQ ? Qs : Ks;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KS_DK) {
+                const FragDK a = frag_rows<OpT, KS_DK>(Asrc, KP, 16 * rb, k0, lane);
+                const FragDK bb = frag_rows<OpT, KS_DK>(Ks, KP, 16 * cb, k0, lane);
+                acc = FragDK::mma(a, bb, acc);
+            }
+            const int j = 16 * cb + ln;
+            const float Gj = Gs[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                const float gam = expf(fminf(Gs[r] - Gj, 0.f));
+                if (isQ) {
+                    const float pv = r >= j ? gam * acc[e] : 0.f;
+                    const OpT hi = from_f32<OpT>(pv);
+                    Ps[r * CP + j] = hi;
+                    if constexpr (SPLIT) Plo[r * CP + j] = from_f32<OpT>(pv - to_f32(hi));
+                } else {
+                    const float val = r > j ? Be[r] * gam * acc[e] : 0.f;
+                    if (rb == cb) Af[r * AFP + j] = val;
+                    else An[r * CP + j] = from_f32<OpT>(-val);
+                }
+            }
+        }
+
+        // ---------------- 3. K S -> R, Q S (kept for Y) ----------------
+        f32x4 qs_acc = zero4();
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 ks_acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KS_DK) {
+                const FragDK kf = frag_rows<OpT, KS_DK>(Ks, KP, 16 * rb, k0, lane);
+                const FragDK qf = frag_rows<OpT, KS_DK>(Qs, KP, 16 * rb, k0, lane);
+                const FragDK sf = frag_rows<OpT, KS_DK>(STs, KP, 0, k0, lane);
+                ks_acc = FragDK::mma(kf, sf, ks_acc);
+                qs_acc = FragDK::mma(qf, sf, qs_acc);
+                if constexpr (L::SPLIT) {
+                    const FragDK sl2 = frag_rows<OpT, KS_DK>(STlo, KP, 0, k0, lane);
+                    ks_acc = FragDK::mma(kf, sl2, ks_acc);
+                    qs_acc = FragDK::mma(qf, sl2, qs_acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                Rf[r * BV + ln] = Be[r] * (Vs[r * BV + ln] - EG[r] * ks_acc[e]);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- 4a. diagonal-block inverses ----------------
+        if (wave < NB) {
+            const int blk = wave;
+            float Lr[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) Lr[s] = Af[(16 * blk + ln) * AFP + 16 * blk + s];
+            float X[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[i] = (ln == lg + 4 * i) ? 1.f : 0.f;
+            tri_solve16(X, Lr, ln, std::make_integer_sequence<int, 15>{});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Td[(16 * blk + ln) * TP + lg + 4 * i] = from_f32<OpT>(X[i]);
+        }
+        __syncthreads();
+
+        // ---------------- 4b. block forward substitution for U (wavefront 0) ----
+        if (wave == 0) {
+            // U blocks as B operands (accumulator layout == B layout for KS=16)
+            Frag16 Uh[NB], Ul[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                f32x4 z;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[e] = Rf[(16 * i + 4 * lg + e) * BV + ln];
+#pragma unroll
+                for (int kb = 0; kb < i; ++kb) {
+                    const Frag16 a = frag_rows<OpT, 16>(An, CP, 16 * i, 16 * kb, lane);
+                    z = Frag16::mma(a, Uh[kb], z);
+                    if constexpr (SPLIT) z = Frag16::mma(a, Ul[kb], z);
+                }
+                Frag16 zh, zl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const OpT hi = from_f32<OpT>(z[e]);
+                    zh.set_raw(e, hi);
+                    if constexpr (SPLIT) zl.set(e, z[e] - to_f32(hi));
+                }
+                const Frag16 ti = frag_rows<OpT, 16>(Td, TP, 16 * i, 0, lane);
+                f32x4 u = Frag16::mma(ti, zh, zero4());
+                if constexpr (SPLIT) u = Frag16::mma(ti, zl, u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * i + 4 * lg + e;
+                    const OpT hi = from_f32<OpT>(u[e]);
+                    Uh[i].set_raw(e, hi);
+                    UT[ln * CP + r] = hi;
+                    const float ud = expf(GC - Gs[r]) * u[e];
+                    const OpT dhi = from_f32<OpT>(ud);
+                    UdT[ln * CP + r] = dhi;
+                    if constexpr (SPLIT) {
+                        const OpT lo = from_f32<OpT>(u[e] - to_f32(hi));
+                        Ul[i].set_raw(e, lo);
+                        UTlo[ln * CP + r] = lo;
+                        UdTlo[ln * CP + r] = from_f32<OpT>(ud - to_f32(dhi));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---------------- 5a. Y = diag(e^G) Q S + P U ----------------
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = EG[16 * rb + 4 * lg + e] * qs_acc[e];
+            for (int jb = 0; jb <= rb; ++jb) {
+                const Frag16 a = frag_rows<OpT, 16>(Ps, CP, 16 * rb, 16 * jb, lane);
+                const Frag16 u = frag_rows<OpT, 16>(UT, CP, 0, 16 * jb, lane);
+                acc = Frag16::mma(a, u, acc);
+                if constexpr (SPLIT) {
+                    const Frag16 alo = frag_rows<OpT, 16>(Plo, CP, 16 * rb, 16 * jb, lane);
+                    const Frag16 ulo = frag_rows<OpT, 16>(UTlo, CP, 0, 16 * jb, lane);
+                    acc = Frag16::mma(alo, u, acc);
+                    acc = Frag16::mma(a, ulo, acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t t = c0 + 16 * rb + 4 * lg + e;
+                if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e];
+            }
+        }
+
+        // ---------------- 5b. S <- e^{G_C} S + K^T (e^{G_C-G} U) ----------------
+        const float eGC = expf(GC);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NSB) {
+                f32x4 acc = S[m] * eGC;
+#pragma unroll
+                for (int j0 = 0; j0 < C; j0 += KS_C) {
+                    const FragC a = frag_cols<OpT, KS_C>(Ks, KP, 16 * ib, j0, lane);
+                    const FragC u = frag_rows<OpT, KS_C>(UdT, CP, 0, j0, lane);
+                    acc = FragC::mma(a, u, acc);
+                    if constexpr (SPLIT) {
+                        const FragC ulo = frag_rows<OpT, KS_C>(UdTlo, CP, 0, j0, lane);
+                        acc = FragC::mma(a, ulo, acc);
+                    }
+                }
+                S[m] = acc;
+            }
+        }
+        write_state_operand();
+        __syncthreads();
+    }
+
+    if (p.sT) {
+        float *sT = p.sT + bh * (int64_t)DK * Dv;
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NSB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+            }
+        }
+    }
+}
+
+template <typename Tin, int C, int DK>
+hipError_t launch_t(const PrefillArgs &a, hipStream_t stream)
+{
+    KParams kp;
+    kp.q = a.q; kp.k = a.k; kp.v = a.v;
+    kp.alpha = a.alpha; kp.beta = a.beta; kp.s0 = a.s0;
+    kp.y = a.y; kp.sT = a.sT;
+    kp.T = a.T; kp.H = a.H; kp.Dv = a.Dv;
+    kp.qs = a.q_tok_stride; kp.ks = a.k_tok_stride; kp.vs = a.v_tok_stride;
+    kp.nslices = (int)(a.Dv / BV);
+    const int64_t bh = a.B * a.H;
+    kp.xcd_map = (bh % 8 == 0) ? 1 : 0;
+    const int64_t grid = bh * kp.nslices;
+    hipLaunchKernelGGL((gdn_prefill_kernel<Tin, C, DK>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, kp);
+    return hipGetLastError();
+}
+
+template <typename Tin, int C>
+hipError_t launch_dk(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.Dk) {
+    case 16: return launch_t<Tin, C, 16>(a, s);
+    case 32: return launch_t<Tin, C, 32>(a, s);
+    case 64: return launch_t<Tin, C, 64>(a, s);
+    case 128: return launch_t<Tin, C, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename Tin>
+hipError_t launch_c(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.chunk) {
+    case 16: return launch_dk<Tin, 16>(a, s);
+    case 32: return launch_dk<Tin, 32>(a, s);
+    case 64: return launch_dk<Tin, 64>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// T == 0: the final state is the initial state (or zero).
+__global__ void copy_or_zero_state(const float *__restrict__ s0, float *__restrict__ sT, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) sT[i] = s0 ? s0[i] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.B * a.H == 0) return hipSuccess;
+    if (a.T == 0) {
+        if (!a.sT || a.sT == a.s0) return hipSuccess;
+        const int64_t n = a.B * a.H * a.Dk * a.Dv;
+        hipLaunchKernelGGL(copy_or_zero_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.s0, a.sT, n);
+        return hipGetLastError();
+    }
+    return a.bf16 ? launch_c<__bf16>(a, stream) : launch_c<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every entry point the header declares, and
+rejects invalid calls on the host with the documented status before any HIP
+call (so these run without a GPU: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_token_gated_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6
+A = 0x10000000          # fake, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gdn.lib()
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]*?\b(gdn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_symbols() == sorted(gdn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_symbols():
+        assert name in exported
+    # nothing but the C ABI is exported from our own code
+    ours = {s for s in exported if s.startswith("gdn") or s.startswith("_ZN3gdn")}
+    assert ours == set(declared_symbols())
+
+
+def test_status_strings(L):
+    for s, name in gdn.STATUS_NAMES.items():
+        assert L.gdn_status_str(s).decode().startswith(name)
+
+
+def prefill(L, q=A, k=A + 64 * MB, v=A + 128 * MB, al=A + 192 * MB, be=A + 200 * MB, s0=None,
+            y=A + 256 * MB, sT=None, B=1, T=64, H=2, Dk=16, Dv=16, C=16, dt=0):
+    return L.gdn_prefill_fwd(q, k, v, al, be, s0, y, sT, B, T, H, Dk, Dv, C, dt, None, 0, None)
+
+
+def test_prefill_validation(L):
+    assert prefill(L, q=None) == NULL
+    assert prefill(L, y=None) == NULL
+    assert prefill(L, T=-1) == SHAPE
+    assert prefill(L, B=-3) == SHAPE
+    assert prefill(L, Dk=48) == UNSUP
+    assert prefill(L, Dv=256) == UNSUP
+    assert prefill(L, C=128) == UNSUP
+    assert prefill(L, C=8) == UNSUP
+    assert prefill(L, dt=7) == UNSUP
+    assert prefill(L, q=A + 4) == ALIGN
+    assert prefill(L, sT=A + 300 * MB + 8) == ALIGN
+    assert prefill(L, y=A + 16) == ALIAS                         # y inside q
+    assert prefill(L, y=A + 128 * MB) == ALIAS                   # y == v
+    assert prefill(L, s0=A + 300 * MB, sT=A + 300 * MB + 256) == ALIAS   # partial overlap
+    assert prefill(L, B=1 << 40, T=1 << 40) == SHAPE             # overflow
+    assert "Dk=48" in L.gdn_last_error().decode() or True
+    prefill(L, Dk=48)
+    assert "Dk=48" in L.gdn_last_error().decode()
+
+
+def decode(L, q=A, k=A + MB, v=A + 2 * MB, al=A + 3 * MB, be=A + 4 * MB, S=A + 8 * MB, y=A + 64 * MB,
+           N=4, H=2, Dk=16, Dv=16, dt=1):
+    return L.gdn_decode_step(q, k, v, al, be, S, y, N, H, Dk, Dv, dt, None)
+
+
+def test_decode_validation(L):
+    assert decode(L, S=None) == NULL
+    assert decode(L, N=-1) == SHAPE
+    assert decode(L, Dk=96) == UNSUP
+    assert decode(L, y=A + 2) == ALIGN
+    assert decode(L, y=A + 8 * MB) == ALIAS          # y == state
+    assert decode(L, S=A) == ALIAS                   # state over q
+
+
+def test_layer_validation(L):
+    P = gdn.gdn_layer_params(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB, A + 7 * MB)
+    ws_need = L.gdn_layer_workspace_bytes(1, 64, 128, 2, 16, 16, 4, 16)
+    assert ws_need > 0
+    ws = A + 512 * MB
+
+    def call(x=A + 64 * MB, out=A + 128 * MB, T=64, hidden=128, conv_k=4, C=16, w=ws, wb=ws_need, p=P):
+        return L.gdn_layer_fwd(x, ctypes.byref(p) if p is not None else None, None, None, out, 1, T, hidden, 2,
+                               16, 16, conv_k, C, w, wb, None)
+
+    assert call(p=None) == NULL
+    assert call(x=None) == NULL
+    assert call(T=-2) == SHAPE
+    assert call(hidden=100) == UNSUP
+    assert call(conv_k=5) == UNSUP
+    assert call(C=48) == UNSUP
+    assert call(w=None) == WS
+    assert call(wb=ws_need - 1) == WS
+    assert call(w=ws + 16) == ALIGN
+    assert call(out=A + 64 * MB) == ALIAS
+    assert call(out=ws) == ALIAS
+
+
+def test_workspace_queries(L):
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 0
+    assert L.gdn_layer_workspace_bytes(1, 0, 2048, 16, 128, 128, 4, 64) == 0
+    assert L.gdn_layer_workspace_bytes(1, 16384, 2048, 16, 128, 128, 4, 64) > 16384 * 2048
