@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one call of the chunked prefill on the 32K-token workload (B=1,
+T=32768, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y)
+with every input already resident in HBM.  The line printed also carries the
+decode step (256 sequences x 32 heads, fp32 128x128 states updated in place)
+and the full layer (B=1, T=16384, hidden 2048, H=16) measured the same way,
+the roofline of the prefill kernel, and the fp64 oracle timed on the host
+cores on a bounded sample of the same workload.
+
+Timing: HIP events recorded on the stream the kernels are launched on
+(torch's current stream), around every launch of the timed region; the
+region itself is bracketed by device synchronisations.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s at T=32K (MFMA % peak); decode state GB/s (HBM % peak)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def prefill_alg(B, T, H, Dk, Dv, C, in_bytes=2, has_s0=False):
+    """Algorithmic bytes and flops of one prefill call (what the method must
+    move and compute, independent of the kernel): q, k, v read once, alpha and
+    beta read once, y (fp32) written once, final state written once."""
+    tok = B * T * H
+    bytes_ = tok * ((2 * Dk + Dv) * in_bytes + 8 + 4 * Dv) + B * H * Dk * Dv * 4 * (2 if has_s0 else 1)
+    f_alg = (3 * C - 1) * Dk + 2 * C * Dv + 6 * Dk * Dv + C * C / 3.0     # per token-head
+    return bytes_, tok * f_alg
+
+
+def decode_alg(N, H, Dk, Dv, in_bytes=2):
+    """State read + written once, q/k/v/alpha/beta read, y (fp32) written."""
+    per = 8 * Dk * Dv + (2 * Dk + Dv) * in_bytes + 8 + 4 * Dv
+    return N * H * per, N * H * 8 * Dk * Dv
+
+
+def layer_flops(B, T, hidden, H, Dk, Dv, C):
+    M = B * T
+    gemm = 2 * M * hidden * (H * (2 * Dk + Dv) + 2 * H + H * Dv) + 2 * M * (H * Dv) * hidden
+    core = B * T * H * ((3 * C - 1) * Dk + 2 * C * Dv + 6 * Dk * Dv + C * C / 3.0)
+    return gemm, core
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill.hip",
+                   "linear_attention_token_gated_amd/csrc/common.hpp"]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            t = json.load(f)["prefill_32k"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(PREFILL_SOURCES):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn warmup times, then `steps` times with a HIP event pair around
+    each launch on the current stream.  Returns (total ms of the bracketed
+    region, list of per-launch ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    return t_all0.elapsed_time(t_all1), [a.elapsed_time(b) for a, b in ev]
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bench_prefill(args, torch, gdn, wl):
+    cfg = wl.PREFILL_32K
+    inp = wl.prefill_config_inputs(cfg)
+    q, k, v = (to_dev(inp[n], torch) for n in ("q", "k", "v"))
+    al, be = to_dev(inp["alpha"], torch), to_dev(inp["beta"], torch)
+    y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
+    sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
+    fn = lambda: gdn.prefill(q, k, v, al, be, None, chunk=cfg.chunk, y=y, final_state=sT)
+    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
+    return cfg, inp, total_ms, per
+
+
+def bench_decode(args, torch, gdn, wl):
+    cfg = wl.DECODE_256
+    inp = wl.decode_config_inputs(cfg)
+    q, k, v = (to_dev(inp[n], torch) for n in ("q", "k", "v"))
+    al, be, S = (to_dev(inp[n], torch) for n in ("alpha", "beta", "S"))
+    y = torch.empty((cfg.N, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
+    fn = lambda: gdn.decode_step(q, k, v, al, be, S, y=y)   # in place: each step is a valid next step
+    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
+    return cfg, total_ms, per
+
+
+def bench_layer(args, torch, gdn, wl):
+    cfg = wl.LAYER_16K
+    inp = wl.layer_config_inputs(cfg)
+    names = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
+    params = {n: to_dev(inp[n], torch) for n in names}
+    x = to_dev(inp["x"], torch)
+    out = torch.empty((cfg.B, cfg.T, cfg.hidden), dtype=torch.float32, device="cuda")
+    sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.layer_workspace_bytes(cfg.B, cfg.T, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv, cfg.conv_k,
+                                               cfg.chunk), dtype=torch.uint8, device="cuda")
+    fn = lambda: gdn.layer_fwd(x, params, cfg.H, cfg.Dk, cfg.Dv, chunk=cfg.chunk, out=out, final_state=sT,
+                               workspace=ws)
+    steps = max(1, min(args.steps, 10))
+    total_ms, per = time_launches(fn, steps, max(1, min(args.warmup, 2)), torch)
+    return cfg, total_ms, per, steps
+
+
+def cpu_baseline(inp, cfg, wl, sample_T):
+    """The oracle, untouched, on the first sample_T tokens of every head."""
+    import oracle
+    sl = slice(0, sample_T)
+    args = [wl.widen(inp[n][:, sl]) for n in ("q", "k", "v", "alpha", "beta")]
+    t0 = time.perf_counter()
+    oracle.gdn_recurrence(*args, None)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.B * sample_T / dt, "unit": "tokens/s", "cores": oracle.last_threads_used,
+            "kind": "oracle",
+            "sample": f"fp64 sequential recurrence on the first {sample_T} tokens of all {cfg.B * cfg.H} "
+                      f"(batch, head) sequences of the 32K workload ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--skip-layer", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    from linear_attention_token_gated_amd import workloads as wl
+
+    gdn.lib()
+    props = torch.cuda.get_device_properties(0)
+
+    cfg, inp, p_total, p_per = bench_prefill(args, torch, gdn, wl)
+    alg_bytes, alg_flops = prefill_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
+    ms_step = p_total / args.steps
+    ms_launch = float(np.mean(p_per))
+    tok_s = cfg.B * cfg.T / (ms_step * 1e-3)
+    achieved_gbps = alg_bytes / (ms_launch * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    d_cfg, d_total, d_per = bench_decode(args, torch, gdn, wl)
+    d_bytes, _ = decode_alg(d_cfg.N, d_cfg.H, d_cfg.Dk, d_cfg.Dv)
+    d_state = 8 * d_cfg.N * d_cfg.H * d_cfg.Dk * d_cfg.Dv
+    d_ms = float(np.mean(d_per))
+
+    layer = None
+    if not args.skip_layer:
+        l_cfg, l_total, l_per, l_steps = bench_layer(args, torch, gdn, wl)
+        gemm_f, core_f = layer_flops(l_cfg.B, l_cfg.T, l_cfg.hidden, l_cfg.H, l_cfg.Dk, l_cfg.Dv, l_cfg.chunk)
+        l_ms = l_total / l_steps
+        layer = {"workload": l_cfg.name, "ms_per_step": round(l_ms, 4),
+                 "tokens_per_s": l_cfg.B * l_cfg.T / (l_ms * 1e-3),
+                 "gemm_tflops_alg": gemm_f / 1e12, "core_tflops_alg": core_f / 1e12,
+                 "tflops_achieved": (gemm_f + core_f) / (l_ms * 1e-3) / 1e12,
+                 "note": "core runs on fp32 q/k/v (fp32 MFMA); projections bf16 MFMA"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, cfg, wl, min(args.cpu_sample_tokens, cfg.T))
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "Dk": cfg.Dk, "Dv": cfg.Dv,
+                   "chunk": cfg.chunk, "qkv": "bf16", "alpha_beta_state_y": "fp32",
+                   "initial_state": "none"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "kernel": "gdn_prefill_kernel<bf16, C=64, Dk=128>",
+                     "ms_per_launch": round(ms_launch, 4),
+                     "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"flops_alg_per_launch": alg_flops,
+                 "tflops_achieved": alg_flops / (ms_launch * 1e-3) / 1e12,
+                 "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": alg_flops / (ms_launch * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "decode": {"workload": d_cfg.name, "ms_per_step": round(d_ms, 4),
+                   "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
+                   "state_GBps": d_state / (d_ms * 1e-3) / 1e9,
+                   "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                   "alg_bytes_per_launch": d_bytes},
+        "layer": layer,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

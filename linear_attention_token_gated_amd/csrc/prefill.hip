@@ -6,6 +6,7 @@
 // C tokens r = 1..C entering with state S (Dk x Dv):
 //
 //   g_r = ln alpha_r,  G_r = g_1 + ... + g_r,  Gamma_rj = exp(G_r - G_j) (r >= j)
+//   (computed in base 2: G2_r = sum log2 alpha, Gamma_rj = 2^(G2_r - G2_j))
 //   A = strict_lower[ beta_r Gamma_rj (k_r . k_j) ]
 //   R = diag(beta) (V - diag(e^G) K S)
 //   U = (I + A)^-1 R                      (u_r = beta_r e_r of eqs (2)-(3))
@@ -75,8 +76,7 @@ template <typename OpT, int C, int DK> struct Lay {
     static constexpr size_t oUdT = oUTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
     static constexpr size_t oUdTlo = oUdT + align16(sizeof(OpT) * BV * CP);
     static constexpr size_t oV = oUdTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
-    static constexpr size_t oAl = oV + align16(4 * C * BV);
-    static constexpr size_t oBe = oAl + align16(4 * C);
+    static constexpr size_t oBe = oV + align16(4 * C * BV);
     static constexpr size_t oG = oBe + align16(4 * C);
     static constexpr size_t oEG = oG + align16(4 * C);
     static constexpr size_t BYTES = oEG + align16(4 * C);
@@ -139,7 +139,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
     OpT *UdT = reinterpret_cast<OpT *>(smem + L::oUdT);
     OpT *UdTlo = reinterpret_cast<OpT *>(smem + L::oUdTlo);
     float *Vs = reinterpret_cast<float *>(smem + L::oV);
-    float *Al = reinterpret_cast<float *>(smem + L::oAl);
     float *Be = reinterpret_cast<float *>(smem + L::oBe);
     float *Gs = reinterpret_cast<float *>(smem + L::oG);
     float *EG = reinterpret_cast<float *>(smem + L::oEG);
@@ -198,90 +197,115 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
     constexpr int EPV = 16 / sizeof(Tin);        // elements per 16-byte vector
     constexpr int VPR = DK / EPV;                // vectors per K/Q row
     constexpr int VVR = BV / EPV;                // vectors per V-slice row
+    constexpr int NKV = (C * VPR + NTHREADS - 1) / NTHREADS;   // K (and Q) vectors per thread
 
-    for (int64_t c0 = 0; c0 < T; c0 += C) {
-        // ---------------- 1. stage the chunk ----------------
-        for (int vi = tid; vi < C * VPR; vi += NTHREADS) {
+    // Registers holding the next chunk while the current one is computed.
+    f32x4 pk[NKV], pq[NKV], pv = zero4();
+    float pal = 1.f, pbe = 0.f;
+    auto prefetch = [&](int64_t c0) {
+#pragma unroll
+        for (int it = 0; it < NKV; ++it) {
+            const int vi = tid + NTHREADS * it;
             const int r = vi / VPR, col = (vi % VPR) * EPV;
             const int64_t t = c0 + r;
-            f32x4 kv = zero4(), qv = zero4();
-            if (t < T) {
+            pk[it] = zero4();
+            pq[it] = zero4();
+            if (vi < C * VPR && t < T) {
                 const int64_t row = b * T + t;
-                kv = *reinterpret_cast<const f32x4 *>(kg + row * p.ks + h * DK + col);
-                qv = *reinterpret_cast<const f32x4 *>(qg + row * p.qs + h * DK + col);
+                pk[it] = *reinterpret_cast<const f32x4 *>(kg + row * p.ks + h * DK + col);
+                pq[it] = *reinterpret_cast<const f32x4 *>(qg + row * p.qs + h * DK + col);
             }
-            *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = kv;
-            *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = qv;
         }
         if (tid < C * VVR) {
             const int r = tid / VVR, col = (tid % VVR) * EPV;
             const int64_t t = c0 + r;
-            Tin tmp[EPV];
-            if (t < T) {
-                *reinterpret_cast<f32x4 *>(tmp) =
-                    *reinterpret_cast<const f32x4 *>(vg + (b * T + t) * p.vs + h * Dv + n0 + col);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) tmp[e] = from_f32<Tin>(0.f);
-            }
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) Vs[r * BV + col + e] = to_f32(tmp[e]);
+            pv = zero4();
+            if (t < T) pv = *reinterpret_cast<const f32x4 *>(vg + (b * T + t) * p.vs + h * Dv + n0 + col);
         }
         if (tid < C) {
             const int64_t t = c0 + tid;
             const bool ok = t < T;
-            Al[tid] = ok ? p.alpha[(b * T + t) * H + h] : 1.f;
-            Be[tid] = ok ? p.beta[(b * T + t) * H + h] : 0.f;
+            pal = ok ? p.alpha[(b * T + t) * H + h] : 1.f;
+            pbe = ok ? p.beta[(b * T + t) * H + h] : 0.f;
         }
-        __syncthreads();
+    };
+    prefetch(0);
 
-        // ---------------- log-decay prefix (wavefront 0) ----------------
+    // Gram tile table: tiles (rb, cb) with cb <= rb, K-part then Q-part.
+    constexpr int NTRI = NB * (NB + 1) / 2;
+    constexpr int NGT = (2 * NTRI + 3) / 4;      // Gram tiles per wavefront (upper bound)
+
+    for (int64_t c0 = 0; c0 < T; c0 += C) {
+        // ---------------- 1. stage the chunk (from registers), prefetch the next ----------------
+#pragma unroll
+        for (int it = 0; it < NKV; ++it) {
+            const int vi = tid + NTHREADS * it;
+            if (vi < C * VPR) {
+                const int r = vi / VPR, col = (vi % VPR) * EPV;
+                *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = pk[it];
+                *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = pq[it];
+            }
+        }
+        if (tid < C * VVR) {
+            const int r = tid / VVR, col = (tid % VVR) * EPV;
+            const Tin *tv = reinterpret_cast<const Tin *>(&pv);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) Vs[r * BV + col + e] = to_f32(tv[e]);
+        }
+        // log2-decay prefix: wavefront 0 scans it (lane = token) and publishes it
+        // before the staging barrier.
+        float g2 = 0.f, be_t = 0.f;
+        if (tid < C) { g2 = __builtin_amdgcn_logf(pal); be_t = pbe; }
         if (wave == 0) {
-            float g = lane < C ? logf(Al[lane]) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const float t = __shfl_up(g, off);
-                if (lane >= off) g += t;
+                const float t = __shfl_up(g2, off);
+                if (lane >= off) g2 += t;
             }
             if (lane < C) {
-                Gs[lane] = g;
-                EG[lane] = expf(g);
+                Gs[lane] = g2;                          // log2 of the cumulative decay
+                EG[lane] = __builtin_amdgcn_exp2f(g2);
+                Be[lane] = be_t;
             }
         }
+        if (c0 + C < T) prefetch(c0 + C);
         __syncthreads();
         const float GC = Gs[C - 1];
 
         // ---------------- 2. Gram tiles: K K^T -> A, Q K^T -> P ----------------
-        constexpr int NTRI = NB * (NB + 1) / 2;
-        for (int tile = wave; tile < 2 * NTRI; tile += 4) {
-            const bool isQ = tile >= NTRI;
-            int idx = isQ ? tile - NTRI : tile;
-            int rb = 0;
-            while (idx > rb) { idx -= rb + 1; ++rb; }
-            const int cb = idx;
-            const OpT *Asrc = isQ ? Qs : Ks;
-            f32x4 acc = zero4();
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += KS_DK) {
-                const FragDK a = frag_rows<OpT, KS_DK>(Asrc, KP, 16 * rb, k0, lane);
-                const FragDK bb = frag_rows<OpT, KS_DK>(Ks, KP, 16 * cb, k0, lane);
-                acc = FragDK::mma(a, bb, acc);
-            }
-            const int j = 16 * cb + ln;
-            const float Gj = Gs[j];
+        for (int it = 0; it < NGT; ++it) {
+            const int tile = wave + 4 * it;
+            if (tile < 2 * NTRI) {
+                const bool isQ = tile >= NTRI;
+                const int idx = isQ ? tile - NTRI : tile;
+                // row-major enumeration of the lower triangle of NB x NB blocks
+                const int rb = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+                const int cb = idx - rb * (rb + 1) / 2;
+                const OpT *Asrc = isQ ? Qs : Ks;
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * lg + e;
-                const float gam = expf(fminf(Gs[r] - Gj, 0.f));
-                if (isQ) {
-                    const float pv = r >= j ? gam * acc[e] : 0.f;
-                    const OpT hi = from_f32<OpT>(pv);
-                    Ps[r * CP + j] = hi;
-                    if constexpr (SPLIT) Plo[r * CP + j] = from_f32<OpT>(pv - to_f32(hi));
-                } else {
-                    const float val = r > j ? Be[r] * gam * acc[e] : 0.f;
-                    if (rb == cb) Af[r * AFP + j] = val;
-                    else An[r * CP + j] = from_f32<OpT>(-val);
+                for (int k0 = 0; k0 < DK; k0 += KS_DK) {
+                    const FragDK a = frag_rows<OpT, KS_DK>(Asrc, KP, 16 * rb, k0, lane);
+                    const FragDK bb = frag_rows<OpT, KS_DK>(Ks, KP, 16 * cb, k0, lane);
+                    acc = FragDK::mma(a, bb, acc);
+                }
+                const int j = 16 * cb + ln;
+                const float Gj = Gs[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gj, 0.f));
+                    if (isQ) {
+                        const float pvv = r >= j ? gam * acc[e] : 0.f;
+                        const OpT hi = from_f32<OpT>(pvv);
+                        Ps[r * CP + j] = hi;
+                        if constexpr (SPLIT) Plo[r * CP + j] = from_f32<OpT>(pvv - to_f32(hi));
+                    } else {
+                        const float val = r > j ? Be[r] * gam * acc[e] : 0.f;
+                        if (rb == cb) Af[r * AFP + j] = val;
+                        else An[r * CP + j] = from_f32<OpT>(-val);
+                    }
                 }
             }
         }
@@ -358,7 +382,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
                     const OpT hi = from_f32<OpT>(u[e]);
                     Uh[i].set_raw(e, hi);
                     UT[ln * CP + r] = hi;
-                    const float ud = expf(GC - Gs[r]) * u[e];
+                    const float ud = __builtin_amdgcn_exp2f(GC - Gs[r]) * u[e];
                     const OpT dhi = from_f32<OpT>(ud);
                     UdT[ln * CP + r] = dhi;
                     if constexpr (SPLIT) {
@@ -397,7 +421,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
         }
 
         // ---------------- 5b. S <- e^{G_C} S + K^T (e^{G_C-G} U) ----------------
-        const float eGC = expf(GC);
+        const float eGC = __builtin_amdgcn_exp2f(GC);
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int ib = wave + 4 * m;
