@@ -70,15 +70,19 @@ PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill.hip",
                    "linear_attention_token_gated_amd/csrc/common.hpp"]
 
 
-def measured_traffic():
-    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+DECODE_SOURCES = ["linear_attention_token_gated_amd/csrc/decode.hip"]
+
+
+def measured_traffic(key="prefill_32k", sources=PREFILL_SOURCES):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by its reading for a copy of known
+    size), if they were taken on the current kernel source; else None."""
     try:
         with open(PROFILE_TRAFFIC) as f:
-            t = json.load(f)["prefill_32k"]
+            t = json.load(f)[key]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(PREFILL_SOURCES):
+    if t.get("source_sha") != source_sha(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -173,8 +177,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-layer", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="for hardware-counter passes: two prefill launches, two decode steps and a "
+                         "1 GiB device copy of known size (the copy calibrates FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -186,6 +193,18 @@ def main():
 
     gdn.lib()
     props = torch.cuda.get_device_properties(0)
+
+    if args.pmc_run:
+        pargs = argparse.Namespace(steps=1, warmup=1)
+        bench_prefill(pargs, torch, gdn, wl)
+        bench_decode(pargs, torch, gdn, wl)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_run": "done", "copy_bytes_read": src.numel() * 4,
+                          "copy_bytes_written": dst.numel() * 4}))
+        return
 
     cfg, inp, p_total, p_per = bench_prefill(args, torch, gdn, wl)
     alg_bytes, alg_flops = prefill_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
@@ -245,7 +264,8 @@ def main():
                    "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
                    "state_GBps": d_state / (d_ms * 1e-3) / 1e9,
                    "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                   "alg_bytes_per_launch": d_bytes},
+                   "alg_bytes_per_launch": d_bytes,
+                   "traffic": measured_traffic("decode_256x32", DECODE_SOURCES)},
         "layer": layer,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
