@@ -24,6 +24,21 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // float -> bf16 conversion is round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// Split four floats into bf16 pairs hi = bf16(x), lo = bf16(x - hi), both
+// round-to-nearest-even.  Two packed conversions give hi; the widened hi is
+// rebuilt from the packed word by a shift (low half) and a mask (high half).
+__device__ __forceinline__ void split4(const f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    const bf16x2 h01 = __builtin_convertvector((f32x2{x[0], x[1]}), bf16x2);
+    const bf16x2 h23 = __builtin_convertvector((f32x2{x[2], x[3]}), bf16x2);
+    const uint32_t u01 = __builtin_bit_cast(uint32_t, h01), u23 = __builtin_bit_cast(uint32_t, h23);
+    const f32x2 r01 = f32x2{x[0] - __uint_as_float(u01 << 16), x[1] - __uint_as_float(u01 & 0xffff0000u)};
+    const f32x2 r23 = f32x2{x[2] - __uint_as_float(u23 << 16), x[3] - __uint_as_float(u23 & 0xffff0000u)};
+    const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
+    const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
+    hi = bf16x4{h01[0], h01[1], h23[0], h23[1]};
+    lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
+}
+
 // ---------------------------------------------------------------------------
 // 16x16 MFMA tiles.
 //

@@ -1101,13 +1101,7 @@ __device__ __forceinline__ void gram_pair(char *nb, float *Ad, float *Ao, const 
             if (isP) {
                 const int idx = rb * (rb + 1) / 2 + cbk;
                 bf16x4 hv, lv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(val[e], hi, lo);
-                    hv[e] = hi;
-                    lv[e] = lo;
-                }
+                split4(val, hv, lv);
                 *reinterpret_cast<bf16x4 *>(Ph + idx * BLK + ln * PB + 4 * lg) = hv;
                 *reinterpret_cast<bf16x4 *>(Pl + idx * BLK + ln * PB + 4 * lg) = lv;
             } else {
@@ -1187,13 +1181,7 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                 const int ib = sw + 4 * m;
                 if (ib < NSB) {
                     bf16x4 hv, lv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        __bf16 hi, lo;
-                        split_bf16(S[m][e], hi, lo);
-                        hv[e] = hi;
-                        lv[e] = lo;
-                    }
+                    split4(S[m], hv, lv);
                     *reinterpret_cast<bf16x4 *>(STh + ln * KP + 16 * ib + 4 * lg) = hv;
                     *reinterpret_cast<bf16x4 *>(STl + ln * KP + 16 * ib + 4 * lg) = lv;
                 }
@@ -1238,15 +1226,13 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                     ks_l = FDK::mma(kf[kk], slo[kk], ks_l);
                 }
                 F16 rh, rl;
+                f32x4 rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
-                    const float rv = Be[r] * ((float)Vs[r * BV + ln] - EG[r] * (ks_h[e] + ks_l[e]));
-                    __bf16 hi, lo;
-                    split_bf16(rv, hi, lo);
-                    rh.set_raw(e, hi);
-                    rl.set_raw(e, lo);
+                    rv[e] = Be[r] * ((float)Vs[r * BV + ln] - EG[r] * (ks_h[e] + ks_l[e]));
                 }
+                split4(rv, rh.v, rl.v);
                 f32x4 w = F16::mma(tf, rh, zero4());
                 w = F16::mma(tf, rl, w);
                 *reinterpret_cast<f32x4 *>(Wx + (rb * 64 + lane) * 4) = w;
@@ -1270,17 +1256,9 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                         const f32x4 ed = *reinterpret_cast<const f32x4 *>(Ed + r0);
                         F16 uh, ul;
                         bf16x4 dh, dl;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float u = acc[k][e] + acc2[k][e];
-                            __bf16 hi, lo, dhi, dlo;
-                            split_bf16(u, hi, lo);
-                            split_bf16(ed[e] * u, dhi, dlo);
-                            uh.set_raw(e, hi);
-                            ul.set_raw(e, lo);
-                            dh[e] = dhi;
-                            dl[e] = dlo;
-                        }
+                        const f32x4 u = acc[k] + acc2[k];
+                        split4(u, uh.v, ul.v);
+                        split4(ed * u, dh, dl);
 #pragma unroll
                         for (int i = k + 1; i < NB; ++i) {
                             const F16 a = frag_rows<__bf16, 16>(Nn + (i * (i - 1) / 2 + k) * BLK, PB, 0, 0, lane);
@@ -1473,25 +1451,16 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                 // lane (row ln, group lg) holds T_ii[ln][lg + 4e]: that k-set is the
                 // MFMA k order for N_ik = T_ii A_ik (the B operand is gathered to match)
                 F16 th, tl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(X[e], hi, lo);
-                    th.set_raw(e, hi);
-                    tl.set_raw(e, lo);
-                }
+                split4(f32x4{X[0], X[1], X[2], X[3]}, th.v, tl.v);
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
                     if (k < i) {
                         const int oidx = i * (i - 1) / 2 + k;
                         F16 ah, al;
+                        f32x4 av;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            __bf16 hi, lo;
-                            split_bf16(Ao[(oidx * 16 + lg + 4 * e) * AP + ln], hi, lo);
-                            ah.set_raw(e, hi);
-                            al.set_raw(e, lo);
-                        }
+                        for (int e = 0; e < 4; ++e) av[e] = Ao[(oidx * 16 + lg + 4 * e) * AP + ln];
+                        split4(av, ah.v, al.v);
                         f32x4 n = F16::mma(th, ah, zero4());
                         n = F16::mma(th, al, n);
                         n = F16::mma(tl, ah, n);
