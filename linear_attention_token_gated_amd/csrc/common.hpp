@@ -122,8 +122,10 @@ __device__ __forceinline__ Frag<OpT, KS> frag_cols(const OpT *base, int pitch, i
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Broadcast lane S of every 16-lane row to the whole row (DPP row_newbcast).
+// Every lane has a valid source, so no old value is needed (bound_ctrl set):
+// the move then carries no extra copy and no wait state of its own.
 template <int S> __device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + S, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + S, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -461,26 +461,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
 }
 
 // ===========================================================================
-// Pipelined kernel for bf16 inputs: 8 wavefronts per workgroup.
+// LDS layout of the bf16 kernel: two chunk buffers (the chunk whose state
+// recurrence runs now, and the next chunk being staged and prepared) plus the
+// arrays that live for one chunk only.  Packed 16x16 blocks (P, the diagonal
+// inverses T_ii, the off-diagonal products N_ik) use a padded row pitch PB.
 //
-//   state waves (0-3) work on chunk c:      prep waves (4-7) prepare chunk c+1:
-//   phase 1  K S, Q S -> R, W_i = T_ii R_i   stage K, Q, V, decay prefix; prefetch c+2
-//   phase 2  block chain U_i = W_i - sum N_ik U_k (wave 0)   Gram tiles -> A, P
-//   phase 3  Y = e^G Q S + P U; S update     diagonal inverses T_ii, N_ik = T_ii A_ik
-//
-// with (I + A)^-1 R computed block-wise: U_i = T_ii R_i - sum_{k<i} N_ik U_k,
-// T_ii = (I + A_ii)^-1, N_ik = T_ii A_ik (both independent of the state, so
-// they are built one chunk ahead).  Every array the state waves read for chunk
-// c lives in chunk buffer c % 2; the prep waves fill the other one.  All eight
-// wavefronts meet at the three barriers of each iteration.
+// Bank behaviour of gfx950 LDS, as measured with SQ_LDS_BANK_CONFLICT for a
+// lane (ln = l % 16, lg = l / 16) reading or writing row ln at a column set by
+// lg, with a row pitch of R dwords:
+//   128-bit reads   conflict-free for R = 8 mod 16      (64 banks, 16 lanes/cycle)
+//   64-bit reads    conflict-free for R = 4 mod 8       (64 banks, 32 lanes/cycle)
+//   128-bit writes  conflict-free for R = 4 mod 8       (32 banks,  8 lanes/cycle)
+//   64-bit writes   conflict-free for R = 2 mod 4       (32 banks, 16 lanes/cycle)
+// Rows read as MFMA fragments (K, Q, S^T, e^{G_C-G} U^T) take the read pitch
+// (frag_pitch).  U^T and the packed blocks are written by 64-bit stores on the
+// U chain and in the Gram epilogues; their pitches (C + 4, PB = 20 bf16) keep
+// those stores conflict-free at the price of a 2-way conflict on their reads.
 // ===========================================================================
-constexpr int PIPE_THREADS = 512;
-constexpr int PB = 24;                 // pitch of a packed 16x16 bf16 block (16 + 8 pad)
+template <int KS> constexpr int frag_pitch(int n) {
+    int r = n / 2;                                    // dwords
+    const int m = KS == 32 ? 16 : 8, want = KS == 32 ? 8 : 4;
+    while (r % m != want) ++r;
+    return 2 * r;
+}
+
+constexpr int PB = 20;                 // pitch of a packed 16x16 bf16 block (16 + 4 pad)
 constexpr int BLK = 16 * PB;           // elements per packed block
 
 template <int C, int DK> struct PipeLay {
-    static constexpr int KP = DK + 8;                 // K/Q row pitch (bf16)
-    static constexpr int CP = C + 8;                  // U^T row pitch (bf16)
     static constexpr int NB = C / 16;
     static constexpr int NSB = DK / 16;
     static constexpr int MS = (NSB + 3) / 4;
@@ -488,6 +496,9 @@ template <int C, int DK> struct PipeLay {
     static constexpr int NOFF = NB * (NB - 1) / 2;    // strictly lower blocks
     static constexpr int KS_DK = DK % 32 == 0 ? 32 : 16;
     static constexpr int KS_C = C % 32 == 0 ? 32 : 16;
+    static constexpr int KP = frag_pitch<KS_DK>(DK);  // K, Q, S^T row pitch (bf16)
+    static constexpr int CPU = C + 4;                 // U^T row pitch (bf16)
+    static constexpr int CPD = frag_pitch<KS_C>(C);   // e^{G_C-G} U^T row pitch (bf16)
     // one chunk buffer
     static constexpr size_t cK = 0;
     static constexpr size_t cQ = cK + align16(2 * C * KP);
@@ -511,482 +522,57 @@ template <int C, int DK> struct PipeLay {
     static constexpr size_t oSTl = oSTh + align16(2 * BV * KP);
     static constexpr size_t oW = oSTl + align16(2 * BV * KP);        // fp32 W_i exchange [NB][64 lanes][4]
     static constexpr size_t oUh = oW + align16(4 * C * BV);
-    static constexpr size_t oUl = oUh + align16(2 * BV * CP);
-    static constexpr size_t oUdh = oUl + align16(2 * BV * CP);
-    static constexpr size_t oUdl = oUdh + align16(2 * BV * CP);
-    static constexpr size_t BYTES = oUdl + align16(2 * BV * CP);
+    static constexpr size_t oUl = oUh + align16(2 * BV * CPU);
+    static constexpr size_t oUdh = oUl + align16(2 * BV * CPU);
+    static constexpr size_t oUdl = oUdh + align16(2 * BV * CPD);
+    static constexpr size_t BYTES = oUdl + align16(2 * BV * CPD);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo)
-{
-    hi = (__bf16)x;
-    lo = (__bf16)(x - (float)hi);
+// Token order of the decayed U^T rows used by the state update.  Within each
+// k-step of KS tokens, lane group g (KS/4 values per lane) takes the tokens
+// 2g + 8(e/2) + (e%2), e = 0..KS/4-1: adjacent pairs, 8 tokens apart.  With
+// the K row pitch of 4 banks mod 32, the four lane groups then gather K
+// columns from rows 2 apart -- 8 banks apart, so the column gather is free of
+// bank conflicts.  ud_pos gives the storage position of token t; the B operand
+// (e^{G_C-G} U^T) is then an ordinary contiguous fragment read.
+template <int KS> __device__ __forceinline__ int ud_pos(int t) {
+    constexpr int E = KS / 4;
+    const int u = t % KS;
+    return (t - u) + ((u & 7) >> 1) * E + (u >> 3) * 2 + (u & 1);
 }
 
-// Gram tiles of one chunk, tiles first, first + stride, ... of the row-major
-// lower-triangle order of NB x NB blocks, two at a time.  Each tile is computed
-// transposed, D = K_cb X_rb^T, so lane (ln, lg) holds row r = 16 rb + ln and
-// columns j = 16 cb + 4 lg + e: four contiguous entries of one row.
-//   IS_P = false: A = strict_lower[beta_r Gamma_rj k_r.k_j] -> fp32 blocks Ad / Ao
-//   IS_P = true:  P = lower_incl[Gamma_rj q_r.k_j] -> bf16 hi + lo blocks Ph / Pl
-template <bool IS_P, int C, int DK>
-__device__ __forceinline__ void gram_tiles(char *nb, float *Ad, float *Ao, int first, int stride, int lane)
-{
-    using L = PipeLay<C, DK>;
-    constexpr int KP = L::KP, NTRI = L::NTRI, AP = L::AP, KS_DK = L::KS_DK, NK = DK / KS_DK;
-    using FDK = Frag<__bf16, KS_DK>;
-    const int ln = lane & 15, lg = lane >> 4;
-    const __bf16 *Ks = reinterpret_cast<const __bf16 *>(nb + L::cK);
-    const __bf16 *Xs = reinterpret_cast<const __bf16 *>(nb + (IS_P ? L::cQ : L::cK));
-    const float *G = reinterpret_cast<const float *>(nb + L::cG);
-    const float *Be = reinterpret_cast<const float *>(nb + L::cBe);
-    __bf16 *Ph = reinterpret_cast<__bf16 *>(nb + L::cPh);
-    __bf16 *Pl = reinterpret_cast<__bf16 *>(nb + L::cPl);
-    for (int t0 = first; t0 < NTRI; t0 += 2 * stride) {
-        const int tt[2] = {t0, t0 + stride};
-        FDK fa[2][NK], fb[2][NK];
+// A operand K^T[r0 + ln][tokens of ud_pos order] of one k-step at k0.
+template <int KS>
+__device__ __forceinline__ Frag<__bf16, KS> k_cols_paired(const __bf16 *Ks, int pitch, int r0, int k0, int lane) {
+    Frag<__bf16, KS> f;
+    const __bf16 *p = Ks + (k0 + 2 * (lane >> 4)) * pitch + r0 + (lane & 15);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int idx = tt[u];
-            if (idx < NTRI) {
-                const int rb = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
-                const int cbk = idx - rb * (rb + 1) / 2;
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    fa[u][kk] = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * cbk, kk * KS_DK, lane);
-                    fb[u][kk] = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * rb, kk * KS_DK, lane);
-                }
-            }
-        }
-        f32x4 acc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            acc[u] = zero4();
-            if (tt[u] < NTRI) {
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) acc[u] = FDK::mma(fa[u][kk], fb[u][kk], acc[u]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int idx = tt[u];
-            if (idx < NTRI) {
-                const int rb = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
-                const int cbk = idx - rb * (rb + 1) / 2;
-                const int r = 16 * rb + ln;
-                const int j0 = 16 * cbk + 4 * lg;
-                const float Gr = G[r];
-                const f32x4 Gj = *reinterpret_cast<const f32x4 *>(G + j0);
-                f32x4 val;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gam = __builtin_amdgcn_exp2f(fminf(Gr - Gj[e], 0.f));
-                    const float keep = (r > j0 + e || (IS_P && r == j0 + e)) ? 1.f : 0.f;
-                    val[e] = gam * acc[u][e] * keep;
-                }
-                if constexpr (IS_P) {
-                    bf16x4 hv, lv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        __bf16 hi, lo;
-                        split_bf16(val[e], hi, lo);
-                        hv[e] = hi;
-                        lv[e] = lo;
-                    }
-                    *reinterpret_cast<bf16x4 *>(Ph + idx * BLK + ln * PB + 4 * lg) = hv;
-                    *reinterpret_cast<bf16x4 *>(Pl + idx * BLK + ln * PB + 4 * lg) = lv;
-                } else {
-                    val *= Be[r];
-                    float *dst = rb == cbk ? Ad + (rb * 16 + ln) * AP
-                                           : Ao + ((rb * (rb - 1) / 2 + cbk) * 16 + ln) * AP;
-                    *reinterpret_cast<f32x4 *>(dst + 4 * lg) = val;
-                }
-            }
-        }
-    }
+    for (int e = 0; e < KS / 4; ++e) f.set_raw(e, p[(8 * (e >> 1) + (e & 1)) * pitch]);
+    return f;
 }
 
-template <int C, int DK>
-__global__ __launch_bounds__(PIPE_THREADS, 1) void gdn_prefill_pipe_kernel(KParams p)
-{
-    using L = PipeLay<C, DK>;
-    using F16 = Frag<__bf16, 16>;
-    using FDK = Frag<__bf16, L::KS_DK>;
-    using FC = Frag<__bf16, L::KS_C>;
-    constexpr int KP = L::KP, CP = L::CP, NB = L::NB, NSB = L::NSB, MS = L::MS, AP = L::AP;
-    constexpr int KS_DK = L::KS_DK, KS_C = L::KS_C;
+// Value of v in lane l (l wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-    auto cbuf = [&](int parity) { return smem + parity * L::CBUF; };
-    float *Ad = reinterpret_cast<float *>(smem + L::oAd);
-    float *Ao = reinterpret_cast<float *>(smem + L::oAo);
-    __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
-    __bf16 *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
-    float *Wx = reinterpret_cast<float *>(smem + L::oW);
-    __bf16 *UTh = reinterpret_cast<__bf16 *>(smem + L::oUh);
-    __bf16 *UTl = reinterpret_cast<__bf16 *>(smem + L::oUl);
-    __bf16 *UdTh = reinterpret_cast<__bf16 *>(smem + L::oUdh);
-    __bf16 *UdTl = reinterpret_cast<__bf16 *>(smem + L::oUdl);
+// v from N lanes lower in the same 16-lane row; lanes with no such source read 0.
+template <int N> __device__ __forceinline__ float row_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, false));
+}
 
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(wave_id());   // wave-uniform
-    const int ln = lane & 15, lg = lane >> 4;
-    const bool is_state = wave < 4;
-    const int sw = wave;          // state wave index (0-3)
-    const int pw = wave - 4;      // prep wave index (0-3)
-    const int ptid = tid - 256;   // prep thread index (0-255)
-
-    const int64_t bid = blockIdx.x;
-    int64_t bh, sl;
-    if (p.xcd_map) {
-        const int64_t xcd = bid & 7, local = bid >> 3;
-        bh = (local / p.nslices) * 8 + xcd;
-        sl = local % p.nslices;
-    } else {
-        bh = bid / p.nslices;
-        sl = bid % p.nslices;
-    }
-    const int64_t H = p.H, T = p.T, Dv = p.Dv;
-    const int64_t b = bh / H, h = bh % H;
-    const int n0 = (int)sl * BV;
-    const __bf16 *qg = static_cast<const __bf16 *>(p.q);
-    const __bf16 *kg = static_cast<const __bf16 *>(p.k);
-    const __bf16 *vg = static_cast<const __bf16 *>(p.v);
-    const int64_t NC = (T + C - 1) / C;
-
-    if (is_state) {
-        // ===================== state waves: chunk it =====================
-        // wave w owns the 16-row blocks ib = w + 4m of the state slice
-        f32x4 S[MS];
-#pragma unroll
-        for (int m = 0; m < MS; ++m) S[m] = zero4();
-        auto write_state_operand = [&]() {
-#pragma unroll
-            for (int m = 0; m < MS; ++m) {
-                const int ib = sw + 4 * m;
-                if (ib < NSB) {
-                    bf16x4 hv, lv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        __bf16 hi, lo;
-                        split_bf16(S[m][e], hi, lo);
-                        hv[e] = hi;
-                        lv[e] = lo;
-                    }
-                    *reinterpret_cast<bf16x4 *>(STh + ln * KP + 16 * ib + 4 * lg) = hv;
-                    *reinterpret_cast<bf16x4 *>(STl + ln * KP + 16 * ib + 4 * lg) = lv;
-                }
-            }
-        };
-        if (p.s0) {
-            const float *s0 = p.s0 + bh * (int64_t)DK * Dv;
-#pragma unroll
-            for (int m = 0; m < MS; ++m) {
-                const int ib = sw + 4 * m;
-                if (ib < NSB) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) S[m][e] = s0[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln];
-                }
-            }
-        }
-        write_state_operand();
-
-        f32x4 qs_acc = zero4();   // Q S of this wave's row block, phase 1 -> phase 3
-        for (int64_t it = -1; it < NC; ++it) {
-            const bool act = it >= 0;
-            const char *cb = cbuf((int)(it & 1));
-            const __bf16 *Ks = reinterpret_cast<const __bf16 *>(cb + L::cK);
-            const float *EG = reinterpret_cast<const float *>(cb + L::cEG);
-
-            // ---- phase 1: K S, Q S -> R;  W_i = T_ii R_i
-            if (act && sw < NB) {
-                const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
-                const __bf16 *Vs = reinterpret_cast<const __bf16 *>(cb + L::cV);
-                const float *Be = reinterpret_cast<const float *>(cb + L::cBe);
-                const __bf16 *Td = reinterpret_cast<const __bf16 *>(cb + L::cTd);
-                const int rb = sw;
-                constexpr int NK = DK / KS_DK;
-                FDK kf[NK], qf[NK], sh[NK], slo[NK];
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    kf[kk] = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * rb, kk * KS_DK, lane);
-                    qf[kk] = frag_rows<__bf16, KS_DK>(Qs, KP, 16 * rb, kk * KS_DK, lane);
-                    sh[kk] = frag_rows<__bf16, KS_DK>(STh, KP, 0, kk * KS_DK, lane);
-                    slo[kk] = frag_rows<__bf16, KS_DK>(STl, KP, 0, kk * KS_DK, lane);
-                }
-                f32x4 ks_h = zero4(), ks_l = zero4(), qs_h = zero4(), qs_l = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    ks_h = FDK::mma(kf[kk], sh[kk], ks_h);
-                    qs_h = FDK::mma(qf[kk], sh[kk], qs_h);
-                    ks_l = FDK::mma(kf[kk], slo[kk], ks_l);
-                    qs_l = FDK::mma(qf[kk], slo[kk], qs_l);
-                }
-                qs_acc = qs_h + qs_l;
-                F16 rh, rl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    const float rv = Be[r] * ((float)Vs[r * BV + ln] - EG[r] * (ks_h[e] + ks_l[e]));
-                    __bf16 hi, lo;
-                    split_bf16(rv, hi, lo);
-                    rh.set_raw(e, hi);
-                    rl.set_raw(e, lo);
-                }
-                const F16 tf = frag_rows<__bf16, 16>(Td + rb * BLK, PB, 0, 0, lane);
-                f32x4 w = F16::mma(tf, rh, zero4());
-                w = F16::mma(tf, rl, w);
-                *reinterpret_cast<f32x4 *>(Wx + (rb * 64 + lane) * 4) = w;
-            }
-            __syncthreads();
-
-            // ---- phase 2: U_i = W_i + sum_k (-N_ik) U_k  (wavefront 0, right-looking);
-            //      waves 1-3 build P of the next chunk meanwhile
-            if (act && sw == 0) {
-                const __bf16 *Nn = reinterpret_cast<const __bf16 *>(cb + L::cNn);
-                const float *Ed = reinterpret_cast<const float *>(cb + L::cEd);
-                f32x4 acc[NB], acc2[NB];
-#pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    acc[i] = *reinterpret_cast<const f32x4 *>(Wx + (i * 64 + lane) * 4);
-                    acc2[i] = zero4();
-                }
-#pragma unroll
-                for (int k = 0; k < NB; ++k) {
-                    const int r0 = 16 * k + 4 * lg;
-                    const f32x4 ed = *reinterpret_cast<const f32x4 *>(Ed + r0);
-                    F16 uh, ul;
-                    bf16x4 dh, dl;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float u = acc[k][e] + acc2[k][e];
-                        __bf16 hi, lo, dhi, dlo;
-                        split_bf16(u, hi, lo);
-                        split_bf16(ed[e] * u, dhi, dlo);
-                        uh.set_raw(e, hi);
-                        ul.set_raw(e, lo);
-                        dh[e] = dhi;
-                        dl[e] = dlo;
-                    }
-#pragma unroll
-                    for (int i = k + 1; i < NB; ++i) {
-                        const F16 a = frag_rows<__bf16, 16>(Nn + (i * (i - 1) / 2 + k) * BLK, PB, 0, 0, lane);
-                        acc[i] = F16::mma(a, uh, acc[i]);
-                        acc2[i] = F16::mma(a, ul, acc2[i]);
-                    }
-                    *reinterpret_cast<bf16x4 *>(UTh + ln * CP + r0) = uh.v;
-                    *reinterpret_cast<bf16x4 *>(UTl + ln * CP + r0) = ul.v;
-                    *reinterpret_cast<bf16x4 *>(UdTh + ln * CP + r0) = dh;
-                    *reinterpret_cast<bf16x4 *>(UdTl + ln * CP + r0) = dl;
-                }
-            } else if (sw > 0 && it + 1 < NC) {
-                gram_tiles<true, C, DK>(cbuf((int)((it + 1) & 1)), Ad, Ao, sw - 1, 3, lane);
-            }
-            __syncthreads();
-
-            // ---- phase 3: Y = e^G Q S + P U;  S <- e^{G_C} S + K^T (e^{G_C-G} U)
-            if (act) {
-                const __bf16 *Ph = reinterpret_cast<const __bf16 *>(cb + L::cPh);
-                const __bf16 *Pl = reinterpret_cast<const __bf16 *>(cb + L::cPl);
-                const float EGC = EG[C - 1];
-                const int64_t c0 = it * C;
-                if (sw < NB) {
-                    const int rb = sw;
-                    f32x4 acc, acc2 = zero4();
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = EG[16 * rb + 4 * lg + e] * qs_acc[e];
-#pragma unroll
-                    for (int jb = 0; jb < NB; ++jb) {
-                        if (jb <= rb) {
-                            const int pidx = rb * (rb + 1) / 2 + jb;
-                            const F16 ah = frag_rows<__bf16, 16>(Ph + pidx * BLK, PB, 0, 0, lane);
-                            const F16 al = frag_rows<__bf16, 16>(Pl + pidx * BLK, PB, 0, 0, lane);
-                            const F16 uh = frag_rows<__bf16, 16>(UTh, CP, 0, 16 * jb, lane);
-                            const F16 ul = frag_rows<__bf16, 16>(UTl, CP, 0, 16 * jb, lane);
-                            acc = F16::mma(ah, uh, acc);
-                            acc2 = F16::mma(al, uh, acc2);
-                            acc2 = F16::mma(ah, ul, acc2);
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t t = c0 + 16 * rb + 4 * lg + e;
-                        if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e] + acc2[e];
-                    }
-                }
-                constexpr int NJ = C / KS_C;
-                FC uh[NJ], ul[NJ], ka[MS][NJ];
-#pragma unroll
-                for (int jj = 0; jj < NJ; ++jj) {
-                    uh[jj] = frag_rows<__bf16, KS_C>(UdTh, CP, 0, jj * KS_C, lane);
-                    ul[jj] = frag_rows<__bf16, KS_C>(UdTl, CP, 0, jj * KS_C, lane);
-                }
-#pragma unroll
-                for (int m = 0; m < MS; ++m) {
-                    const int ib = sw + 4 * m;
-                    if (ib < NSB) {
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = frag_cols<__bf16, KS_C>(Ks, KP, 16 * ib, jj * KS_C, lane);
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < MS; ++m) {
-                    const int ib = sw + 4 * m;
-                    if (ib < NSB) {
-                        f32x4 acc = S[m] * EGC, acc2 = zero4();
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) {
-                            acc = FC::mma(ka[m][jj], uh[jj], acc);
-                            acc2 = FC::mma(ka[m][jj], ul[jj], acc2);
-                        }
-                        S[m] = acc + acc2;
-                    }
-                }
-                write_state_operand();
-            }
-            __syncthreads();
-        }
-
-        if (p.sT) {
-            float *sT = p.sT + bh * (int64_t)DK * Dv;
-#pragma unroll
-            for (int m = 0; m < MS; ++m) {
-                const int ib = sw + 4 * m;
-                if (ib < NSB) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sT[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
-                }
-            }
-        }
-    } else {
-        // ===================== prep waves: chunk it + 1 =====================
-        constexpr int VPR = DK / 8;                         // 16-byte vectors per K/Q row
-        constexpr int NKV = (C * VPR + 255) / 256;          // per prep thread
-        f32x4 pk[NKV], pq[NKV], pv = zero4();
-        float pal = 1.f, pbe = 0.f;
-        auto prefetch = [&](int64_t c) {
-            const int64_t c0 = c * C;
-#pragma unroll
-            for (int i = 0; i < NKV; ++i) {
-                const int vi = ptid + 256 * i;
-                const int r = vi / VPR, col = (vi % VPR) * 8;
-                const int64_t t = c0 + r;
-                pk[i] = zero4();
-                pq[i] = zero4();
-                if (vi < C * VPR && t < T) {
-                    const int64_t row = b * T + t;
-                    pk[i] = *reinterpret_cast<const f32x4 *>(kg + row * p.ks + h * DK + col);
-                    pq[i] = *reinterpret_cast<const f32x4 *>(qg + row * p.qs + h * DK + col);
-                }
-            }
-            if (ptid < C * 2) {            // V slice: 16 bf16 = two 16-byte vectors per row
-                const int r = ptid >> 1, col = (ptid & 1) * 8;
-                const int64_t t = c0 + r;
-                pv = zero4();
-                if (t < T) pv = *reinterpret_cast<const f32x4 *>(vg + (b * T + t) * p.vs + h * Dv + n0 + col);
-            }
-            if (ptid < C) {
-                const int64_t t = c0 + ptid;
-                const bool ok = t < T;
-                pal = ok ? p.alpha[(b * T + t) * H + h] : 1.f;
-                pbe = ok ? p.beta[(b * T + t) * H + h] : 0.f;
-            }
-        };
-        prefetch(0);
-
-        for (int64_t it = -1; it < NC; ++it) {
-            const bool act = it + 1 < NC;
-            char *nb = cbuf((int)((it + 1) & 1));
-            __bf16 *Ks = reinterpret_cast<__bf16 *>(nb + L::cK);
-            __bf16 *Qs = reinterpret_cast<__bf16 *>(nb + L::cQ);
-
-            // ---- phase 1: stage K, Q, V of chunk it+1; log2-decay prefix
-            if (act) {
-                __bf16 *Vs = reinterpret_cast<__bf16 *>(nb + L::cV);
-#pragma unroll
-                for (int i = 0; i < NKV; ++i) {
-                    const int vi = ptid + 256 * i;
-                    if (vi < C * VPR) {
-                        const int r = vi / VPR, col = (vi % VPR) * 8;
-                        *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = pk[i];
-                        *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = pq[i];
-                    }
-                }
-                if (ptid < C * 2) *reinterpret_cast<f32x4 *>(Vs + (ptid >> 1) * BV + (ptid & 1) * 8) = pv;
-                if (pw == 0) {
-                    // inclusive prefix of log2 alpha over the chunk (lane = token)
-                    float g2 = lane < C ? __builtin_amdgcn_logf(pal) : 0.f;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float t = __shfl_up(g2, off);
-                        if (lane >= off) g2 += t;
-                    }
-                    const float gC = __shfl(g2, C - 1);
-                    if (lane < C) {
-                        reinterpret_cast<float *>(nb + L::cG)[lane] = g2;
-                        reinterpret_cast<float *>(nb + L::cEG)[lane] = __builtin_amdgcn_exp2f(g2);
-                        reinterpret_cast<float *>(nb + L::cBe)[lane] = pbe;
-                        reinterpret_cast<float *>(nb + L::cEd)[lane] = __builtin_amdgcn_exp2f(gC - g2);
-                    }
-                }
-            }
-            __syncthreads();
-
-            // ---- phase 2: Gram tiles of K K^T -> A (fp32 blocks); prefetch chunk it+2
-            if (act) gram_tiles<false, C, DK>(nb, Ad, Ao, pw, 4, lane);
-            if (it + 2 < NC) prefetch(it + 2);      // consumed by phase 1 of the next iteration
-            __syncthreads();
-
-            // ---- phase 3: T_ii and N_ik = T_ii A_ik
-            if (act && pw < NB) {
-                const int i = pw;
-                float Lr[16];
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const f32x4 v4 = *reinterpret_cast<const f32x4 *>(Ad + (i * 16 + ln) * AP + 4 * s4);
-                    Lr[4 * s4] = v4[0]; Lr[4 * s4 + 1] = v4[1]; Lr[4 * s4 + 2] = v4[2]; Lr[4 * s4 + 3] = v4[3];
-                }
-                float X[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) X[e] = (ln == lg + 4 * e) ? 1.f : 0.f;
-                tri_solve16(X, Lr, ln, std::make_integer_sequence<int, 15>{});
-                __bf16 *Td = reinterpret_cast<__bf16 *>(nb + L::cTd);
-                __bf16 *Nn = reinterpret_cast<__bf16 *>(nb + L::cNn);
-                // lane (row ln, group lg) holds T_ii[ln][lg + 4e]: that k-set is the
-                // MFMA k order for N_ik = T_ii A_ik (the B operand is gathered to match)
-                F16 th, tl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Td[i * BLK + ln * PB + lg + 4 * e] = (__bf16)X[e];
-                    __bf16 hi, lo;
-                    split_bf16(X[e], hi, lo);
-                    th.set_raw(e, hi);
-                    tl.set_raw(e, lo);
-                }
-#pragma unroll
-                for (int k = 0; k < NB; ++k) {
-                    if (k < i) {
-                        const int oidx = i * (i - 1) / 2 + k;
-                        F16 ah, al;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            __bf16 hi, lo;
-                            split_bf16(Ao[(oidx * 16 + lg + 4 * e) * AP + ln], hi, lo);
-                            ah.set_raw(e, hi);
-                            al.set_raw(e, lo);
-                        }
-                        f32x4 n = F16::mma(th, ah, zero4());
-                        n = F16::mma(th, al, n);
-                        n = F16::mma(tl, ah, n);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Nn[oidx * BLK + (4 * lg + e) * PB + ln] = (__bf16)(-n[e]);
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+// Inclusive prefix sum over the 64 lanes: a scan inside each 16-lane row by
+// DPP row shifts, then the totals of the earlier rows added from scalars.
+__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    const float t0 = lane_value(x, 15), t1 = lane_value(x, 31), t2 = lane_value(x, 47);
+    const int row = lane >> 4;
+    const float base = row == 0 ? 0.f : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+    return x + base;
 }
 
 // ===========================================================================
@@ -995,16 +581,18 @@ __global__ __launch_bounds__(PIPE_THREADS, 1) void gdn_prefill_pipe_kernel(KPara
 // Only the state recurrence itself sits on the per-chunk critical path; all
 // other work runs on other wavefronts in the same three phases:
 //
-//  waves    phase 1                      phase 2                     phase 3
-//  0        K S -> R -> W_0 = T_00 R_0   U chain (right-looking)     S update
-//  1-3      K S -> R -> W_i              Gram jobs (chunk c+1)       S update
-//  4-7      Q S (row block w-4)          Gram jobs (chunk c+1)       Y = e^G Q S + P U
-//  8-11     stage c+1; prefetch c+2      diagonal A_ii + T_ii        N_ik = T_ii A_ik
-//  12-15    stage c+1; prefetch c+2      Gram jobs (chunk c+1)       -
+//  waves    phase 1                       phase 2                    phase 3
+//  0        K S -> R -> W_0 = T_00 R_0    U chain (right-looking)    S update
+//  1-3      K S -> R -> W_i               Gram jobs (chunk c+1)      S update
+//  4-7      Q S (row block w-4)           Gram jobs (chunk c+1)      Y = e^G Q S + P U
+//  8-11     N_ik = T_ii A_ik of chunk c   diagonal A_ii (c+1)        T_ii (c+1)
+//           (9-11); stage c+1
+//  12-15    stage c+1; decay scan of      Gram jobs (chunk c+1)      -
+//           c+1 (12); prefetch c+2
 //
 // Gram jobs are the strictly-lower blocks of A = K K^T and the lower blocks
-// of P = Q K^T of chunk c+1, spread over eleven wavefronts.  The LDS layout
-// is the one of the 8-wave kernel (two chunk buffers).
+// of P = Q K^T of chunk c+1, spread over eleven wavefronts.  Staging copies
+// the K, Q and V rows that were loaded into registers one iteration earlier.
 // ===========================================================================
 constexpr int WIDE_THREADS = 1024;
 
@@ -1120,7 +708,7 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
     using F16 = Frag<__bf16, 16>;
     using FDK = Frag<__bf16, L::KS_DK>;
     using FC = Frag<__bf16, L::KS_C>;
-    constexpr int KP = L::KP, CP = L::CP, NB = L::NB, NSB = L::NSB, MS = L::MS, AP = L::AP;
+    constexpr int KP = L::KP, CPU = L::CPU, CPD = L::CPD, NB = L::NB, NSB = L::NSB, MS = L::MS, AP = L::AP;
     constexpr int KS_DK = L::KS_DK, KS_C = L::KS_C, NK = DK / KS_DK;
     constexpr int NJOB = L::NOFF + L::NTRI;     // Gram jobs per chunk
     constexpr int NWORK = 11;                   // wavefronts taking Gram jobs
@@ -1265,10 +853,15 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                             acc[i] = F16::mma(a, uh, acc[i]);
                             acc2[i] = F16::mma(a, ul, acc2[i]);
                         }
-                        *reinterpret_cast<bf16x4 *>(UTh + ln * CP + r0) = uh.v;
-                        *reinterpret_cast<bf16x4 *>(UTl + ln * CP + r0) = ul.v;
-                        *reinterpret_cast<bf16x4 *>(UdTh + ln * CP + r0) = dh;
-                        *reinterpret_cast<bf16x4 *>(UdTl + ln * CP + r0) = dl;
+                        *reinterpret_cast<bf16x4 *>(UTh + ln * CPU + r0) = uh.v;
+                        *reinterpret_cast<bf16x4 *>(UTl + ln * CPU + r0) = ul.v;
+                        // tokens (r0, r0 + 1) and (r0 + 2, r0 + 3) stay adjacent in the
+                        // permuted order of the decayed U^T
+                        const int pa = ln * CPD + ud_pos<KS_C>(r0), pb = ln * CPD + ud_pos<KS_C>(r0 + 2);
+                        *reinterpret_cast<bf16x2 *>(UdTh + pa) = bf16x2{dh[0], dh[1]};
+                        *reinterpret_cast<bf16x2 *>(UdTh + pb) = bf16x2{dh[2], dh[3]};
+                        *reinterpret_cast<bf16x2 *>(UdTl + pa) = bf16x2{dl[0], dl[1]};
+                        *reinterpret_cast<bf16x2 *>(UdTl + pb) = bf16x2{dl[2], dl[3]};
                     }
                 }
             } else {
@@ -1284,15 +877,15 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                 FC uh[NJ], ul[NJ], ka[MS][NJ];
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) {
-                    uh[jj] = frag_rows<__bf16, KS_C>(UdTh, CP, 0, jj * KS_C, lane);
-                    ul[jj] = frag_rows<__bf16, KS_C>(UdTl, CP, 0, jj * KS_C, lane);
+                    uh[jj] = frag_rows<__bf16, KS_C>(UdTh, CPD, 0, jj * KS_C, lane);
+                    ul[jj] = frag_rows<__bf16, KS_C>(UdTl, CPD, 0, jj * KS_C, lane);
                 }
 #pragma unroll
                 for (int m = 0; m < MS; ++m) {
                     const int ib = sw + 4 * m;
                     if (ib < NSB) {
 #pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = frag_cols<__bf16, KS_C>(Ks, KP, 16 * ib, jj * KS_C, lane);
+                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = k_cols_paired<KS_C>(Ks, KP, 16 * ib, jj * KS_C, lane);
                     }
                 }
 #pragma unroll
@@ -1369,8 +962,8 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                         const int pidx = rb * (rb + 1) / 2 + jb;
                         const F16 ah = frag_rows<__bf16, 16>(Ph + pidx * BLK, PB, 0, 0, lane);
                         const F16 al = frag_rows<__bf16, 16>(Pl + pidx * BLK, PB, 0, 0, lane);
-                        const F16 uh = frag_rows<__bf16, 16>(UTh, CP, 0, 16 * jb, lane);
-                        const F16 ul = frag_rows<__bf16, 16>(UTl, CP, 0, 16 * jb, lane);
+                        const F16 uh = frag_rows<__bf16, 16>(UTh, CPU, 0, 16 * jb, lane);
+                        const F16 ul = frag_rows<__bf16, 16>(UTl, CPU, 0, 16 * jb, lane);
                         acc = F16::mma(ah, uh, acc);
                         acc2 = F16::mma(al, uh, acc2);
                         acc2 = F16::mma(ah, ul, acc2);
@@ -1486,14 +1079,9 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                 if (gw == 4) {
                     // inclusive prefix of log2 alpha over the chunk (lane = token) and the
                     // decay factors used by the Gram tiles and the state update
-                    float g2 = lane < C ? __builtin_amdgcn_logf(pal) : 0.f;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float t = __shfl_up(g2, off);
-                        if (lane >= off) g2 += t;
-                    }
-                    const float gC = __shfl(g2, C - 1);
-                    const float gblk = __shfl(g2, lane & ~15);      // G at the first row of this lane's block
+                    const float g2 = wave_inclusive_sum(lane < C ? __builtin_amdgcn_logf(pal) : 0.f, lane);
+                    const float gC = lane_value(g2, C - 1);
+                    const float gblk = row_bcast<0>(g2);      // G at the first row of this lane's block
                     if (lane < C) {
                         reinterpret_cast<float *>(nb + L::cG)[lane] = g2;
                         reinterpret_cast<float *>(nb + L::cEG)[lane] = __builtin_amdgcn_exp2f(g2);
@@ -1503,7 +1091,7 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                     }
 #pragma unroll
                     for (int rb = 1; rb < NB; ++rb) {
-                        const float gref = __shfl(g2, 16 * rb);
+                        const float gref = lane_value(g2, 16 * rb);
                         if (lane < C)
                             reinterpret_cast<float *>(nb + L::cEb)[rb * C + lane] =
                                 lane < 16 * rb ? __builtin_amdgcn_exp2f(gref - g2) : 0.f;
