@@ -517,8 +517,10 @@ template <int C, int DK> struct PipeLay {
     // shared arrays after the two chunk buffers
     static constexpr int AP = 20;                                    // fp32 A block row pitch
     static constexpr size_t oAd = 2 * CBUF;                          // fp32 diagonal A blocks [NB][16][AP]
-    static constexpr size_t oAo = oAd + align16(4 * NB * 16 * AP);   // fp32 off-diagonal A blocks
-    static constexpr size_t oSTh = oAo + align16(4 * (NOFF > 0 ? NOFF : 1) * 16 * AP);
+    // off-diagonal A blocks as bf16 hi/lo, lane order: lane l holds A_ik[4(l/16) + e][l % 16]
+    static constexpr size_t oAoh = oAd + align16(4 * NB * 16 * AP);
+    static constexpr size_t oAol = oAoh + align16(2 * (NOFF > 0 ? NOFF : 1) * 256);
+    static constexpr size_t oSTh = oAol + align16(2 * (NOFF > 0 ? NOFF : 1) * 256);
     static constexpr size_t oSTl = oSTh + align16(2 * BV * KP);
     static constexpr size_t oW = oSTl + align16(2 * BV * KP);        // fp32 W_i exchange [NB][64 lanes][4]
     static constexpr size_t oUh = oW + align16(4 * C * BV);
@@ -618,10 +620,16 @@ __device__ __forceinline__ GTile gram_job(int job)
     return t;
 }
 
-// Two Gram tiles of chunk buffer nb (kind 0 skips), computed transposed so that
-// lane (ln, lg) holds row r = 16 rb + ln, columns j = 16 cb + 4 lg + e.
+// Two Gram tiles of chunk buffer nb (kind 0 skips).  P blocks and the diagonal
+// A blocks are computed transposed, so that lane (ln, lg) holds row
+// r = 16 rb + ln, columns j = 16 cb + 4 lg + e: four contiguous entries of a
+// row, stored as the rows later read as MFMA A operands.  Off-diagonal A
+// blocks are computed as they stand, lane (ln, lg) holding A[16 rb + 4 lg + e]
+// [16 cb + ln]: exactly the A operand of N_ik^T = A_ik^T T_ii^T, so they are
+// stored in lane order.
 template <int C, int DK>
-__device__ __forceinline__ void gram_pair(char *nb, float *Ad, float *Ao, const GTile t0, const GTile t1, int lane)
+__device__ __forceinline__ void gram_pair(char *nb, float *Ad, __bf16 *Aoh, __bf16 *Aol, const GTile t0,
+                                          const GTile t1, int lane)
 {
     using L = PipeLay<C, DK>;
     constexpr int KP = L::KP, AP = L::AP, KS_DK = L::KS_DK, NK = DK / KS_DK;
@@ -647,10 +655,12 @@ __device__ __forceinline__ void gram_pair(char *nb, float *Ad, float *Ao, const 
         for (int u = 0; u < 2; ++u) {
             if (tt[u].kind) {
                 const __bf16 *Xs = tt[u].kind == 2 ? Qs : Ks;
+                const bool direct = tt[u].kind == 1 && tt[u].rb != tt[u].cb;
+                const int ra = direct ? tt[u].rb : tt[u].cb, rbb = direct ? tt[u].cb : tt[u].rb;
 #pragma unroll
                 for (int kk = 0; kk < KG; ++kk) {
-                    fa[u][kk] = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * tt[u].cb, (k0 + kk) * KS_DK, lane);
-                    fb[u][kk] = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * tt[u].rb, (k0 + kk) * KS_DK, lane);
+                    fa[u][kk] = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * ra, (k0 + kk) * KS_DK, lane);
+                    fb[u][kk] = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * rbb, (k0 + kk) * KS_DK, lane);
                 }
             }
         }
@@ -670,6 +680,20 @@ __device__ __forceinline__ void gram_pair(char *nb, float *Ad, float *Ao, const 
             const int r = 16 * rb + ln;
             const int j0 = 16 * cbk + 4 * lg;
             f32x4 val;
+            if (!isP && rb != cbk) {
+                // off-diagonal A block, direct layout: rows r0 + e, column j
+                const int r0 = 16 * rb + 4 * lg, j = 16 * cbk + ln;
+                const f32x4 ea4 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(nb + L::cEa) + r0);
+                const f32x4 be4 = *reinterpret_cast<const f32x4 *>(Be + r0);
+                const float eb = reinterpret_cast<const float *>(nb + L::cEb)[rb * C + j];
+                val = acc[u] * eb * ea4 * be4;
+                const int oidx = rb * (rb - 1) / 2 + cbk;
+                bf16x4 hv, lv;
+                split4(val, hv, lv);
+                *reinterpret_cast<bf16x4 *>(Aoh + oidx * 256 + lane * 4) = hv;
+                *reinterpret_cast<bf16x4 *>(Aol + oidx * 256 + lane * 4) = lv;
+                continue;
+            }
             if (rb == cbk) {
                 // diagonal block: Gamma_rj = 2^(G_r - G_j) per entry, masked to the triangle
                 const float Gr = G[r];
@@ -694,8 +718,7 @@ __device__ __forceinline__ void gram_pair(char *nb, float *Ad, float *Ao, const 
                 *reinterpret_cast<bf16x4 *>(Pl + idx * BLK + ln * PB + 4 * lg) = lv;
             } else {
                 val *= Be[r];
-                float *dst = rb == cbk ? Ad + (rb * 16 + ln) * AP : Ao + ((rb * (rb - 1) / 2 + cbk) * 16 + ln) * AP;
-                *reinterpret_cast<f32x4 *>(dst + 4 * lg) = val;
+                *reinterpret_cast<f32x4 *>(Ad + (rb * 16 + ln) * AP + 4 * lg) = val;
             }
         }
     }
@@ -716,7 +739,8 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     auto cbuf = [&](int parity) { return smem + parity * L::CBUF; };
     float *Ad = reinterpret_cast<float *>(smem + L::oAd);
-    float *Ao = reinterpret_cast<float *>(smem + L::oAo);
+    __bf16 *Aoh = reinterpret_cast<__bf16 *>(smem + L::oAoh);
+    __bf16 *Aol = reinterpret_cast<__bf16 *>(smem + L::oAol);
     __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
     __bf16 *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
     float *Wx = reinterpret_cast<float *>(smem + L::oW);
@@ -753,7 +777,7 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
         if (work >= 0 && it + 1 < NC) {
             char *nb = cbuf((int)((it + 1) & 1));
             for (int j = work; j < NJOB; j += 2 * NWORK)
-                gram_pair<C, DK>(nb, Ad, Ao, gram_job<C, DK>(j), gram_job<C, DK>(j + NWORK), lane);
+                gram_pair<C, DK>(nb, Ad, Aoh, Aol, gram_job<C, DK>(j), gram_job<C, DK>(j + NWORK), lane);
         }
     };
 
@@ -1041,8 +1065,9 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                 // N_ik = T_ii A_ik of chunk it (T_ii from the previous phase 3)
                 const int i = gw;
                 __bf16 *Nn = reinterpret_cast<__bf16 *>(cbuf((int)(it & 1)) + L::cNn);
-                // lane (row ln, group lg) holds T_ii[ln][lg + 4e]: that k-set is the
-                // MFMA k order for N_ik = T_ii A_ik (the B operand is gathered to match)
+                // lane (ln, lg) holds T_ii[ln][4 lg + e]: the B operand of
+                // N_ik^T = A_ik^T T_ii^T, whose A operand the Gram epilogue stored in
+                // lane order; the result row ln, columns 4 lg + e, is a row of N_ik
                 F16 th, tl;
                 split4(f32x4{X[0], X[1], X[2], X[3]}, th.v, tl.v);
 #pragma unroll
@@ -1050,15 +1075,13 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                     if (k < i) {
                         const int oidx = i * (i - 1) / 2 + k;
                         F16 ah, al;
-                        f32x4 av;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) av[e] = Ao[(oidx * 16 + lg + 4 * e) * AP + ln];
-                        split4(av, ah.v, al.v);
-                        f32x4 n = F16::mma(th, ah, zero4());
-                        n = F16::mma(th, al, n);
-                        n = F16::mma(tl, ah, n);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Nn[oidx * BLK + (4 * lg + e) * PB + ln] = (__bf16)(-n[e]);
+                        ah.v = *reinterpret_cast<const bf16x4 *>(Aoh + oidx * 256 + lane * 4);
+                        al.v = *reinterpret_cast<const bf16x4 *>(Aol + oidx * 256 + lane * 4);
+                        f32x4 n = F16::mma(ah, th, zero4());
+                        n = F16::mma(al, th, n);
+                        n = F16::mma(ah, tl, n);
+                        *reinterpret_cast<bf16x4 *>(Nn + oidx * BLK + ln * PB + 4 * lg) =
+                            __builtin_convertvector(-n, bf16x4);
                     }
                 }
             }
@@ -1103,7 +1126,7 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
 
             // ---- phase 2
             if (gw < 4) {
-                if (act && gw < NB) gram_pair<C, DK>(nb, Ad, Ao, GTile{1, gw, gw}, GTile{0, 0, 0}, lane);
+                if (act && gw < NB) gram_pair<C, DK>(nb, Ad, Aoh, Aol, GTile{1, gw, gw}, GTile{0, 0, 0}, lane);
             } else {
                 gram_jobs(it);
             }
@@ -1118,12 +1141,13 @@ __global__ __launch_bounds__(WIDE_THREADS, 1) void gdn_prefill_wide_kernel(KPara
                     const f32x4 v4 = *reinterpret_cast<const f32x4 *>(Ad + (i * 16 + ln) * AP + 4 * s4);
                     Lr[4 * s4] = v4[0]; Lr[4 * s4 + 1] = v4[1]; Lr[4 * s4 + 2] = v4[2]; Lr[4 * s4 + 3] = v4[3];
                 }
+                // lane (ln, lg) carries row ln of T_ii, columns 4 lg + e
 #pragma unroll
-                for (int e = 0; e < 4; ++e) X[e] = (ln == lg + 4 * e) ? 1.f : 0.f;
+                for (int e = 0; e < 4; ++e) X[e] = (ln == 4 * lg + e) ? 1.f : 0.f;
                 tri_solve16(X, Lr, ln, std::make_integer_sequence<int, 15>{});
                 __bf16 *Td = reinterpret_cast<__bf16 *>(nb + L::cTd);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Td[i * BLK + ln * PB + lg + 4 * e] = (__bf16)X[e];
+                *reinterpret_cast<bf16x4 *>(Td + i * BLK + ln * PB + 4 * lg) =
+                    __builtin_convertvector((f32x4{X[0], X[1], X[2], X[3]}), bf16x4);
             }
             __syncthreads();
         }
