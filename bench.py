@@ -124,7 +124,9 @@ def bench_prefill(args, torch, gdn, wl):
     al, be = to_dev(inp["alpha"], torch), to_dev(inp["beta"], torch)
     y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
-    fn = lambda: gdn.prefill(q, k, v, al, be, None, chunk=cfg.chunk, y=y, final_state=sT)
+    ws = torch.empty(gdn.prefill_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk, "bf16"),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda: gdn.prefill(q, k, v, al, be, None, chunk=cfg.chunk, y=y, final_state=sT, workspace=ws)
     total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
     return cfg, inp, total_ms, per
 

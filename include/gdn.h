@@ -68,8 +68,15 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   B, H, T >= 0; B*H == 0 or T == 0 launch nothing except, for T == 0,
  *   final_state = initial_state (or zeros).  Any T is accepted: a ragged last
  *   chunk is padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
- *   workspace     unused by the current kernels (gdn_prefill_workspace_bytes
- *                 returns 0); may be NULL.
+ *   workspace     device scratch of at least gdn_prefill_workspace_bytes(...)
+ *                 bytes, 256-byte aligned, owned by the caller and not
+ *                 overlapping any other argument.  GDN_BF16 needs one record
+ *                 per (sequence, head, chunk) -- the chunk quantities that do
+ *                 not depend on the state (decay factors, (I + A)^-1 diag(beta)
+ *                 and the masked Q K^T block, as bf16 hi/lo MFMA fragments;
+ *                 21056 bytes at C = 64); GDN_F32 needs none (size 0, may be
+ *                 NULL).  Too small or missing: GDN_ERR_WORKSPACE.  Its
+ *                 contents are overwritten; nothing in it is kept between calls.
  * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
  */
 GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
@@ -81,6 +88,9 @@ GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Bytes of workspace gdn_prefill_fwd needs for these sizes: B*H*ceil(T/C)
+ * records for GDN_BF16, 0 for GDN_F32, for empty problems and for arguments
+ * gdn_prefill_fwd would reject. */
 GDN_API size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                    int64_t Dv, int64_t chunk, gdn_dtype dtype);
 

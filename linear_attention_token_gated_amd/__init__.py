@@ -112,10 +112,17 @@ def _need(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def prefill_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype="bf16") -> int:
+    code = {"f32": 0, "bf16": 1}[dtype]
+    return int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), code))
+
+
 def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_final_state: bool = True,
-            y=None, final_state=None):
+            y=None, final_state=None, workspace=None):
     """Chunked prefill.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (float32 or bfloat16);
     alpha, beta: [B,T,H] float32; initial_state: [B,H,Dk,Dv] float32 or None.
+    workspace: a device buffer of prefill_workspace_bytes(...) bytes, or None
+    to allocate one for this call.
     Returns (y [B,T,H,Dv] float32, final_state or None)."""
     import torch
     B, T, H, Dk = q.shape
@@ -130,9 +137,13 @@ def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_fi
         final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _need(y, "y", torch.float32)
     _need(final_state, "final_state", torch.float32)
+    need = int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _dtype_code(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().gdn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
                                  _ptr(y), _ptr(final_state), B, T, H, Dk, Dv, int(chunk), _dtype_code(q),
-                                 None, 0, _stream(q.device)))
+                                 _ptr(workspace), ws_bytes, _stream(q.device)))
     return y, final_state
 
 

@@ -8,6 +8,7 @@
 
 #include "../../include/gdn.h"
 #include "launch.hpp"
+#include "prep_layout.hpp"
 
 namespace {
 
@@ -89,9 +90,15 @@ const char *gdn_status_str(gdn_status s)
 
 const char *gdn_last_error(void) { return g_err; }
 
-size_t gdn_prefill_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, gdn_dtype)
+size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
+                                   gdn_dtype dtype)
 {
-    return 0;
+    if (B <= 0 || T <= 0 || H <= 0 || dtype != GDN_BF16 || !is_pow2_dim(Dk) || !is_pow2_dim(Dv) ||
+        (chunk != 16 && chunk != 32 && chunk != 64))
+        return 0;
+    int64_t n;
+    if (!count(&n, {B, H, (T + chunk - 1) / chunk, (int64_t)gdn::prep_record_bytes(chunk)})) return 0;
+    return gdn::prefill_workspace_bytes(B, T, H, chunk, true);
 }
 
 gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const float *alpha,
@@ -100,8 +107,6 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
                            int64_t Dv, int64_t chunk, gdn_dtype dtype, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0)
         return fail(GDN_ERR_SHAPE, "gdn_prefill_fwd: negative size (B=%lld T=%lld H=%lld Dk=%lld Dv=%lld chunk=%lld)",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv, (long long)chunk);
@@ -139,6 +144,19 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
         if (overlap(rs, inputs[i])) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: final_state overlaps %s", inputs[i].name);
     if (final_state != initial_state && overlap(rs, inputs[5]))
         return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: final_state partially overlaps initial_state");
+    const size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "gdn_prefill_fwd: workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(GDN_ERR_ALIGN, "gdn_prefill_fwd: workspace is not 256-byte aligned");
+        const Range rw{workspace, need, "workspace"};
+        if (overlap(rw, ry)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps y");
+        if (overlap(rw, rs)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps final_state");
+        for (const Range &r : inputs)
+            if (overlap(rw, r)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps %s", r.name);
+    }
 
     gdn::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
@@ -146,6 +164,7 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
     a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.chunk = chunk;
     a.q_tok_stride = H * Dk; a.k_tok_stride = H * Dk; a.v_tok_stride = H * Dv;
     a.bf16 = dtype == GDN_BF16;
+    a.ws = need > 0 ? workspace : nullptr;
     return hip_status(gdn::launch_prefill(a, stream), "gdn_prefill_fwd launch");
 }
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace gdn {
@@ -119,6 +120,16 @@ __device__ __forceinline__ Frag<OpT, KS> frag_cols(const OpT *base, int pitch, i
     return f;
 }
 
+// Calls f(std::integral_constant<int, i>{}) for i = 0..N-1: loops whose
+// index must be a constant expression (if constexpr on it).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Broadcast lane S of every 16-lane row to the whole row (DPP row_newbcast).
@@ -128,7 +139,45 @@ template <int S> __device__ __forceinline__ float row_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + S, 0xF, 0xF, true));
 }
 
+constexpr int BV = 16;   // value columns carried by one prefill workgroup
+
+constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// LDS row pitch (bf16 elements) for rows of n elements read as 16x16 MFMA
+// fragments: 128-bit reads (KS = 32) are free of bank conflicts on gfx950 when
+// the pitch is 8 mod 16 dwords, 64-bit reads (KS = 16) when it is 4 mod 8.
+template <int KS> constexpr int frag_pitch(int n) {
+    int r = n / 2;                                    // dwords
+    const int m = KS == 32 ? 16 : 8, want = KS == 32 ? 8 : 4;
+    while (r % m != want) ++r;
+    return 2 * r;
+}
+
+// Value of v in lane l (l wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// v from N lanes lower in the same 16-lane row; lanes with no such source read 0.
+template <int N> __device__ __forceinline__ float row_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Inclusive prefix sum over the 64 lanes: a scan inside each 16-lane row by
+// DPP row shifts, then the totals of the earlier rows added from scalars.
+__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    const float t0 = lane_value(x, 15), t1 = lane_value(x, 31), t2 = lane_value(x, 47);
+    const int row = lane >> 4;
+    const float base = row == 0 ? 0.f : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+    return x + base;
+}
+
 
 }  // namespace gdn

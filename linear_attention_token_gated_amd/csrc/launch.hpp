@@ -27,10 +27,16 @@ struct PrefillArgs {
     int64_t B, T, H, Dk, Dv, chunk;
     int64_t q_tok_stride, k_tok_stride, v_tok_stride;   // elements per token (all heads)
     bool bf16;
+    void *ws;                       // bf16: prefill_workspace_bytes(...) bytes, 256-byte aligned
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// bf16 prefill: per-chunk preparation into the workspace, then the recurrence
+size_t prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t chunk, bool bf16);
+hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_recurrence(const PrefillArgs &a, hipStream_t stream);
 
 // Layer helpers (layer.hip)
 struct LayerArgs {

@@ -47,8 +47,8 @@ def test_status_strings(L):
 
 
 def prefill(L, q=A, k=A + 64 * MB, v=A + 128 * MB, al=A + 192 * MB, be=A + 200 * MB, s0=None,
-            y=A + 256 * MB, sT=None, B=1, T=64, H=2, Dk=16, Dv=16, C=16, dt=0):
-    return L.gdn_prefill_fwd(q, k, v, al, be, s0, y, sT, B, T, H, Dk, Dv, C, dt, None, 0, None)
+            y=A + 256 * MB, sT=None, B=1, T=64, H=2, Dk=16, Dv=16, C=16, dt=0, w=None, wb=0):
+    return L.gdn_prefill_fwd(q, k, v, al, be, s0, y, sT, B, T, H, Dk, Dv, C, dt, w, wb, None)
 
 
 def test_prefill_validation(L):
@@ -70,6 +70,20 @@ def test_prefill_validation(L):
     assert "Dk=48" in L.gdn_last_error().decode() or True
     prefill(L, Dk=48)
     assert "Dk=48" in L.gdn_last_error().decode()
+
+
+def test_prefill_workspace_validation(L):
+    # bf16 needs one record per (sequence, head, chunk); every case below fails
+    # on the host before anything is launched
+    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1)
+    assert need == 2 * 4 * 2240
+    W = A + 400 * MB
+    assert prefill(L, dt=1) == WS                                # missing
+    assert prefill(L, dt=1, w=W, wb=need - 1) == WS              # too small
+    assert prefill(L, dt=1, w=W + 16, wb=need) == ALIGN          # not 256-byte aligned
+    assert prefill(L, dt=1, w=A + 256 * MB, wb=need) == ALIAS    # workspace == y
+    assert prefill(L, dt=1, w=A + 64 * MB, wb=need) == ALIAS     # workspace == k
+    assert "workspace" in L.gdn_last_error().decode()
 
 
 def decode(L, q=A, k=A + MB, v=A + 2 * MB, al=A + 3 * MB, be=A + 4 * MB, S=A + 8 * MB, y=A + 64 * MB,
@@ -110,6 +124,11 @@ def test_layer_validation(L):
 
 
 def test_workspace_queries(L):
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 0
+    # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
+    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 0      # fp32 needs none
+    assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
+    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
     assert L.gdn_layer_workspace_bytes(1, 0, 2048, 16, 128, 128, 4, 64) == 0
     assert L.gdn_layer_workspace_bytes(1, 16384, 2048, 16, 128, 128, 4, 64) > 16384 * 2048
