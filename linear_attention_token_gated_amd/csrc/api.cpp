@@ -123,6 +123,10 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
         return fail(GDN_ERR_SHAPE, "gdn_prefill_fwd: sizes overflow");
     if (B * H > (int64_t)1 << 26 || (B * H) * (Dv / 16) > INT32_MAX)
         return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: B*H=%lld too large for one launch", (long long)(B * H));
+    // bf16 chunks are copied with 32-bit byte offsets within one chunk of rows
+    if (dtype == GDN_BF16 && chunk * H * (Dk > Dv ? Dk : Dv) * 2 >= ((int64_t)1 << 31))
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: H=%lld too large for bf16 (chunk * H * max(Dk, Dv) * 2 must stay below 2^31)",
+                    (long long)H);
     const bool need_io = n_tok > 0;
     if (need_io && (!q || !k || !v || !alpha || !beta || !y))
         return fail(GDN_ERR_NULL, "gdn_prefill_fwd: q, k, v, alpha, beta and y are required");

@@ -41,8 +41,11 @@ template <int C, int DK> struct PrepLds {
     static constexpr size_t oK = 0;
     static constexpr size_t oQ = oK + align16(2 * C * KP);
     static constexpr size_t oA = oQ + align16(2 * C * KP);      // A blocks [NTRI][16][AP], row-major
-    static constexpr size_t oT = oA + align16(4 * NTRI * 16 * AP);   // (I + A)^-1 blocks, row-major
-    static constexpr size_t oG = oT + align16(4 * NTRI * 16 * AP);
+    // (I + A)^-1 blocks, row-major: written only after the Gram blocks are done,
+    // so they reuse the space of the K and Q rows where that is large enough
+    static constexpr bool T_IN_KQ = 4 * NTRI * 16 * AP <= 2 * 2 * C * KP;
+    static constexpr size_t oT = T_IN_KQ ? oK : oA + align16(4 * NTRI * 16 * AP);
+    static constexpr size_t oG = (T_IN_KQ ? oA : oT) + align16(4 * NTRI * 16 * AP);
     static constexpr size_t oBe = oG + align16(4 * C);
     static constexpr size_t oEa = oBe + align16(4 * C);         // 2^(G_r - G_{16 floor(r/16)})
     static constexpr size_t oEb = oEa + align16(4 * C);         // [NB][C] 2^(G_{16 rb} - G_j), j < 16 rb
@@ -64,7 +67,7 @@ __device__ __forceinline__ void fsub16(float (&X)[4], const float (&Lr)[16], std
 }
 
 template <int C, int DK>
-__global__ __launch_bounds__(PREP_THREADS) void gdn_chunk_prep_kernel(PrepParams p)
+__global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepParams p)
 {
     using L = PrepLds<C, DK>;
     using Rec = PrepRecord<C>;
