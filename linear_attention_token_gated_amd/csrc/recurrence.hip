@@ -16,20 +16,23 @@
 // MFMA accumulators).  Twelve wavefronts, three phases per chunk:
 //
 //  waves   phase 1                     phase 2                 phase 3
-//  0-3     K S of row block w -> R_w   U_w = sum_k T'_wk R_k    S update (rows 16w, 16(w+4))
-//  4-7     Y of chunk c-1: + P U       EG Q S of row block w-4  -
-//  8-11    copy chunk c+2 into LDS, a third in each phase; wait for chunk c+1
+//  0-3     K S, Q S of row block w     U_w = sum_k T'_wk R_k    S update (rows 16w, 16(w+4))
+//          -> R_w, EG Q S
+//  4-7     store Y of chunk c-1        -                       Y = EG Q S + P U
+//  8-11    T' of chunk c+1 and chunk c+2 into LDS, spread over the phases;
+//          wait for chunk c+1
 //
 // Three LDS chunk buffers hold K, Q, the V slice and the decay vectors.  The
 // staging waves fill them with buffer loads that write LDS directly (no
 // registers, no LDS store instructions), two chunks ahead; the only wait is one
 // exact count of those loads before the barrier that hands a buffer over.
+// T' of the next chunk goes the same way into a ring of two slots.
 // Rows past the end of the sequence lie outside the buffer range of the load
 // and arrive as zeros.  K and Q rows are stored unpadded with their 16-byte
 // granules permuted by row (granule g of row r at position g ^ (r mod G)):
 // fragment reads and the column gather of the state update then hit distinct
-// LDS banks.  The T' and P fragments of the record go straight into the
-// registers of the wavefronts that use them, one chunk ahead.
+// LDS banks.  The P fragments of the record go straight into the registers
+// of the wavefronts that use them, one chunk ahead.
 //
 // Precision: q, k, v are exact bf16 MFMA operands, every product accumulates
 // in fp32.  Operands computed in fp32 -- S, R, U, the decayed U, and from the
@@ -100,7 +103,11 @@ template <int C, int DK> struct RecLay {
     static constexpr size_t oUl = oUh + align16(2 * BV * CPU);
     static constexpr size_t oUdh = oUl + align16(2 * BV * CPU);
     static constexpr size_t oUdl = oUdh + align16(2 * BV * CPD);
-    static constexpr size_t oJunk = round1k(oUdl + align16(2 * BV * CPD));   // target of padding loads
+    // T' of two chunks (chunk c in slot c % 2), the record's 1 KB blocks as they are
+    static constexpr int NTRI = NB * (NB + 1) / 2;
+    static constexpr size_t oTr = round1k(oUdl + align16(2 * BV * CPD));
+    static constexpr size_t oEq = oTr + (size_t)2 * NTRI * 1024;    // diag(EG) Q S [NB][64 lanes] f32x4
+    static constexpr size_t oJunk = round1k(oEq + (size_t)NB * 1024);   // target of padding loads
     static constexpr size_t BYTES = oJunk + 1024;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     // staging loads per chunk (one 64-lane, 16-byte-per-lane load each)
@@ -130,38 +137,81 @@ __device__ __forceinline__ Frag<__bf16, KS> frag_kq(const __bf16 *base, int r0, 
 }
 
 // Token order of the decayed U^T rows used by the state update.  Within each
-// k-step of KS tokens, lane group g (KS/4 values per lane) takes the tokens
-// 2g + 8(e/2) + (e%2), e = 0..KS/4-1: adjacent pairs, 8 tokens apart, so the
-// K column gather reads rows two tokens apart in the four lane groups.
-// ud_pos gives the storage position of token t; the B operand is then an
-// ordinary contiguous fragment read.
+// k-step of KS tokens, lane group g takes the tokens 4g..4g+3 and, for KS = 32,
+// 16+4g..16+4g+3 (the order in which the transposing reads below deliver K^T).
+// ud_pos gives the storage position of token t, so that the B operand is an
+// ordinary contiguous fragment read and four consecutive tokens stay adjacent.
 template <int KS> __device__ __forceinline__ int ud_pos(int t) {
-    constexpr int E = KS / 4;
-    const int u = t % KS;
-    return (t - u) + ((u & 7) >> 1) * E + (u >> 3) * 2 + (u & 1);
+    if constexpr (KS == 16) {
+        return t;
+    } else {
+        const int u = t % 32;
+        return (t - u) + 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3);
+    }
 }
 
-// A operand K^T[r0 + ln][tokens of ud_pos order] of one k-step at k0.  The
-// token of element e is t = k0 + 2g + 8(e/2) + (e%2); k0 is a multiple of the
-// granule count G, and 2g + (e%2) < 8, so t mod G = (2g + e%2) ^ (8(e/2) mod G):
-// the permuted granule takes two lane-dependent values per e%2, and the rest
-// of the address is a compile-time row offset.
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4v *lds_i16x4;
+
+// Transposing LDS read of 16-bit elements (gfx950): lane j of each group of 16
+// supplies the address of 4 consecutive elements; lane i of the group receives
+// element i % 4 of the rows supplied by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.
+__device__ __forceinline__ bf16x4 read_tr16(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (lds_i16x4)(uintptr_t)(uint32_t)(uintptr_t)p));
+}
+
+// A operand K^T[r0 + m][tokens of ud_pos order] of one k-step at k0 from the
+// row-major (granule-permuted) K chunk: lane j of group g points at row
+// k0 + 4g + j/4 (and 16 rows further for KS = 32), columns r0 + 4(j%4)..+3;
+// lane m of the group then holds column r0 + m at the four tokens.  Each read
+// covers 16 consecutive rows, whose permuted granules fall on distinct banks.
 template <int KS, int DK>
-__device__ __forceinline__ Frag<__bf16, KS> k_cols_paired(const __bf16 *Ks, int r0, int k0, int lane) {
-    constexpr int G = DK / 8;
+__device__ __forceinline__ Frag<__bf16, KS> k_cols_tr(const __bf16 *Ks, int r0, int k0, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const int row = k0 + 4 * g + (j >> 2), col = r0 + 4 * (j & 3);
     Frag<__bf16, KS> f;
-    const int col = r0 + (lane & 15), g2 = 2 * (lane >> 4);
-    const int base = g2 * DK + (col & 7);
-    int off[2][2];                                   // [e % 2][(e / 2) % 2]
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int x = (col >> 3) ^ ((g2 + i) & (G - 1));
-        off[i][0] = base + i * DK + x * 8;
-        off[i][1] = base + i * DK + (x ^ (8 & (G - 1))) * 8;
+    if constexpr (KS == 16) {
+        f.v = read_tr16(Ks + kq_idx<DK>(row, col));
+    } else {
+        const bf16x4 a = read_tr16(Ks + kq_idx<DK>(row, col));
+        const bf16x4 b = read_tr16(Ks + kq_idx<DK>(row + 16, col));
+        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
-#pragma unroll
-    for (int e = 0; e < KS / 4; ++e) f.set_raw(e, Ks[(k0 + 8 * (e >> 1)) * DK + off[e & 1][(e >> 1) & 1]]);
     return f;
+}
+
+// Two 16-deep MFMA fragments (k-blocks a and b) as one 32-deep fragment.  Used
+// on both operands of a product, the pairing only reorders the terms of the
+// k-sum: A[m][a-block k], A[m][b-block k] meet B[a-block k][n], B[b-block k][n].
+__device__ __forceinline__ Frag<__bf16, 32> pair16(bf16x4 a, bf16x4 b) {
+    Frag<__bf16, 32> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+// sum over the blocks k < NK2 of A_k B_k (hi/lo pairs, three products each),
+// two blocks per 32-deep MFMA and a 16-deep one for an odd last block
+template <int NK2>
+__device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al, const bf16x4 *bh, const bf16x4 *bl,
+                                              f32x4 &acc, f32x4 &acc2) {
+    using F16 = Frag<__bf16, 16>;
+    using F32 = Frag<__bf16, 32>;
+    static_for<NK2 / 2>([&](auto i_c) {
+        constexpr int k = 2 * decltype(i_c)::value;
+        const F32 a = pair16(ah[k], ah[k + 1]), a2 = pair16(al[k], al[k + 1]);
+        const F32 b = pair16(bh[k], bh[k + 1]), b2 = pair16(bl[k], bl[k + 1]);
+        acc = F32::mma(a, b, acc);
+        acc2 = F32::mma(a, b2, acc2);
+        acc2 = F32::mma(a2, b, acc2);
+    });
+    if constexpr (NK2 % 2) {
+        F16 a, a2, b, b2;
+        a.v = ah[NK2 - 1]; a2.v = al[NK2 - 1]; b.v = bh[NK2 - 1]; b2.v = bl[NK2 - 1];
+        acc = F16::mma(a, b, acc);
+        acc2 = F16::mma(a, b2, acc2);
+        acc2 = F16::mma(a2, b, acc2);
+    }
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone
@@ -249,20 +299,6 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         };
         write_state_operand();
 
-        // T' fragments of this row block, two register sets (chunk j in set j % 2)
-        bf16x4 tfh[2][NT], tfl[2][NT];
-        auto load_t = [&](auto set_c, int64_t c) {
-            constexpr int s_ = decltype(set_c)::value;
-            if constexpr (has_rb) {
-                const bf16x4 *tf = reinterpret_cast<const bf16x4 *>(recs + c * (int64_t)Rec::BYTES + Rec::oT);
-#pragma unroll
-                for (int k = 0; k <= rb; ++k) {
-                    tfh[s_][k] = tf[tri_idx(rb, k) * 128 + lane];
-                    tfl[s_][k] = tf[tri_idx(rb, k) * 128 + 64 + lane];
-                }
-            }
-        };
-        load_t(S0{}, 0);
         __syncthreads();                        // chunk 0 staged, S^T written
 
         auto iter = [&](auto set_c, int64_t c) {
@@ -270,22 +306,31 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             const char *cb = cbuf(c);
             const __bf16 *Ks = reinterpret_cast<const __bf16 *>(cb + L::cK);
             const float *dec = reinterpret_cast<const float *>(cb + L::cDec);
-            // ---- phase 1: R_rb = V_rb - diag(EG) K_rb S
+            // ---- phase 1: R_rb = V_rb - diag(EG) K_rb S, and diag(EG) Q_rb S for
+            // the output (the state operand is read once for both)
             if constexpr (has_rb) {
                 const __bf16 *Vs = reinterpret_cast<const __bf16 *>(cb + L::cV);
+                const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * rb + 4 * lg);
-                FDK kf[NK], sh[NK], slo[NK];
+                FDK kf[NK], qf[NK], sh[NK], slo[NK];
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
                     kf[kk] = frag_kq<KS_DK, DK>(Ks, 16 * rb, kk * KS_DK, lane);
                     sh[kk] = frag_rows<__bf16, KS_DK>(STh, KPS, 0, kk * KS_DK, lane);
                     slo[kk] = frag_rows<__bf16, KS_DK>(STl, KPS, 0, kk * KS_DK, lane);
                 }
-                f32x4 ks_h = zero4(), ks_l = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) qf[kk] = frag_kq<KS_DK, DK>(Qs, 16 * rb, kk * KS_DK, lane);
+                f32x4 ks_h = zero4(), ks_l = zero4(), qs_h = zero4(), qs_l = zero4();
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
                     ks_h = FDK::mma(kf[kk], sh[kk], ks_h);
                     ks_l = FDK::mma(kf[kk], slo[kk], ks_l);
+                }
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    qs_h = FDK::mma(qf[kk], sh[kk], qs_h);
+                    qs_l = FDK::mma(qf[kk], slo[kk], qs_l);
                 }
                 f32x4 rv;
 #pragma unroll
@@ -295,9 +340,8 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 split4(rv, hv, lv);
                 Rh[rb * 64 + lane] = hv;
                 Rl[rb * 64 + lane] = lv;
+                reinterpret_cast<f32x4 *>(smem + L::oEq)[rb * 64 + lane] = eg * (qs_h + qs_l);
             }
-            // the next chunk's T' (the last chunk's again at the end: no branch)
-            load_t(std::integral_constant<int, 1 - s_>{}, clampc(c + 1));
             __syncthreads();
 
             // ---- phase 2: U_rb = sum_{k <= rb} T'_rb,k R_k
@@ -305,34 +349,27 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 f32x4 u = zero4(), u2 = zero4();
                 const int r0 = 16 * rb + 4 * lg;
                 const f32x4 ed = *reinterpret_cast<const f32x4 *>(dec + C + r0);
-                F16 rh[NT], rl[NT];
+                // T' of this chunk: slot c % 2 (s_ == c % 2)
+                const bf16x4 *Tp = reinterpret_cast<const bf16x4 *>(smem + L::oTr + (size_t)s_ * L::NTRI * 1024);
+                bf16x4 rh[NT], rl[NT], ah[NT], al[NT];
                 static_for<NT>([&](auto k_c) {
                     constexpr int k = decltype(k_c)::value;
-                    rh[k].v = Rh[k * 64 + lane];
-                    rl[k].v = Rl[k * 64 + lane];
+                    rh[k] = Rh[k * 64 + lane];
+                    rl[k] = Rl[k * 64 + lane];
+                    ah[k] = Tp[tri_idx(rb, k) * 128 + lane];
+                    al[k] = Tp[tri_idx(rb, k) * 128 + 64 + lane];
                 });
-                static_for<NT>([&](auto k_c) {
-                    constexpr int k = decltype(k_c)::value;
-                    F16 ah, al;
-                    ah.v = tfh[s_][k];
-                    al.v = tfl[s_][k];
-                    u = F16::mma(ah, rh[k], u);
-                    u2 = F16::mma(ah, rl[k], u2);
-                    u2 = F16::mma(al, rh[k], u2);
-                });
+                pair_products<NT>(ah, al, rh, rl, u, u2);
                 u += u2;
                 bf16x4 uh, ul, dh, dl;
                 split4(u, uh, ul);
                 split4(ed * u, dh, dl);
                 *reinterpret_cast<bf16x4 *>(UTh + ln * CPU + r0) = uh;
                 *reinterpret_cast<bf16x4 *>(UTl + ln * CPU + r0) = ul;
-                // tokens (r0, r0 + 1) and (r0 + 2, r0 + 3) stay adjacent in the
-                // permuted order of the decayed U^T
-                const int pa = ln * CPD + ud_pos<KS_C>(r0), pb = ln * CPD + ud_pos<KS_C>(r0 + 2);
-                *reinterpret_cast<bf16x2 *>(UdTh + pa) = bf16x2{dh[0], dh[1]};
-                *reinterpret_cast<bf16x2 *>(UdTh + pb) = bf16x2{dh[2], dh[3]};
-                *reinterpret_cast<bf16x2 *>(UdTl + pa) = bf16x2{dl[0], dl[1]};
-                *reinterpret_cast<bf16x2 *>(UdTl + pb) = bf16x2{dl[2], dl[3]};
+                // tokens r0..r0+3 stay adjacent in the order of the decayed U^T
+                const int pd = ln * CPD + ud_pos<KS_C>(r0);
+                *reinterpret_cast<bf16x4 *>(UdTh + pd) = dh;
+                *reinterpret_cast<bf16x4 *>(UdTl + pd) = dl;
             }
             __syncthreads();
 
@@ -351,7 +388,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                     const int ib = rb + 4 * m;
                     if (ib < NSB) {
 #pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = k_cols_paired<KS_C, DK>(Ks, 16 * ib, jj * KS_C, lane);
+                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = k_cols_tr<KS_C, DK>(Ks, 16 * ib, jj * KS_C, lane);
                     }
                 }
 #pragma unroll
@@ -392,17 +429,15 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
     };
 
     // Y-waves: row block rb = w - 4, compile-time in each copy.  The output
-    // of a chunk is off the critical path of the recurrence, so it is spread
-    // over the phases the S-waves leave light: Q S of chunk c in phase 2 of
-    // iteration c (the state operand still holds the chunk's initial state),
-    // and P U of chunk c with the store of its rows in phase 1 of iteration
-    // c + 1 (U of chunk c stays in LDS until phase 2 of that iteration).
+    // of a chunk is off the critical path of the recurrence: P U in phase 3
+    // (U is complete; diag(EG) Q S comes from the S-wave of the row block),
+    // then the loads of the next chunk's P fragments, and the stores of the
+    // rows in phase 1 of the next iteration.
     auto y_wave = [&](auto rb_c) {
         constexpr int rb = decltype(rb_c)::value;
         constexpr bool has_rb = rb < NB;
         constexpr int NP = has_rb ? rb + 1 : 1;     // P blocks of this row block
-        // P fragments of this row block for the chunk whose output is pending
-        bf16x4 pfh[NP], pfl[NP];
+        bf16x4 pfh[NP], pfl[NP];                    // P fragments of this row block
         auto load_p = [&](int64_t c) {
             if constexpr (has_rb) {
                 const bf16x4 *pf = reinterpret_cast<const bf16x4 *>(recs + c * (int64_t)Rec::BYTES + Rec::oP);
@@ -413,30 +448,9 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 }
             }
         };
-        f32x4 eqs = zero4();                        // diag(EG) Q S of the pending chunk
-        // Y rows of chunk c: diag(EG) Q S + P U, U read from LDS
-        auto finish = [&](int64_t c) {
+        f32x4 yv = zero4();                         // output rows waiting to be stored
+        auto store_y = [&](int64_t c) {
             if constexpr (has_rb) {
-                f32x4 acc = eqs, acc2 = zero4();
-                F16 uh[NP], ul[NP];
-                static_for<NP>([&](auto j_c) {
-                    constexpr int jb = decltype(j_c)::value;
-                    uh[jb] = frag_rows<__bf16, 16>(UTh, CPU, 0, 16 * jb, lane);
-                    ul[jb] = frag_rows<__bf16, 16>(UTl, CPU, 0, 16 * jb, lane);
-                });
-                static_for<NP>([&](auto j_c) {
-                    constexpr int jb = decltype(j_c)::value;
-                    F16 ah, al;
-                    ah.v = pfh[jb];
-                    al.v = pfl[jb];
-                    acc = F16::mma(ah, uh[jb], acc);
-                    acc2 = F16::mma(al, uh[jb], acc2);
-                    acc2 = F16::mma(ah, ul[jb], acc2);
-                });
-                f32x4 yv = acc + acc2;
-                // keep the sum next to its MFMAs: an MFMA result read right after
-                // a branch can miss its wait states
-                asm volatile("" : "+v"(yv));
                 const int64_t c0 = c * C;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -449,38 +463,30 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         __syncthreads();
 
         for (int64_t c = 0; c < NC; ++c) {
-            const char *cb = cbuf(c);
-            // ---- phase 1: output of chunk c - 1, then the P fragments of chunk c
-            if (c > 0) finish(c - 1);
-            if (c > 0) load_p(c);
+            // ---- phase 1: rows of chunk c - 1
+            if (c > 0) store_y(c - 1);
             __syncthreads();
-            // ---- phase 2: diag(EG) Q S of this row block (state at the chunk's start)
+            __syncthreads();
+            // ---- phase 3: Y = diag(EG) Q S + P U; then the next chunk's P (the
+            // last chunk's again at the end: no branch)
             if constexpr (has_rb) {
-                const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
-                const float *dec = reinterpret_cast<const float *>(cb + L::cDec);
-                FDK qf[NK], sh[NK], slo[NK];
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    qf[kk] = frag_kq<KS_DK, DK>(Qs, 16 * rb, kk * KS_DK, lane);
-                    sh[kk] = frag_rows<__bf16, KS_DK>(STh, KPS, 0, kk * KS_DK, lane);
-                    slo[kk] = frag_rows<__bf16, KS_DK>(STl, KPS, 0, kk * KS_DK, lane);
-                }
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * rb + 4 * lg);
-                f32x4 qh = zero4(), ql = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    qh = FDK::mma(qf[kk], sh[kk], qh);
-                    ql = FDK::mma(qf[kk], slo[kk], ql);
-                }
-                eqs = eg * (qh + ql);
-                asm volatile("" : "+v"(eqs));
+                f32x4 acc = reinterpret_cast<const f32x4 *>(smem + L::oEq)[rb * 64 + lane], acc2 = zero4();
+                bf16x4 uh[NP], ul[NP];
+                static_for<NP>([&](auto j_c) {
+                    constexpr int jb = decltype(j_c)::value;
+                    uh[jb] = *reinterpret_cast<const bf16x4 *>(UTh + ln * CPU + 16 * jb + 4 * lg);
+                    ul[jb] = *reinterpret_cast<const bf16x4 *>(UTl + ln * CPU + 16 * jb + 4 * lg);
+                });
+                pair_products<NP>(pfh, pfl, uh, ul, acc, acc2);
+                yv = acc + acc2;
+                // keep the sum next to its MFMAs: an MFMA result read right after
+                // a branch can miss its wait states
+                asm volatile("" : "+v"(yv));
             }
-            __syncthreads();
-            // ---- phase 3: the S-waves update the state
+            load_p(clampc(c + 1));
             __syncthreads();
         }
-        // U of the last chunk was written before the last phase 2 barrier
-        if (NC > 0) finish(NC - 1);
+        if (NC > 0) store_y(NC - 1);
     };
 
     // Staging waves: JW loads of 64 lanes x 16 bytes per chunk each, written
@@ -528,6 +534,16 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 voff[i] = OOB_OFFSET;
             }
         });
+        // T' of chunk c into slot c % 2: record blocks t = lw, lw + 4, ...
+        constexpr int NTW = (L::NTRI - lw + 3) / 4;
+        auto stage_t = [&](int64_t c, int64_t slot) {
+            const void *br = recs + c * (int64_t)Rec::BYTES + Rec::oT;
+            char *dst = smem + L::oTr + (size_t)(slot & 1) * L::NTRI * 1024;
+            static_for<NTW>([&](auto i_c) {
+                constexpr int t = lw + 4 * decltype(i_c)::value;
+                load_to_lds(br, (uint32_t)(L::NTRI * 1024), (uint32_t)(t * 1024 + lane * 16), dst + t * 1024);
+            });
+        };
         // loads [I0, I1) of chunk c into chunk buffer cb_idx % 3
         auto stage = [&](int64_t c, int64_t cb_idx, auto i0_c, auto i1_c) {
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
@@ -560,7 +576,9 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         using P1 = std::integral_constant<int, JW / 3>;
         using P2 = std::integral_constant<int, 2 * JW / 3>;
         using PJ = std::integral_constant<int, JW>;
-        // chunks 0 and 1 in flight; chunk 0 complete before the first barrier
+        // T' of chunk 0 and chunks 0 and 1 in flight; all but chunk 1 complete
+        // before the first barrier
+        stage_t(0, 0);
         stage(0, 0, Z{}, PJ{});
         stage(clampc(1), 1, Z{}, PJ{});
         wait_vmcnt<JW>();
@@ -570,14 +588,18 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             // was iteration c-1 (past the end, the last chunk again: that buffer is
             // never read).  The loads are spread over the three phases so that
             // their issue overlaps the computation.
+            // T' of chunk c+1 first, into slot (c+1) % 2, last read in phase 2 of
+            // iteration c-1
+            stage_t(clampc(c + 1), c + 1);
             const int64_t cn = clampc(c + 2);
             stage(cn, c + 2, Z{}, P1{});
             __builtin_amdgcn_s_barrier();
             stage(cn, c + 2, P1{}, P2{});
             __builtin_amdgcn_s_barrier();
             stage(cn, c + 2, P2{}, PJ{});
-            // chunk c+1 must be complete before the barrier that starts iteration
-            // c+1; chunk c+2 may still be in flight
+            // T' of chunk c+1 and chunk c+1 must be complete before the barrier
+            // that starts iteration c+1; chunk c+2 (the last JW loads) may still
+            // be in flight
             wait_vmcnt<JW>();
             __builtin_amdgcn_s_barrier();
         }
