@@ -99,23 +99,40 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     const __bf16 *qg = static_cast<const __bf16 *>(p.q);
     char *out = static_cast<char *>(p.ws) + rec * Rec::BYTES;
 
-    // ---- 1. K and Q rows of the chunk (zero past the end), gates and decay scan
-    for (int vi = tid; vi < C * VPR; vi += PREP_THREADS) {
+    // ---- 1. K and Q rows of the chunk (zero past the end), gates and decay scan.
+    //         Every load is issued before the first is used (rows past the end
+    //         read the last row and are zeroed), so the chunk costs one memory
+    //         round trip.
+    constexpr int NLD = (C * VPR + PREP_THREADS - 1) / PREP_THREADS;
+    f32x4 kv[NLD], qv[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int vi = tid + i * PREP_THREADS;
+        const int r = (vi < C * VPR ? vi : 0) / VPR, col = (vi % VPR) * 8;
+        const int64_t tok = b * p.T + (t0 + r < p.T ? t0 + r : p.T - 1);
+        kv[i] = *reinterpret_cast<const f32x4 *>(kg + tok * p.ks + h * DK + col);
+        qv[i] = *reinterpret_cast<const f32x4 *>(qg + tok * p.qs + h * DK + col);
+    }
+    const bool real = lane < C && t0 + lane < p.T;
+    const int64_t gi = (b * p.T + (real ? t0 + lane : 0)) * p.H + h;
+    float al = 1.f, be = 0.f;
+    if (wave == 0) {
+        al = p.alpha[gi];
+        be = p.beta[gi];
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int vi = tid + i * PREP_THREADS;
         const int r = vi / VPR, col = (vi % VPR) * 8;
-        f32x4 kv = zero4(), qv = zero4();
-        if (t0 + r < p.T) {
-            const int64_t tok = b * p.T + t0 + r;
-            kv = *reinterpret_cast<const f32x4 *>(kg + tok * p.ks + h * DK + col);
-            qv = *reinterpret_cast<const f32x4 *>(qg + tok * p.qs + h * DK + col);
+        if (vi < C * VPR) {
+            const bool in = t0 + r < p.T;
+            *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = in ? kv[i] : zero4();
+            *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = in ? qv[i] : zero4();
         }
-        *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = kv;
-        *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = qv;
     }
     if (wave == 0) {
-        const bool real = lane < C && t0 + lane < p.T;
-        const int64_t gi = (b * p.T + t0 + lane) * p.H + h;
-        const float al = real ? p.alpha[gi] : 1.f;
-        const float be = real ? p.beta[gi] : 0.f;
+        al = real ? al : 1.f;
+        be = real ? be : 0.f;
         const float g2 = wave_inclusive_sum(lane < C ? __builtin_amdgcn_logf(al) : 0.f, lane);
         const float gC = lane_value(g2, C - 1);
         const float gblk = row_bcast<0>(g2);
