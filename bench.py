@@ -3,17 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-A step is one call of the chunked prefill on the 32K-token workload (B=1,
-T=32768, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y)
-with every input already resident in HBM.  The line printed also carries the
-decode step (256 sequences x 32 heads, fp32 128x128 states updated in place)
-and the full layer (B=1, T=16384, hidden 2048, H=16) measured the same way,
-the roofline of the prefill kernel, and the fp64 oracle timed on the host
-cores on a bounded sample of the same workload.
+A step is one chunked prefill on the 32K-token workload (B=1, T=32768,
+H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y) with every
+input already resident in HBM: gdn_prefill_prepare (the per-chunk
+preparation kernel) then gdn_prefill_recurrence (the state recurrence
+kernel), which together are exactly gdn_prefill_fwd.  The line printed also
+carries the decode step (256 sequences x 32 heads, fp32 128x128 states
+updated in place) and the full layer (B=1, T=16384, hidden 2048, H=16)
+measured the same way, the roofline of the recurrence kernel (the larger part
+of the step) with the preparation kernel beside it, and the fp64 oracle timed
+on the host cores on a bounded sample of the same workload.
 
 Timing: HIP events recorded on the stream the kernels are launched on
-(torch's current stream), around every launch of the timed region; the
-region itself is bracketed by device synchronisations.
+(torch's current stream), around every launch of the timed region (each of
+the two prefill kernels has its own pair); the region itself is bracketed by
+device synchronisations.
 """
 from __future__ import annotations
 
@@ -45,6 +49,28 @@ def prefill_alg(B, T, H, Dk, Dv, C, in_bytes=2, has_s0=False):
     return bytes_, tok * f_alg
 
 
+def record_bytes(C):
+    """Bytes of one per-chunk record of the preparation kernel: T' and P as
+    bf16 hi/lo 16x16 blocks (C/16 (C/16 + 1) / 2 of each, 1 KB per block),
+    then the decay vectors (2C + 16 floats)."""
+    nb = C // 16
+    return 2 * (nb * (nb + 1) // 2) * 1024 + (2 * C + 16) * 4
+
+
+def prep_alg(B, T, H, Dk, C, in_bytes=2):
+    """Preparation kernel: q, k, alpha, beta read once, one record written per
+    (sequence, head, chunk)."""
+    return B * T * H * (2 * Dk * in_bytes + 8) + B * H * (-(-T // C)) * record_bytes(C)
+
+
+def recurrence_alg(B, T, H, Dk, Dv, C, in_bytes=2, has_s0=False):
+    """Recurrence kernel: q, k, v and the records read once, y (fp32) and the
+    final state written once."""
+    tok = B * T * H
+    return (tok * ((2 * Dk + Dv) * in_bytes + 4 * Dv) + B * H * (-(-T // C)) * record_bytes(C)
+            + B * H * Dk * Dv * 4 * (2 if has_s0 else 1))
+
+
 def decode_alg(N, H, Dk, Dv, in_bytes=2):
     """State read + written once, q/k/v/alpha/beta read, y (fp32) written."""
     per = 8 * Dk * Dv + (2 * Dk + Dv) * in_bytes + 8 + 4 * Dv
@@ -66,7 +92,9 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill.hip",
+PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/recurrence.hip",
+                   "linear_attention_token_gated_amd/csrc/chunk_prep.hip",
+                   "linear_attention_token_gated_amd/csrc/prep_layout.hpp",
                    "linear_attention_token_gated_amd/csrc/common.hpp"]
 
 
@@ -87,26 +115,33 @@ def measured_traffic(key="prefill_32k", sources=PREFILL_SOURCES):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, torch):
-    """Run fn warmup times, then `steps` times with a HIP event pair around
-    each launch on the current stream.  Returns (total ms of the bracketed
-    region, list of per-launch ms)."""
+def time_launches(fns, steps, warmup, torch):
+    """A step calls every function of `fns` in order.  Run `warmup` steps,
+    then `steps` steps with a HIP event pair around each call on the current
+    stream.  Returns (total ms of the bracketed region, per function a list of
+    per-call ms)."""
+    if callable(fns):
+        fns = [fns]
     for _ in range(warmup):
-        fn()
+        for fn in fns:
+            fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record(stream)
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    for step in ev:
+        for fn, (a, b) in zip(fns, step):
+            a.record(stream)
+            fn()
+            b.record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
-    return t_all0.elapsed_time(t_all1), [a.elapsed_time(b) for a, b in ev]
+    per = [[step[i][0].elapsed_time(step[i][1]) for step in ev] for i in range(len(fns))]
+    return t_all0.elapsed_time(t_all1), (per[0] if len(fns) == 1 else per)
 
 
 def to_dev(a, torch):
@@ -126,9 +161,10 @@ def bench_prefill(args, torch, gdn, wl):
     sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
     ws = torch.empty(gdn.prefill_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk, "bf16"),
                      dtype=torch.uint8, device="cuda")
-    fn = lambda: gdn.prefill(q, k, v, al, be, None, chunk=cfg.chunk, y=y, final_state=sT, workspace=ws)
-    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
-    return cfg, inp, total_ms, per
+    prep = lambda: gdn.prefill_prepare(q, k, al, be, ws, chunk=cfg.chunk)
+    rec = lambda: gdn.prefill_recurrence(q, k, v, ws, None, chunk=cfg.chunk, y=y, final_state=sT)
+    total_ms, (per_prep, per_rec) = time_launches([prep, rec], args.steps, args.warmup, torch)
+    return cfg, inp, total_ms, per_prep, per_rec
 
 
 def bench_decode(args, torch, gdn, wl):
@@ -208,13 +244,15 @@ def main():
                           "copy_bytes_written": dst.numel() * 4}))
         return
 
-    cfg, inp, p_total, p_per = bench_prefill(args, torch, gdn, wl)
+    cfg, inp, p_total, p_prep, p_rec = bench_prefill(args, torch, gdn, wl)
     alg_bytes, alg_flops = prefill_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
     ms_step = p_total / args.steps
-    ms_launch = float(np.mean(p_per))
+    ms_prep, ms_rec = float(np.mean(p_prep)), float(np.mean(p_rec))
     tok_s = cfg.B * cfg.T / (ms_step * 1e-3)
-    achieved_gbps = alg_bytes / (ms_launch * 1e-3) / 1e9
-    traffic = measured_traffic()
+    rec_bytes = recurrence_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
+    prep_bytes = prep_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.chunk)
+    achieved_gbps = rec_bytes / (ms_rec * 1e-3) / 1e9
+    traffic = measured_traffic("prefill_32k_recurrence")
 
     d_cfg, d_total, d_per = bench_decode(args, torch, gdn, wl)
     d_bytes, _ = decode_alg(d_cfg.N, d_cfg.H, d_cfg.Dk, d_cfg.Dv)
@@ -255,13 +293,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "kernel": "gdn_prefill_kernel<bf16, C=64, Dk=128>",
-                     "ms_per_launch": round(ms_launch, 4),
-                     "alg_bytes_per_launch": alg_bytes},
-        "mfma": {"flops_alg_per_launch": alg_flops,
-                 "tflops_achieved": alg_flops / (ms_launch * 1e-3) / 1e12,
+                     "kernel": "gdn_recurrence_kernel<C=64, Dk=128>",
+                     "ms_per_launch": round(ms_rec, 4),
+                     "alg_bytes_per_launch": rec_bytes},
+        "prep_kernel": {"kernel": "gdn_chunk_prep_kernel<C=64, Dk=128>", "ms_per_launch": round(ms_prep, 4),
+                        "alg_bytes_per_launch": prep_bytes,
+                        "achieved_GBps": prep_bytes / (ms_prep * 1e-3) / 1e9,
+                        "hbm_frac": prep_bytes / (ms_prep * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                        "traffic": measured_traffic("prefill_32k_prep")},
+        "step_hbm": {"alg_bytes_per_step": alg_bytes, "achieved_GBps": alg_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac": alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "mfma": {"flops_alg_per_step": alg_flops,
+                 "tflops_achieved": alg_flops / (ms_step * 1e-3) / 1e12,
                  "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": alg_flops / (ms_launch * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                 "frac": alg_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "decode": {"workload": d_cfg.name, "ms_per_step": round(d_ms, 4),
                    "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
                    "state_GBps": d_state / (d_ms * 1e-3) / 1e9,

@@ -95,6 +95,36 @@ GDN_API size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int6
                                    int64_t Dv, int64_t chunk, gdn_dtype dtype);
 
 /*
+ * The two stages of gdn_prefill_fwd for bf16 inputs, for callers that want to
+ * schedule or time them apart (one after the other on a stream, they are
+ * exactly gdn_prefill_fwd).  Arguments mean what they mean there.
+ *
+ * gdn_prefill_prepare -- the part of each chunk that depends on neither the
+ * state nor v (decay prefix, (I + A)^-1 diag(beta), the masked Q K^T of the
+ * chunk form of eqs (1)-(4)), for every (sequence, head, chunk) in parallel,
+ * written into `workspace` (gdn_prefill_workspace_bytes(..., GDN_BF16) bytes,
+ * 256-byte aligned).  q, k: [B, T, H, Dk] bf16; alpha, beta: [B, T, H].
+ *
+ * gdn_prefill_recurrence -- the state recurrence over the chunks, reading the
+ * workspace written by gdn_prefill_prepare for the same q, k, alpha, beta and
+ * sizes (not checked: other contents give meaningless output, never an
+ * out-of-bounds access).  q, k, v, initial_state, y, final_state as in
+ * gdn_prefill_fwd, bf16 inputs.
+ *
+ * Errors as gdn_prefill_fwd's; on a non-OK status nothing was launched.
+ */
+GDN_API gdn_status gdn_prefill_prepare(const void *q, const void *k, const float *alpha,
+                                       const float *beta, int64_t B, int64_t T, int64_t H,
+                                       int64_t Dk, int64_t chunk, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+GDN_API gdn_status gdn_prefill_recurrence(const void *q, const void *k, const void *v,
+                                          const float *initial_state, float *y,
+                                          float *final_state, int64_t B, int64_t T, int64_t H,
+                                          int64_t Dk, int64_t Dv, int64_t chunk,
+                                          const void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/*
  * gdn_decode_step -- one new token for each of N independent sequences: the
  * single-token form of eqs (1)-(4) applied to a stored state, updated in place
  * (the fixed-size state that summarises the prefix).

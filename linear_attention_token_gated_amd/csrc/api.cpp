@@ -101,40 +101,50 @@ size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, 
     return gdn::prefill_workspace_bytes(B, T, H, chunk, true);
 }
 
-gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const float *alpha,
-                           const float *beta, const float *initial_state, float *y,
-                           float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk,
-                           int64_t Dv, int64_t chunk, gdn_dtype dtype, void *workspace,
-                           size_t workspace_bytes, hipStream_t stream)
+namespace {
+
+constexpr int STAGE_PREP = 1, STAGE_REC = 2;
+
+// gdn_prefill_fwd and its two stages: `stages` selects the chunk preparation
+// (bf16 only), the recurrence, or both; `fn` names the entry point in errors.
+gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, const float *initial_state, float *y,
+                        float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                        int64_t chunk, gdn_dtype dtype, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream)
 {
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0)
-        return fail(GDN_ERR_SHAPE, "gdn_prefill_fwd: negative size (B=%lld T=%lld H=%lld Dk=%lld Dv=%lld chunk=%lld)",
+        return fail(GDN_ERR_SHAPE, "%s: negative size (B=%lld T=%lld H=%lld Dk=%lld Dv=%lld chunk=%lld)", fn,
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv, (long long)chunk);
     if (dtype != GDN_F32 && dtype != GDN_BF16)
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: dtype %d", (int)dtype);
+        return fail(GDN_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
     if (!is_pow2_dim(Dk) || !is_pow2_dim(Dv))
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: Dk=%lld Dv=%lld (supported: 16, 32, 64, 128)",
+        return fail(GDN_ERR_UNSUPPORTED, "%s: Dk=%lld Dv=%lld (supported: 16, 32, 64, 128)", fn,
                     (long long)Dk, (long long)Dv);
     if (chunk != 16 && chunk != 32 && chunk != 64)
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: chunk=%lld (supported: 16, 32, 64)", (long long)chunk);
+        return fail(GDN_ERR_UNSUPPORTED, "%s: chunk=%lld (supported: 16, 32, 64)", fn, (long long)chunk);
     int64_t n_tok, n_qk, n_v, n_s;
     if (!count(&n_tok, {B, T, H}) || !count(&n_qk, {B, T, H, Dk}) || !count(&n_v, {B, T, H, Dv}) ||
         !count(&n_s, {B, H, Dk, Dv}) || n_qk > INT64_MAX / 4 || n_v > INT64_MAX / 4)
-        return fail(GDN_ERR_SHAPE, "gdn_prefill_fwd: sizes overflow");
+        return fail(GDN_ERR_SHAPE, "%s: sizes overflow", fn);
     if (B * H > (int64_t)1 << 26 || (B * H) * (Dv / 16) > INT32_MAX)
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: B*H=%lld too large for one launch", (long long)(B * H));
+        return fail(GDN_ERR_UNSUPPORTED, "%s: B*H=%lld too large for one launch", fn, (long long)(B * H));
     // bf16 chunks are copied with 32-bit byte offsets within one chunk of rows
     if (dtype == GDN_BF16 && chunk * H * (Dk > Dv ? Dk : Dv) * 2 >= ((int64_t)1 << 31))
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fwd: H=%lld too large for bf16 (chunk * H * max(Dk, Dv) * 2 must stay below 2^31)",
+        return fail(GDN_ERR_UNSUPPORTED, "%s: H=%lld too large for bf16 (chunk * H * max(Dk, Dv) * 2 must stay below 2^31)", fn,
                     (long long)H);
-    const bool need_io = n_tok > 0;
-    if (need_io && (!q || !k || !v || !alpha || !beta || !y))
-        return fail(GDN_ERR_NULL, "gdn_prefill_fwd: q, k, v, alpha, beta and y are required");
+    if (stages != (STAGE_PREP | STAGE_REC) && dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "%s: the separate stages exist for bf16 inputs only", fn);
+    if (n_tok > 0) {
+        if (!q || !k) return fail(GDN_ERR_NULL, "%s: q and k are required", fn);
+        if ((stages & STAGE_PREP) && (!alpha || !beta)) return fail(GDN_ERR_NULL, "%s: alpha and beta are required", fn);
+        if ((stages & STAGE_REC) && (!v || !y)) return fail(GDN_ERR_NULL, "%s: v and y are required", fn);
+    }
     const void *ptrs[] = {q, k, v, alpha, beta, initial_state, y, final_state};
     const char *names[] = {"q", "k", "v", "alpha", "beta", "initial_state", "y", "final_state"};
     for (int i = 0; i < 8; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
-            return fail(GDN_ERR_ALIGN, "gdn_prefill_fwd: %s is not 16-byte aligned", names[i]);
+            return fail(GDN_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
     const size_t esz = dtype == GDN_BF16 ? 2 : 4;
     const Range ry{y, (size_t)n_v * 4, "y"};
     const Range inputs[] = {{q, (size_t)n_qk * esz, "q"}, {k, (size_t)n_qk * esz, "k"},
@@ -142,24 +152,24 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
                             {beta, (size_t)n_tok * 4, "beta"}, {initial_state, (size_t)n_s * 4, "initial_state"},
                             {final_state, (size_t)n_s * 4, "final_state"}};
     for (const Range &r : inputs)
-        if (overlap(ry, r)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: y overlaps %s", r.name);
+        if (overlap(ry, r)) return fail(GDN_ERR_ALIAS, "%s: y overlaps %s", fn, r.name);
     const Range rs{final_state, (size_t)n_s * 4, "final_state"};
     for (int i = 0; i < 5; ++i)
-        if (overlap(rs, inputs[i])) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: final_state overlaps %s", inputs[i].name);
+        if (overlap(rs, inputs[i])) return fail(GDN_ERR_ALIAS, "%s: final_state overlaps %s", fn, inputs[i].name);
     if (final_state != initial_state && overlap(rs, inputs[5]))
-        return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: final_state partially overlaps initial_state");
+        return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
     const size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
-            return fail(GDN_ERR_WORKSPACE, "gdn_prefill_fwd: workspace of %zu bytes needed, %zu given", need,
+            return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                         workspace ? workspace_bytes : (size_t)0);
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-            return fail(GDN_ERR_ALIGN, "gdn_prefill_fwd: workspace is not 256-byte aligned");
+            return fail(GDN_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
         const Range rw{workspace, need, "workspace"};
-        if (overlap(rw, ry)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps y");
-        if (overlap(rw, rs)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps final_state");
+        if (overlap(rw, ry)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps y", fn);
+        if (overlap(rw, rs)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps final_state", fn);
         for (const Range &r : inputs)
-            if (overlap(rw, r)) return fail(GDN_ERR_ALIAS, "gdn_prefill_fwd: workspace overlaps %s", r.name);
+            if (overlap(rw, r)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps %s", fn, r.name);
     }
 
     gdn::PrefillArgs a;
@@ -169,7 +179,37 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
     a.q_tok_stride = H * Dk; a.k_tok_stride = H * Dk; a.v_tok_stride = H * Dv;
     a.bf16 = dtype == GDN_BF16;
     a.ws = need > 0 ? workspace : nullptr;
-    return hip_status(gdn::launch_prefill(a, stream), "gdn_prefill_fwd launch");
+    return hip_status(gdn::launch_prefill(a, stream, stages), fn);
+}
+
+}  // namespace
+
+gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *beta, const float *initial_state, float *y,
+                           float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                           int64_t Dv, int64_t chunk, gdn_dtype dtype, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_impl("gdn_prefill_fwd", STAGE_PREP | STAGE_REC, q, k, v, alpha, beta, initial_state, y,
+                        final_state, B, T, H, Dk, Dv, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_prepare(const void *q, const void *k, const float *alpha, const float *beta,
+                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t chunk,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_impl("gdn_prefill_prepare", STAGE_PREP, q, k, nullptr, alpha, beta, nullptr, nullptr, nullptr,
+                        B, T, H, Dk, Dk, chunk, GDN_BF16, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_recurrence(const void *q, const void *k, const void *v, const float *initial_state,
+                                  float *y, float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                  int64_t Dv, int64_t chunk, const void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    return prefill_impl("gdn_prefill_recurrence", STAGE_REC, q, k, v, nullptr, nullptr, initial_state, y,
+                        final_state, B, T, H, Dk, Dv, chunk, GDN_BF16, const_cast<void *>(workspace),
+                        workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,

@@ -31,7 +31,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// stages: 1 = chunk preparation (bf16), 2 = recurrence, 3 = both
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages = 3);
 
 // bf16 prefill: per-chunk preparation into the workspace, then the recurrence
 size_t prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t chunk, bool bf16);

@@ -15,27 +15,18 @@
 //
 // Columns of S, V, Y are independent (e_t[j] only involves column j of S and
 // v_t[j]), so each workgroup owns one 16-column slice of Dv for one (b, h) and
-// carries that slice of S through every chunk in MFMA accumulator registers
-// (fp32 master copy).  Within a chunk:
+// carries that slice of S through every chunk in MFMA accumulator registers.
+// This file holds the fp32-input path, all of it in one kernel of 4
+// wavefronts on fp32 MFMA (16x16x4); within a chunk:
 //   1. stage K, Q (Dk wide), the V slice, alpha, beta into LDS; prefix-sum ln alpha
-//   2. Gram tiles K K^T and Q K^T on MFMA -> A (fp32 diagonal blocks, operand
-//      precision off-diagonal blocks) and P
-//   3. K S and Q S on MFMA -> R
+//   2. Gram tiles K K^T and Q K^T -> A and P
+//   3. K S and Q S -> R
 //   4. (I + A)^-1 of each 16x16 diagonal block by in-register forward
 //      substitution (DPP row broadcast), then block forward substitution for U
-//      on MFMA, chaining accumulator tiles directly as the next B operand
-//   5. Y = diag(e^G) Q S + P U -> y (fp32);  S <- e^{G_C} S + K^T (e^{G_C-G} U)
+//   5. Y = diag(e^G) Q S + P U -> y;  S <- e^{G_C} S + K^T (e^{G_C-G} U)
 // Ragged tails are padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
-//
-// Precision (bf16 inputs): q, k, v are exact bf16 MFMA operands and every
-// product accumulates in fp32.  The operands that are computed in fp32 and
-// feed an MFMA -- the state S, P, the substitution right-hand side Z, U and
-// the decayed U of the state update -- are carried as a bf16 pair hi + lo with
-// hi = bf16(x), lo = bf16(x - hi), and each product with them is summed over
-// the pair (hi*hi + hi*lo + lo*hi where both sides are split).  Rounding any of
-// them to a single bf16 costs about 1e-2 in max|err|/RMS(y) at the 4K workload;
-// the pair keeps the whole path near 2e-3.  The diagonal-block inverses and
-// the off-diagonal blocks of A are single bf16 (they contribute ~2e-3).
+// bf16 inputs take the two-kernel path of chunk_prep.hip and recurrence.hip;
+// launch_prefill below dispatches between them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -506,20 +497,22 @@ __global__ void copy_or_zero_state(const float *__restrict__ s0, float *__restri
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages)
 {
     if (a.B * a.H == 0) return hipSuccess;
     if (a.T == 0) {
-        if (!a.sT || a.sT == a.s0) return hipSuccess;
+        if (!(stages & 2) || !a.sT || a.sT == a.s0) return hipSuccess;
         const int64_t n = a.B * a.H * a.Dk * a.Dv;
         hipLaunchKernelGGL(copy_or_zero_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.s0, a.sT, n);
         return hipGetLastError();
     }
     if (a.bf16) {
         // per-chunk preparation of every (b, h, chunk), then the recurrence
-        hipError_t e = launch_chunk_prep(a, stream);
-        if (e != hipSuccess) return e;
-        return launch_recurrence(a, stream);
+        if (stages & 1) {
+            const hipError_t e = launch_chunk_prep(a, stream);
+            if (e != hipSuccess) return e;
+        }
+        return (stages & 2) ? launch_recurrence(a, stream) : hipSuccess;
     }
     return launch_c<float>(a, stream);
 }
