@@ -89,37 +89,51 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int ln = lane & 15, lg = lane >> 4;
-
-    const int64_t rec = blockIdx.x;                 // ((b * H) + h) * NC + c
-    const int64_t NC = (p.T + C - 1) / C;
-    const int64_t c = rec % NC, bh = rec / NC;
-    const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t t0 = c * C;
     const __bf16 *kg = static_cast<const __bf16 *>(p.k);
     const __bf16 *qg = static_cast<const __bf16 *>(p.q);
-    char *out = static_cast<char *>(p.ws) + rec * Rec::BYTES;
+    const int64_t NC = (p.T + C - 1) / C;
+    const int64_t BH = p.BH, nwork = BH * NC;
 
-    // ---- 1. K and Q rows of the chunk (zero past the end), gates and decay scan.
-    //         Every load is issued before the first is used (rows past the end
-    //         read the last row and are zeroed), so the chunk costs one memory
-    //         round trip.
+    // Work items are taken chunk-major, so the workgroups running at one time
+    // share the rows of K, Q and the gates.  With a grid that is a multiple of
+    // 8, the items of chunk c go to the workgroups with id = c mod 8, which the
+    // hardware places on one XCD: every gate row is then fetched into one L2.
+    // The rows of the next item are loaded into registers while the current
+    // one is computed.
+    const bool xcd = gridDim.x % 8 == 0;
+    const int64_t gx = xcd ? blockIdx.x & 7 : 0;                   // chunk residue of this workgroup
+    const int64_t stride = xcd ? gridDim.x >> 3 : gridDim.x;       // workgroups per residue
+    const int64_t mine = xcd ? (NC > gx ? (NC - gx + 7) / 8 : 0) * BH : nwork;   // items of this residue
+    // item i of this residue -> (chunk, bh)
+    auto item_c = [&](int64_t i) { return xcd ? gx + 8 * (i / BH) : i / BH; };
     constexpr int NLD = (C * VPR + PREP_THREADS - 1) / PREP_THREADS;
     f32x4 kv[NLD], qv[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int vi = tid + i * PREP_THREADS;
-        const int r = (vi < C * VPR ? vi : 0) / VPR, col = (vi % VPR) * 8;
-        const int64_t tok = b * p.T + (t0 + r < p.T ? t0 + r : p.T - 1);
-        kv[i] = *reinterpret_cast<const f32x4 *>(kg + tok * p.ks + h * DK + col);
-        qv[i] = *reinterpret_cast<const f32x4 *>(qg + tok * p.qs + h * DK + col);
-    }
-    const bool real = lane < C && t0 + lane < p.T;
-    const int64_t gi = (b * p.T + (real ? t0 + lane : 0)) * p.H + h;
     float al = 1.f, be = 0.f;
-    if (wave == 0) {
-        al = p.alpha[gi];
-        be = p.beta[gi];
-    }
+    auto fetch = [&](int64_t i) {
+        const int64_t c = item_c(i), bh = i % BH, b = bh / p.H, h = bh % p.H, t0 = c * C;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int vi = tid + i * PREP_THREADS;
+            const int r = (vi < C * VPR ? vi : 0) / VPR, col = (vi % VPR) * 8;
+            const int64_t tok = b * p.T + (t0 + r < p.T ? t0 + r : p.T - 1);   // rows past the end: zeroed later
+            kv[i] = *reinterpret_cast<const f32x4 *>(kg + tok * p.ks + h * DK + col);
+            qv[i] = *reinterpret_cast<const f32x4 *>(qg + tok * p.qs + h * DK + col);
+        }
+        if (wave == 0) {
+            const int64_t gi = (b * p.T + (lane < C && t0 + lane < p.T ? t0 + lane : 0)) * p.H + h;
+            al = p.alpha[gi];
+            be = p.beta[gi];
+        }
+    };
+    const int64_t first = xcd ? blockIdx.x >> 3 : blockIdx.x;
+    if (first < mine) fetch(first);
+
+    for (int64_t i = first; i < mine; i += stride) {
+    const int64_t c = item_c(i), bh = i % BH;
+    const int64_t t0 = c * C;
+    char *out = static_cast<char *>(p.ws) + (bh * NC + c) * Rec::BYTES;
+
+    // ---- 1. K and Q rows of the chunk (zero past the end), gates and decay scan
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int vi = tid + i * PREP_THREADS;
@@ -131,6 +145,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         }
     }
     if (wave == 0) {
+        const bool real = lane < C && t0 + lane < p.T;
         al = real ? al : 1.f;
         be = real ? be : 0.f;
         const float g2 = wave_inclusive_sum(lane < C ? __builtin_amdgcn_logf(al) : 0.f, lane);
@@ -151,50 +166,81 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
             if (lane < C) Ebs[rb * C + lane] = lane < 16 * rb ? __builtin_amdgcn_exp2f(gref - g2) : 0.f;
         }
     }
+    // the next item's rows (the registers of this one are consumed)
+    if (i + stride < mine) fetch(i + stride);
     __syncthreads();
 
     // ---- 2. Gram blocks: A (NTRI blocks, fp32 into LDS) and P (NTRI blocks, bf16
     //         hi/lo fragments into the record).  Each is computed transposed, D =
     //         K_cb X_rb^T, so lane (ln, lg) holds row r = 16 rb + ln, columns
-    //         j = 16 cb + 4 lg + e: the A-operand fragment of that block.
-    for (int job = wave; job < 2 * NTRI; job += 4) {
-        const bool isP = job >= NTRI;
-        const int idx = isP ? job - NTRI : job;
-        int rb = 0;
-        while (tri_idx(rb + 1, 0) <= idx) ++rb;
-        const int cb = idx - tri_idx(rb, 0);
+    //         j = 16 cb + 4 lg + e: the A-operand fragment of that block.  A wave
+    //         takes whole block rows (the X_rb fragments are loaded once per row):
+    //         A row NB-1-m with P row m, or P row NB-1-m with A row m, so that
+    //         every wave has NB + 1 blocks.
+    auto gram_row = [&](auto isP_c, auto rb_c) {
+        constexpr bool isP = decltype(isP_c)::value;
+        constexpr int rb = decltype(rb_c)::value;
         const __bf16 *Xs = isP ? Qs : Ks;
-        f32x4 acc = zero4();
+        FDK fb[NK];
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const FDK fa = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * cb, kk * KS_DK, lane);
-            const FDK fb = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * rb, kk * KS_DK, lane);
-            acc = FDK::mma(fa, fb, acc);
-        }
-        const int r = 16 * rb + ln, j0 = 16 * cb + 4 * lg;
-        f32x4 val;
-        if (rb == cb) {
-            const float Gr = Gs[r];
-            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gs + j0);
+        for (int kk = 0; kk < NK; ++kk) fb[kk] = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * rb, kk * KS_DK, lane);
+        const int r = 16 * rb + ln;
+        const float Gr = Gs[r], Ear = Eas[r], ber = Bes[r];
+        static_for<rb + 1>([&](auto cb_c) {
+            constexpr int cb = decltype(cb_c)::value;
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool keep = r > j0 + e || (isP && r == j0 + e);
-                val[e] = keep ? __builtin_amdgcn_exp2f(Gr - Gj[e]) * acc[e] : 0.f;
+            for (int kk = 0; kk < NK; ++kk)
+                acc = FDK::mma(frag_rows<__bf16, KS_DK>(Ks, KP, 16 * cb, kk * KS_DK, lane), fb[kk], acc);
+            const int j0 = 16 * cb + 4 * lg;
+            f32x4 val;
+            if constexpr (rb == cb) {
+                const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gs + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = r > j0 + e || (isP && r == j0 + e);
+                    val[e] = keep ? __builtin_amdgcn_exp2f(Gr - Gj[e]) * acc[e] : 0.f;
+                }
+            } else {
+                // r > j: 2^(G_r - G_j) = 2^(G_r - G_{16 rb}) 2^(G_{16 rb} - G_j), both factors <= 1
+                const f32x4 eb = *reinterpret_cast<const f32x4 *>(Ebs + rb * C + j0);
+                val = acc * eb * Ear;
             }
-        } else {
-            // r > j: 2^(G_r - G_j) = 2^(G_r - G_{16 rb}) 2^(G_{16 rb} - G_j), both factors <= 1
-            const f32x4 eb = *reinterpret_cast<const f32x4 *>(Ebs + rb * C + j0);
-            val = acc * eb * Eas[r];
+            constexpr int idx = rb * (rb + 1) / 2 + cb;
+            if constexpr (isP) {
+                bf16x4 hv, lv;
+                split4(val, hv, lv);
+                bf16x4 *pf = reinterpret_cast<bf16x4 *>(out + Rec::oP) + idx * 128;
+                pf[lane] = hv;
+                pf[64 + lane] = lv;
+            } else {
+                *reinterpret_cast<f32x4 *>(As + (idx * 16 + ln) * AP + 4 * lg) = val * ber;
+            }
+        });
+    };
+    using TF = std::true_type;
+    using FF = std::false_type;
+    auto gram_wave = [&](auto w_c) {
+        constexpr int w = decltype(w_c)::value, m = w / 2, hi = NB - 1 - m;
+        constexpr bool odd = w % 2;
+        if constexpr (m < (NB + 1) / 2) {
+            if constexpr (hi == m) {
+                if constexpr (odd) gram_row(TF{}, std::integral_constant<int, m>{});
+                else gram_row(FF{}, std::integral_constant<int, m>{});
+            } else if constexpr (odd) {
+                gram_row(TF{}, std::integral_constant<int, hi>{});
+                gram_row(FF{}, std::integral_constant<int, m>{});
+            } else {
+                gram_row(FF{}, std::integral_constant<int, hi>{});
+                gram_row(TF{}, std::integral_constant<int, m>{});
+            }
         }
-        if (isP) {
-            bf16x4 hv, lv;
-            split4(val, hv, lv);
-            bf16x4 *pf = reinterpret_cast<bf16x4 *>(out + Rec::oP) + idx * 128;
-            pf[lane] = hv;
-            pf[64 + lane] = lv;
-        } else {
-            *reinterpret_cast<f32x4 *>(As + (idx * 16 + ln) * AP + 4 * lg) = val * Bes[r];
-        }
+    };
+    switch (wave) {
+    case 0: gram_wave(std::integral_constant<int, 0>{}); break;
+    case 1: gram_wave(std::integral_constant<int, 1>{}); break;
+    case 2: gram_wave(std::integral_constant<int, 2>{}); break;
+    default: gram_wave(std::integral_constant<int, 3>{}); break;
     }
     __syncthreads();
 
@@ -260,12 +306,28 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         tf[lane] = hv;
         tf[64 + lane] = lv;
     }
+    // T reuses the K/Q rows: the next item's rows go there after this barrier
+    __syncthreads();
+    }
+}
+
+// Workgroups of the persistent preparation grid: three per CU (the LDS of
+// one workgroup allows three), never more than there are records.
+int prep_grid(int64_t nrec)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t g = (int64_t)cus * 3;
+    return (int)(nrec < g ? nrec : g);
 }
 
 template <int C, int DK>
 hipError_t launch_prep_t(const PrepParams &p, int64_t nrec, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gdn_chunk_prep_kernel<C, DK>), dim3((unsigned)nrec), dim3(PREP_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((gdn_chunk_prep_kernel<C, DK>), dim3((unsigned)prep_grid(nrec)), dim3(PREP_THREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -287,7 +349,7 @@ hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream)
 {
     PrepParams p;
     p.q = a.q; p.k = a.k; p.alpha = a.alpha; p.beta = a.beta; p.ws = a.ws;
-    p.T = a.T; p.H = a.H;
+    p.T = a.T; p.H = a.H; p.BH = a.B * a.H;
     p.qs = a.q_tok_stride; p.ks = a.k_tok_stride;
     const int64_t nrec = a.B * a.H * ((a.T + a.chunk - 1) / a.chunk);
     switch (a.chunk) {

@@ -40,6 +40,7 @@ struct PrepParams {
     const float *alpha, *beta;
     void *ws;
     int64_t T, H;
+    int64_t BH;              // B * H
     int64_t qs, ks;          // token strides (elements)
 };
 
