@@ -232,7 +232,9 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
     constexpr int KS_DK = L::KS_DK, KS_C = L::KS_C, NK = DK / KS_DK;
 
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
-    auto cbuf = [&](int64_t c) { return smem + (c % NBUF) * L::CBUF; };
+    // chunk buffer i (chunk c lives in buffer c % NBUF; the loops track the index)
+    auto cbuf = [&](int i) { return smem + i * L::CBUF; };
+    auto next_buf = [](int i) { return i == NBUF - 1 ? 0 : i + 1; };
     __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
     __bf16 *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
     bf16x4 *Rh = reinterpret_cast<bf16x4 *>(smem + L::oRh);
@@ -301,9 +303,9 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
 
         __syncthreads();                        // chunk 0 staged, S^T written
 
-        auto iter = [&](auto set_c, int64_t c) {
+        auto iter = [&](auto set_c, int64_t c, int cbi) {
             constexpr int s_ = decltype(set_c)::value;
-            const char *cb = cbuf(c);
+            const char *cb = cbuf(cbi);
             const __bf16 *Ks = reinterpret_cast<const __bf16 *>(cb + L::cK);
             const float *dec = reinterpret_cast<const float *>(cb + L::cDec);
             // ---- phase 1: R_rb = V_rb - diag(EG) K_rb S, and diag(EG) Q_rb S for
@@ -312,26 +314,28 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 const __bf16 *Vs = reinterpret_cast<const __bf16 *>(cb + L::cV);
                 const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * rb + 4 * lg);
+                // software-pipelined: the fragments of k-step kk + 2 are read while
+                // the MFMAs of step kk run (the scheduling barriers keep that order)
                 FDK kf[NK], qf[NK], sh[NK], slo[NK];
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
+                auto ld = [&](int kk) {
                     kf[kk] = frag_kq<KS_DK, DK>(Ks, 16 * rb, kk * KS_DK, lane);
                     sh[kk] = frag_rows<__bf16, KS_DK>(STh, KPS, 0, kk * KS_DK, lane);
                     slo[kk] = frag_rows<__bf16, KS_DK>(STl, KPS, 0, kk * KS_DK, lane);
-                }
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) qf[kk] = frag_kq<KS_DK, DK>(Qs, 16 * rb, kk * KS_DK, lane);
+                    qf[kk] = frag_kq<KS_DK, DK>(Qs, 16 * rb, kk * KS_DK, lane);
+                };
+                ld(0);
+                if constexpr (NK > 1) ld(1);
                 f32x4 ks_h = zero4(), ks_l = zero4(), qs_h = zero4(), qs_l = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
+                static_for<NK>([&](auto kk_c) {
+                    constexpr int kk = decltype(kk_c)::value;
+                    __builtin_amdgcn_sched_barrier(0);
                     ks_h = FDK::mma(kf[kk], sh[kk], ks_h);
                     ks_l = FDK::mma(kf[kk], slo[kk], ks_l);
-                }
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
                     qs_h = FDK::mma(qf[kk], sh[kk], qs_h);
                     qs_l = FDK::mma(qf[kk], slo[kk], qs_l);
-                }
+                    if constexpr (kk + 2 < NK) ld(kk + 2);
+                });
+                __builtin_amdgcn_sched_barrier(0);
                 f32x4 rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -409,11 +413,14 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             __syncthreads();
         };
         int64_t c = 0;
+        int cbi = 0;
         for (; c + 1 < NC; c += 2) {
-            iter(S0{}, c);
-            iter(S1{}, c + 1);
+            iter(S0{}, c, cbi);
+            cbi = next_buf(cbi);
+            iter(S1{}, c + 1, cbi);
+            cbi = next_buf(cbi);
         }
-        if (c < NC) iter(S0{}, c);
+        if (c < NC) iter(S0{}, c, cbi);
 
         if (p.sT) {
             float *sT = p.sT + bh * (int64_t)DK * Dv;
@@ -544,8 +551,8 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 load_to_lds(br, (uint32_t)(L::NTRI * 1024), (uint32_t)(t * 1024 + lane * 16), dst + t * 1024);
             });
         };
-        // loads [I0, I1) of chunk c into chunk buffer cb_idx % 3
-        auto stage = [&](int64_t c, int64_t cb_idx, auto i0_c, auto i1_c) {
+        // loads [I0, I1) of chunk c into chunk buffer cb_idx
+        auto stage = [&](int64_t c, int cb_idx, auto i0_c, auto i1_c) {
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
             const int64_t c0 = c * C;
             const int64_t valid = T - c0 < C ? T - c0 : C;                 // rows of this chunk
@@ -583,6 +590,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         stage(clampc(1), 1, Z{}, PJ{});
         wait_vmcnt<JW>();
         __builtin_amdgcn_s_barrier();
+        int nbi = 2 % NBUF;                         // buffer of chunk c + 2
         for (int64_t c = 0; c < NC; ++c) {
             // chunk c+2 two iterations ahead into buffer (c+2) % 3, whose last reader
             // was iteration c-1 (past the end, the last chunk again: that buffer is
@@ -592,11 +600,12 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             // iteration c-1
             stage_t(clampc(c + 1), c + 1);
             const int64_t cn = clampc(c + 2);
-            stage(cn, c + 2, Z{}, P1{});
+            stage(cn, nbi, Z{}, P1{});
             __builtin_amdgcn_s_barrier();
-            stage(cn, c + 2, P1{}, P2{});
+            stage(cn, nbi, P1{}, P2{});
             __builtin_amdgcn_s_barrier();
-            stage(cn, c + 2, P2{}, PJ{});
+            stage(cn, nbi, P2{}, PJ{});
+            nbi = next_buf(nbi);
             // T' of chunk c+1 and chunk c+1 must be complete before the barrier
             // that starts iteration c+1; chunk c+2 (the last JW loads) may still
             // be in flight
