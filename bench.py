@@ -218,8 +218,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
-                    help="for hardware-counter passes: two prefill launches, two decode steps and a "
-                         "1 GiB device copy of known size (the copy calibrates FETCH_SIZE / WRITE_SIZE)")
+                    help="for hardware-counter passes: two prefill launches, two decode steps, two layer "
+                         "calls and a 1 GiB device copy of known size (the copy calibrates FETCH_SIZE / "
+                         "WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -236,6 +237,7 @@ def main():
         pargs = argparse.Namespace(steps=1, warmup=1)
         bench_prefill(pargs, torch, gdn, wl)
         bench_decode(pargs, torch, gdn, wl)
+        bench_layer(pargs, torch, gdn, wl)
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)

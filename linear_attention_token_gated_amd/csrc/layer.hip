@@ -127,10 +127,15 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-
 __device__ __forceinline__ float softplusf_(float x) { return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
 
 // ---------------------------------------------------------------------------
-// Prologue: one workgroup per token.  Each thread handles 8 consecutive
-// channels (one 16-byte vector) of the H*(2Dk+Dv) q|k|v channels; a q or k
-// head is Dk/8 consecutive lanes, reduced with xor-shuffles for its L2 norm.
+// Prologue: one workgroup per tile of PRO_TT consecutive tokens of one
+// sequence and 256 vectors of channels.  Each thread owns 8 consecutive
+// channels (one 16-byte vector) of the H*(2Dk+Dv) q|k|v channels and walks the
+// tile's tokens in order, keeping the last conv_k-1 inputs in registers, so
+// every input row is read once (plus conv_k-1 rows before the tile).  A q or
+// k head is Dk/8 consecutive lanes, reduced with xor-shuffles for its L2 norm.
 // ---------------------------------------------------------------------------
+constexpr int PRO_TT = 32;
+
 template <int DK>
 __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__ pre, const __bf16 *__restrict__ conv_w,
                                                        const float *__restrict__ ab, const float *__restrict__ Aexp,
@@ -138,50 +143,92 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
                                                        float *__restrict__ alpha, float *__restrict__ beta, int64_t T,
                                                        int H, int nqkv, int conv_k)
 {
-    const int64_t row = blockIdx.x;          // b*T + t
-    const int64_t t = row % T;
+    const int64_t ntile = (T + PRO_TT - 1) / PRO_TT;
+    const int64_t b = blockIdx.x / ntile, t0 = (blockIdx.x % ntile) * PRO_TT;
+    const int64_t tend = t0 + PRO_TT < T ? t0 + PRO_TT : T;
     const int nvec = nqkv / 8;
     const int nqk_vec = 2 * H * DK / 8;      // vectors holding q and k channels
     constexpr int HV = DK / 8;               // vectors per q/k head (power of two, <= 16)
-
-    for (int base = 0; base < nvec; base += 256) {
-        const int vi = base + threadIdx.x;
-        const bool active = vi < nvec;
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            const int c0 = vi * 8;
-            for (int j = 0; j < conv_k; ++j) {
-                const int64_t lag = conv_k - 1 - j;           // tap j reads token t - lag
-                if (t - lag < 0) continue;
-                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(pre + (row - lag) * nqkv + c0);
-                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(pre + (row - lag) * nqkv + c0 + 4);
-                const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    const int vi = blockIdx.y * 256 + threadIdx.x;
+    const bool active = vi < nvec;
+    const int c0 = active ? vi * 8 : 0;
+    const float scale_qk = vi < nqk_vec;     // 1: an L2-normalised q or k channel
+    auto load8 = [&](int64_t t, float (&x)[8]) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(pre + (b * T + t) * nqkv + c0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(pre + (b * T + t) * nqkv + c0 + 4);
+        x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
+        x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+    };
+    // taps: w[j] multiplies the input of token t - (conv_k - 1 - j)
+    float w[4][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf((float)conv_w[(int64_t)(c0 + e) * conv_k + j], x[e], o[e]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[j][e] = j < conv_k ? (float)conv_w[(int64_t)(c0 + e) * conv_k + j] : 0.f;
+    // win[l - 1] = input of token t - l (zero before the sequence start)
+    float win[3][8];
+#pragma unroll
+    for (int l = 1; l <= 3; ++l) {
+        if (l < conv_k && t0 - l >= 0) {
+            load8(t0 - l, win[l - 1]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[l - 1][e] = 0.f;
+        }
+    }
+    float xn[8];
+    load8(t0, xn);
+    for (int64_t t = t0; t < tend; ++t) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = xn[e];
+        if (t + 1 < tend) load8(t + 1, xn);                // the next row is in flight meanwhile
+        // taps in the order j = 0 .. conv_k-1 (oldest input first); taps before the
+        // sequence start add nothing
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int lag = conv_k - 1 - j;
+            if (j < conv_k && t - lag >= 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = lag == 0 ? x[e] : lag == 1 ? win[0][e] : lag == 2 ? win[1][e] : win[2][e];
+                    o[e] = fmaf(w[j][e], xv, o[e]);
+                }
             }
         }
-        // L2 normalisation of q and k heads (wave-uniform: heads never straddle
-        // the q|k / v boundary and vector groups are lane-aligned)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            win[2][e] = win[1][e];
+            win[1][e] = win[0][e];
+            win[0][e] = x[e];
+        }
+        // L2 normalisation of q and k heads (heads never straddle the q|k / v
+        // boundary and vector groups are lane-aligned)
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
 #pragma unroll
         for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
         if (active) {
-            const float scale = vi < nqk_vec ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
+            const float scale = scale_qk ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
             f32x4 o0, o1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
-            *reinterpret_cast<f32x4 *>(post + row * nqkv + vi * 8) = o0;
-            *reinterpret_cast<f32x4 *>(post + row * nqkv + vi * 8 + 4) = o1;
+            *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0) = o0;
+            *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0 + 4) = o1;
         }
     }
-    // eq (10) decay and eq (9) write strength for every head of this token
-    for (int hh = threadIdx.x; hh < H; hh += 256) {
-        const float a = ab[row * 2 * H + hh];
-        const float bb = ab[row * 2 * H + H + hh];
-        alpha[row * H + hh] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
-        beta[row * H + hh] = sigmoidf_(bb);
+    // eq (10) decay and eq (9) write strength for every head of the tile's tokens
+    if (blockIdx.y == 0) {
+        for (int64_t i = threadIdx.x; i < (tend - t0) * H; i += 256) {
+            const int64_t row = b * T + t0 + i / H;
+            const int hh = (int)(i % H);
+            const float a = ab[row * 2 * H + hh];
+            const float bb = ab[row * 2 * H + H + hh];
+            alpha[row * H + hh] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
+            beta[row * H + hh] = sigmoidf_(bb);
+        }
     }
 }
 
@@ -255,8 +302,10 @@ hipError_t launch_prologue_dk(const float *pre, const __bf16 *conv_w, const floa
                               const float *b_alpha, float *post, float *alpha, float *beta, int64_t M, int64_t T,
                               int H, int nqkv, int conv_k, hipStream_t s)
 {
-    hipLaunchKernelGGL((prologue_kernel<DK>), dim3((unsigned)M), dim3(256), 0, s, pre, conv_w, ab, A, b_alpha, post,
-                       alpha, beta, T, H, nqkv, conv_k);
+    const int64_t tiles = (M / T) * ((T + PRO_TT - 1) / PRO_TT);   // M = B * T, T > 0
+    const unsigned slabs = (unsigned)((nqkv / 8 + 255) / 256);
+    hipLaunchKernelGGL((prologue_kernel<DK>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab, A,
+                       b_alpha, post, alpha, beta, T, H, nqkv, conv_k);
     return hipGetLastError();
 }
 

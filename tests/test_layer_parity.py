@@ -42,6 +42,17 @@ def test_layer_small(oracle_mod, B, T, hidden, H, Dk, Dv, chunk):
     assert eo <= TOL_BF16 and eS <= TOL_BF16
 
 
+@pytest.mark.parametrize("conv_k", [1, 2, 3])
+def test_layer_conv_widths(oracle_mod, conv_k):
+    """Short convolutions narrower than 4 taps, over a tile boundary of the prologue."""
+    B, T, hidden, H, Dk, Dv, chunk = 2, 70, 128, 2, 32, 32, 16
+    print(f"case: layer B={B} T={T} conv_k={conv_k}", flush=True)
+    inp = wl.layer_inputs(B, T, hidden, H, Dk, Dv, conv_k=conv_k, w_std=0.05, seed=11 + conv_k,
+                          gamma_std=0.1, A_val=0.3, b_alpha_val=-0.5)
+    eo, eS, _ = _run(oracle_mod, inp, B, T, hidden, H, Dk, Dv, chunk)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
 def test_layer_causal_on_gpu(oracle_mod):
     """Changing tokens after t leaves out[:t+1] bit-identical on the GPU."""
     print("case: layer causality", flush=True)
