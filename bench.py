@@ -77,6 +77,16 @@ def decode_alg(N, H, Dk, Dv, in_bytes=2):
     return N * H * per, N * H * 8 * Dk * Dv
 
 
+def layer_decode_alg(N, hidden, H, Dk, Dv, conv_k):
+    """One layer-decode step: the four weight matrices (bf16) and x read once,
+    the conv history (fp32) and the states read and written once, out (fp32)
+    written once; gate and norm vectors are negligible."""
+    nqkv = H * (2 * Dk + Dv)
+    weights = 2 * hidden * (nqkv + H * Dv + 2 * H) + 2 * H * Dv * hidden
+    return (weights + N * hidden * 2 + 2 * N * (conv_k - 1) * nqkv * 4 + 2 * N * H * Dk * Dv * 4
+            + N * hidden * 4)
+
+
 def layer_flops(B, T, hidden, H, Dk, Dv, C):
     M = B * T
     gemm = 2 * M * hidden * (H * (2 * Dk + Dv) + 2 * H + H * Dv) + 2 * M * (H * Dv) * hidden
@@ -195,6 +205,22 @@ def bench_layer(args, torch, gdn, wl):
     return cfg, total_ms, per, steps
 
 
+def bench_layer_decode(args, torch, gdn, wl):
+    cfg = wl.LAYER_DECODE_256
+    inp, cs0, S0 = wl.layer_decode_config_inputs(cfg)
+    names = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
+    params = {n: to_dev(inp[n], torch) for n in names}
+    x = to_dev(inp["x"], torch)[:, 0].contiguous()
+    cs, S = to_dev(cs0, torch), to_dev(S0, torch)
+    out = torch.empty((cfg.B, cfg.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.layer_decode_workspace_bytes(cfg.B, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv),
+                     dtype=torch.uint8, device="cuda")
+    # in place: each step is a valid next step of the same sequences
+    fn = lambda: gdn.layer_decode_step(x, params, cfg.H, cfg.Dk, cfg.Dv, cs, S, out=out, workspace=ws)
+    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
+    return cfg, total_ms, per
+
+
 def cpu_baseline(inp, cfg, wl, sample_T):
     """The oracle, untouched, on the first sample_T tokens of every head."""
     import oracle
@@ -238,6 +264,7 @@ def main():
         bench_prefill(pargs, torch, gdn, wl)
         bench_decode(pargs, torch, gdn, wl)
         bench_layer(pargs, torch, gdn, wl)
+        bench_layer_decode(pargs, torch, gdn, wl)
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -271,6 +298,14 @@ def main():
                  "gemm_tflops_alg": gemm_f / 1e12, "core_tflops_alg": core_f / 1e12,
                  "tflops_achieved": (gemm_f + core_f) / (l_ms * 1e-3) / 1e12,
                  "note": "core runs on fp32 q/k/v (fp32 MFMA); projections bf16 MFMA"}
+
+    ld_cfg, ld_total, ld_per = bench_layer_decode(args, torch, gdn, wl)
+    ld_ms = float(np.mean(ld_per))
+    ld_bytes = layer_decode_alg(ld_cfg.B, ld_cfg.hidden, ld_cfg.H, ld_cfg.Dk, ld_cfg.Dv, ld_cfg.conv_k)
+    layer_decode = {"workload": ld_cfg.name, "ms_per_step": round(ld_ms, 4),
+                    "tokens_per_s": ld_cfg.B / (ld_ms * 1e-3), "alg_bytes_per_step": ld_bytes,
+                    "GBps": ld_bytes / (ld_ms * 1e-3) / 1e9,
+                    "hbm_frac": ld_bytes / (ld_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -316,6 +351,7 @@ def main():
                    "alg_bytes_per_launch": d_bytes,
                    "traffic": measured_traffic("decode_256x32", DECODE_SOURCES)},
         "layer": layer,
+        "layer_decode": layer_decode,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }

@@ -184,6 +184,35 @@ GDN_API gdn_status gdn_layer_fwd(const void *x, const gdn_layer_params *p,
 GDN_API size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H,
                                  int64_t Dk, int64_t Dv, int64_t conv_k, int64_t chunk);
 
+/*
+ * gdn_layer_decode_step -- one new token of gdn_layer_fwd for each of N
+ * sequences, carrying the layer's two pieces of history: the short
+ * convolution's last conv_k-1 inputs and the recurrent state of eqs (1)-(4)
+ * (same page and formulas as gdn_layer_fwd, at T = 1 with the history given).
+ * Running it T times from a zero history gives gdn_layer_fwd on the T tokens.
+ *
+ *   x          [N, hidden] bf16: the new token of each sequence
+ *   p          as in gdn_layer_fwd
+ *   conv_state [N, conv_k-1, H*(2Dk+Dv)] float32, in place: the in-projection
+ *              rows x W_qkv^T of the previous conv_k-1 tokens, oldest first
+ *              (zeros before a sequence starts); shifted by one token and the
+ *              new row appended.  May be NULL when conv_k == 1.
+ *   state      [N, H, Dk, Dv] float32, in place: S_{t-1} -> S_t
+ *   out        [N, hidden] float32
+ *   hidden % 64 == 0; conv_k in [1, 4]; Dk, Dv in {16, 32, 64, 128}.
+ *   workspace: at least gdn_layer_decode_workspace_bytes(...) bytes, 256-byte
+ *   aligned.  out must not overlap any input, state or conv_state; state and
+ *   conv_state must not overlap each other or the inputs.
+ */
+GDN_API gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *p,
+                                         float *conv_state, float *state, float *out,
+                                         int64_t N, int64_t hidden, int64_t H, int64_t Dk,
+                                         int64_t Dv, int64_t conv_k, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+GDN_API size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H,
+                                                int64_t Dk, int64_t Dv);
+
 /* Static description of a status code. */
 GDN_API const char *gdn_status_str(gdn_status s);
 

@@ -29,7 +29,8 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_prepare", "gdn_prefill_recurrence",
-            "gdn_decode_step", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_status_str", "gdn_last_error")
+            "gdn_decode_step", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
+            "gdn_layer_decode_workspace_bytes", "gdn_status_str", "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -74,6 +75,11 @@ def lib():
     L.gdn_layer_fwd.restype = ctypes.c_int
     L.gdn_layer_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64]
     L.gdn_layer_workspace_bytes.restype = sz
+    L.gdn_layer_decode_step.argtypes = [vp, ctypes.POINTER(gdn_layer_params), vp, vp, vp, i64, i64, i64, i64, i64,
+                                        i64, vp, sz, vp]
+    L.gdn_layer_decode_step.restype = ctypes.c_int
+    L.gdn_layer_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    L.gdn_layer_decode_workspace_bytes.restype = sz
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_last_error.argtypes = []
@@ -238,3 +244,36 @@ def layer_fwd(x, params: dict, H: int, Dk: int, Dv: int, initial_state=None, chu
                                B, T, hidden, H, Dk, Dv, conv_k, int(chunk), _ptr(workspace),
                                workspace.numel(), _stream(x.device)))
     return out, final_state
+
+
+def layer_decode_workspace_bytes(N, hidden, H, Dk, Dv) -> int:
+    return int(lib().gdn_layer_decode_workspace_bytes(N, hidden, H, Dk, Dv))
+
+
+def layer_decode_step(x, params: dict, H: int, Dk: int, Dv: int, conv_state, state, out=None, workspace=None):
+    """One new token of the layer for each of N sequences.  x: [N, hidden]
+    bfloat16; conv_state: [N, conv_k-1, H*(2Dk+Dv)] float32 (None when
+    conv_k == 1) and state: [N, H, Dk, Dv] float32, both updated in place.
+    Returns out [N, hidden] float32."""
+    import torch
+    N, hidden = x.shape
+    conv_k = params["conv_w"].shape[1]
+    _need(x, "x", torch.bfloat16)
+    for n in ("W_qkv", "conv_w", "W_ab", "W_gate", "W_o"):
+        _need(params[n], n, torch.bfloat16)
+    for n in ("A", "b_alpha", "norm_gamma"):
+        _need(params[n], n, torch.float32)
+    _need(conv_state, "conv_state", torch.float32)
+    _need(state, "state", torch.float32)
+    if out is None:
+        out = torch.empty((N, hidden), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32)
+    need = layer_decode_workspace_bytes(N, hidden, H, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    p = gdn_layer_params(*(_ptr(params[n]) for n in ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate",
+                                                      "norm_gamma", "W_o")))
+    _check(lib().gdn_layer_decode_step(_ptr(x), ctypes.byref(p), _ptr(conv_state), _ptr(state), _ptr(out),
+                                       N, hidden, H, Dk, Dv, conv_k, _ptr(workspace), workspace.numel(),
+                                       _stream(x.device)))
+    return out

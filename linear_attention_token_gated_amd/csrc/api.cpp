@@ -327,4 +327,80 @@ gdn_status gdn_layer_fwd(const void *x, const gdn_layer_params *p, const float *
     return hip_status(gdn::launch_layer(a, stream), "gdn_layer_fwd launch");
 }
 
+size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
+{
+    if (N < 0 || hidden < 0 || H < 0 || Dk < 0 || Dv < 0) return 0;
+    return gdn::layer_workspace_bytes(N, 1, hidden, H, Dk, Dv);
+}
+
+gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *p, float *conv_state, float *state,
+                                 float *out, int64_t N, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv,
+                                 int64_t conv_k, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0 || hidden < 0 || H < 0 || Dk < 0 || Dv < 0 || conv_k < 0)
+        return fail(GDN_ERR_SHAPE, "gdn_layer_decode_step: negative size");
+    if (!is_pow2_dim(Dk) || !is_pow2_dim(Dv))
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_layer_decode_step: Dk=%lld Dv=%lld (supported: 16, 32, 64, 128)",
+                    (long long)Dk, (long long)Dv);
+    if (conv_k < 1 || conv_k > 4)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_layer_decode_step: conv_k=%lld (supported: 1..4)", (long long)conv_k);
+    if (hidden % 64 != 0 || hidden == 0)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_layer_decode_step: hidden=%lld must be a positive multiple of 64",
+                    (long long)hidden);
+    int64_t n_x, n_s, n_w, n_c;
+    if (!count(&n_x, {N, hidden}) || !count(&n_s, {N, H, Dk, Dv}) || !count(&n_w, {H, 2 * Dk + Dv, hidden}) ||
+        !count(&n_c, {N, conv_k - 1, H, 2 * Dk + Dv}) || n_s > INT64_MAX / 8 || n_c > INT64_MAX / 8)
+        return fail(GDN_ERR_SHAPE, "gdn_layer_decode_step: sizes overflow");
+    if (N * H > INT32_MAX || N > (int64_t)1 << 31)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_layer_decode_step: N*H=%lld too large for one launch",
+                    (long long)(N * H));
+    if (!p) return fail(GDN_ERR_NULL, "gdn_layer_decode_step: params is NULL");
+    if (N > 0 && H > 0) {
+        if (!x || !out || !state || !p->W_qkv || !p->conv_w || !p->W_ab || !p->A || !p->b_alpha || !p->W_gate ||
+            !p->norm_gamma || !p->W_o)
+            return fail(GDN_ERR_NULL, "gdn_layer_decode_step: x, out, state and every parameter are required");
+        if (conv_k > 1 && !conv_state)
+            return fail(GDN_ERR_NULL, "gdn_layer_decode_step: conv_state is required when conv_k > 1");
+    }
+    const void *ptrs[] = {x, out, state, conv_state, p->W_qkv, p->conv_w, p->W_ab, p->A,
+                          p->b_alpha, p->W_gate, p->norm_gamma, p->W_o, workspace};
+    const char *names[] = {"x", "out", "state", "conv_state", "W_qkv", "conv_w", "W_ab", "A",
+                           "b_alpha", "W_gate", "norm_gamma", "W_o", "workspace"};
+    for (int i = 0; i < 13; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GDN_ERR_ALIGN, "gdn_layer_decode_step: %s is not 16-byte aligned", names[i]);
+    const size_t need = gdn::layer_workspace_bytes(N, 1, hidden, H, Dk, Dv);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDN_ERR_WORKSPACE, "gdn_layer_decode_step: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(GDN_ERR_ALIGN, "gdn_layer_decode_step: workspace is not 256-byte aligned");
+    const Range ro{out, (size_t)n_x * 4, "out"};
+    const Range rs{state, (size_t)n_s * 4, "state"};
+    const Range rc{conv_state, (size_t)n_c * 4, "conv_state"};
+    const Range rw{workspace, need, "workspace"};
+    const Range inputs[] = {{x, (size_t)n_x * 2, "x"}, {p->W_qkv, (size_t)n_w * 2, "W_qkv"},
+                            {p->W_o, (size_t)(hidden * H * Dv) * 2, "W_o"},
+                            {p->W_gate, (size_t)(hidden * H * Dv) * 2, "W_gate"},
+                            {p->W_ab, (size_t)(2 * H * hidden) * 2, "W_ab"}};
+    for (const Range &r : inputs) {
+        if (overlap(ro, r)) return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: out overlaps %s", r.name);
+        if (overlap(rs, r)) return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: state overlaps %s", r.name);
+        if (overlap(rc, r)) return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: conv_state overlaps %s", r.name);
+        if (overlap(rw, r)) return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: workspace overlaps %s", r.name);
+    }
+    if (overlap(ro, rs) || overlap(ro, rc) || overlap(ro, rw))
+        return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: out overlaps state, conv_state or workspace");
+    if (overlap(rs, rc) || overlap(rs, rw) || overlap(rc, rw))
+        return fail(GDN_ERR_ALIAS, "gdn_layer_decode_step: state, conv_state and workspace must not overlap");
+
+    gdn::LayerDecodeArgs a;
+    a.x = x; a.W_qkv = p->W_qkv; a.conv_w = p->conv_w; a.W_ab = p->W_ab; a.W_gate = p->W_gate;
+    a.W_o = p->W_o; a.A = p->A; a.b_alpha = p->b_alpha; a.norm_gamma = p->norm_gamma;
+    a.conv_state = conv_state; a.state = state; a.out = out;
+    a.N = N; a.hidden = hidden; a.H = H; a.Dk = Dk; a.Dv = Dv; a.conv_k = conv_k;
+    a.ws = workspace;
+    return hip_status(gdn::launch_layer_decode(a, stream), "gdn_layer_decode_step launch");
+}
+
 }  // extern "C"

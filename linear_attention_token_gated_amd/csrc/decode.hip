@@ -37,7 +37,7 @@ template <typename Tin, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void gdn_decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta,
-    float *__restrict__ state, float *__restrict__ y)
+    float *__restrict__ state, float *__restrict__ y, int H, int64_t qn, int64_t kn, int64_t vn)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
@@ -55,11 +55,13 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void gdn_decode_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(S4 + (rg + RG * i) * CG + cg);
 
+    // sequence n = nh / H, head nh % H; qn, kn, vn: elements between sequences
+    const int64_t n = nh / H, hh = nh % H;
     for (int i = tid; i < DK; i += NT) {
-        sk[i] = to_f32(k[nh * DK + i]);
-        sq[i] = to_f32(q[nh * DK + i]);
+        sk[i] = to_f32(k[n * kn + hh * DK + i]);
+        sq[i] = to_f32(q[n * qn + hh * DK + i]);
     }
-    for (int i = tid; i < DV; i += NT) sv[i] = to_f32(v[nh * DV + i]);
+    for (int i = tid; i < DV; i += NT) sv[i] = to_f32(v[n * vn + hh * DV + i]);
     const float a_t = alpha[nh];
     const float b_t = beta[nh];
     __syncthreads();
@@ -122,7 +124,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream)
     const int64_t grid = a.N * a.H;
     hipLaunchKernelGGL((gdn_decode_kernel<Tin, DK, DV>), dim3((unsigned)grid), dim3(Sh::NT), 0, stream,
                        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.alpha, a.beta,
-                       a.state, a.y);
+                       a.state, a.y, (int)a.H, a.q_seq_stride ? a.q_seq_stride : a.H * DK,
+                       a.k_seq_stride ? a.k_seq_stride : a.H * DK, a.v_seq_stride ? a.v_seq_stride : a.H * DV);
     return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@ struct DecodeArgs {
     float *state, *y;
     int64_t N, H, Dk, Dv;
     bool bf16;
+    // elements between consecutive sequences of q, k, v; 0: dense [N, H, D]
+    int64_t q_seq_stride = 0, k_seq_stride = 0, v_seq_stride = 0;
 };
 
 // Prefill over [B, T, H, *] tensors.  Row strides (elements between
@@ -52,5 +54,17 @@ struct LayerArgs {
 };
 size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv);
 hipError_t launch_layer(const LayerArgs &a, hipStream_t stream);
+
+// One token of the layer for N sequences: x [N, hidden]; conv_state [N, conv_k-1,
+// H(2Dk+Dv)] and state [N, H, Dk, Dv] updated in place; out [N, hidden]
+struct LayerDecodeArgs {
+    const void *x;
+    const void *W_qkv, *conv_w, *W_ab, *W_gate, *W_o;
+    const float *A, *b_alpha, *norm_gamma;
+    float *conv_state, *state, *out;
+    int64_t N, hidden, H, Dk, Dv, conv_k;
+    void *ws;
+};
+hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t stream);
 
 }  // namespace gdn

@@ -233,6 +233,85 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Decode prologue: one token per sequence.  conv_state row r of sequence n
+// holds the in-projection of token t - (conv_k - 1 - r), oldest first; tap j
+// (j < conv_k - 1) reads row j and tap conv_k - 1 the current token.  The
+// rows are then shifted by one, in place: each thread reads and writes only
+// its own 8 channels.  L2 norm and gates as in the prologue.
+// ---------------------------------------------------------------------------
+template <int DK>
+__global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__restrict__ pre,
+                                                              const __bf16 *__restrict__ conv_w,
+                                                              const float *__restrict__ ab,
+                                                              const float *__restrict__ Aexp,
+                                                              const float *__restrict__ b_alpha,
+                                                              float *__restrict__ conv_state, float *__restrict__ post,
+                                                              float *__restrict__ alpha, float *__restrict__ beta,
+                                                              int H, int nqkv, int conv_k)
+{
+    const int64_t n = blockIdx.x;
+    const int nvec = nqkv / 8;
+    const int nqk_vec = 2 * H * DK / 8;
+    constexpr int HV = DK / 8;
+    const int vi = blockIdx.y * 256 + threadIdx.x;
+    const bool active = vi < nvec;
+    const int c0 = active ? vi * 8 : 0;
+    auto ld8 = [&](const float *src, float (&x)[8]) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
+        x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
+        x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+    };
+    float rows[4][8];                        // taps 0 .. conv_k-1: history rows, then the current token
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < conv_k - 1) {
+            ld8(conv_state + (n * (conv_k - 1) + j) * nqkv + c0, rows[j]);
+        } else if (j == conv_k - 1) {
+            ld8(pre + n * nqkv + c0, rows[j]);
+        }
+    }
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < conv_k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf((float)conv_w[(int64_t)(c0 + e) * conv_k + j], rows[j][e], o[e]);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
+#pragma unroll
+    for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
+    if (active) {
+        const float scale = vi < nqk_vec ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
+        f32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
+        *reinterpret_cast<f32x4 *>(post + n * nqkv + c0) = o0;
+        *reinterpret_cast<f32x4 *>(post + n * nqkv + c0 + 4) = o1;
+        // history shifted by one token: row r <- tap r + 1
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            if (r < conv_k - 1) {
+                float *dst = conv_state + (n * (conv_k - 1) + r) * nqkv + c0;
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{rows[r + 1][0], rows[r + 1][1], rows[r + 1][2], rows[r + 1][3]};
+                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{rows[r + 1][4], rows[r + 1][5], rows[r + 1][6], rows[r + 1][7]};
+            }
+        }
+    }
+    if (blockIdx.y == 0) {
+        for (int hh = threadIdx.x; hh < H; hh += 256) {
+            const float a = ab[n * 2 * H + hh];
+            const float bb = ab[n * 2 * H + H + hh];
+            alpha[n * H + hh] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
+            beta[n * H + hh] = sigmoidf_(bb);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Epilogue: one workgroup per token; per head, RMSNorm over Dv with gain
 // (1 + gamma), times sigmoid(z); written as the bf16 operand of W_o.
 // ---------------------------------------------------------------------------
@@ -317,6 +396,17 @@ hipError_t launch_epilogue_dv(const float *y, const __bf16 *z, const float *gamm
     return hipGetLastError();
 }
 
+template <int DK>
+hipError_t launch_decode_prologue_dk(const float *pre, const __bf16 *conv_w, const float *ab, const float *A,
+                                     const float *b_alpha, float *conv_state, float *post, float *alpha, float *beta,
+                                     int64_t N, int H, int nqkv, int conv_k, hipStream_t s)
+{
+    const unsigned slabs = (unsigned)((nqkv / 8 + 255) / 256);
+    hipLaunchKernelGGL((decode_prologue_kernel<DK>), dim3((unsigned)N, slabs), dim3(256), 0, s, pre, conv_w, ab, A,
+                       b_alpha, conv_state, post, alpha, beta, H, nqkv, conv_k);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
@@ -380,6 +470,57 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     }
     if (e) return e;
     return gemm_nt<float>(g, (const __bf16 *)a.W_o, a.out, M, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+}
+
+hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
+{
+    const int64_t N = a.N, H = a.H, Dk = a.Dk, Dv = a.Dv, hidden = a.hidden;
+    if (N == 0 || H == 0) return hipSuccess;
+    const WsLayout w = ws_layout(N, 1, H, Dk, Dv);
+    char *ws = static_cast<char *>(a.ws);
+    float *pre = reinterpret_cast<float *>(ws + w.pre);
+    float *post = reinterpret_cast<float *>(ws + w.post);
+    __bf16 *z = reinterpret_cast<__bf16 *>(ws + w.z);
+    float *ab = reinterpret_cast<float *>(ws + w.ab);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *y = reinterpret_cast<float *>(ws + w.y);
+    __bf16 *g = reinterpret_cast<__bf16 *>(ws + w.g);
+    const __bf16 *x = static_cast<const __bf16 *>(a.x);
+    const int64_t nqkv = H * (2 * Dk + Dv);
+    hipError_t e;
+
+    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
+    if ((e = gemm_nt<__bf16>(x, (const __bf16 *)a.W_gate, z, N, H * Dv, hidden, hidden, hidden, H * Dv, s)))
+        return e;
+    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_ab, ab, N, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
+
+    const __bf16 *cw = (const __bf16 *)a.conv_w;
+    switch (Dk) {
+    case 16: e = launch_decode_prologue_dk<16>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 32: e = launch_decode_prologue_dk<32>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 64: e = launch_decode_prologue_dk<64>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 128: e = launch_decode_prologue_dk<128>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e) return e;
+
+    DecodeArgs d{};
+    d.q = post; d.k = post + H * Dk; d.v = post + 2 * H * Dk;
+    d.alpha = alpha; d.beta = beta; d.state = a.state; d.y = y;
+    d.N = N; d.H = H; d.Dk = Dk; d.Dv = Dv; d.bf16 = false;
+    d.q_seq_stride = nqkv; d.k_seq_stride = nqkv; d.v_seq_stride = nqkv;
+    if ((e = launch_decode(d, s))) return e;
+
+    switch (Dv) {
+    case 16: e = launch_epilogue_dv<16>(y, z, a.norm_gamma, g, N, (int)H, s); break;
+    case 32: e = launch_epilogue_dv<32>(y, z, a.norm_gamma, g, N, (int)H, s); break;
+    case 64: e = launch_epilogue_dv<64>(y, z, a.norm_gamma, g, N, (int)H, s); break;
+    case 128: e = launch_epilogue_dv<128>(y, z, a.norm_gamma, g, N, (int)H, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e) return e;
+    return gemm_nt<float>(g, (const __bf16 *)a.W_o, a.out, N, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
 }
 
 }  // namespace gdn

@@ -94,6 +94,9 @@ PREFILL_4K = PrefillConfig("prefill-4k (B=2 T=4096 H=16 d=128 C=64 bf16)", 2, 40
 PREFILL_32K = PrefillConfig("prefill-32k (B=1 T=32768 H=32 d=128 C=64 bf16)", 1, 32768, 32, 128, 128, 64, "bf16", None, 2)
 DECODE_256 = DecodeConfig("decode (N=256 H=32 d=128 fp32 state)", 256, 32, 128, 128, "bf16", 0.02, 3)
 LAYER_16K = LayerConfig("layer (B=1 T=16384 hidden=2048 H=16 d=128 conv=4 C=64)", 1, 16384, 2048, 16, 128, 128, 4, 64, 0.02, 4)
+# one new token for each of 256 sequences (B = N, T = 1; chunk unused)
+LAYER_DECODE_256 = LayerConfig("layer decode (N=256 hidden=2048 H=16 d=128 conv=4)", 256, 1, 2048, 16, 128, 128, 4, 64,
+                               0.02, 5)
 
 
 def _sigmoid32(x):
@@ -170,6 +173,19 @@ def layer_inputs(B, T, hidden, H, Dk, Dv, conv_k=4, w_std=0.02, seed=4,
     return dict(x=to_bf16_bits(x), W_qkv=to_bf16_bits(W_qkv), conv_w=to_bf16_bits(conv_w),
                 W_ab=to_bf16_bits(W_ab), A=A, b_alpha=b_alpha, W_gate=to_bf16_bits(W_gate),
                 norm_gamma=gamma, W_o=to_bf16_bits(W_o))
+
+
+def layer_decode_config_inputs(cfg: LayerConfig):
+    """Inputs of one layer-decode step: the layer inputs of a one-token batch of
+    cfg.B sequences, plus a history: conv rows ~ N(0, hidden * w_std^2) (the
+    spread of x W_qkv^T with x ~ N(0, 1)) and states ~ N(0, 0.02^2)."""
+    inp = layer_inputs(cfg.B, 1, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv, cfg.conv_k, cfg.w_std, cfg.seed)
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + 1000))
+    ch = cfg.H * (2 * cfg.Dk + cfg.Dv)
+    cs = rng.standard_normal((cfg.B, cfg.conv_k - 1, ch), dtype=np.float32) * np.float32(
+        np.sqrt(cfg.hidden) * cfg.w_std)
+    S = rng.standard_normal((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=np.float32) * np.float32(0.02)
+    return inp, cs, S
 
 
 def layer_config_inputs(cfg: LayerConfig):

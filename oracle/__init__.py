@@ -237,3 +237,36 @@ def gdn_layer_fwd(x, W_qkv, conv_w, W_ab, A, b_alpha, W_gate, norm_gamma, W_o,
         return dict(qkv=qkv, ab=ab, z=z, conv=conv, q=q, k=k, v=v, alpha=alpha,
                     beta=beta, y=y, yn=yn, g=g, o=o, ST=ST)
     return o, ST
+
+
+def gdn_layer_decode_step(x, W_qkv, conv_w, W_ab, A, b_alpha, W_gate, norm_gamma, W_o,
+                          H: int, Dk: int, Dv: int, conv_state, S):
+    """One new token of the layer for each of N sequences (same section and
+    formulas as ``gdn_layer_fwd``, one token at a time with its history given).
+
+    x: [N, hidden]; conv_state: [N, K-1, Ch], the in-projection rows of the
+    previous K-1 tokens, oldest first (zeros before a sequence starts);
+    S: [N, H, Dk, Dv] the state after the previous token.
+    Returns (o [N, hidden], new conv_state, new S); the inputs are not modified.
+    """
+    x = _f64(x)
+    conv_w = _f64(conv_w)
+    N = x.shape[0]
+    K = conv_w.shape[1]
+    qkv = linear(x, W_qkv)                              # this token's in-projection
+    ab = linear(x, W_ab)
+    z = linear(x, W_gate)
+    hist = _f64(conv_state).reshape(N, K - 1, -1) if K > 1 else np.zeros((N, 0, qkv.shape[1]))
+    window = np.concatenate([hist, qkv[:, None, :]], axis=1)      # [N, K, Ch], tap j = row j
+    conv = np.zeros_like(qkv)
+    for j in range(K):
+        conv += conv_w[None, :, j] * window[:, j, :]
+    q = l2_normalize(conv[:, :H * Dk].reshape(N, H, Dk))
+    k = l2_normalize(conv[:, H * Dk:2 * H * Dk].reshape(N, H, Dk))
+    v = conv[:, 2 * H * Dk:].reshape(N, H, Dv)
+    alpha = decay(ab[:, :H], A, b_alpha)
+    beta = write_strength(ab[:, H:])
+    y, S_new = gdn_decode_step(q, k, v, alpha, beta, _f64(S))
+    g = sigmoid(z).reshape(N, H, Dv) * rmsnorm_zero_centred(y, norm_gamma)
+    o = linear(g.reshape(N, H * Dv), W_o)
+    return o, window[:, 1:, :].copy(), S_new

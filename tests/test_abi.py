@@ -159,6 +159,36 @@ def test_layer_validation(L):
     assert call(out=ws) == ALIAS
 
 
+def test_layer_decode_validation(L):
+    P = gdn.gdn_layer_params(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB, A + 7 * MB)
+    ws_need = L.gdn_layer_decode_workspace_bytes(4, 128, 2, 16, 16)
+    assert ws_need > 0
+    ws = A + 512 * MB
+
+    def call(x=A + 64 * MB, cs=A + 96 * MB, S=A + 160 * MB, out=A + 128 * MB, N=4, hidden=128, conv_k=4,
+             w=ws, wb=ws_need, p=P, Dk=16):
+        return L.gdn_layer_decode_step(x, ctypes.byref(p) if p is not None else None, cs, S, out, N, hidden, 2,
+                                       Dk, 16, conv_k, w, wb, None)
+
+    assert call(p=None) == NULL
+    assert call(x=None) == NULL
+    assert call(S=None) == NULL
+    assert call(cs=None) == NULL                   # history needed for conv_k > 1
+    assert call(N=-1) == SHAPE
+    assert call(hidden=96) == UNSUP
+    assert call(conv_k=0) == UNSUP
+    assert call(Dk=24) == UNSUP
+    assert call(w=None) == WS
+    assert call(wb=ws_need - 1) == WS
+    assert call(w=ws + 16) == ALIGN
+    assert call(cs=A + 96 * MB + 4) == ALIGN
+    assert call(out=A + 64 * MB) == ALIAS          # out over x
+    assert call(S=A + 96 * MB) == ALIAS            # state over conv_state
+    assert call(cs=ws) == ALIAS                    # conv_state over workspace
+    assert call(out=A + 160 * MB) == ALIAS         # out over state
+    assert "gdn_layer_decode_step" in L.gdn_last_error().decode()
+
+
 def test_workspace_queries(L):
     # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
     assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056

@@ -1,0 +1,120 @@
+"""GPU parity of gdn_layer_decode_step (one new token of the layer per
+sequence, conv history and recurrent state carried in place) against the
+oracle: T steps from an empty history against the oracle's whole-sequence
+layer, one step from an arbitrary history against the oracle's decode step."""
+import numpy as np
+import pytest
+
+from helpers import TOL_BF16, dev, host, rel_err
+from linear_attention_token_gated_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
+
+
+def _params(inp):
+    return {n: dev(inp[n]) for n in NAMES}
+
+
+@pytest.mark.parametrize("conv_k", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,hidden,H,Dk,Dv", [(3, 128, 2, 32, 64), (2, 192, 4, 16, 32), (5, 128, 1, 128, 128)])
+def test_steps_equal_layer(oracle_mod, conv_k, N, hidden, H, Dk, Dv):
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    T = 7
+    print(f"case: layer decode N={N} T={T} hidden={hidden} H={H} Dk={Dk} Dv={Dv} conv_k={conv_k}", flush=True)
+    inp = wl.layer_inputs(N, T, hidden, H, Dk, Dv, conv_k=conv_k, w_std=0.05, seed=conv_k + Dk,
+                          gamma_std=0.1, A_val=0.3, b_alpha_val=-0.5)
+    S0 = (np.random.default_rng(Dv).standard_normal((N, H, Dk, Dv)) * 0.05).astype(np.float32)
+    p = _params(inp)
+    x = dev(inp["x"])
+    Ch = H * (2 * Dk + Dv)
+    cs = torch.zeros((N, conv_k - 1, Ch), dtype=torch.float32, device="cuda") if conv_k > 1 else None
+    S = dev(S0)
+    outs = []
+    for t in range(T):
+        outs.append(gdn.layer_decode_step(x[:, t].contiguous(), p, H, Dk, Dv, cs, S).clone())
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.gdn_layer_fwd(wl.widen(inp["x"]), *(wl.widen(inp[n]) for n in NAMES),
+                                            H=H, Dk=Dk, Dv=Dv, S0=wl.widen(S0))
+    eo = rel_err(np.stack([host(o) for o in outs], axis=1), o_ref)
+    eS = rel_err(host(S), S_ref)
+    print(f"  err out={eo:.3e} S={eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+    if conv_k > 1:
+        qkv = oracle_mod.linear(wl.widen(inp["x"]), wl.widen(inp["W_qkv"]))
+        assert rel_err(host(cs), qkv[:, T - (conv_k - 1):]) <= 1e-4
+
+
+def test_one_step_from_history(oracle_mod):
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    N, hidden, H, Dk, Dv, conv_k = 4, 128, 2, 64, 32, 4
+    print("case: layer decode from an arbitrary history", flush=True)
+    inp = wl.layer_inputs(N, 1, hidden, H, Dk, Dv, conv_k=conv_k, w_std=0.05, seed=21, gamma_std=0.1)
+    rng = np.random.default_rng(4)
+    Ch = H * (2 * Dk + Dv)
+    cs0 = (rng.standard_normal((N, conv_k - 1, Ch)) * 0.5).astype(np.float32)
+    S0 = (rng.standard_normal((N, H, Dk, Dv)) * 0.05).astype(np.float32)
+    cs, S = dev(cs0), dev(S0)
+    out = gdn.layer_decode_step(dev(inp["x"])[:, 0].contiguous(), _params(inp), H, Dk, Dv, cs, S)
+    torch.cuda.synchronize()
+    o_ref, cs_ref, S_ref = oracle_mod.gdn_layer_decode_step(
+        wl.widen(inp["x"])[:, 0], *(wl.widen(inp[n]) for n in NAMES), H=H, Dk=Dk, Dv=Dv,
+        conv_state=wl.widen(cs0), S=wl.widen(S0))
+    eo, eS = rel_err(host(out), o_ref), rel_err(host(S), S_ref)
+    print(f"  err out={eo:.3e} S={eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+    # the shifted rows are copies; the appended row is this token's fp32 in-projection
+    np.testing.assert_array_equal(host(cs)[:, :conv_k - 2], cs0[:, 1:])
+    assert rel_err(host(cs)[:, conv_k - 2], cs_ref[:, conv_k - 2]) <= 1e-4
+
+
+def test_decode_matches_gpu_layer(oracle_mod):
+    """Token-by-token layer decode on the GPU follows the GPU's whole-sequence layer."""
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    N, T, hidden, H, Dk, Dv = 2, 40, 128, 2, 32, 32
+    print(f"case: layer decode vs layer N={N} T={T}", flush=True)
+    inp = wl.layer_inputs(N, T, hidden, H, Dk, Dv, w_std=0.05, seed=8)
+    p = _params(inp)
+    x = dev(inp["x"])
+    out_l, S_l = gdn.layer_fwd(x, p, H, Dk, Dv, chunk=16)
+    cs = torch.zeros((N, 3, H * (2 * Dk + Dv)), dtype=torch.float32, device="cuda")
+    S = torch.zeros((N, H, Dk, Dv), dtype=torch.float32, device="cuda")
+    outs = [gdn.layer_decode_step(x[:, t].contiguous(), p, H, Dk, Dv, cs, S).clone() for t in range(T)]
+    torch.cuda.synchronize()
+    assert rel_err(np.stack([host(o) for o in outs], axis=1), host(out_l)) <= 1e-3
+    assert rel_err(host(S), host(S_l)) <= 1e-3
+
+
+def test_workload_size_one_step(oracle_mod):
+    """The layer-decode workload (256 sequences, hidden 2048, 16 heads of 128), one
+    step from a random history, against the oracle."""
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    cfg = wl.LAYER_DECODE_256
+    print(f"case: {cfg.name}", flush=True)
+    inp, cs0, S0 = wl.layer_decode_config_inputs(cfg)
+    cs, S = dev(cs0), dev(S0)
+    out = gdn.layer_decode_step(dev(inp["x"])[:, 0].contiguous(), _params(inp), cfg.H, cfg.Dk, cfg.Dv, cs, S)
+    torch.cuda.synchronize()
+    o_ref, _, S_ref = oracle_mod.gdn_layer_decode_step(
+        wl.widen(inp["x"])[:, 0], *(wl.widen(inp[n]) for n in NAMES), H=cfg.H, Dk=cfg.Dk, Dv=cfg.Dv,
+        conv_state=wl.widen(cs0), S=wl.widen(S0))
+    eo, eS = rel_err(host(out), o_ref), rel_err(host(S), S_ref)
+    print(f"  err out={eo:.3e} S={eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_empty_batch():
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    inp = wl.layer_inputs(1, 1, 64, 1, 16, 16, w_std=0.05, seed=1)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    cs = torch.empty((0, 3, 48), dtype=torch.float32, device="cuda")
+    S = torch.empty((0, 1, 16, 16), dtype=torch.float32, device="cuda")
+    out = gdn.layer_decode_step(x, _params(inp), 1, 16, 16, cs, S)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)

@@ -7,6 +7,7 @@ case; the full layer is checked for causality and for its reduction to the
 core recurrence when the wrapper is made trivial.
 """
 import numpy as np
+import pytest
 import scipy.special as sps
 
 
@@ -125,3 +126,49 @@ def test_layer_reduces_to_core(oracle_mod):
     z = p["x"] @ p["W_gate"].T
     g = sps.expit(z).reshape(1, 8, H, Dv) * parts["yn"]
     np.testing.assert_allclose(parts["o"], g.reshape(1, 8, H * Dv) @ p["W_o"].T, rtol=1e-12)
+
+
+def _layer_params(oracle_mod, inp):
+    from linear_attention_token_gated_amd import workloads as wl
+    names = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
+    return [wl.widen(inp[n]) for n in names]
+
+
+@pytest.mark.parametrize("conv_k", [1, 2, 4])
+def test_layer_decode_steps_equal_layer(oracle_mod, conv_k):
+    """T single-token steps of the layer from an empty history and a given state
+    reproduce the whole-sequence layer on those T tokens (same section, computed
+    by an independent route: conv over a carried window, recurrence one token at
+    a time)."""
+    from linear_attention_token_gated_amd import workloads as wl
+    B, T, hidden, H, Dk, Dv = 2, 9, 64, 2, 8, 4
+    inp = wl.layer_inputs(B, T, hidden, H, Dk, Dv, conv_k=conv_k, w_std=0.2, seed=5 + conv_k,
+                          gamma_std=0.2, A_val=0.4, b_alpha_val=-0.3)
+    P = _layer_params(oracle_mod, inp)
+    x = wl.widen(inp["x"])
+    S0 = np.random.default_rng(2).standard_normal((B, H, Dk, Dv)) * 0.3
+    o_ref, S_ref = oracle_mod.gdn_layer_fwd(x, *P, H=H, Dk=Dk, Dv=Dv, S0=S0)
+    Ch = H * (2 * Dk + Dv)
+    conv_state = np.zeros((B, conv_k - 1, Ch))
+    S = S0.copy()
+    for t in range(T):
+        o, conv_state, S = oracle_mod.gdn_layer_decode_step(x[:, t], *P, H=H, Dk=Dk, Dv=Dv,
+                                                            conv_state=conv_state, S=S)
+        np.testing.assert_allclose(o, o_ref[:, t], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-12)
+    # the carried window holds the last conv_k-1 in-projection rows
+    qkv = oracle_mod.linear(x, P[0])
+    if conv_k > 1:
+        np.testing.assert_allclose(conv_state, qkv[:, T - (conv_k - 1):], rtol=1e-13, atol=1e-13)
+
+
+def test_layer_decode_step_leaves_inputs(oracle_mod):
+    from linear_attention_token_gated_amd import workloads as wl
+    B, hidden, H, Dk, Dv = 3, 64, 1, 8, 8
+    inp = wl.layer_inputs(B, 1, hidden, H, Dk, Dv, conv_k=4, w_std=0.2, seed=1)
+    P = _layer_params(oracle_mod, inp)
+    cs = np.random.default_rng(0).standard_normal((B, 3, H * (2 * Dk + Dv)))
+    S = np.random.default_rng(1).standard_normal((B, H, Dk, Dv))
+    cs0, S0 = cs.copy(), S.copy()
+    oracle_mod.gdn_layer_decode_step(wl.widen(inp["x"])[:, 0], *P, H=H, Dk=Dk, Dv=Dv, conv_state=cs, S=S)
+    assert np.array_equal(cs, cs0) and np.array_equal(S, S0)
