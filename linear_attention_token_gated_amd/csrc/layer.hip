@@ -33,44 +33,63 @@ constexpr float kRmsEps = 1e-6f;
 
 // ---------------------------------------------------------------------------
 // C[M, N] = A[M, K] * B[N, K]^T, bf16 operands, fp32 accumulation.
-// 128 x 128 workgroup tile, 4 wavefronts in a 2 x 2 grid of 64 x 64, K step 64
-// through LDS with the next K step prefetched into registers.  Rows/cols past
-// M/N and k past K are zero-filled; K must be a multiple of 8.
+// 128 x 128 workgroup tile, 4 wavefronts in a 2 x 2 grid of 64 x 64, K steps
+// of 64.  The tiles of A and B reach LDS through buffer loads that write LDS
+// directly, two K steps ahead into three stages; one barrier per K step.
+// Rows (128 bytes, two to a 256-byte line of the 64 banks) are stored
+// unpadded, 16-byte granule g of row r at position g ^ ((r / 2) mod 8): the
+// 16 rows of a fragment read then hit all 64 banks once.  Rows past M / N
+// lie outside the buffer range of the load and k past K gets an offset
+// outside it: both read as zeros.  K must be a multiple of 8.
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 64, GPITCH = GBK + 8;
+constexpr int GBM = 128, GBN = 128, GBK = 64, GSTAGES = 3;
+constexpr int GTILE = GBM * GBK * 2;                 // bytes of one A (or B) tile
+constexpr uint32_t G_OOB = 0x7FFFFFF0u;
+
+typedef __attribute__((address_space(3))) void *glds_ptr;
+__device__ __forceinline__ void gload_lds(const void *base, uint32_t nrec, uint32_t voff, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)nrec, 0x00020000),
+        (glds_ptr)(uintptr_t)(uint32_t)(uintptr_t)dst, 16, voff, 0, 0, 0);
+}
+
+// position of element (r, k) of a [rows][64] tile with permuted granules
+__device__ __forceinline__ int gsw(int r, int k) { return r * GBK + ((((k >> 3) ^ (r >> 1)) & 7) << 3) + (k & 7); }
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
-                                                      OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
-                                                      int64_t ldb, int64_t ldc)
+__global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
+                                                         OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
+                                                         int64_t ldb, int64_t ldc)
 {
-    __shared__ __attribute__((aligned(16))) __bf16 As[GBM * GPITCH];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[GBN * GPITCH];
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    __shared__ __attribute__((aligned(1024))) char smem[GSTAGES * 2 * GTILE];
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
+    const int64_t mrows = M - m0 < GBM ? M - m0 : GBM, nrows = N - n0 < GBN ? N - n0 : GBN;
+    const int ntk = (K + GBK - 1) / GBK;
 
-    // each thread moves 4 16-byte vectors of A and 4 of B per K step
-    f32x4 ra[4], rb[4];
-    auto load_tiles = [&](int k0) {
+    // load t (t = 0..3) of this wave moves rows 8 i .. 8 i + 7 (i = wave + 4 t) of
+    // the A tile and of the B tile: lane -> row 8 i + lane / 8, stored granule lane % 8
+    uint32_t roff_a[4], roff_b[4];
+    int lgk[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vi = tid + 256 * i;
-            const int r = vi >> 3, c = (vi & 7) * 8;
-            const int64_t gm = m0 + r, gn = n0 + r;
-            const int gk = k0 + c;
-            ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const f32x4 *>(A + gm * lda + gk) : zero4();
-            rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const f32x4 *>(Bm + gn * ldb + gk) : zero4();
-        }
-    };
-    auto store_tiles = [&]() {
+    for (int t = 0; t < 4; ++t) {
+        const int r = 8 * (wave + 4 * t) + (lane >> 3);
+        lgk[t] = 8 * ((lane ^ (r >> 1)) & 7);                           // k offset of this lane's granule
+        roff_a[t] = (uint32_t)(r * lda * 2 + lgk[t] * 2);
+        roff_b[t] = (uint32_t)(r * ldb * 2 + lgk[t] * 2);
+    }
+    auto issue = [&](int kt, int stage) {
+        const int k0 = kt * GBK;
+        char *sa = smem + stage * 2 * GTILE, *sb = sa + GTILE;
+        const __bf16 *ba = A + m0 * lda + k0, *bb = Bm + n0 * ldb + k0;
+        const uint32_t na = (uint32_t)((mrows * lda - k0) * 2), nb = (uint32_t)((nrows * ldb - k0) * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vi = tid + 256 * i;
-            const int r = vi >> 3, c = (vi & 7) * 8;
-            *reinterpret_cast<f32x4 *>(As + r * GPITCH + c) = ra[i];
-            *reinterpret_cast<f32x4 *>(Bs + r * GPITCH + c) = rb[i];
+        for (int t = 0; t < 4; ++t) {
+            const bool kin = k0 + lgk[t] < K;
+            gload_lds(ba, na, kin ? roff_a[t] : G_OOB, sa + (wave + 4 * t) * 1024);
+            gload_lds(bb, nb, kin ? roff_b[t] : G_OOB, sb + (wave + 4 * t) * 1024);
         }
     };
 
@@ -80,25 +99,37 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16 *__restrict__
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
-    load_tiles(0);
-    for (int k0 = 0; k0 < K; k0 += GBK) {
-        store_tiles();
-        __syncthreads();
-        if (k0 + GBK < K) load_tiles(k0 + GBK);
+    issue(0, 0);
+    issue(ntk > 1 ? 1 : 0, 1);
+    int st = 0;
+    for (int kt = 0; kt < ntk; ++kt) {
+        // tile kt complete (tile kt+1 may still be in flight), for every wave after
+        // the barrier, which also finds every wave done with tile kt-1
+        __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // tile kt+2 into the stage of tile kt-1 (past the end, the last tile again:
+        // that stage is never read)
+        issue(kt + 2 < ntk ? kt + 2 : ntk - 1, st == 0 ? 2 : st - 1);
+        const __bf16 *As = reinterpret_cast<const __bf16 *>(smem + st * 2 * GTILE);
+        const __bf16 *Bs = As + GBM * GBK;
 #pragma unroll
         for (int kk = 0; kk < GBK; kk += 32) {
             Frag<__bf16, 32> af[4], bf[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = frag_rows<__bf16, 32>(As, GPITCH, wm * 64 + 16 * i, kk, lane);
+            for (int i = 0; i < 4; ++i) af[i].load(As + gsw(wm * 64 + 16 * i + ln, kk + 8 * lg));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = frag_rows<__bf16, 32>(Bs, GPITCH, wn * 64 + 16 * j, kk, lane);
+            for (int j = 0; j < 4; ++j) bf[j].load(Bs + gsw(wn * 64 + 16 * j + ln, kk + 8 * lg));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = Frag<__bf16, 32>::mma(af[i], bf[j], acc[i][j]);
         }
-        __syncthreads();
+        st = st == GSTAGES - 1 ? 0 : st + 1;
     }
+    // no LDS write may land after the workgroup ends
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
