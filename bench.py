@@ -77,6 +77,12 @@ def decode_alg(N, H, Dk, Dv, in_bytes=2):
     return N * H * per, N * H * 8 * Dk * Dv
 
 
+def verify_alg(N, T, H, Dk, Dv, in_bytes=2):
+    """States read once, the T snapshots written once, q/k/v/alpha/beta read and
+    y (fp32) written once per token."""
+    return N * H * Dk * Dv * 4 * (1 + T) + N * T * H * ((2 * Dk + Dv) * in_bytes + 8 + 4 * Dv)
+
+
 def layer_decode_alg(N, hidden, H, Dk, Dv, conv_k):
     """One layer-decode step: the four weight matrices (bf16) and x read once,
     the conv history (fp32) and the states read and written once, out (fp32)
@@ -205,6 +211,17 @@ def bench_layer(args, torch, gdn, wl):
     return cfg, total_ms, per, steps
 
 
+def bench_verify(args, torch, gdn, wl):
+    cfg = wl.VERIFY_256x4
+    inp = wl.prefill_config_inputs(cfg)
+    q, k, v, al, be, S = (to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "S0"))
+    y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
+    so = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
+    fn = lambda: gdn.decode_verify(q, k, v, al, be, S, states_out=so, y=y)
+    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
+    return cfg, total_ms, per
+
+
 def bench_layer_decode(args, torch, gdn, wl):
     cfg = wl.LAYER_DECODE_256
     inp, cs0, S0 = wl.layer_decode_config_inputs(cfg)
@@ -265,6 +282,7 @@ def main():
         bench_decode(pargs, torch, gdn, wl)
         bench_layer(pargs, torch, gdn, wl)
         bench_layer_decode(pargs, torch, gdn, wl)
+        bench_verify(pargs, torch, gdn, wl)
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -306,6 +324,12 @@ def main():
                     "tokens_per_s": ld_cfg.B / (ld_ms * 1e-3), "alg_bytes_per_step": ld_bytes,
                     "GBps": ld_bytes / (ld_ms * 1e-3) / 1e9,
                     "hbm_frac": ld_bytes / (ld_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+    v_cfg, v_total, v_per = bench_verify(args, torch, gdn, wl)
+    v_ms = float(np.mean(v_per))
+    v_bytes = verify_alg(v_cfg.B, v_cfg.T, v_cfg.H, v_cfg.Dk, v_cfg.Dv)
+    verify = {"workload": v_cfg.name, "ms_per_step": round(v_ms, 4), "alg_bytes_per_step": v_bytes,
+              "GBps": v_bytes / (v_ms * 1e-3) / 1e9, "hbm_frac": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -352,6 +376,7 @@ def main():
                    "traffic": measured_traffic("decode_256x32", DECODE_SOURCES)},
         "layer": layer,
         "layer_decode": layer_decode,
+        "verify": verify,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }

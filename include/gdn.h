@@ -144,6 +144,27 @@ GDN_API gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            gdn_dtype dtype, hipStream_t stream);
 
 /*
+ * gdn_decode_verify -- T consecutive tokens of each of N sequences from their
+ * stored states, eqs (1)-(4) token by token (T calls of gdn_decode_step, in
+ * one launch), with the state after every token written out: a caller that
+ * checks drafted tokens keeps the state after the prefix it accepts.
+ *
+ *   q, k        [N, T, H, Dk]  dtype
+ *   v           [N, T, H, Dv]  dtype
+ *   alpha, beta [N, T, H]      float32
+ *   state       [N, H, Dk, Dv] float32, the states before the first token (read only)
+ *   states_out  [N, T, H, Dk, Dv] float32: [:, t] is the state after token t
+ *   y           [N, T, H, Dv]  float32
+ *   Dk, Dv in {16, 32, 64, 128}.  states_out and y must not overlap each
+ *   other or any input; state is not modified.
+ */
+GDN_API gdn_status gdn_decode_verify(const void *q, const void *k, const void *v,
+                                     const float *alpha, const float *beta,
+                                     const float *state, float *states_out, float *y,
+                                     int64_t N, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                     gdn_dtype dtype, hipStream_t stream);
+
+/*
  * gdn_layer_fwd -- the GDN token-mixing layer around the core (picx.dev
  * summary, "1. GDN Hybrid Token Mixing": short causal convolution, L2-normalised
  * queries and keys, eq (9) beta, eq (10) alpha, eq (11) sigmoid-gated

@@ -29,7 +29,7 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_prepare", "gdn_prefill_recurrence",
-            "gdn_decode_step", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
+            "gdn_decode_step", "gdn_decode_verify", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
             "gdn_layer_decode_workspace_bytes", "gdn_status_str", "gdn_last_error")
 
 
@@ -70,6 +70,8 @@ def lib():
     L.gdn_prefill_recurrence.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
+    L.gdn_decode_verify.restype = ctypes.c_int
     L.gdn_layer_fwd.argtypes = [vp, ctypes.POINTER(gdn_layer_params), vp, vp, vp, i64, i64, i64, i64,
                                 i64, i64, i64, i64, vp, sz, vp]
     L.gdn_layer_fwd.restype = ctypes.c_int
@@ -212,6 +214,29 @@ def decode_step(q, k, v, alpha, beta, state, y=None):
     _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
                                  N, H, Dk, Dv, _dtype_code(q), _stream(q.device)))
     return y
+
+
+def decode_verify(q, k, v, alpha, beta, state, states_out=None, y=None):
+    """T tokens per sequence from stored states.  q, k: [N,T,H,Dk]; v: [N,T,H,Dv]
+    (float32 or bfloat16); alpha, beta: [N,T,H] float32; state: [N,H,Dk,Dv]
+    float32 (not modified).  Returns (y [N,T,H,Dv], states_out [N,T,H,Dk,Dv]),
+    states_out[:, t] being the state after token t."""
+    import torch
+    N, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n in ((alpha, "alpha"), (beta, "beta"), (state, "state")):
+        _need(t, n, torch.float32)
+    if y is None:
+        y = torch.empty((N, T, H, Dv), dtype=torch.float32, device=q.device)
+    if states_out is None:
+        states_out = torch.empty((N, T, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _need(y, "y", torch.float32)
+    _need(states_out, "states_out", torch.float32)
+    _check(lib().gdn_decode_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                                   _ptr(states_out), _ptr(y), N, T, H, Dk, Dv, _dtype_code(q), _stream(q.device)))
+    return y, states_out
 
 
 def layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k=4, chunk=64) -> int:

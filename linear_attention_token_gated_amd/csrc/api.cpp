@@ -253,6 +253,49 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     return hip_status(gdn::launch_decode(a, stream), "gdn_decode_step launch");
 }
 
+gdn_status gdn_decode_verify(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                             const float *state, float *states_out, float *y, int64_t N, int64_t T, int64_t H,
+                             int64_t Dk, int64_t Dv, gdn_dtype dtype, hipStream_t stream)
+{
+    if (N < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0)
+        return fail(GDN_ERR_SHAPE, "gdn_decode_verify: negative size");
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_verify: dtype %d", (int)dtype);
+    if (!is_pow2_dim(Dk) || !is_pow2_dim(Dv))
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_verify: Dk=%lld Dv=%lld (supported: 16, 32, 64, 128)",
+                    (long long)Dk, (long long)Dv);
+    int64_t n_tok, n_s, n_so;
+    if (!count(&n_tok, {N, T, H}) || !count(&n_s, {N, H, Dk, Dv}) || !count(&n_so, {N, T, H, Dk, Dv}) ||
+        n_so > INT64_MAX / 4 || n_tok > INT64_MAX / (4 * 128))
+        return fail(GDN_ERR_SHAPE, "gdn_decode_verify: sizes overflow");
+    if (N * H > INT32_MAX || T > INT32_MAX)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_verify: N*H=%lld or T=%lld too large for one launch",
+                    (long long)(N * H), (long long)T);
+    if (n_tok > 0 && (!q || !k || !v || !alpha || !beta || !state || !states_out || !y))
+        return fail(GDN_ERR_NULL, "gdn_decode_verify: every pointer is required");
+    const void *ptrs[] = {q, k, v, alpha, beta, state, states_out, y};
+    const char *names[] = {"q", "k", "v", "alpha", "beta", "state", "states_out", "y"};
+    for (int i = 0; i < 8; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GDN_ERR_ALIGN, "gdn_decode_verify: %s is not 16-byte aligned", names[i]);
+    const size_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const Range ry{y, (size_t)(n_tok * Dv) * 4, "y"};
+    const Range ro{states_out, (size_t)n_so * 4, "states_out"};
+    const Range inputs[] = {{q, (size_t)(n_tok * Dk) * esz, "q"}, {k, (size_t)(n_tok * Dk) * esz, "k"},
+                            {v, (size_t)(n_tok * Dv) * esz, "v"}, {alpha, (size_t)n_tok * 4, "alpha"},
+                            {beta, (size_t)n_tok * 4, "beta"}, {state, (size_t)n_s * 4, "state"}};
+    for (const Range &r : inputs) {
+        if (overlap(ry, r)) return fail(GDN_ERR_ALIAS, "gdn_decode_verify: y overlaps %s", r.name);
+        if (overlap(ro, r)) return fail(GDN_ERR_ALIAS, "gdn_decode_verify: states_out overlaps %s", r.name);
+    }
+    if (overlap(ry, ro)) return fail(GDN_ERR_ALIAS, "gdn_decode_verify: y overlaps states_out");
+
+    gdn::VerifyArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s_in = state; a.s_out = states_out; a.y = y;
+    a.N = N; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.bf16 = dtype == GDN_BF16;
+    return hip_status(gdn::launch_verify(a, stream), "gdn_decode_verify launch");
+}
+
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk,
                                  int64_t Dv, int64_t conv_k, int64_t chunk)
 {

@@ -33,6 +33,18 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// T tokens per sequence from stored states, every intermediate state written
+struct VerifyArgs {
+    const void *q, *k, *v;          // [N, T, H, Dk], [N, T, H, Dv]
+    const float *alpha, *beta;      // [N, T, H]
+    const float *s_in;              // [N, H, Dk, Dv]
+    float *s_out;                   // [N, T, H, Dk, Dv]
+    float *y;                       // [N, T, H, Dv]
+    int64_t N, T, H, Dk, Dv;
+    bool bf16;
+};
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 // stages: 1 = chunk preparation (bf16), 2 = recurrence, 3 = both
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages = 3);
 

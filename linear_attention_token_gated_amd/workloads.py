@@ -94,6 +94,10 @@ PREFILL_4K = PrefillConfig("prefill-4k (B=2 T=4096 H=16 d=128 C=64 bf16)", 2, 40
 PREFILL_32K = PrefillConfig("prefill-32k (B=1 T=32768 H=32 d=128 C=64 bf16)", 1, 32768, 32, 128, 128, 64, "bf16", None, 2)
 DECODE_256 = DecodeConfig("decode (N=256 H=32 d=128 fp32 state)", 256, 32, 128, 128, "bf16", 0.02, 3)
 LAYER_16K = LayerConfig("layer (B=1 T=16384 hidden=2048 H=16 d=128 conv=4 C=64)", 1, 16384, 2048, 16, 128, 128, 4, 64, 0.02, 4)
+# verification of 4 drafted tokens for each of 256 sequences from stored states
+# (layout [N, T, H, *] of a prefill batch; the chunk field is unused)
+VERIFY_256x4 = PrefillConfig("decode verify (N=256 T=4 H=32 d=128 fp32 states)", 256, 4, 32, 128, 128, 16, "bf16",
+                             0.02, 6)
 # one new token for each of 256 sequences (B = N, T = 1; chunk unused)
 LAYER_DECODE_256 = LayerConfig("layer decode (N=256 hidden=2048 H=16 d=128 conv=4)", 256, 1, 2048, 16, 128, 128, 4, 64,
                                0.02, 5)

@@ -139,6 +139,25 @@ def gdn_decode_step(q, k, v, alpha, beta, S, nthreads: int = 0, _core=None):
     return y, S_new
 
 
+def gdn_decode_verify(q, k, v, alpha, beta, S):
+    """T consecutive tokens of each of N sequences from stored states (eqs
+    (1)-(4) token by token), keeping the state after every token.
+
+    q, k: [N, T, H, Dk]; v: [N, T, H, Dv]; alpha, beta: [N, T, H]; S: [N, H, Dk, Dv].
+    Returns (y [N, T, H, Dv], states [N, T, H, Dk, Dv]); S is not modified.
+    """
+    q, k, v, alpha, beta = (_f64(a) for a in (q, k, v, alpha, beta))
+    N, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    y = np.empty((N, T, H, Dv))
+    states = np.empty((N, T, H, Dk, Dv))
+    cur = _f64(S)
+    for t in range(T):
+        y[:, t], cur = gdn_decode_step(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], cur)
+        states[:, t] = cur
+    return y, states
+
+
 # ---------------------------------------------------------------------------
 # Layer wrapper (picx.dev summary, "1. GDN Hybrid Token Mixing", eqs (9)-(11)).
 # Each stage is its own function so the tests can pin it on its own.

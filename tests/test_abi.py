@@ -136,6 +136,24 @@ def test_decode_validation(L):
     assert decode(L, S=A) == ALIAS                   # state over q
 
 
+def verify(L, q=A, k=A + MB, v=A + 2 * MB, al=A + 3 * MB, be=A + 4 * MB, S=A + 8 * MB, So=A + 32 * MB,
+           y=A + 64 * MB, N=4, T=3, H=2, Dk=16, Dv=16, dt=1):
+    return L.gdn_decode_verify(q, k, v, al, be, S, So, y, N, T, H, Dk, Dv, dt, None)
+
+
+def test_verify_validation(L):
+    assert verify(L, So=None) == NULL
+    assert verify(L, S=None) == NULL
+    assert verify(L, T=-1) == SHAPE
+    assert verify(L, Dv=48) == UNSUP
+    assert verify(L, dt=5) == UNSUP
+    assert verify(L, y=A + 8) == ALIGN
+    assert verify(L, So=A + 8 * MB) == ALIAS         # states_out over state
+    assert verify(L, y=A + 32 * MB) == ALIAS         # y over states_out
+    assert verify(L, y=A + 2 * MB) == ALIAS          # y over v
+    assert "gdn_decode_verify" in L.gdn_last_error().decode()
+
+
 def test_layer_validation(L):
     P = gdn.gdn_layer_params(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB, A + 7 * MB)
     ws_need = L.gdn_layer_workspace_bytes(1, 64, 128, 2, 16, 16, 4, 16)
