@@ -10,6 +10,8 @@ Architecture"):
 
 * core recurrence -- section "Theoretical foundations", eqs (1)-(4); computed by
   ``oracle.c`` token by token in double precision;
+* its reverse mode (gradients of a loss through eqs (1)-(4)) -- the chain rule
+  applied to the same four steps in reverse token order, also in ``oracle.c``;
 * layer wrapper -- section "Methodology / 1. GDN Hybrid Token Mixing": short
   causal convolution, L2-normalised queries and keys, eq (9) write strength,
   eq (10) decay, eq (11) sigmoid-gated, zero-centred RMSNorm output.
@@ -64,6 +66,8 @@ def _configure(lib):
                                            i64, i64, i64, i64,
                                            ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.oracle_gdn_decode_step.restype = ctypes.c_int
+    lib.oracle_gdn_recurrence_bwd.argtypes = [dp] * 14 + [i64] * 5 + [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.oracle_gdn_recurrence_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -114,6 +118,39 @@ def gdn_recurrence(q, k, v, alpha, beta, S0=None, nthreads: int = 0, _core=None)
         raise MemoryError("oracle_gdn_recurrence: allocation failed")
     last_threads_used = used.value
     return y, ST
+
+
+def gdn_recurrence_bwd(q, k, v, alpha, beta, S0, dy, dST=None, nthreads: int = 0, _core=None):
+    """Gradients of eqs (1)-(4) over whole sequences (reverse mode, token by
+    token, in ``oracle.c``).
+
+    Inputs as for :func:`gdn_recurrence`, plus dy [B, T, H, Dv] = dL/dy and
+    dST [B, H, Dk, Dv] = dL/dS_T (None: zero).  Returns a dict with dq, dk
+    [B,T,H,Dk], dv [B,T,H,Dv], dalpha, dbeta [B,T,H] and dS0 [B,H,Dk,Dv]
+    (the gradient with respect to the initial state, also when S0 is None,
+    i.e. zero).
+    """
+    global last_threads_used
+    q, k, v, alpha, beta, dy = (_f64(a) for a in (q, k, v, alpha, beta, dy))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and v.shape == (B, T, H, Dv) and dy.shape == (B, T, H, Dv)
+    assert alpha.shape == (B, T, H) and beta.shape == (B, T, H)
+    S0 = None if S0 is None else _f64(S0)
+    dST = None if dST is None else _f64(dST)
+    for s in (S0, dST):
+        assert s is None or s.shape == (B, H, Dk, Dv)
+    out = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)), dv=np.zeros((B, T, H, Dv)),
+               dalpha=np.zeros((B, T, H)), dbeta=np.zeros((B, T, H)), dS0=np.zeros((B, H, Dk, Dv)))
+    used = ctypes.c_int(0)
+    rc = (_core or _load()).oracle_gdn_recurrence_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dy), _ptr(dST),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]),
+        _ptr(out["dS0"]), B, T, H, Dk, Dv, int(nthreads), ctypes.byref(used))
+    if rc != 0:
+        raise MemoryError("oracle_gdn_recurrence_bwd: allocation failed")
+    last_threads_used = used.value
+    return out
 
 
 def gdn_decode_step(q, k, v, alpha, beta, S, nthreads: int = 0, _core=None):

@@ -160,3 +160,160 @@ int oracle_gdn_decode_step(const double *q, const double *k, const double *v,
     if (threads_used) *threads_used = used;
     return failed ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Reverse mode of eqs (1)-(4): gradients of a scalar loss L whose partial
+ * derivatives with respect to the outputs are given, dL/dy_t = dy_t for every
+ * token and dL/dS_T = dST (NULL: zero).  Per (b, h) the token steps are undone
+ * in reverse order; step t, entered with dS = dL/dS_t (everything after token
+ * t already folded in), applies the chain rule to each of (4), (3), (2), (1):
+ *
+ *   (4) y_t = S_t^T q_t          dS += q_t dy_t^T;   dq_t = S_t dy_t
+ *   (3) S_t = S~ + beta k e^T    dbeta_t = k^T dS e;  de = beta dS^T k;
+ *                                dk_t = beta dS e;    dS~ = dS
+ *   (2) e = v - S~^T k           dv_t = de;  dk_t -= S~ de;  dS~ -= k de^T
+ *   (1) S~ = alpha S_{t-1}       dalpha_t = <S_{t-1}, dS~>;  dS = alpha dS~
+ *
+ * and after token 0, dS0 = dS.  S_{t-1} is needed in reverse order: the states
+ * entering every SEG-th token are kept on the way forward and each segment's
+ * states are recomputed from its checkpoint, in the same token steps as the
+ * forward loop above.
+ *
+ * Layouts as above; dq, dk like q; dv, dy like v; dalpha, dbeta like alpha;
+ * dS0, dST like S0.  Returns 0, or -1 on allocation failure.
+ * ------------------------------------------------------------------------- */
+#define BWD_SEG 64
+
+int oracle_gdn_recurrence_bwd(const double *q, const double *k, const double *v,
+                              const double *alpha, const double *beta, const double *S0,
+                              const double *dy, const double *dST,
+                              double *dq, double *dk, double *dv, double *dalpha,
+                              double *dbeta, double *dS0,
+                              int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                              int nthreads, int *threads_used)
+{
+    const int nt = set_threads(nthreads);
+    const int64_t SS = Dk * Dv;
+    const int64_t nseg = (T + BWD_SEG - 1) / BWD_SEG;
+    int failed = 0;
+    int used = 1;
+    #pragma omp parallel num_threads(nt)
+    {
+        #ifdef _OPENMP
+        #pragma omp single
+        used = omp_get_num_threads();
+        #endif
+        /* ck: state entering token s*SEG for every segment s;
+         * prev: state entering each token of the current segment */
+        double *ck   = (double *)malloc(sizeof(double) * (size_t)((nseg > 0 ? nseg : 1) * SS));
+        double *prev = (double *)malloc(sizeof(double) * (size_t)(BWD_SEG * SS));
+        double *S    = (double *)malloc(sizeof(double) * (size_t)SS);
+        double *St   = (double *)malloc(sizeof(double) * (size_t)SS);
+        double *dS   = (double *)malloc(sizeof(double) * (size_t)SS);
+        double *e    = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *de   = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *yt   = (double *)malloc(sizeof(double) * (size_t)Dv);
+        const int ok = ck && prev && S && St && dS && e && de && yt;
+        if (!ok) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            if (!ok) continue;
+            const int64_t b = bh / H, h = bh % H;
+
+            /* forward, keeping a checkpoint at the start of every segment */
+            if (S0) memcpy(S, S0 + bh * SS, sizeof(double) * (size_t)SS);
+            else    memset(S, 0, sizeof(double) * (size_t)SS);
+            for (int64_t t = 0; t < T; ++t) {
+                if (t % BWD_SEG == 0) memcpy(ck + (t / BWD_SEG) * SS, S, sizeof(double) * (size_t)SS);
+                const int64_t row = (b * T + t) * H + h;
+                gated_delta_token(S, St, e, q + row * Dk, k + row * Dk, v + row * Dv,
+                                  alpha[row], beta[row], yt, Dk, Dv);
+            }
+
+            if (dST) memcpy(dS, dST + bh * SS, sizeof(double) * (size_t)SS);
+            else     memset(dS, 0, sizeof(double) * (size_t)SS);
+
+            for (int64_t s = nseg - 1; s >= 0; --s) {
+                const int64_t t0 = s * BWD_SEG;
+                const int64_t t1 = t0 + BWD_SEG < T ? t0 + BWD_SEG : T;
+                /* states entering tokens t0..t1-1 */
+                memcpy(S, ck + s * SS, sizeof(double) * (size_t)SS);
+                for (int64_t t = t0; t < t1; ++t) {
+                    memcpy(prev + (t - t0) * SS, S, sizeof(double) * (size_t)SS);
+                    const int64_t row = (b * T + t) * H + h;
+                    gated_delta_token(S, St, e, q + row * Dk, k + row * Dk, v + row * Dv,
+                                      alpha[row], beta[row], yt, Dk, Dv);
+                }
+                for (int64_t t = t1 - 1; t >= t0; --t) {
+                    const int64_t row = (b * T + t) * H + h;
+                    const double *qt = q + row * Dk, *kt = k + row * Dk, *vt = v + row * Dv;
+                    const double *dyt = dy + row * Dv;
+                    const double *Sp = prev + (t - t0) * SS;
+                    const double a = alpha[row], bt = beta[row];
+
+                    /* recompute S~, e and S_t of this token */
+                    for (int64_t i = 0; i < SS; ++i) St[i] = a * Sp[i];
+                    for (int64_t j = 0; j < Dv; ++j) {
+                        double pred = 0.0;
+                        for (int64_t i = 0; i < Dk; ++i) pred += St[i * Dv + j] * kt[i];
+                        e[j] = vt[j] - pred;
+                    }
+                    for (int64_t i = 0; i < Dk; ++i)
+                        for (int64_t j = 0; j < Dv; ++j)
+                            S[i * Dv + j] = St[i * Dv + j] + bt * kt[i] * e[j];
+
+                    /* (4) */
+                    for (int64_t i = 0; i < Dk; ++i) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < Dv; ++j) acc += S[i * Dv + j] * dyt[j];
+                        dq[row * Dk + i] = acc;
+                    }
+                    for (int64_t i = 0; i < Dk; ++i)
+                        for (int64_t j = 0; j < Dv; ++j)
+                            dS[i * Dv + j] += qt[i] * dyt[j];
+
+                    /* (3) */
+                    double db = 0.0;
+                    for (int64_t i = 0; i < Dk; ++i)
+                        for (int64_t j = 0; j < Dv; ++j)
+                            db += kt[i] * dS[i * Dv + j] * e[j];
+                    dbeta[row] = db;
+                    for (int64_t j = 0; j < Dv; ++j) {
+                        double acc = 0.0;
+                        for (int64_t i = 0; i < Dk; ++i) acc += dS[i * Dv + j] * kt[i];
+                        de[j] = bt * acc;
+                    }
+                    for (int64_t i = 0; i < Dk; ++i) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < Dv; ++j) acc += dS[i * Dv + j] * e[j];
+                        dk[row * Dk + i] = bt * acc;
+                    }
+
+                    /* (2) */
+                    for (int64_t j = 0; j < Dv; ++j) dv[row * Dv + j] = de[j];
+                    for (int64_t i = 0; i < Dk; ++i) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < Dv; ++j) acc += St[i * Dv + j] * de[j];
+                        dk[row * Dk + i] -= acc;
+                    }
+                    for (int64_t i = 0; i < Dk; ++i)
+                        for (int64_t j = 0; j < Dv; ++j)
+                            dS[i * Dv + j] -= kt[i] * de[j];
+
+                    /* (1) */
+                    double da = 0.0;
+                    for (int64_t i = 0; i < SS; ++i) da += Sp[i] * dS[i];
+                    dalpha[row] = da;
+                    for (int64_t i = 0; i < SS; ++i) dS[i] *= a;
+                }
+            }
+            if (dS0) memcpy(dS0 + bh * SS, dS, sizeof(double) * (size_t)SS);
+        }
+        free(ck); free(prev); free(S); free(St); free(dS); free(e); free(de); free(yt);
+    }
+    if (threads_used) *threads_used = used;
+    return failed ? -1 : 0;
+}

@@ -46,6 +46,7 @@ def _mutant_module(tmp_path, name, old, new):
     ns = types.SimpleNamespace(
         gdn_recurrence=lambda *a, **kw: oracle.gdn_recurrence(*a, _core=core, **kw),
         gdn_decode_step=lambda *a, **kw: oracle.gdn_decode_step(*a, _core=core, **kw),
+        gdn_recurrence_bwd=lambda *a, **kw: oracle.gdn_recurrence_bwd(*a, _core=core, **kw),
     )
     return ns
 
@@ -63,4 +64,39 @@ def test_mutant_is_caught(tmp_path, name):
                 fn(mod)
         except (AssertionError, ValueError):
             caught.append(fn.__name__)
+    assert caught, f"mutant {name} passed every pin"
+
+
+# Mistakes planted in the reverse mode; each must fail a pin of
+# test_oracle_bwd_pins (finite differences, closed form, invariants).
+BWD_MUTANTS = {
+    "bwd-dq-pre-write-state": ("acc += S[i * Dv + j] * dyt[j];", "acc += St[i * Dv + j] * dyt[j];"),
+    "bwd-dbeta-without-dS": ("db += kt[i] * dS[i * Dv + j] * e[j];", "db += kt[i] * e[j];"),
+    "bwd-undecayed-adjoint": ("for (int64_t i = 0; i < SS; ++i) dS[i] *= a;", "(void)a;"),
+    "bwd-dk-sign": ("dk[row * Dk + i] -= acc;", "dk[row * Dk + i] += acc;"),
+    "bwd-dalpha-current-state": ("da += Sp[i] * dS[i];", "da += S[i] * dS[i];"),
+    "bwd-readout-term-dropped": ("dS[i * Dv + j] += qt[i] * dyt[j];", "dS[i * Dv + j] += 0.0 * qt[i] * dyt[j];"),
+    "bwd-de-without-beta": ("de[j] = bt * acc;", "de[j] = acc;"),
+    "bwd-first-checkpoint-only": ("memcpy(S, ck + s * SS,", "memcpy(S, ck,"),
+    "bwd-write-term-not-removed": ("dS[i * Dv + j] -= kt[i] * de[j];", "dS[i * Dv + j] -= 0.0 * kt[i] * de[j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(tmp_path, name):
+    import test_oracle_bwd_pins as bpins
+    old, new = BWD_MUTANTS[name]
+    core = _mutant_module(tmp_path, name, old, new)
+    caught = []
+    for n in dir(bpins):
+        if not n.startswith("test_"):
+            continue
+        fn = getattr(bpins, n)
+        try:
+            if "shape" in fn.__code__.co_varnames[:fn.__code__.co_argcount]:
+                fn(core, (1, 70, 1, 3, 2, 16))
+            else:
+                fn(core)
+        except (AssertionError, ValueError):
+            caught.append(n)
     assert caught, f"mutant {name} passed every pin"
