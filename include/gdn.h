@@ -125,6 +125,46 @@ GDN_API gdn_status gdn_prefill_recurrence(const void *q, const void *k, const vo
                                           hipStream_t stream);
 
 /*
+ * gdn_prefill_bwd -- gradients of gdn_prefill_fwd: the reverse mode of eqs
+ * (1)-(4) ("Theoretical foundations" of the picx.dev summary of "On the Design
+ * of Qwen3.8-Next Architecture") for a scalar loss L, given dL/dy of every
+ * token and dL/dS_T.  Computed chunk by chunk: the states entering every chunk
+ * are recomputed, the state gradient is carried backwards over the chunks, and
+ * each chunk's token gradients follow from those two boundary values.
+ *
+ *   q, k, v, alpha, beta, initial_state   as in gdn_prefill_fwd (the inputs
+ *                 of the forward call whose gradients are wanted)
+ *   dy            [B, T, H, Dv]  float32, dL/dy
+ *   dfinal_state  [B, H, Dk, Dv] float32, dL/dS_T, or NULL for zero
+ *   dq, dk        [B, T, H, Dk]  float32 outputs
+ *   dv            [B, T, H, Dv]  float32 output
+ *   dalpha, dbeta [B, T, H]      float32 outputs
+ *   dinitial_state [B, H, Dk, Dv] float32 output dL/dS_0, or NULL if not wanted
+ *                 (written also when initial_state is NULL: the gradient at S_0 = 0)
+ *   chunk in {16, 32, 64}; Dk, Dv in {16, 32, 64, 128}; B, T, H >= 0.
+ *   workspace     at least gdn_prefill_bwd_workspace_bytes(...) bytes,
+ *                 256-byte aligned, caller-owned: one record per (sequence,
+ *                 head, chunk) holding (I + A)^-1, the masked Q K^T and K K^T
+ *                 blocks and the decay prefix (3C^2 + C floats, rounded up to
+ *                 64), plus the state entering and the state gradient leaving
+ *                 every chunk (2 Dk Dv floats each); 1.5 GB for B=2, T=4096,
+ *                 H=16, d=128, C=64.  Overwritten; nothing kept between calls.
+ * Every output must not overlap any input, another output or the workspace.
+ * T == 0 writes dinitial_state = dfinal_state (or zeros) and nothing else.
+ * All arithmetic is float32 whatever the input dtype.
+ */
+GDN_API size_t gdn_prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                               int64_t Dv, int64_t chunk);
+GDN_API gdn_status gdn_prefill_bwd(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta,
+                                   const float *initial_state, const float *dy,
+                                   const float *dfinal_state, float *dq, float *dk, float *dv,
+                                   float *dalpha, float *dbeta, float *dinitial_state,
+                                   int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                   int64_t chunk, gdn_dtype dtype, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * gdn_decode_step -- one new token for each of N independent sequences: the
  * single-token form of eqs (1)-(4) applied to a stored state, updated in place
  * (the fixed-size state that summarises the prefix).

@@ -29,6 +29,7 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_prepare", "gdn_prefill_recurrence",
+            "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes",
             "gdn_decode_step", "gdn_decode_verify", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
             "gdn_layer_decode_workspace_bytes", "gdn_status_str", "gdn_last_error")
 
@@ -68,6 +69,10 @@ def lib():
     L.gdn_prefill_prepare.restype = ctypes.c_int
     L.gdn_prefill_recurrence.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
     L.gdn_prefill_recurrence.restype = ctypes.c_int
+    L.gdn_prefill_bwd.argtypes = [vp] * 14 + [i64] * 6 + [ctypes.c_int, vp, sz, vp]
+    L.gdn_prefill_bwd.restype = ctypes.c_int
+    L.gdn_prefill_bwd_workspace_bytes.argtypes = [i64] * 6
+    L.gdn_prefill_bwd_workspace_bytes.restype = sz
     L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
@@ -196,6 +201,47 @@ def prefill_recurrence(q, k, v, workspace, initial_state=None, chunk: int = 64, 
                                         B, T, H, Dk, Dv, int(chunk), _ptr(workspace), ws_bytes,
                                         _stream(q.device)))
     return y, final_state
+
+
+def prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk=64) -> int:
+    return int(lib().gdn_prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk)))
+
+
+def prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, dfinal_state=None, chunk: int = 64,
+                want_dinitial_state: bool = True, out=None, workspace=None):
+    """Gradients of prefill for dL/dy = dy [B,T,H,Dv] float32 and dL/dS_T =
+    dfinal_state (or None).  Inputs as for prefill.  `out` may hold
+    preallocated float32 tensors under the names of the result.  Returns a
+    dict dq, dk [B,T,H,Dk], dv [B,T,H,Dv], dalpha, dbeta [B,T,H] and
+    dinitial_state [B,H,Dk,Dv] (None unless wanted)."""
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n in ((alpha, "alpha"), (beta, "beta"), (initial_state, "initial_state"), (dy, "dy"),
+                 (dfinal_state, "dfinal_state")):
+        _need(t, n, torch.float32)
+    shapes = dict(dq=(B, T, H, Dk), dk=(B, T, H, Dk), dv=(B, T, H, Dv), dalpha=(B, T, H), dbeta=(B, T, H),
+                  dinitial_state=(B, H, Dk, Dv))
+    res = dict(out or {})
+    for n, shp in shapes.items():
+        if n == "dinitial_state" and not want_dinitial_state:
+            res.setdefault(n, None)
+            continue
+        if res.get(n) is None:
+            res[n] = torch.empty(shp, dtype=torch.float32, device=q.device)
+        _need(res[n], n, torch.float32)
+    need = prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().gdn_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+                                 _ptr(dy), _ptr(dfinal_state), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+                                 _ptr(res["dalpha"]), _ptr(res["dbeta"]), _ptr(res["dinitial_state"]),
+                                 B, T, H, Dk, Dv, int(chunk), _dtype_code(q), _ptr(workspace), ws_bytes,
+                                 _stream(q.device)))
+    return res
 
 
 def decode_step(q, k, v, alpha, beta, state, y=None):

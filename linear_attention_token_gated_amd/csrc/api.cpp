@@ -370,6 +370,84 @@ gdn_status gdn_layer_fwd(const void *x, const gdn_layer_params *p, const float *
     return hip_status(gdn::launch_layer(a, stream), "gdn_layer_fwd launch");
 }
 
+size_t gdn_prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || !is_pow2_dim(Dk) || !is_pow2_dim(Dv) ||
+        (chunk != 16 && chunk != 32 && chunk != 64))
+        return 0;
+    int64_t n;
+    if (!count(&n, {B, H, (T + chunk - 1) / chunk, gdn::bwd_record_floats(chunk) + 2 * Dk * Dv, 4})) return 0;
+    return gdn::prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk);
+}
+
+gdn_status gdn_prefill_bwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                           const float *initial_state, const float *dy, const float *dfinal_state, float *dq,
+                           float *dk, float *dv, float *dalpha, float *dbeta, float *dinitial_state, int64_t B,
+                           int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk, gdn_dtype dtype,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *fn = "gdn_prefill_bwd";
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0)
+        return fail(GDN_ERR_SHAPE, "%s: negative size", fn);
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+    if (!is_pow2_dim(Dk) || !is_pow2_dim(Dv))
+        return fail(GDN_ERR_UNSUPPORTED, "%s: Dk=%lld Dv=%lld (supported: 16, 32, 64, 128)", fn, (long long)Dk,
+                    (long long)Dv);
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return fail(GDN_ERR_UNSUPPORTED, "%s: chunk=%lld (supported: 16, 32, 64)", fn, (long long)chunk);
+    int64_t n_tok, n_qk, n_v, n_s, n_ch;
+    if (!count(&n_tok, {B, T, H}) || !count(&n_qk, {B, T, H, Dk, 4}) || !count(&n_v, {B, T, H, Dv, 4}) ||
+        !count(&n_s, {B, H, Dk, Dv, 4}) || !count(&n_ch, {B, H, (T + chunk - 1) / chunk}))
+        return fail(GDN_ERR_SHAPE, "%s: sizes overflow", fn);
+    if (n_ch > INT32_MAX || B * H * (Dv / 16) > INT32_MAX)
+        return fail(GDN_ERR_UNSUPPORTED, "%s: B*H*chunks=%lld too large for one launch", fn, (long long)n_ch);
+    if (n_tok > 0) {
+        if (!q || !k || !v || !alpha || !beta || !dy)
+            return fail(GDN_ERR_NULL, "%s: q, k, v, alpha, beta and dy are required", fn);
+        if (!dq || !dk || !dv || !dalpha || !dbeta)
+            return fail(GDN_ERR_NULL, "%s: dq, dk, dv, dalpha and dbeta are required", fn);
+    }
+    const void *ptrs[] = {q, k, v, alpha, beta, initial_state, dy, dfinal_state,
+                          dq, dk, dv, dalpha, dbeta, dinitial_state};
+    const char *names[] = {"q", "k", "v", "alpha", "beta", "initial_state", "dy", "dfinal_state",
+                           "dq", "dk", "dv", "dalpha", "dbeta", "dinitial_state"};
+    for (int i = 0; i < 14; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GDN_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+    const size_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const size_t need = n_tok > 0 ? gdn_prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk) : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(GDN_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+    }
+    const Range inputs[] = {{q, (size_t)n_qk / 4 * esz, "q"}, {k, (size_t)n_qk / 4 * esz, "k"},
+                            {v, (size_t)n_v / 4 * esz, "v"}, {alpha, (size_t)n_tok * 4, "alpha"},
+                            {beta, (size_t)n_tok * 4, "beta"}, {initial_state, (size_t)n_s, "initial_state"},
+                            {dy, (size_t)n_v, "dy"}, {dfinal_state, (size_t)n_s, "dfinal_state"}};
+    const Range outputs[] = {{dq, (size_t)n_qk, "dq"}, {dk, (size_t)n_qk, "dk"}, {dv, (size_t)n_v, "dv"},
+                             {dalpha, (size_t)n_tok * 4, "dalpha"}, {dbeta, (size_t)n_tok * 4, "dbeta"},
+                             {dinitial_state, (size_t)n_s, "dinitial_state"}, {workspace, need, "workspace"}};
+    for (int i = 0; i < 7; ++i) {
+        for (const Range &r : inputs)
+            if (overlap(outputs[i], r)) return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", fn, outputs[i].name, r.name);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outputs[i], outputs[j]))
+                return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", fn, outputs[i].name, outputs[j].name);
+    }
+
+    gdn::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s0 = initial_state;
+    a.dy = dy; a.dsT = dfinal_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = dinitial_state;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.chunk = chunk;
+    a.bf16 = dtype == GDN_BF16;
+    a.ws = need > 0 ? workspace : nullptr;
+    return hip_status(gdn::launch_prefill_bwd(a, stream), fn);
+}
+
 size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
 {
     if (N < 0 || hidden < 0 || H < 0 || Dk < 0 || Dv < 0) return 0;

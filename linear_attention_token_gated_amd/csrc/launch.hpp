@@ -53,6 +53,24 @@ size_t prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t chunk, b
 hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_recurrence(const PrefillArgs &a, hipStream_t stream);
 
+// Gradients of the prefill (backward.hip): dL/dq, dk, dv, dalpha, dbeta, dS_0
+// from dL/dy and dL/dS_T
+struct BwdArgs {
+    const void *q, *k, *v;          // [B, T, H, Dk], [B, T, H, Dv]
+    const float *alpha, *beta;      // [B, T, H]
+    const float *s0;                // [B, H, Dk, Dv] or null
+    const float *dy;                // [B, T, H, Dv]
+    const float *dsT;               // [B, H, Dk, Dv] or null
+    float *dq, *dk, *dv, *dalpha, *dbeta;
+    float *ds0;                     // [B, H, Dk, Dv] or null
+    int64_t B, T, H, Dk, Dv, chunk;
+    bool bf16;
+    void *ws;                       // prefill_bwd_workspace_bytes(...) bytes, 256-byte aligned
+};
+int64_t bwd_record_floats(int64_t C);
+size_t prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C);
+hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
+
 // Layer helpers (layer.hip)
 struct LayerArgs {
     const void *x;

@@ -81,27 +81,6 @@ struct KParams {
     int xcd_map;             // 1: group the slices of a head on one XCD
 };
 
-// Forward substitution of (I + L) X = I for a 16x16 strictly lower L, inside
-// one wavefront.  Lane (r = l%16, g = l/16) owns row r of X, columns g+4i.
-// Step s: row s is final; every row r > s subtracts L[r][s] * X[s][:].
-// X[s][c] lives in lane s of the same 16-lane row (same g) -> DPP broadcast.
-template <int S>
-__device__ __forceinline__ void tri_step(float (&X)[4], const float (&Lr)[16], int r) {
-    // rows r <= S have L[r][S] = 0 (L is strictly lower), so the update is an
-    // exact no-op there and needs no select
-    (void)r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float xs = row_bcast<S>(X[i]);
-        X[i] = fmaf(-Lr[S], xs, X[i]);
-    }
-}
-template <int... S>
-__device__ __forceinline__ void tri_solve16(float (&X)[4], const float (&Lr)[16], int r,
-                                            std::integer_sequence<int, S...>) {
-    (tri_step<S>(X, Lr, r), ...);
-}
-
 template <typename Tin, int C, int DK>
 __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
 {

@@ -140,6 +140,24 @@ def prefill_config_inputs(cfg: PrefillConfig):
     return prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.dtype, cfg.s0_std, cfg.seed)
 
 
+def bwd_inputs(B, T, H, Dk, Dv, dtype="bf16", s0_std=None, seed=0, dst_std=None):
+    """Inputs of a prefill backward: the prefill recipe's inputs (same seed,
+    same draws) plus the output gradients dy ~ N(0, 1) [B, T, H, Dv] and
+    dST ~ N(0, dst_std^2) [B, H, Dk, Dv] (None if dst_std is None), float32,
+    drawn from a generator seeded with seed + 500."""
+    inp = prefill_inputs(B, T, H, Dk, Dv, dtype, s0_std, seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 500))
+    inp["dy"] = rng.standard_normal((B, T, H, Dv), dtype=np.float32)
+    inp["dST"] = None
+    if dst_std is not None:
+        inp["dST"] = (rng.standard_normal((B, H, Dk, Dv), dtype=np.float32) * np.float32(dst_std)).astype(np.float32)
+    return inp
+
+
+def bwd_config_inputs(cfg: PrefillConfig, dst_std=1.0):
+    return bwd_inputs(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.dtype, cfg.s0_std, cfg.seed, dst_std)
+
+
 def decode_inputs(N, H, Dk, Dv, dtype="bf16", s_std=0.02, seed=3):
     """One token per sequence, same distributions as the prefill recipe;
     state S ~ N(0, s_std^2) in float32."""

@@ -226,3 +226,40 @@ def test_bench_record_size_matches_library(L):
     import bench
     for C in (16, 32, 64):
         assert bench.record_bytes(C) == L.gdn_prefill_workspace_bytes(1, C, 1, 128, 128, C, 1)
+
+
+def prefill_bwd(L, q=A, k=A + 8 * MB, v=A + 16 * MB, al=A + 24 * MB, be=A + 25 * MB, s0=A + 26 * MB,
+                dy=A + 32 * MB, dsT=A + 40 * MB, dq=A + 48 * MB, dk=A + 56 * MB, dv=A + 64 * MB,
+                da=A + 72 * MB, db=A + 73 * MB, ds0=A + 74 * MB, B=1, T=64, H=2, Dk=16, Dv=16, C=16, dt=0,
+                w=A + 512 * MB, wb=None):
+    if wb is None:
+        wb = L.gdn_prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, C)
+    return L.gdn_prefill_bwd(q, k, v, al, be, s0, dy, dsT, dq, dk, dv, da, db, ds0, B, T, H, Dk, Dv, C, dt,
+                             w, wb, None)
+
+
+def test_prefill_bwd_validation(L):
+    need = L.gdn_prefill_bwd_workspace_bytes(1, 64, 2, 16, 16, 16)
+    # one record of 3*16*16+16 floats (rounded up to 64) plus two 16x16 states per chunk
+    assert need == 4 * 2 * 4 * (832 + 2 * 256)
+    assert L.gdn_prefill_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64) == 4 * 32 * 64 * (12352 + 2 * 16384)
+    assert L.gdn_prefill_bwd_workspace_bytes(1, 0, 2, 16, 16, 16) == 0
+    assert L.gdn_prefill_bwd_workspace_bytes(1, 64, 2, 48, 16, 16) == 0
+    assert prefill_bwd(L, q=None) == NULL
+    assert prefill_bwd(L, dy=None) == NULL
+    assert prefill_bwd(L, db=None) == NULL
+    assert prefill_bwd(L, T=-1) == SHAPE
+    assert prefill_bwd(L, Dk=48) == UNSUP
+    assert prefill_bwd(L, C=128) == UNSUP
+    assert prefill_bwd(L, dt=7) == UNSUP
+    assert prefill_bwd(L, w=None) == WS
+    assert prefill_bwd(L, wb=need - 1) == WS
+    assert prefill_bwd(L, w=A + 512 * MB + 16) == ALIGN
+    assert prefill_bwd(L, dq=A + 48 * MB + 4) == ALIGN
+    assert prefill_bwd(L, dq=A) == ALIAS                   # dq over q
+    assert prefill_bwd(L, dv=A + 56 * MB) == ALIAS         # dv over dk
+    assert prefill_bwd(L, ds0=A + 26 * MB) == ALIAS        # dS_0 over initial_state
+    assert prefill_bwd(L, w=A + 64 * MB) == ALIAS          # workspace over dv
+    assert "gdn_prefill_bwd" in L.gdn_last_error().decode()
+    # T == 0 needs no workspace and checks only what it writes
+    assert prefill_bwd(L, T=0, w=None, wb=0, q=None, dq=None, ds0=A + 26 * MB) == ALIAS

@@ -1,0 +1,112 @@
+"""GPU parity of gdn_prefill_bwd (chunked reverse mode) against the fp64
+token-by-token reverse mode of the oracle, element by element, for every
+gradient: dq, dk, dv, dalpha, dbeta and dS_0."""
+import numpy as np
+import pytest
+
+from helpers import TOL_F32, dev, host, rel_err
+from linear_attention_token_gated_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GRADS = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dalpha", "dalpha"), ("dbeta", "dbeta"),
+         ("dinitial_state", "dS0"))
+
+
+def _gpu(inp, chunk, **kw):
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    g = gdn.prefill_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["alpha"]), dev(inp["beta"]),
+                        dev(inp["dy"]), initial_state=dev(inp["S0"]), dfinal_state=dev(inp["dST"]), chunk=chunk, **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(oracle, inp):
+    return oracle.gdn_recurrence_bwd(*(wl.widen(inp[n]) for n in ("q", "k", "v", "alpha", "beta")),
+                                     wl.widen(inp["S0"]), wl.widen(inp["dy"]), wl.widen(inp["dST"]))
+
+
+def _check(oracle, inp, chunk, tol=TOL_F32):
+    g = _gpu(inp, chunk)
+    ref = _oracle(oracle, inp)
+    errs = {n: rel_err(host(g[n]), ref[r]) for n, r in GRADS}
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (32, 64), (64, 32), (128, 128), (16, 128)])
+def test_bwd_shapes_chunks_ragged(oracle_mod, dtype, chunk, Dk, Dv):
+    T = 3 * chunk + 5            # several chunks and a ragged tail
+    print(f"case: bwd B=2 T={T} H=3 Dk={Dk} Dv={Dv} C={chunk} {dtype}", flush=True)
+    inp = wl.bwd_inputs(2, T, 3, Dk, Dv, dtype=dtype, s0_std=0.3, seed=Dk + 3 * Dv + chunk, dst_std=1.0)
+    _check(oracle_mod, inp, chunk)
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 17, 63, 64, 65])
+def test_bwd_short_sequences(oracle_mod, T):
+    print(f"case: bwd short T={T}", flush=True)
+    inp = wl.bwd_inputs(1, T, 2, 64, 64, dtype="f32", s0_std=0.2, seed=T, dst_std=0.5)
+    _check(oracle_mod, inp, 64)
+
+
+def test_bwd_no_state_no_final_gradient(oracle_mod):
+    """initial_state and dfinal_state NULL; dinitial_state is still the gradient at S_0 = 0."""
+    print("case: bwd without S0 / dST", flush=True)
+    inp = wl.bwd_inputs(2, 150, 2, 128, 128, dtype="bf16", s0_std=None, seed=7, dst_std=None)
+    _check(oracle_mod, inp, 64)
+
+
+def test_bwd_empty_sequence():
+    """T = 0: only dinitial_state = dfinal_state is written."""
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    print("case: bwd T=0", flush=True)
+    inp = wl.bwd_inputs(2, 0, 2, 32, 32, dtype="f32", s0_std=0.1, seed=3, dst_std=1.0)
+    g = _gpu(inp, 64)
+    assert np.array_equal(host(g["dinitial_state"]), wl.widen(inp["dST"]))
+    inp["dST"] = None
+    g = _gpu(inp, 64)
+    assert not host(g["dinitial_state"]).any()
+
+
+def test_bwd_chunk_size_invariance(oracle_mod):
+    print("case: bwd chunk invariance C=16/32/64", flush=True)
+    inp = wl.bwd_inputs(1, 200, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=11, dst_std=1.0)
+    ref = _oracle(oracle_mod, inp)
+    for C in (16, 32, 64):
+        g = _gpu(inp, C)
+        for n, r in GRADS:
+            assert rel_err(host(g[n]), ref[r]) <= TOL_F32, (C, n)
+
+
+def test_bwd_repeatable():
+    """Same inputs, same bits: every reduction has a fixed order."""
+    print("case: bwd bitwise repeatable", flush=True)
+    inp = wl.bwd_inputs(1, 300, 2, 128, 128, dtype="bf16", s0_std=0.02, seed=12, dst_std=1.0)
+    a, b = _gpu(inp, 64), _gpu(inp, 64)
+    for n, _ in GRADS:
+        assert np.array_equal(host(a[n]), host(b[n])), n
+
+
+def test_bwd_4k_bf16_sampled_heads(oracle_mod):
+    """The 4K-token workload at full size in the benchmark's launch
+    configuration; the oracle recomputes two whole (sequence, head) pairs."""
+    cfg = wl.PREFILL_4K
+    print(f"case: bwd {cfg.name} sampled heads", flush=True)
+    inp = wl.bwd_config_inputs(cfg)
+    g = _gpu(inp, cfg.chunk)
+    for b, h in ((0, 3), (1, cfg.H - 1)):
+        sub = {n: None if inp[n] is None else
+               inp[n][b:b + 1, h:h + 1] if n in ("S0", "dST") else inp[n][b:b + 1, :, h:h + 1]
+               for n in ("q", "k", "v", "alpha", "beta", "dy", "S0", "dST")}
+        ref = _oracle(oracle_mod, sub)
+        for n, r in GRADS:
+            x = host(g[n])
+            x = x[b:b + 1, :, h:h + 1] if n != "dinitial_state" else x[b:b + 1, h:h + 1]
+            e = rel_err(x, ref[r])
+            print(f"  b={b} h={h} {n}={e:.2e}", flush=True)
+            assert e <= TOL_F32, (b, h, n, e)
