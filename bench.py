@@ -9,7 +9,8 @@ input already resident in HBM: gdn_prefill_prepare (the per-chunk
 preparation kernel) then gdn_prefill_recurrence (the state recurrence
 kernel), which together are exactly gdn_prefill_fwd.  The line printed also
 carries the decode step (256 sequences x 32 heads, fp32 128x128 states
-updated in place) and the full layer (B=1, T=16384, hidden 2048, H=16)
+updated in place), the full layer (B=1, T=16384, hidden 2048, H=16) and the
+backward of the 32K prefill (every input gradient from dy and dS_T)
 measured the same way, the roofline of the recurrence kernel (the larger part
 of the step) with the preparation kernel beside it, and the fp64 oracle timed
 on the host cores on a bounded sample of the same workload.
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=32K (MFMA % peak); decode state GB/s (HBM % peak)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -91,6 +93,23 @@ def layer_decode_alg(N, hidden, H, Dk, Dv, conv_k):
     weights = 2 * hidden * (nqkv + H * Dv + 2 * H) + 2 * H * Dv * hidden
     return (weights + N * hidden * 2 + 2 * N * (conv_k - 1) * nqkv * 4 + 2 * N * H * Dk * Dv * 4
             + N * hidden * 4)
+
+
+def bwd_flops(B, T, H, Dk, Dv, C):
+    """Flops of the chunked reverse mode, per (sequence, head, chunk) summed
+    over its four kernels: the Gram blocks and inverse of the preparation, the
+    two state passes (K S, the triangular C x C products, the state updates)
+    and the chunk gradients (K S, Q S, K dS', three triangular products, dP and
+    dA, the three C x Dk outer-product sums over Dv, and the four C x C by C x
+    Dk products of dQ and dK).  Triangular products count the 16 x 16 blocks
+    on and below the diagonal."""
+    nb = C // 16
+    tri = nb * (nb + 1) // 2 * 256            # entries of the lower blocks
+    prep = 2 * tri * Dk + C ** 3 / 6.0
+    fwd = 2 * C * Dk * Dv + tri * Dv
+    adj = 3 * C * Dk * Dv + 2 * tri * Dv
+    chunk = 6 * C * Dk * Dv + 5 * tri * Dv + 4 * tri * Dk
+    return 2.0 * B * H * (-(-T // C)) * (prep + fwd + adj + chunk)
 
 
 def layer_flops(B, T, hidden, H, Dk, Dv, C):
@@ -238,6 +257,23 @@ def bench_layer_decode(args, torch, gdn, wl):
     return cfg, total_ms, per
 
 
+def bench_bwd(args, torch, gdn, wl):
+    cfg = wl.PREFILL_32K
+    inp = wl.bwd_config_inputs(cfg)
+    t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "dy", "S0", "dST")}
+    out = {n: torch.empty(shp, dtype=torch.float32, device="cuda") for n, shp in
+           (("dq", (cfg.B, cfg.T, cfg.H, cfg.Dk)), ("dk", (cfg.B, cfg.T, cfg.H, cfg.Dk)),
+            ("dv", (cfg.B, cfg.T, cfg.H, cfg.Dv)), ("dalpha", (cfg.B, cfg.T, cfg.H)),
+            ("dbeta", (cfg.B, cfg.T, cfg.H)), ("dinitial_state", (cfg.B, cfg.H, cfg.Dk, cfg.Dv)))}
+    ws = torch.empty(gdn.prefill_bwd_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda: gdn.prefill_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["dy"], t["S0"], t["dST"],
+                                 chunk=cfg.chunk, out=out, workspace=ws)
+    steps = max(1, min(args.steps, 10))
+    total_ms, per = time_launches(fn, steps, max(1, min(args.warmup, 2)), torch)
+    return cfg, total_ms, per, steps
+
+
 def cpu_baseline(inp, cfg, wl, sample_T):
     """The oracle, untouched, on the first sample_T tokens of every head."""
     import oracle
@@ -283,6 +319,7 @@ def main():
         bench_layer(pargs, torch, gdn, wl)
         bench_layer_decode(pargs, torch, gdn, wl)
         bench_verify(pargs, torch, gdn, wl)
+        bench_bwd(pargs, torch, gdn, wl)
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -331,6 +368,16 @@ def main():
     verify = {"workload": v_cfg.name, "ms_per_step": round(v_ms, 4), "alg_bytes_per_step": v_bytes,
               "GBps": v_bytes / (v_ms * 1e-3) / 1e9, "hbm_frac": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
+    b_cfg, b_total, b_per, b_steps = bench_bwd(args, torch, gdn, wl)
+    b_ms = float(np.mean(b_per))
+    b_flops = bwd_flops(b_cfg.B, b_cfg.T, b_cfg.H, b_cfg.Dk, b_cfg.Dv, b_cfg.chunk)
+    bwd = {"workload": b_cfg.name + ", gradients of every input from dy and dS_T",
+           "ms_per_call": round(b_ms, 4), "tokens_per_s": b_cfg.B * b_cfg.T / (b_ms * 1e-3),
+           "bwd_over_fwd": b_ms / ms_step, "flops_alg_per_call": b_flops,
+           "tflops_achieved": b_flops / (b_ms * 1e-3) / 1e12, "peak_tflops": FP32_PEAK_TFLOPS,
+           "frac": b_flops / (b_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+           "note": "four kernels (prep, state pass, adjoint state pass, chunk gradients), all fp32 MFMA"}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, cfg, wl, min(args.cpu_sample_tokens, cfg.T))
@@ -377,6 +424,7 @@ def main():
         "layer": layer,
         "layer_decode": layer_decode,
         "verify": verify,
+        "bwd": bwd,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }

@@ -146,9 +146,11 @@ GDN_API gdn_status gdn_prefill_recurrence(const void *q, const void *k, const vo
  *                 256-byte aligned, caller-owned: one record per (sequence,
  *                 head, chunk) holding (I + A)^-1, the masked Q K^T and K K^T
  *                 blocks and the decay prefix (3C^2 + C floats, rounded up to
- *                 64), plus the state entering and the state gradient leaving
- *                 every chunk (2 Dk Dv floats each); 1.5 GB for B=2, T=4096,
- *                 H=16, d=128, C=64.  Overwritten; nothing kept between calls.
+ *                 64), the state entering and the state gradient leaving
+ *                 every chunk (Dk Dv floats each), and the chunk's U,
+ *                 V - diag(e^G) K S and dX (C Dv floats each); 0.57 GB for
+ *                 B=2, T=4096, H=16, d=128, C=64 and 4.6 GB for B=1,
+ *                 T=32768, H=32.  Overwritten; nothing kept between calls.
  * Every output must not overlap any input, another output or the workspace.
  * T == 0 writes dinitial_state = dfinal_state (or zeros) and nothing else.
  * All arithmetic is float32 whatever the input dtype.

@@ -50,6 +50,7 @@ struct BwdParams {
     const float *alpha, *beta, *s0, *dy, *dsT;
     float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
     float *rec, *sc, *dsc;
+    float *ub, *wb, *dxb;      // per chunk [C][Dv]: U, W~ = V - e^G K S (state pass), dX (adjoint pass)
     int64_t T, H, Dv, NC;
     int64_t rec_floats;
 };
@@ -59,48 +60,74 @@ template <int C> struct Rec {
     static constexpr int oT = 0, oP = C * C, oA = 2 * C * C, oG = 3 * C * C;
 };
 
-__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ f32x4 load4(const __bf16 *p) {
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-}
+// Register-staged copies into LDS.  Every load of a tile is issued before any
+// of them is used (fixed trip counts, raw input kept in registers), so a tile
+// costs one memory latency, and the next chunk's tiles can be in flight while
+// the current chunk is computed.  Conversion to fp32 happens at the LDS store.
+template <typename Tin> struct Raw4;
+template <> struct Raw4<float> {
+    using type = f32x4;
+    static __device__ __forceinline__ type load(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+    static __device__ __forceinline__ type zero() { return zero4(); }
+    static __device__ __forceinline__ f32x4 widen(type x) { return x; }
+};
+template <> struct Raw4<__bf16> {
+    using type = bf16x4;
+    static __device__ __forceinline__ type load(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+    static __device__ __forceinline__ type zero() { return bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f}; }
+    static __device__ __forceinline__ f32x4 widen(type x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+};
 
-// Rows t = c0 .. c0+C-1 of head h of a [B, T, H, D] tensor into LDS (pitch P
-// floats), zeros past T.
-template <typename Tin, int C, int D, int P>
-__device__ __forceinline__ void stage_rows(float *dst, const Tin *src, int64_t b, int64_t h, int64_t c0, int64_t T,
-                                           int64_t H) {
-    for (int i = threadIdx.x; i < C * D / 4; i += NT) {
-        const int r = i / (D / 4), col = (i % (D / 4)) * 4;
-        const int64_t t = c0 + r;
-        f32x4 x = zero4();
-        if (t < T) x = load4(src + ((b * T + t) * H + h) * D + col);
-        *reinterpret_cast<f32x4 *>(dst + r * P + col) = x;
+// Rows t = c0 .. c0+C-1, columns n0 .. n0+W-1 of head h of a [B, T, H, ld]
+// tensor; zeros past T.  Stored with pitch P floats.
+template <typename Tin, int C, int W, int NTH = NT> struct RowsTile {
+    using R = Raw4<Tin>;
+    static constexpr int NU = C * W / 4, NV = (NU + NTH - 1) / NTH;
+    typename R::type v[NV];
+    __device__ __forceinline__ void load(const Tin *src, int64_t b, int64_t h, int64_t c0, int64_t T, int64_t H,
+                                         int64_t ld, int n0 = 0) {
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int vi = threadIdx.x + NTH * it;
+            const int r = vi / (W / 4), col = (vi % (W / 4)) * 4;
+            const int64_t t = c0 + r;
+            v[it] = R::zero();
+            if ((NU % NTH == 0 || vi < NU) && t < T) v[it] = R::load(src + ((b * T + t) * H + h) * ld + n0 + col);
+        }
     }
-}
+    template <int P> __device__ __forceinline__ void store(float *dst) const {
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int vi = threadIdx.x + NTH * it;
+            const int r = vi / (W / 4), col = (vi % (W / 4)) * 4;
+            if (NU % NTH == 0 || vi < NU) *reinterpret_cast<f32x4 *>(dst + r * P + col) = R::widen(v[it]);
+        }
+    }
+};
 
-// C x 16 slice (columns n0..n0+15) of rows c0.. of head h of a [B, T, H, Dv]
-// tensor, into LDS with pitch VP.
-template <typename Tin, int C>
-__device__ __forceinline__ void stage_slice(float *dst, const Tin *src, int64_t b, int64_t h, int64_t c0, int64_t T,
-                                            int64_t H, int64_t Dv, int n0) {
-    for (int i = threadIdx.x; i < C * 4; i += NT) {
-        const int r = i >> 2, col = (i & 3) * 4;
-        const int64_t t = c0 + r;
-        f32x4 x = zero4();
-        if (t < T) x = load4(src + ((b * T + t) * H + h) * Dv + n0 + col);
-        *reinterpret_cast<f32x4 *>(dst + r * VP + col) = x;
+// R x W block of a dense row-major fp32 matrix with row stride `ld`, stored
+// with pitch P floats.
+template <int R, int W, int NTH = NT> struct DenseTile {
+    static constexpr int NU = R * W / 4, NV = (NU + NTH - 1) / NTH;
+    f32x4 v[NV];
+    __device__ __forceinline__ void load(const float *src, int64_t ld) {
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int vi = threadIdx.x + NTH * it;
+            const int r = vi / (W / 4), col = (vi % (W / 4)) * 4;
+            v[it] = zero4();
+            if (NU % NTH == 0 || vi < NU) v[it] = *reinterpret_cast<const f32x4 *>(src + r * ld + col);
+        }
     }
-}
-
-// C x C matrix (dense, row-major) into LDS with pitch P
-template <int C, int P>
-__device__ __forceinline__ void stage_cc(float *dst, const float *src) {
-    for (int i = threadIdx.x; i < C * C / 4; i += NT) {
-        const int r = i / (C / 4), col = (i % (C / 4)) * 4;
-        *reinterpret_cast<f32x4 *>(dst + r * P + col) = load4(src + r * C + col);
+    template <int P> __device__ __forceinline__ void store(float *dst) const {
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int vi = threadIdx.x + NTH * it;
+            const int r = vi / (W / 4), col = (vi % (W / 4)) * 4;
+            if (NU % NTH == 0 || vi < NU) *reinterpret_cast<f32x4 *>(dst + r * P + col) = v[it];
+        }
     }
-}
+};
 
 // lower-triangle block index -> (rb, cb), row-major over rb
 __device__ __forceinline__ void tri_block(int idx, int &rb, int &cb) {
@@ -109,12 +136,13 @@ __device__ __forceinline__ void tri_block(int idx, int &rb, int &cb) {
     cb = idx - rb * (rb + 1) / 2;
 }
 
-// sum over the 16 lanes of each 16-lane row
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+// Sum over the 16 lanes of each 16-lane row, left in the row's last lane
+// (ln == 15): an inclusive scan by DPP row shifts, no LDS traffic.
+__device__ __forceinline__ float row16_total(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
     return x;
 }
 
@@ -137,8 +165,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     const int64_t H = p.H, T = p.T, b = bh / H, h = bh % H, c0 = c * C;
     float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
 
-    stage_rows<Tin, C, DK, KP>(Ks, static_cast<const Tin *>(p.k), b, h, c0, T, H);
-    stage_rows<Tin, C, DK, KP>(Qs, static_cast<const Tin *>(p.q), b, h, c0, T, H);
+    {
+        RowsTile<Tin, C, DK> tk, tq;
+        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
+        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+        tk.template store<KP>(Ks);
+        tq.template store<KP>(Qs);
+    }
     if (wave == 0) {
         const int64_t t = c0 + lane;
         const bool ok = lane < C && t < T;
@@ -295,10 +328,47 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
         }
     }
 
-    for (int64_t it = 0; it < NC; ++it) {
-        const int64_t c = ADJ ? NC - 1 - it : it;
+    // registers holding the next chunk's tiles
+    using InT = typename std::conditional<ADJ, float, Tin>::type;
+    RowsTile<Tin, C, DK> rk, rq;
+    DenseTile<C, C> rt, rp;
+    RowsTile<InT, C, BV> ri;
+    float rg = 0.f, rbeta = 0.f;
+    auto fetch = [&](int64_t c) {
         const int64_t c0 = c * C;
         const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
+        rk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
+        rt.load(rec + Rec<C>::oT, C);
+        if constexpr (ADJ) {
+            rq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+            rp.load(rec + Rec<C>::oP, C);
+            ri.load(p.dy, b, h, c0, T, H, Dv, n0);
+        } else {
+            ri.load(static_cast<const Tin *>(p.v), b, h, c0, T, H, Dv, n0);
+        }
+        if (threadIdx.x < C) {
+            const int64_t t = c0 + threadIdx.x;
+            rg = rec[Rec<C>::oG + threadIdx.x];
+            rbeta = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
+        }
+    };
+    fetch(ADJ ? NC - 1 : 0);
+
+    for (int64_t it = 0; it < NC; ++it) {
+        const int64_t c = ADJ ? NC - 1 - it : it;
+
+        rk.template store<KP>(Ks);
+        rt.template store<CP>(Ts);
+        ri.template store<VP>(Ins);
+        if constexpr (ADJ) {
+            rq.template store<KP>(Qs);
+            rp.template store<CP>(Ps);
+        }
+        if (threadIdx.x < C) {
+            Gs[threadIdx.x] = rg;
+            Bs[threadIdx.x] = rbeta;
+        }
+        if (it + 1 < NC) fetch(ADJ ? c - 1 : c + 1);
 
         // keep the state at this chunk boundary for the chunk-gradient pass,
         // and stage it transposed as the B operand of K S
@@ -314,20 +384,6 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                     STs[ln * KP + row] = S[m][e];
                 }
             }
-        }
-        stage_rows<Tin, C, DK, KP>(Ks, static_cast<const Tin *>(p.k), b, h, c0, T, H);
-        stage_cc<C, CP>(Ts, rec + Rec<C>::oT);
-        if constexpr (ADJ) {
-            stage_rows<Tin, C, DK, KP>(Qs, static_cast<const Tin *>(p.q), b, h, c0, T, H);
-            stage_cc<C, CP>(Ps, rec + Rec<C>::oP);
-            stage_slice<float, C>(Ins, p.dy, b, h, c0, T, H, Dv, n0);
-        } else {
-            stage_slice<Tin, C>(Ins, static_cast<const Tin *>(p.v), b, h, c0, T, H, Dv, n0);
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            const int64_t t = c0 + i;
-            Gs[i] = rec[Rec<C>::oG + i];
-            Bs[i] = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
         }
         __syncthreads();
         const float GC = Gs[C - 1];
@@ -355,10 +411,13 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Xs[(16 * rb + 4 * lg + e) * VP + ln] = acc[e];
             } else {
+                float *wg = p.wb + (bh * NC + c) * C * Dv + n0 + ln;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
-                    Xs[r * VP + ln] = Bs[r] * (Ins[r * VP + ln] - __builtin_amdgcn_exp2f(Gs[r]) * ks[e]);
+                    const float wt = Ins[r * VP + ln] - __builtin_amdgcn_exp2f(Gs[r]) * ks[e];
+                    Xs[r * VP + ln] = Bs[r] * wt;
+                    wg[r * Dv] = wt;
                 }
             }
         }
@@ -373,19 +432,27 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                 for (int kb = rb; kb < NB; ++kb)
                     acc = F16::mma(frag_cols<float, 16>(Ts, CP, 16 * rb, 16 * kb, lane),
                                    frag_cols<float, 16>(Xs, VP, 0, 16 * kb, lane), acc);
+                // acc = dX = T^T dU; dV = diag(beta) dX
+                float *xg = p.dxb + (bh * NC + c) * C * Dv + n0 + ln;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
+                    const int64_t t = c * C + r;
                     UdT[ln * CP + r] = -__builtin_amdgcn_exp2f(Gs[r]) * Bs[r] * acc[e];
+                    xg[r * Dv] = acc[e];
+                    if (t < T) p.dv[((b * T + t) * H + h) * Dv + n0 + ln] = Bs[r] * acc[e];
                 }
             } else {
                 for (int kb = 0; kb <= rb; ++kb)
                     acc = F16::mma(frag_rows<float, 16>(Ts, CP, 16 * rb, 16 * kb, lane),
                                    frag_cols<float, 16>(Xs, VP, 0, 16 * kb, lane), acc);
+                // acc = U = T X
+                float *ug = p.ub + (bh * NC + c) * C * Dv + n0 + ln;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
                     UdT[ln * CP + r] = __builtin_amdgcn_exp2f(GC - Gs[r]) * acc[e];
+                    ug[r * Dv] = acc[e];
                 }
             }
         }
@@ -428,45 +495,51 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
 
 // ===========================================================================
 // 4. chunk gradients
+//
+// U, W~ (state pass) and dX (adjoint pass) of the chunk are read back, so
+// every value slice only adds outer products into accumulators:
+//   dP += dY U^T, dM += dX U^T (lower blocks),
+//   dQa += dY S^T, dKa += dX S^T, dKb += U dS'^T.
+// The per-token terms of dG that involve K S, Q S and K dS' are row dot
+// products with these sums: sum_j dY_rj (QS)_rj = q_r . dQa_r,
+// sum_j dX_rj (KS)_rj = k_r . dKa_r, sum_j U_rj (K dS')_rj = k_r . dKb_r.
 // ===========================================================================
 template <int C, int DK> struct GradLay {
-    static constexpr int KP = DK + 4, CP = C + 4, NB = C / 16;
+    static constexpr int KP = DK + 4, CP = C + 4, NB = C / 16, NKB = DK / 16;
     static constexpr size_t oK = 0;
     static constexpr size_t oQ = oK + 4 * C * KP;
-    static constexpr size_t oT = oQ + 4 * C * KP;          // T, then dKK
+    static constexpr size_t oT = oQ + 4 * C * KP;          // dKK
     static constexpr size_t oP = oT + 4 * C * CP;          // P, then dQK
     // S slice [DK][VP] and dS' slice [DK][VP]; Ak [C][CP] over both after the slices
     static constexpr size_t SREG = 2 * DK * VP > C * CP ? 2 * DK * VP : C * CP;
     static constexpr size_t oS = oP + 4 * C * CP;
     static constexpr size_t oDS = oS + 4 * DK * VP;
     static constexpr size_t oDY = oS + 4 * SREG;
-    static constexpr size_t oX = oDY + 4 * C * VP;
-    static constexpr size_t oU = oX + 4 * C * VP;
-    static constexpr size_t oDU = oU + 4 * C * VP;
-    static constexpr size_t oDX = oDU + 4 * C * VP;
+    static constexpr size_t oU = oDY + 4 * C * VP;
+    static constexpr size_t oDX = oU + 4 * C * VP;
     static constexpr size_t oG = oDX + 4 * C * VP;
     static constexpr size_t oB = oG + 4 * C;
     static constexpr size_t oAl = oB + 4 * C;
-    static constexpr size_t oTG = oAl + 4 * C;             // per-token dG partials
-    static constexpr size_t oTB = oTG + 4 * C;             // per-token dbeta partials
-    static constexpr size_t oRP = oTB + 4 * C;                 // [2][NB][NB][16] row sums (P part, A part)
+    static constexpr size_t oTB = oAl + 4 * C;                 // per-token sum_j dX_rj W~_rj
+    static constexpr size_t oSP = oTB + 4 * C;                 // [3][NB*NKB][16] row dot products per tile
+    static constexpr size_t oRP = oSP + 4 * 3 * NB * NKB * 16; // [2][NB][NB][16] row sums (P part, A part)
     static constexpr size_t oCP = oRP + 4 * 2 * NB * NB * 16;  // [2][NB][NB][16] column sums
     static constexpr size_t oRB = oCP + 4 * 2 * NB * NB * 16;  // [NB][NB][16] dbeta row sums
     static constexpr size_t oRed = oRB + 4 * NB * NB * 16;
-    static constexpr size_t BYTES = oRed + 4 * 8;
+    static constexpr size_t BYTES = oRed + 4 * 16;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+constexpr int NWG = 8, NTG = 64 * NWG;   // chunk-gradient kernel: 8 wavefronts, two per SIMD
+
 template <typename Tin, int C, int DK>
-__global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
+__global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
 {
     using L = GradLay<C, DK>;
     constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16;
-    constexpr int KSD = DK % 32 == 0 ? 32 : 16;
     constexpr int NTRI = NB * (NB + 1) / 2;
-    constexpr int NCC = (2 * NTRI + 3) / 4;            // C x C tiles per wave (dP, dM)
-    constexpr int NTILE = NB * NKB, NCK = (NTILE + 3) / 4;   // C x DK tiles per wave
-    using FD = Frag<float, KSD>;
+    constexpr int NCC = (2 * NTRI + NWG - 1) / NWG;              // C x C tiles per wave (dP, dM)
+    constexpr int NTILE = NB * NKB, NCK = (NTILE + NWG - 1) / NWG; // C x DK tiles per wave
     using F16 = Frag<float, 16>;
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -477,15 +550,13 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     float *Ss = reinterpret_cast<float *>(smem + L::oS);
     float *dSs = reinterpret_cast<float *>(smem + L::oDS);
     float *dYs = reinterpret_cast<float *>(smem + L::oDY);
-    float *Xs = reinterpret_cast<float *>(smem + L::oX);
     float *Us = reinterpret_cast<float *>(smem + L::oU);
-    float *dUs = reinterpret_cast<float *>(smem + L::oDU);
     float *dXs = reinterpret_cast<float *>(smem + L::oDX);
     float *Gs = reinterpret_cast<float *>(smem + L::oG);
     float *Bs = reinterpret_cast<float *>(smem + L::oB);
     float *Als = reinterpret_cast<float *>(smem + L::oAl);
-    float *tokG = reinterpret_cast<float *>(smem + L::oTG);
     float *tokB = reinterpret_cast<float *>(smem + L::oTB);
+    float *sp = reinterpret_cast<float *>(smem + L::oSP);
     float *rowE = reinterpret_cast<float *>(smem + L::oRP);
     float *colE = reinterpret_cast<float *>(smem + L::oCP);
     float *rowB = reinterpret_cast<float *>(smem + L::oRB);
@@ -498,13 +569,21 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     const float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
     const float *Sg = p.sc + (bh * p.NC + c) * DK * Dv;
     const float *dSg = p.dsc + (bh * p.NC + c) * DK * Dv;
-    const Tin *vg = static_cast<const Tin *>(p.v);
+    const float *Ug = p.ub + (bh * p.NC + c) * C * Dv;
+    const float *Wg = p.wb + (bh * p.NC + c) * C * Dv;
+    const float *Xg = p.dxb + (bh * p.NC + c) * C * Dv;
 
-    stage_rows<Tin, C, DK, KP>(Ks, static_cast<const Tin *>(p.k), b, h, c0, T, H);
-    stage_rows<Tin, C, DK, KP>(Qs, static_cast<const Tin *>(p.q), b, h, c0, T, H);
-    stage_cc<C, CP>(Ts, rec + Rec<C>::oT);
-    stage_cc<C, CP>(Ps, rec + Rec<C>::oP);
-    for (int i = tid; i < C; i += NT) {
+    {
+        RowsTile<Tin, C, DK, NTG> tk, tq;
+        DenseTile<C, C, NTG> tp;
+        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
+        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+        tp.load(rec + Rec<C>::oP, C);
+        tk.template store<KP>(Ks);
+        tq.template store<KP>(Qs);
+        tp.template store<CP>(Ps);
+    }
+    for (int i = tid; i < C; i += NTG) {
         const int64_t t = c0 + i;
         const bool ok = t < T;
         Gs[i] = rec[Rec<C>::oG + i];
@@ -518,98 +597,44 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     for (int m = 0; m < NCK; ++m) dQa[m] = dKa[m] = dKb[m] = zero4();
 #pragma unroll
     for (int m = 0; m < NCC; ++m) dPM[m] = zero4();
-    f32x4 pG = zero4(), pB = zero4();   // per-token partials of this wave's rows
-    float pGC = 0.f, pSS = 0.f;
+    float pW = 0.f, pSS = 0.f;   // sum dX o W~ over this thread's row piece; <S, dS'> piece
+
+    // registers holding the next value slice
+    DenseTile<DK, BV, NTG> rs, rds;
+    DenseTile<C, BV, NTG> ru, rx, rw;
+    RowsTile<float, C, BV, NTG> rdy;
+    static_assert(DenseTile<C, BV, NTG>::NV == 1, "one C x 16 slice unit per thread");
+    auto fetch_slice = [&](int n0) {
+        rs.load(Sg + n0, Dv);
+        rds.load(dSg + n0, Dv);
+        ru.load(Ug + n0, Dv);
+        rx.load(Xg + n0, Dv);
+        rw.load(Wg + n0, Dv);
+        rdy.load(p.dy, b, h, c0, T, H, Dv, n0);
+    };
+    fetch_slice(0);
 
     for (int n0 = 0; n0 < Dv; n0 += BV) {
-        // ---- stage S, dS' slices and the dY slice
-        for (int i = tid; i < DK * 4; i += NT) {
-            const int r = i >> 2, col = (i & 3) * 4;
-            const f32x4 s = load4(Sg + r * Dv + n0 + col);
-            const f32x4 ds = load4(dSg + r * Dv + n0 + col);
-            *reinterpret_cast<f32x4 *>(Ss + r * VP + col) = s;
-            *reinterpret_cast<f32x4 *>(dSs + r * VP + col) = ds;
-            pSS += s[0] * ds[0] + s[1] * ds[1] + s[2] * ds[2] + s[3] * ds[3];
-        }
-        stage_slice<float, C>(dYs, p.dy, b, h, c0, T, H, Dv, n0);
-        __syncthreads();
-        const float GC = Gs[C - 1];
-
-        // ---- A: K S, Q S, K dS' of this wave's token block; X = beta W~
-        f32x4 KS = zero4(), QS = zero4(), KD = zero4(), Wt = zero4();
-        if (wave < NB) {
-            const int rb = wave;
+        rs.template store<VP>(Ss);
+        rds.template store<VP>(dSs);
+        ru.template store<VP>(Us);
+        rx.template store<VP>(dXs);
+        rdy.template store<VP>(dYs);
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += KSD) {
-                const FD kf = frag_rows<float, KSD>(Ks, KP, 16 * rb, k0, lane);
-                const FD qf = frag_rows<float, KSD>(Qs, KP, 16 * rb, k0, lane);
-                const FD sf = frag_cols<float, KSD>(Ss, VP, 0, k0, lane);
-                const FD df = frag_cols<float, KSD>(dSs, VP, 0, k0, lane);
-                KS = FD::mma(kf, sf, KS);
-                QS = FD::mma(qf, sf, QS);
-                KD = FD::mma(kf, df, KD);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * lg + e;
-                const int64_t t = c0 + r;
-                const float vv = t < T ? to_f32(vg[((b * T + t) * H + h) * Dv + n0 + ln]) : 0.f;
-                Wt[e] = vv - __builtin_amdgcn_exp2f(Gs[r]) * KS[e];
-                Xs[r * VP + ln] = Bs[r] * Wt[e];
-            }
+        for (int it = 0; it < DenseTile<DK, BV, NTG>::NV; ++it) {
+            const f32x4 a = rs.v[it], d = rds.v[it];
+            pSS += a[0] * d[0] + a[1] * d[1] + a[2] * d[2] + a[3] * d[3];
         }
+        {
+            const f32x4 a = rx.v[0], w = rw.v[0];
+            pW += a[0] * w[0] + a[1] * w[1] + a[2] * w[2] + a[3] * w[3];
+        }
+        if (n0 + BV < Dv) fetch_slice(n0 + BV);
         __syncthreads();
 
-        // ---- B: U = T X;  dU = P^T dY + d o K dS'
-        if (wave < NB) {
-            const int rb = wave;
-            f32x4 U = zero4(), dU;
-            for (int kb = 0; kb <= rb; ++kb)
-                U = F16::mma(frag_rows<float, 16>(Ts, CP, 16 * rb, 16 * kb, lane),
-                             frag_cols<float, 16>(Xs, VP, 0, 16 * kb, lane), U);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dU[e] = __builtin_amdgcn_exp2f(GC - Gs[16 * rb + 4 * lg + e]) * KD[e];
-            for (int kb = rb; kb < NB; ++kb)
-                dU = F16::mma(frag_cols<float, 16>(Ps, CP, 16 * rb, 16 * kb, lane),
-                              frag_cols<float, 16>(dYs, VP, 0, 16 * kb, lane), dU);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * lg + e;
-                Us[r * VP + ln] = U[e];
-                dUs[r * VP + ln] = dU[e];
-                const float dr = __builtin_amdgcn_exp2f(GC - Gs[r]), br = __builtin_amdgcn_exp2f(Gs[r]);
-                const float s3 = U[e] * KD[e];
-                pG[e] += br * dYs[r * VP + ln] * QS[e] - dr * s3;
-                pGC += dr * s3;
-            }
-        }
-        __syncthreads();
-
-        // ---- C: dX = T^T dU;  dV = beta dX
-        if (wave < NB) {
-            const int rb = wave;
-            f32x4 dX = zero4();
-            for (int kb = rb; kb < NB; ++kb)
-                dX = F16::mma(frag_cols<float, 16>(Ts, CP, 16 * rb, 16 * kb, lane),
-                              frag_cols<float, 16>(dUs, VP, 0, 16 * kb, lane), dX);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * lg + e;
-                const int64_t t = c0 + r;
-                dXs[r * VP + ln] = dX[e];
-                const float dW = Bs[r] * dX[e];
-                if (t < T) p.dv[((b * T + t) * H + h) * Dv + n0 + ln] = dW;
-                pG[e] -= __builtin_amdgcn_exp2f(Gs[r]) * dW * KS[e];
-                pB[e] += dX[e] * Wt[e];
-            }
-        }
-        __syncthreads();
-
-        // ---- D: dP += dY U^T, dM += dX U^T (lower blocks);
-        //         dQa += dY S^T, dKa += dX S^T, dKb += U dS'^T
 #pragma unroll
         for (int m = 0; m < NCC; ++m) {
-            const int tile = wave + 4 * m;
+            const int tile = wave + NWG * m;
             if (tile < 2 * NTRI) {
                 const bool isM = tile >= NTRI;
                 int rb, jb;
@@ -620,7 +645,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
         }
 #pragma unroll
         for (int m = 0; m < NCK; ++m) {
-            const int tile = wave + 4 * m;
+            const int tile = wave + NWG * m;
             if (tile < NTILE) {
                 const int rb = tile / NKB, kb = tile % NKB;
                 const F16 sf = frag_rows<float, 16>(Ss, VP, 16 * kb, 0, lane);
@@ -634,29 +659,43 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     }
 
     // ---- E: per-token partials to LDS; Ak into the freed slice buffers
-    if (wave < NB) {
+    {
+        // the 4 consecutive threads of a staged row piece hold one row's 16 columns
+        float w = pW;
+        w += __shfl_xor(w, 1);
+        w += __shfl_xor(w, 2);
+        if ((tid & 3) == 0 && tid / 4 < C) tokB[tid / 4] = w;
+        float y = pSS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float g = row16_sum(pG[e]), bb = row16_sum(pB[e]);
-            if (ln == 0) {
-                tokG[16 * wave + 4 * lg + e] = g;
-                tokB[16 * wave + 4 * lg + e] = bb;
+        for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off);
+        if (lane == 0) red[wave] = y;
+    }
+    // row dot products q . dQa, k . dKa, k . dKb of every C x DK tile
+#pragma unroll
+    for (int m = 0; m < NCK; ++m) {
+        const int tile = wave + NWG * m;
+        if (tile < NTILE) {
+            const int rb = tile / NKB, kb = tile % NKB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e, col = 16 * kb + ln;
+                const float qv = Qs[r * KP + col], kv = Ks[r * KP + col];
+                const float a1 = row16_total(qv * dQa[m][e]);
+                const float a2 = row16_total(kv * dKa[m][e]);
+                const float a3 = row16_total(kv * dKb[m][e]);
+                if (ln == 15) {
+                    sp[(0 * NTILE + tile) * 16 + 4 * lg + e] = a1;
+                    sp[(1 * NTILE + tile) * 16 + 4 * lg + e] = a2;
+                    sp[(2 * NTILE + tile) * 16 + 4 * lg + e] = a3;
+                }
             }
         }
     }
     {
-        float x = pGC, y = pSS;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            x += __shfl_xor(x, off);
-            y += __shfl_xor(y, off);
-        }
-        if (lane == 0) {
-            red[wave] = x;
-            red[4 + wave] = y;
-        }
+        DenseTile<C, C, NTG> ta;
+        ta.load(rec + Rec<C>::oA, C);
+        ta.template store<CP>(Aks);
     }
-    stage_cc<C, CP>(Aks, rec + Rec<C>::oA);
     __syncthreads();
 
     // dP tiles -> dQK = Gamma o dP (into Ps); dM tiles -> dA = -dM, dKK =
@@ -665,7 +704,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     // Every (part, block) has exactly one writer, so the sums are deterministic.
 #pragma unroll
     for (int m = 0; m < NCC; ++m) {
-        const int tile = wave + 4 * m;
+        const int tile = wave + NWG * m;
         if (tile < 2 * NTRI) {
             const int part = tile >= NTRI ? 1 : 0;
             int rb, jb;
@@ -690,9 +729,9 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
                     Ps[r * CP + j] = gam * dP;
                 }
                 cs += E;
-                const float rs = row16_sum(E);
-                const float rsb = row16_sum(rbeta);
-                if (ln == 0) {
+                const float rs = row16_total(E);
+                const float rsb = row16_total(rbeta);
+                if (ln == 15) {
                     rowE[((part * NB + rb) * NB + jb) * 16 + 4 * lg + e] = rs;
                     if (part) rowB[(rb * NB + jb) * 16 + 4 * lg + e] = rsb;
                 }
@@ -708,7 +747,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     //         dK = -e^G beta o dKa + d o dKb + dKK K + dKK^T K + dQK^T Q
 #pragma unroll
     for (int m = 0; m < NCK; ++m) {
-        const int tile = wave + 4 * m;
+        const int tile = wave + NWG * m;
         if (tile < NTILE) {
             const int rb = tile / NKB, kb = tile % NKB;
             const float GC = Gs[C - 1];
@@ -746,17 +785,33 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdParams p)
     // ---- G: dG per token, d ln alpha = suffix sums of dG, dalpha, dbeta
     if (wave == 0) {
         const int rr = C - 1 - lane;    // lane l carries token C-1-l (reversed for the scan)
-        float g = 0.f;
+        const float GC = Gs[C - 1];
+        float g = 0.f, d3 = 0.f;
         if (lane < C) {
             const int rb = rr / 16, ri = rr % 16;
-            g = tokG[rr];
+            float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int tile = rb * NKB + kb;
+                s1 += sp[(0 * NTILE + tile) * 16 + ri];
+                s2 += sp[(1 * NTILE + tile) * 16 + ri];
+                s3 += sp[(2 * NTILE + tile) * 16 + ri];
+            }
+            const float br = __builtin_amdgcn_exp2f(Gs[rr]), dr = __builtin_amdgcn_exp2f(GC - Gs[rr]);
+            d3 = dr * s3;
+            g = br * s1 - br * Bs[rr] * s2 - d3;
             for (int jb = 0; jb <= rb; ++jb)
                 g += rowE[(rb * NB + jb) * 16 + ri] + rowE[((NB + rb) * NB + jb) * 16 + ri];
             for (int ib = rb; ib < NB; ++ib)
                 g -= colE[(ib * NB + rb) * 16 + ri] + colE[((NB + ib) * NB + rb) * 16 + ri];
-            if (rr == C - 1)
-                g += (red[0] + red[1]) + (red[2] + red[3]) +
-                     __builtin_amdgcn_exp2f(Gs[C - 1]) * ((red[4] + red[5]) + (red[6] + red[7]));
+        }
+        // e^{G_C} and the d_r factors all depend on G_C: their terms go to the last token
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) d3 += __shfl_xor(d3, off);
+        {
+            float ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWG; ++w) ss += red[w];
+            if (lane == 0) g += d3 + __builtin_amdgcn_exp2f(GC) * ss;
         }
         const float suf = wave_inclusive_sum(g, lane);   // lane l: sum over tokens >= C-1-l
         if (lane < C) {
@@ -791,11 +846,14 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     kp.rec = ws;
     kp.sc = kp.rec + bh * kp.NC * kp.rec_floats;
     kp.dsc = kp.sc + bh * kp.NC * DK * a.Dv;
+    kp.ub = kp.dsc + bh * kp.NC * DK * a.Dv;
+    kp.wb = kp.ub + bh * kp.NC * C * a.Dv;
+    kp.dxb = kp.wb + bh * kp.NC * C * a.Dv;
     const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
     hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
     hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, false>), dim3(nslice), dim3(NT), 0, stream, kp);
     hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, true>), dim3(nslice), dim3(NT), 0, stream, kp);
-    hipLaunchKernelGGL((bwd_chunk_kernel<Tin, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
+    hipLaunchKernelGGL((bwd_chunk_kernel<Tin, C, DK>), dim3(nchunk), dim3(NTG), 0, stream, kp);
     return hipGetLastError();
 }
 
@@ -836,7 +894,7 @@ int64_t bwd_record_floats(int64_t C) { return (3 * C * C + C + 63) / 64 * 64; }
 size_t prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C)
 {
     const int64_t nc = (T + C - 1) / C;
-    return (size_t)(4 * B * H * nc * (bwd_record_floats(C) + 2 * Dk * Dv));
+    return (size_t)(4 * B * H * nc * (bwd_record_floats(C) + 2 * Dk * Dv + 3 * C * Dv));
 }
 
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)

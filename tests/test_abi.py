@@ -240,9 +240,10 @@ def prefill_bwd(L, q=A, k=A + 8 * MB, v=A + 16 * MB, al=A + 24 * MB, be=A + 25 *
 
 def test_prefill_bwd_validation(L):
     need = L.gdn_prefill_bwd_workspace_bytes(1, 64, 2, 16, 16, 16)
-    # one record of 3*16*16+16 floats (rounded up to 64) plus two 16x16 states per chunk
-    assert need == 4 * 2 * 4 * (832 + 2 * 256)
-    assert L.gdn_prefill_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64) == 4 * 32 * 64 * (12352 + 2 * 16384)
+    # per chunk: a record of 3*16*16+16 floats (rounded up to 64), two 16x16
+    # states and three 16x16 chunk matrices
+    assert need == 4 * 2 * 4 * (832 + 2 * 256 + 3 * 256)
+    assert L.gdn_prefill_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64) == 4 * 32 * 64 * (12352 + 2 * 16384 + 3 * 8192)
     assert L.gdn_prefill_bwd_workspace_bytes(1, 0, 2, 16, 16, 16) == 0
     assert L.gdn_prefill_bwd_workspace_bytes(1, 64, 2, 48, 16, 16) == 0
     assert prefill_bwd(L, q=None) == NULL
