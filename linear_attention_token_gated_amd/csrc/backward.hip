@@ -53,6 +53,7 @@ struct BwdParams {
     float *ub, *wb, *dxb;      // per chunk [C][Dv]: U, W~ = V - e^G K S (state pass), dX (adjoint pass)
     int64_t T, H, Dv, NC;
     int64_t rec_floats;
+    int xcd_map;               // state passes: the slices of one head on one XCD (B*H % 8 == 0)
 };
 
 // ---- per-chunk record: T [C][C], P [C][C], Ak [C][C], G2 [C] (log2 cumulative decay)
@@ -136,6 +137,21 @@ __device__ __forceinline__ void tri_block(int idx, int &rb, int &cb) {
     cb = idx - rb * (rb + 1) / 2;
 }
 
+// Workgroup -> (b*H + h, value slice) for the state passes.  Workgroups are
+// dealt to the 8 XCDs round-robin; with xcd_map the NS slices of one head get
+// ids equal mod 8, so they run on one XCD and share its L2 copy of the chunk's
+// K, Q, T and P.
+__device__ __forceinline__ void slice_of(int64_t bid, int64_t NS, int xcd_map, int64_t &bh, int64_t &sl) {
+    if (xcd_map) {
+        const int64_t xcd = bid & 7, local = bid >> 3;
+        bh = (local / NS) * 8 + xcd;
+        sl = local % NS;
+    } else {
+        bh = bid / NS;
+        sl = bid % NS;
+    }
+}
+
 // Sum over the 16 lanes of each 16-lane row, left in the row's last lane
 // (ln == 15): an inclusive scan by DPP row shifts, no LDS traffic.
 __device__ __forceinline__ float row16_total(float x) {
@@ -146,16 +162,32 @@ __device__ __forceinline__ float row16_total(float x) {
     return x;
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it carries no memory
+// fence, so global loads in flight (prefetch) and global stores (outputs) are
+// not waited for; every value these kernels pass between wavefronts goes
+// through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt and expcnt at their maximum, lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ===========================================================================
 // 1. prep: G2, T = (I + A)^-1, P, Ak of one chunk
 // ===========================================================================
 template <typename Tin, int C, int DK>
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 {
-    constexpr int KP = DK + 4, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
+    // K and Q stay in the input type: bf16 inputs run the Gram on bf16 MFMA
+    // (exact products, fp32 sums), fp32 inputs on fp32 MFMA
+    constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
+    constexpr int KP = DK + PAD, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
     constexpr int NTRI = NB * (NB + 1) / 2;
-    __shared__ __attribute__((aligned(16))) float Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) float Qs[C * KP];
+    using FG = Frag<Tin, KSD>;
+    __shared__ __attribute__((aligned(16))) Tin Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) Tin Qs[C * KP];
     __shared__ __attribute__((aligned(16))) float As[C * CP];
     __shared__ __attribute__((aligned(16))) float Ts[C * CP];
     __shared__ float Gs[C], Bs[C];
@@ -166,11 +198,19 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
 
     {
+        using R = Raw4<Tin>;
         RowsTile<Tin, C, DK> tk, tq;
         tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
         tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
-        tk.template store<KP>(Ks);
-        tq.template store<KP>(Qs);
+#pragma unroll
+        for (int it = 0; it < RowsTile<Tin, C, DK>::NV; ++it) {
+            const int vi = tid + NT * it;
+            const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
+            if (RowsTile<Tin, C, DK>::NU % NT == 0 || vi < RowsTile<Tin, C, DK>::NU) {
+                *reinterpret_cast<typename R::type *>(Ks + r * KP + col) = tk.v[it];
+                *reinterpret_cast<typename R::type *>(Qs + r * KP + col) = tq.v[it];
+            }
+        }
     }
     if (wave == 0) {
         const int64_t t = c0 + lane;
@@ -199,14 +239,12 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
         const bool isQ = tile >= NTRI;
         int rb, cb;
         tri_block(isQ ? tile - NTRI : tile, rb, cb);
-        const float *src = isQ ? Qs : Ks;
+        const Tin *src = isQ ? Qs : Ks;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += KSD) {
-            const Frag<float, KSD> a = frag_rows<float, KSD>(src, KP, 16 * rb, k0, lane);
-            const Frag<float, KSD> bb = frag_rows<float, KSD>(Ks, KP, 16 * cb, k0, lane);
-            acc = Frag<float, KSD>::mma(a, bb, acc);
-        }
+        for (int k0 = 0; k0 < DK; k0 += KSD)
+            acc = FG::mma(frag_rows<Tin, KSD>(src, KP, 16 * rb, k0, lane),
+                          frag_rows<Tin, KSD>(Ks, KP, 16 * cb, k0, lane), acc);
         const int j = 16 * cb + ln;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -312,7 +350,8 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
 
     const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
     const int64_t NS = p.Dv / BV;
-    const int64_t bh = blockIdx.x / NS, sl = blockIdx.x % NS;
+    int64_t bh, sl;
+    slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
     const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
     const int n0 = (int)sl * BV;
 
@@ -385,7 +424,7 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         const float GC = Gs[C - 1];
 
         // step 1: K S (per 16-token block); forward: X = diag(beta)(V - e^G K S);
@@ -421,7 +460,7 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // step 2: forward: U = T X, stored as d o U (transposed);
         // adjoint: dR = diag(beta) T^T dU, stored as -e^G o dR (transposed)
@@ -456,7 +495,7 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // step 3: S <- e^{G_C} S + K^T UdT (+ Q^T (e^G o dY) for the adjoint)
         const float eGC = __builtin_amdgcn_exp2f(GC);
@@ -476,11 +515,486 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
                 S[m] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if constexpr (ADJ) {
         if (p.ds0) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p.ds0[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+                }
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// 2./3. state passes, bf16 inputs: bf16 MFMA with hi/lo operands
+//
+// Same steps as bwd_carry_kernel.  K and Q are exact in bf16; every other
+// operand (the state, T, P, X, dY, dU and the decayed products) is split into
+// a bf16 pair hi + lo and multiplied as hi*hi + hi*lo + lo*hi (two products
+// where one side is exact), which keeps about 16 bits of every operand.
+// Transposed operands (K^T, Q^T, T^T, P^T) come from the row-major LDS copies
+// through transposing reads (ds_read_tr16_b64).
+// ===========================================================================
+typedef short i16x4t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4t *lds_i16x4p;
+
+// Lane j of each 16-lane group supplies the address of 4 consecutive bf16;
+// lane i of the group receives element i % 4 of the 4-element pieces of
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (lds_i16x4p)(uintptr_t)(uint32_t)(uintptr_t)p));
+}
+
+// A operand (16-deep) of M^T, rows r0..r0+15 of M^T = columns of the row-major
+// M (pitch P), k = rows k0..k0+15 of M: lane l holds M[k0 + 4(l/16) + e][r0 + l%16].
+__device__ __forceinline__ Frag<__bf16, 16> tr_frag16(const __bf16 *M, int P, int r0, int k0, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    Frag<__bf16, 16> f;
+    f.v = tr_read(M + (k0 + 4 * g + (j >> 2)) * P + r0 + 4 * (j & 3));
+    return f;
+}
+
+// 32-deep A operand of M^T as two 16-deep pieces: lane group g holds k = k0 +
+// 4g..+3 then k0 + 16 + 4g..+3.  B operands for it come from pair_rows32.
+__device__ __forceinline__ Frag<__bf16, 32> tr_frag32(const __bf16 *M, int P, int r0, int k0, int lane) {
+    const bf16x4 a = tr_frag16(M, P, r0, k0, lane).v, b = tr_frag16(M, P, r0, k0 + 16, lane).v;
+    Frag<__bf16, 32> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+// B operand (rows of B^T, pitch P) with the k order of tr_frag32
+__device__ __forceinline__ Frag<__bf16, 32> pair_rows32(const __bf16 *Bt, int P, int r0, int k0, int lane) {
+    const int g = lane >> 4;
+    const __bf16 *row = Bt + (r0 + (lane & 15)) * P + k0 + 4 * g;
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row), b = *reinterpret_cast<const bf16x4 *>(row + 16);
+    Frag<__bf16, 32> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+__device__ __forceinline__ void store_split4(__bf16 *hi, __bf16 *lo, const f32x4 x) {
+    bf16x4 h, l;
+    split4(x, h, l);
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+
+template <int C, int DK, bool ADJ> struct Carry16Lay {
+    static constexpr int KP = DK + 8, CP = C + 8;   // bf16 pitches
+    static constexpr size_t KB = 2 * C * KP, CB = 2 * C * CP, SB = 2 * BV * KP, TB = 2 * BV * CP;
+    static constexpr size_t oK = 0;                           // K, two buffers
+    static constexpr size_t oQ = oK + 2 * KB;                 // Q, two buffers (adjoint)
+    static constexpr size_t oTh = oQ + (ADJ ? 2 * KB : 0);
+    static constexpr size_t oTl = oTh + CB;
+    static constexpr size_t oPh = oTl + CB;                   // P (adjoint)
+    static constexpr size_t oPl = oPh + (ADJ ? CB : 0);
+    static constexpr size_t oSTh = oPl + (ADJ ? CB : 0);      // state operand, transposed
+    static constexpr size_t oSTl = oSTh + SB;
+    static constexpr size_t oXh = oSTl + SB;                  // X^T (state pass) or dU^T (adjoint)
+    static constexpr size_t oXl = oXh + TB;
+    static constexpr size_t oYh = oXl + TB;                   // dY^T (adjoint)
+    static constexpr size_t oYl = oYh + (ADJ ? TB : 0);
+    static constexpr size_t oUh = oYl + (ADJ ? TB : 0);       // decayed U^T or -e^G dR^T
+    static constexpr size_t oUl = oUh + TB;
+    static constexpr size_t oBh = oUl + TB;                   // (e^G o dY)^T, two buffers (adjoint)
+    static constexpr size_t oBl = oBh + (ADJ ? 2 * TB : 0);
+    static constexpr size_t oIn = oBl + (ADJ ? 2 * TB : 0);   // V slice, fp32 (state pass)
+    static constexpr size_t oG = oIn + (ADJ ? 0 : 4 * C * VP);   // G2, two buffers
+    static constexpr size_t oB = oG + 4 * 2 * C;              // beta, two buffers
+    static constexpr size_t BYTES = oB + 4 * 2 * C;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// 8 wavefronts: waves 0-3 carry the chain of every chunk (K S, the C x C
+// product, the state update) and the stores of what they produce; waves 4-7
+// stage the next chunk into LDS while the chain runs and prefetch the one after
+// it into registers.  Per chunk c (barriers A, B, C):
+//   A..B  chain: step 1 on chunk c
+//   B..C  chain: step 2;  staging: P, dY^T, e^G dY (or V) of the next chunk
+//   C..A  chain: step 3;  staging: K, Q, T, G2, beta of the next chunk
+// Single-buffered operands are rewritten only after their last read in chunk c.
+constexpr int NTC = 512;
+
+template <int C, int DK, bool ADJ>
+__global__ __launch_bounds__(NTC) void bwd_carry16_kernel(BwdParams p)
+{
+    using L = Carry16Lay<C, DK, ADJ>;
+    constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4;
+    using F16 = Frag<__bf16, 16>;
+    using F32 = Frag<__bf16, 32>;
+    static_assert(DK % 32 == 0 || DK == 16, "Dk");
+    constexpr int NST = 256;                                   // staging threads
+    constexpr int NUK = C * DK / 4, NVK = (NUK + NST - 1) / NST;
+    constexpr int NUT = C * C / 4, NVT = (NUT + NST - 1) / NST;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __bf16 *Kb = reinterpret_cast<__bf16 *>(smem + L::oK);
+    __bf16 *Qb = reinterpret_cast<__bf16 *>(smem + L::oQ);
+    __bf16 *Th = reinterpret_cast<__bf16 *>(smem + L::oTh);
+    __bf16 *Tl = reinterpret_cast<__bf16 *>(smem + L::oTl);
+    __bf16 *Ph = reinterpret_cast<__bf16 *>(smem + L::oPh);
+    __bf16 *Pl = reinterpret_cast<__bf16 *>(smem + L::oPl);
+    __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
+    __bf16 *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
+    __bf16 *Xh = reinterpret_cast<__bf16 *>(smem + L::oXh);
+    __bf16 *Xl = reinterpret_cast<__bf16 *>(smem + L::oXl);
+    __bf16 *Yh = reinterpret_cast<__bf16 *>(smem + L::oYh);
+    __bf16 *Yl = reinterpret_cast<__bf16 *>(smem + L::oYl);
+    __bf16 *Uh = reinterpret_cast<__bf16 *>(smem + L::oUh);
+    __bf16 *Ul = reinterpret_cast<__bf16 *>(smem + L::oUl);
+    __bf16 *Bhb = reinterpret_cast<__bf16 *>(smem + L::oBh);
+    __bf16 *Blb = reinterpret_cast<__bf16 *>(smem + L::oBl);
+    float *Ins = reinterpret_cast<float *>(smem + L::oIn);
+    float *Gb = reinterpret_cast<float *>(smem + L::oG);
+    float *Bb = reinterpret_cast<float *>(smem + L::oB);
+
+    const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
+    const bool chain = wave < 4;
+    const int ts = threadIdx.x - 256;                          // staging thread index
+    const int64_t NS = p.Dv / BV;
+    int64_t bh, sl;
+    slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
+    const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
+    const int n0 = (int)sl * BV;
+    const __bf16 *kg = static_cast<const __bf16 *>(p.k);
+    const __bf16 *qg = static_cast<const __bf16 *>(p.q);
+    const __bf16 *vg = static_cast<const __bf16 *>(p.v);
+
+    // ---- staging registers: set A (P, dY or V) and set B (K, Q, T, G2, beta).
+    // Every load is issued unconditionally (clamped row and unit indices, the
+    // zeros past T applied when the data is written), so the compiler can wait
+    // on exact outstanding-load counts instead of draining the prefetch.
+    f32x4 rP[NVT], rT[NVT];
+    bf16x4 rK[NVK], rQ[NVK];
+    f32x4 rY = zero4();                      // dY piece (adjoint)
+    bf16x4 rV = Raw4<__bf16>::zero();        // V piece (state pass)
+    float rG = 0.f, rBe = 0.f, rGa = 0.f;    // rGa: G2 of this thread's set-A token (e^G o dY)
+    int64_t cA = 0, cB = 0;                  // chunk held by set A, set B
+    const int ua = ts < C * 4 ? ts : C * 4 - 1;    // clamped set-A unit (row ua/4, columns 4(ua%4)..)
+    const int ug = ts < C ? ts : C - 1;            // clamped token of G2 / beta
+    auto load_a = [&](int64_t c) {
+        cA = c;
+        const int64_t c0 = c * C;
+        const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
+        if constexpr (ADJ) {
+#pragma unroll
+            for (int i = 0; i < NVT; ++i) {
+                int u = ts + NST * i;
+                u = (NUT % NST == 0 || u < NUT) ? u : NUT - 1;
+                const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+                rP[i] = *reinterpret_cast<const f32x4 *>(rec + Rec<C>::oP + r * C + col);
+            }
+        }
+        const int r = ua >> 2, col = (ua & 3) * 4;
+        const int64_t t = c0 + r < T ? c0 + r : T - 1;
+        if constexpr (ADJ) {
+            rY = *reinterpret_cast<const f32x4 *>(p.dy + ((b * T + t) * H + h) * Dv + n0 + col);
+            rGa = rec[Rec<C>::oG + r];
+        } else {
+            rV = *reinterpret_cast<const bf16x4 *>(vg + ((b * T + t) * H + h) * Dv + n0 + col);
+        }
+    };
+    auto load_b = [&](int64_t c) {
+        cB = c;
+        const int64_t c0 = c * C;
+        const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
+#pragma unroll
+        for (int i = 0; i < NVK; ++i) {
+            int u = ts + NST * i;
+            u = (NUK % NST == 0 || u < NUK) ? u : NUK - 1;
+            const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+            const int64_t t = c0 + r < T ? c0 + r : T - 1;
+            rK[i] = *reinterpret_cast<const bf16x4 *>(kg + ((b * T + t) * H + h) * DK + col);
+            if constexpr (ADJ) rQ[i] = *reinterpret_cast<const bf16x4 *>(qg + ((b * T + t) * H + h) * DK + col);
+        }
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            int u = ts + NST * i;
+            u = (NUT % NST == 0 || u < NUT) ? u : NUT - 1;
+            const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+            rT[i] = *reinterpret_cast<const f32x4 *>(rec + Rec<C>::oT + r * C + col);
+        }
+        const int64_t tg = c0 + ug < T ? c0 + ug : T - 1;
+        rG = rec[Rec<C>::oG + ug];
+        rBe = p.beta[(b * T + tg) * H + h];
+    };
+    // set A into LDS: P hi/lo; dY^T hi/lo and (e^G o dY)^T into buffer nb, or V
+    auto write_a = [&](int nb) {
+        if constexpr (ADJ) {
+#pragma unroll
+            for (int i = 0; i < NVT; ++i) {
+                const int u = ts + NST * i;
+                const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+                if (NUT % NST == 0 || u < NUT) store_split4(Ph + r * CP + col, Pl + r * CP + col, rP[i]);
+            }
+        }
+        if (C * 4 >= NST || ts < C * 4) {
+            const int r = ts >> 2, col = (ts & 3) * 4;
+            const bool ok = cA * C + r < T;
+            if constexpr (ADJ) {
+                // e^G of this token (loaded with set A)
+                const float eg = __builtin_amdgcn_exp2f(rGa);
+                const f32x4 y = ok ? rY : zero4();
+                bf16x4 hh, ll, bh2, bl2;
+                split4(y, hh, ll);
+                split4(y * eg, bh2, bl2);
+                __bf16 *Bh = Bhb + nb * BV * CP, *Bl = Blb + nb * BV * CP;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    Yh[(col + q) * CP + r] = hh[q];
+                    Yl[(col + q) * CP + r] = ll[q];
+                    Bh[(col + q) * CP + r] = bh2[q];
+                    Bl[(col + q) * CP + r] = bl2[q];
+                }
+            } else {
+                *reinterpret_cast<f32x4 *>(Ins + r * VP + col) = ok ? Raw4<__bf16>::widen(rV) : zero4();
+            }
+        }
+    };
+    auto write_b = [&](int nb) {
+        __bf16 *Kd = Kb + nb * C * KP, *Qd = Qb + nb * C * KP;
+#pragma unroll
+        for (int i = 0; i < NVK; ++i) {
+            const int u = ts + NST * i;
+            const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+            if (NUK % NST == 0 || u < NUK) {
+                const bool ok = cB * C + r < T;
+                *reinterpret_cast<bf16x4 *>(Kd + r * KP + col) = ok ? rK[i] : Raw4<__bf16>::zero();
+                if constexpr (ADJ) *reinterpret_cast<bf16x4 *>(Qd + r * KP + col) = ok ? rQ[i] : Raw4<__bf16>::zero();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int u = ts + NST * i;
+            const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+            if (NUT % NST == 0 || u < NUT) store_split4(Th + r * CP + col, Tl + r * CP + col, rT[i]);
+        }
+        if (C >= NST || ts < C) {
+            Gb[nb * C + ts] = rG;
+            Bb[nb * C + ts] = cB * C + ts < T ? rBe : 0.f;
+        }
+    };
+
+    const int64_t cfirst = ADJ ? NC - 1 : 0;
+    const int64_t cstep = ADJ ? -1 : 1;
+
+    // ---- state slice in the chain waves' accumulators
+    f32x4 S[MS];
+    const float *init = ADJ ? p.dsT : p.s0;
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        S[m] = zero4();
+        const int ib = wave + 4 * m;
+        if (chain && ib < NKB && init) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = init[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln];
+        }
+    }
+    // keep the state at the boundary of chunk c; stage it transposed (hi/lo)
+    auto keep_state = [&](int64_t c) {
+        float *keep = (ADJ ? p.dsc : p.sc) + (bh * NC + c) * DK * Dv;
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+                const int row = 16 * ib + 4 * lg;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) keep[(row + e) * Dv + n0 + ln] = S[m][e];
+                store_split4(STh + ln * KP + row, STl + ln * KP + row, S[m]);
+            }
+        }
+    };
+
+    // The two roles run separate loops with the same barrier sequence (one
+    // barrier after the prologue, three per chunk), so the chain waves' code
+    // holds no global load and never waits on its own stores.
+    if (!chain) {
+        // ---- staging waves
+        // the first chunk (G2 of set B is needed by write_a), then prefetch the
+        // second; past the last chunk the last one is fetched again (never read)
+        auto clampc = [&](int64_t c) { return c < 0 ? 0 : c >= NC ? NC - 1 : c; };
+        load_b(cfirst);
+        load_a(cfirst);
+        write_b(0);
+        write_a(0);
+        // same issue order as in the loop (set A, then set B), so the waits in
+        // the loop count the same younger loads on both entries
+        load_a(clampc(cfirst + cstep));
+        __builtin_amdgcn_sched_barrier(0);   // keep the set-A loads ahead of set B
+        load_b(clampc(cfirst + cstep));
+        lds_barrier();
+        for (int64_t it = 0; it < NC; ++it) {
+            const int64_t c = cfirst + cstep * it;
+            const int nbuf = (int)(it & 1) ^ 1;
+            lds_barrier();                  // A..B: step 1 runs
+            // set A of the next chunk (single-buffered parts: last read in step 1)
+            write_a(nbuf);
+            load_a(clampc(c + 2 * cstep));
+            lds_barrier();                  // B..C: step 2 runs
+            // set B of the next chunk (T: last read in step 2)
+            write_b(nbuf);
+            load_b(clampc(c + 2 * cstep));
+            lds_barrier();                  // C..A: step 3 runs
+        }
+    } else {
+        // ---- chain waves
+        keep_state(cfirst);
+        lds_barrier();
+        for (int64_t it = 0; it < NC; ++it) {
+            const int64_t c = cfirst + cstep * it;
+            const int buf = (int)(it & 1);
+            const bool more = it + 1 < NC;
+            const __bf16 *Ks = Kb + buf * C * KP, *Qs = Qb + buf * C * KP;
+            const __bf16 *Bh = Bhb + buf * BV * CP, *Bl = Blb + buf * BV * CP;
+            const float *Gs = Gb + buf * C, *Bs = Bb + buf * C;
+            const float GC = Gs[C - 1];
+
+            // ---- A..B: step 1
+            if (wave < NB) {
+                const int rb = wave;
+                f32x4 ks = zero4(), ks2 = zero4();
+                if constexpr (DK % 32 == 0) {
+#pragma unroll
+                    for (int k0 = 0; k0 < DK; k0 += 32) {
+                        const F32 a = frag_rows<__bf16, 32>(Ks, KP, 16 * rb, k0, lane);
+                        ks = F32::mma(a, frag_rows<__bf16, 32>(STh, KP, 0, k0, lane), ks);
+                        ks2 = F32::mma(a, frag_rows<__bf16, 32>(STl, KP, 0, k0, lane), ks2);
+                    }
+                } else {
+                    const F16 a = frag_rows<__bf16, 16>(Ks, KP, 16 * rb, 0, lane);
+                    ks = F16::mma(a, frag_rows<__bf16, 16>(STh, KP, 0, 0, lane), ks);
+                    ks2 = F16::mma(a, frag_rows<__bf16, 16>(STl, KP, 0, 0, lane), ks2);
+                }
+                ks += ks2;
+                const int r0 = 16 * rb + 4 * lg;
+                if constexpr (ADJ) {
+                    f32x4 acc, acc2 = zero4();
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_exp2f(GC - Gs[r0 + e]) * ks[e];
+                    for (int kb = rb; kb < NB; ++kb) {
+                        const F16 ah = tr_frag16(Ph, CP, 16 * rb, 16 * kb, lane);
+                        const F16 al = tr_frag16(Pl, CP, 16 * rb, 16 * kb, lane);
+                        const F16 yh = frag_rows<__bf16, 16>(Yh, CP, 0, 16 * kb, lane);
+                        const F16 yl = frag_rows<__bf16, 16>(Yl, CP, 0, 16 * kb, lane);
+                        acc = F16::mma(ah, yh, acc);
+                        acc2 = F16::mma(ah, yl, acc2);
+                        acc2 = F16::mma(al, yh, acc2);
+                    }
+                    acc += acc2;
+                    store_split4(Xh + ln * CP + r0, Xl + ln * CP + r0, acc);
+                } else {
+                    float *wg = p.wb + (bh * NC + c) * C * Dv + n0 + ln;
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float wt = Ins[(r0 + e) * VP + ln] - __builtin_amdgcn_exp2f(Gs[r0 + e]) * ks[e];
+                        x[e] = Bs[r0 + e] * wt;
+                        wg[(r0 + e) * Dv] = wt;
+                    }
+                    store_split4(Xh + ln * CP + r0, Xl + ln * CP + r0, x);
+                }
+            }
+            lds_barrier();
+
+            // ---- B..C: step 2
+            if (wave < NB) {
+                const int rb = wave;
+                const int r0 = 16 * rb + 4 * lg;
+                f32x4 acc = zero4(), acc2 = zero4();
+                if constexpr (ADJ) {
+                    for (int kb = rb; kb < NB; ++kb) {
+                        const F16 ah = tr_frag16(Th, CP, 16 * rb, 16 * kb, lane);
+                        const F16 al = tr_frag16(Tl, CP, 16 * rb, 16 * kb, lane);
+                        const F16 xh = frag_rows<__bf16, 16>(Xh, CP, 0, 16 * kb, lane);
+                        const F16 xl = frag_rows<__bf16, 16>(Xl, CP, 0, 16 * kb, lane);
+                        acc = F16::mma(ah, xh, acc);
+                        acc2 = F16::mma(ah, xl, acc2);
+                        acc2 = F16::mma(al, xh, acc2);
+                    }
+                    acc += acc2;
+                    float *xg = p.dxb + (bh * NC + c) * C * Dv + n0 + ln;
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = r0 + e;
+                        const int64_t t = c * C + r;
+                        o[e] = -__builtin_amdgcn_exp2f(Gs[r]) * Bs[r] * acc[e];
+                        xg[r * Dv] = acc[e];
+                        if (t < T) p.dv[((b * T + t) * H + h) * Dv + n0 + ln] = Bs[r] * acc[e];
+                    }
+                    store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, o);
+                } else {
+                    for (int kb = 0; kb <= rb; ++kb) {
+                        const F16 ah = frag_rows<__bf16, 16>(Th, CP, 16 * rb, 16 * kb, lane);
+                        const F16 al = frag_rows<__bf16, 16>(Tl, CP, 16 * rb, 16 * kb, lane);
+                        const F16 xh = frag_rows<__bf16, 16>(Xh, CP, 0, 16 * kb, lane);
+                        const F16 xl = frag_rows<__bf16, 16>(Xl, CP, 0, 16 * kb, lane);
+                        acc = F16::mma(ah, xh, acc);
+                        acc2 = F16::mma(ah, xl, acc2);
+                        acc2 = F16::mma(al, xh, acc2);
+                    }
+                    acc += acc2;
+                    float *ug = p.ub + (bh * NC + c) * C * Dv + n0 + ln;
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = r0 + e;
+                        o[e] = __builtin_amdgcn_exp2f(GC - Gs[r]) * acc[e];
+                        ug[r * Dv] = acc[e];
+                    }
+                    store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, o);
+                }
+            }
+            lds_barrier();
+
+            // ---- C..A: step 3
+            const float eGC = __builtin_amdgcn_exp2f(GC);
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+                    f32x4 acc = S[m] * eGC, acc2 = zero4();
+                    if constexpr (C % 32 == 0) {
+#pragma unroll
+                        for (int j0 = 0; j0 < C; j0 += 32) {
+                            const F32 ka = tr_frag32(Ks, KP, 16 * ib, j0, lane);
+                            acc = F32::mma(ka, pair_rows32(Uh, CP, 0, j0, lane), acc);
+                            acc2 = F32::mma(ka, pair_rows32(Ul, CP, 0, j0, lane), acc2);
+                            if constexpr (ADJ) {
+                                const F32 qa = tr_frag32(Qs, KP, 16 * ib, j0, lane);
+                                acc = F32::mma(qa, pair_rows32(Bh, CP, 0, j0, lane), acc);
+                                acc2 = F32::mma(qa, pair_rows32(Bl, CP, 0, j0, lane), acc2);
+                            }
+                        }
+                    } else {
+                        const F16 ka = tr_frag16(Ks, KP, 16 * ib, 0, lane);
+                        acc = F16::mma(ka, frag_rows<__bf16, 16>(Uh, CP, 0, 0, lane), acc);
+                        acc2 = F16::mma(ka, frag_rows<__bf16, 16>(Ul, CP, 0, 0, lane), acc2);
+                        if constexpr (ADJ) {
+                            const F16 qa = tr_frag16(Qs, KP, 16 * ib, 0, lane);
+                            acc = F16::mma(qa, frag_rows<__bf16, 16>(Bh, CP, 0, 0, lane), acc);
+                            acc2 = F16::mma(qa, frag_rows<__bf16, 16>(Bl, CP, 0, 0, lane), acc2);
+                        }
+                    }
+                    S[m] = acc + acc2;
+                }
+            }
+            if (more) keep_state(c + cstep);
+            lds_barrier();
+        }
+    }
+
+    if constexpr (ADJ) {
+        if (chain && p.ds0) {
 #pragma unroll
             for (int m = 0; m < MS; ++m) {
                 const int ib = wave + 4 * m;
@@ -630,7 +1144,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
             pW += a[0] * w[0] + a[1] * w[1] + a[2] * w[2] + a[3] * w[3];
         }
         if (n0 + BV < Dv) fetch_slice(n0 + BV);
-        __syncthreads();
+        lds_barrier();
 
 #pragma unroll
         for (int m = 0; m < NCC; ++m) {
@@ -655,7 +1169,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
                 dKb[m] = F16::mma(frag_rows<float, 16>(Us, VP, 16 * rb, 0, lane), df, dKb[m]);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- E: per-token partials to LDS; Ak into the freed slice buffers
@@ -696,7 +1210,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
         ta.load(rec + Rec<C>::oA, C);
         ta.template store<CP>(Aks);
     }
-    __syncthreads();
+    lds_barrier();
 
     // dP tiles -> dQK = Gamma o dP (into Ps); dM tiles -> dA = -dM, dKK =
     // Gamma o diag(beta) dA (into Ts).  E = dP o P + diag(beta) dA o Ak feeds
@@ -741,7 +1255,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
             if (lg == 0) colE[((part * NB + rb) * NB + jb) * 16 + ln] = cs;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- F: dQ = e^G o dQa + dQK K;
     //         dK = -e^G beta o dKa + d o dKb + dKK K + dKK^T K + dQK^T Q
@@ -841,6 +1355,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     kp.T = a.T; kp.H = a.H; kp.Dv = a.Dv;
     kp.NC = (a.T + C - 1) / C;
     kp.rec_floats = bwd_record_floats(C);
+    kp.xcd_map = (a.B * a.H) % 8 == 0 ? 1 : 0;
     const int64_t bh = a.B * a.H;
     float *ws = static_cast<float *>(a.ws);
     kp.rec = ws;
@@ -851,8 +1366,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     kp.dxb = kp.wb + bh * kp.NC * C * a.Dv;
     const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
     hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
-    hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, false>), dim3(nslice), dim3(NT), 0, stream, kp);
-    hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, true>), dim3(nslice), dim3(NT), 0, stream, kp);
+    if constexpr (std::is_same<Tin, __bf16>::value) {
+        hipLaunchKernelGGL((bwd_carry16_kernel<C, DK, false>), dim3(nslice), dim3(NTC), 0, stream, kp);
+        hipLaunchKernelGGL((bwd_carry16_kernel<C, DK, true>), dim3(nslice), dim3(NTC), 0, stream, kp);
+    } else {
+        hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, false>), dim3(nslice), dim3(NT), 0, stream, kp);
+        hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, true>), dim3(nslice), dim3(NT), 0, stream, kp);
+    }
     hipLaunchKernelGGL((bwd_chunk_kernel<Tin, C, DK>), dim3(nchunk), dim3(NTG), 0, stream, kp);
     return hipGetLastError();
 }
