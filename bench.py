@@ -112,6 +112,27 @@ def bwd_flops(B, T, H, Dk, Dv, C):
     return 2.0 * B * H * (-(-T // C)) * (prep + fwd + adj + chunk)
 
 
+def bwd_kernel_alg(B, T, H, Dk, Dv, C, in_bytes=2):
+    """Algorithmic HBM bytes of each backward kernel: its inputs read once and
+    its outputs written once, the workspace included (per-chunk records: T, P,
+    Gamma o K K^T and the decay prefix; the state entering and the state
+    gradient leaving every chunk; the chunk's U, V - e^G K S and dX)."""
+    nc = -(-T // C)
+    tok, ch = B * T * H, B * H * nc
+    qk, v = tok * Dk * in_bytes, tok * Dv * in_bytes
+    f32v = tok * Dv * 4
+    cc = ch * C * C * 4
+    g = ch * C * 4
+    st = ch * Dk * Dv * 4
+    cv = ch * C * Dv * 4
+    return {
+        "prep": 2 * qk + 8 * tok + ch * 4 * ((3 * C * C + C + 63) // 64 * 64),
+        "state": qk + v + cc + g + 4 * tok + st + 2 * cv,
+        "adjoint": 2 * qk + f32v + 2 * cc + g + 4 * tok + st + cv + f32v,
+        "chunk": 2 * qk + f32v + 2 * st + 3 * cv + 2 * cc + g + 8 * tok + 2 * tok * Dk * 4 + 8 * tok,
+    }
+
+
 def layer_flops(B, T, hidden, H, Dk, Dv, C):
     M = B * T
     gemm = 2 * M * hidden * (H * (2 * Dk + Dv) + 2 * H + H * Dv) + 2 * M * (H * Dv) * hidden
@@ -376,7 +397,9 @@ def main():
            "bwd_over_fwd": b_ms / ms_step, "flops_alg_per_call": b_flops,
            "tflops_achieved": b_flops / (b_ms * 1e-3) / 1e12, "peak_tflops": FP32_PEAK_TFLOPS,
            "frac": b_flops / (b_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
-           "note": "four kernels (prep, state pass, adjoint state pass, chunk gradients), all fp32 MFMA"}
+           "alg_bytes_per_kernel": bwd_kernel_alg(b_cfg.B, b_cfg.T, b_cfg.H, b_cfg.Dk, b_cfg.Dv, b_cfg.chunk),
+           "note": "four kernels: preparation (Gram on bf16 MFMA), state pass and adjoint state pass (bf16 MFMA, "
+                   "hi/lo operands), chunk gradients (fp32 MFMA); frac is against the fp32 MFMA peak"}
 
     cpu = None
     if not args.no_cpu_baseline:
