@@ -1342,6 +1342,385 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
     }
 }
 
+// ===========================================================================
+// 4'. chunk gradients, bf16 inputs: bf16 MFMA with hi/lo operands
+//
+// The steps of bwd_chunk_kernel with 32 value columns per pass: S, dS', U, dX
+// and dY enter as bf16 pairs (three 16x16x32 products per fp32 product); the
+// final products take K and Q exactly and dQK, dKK as pairs, with K^T, Q^T and
+// dKK^T, dQK^T from transposing reads.
+// ===========================================================================
+template <int C, int DK> struct Grad16Lay {
+    static constexpr int KP = DK + 8, CP = C + 4, HP = C + 8;   // K/Q bf16, P fp32, dQK/dKK bf16
+    static constexpr int SW = 32, SP = SW + 16;                  // value columns per pass, bf16 pitch
+    static constexpr int NB = C / 16, NKB = DK / 16;
+    static constexpr size_t oK = 0;
+    static constexpr size_t oQ = oK + 2 * C * KP;
+    static constexpr size_t oP = oQ + 2 * C * KP;             // P (fp32)
+    // value-slice operands (hi, lo); after the passes: Ak (fp32) and dQK, dKK (hi, lo)
+    static constexpr size_t SLICE = 2 * 2 * (2 * DK * SP + 3 * C * SP);
+    static constexpr size_t AFTER = 4 * C * CP + 4 * 2 * C * HP;
+    static constexpr size_t oR = oP + 4 * C * CP;
+    static constexpr size_t oSh = oR, oSl = oSh + 2 * DK * SP, oDSh = oSl + 2 * DK * SP, oDSl = oDSh + 2 * DK * SP;
+    static constexpr size_t oUh = oDSl + 2 * DK * SP, oUl = oUh + 2 * C * SP;
+    static constexpr size_t oXh = oUl + 2 * C * SP, oXl = oXh + 2 * C * SP;
+    static constexpr size_t oYh = oXl + 2 * C * SP, oYl = oYh + 2 * C * SP;
+    static constexpr size_t oAk = oR;
+    static constexpr size_t oQKh = oAk + 4 * C * CP, oQKl = oQKh + 2 * C * HP;
+    static constexpr size_t oKKh = oQKl + 2 * C * HP, oKKl = oKKh + 2 * C * HP;
+    static constexpr size_t oG = oR + (SLICE > AFTER ? SLICE : AFTER);
+    static constexpr size_t oB = oG + 4 * C;
+    static constexpr size_t oAl = oB + 4 * C;
+    static constexpr size_t oTB = oAl + 4 * C;
+    static constexpr size_t oSP = oTB + 4 * C;
+    static constexpr size_t oRP = oSP + 4 * 3 * NB * NKB * 16;
+    static constexpr size_t oCP = oRP + 4 * 2 * NB * NB * 16;
+    static constexpr size_t oRB = oCP + 4 * 2 * NB * NB * 16;
+    static constexpr size_t oRed = oRB + 4 * NB * NB * 16;
+    static constexpr size_t BYTES = oRed + 4 * 16;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int C, int DK>
+__global__ __launch_bounds__(NTG) void bwd_chunk16_kernel(BwdParams p)
+{
+    using L = Grad16Lay<C, DK>;
+    constexpr int KP = L::KP, CP = L::CP, HP = L::HP, SW = L::SW, SP = L::SP, NB = C / 16, NKB = DK / 16;
+    constexpr int NTRI = NB * (NB + 1) / 2;
+    constexpr int NCC = (2 * NTRI + NWG - 1) / NWG;
+    constexpr int NTILE = NB * NKB, NCK = (NTILE + NWG - 1) / NWG;
+    using F16 = Frag<__bf16, 16>;
+    using F32 = Frag<__bf16, 32>;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __bf16 *Ks = reinterpret_cast<__bf16 *>(smem + L::oK);
+    __bf16 *Qs = reinterpret_cast<__bf16 *>(smem + L::oQ);
+    float *Ps = reinterpret_cast<float *>(smem + L::oP);
+    __bf16 *Sh = reinterpret_cast<__bf16 *>(smem + L::oSh), *Sl = reinterpret_cast<__bf16 *>(smem + L::oSl);
+    __bf16 *DSh = reinterpret_cast<__bf16 *>(smem + L::oDSh), *DSl = reinterpret_cast<__bf16 *>(smem + L::oDSl);
+    __bf16 *Uh = reinterpret_cast<__bf16 *>(smem + L::oUh), *Ul = reinterpret_cast<__bf16 *>(smem + L::oUl);
+    __bf16 *Xh = reinterpret_cast<__bf16 *>(smem + L::oXh), *Xl = reinterpret_cast<__bf16 *>(smem + L::oXl);
+    __bf16 *Yh = reinterpret_cast<__bf16 *>(smem + L::oYh), *Yl = reinterpret_cast<__bf16 *>(smem + L::oYl);
+    float *Aks = reinterpret_cast<float *>(smem + L::oAk);
+    __bf16 *QKh = reinterpret_cast<__bf16 *>(smem + L::oQKh), *QKl = reinterpret_cast<__bf16 *>(smem + L::oQKl);
+    __bf16 *KKh = reinterpret_cast<__bf16 *>(smem + L::oKKh), *KKl = reinterpret_cast<__bf16 *>(smem + L::oKKl);
+    float *Gs = reinterpret_cast<float *>(smem + L::oG);
+    float *Bs = reinterpret_cast<float *>(smem + L::oB);
+    float *Als = reinterpret_cast<float *>(smem + L::oAl);
+    float *tokB = reinterpret_cast<float *>(smem + L::oTB);
+    float *sp = reinterpret_cast<float *>(smem + L::oSP);
+    float *rowE = reinterpret_cast<float *>(smem + L::oRP);
+    float *colE = reinterpret_cast<float *>(smem + L::oCP);
+    float *rowB = reinterpret_cast<float *>(smem + L::oRB);
+    float *red = reinterpret_cast<float *>(smem + L::oRed);
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+    const int64_t H = p.H, T = p.T, Dv = p.Dv, b = bh / H, h = bh % H, c0 = c * C;
+    const float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
+    const float *Sg = p.sc + (bh * p.NC + c) * DK * Dv;
+    const float *dSg = p.dsc + (bh * p.NC + c) * DK * Dv;
+    const float *Ug = p.ub + (bh * p.NC + c) * C * Dv;
+    const float *Wg = p.wb + (bh * p.NC + c) * C * Dv;
+    const float *Xg = p.dxb + (bh * p.NC + c) * C * Dv;
+
+    {
+        using R = Raw4<__bf16>;
+        RowsTile<__bf16, C, DK, NTG> tk, tq;
+        DenseTile<C, C, NTG> tp;
+        tk.load(static_cast<const __bf16 *>(p.k), b, h, c0, T, H, DK);
+        tq.load(static_cast<const __bf16 *>(p.q), b, h, c0, T, H, DK);
+        tp.load(rec + Rec<C>::oP, C);
+#pragma unroll
+        for (int it = 0; it < RowsTile<__bf16, C, DK, NTG>::NV; ++it) {
+            const int vi = tid + NTG * it;
+            const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
+            if (RowsTile<__bf16, C, DK, NTG>::NU % NTG == 0 || vi < RowsTile<__bf16, C, DK, NTG>::NU) {
+                *reinterpret_cast<R::type *>(Ks + r * KP + col) = tk.v[it];
+                *reinterpret_cast<R::type *>(Qs + r * KP + col) = tq.v[it];
+            }
+        }
+        tp.template store<CP>(Ps);
+    }
+    for (int i = tid; i < C; i += NTG) {
+        const int64_t t = c0 + i;
+        const bool ok = t < T;
+        Gs[i] = rec[Rec<C>::oG + i];
+        Bs[i] = ok ? p.beta[(b * T + t) * H + h] : 0.f;
+        Als[i] = ok ? p.alpha[(b * T + t) * H + h] : 1.f;
+    }
+
+    f32x4 dQa[NCK], dKa[NCK], dKb[NCK], dPM[NCC];
+#pragma unroll
+    for (int m = 0; m < NCK; ++m) dQa[m] = dKa[m] = dKb[m] = zero4();
+#pragma unroll
+    for (int m = 0; m < NCC; ++m) dPM[m] = zero4();
+    float pW = 0.f, pSS = 0.f;   // sum dX o W~ over this thread's row piece; <S, dS'> piece
+
+    DenseTile<DK, SW, NTG> rs, rds;
+    DenseTile<C, SW, NTG> ru, rx, rw;
+    RowsTile<float, C, SW, NTG> rdy;
+    static_assert(DenseTile<C, SW, NTG>::NV == 1, "one C x 32 slice unit per thread");
+    auto fetch_slice = [&](int n0) {
+        rs.load(Sg + n0, Dv);
+        rds.load(dSg + n0, Dv);
+        ru.load(Ug + n0, Dv);
+        rx.load(Xg + n0, Dv);
+        rw.load(Wg + n0, Dv);
+        rdy.load(p.dy, b, h, c0, T, H, Dv, n0);
+    };
+    fetch_slice(0);
+
+    for (int n0 = 0; n0 < Dv; n0 += SW) {
+#pragma unroll
+        for (int it = 0; it < DenseTile<DK, SW, NTG>::NV; ++it) {
+            const int vi = tid + NTG * it;
+            const int r = vi / (SW / 4), col = (vi % (SW / 4)) * 4;
+            if (DenseTile<DK, SW, NTG>::NU % NTG == 0 || vi < DenseTile<DK, SW, NTG>::NU) {
+                store_split4(Sh + r * SP + col, Sl + r * SP + col, rs.v[it]);
+                store_split4(DSh + r * SP + col, DSl + r * SP + col, rds.v[it]);
+            }
+            const f32x4 a = rs.v[it], d = rds.v[it];
+            pSS += a[0] * d[0] + a[1] * d[1] + a[2] * d[2] + a[3] * d[3];
+        }
+        {
+            const int vi = tid;
+            const int r = vi / (SW / 4), col = (vi % (SW / 4)) * 4;
+            if (DenseTile<C, SW, NTG>::NU % NTG == 0 || vi < DenseTile<C, SW, NTG>::NU) {
+                store_split4(Uh + r * SP + col, Ul + r * SP + col, ru.v[0]);
+                store_split4(Xh + r * SP + col, Xl + r * SP + col, rx.v[0]);
+                store_split4(Yh + r * SP + col, Yl + r * SP + col, rdy.v[0]);
+            }
+            const f32x4 a = rx.v[0], w = rw.v[0];
+            pW += a[0] * w[0] + a[1] * w[1] + a[2] * w[2] + a[3] * w[3];
+        }
+        if (n0 + SW < Dv) fetch_slice(n0 + SW);
+        lds_barrier();
+
+#pragma unroll
+        for (int m = 0; m < NCC; ++m) {
+            const int tile = wave + NWG * m;
+            if (tile < 2 * NTRI) {
+                const bool isM = tile >= NTRI;
+                int rb, jb;
+                tri_block(isM ? tile - NTRI : tile, rb, jb);
+                const F32 ah = frag_rows<__bf16, 32>(isM ? Xh : Yh, SP, 16 * rb, 0, lane);
+                const F32 al = frag_rows<__bf16, 32>(isM ? Xl : Yl, SP, 16 * rb, 0, lane);
+                const F32 bh2 = frag_rows<__bf16, 32>(Uh, SP, 16 * jb, 0, lane);
+                const F32 bl2 = frag_rows<__bf16, 32>(Ul, SP, 16 * jb, 0, lane);
+                dPM[m] = F32::mma(ah, bh2, dPM[m]);
+                dPM[m] = F32::mma(ah, bl2, dPM[m]);
+                dPM[m] = F32::mma(al, bh2, dPM[m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NCK; ++m) {
+            const int tile = wave + NWG * m;
+            if (tile < NTILE) {
+                const int rb = tile / NKB, kb = tile % NKB;
+                const F32 sh = frag_rows<__bf16, 32>(Sh, SP, 16 * kb, 0, lane);
+                const F32 sl = frag_rows<__bf16, 32>(Sl, SP, 16 * kb, 0, lane);
+                const F32 dh = frag_rows<__bf16, 32>(DSh, SP, 16 * kb, 0, lane);
+                const F32 dl = frag_rows<__bf16, 32>(DSl, SP, 16 * kb, 0, lane);
+                const F32 yh = frag_rows<__bf16, 32>(Yh, SP, 16 * rb, 0, lane);
+                const F32 yl = frag_rows<__bf16, 32>(Yl, SP, 16 * rb, 0, lane);
+                const F32 xh = frag_rows<__bf16, 32>(Xh, SP, 16 * rb, 0, lane);
+                const F32 xl = frag_rows<__bf16, 32>(Xl, SP, 16 * rb, 0, lane);
+                const F32 uh = frag_rows<__bf16, 32>(Uh, SP, 16 * rb, 0, lane);
+                const F32 ul = frag_rows<__bf16, 32>(Ul, SP, 16 * rb, 0, lane);
+                dQa[m] = F32::mma(yh, sh, dQa[m]);
+                dKa[m] = F32::mma(xh, sh, dKa[m]);
+                dKb[m] = F32::mma(uh, dh, dKb[m]);
+                dQa[m] = F32::mma(yh, sl, dQa[m]);
+                dKa[m] = F32::mma(xh, sl, dKa[m]);
+                dKb[m] = F32::mma(uh, dl, dKb[m]);
+                dQa[m] = F32::mma(yl, sh, dQa[m]);
+                dKa[m] = F32::mma(xl, sh, dKa[m]);
+                dKb[m] = F32::mma(ul, dh, dKb[m]);
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- E: per-token partials to LDS; Ak into the freed slice buffers
+    {
+        float w = pW;
+        // the 8 consecutive threads of a staged row piece hold one row's 32 columns
+        w += __shfl_xor(w, 1);
+        w += __shfl_xor(w, 2);
+        w += __shfl_xor(w, 4);
+        if ((tid & 7) == 0 && tid / 8 < C) tokB[tid / 8] = w;
+        float y = pSS;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off);
+        if (lane == 0) red[wave] = y;
+    }
+#pragma unroll
+    for (int m = 0; m < NCK; ++m) {
+        const int tile = wave + NWG * m;
+        if (tile < NTILE) {
+            const int rb = tile / NKB, kb = tile % NKB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e, col = 16 * kb + ln;
+                const float qv = (float)Qs[r * KP + col], kv = (float)Ks[r * KP + col];
+                const float a1 = row16_total(qv * dQa[m][e]);
+                const float a2 = row16_total(kv * dKa[m][e]);
+                const float a3 = row16_total(kv * dKb[m][e]);
+                if (ln == 15) {
+                    sp[(0 * NTILE + tile) * 16 + 4 * lg + e] = a1;
+                    sp[(1 * NTILE + tile) * 16 + 4 * lg + e] = a2;
+                    sp[(2 * NTILE + tile) * 16 + 4 * lg + e] = a3;
+                }
+            }
+        }
+    }
+    {
+        DenseTile<C, C, NTG> ta;
+        ta.load(rec + Rec<C>::oA, C);
+        ta.template store<CP>(Aks);
+    }
+    lds_barrier();
+
+    // dP tiles -> dQK = Gamma o dP; dM tiles -> dA = -dM, dKK = Gamma o diag(beta) dA;
+    // both as bf16 pairs for the final products.  Row/column sums as in the fp32 kernel.
+#pragma unroll
+    for (int m = 0; m < NCC; ++m) {
+        const int tile = wave + NWG * m;
+        if (tile < 2 * NTRI) {
+            const int part = tile >= NTRI ? 1 : 0;
+            int rb, jb;
+            tri_block(part ? tile - NTRI : tile, rb, jb);
+            const int j = 16 * jb + ln;
+            float cs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gs[j], 0.f));
+                float E, rbeta = 0.f, outv;
+                if (part) {
+                    const float dA = r > j ? -dPM[m][e] : 0.f;
+                    const float ak = Aks[r * CP + j];
+                    const float dAk = Bs[r] * dA;
+                    outv = gam * dAk;
+                    E = dAk * ak;
+                    rbeta = dA * ak;
+                } else {
+                    const float dP = r >= j ? dPM[m][e] : 0.f;
+                    E = dP * Ps[r * CP + j];
+                    outv = gam * dP;
+                }
+                const __bf16 hi = (__bf16)outv;
+                const __bf16 lo = (__bf16)(outv - (float)hi);
+                __bf16 *dh = part ? KKh : QKh, *dl = part ? KKl : QKl;
+                dh[r * HP + j] = hi;
+                dl[r * HP + j] = lo;
+                cs += E;
+                const float rs = row16_total(E);
+                const float rsb = row16_total(rbeta);
+                if (ln == 15) {
+                    rowE[((part * NB + rb) * NB + jb) * 16 + 4 * lg + e] = rs;
+                    if (part) rowB[(rb * NB + jb) * 16 + 4 * lg + e] = rsb;
+                }
+            }
+            cs += __shfl_xor(cs, 16);
+            cs += __shfl_xor(cs, 32);
+            if (lg == 0) colE[((part * NB + rb) * NB + jb) * 16 + ln] = cs;
+        }
+    }
+    lds_barrier();
+
+    // ---- F: dQ = e^G o dQa + dQK K;
+    //         dK = -e^G beta o dKa + d o dKb + dKK K + dKK^T K + dQK^T Q
+#pragma unroll
+    for (int m = 0; m < NCK; ++m) {
+        const int tile = wave + NWG * m;
+        if (tile < NTILE) {
+            const int rb = tile / NKB, kb = tile % NKB;
+            const float GC = Gs[C - 1];
+            f32x4 dq, dk, dq2 = zero4(), dk2 = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                const float br = __builtin_amdgcn_exp2f(Gs[r]), dr = __builtin_amdgcn_exp2f(GC - Gs[r]);
+                dq[e] = br * dQa[m][e];
+                dk[e] = dr * dKb[m][e] - br * Bs[r] * dKa[m][e];
+            }
+            for (int jb = 0; jb <= rb; ++jb) {
+                // K block jb as the B operand: B[k = token][n = dk column]
+                const F16 kf = tr_frag16(Ks, KP, 16 * kb, 16 * jb, lane);
+                dq = F16::mma(frag_rows<__bf16, 16>(QKh, HP, 16 * rb, 16 * jb, lane), kf, dq);
+                dq2 = F16::mma(frag_rows<__bf16, 16>(QKl, HP, 16 * rb, 16 * jb, lane), kf, dq2);
+                dk = F16::mma(frag_rows<__bf16, 16>(KKh, HP, 16 * rb, 16 * jb, lane), kf, dk);
+                dk2 = F16::mma(frag_rows<__bf16, 16>(KKl, HP, 16 * rb, 16 * jb, lane), kf, dk2);
+            }
+            for (int ib = rb; ib < NB; ++ib) {
+                const F16 kf = tr_frag16(Ks, KP, 16 * kb, 16 * ib, lane);
+                const F16 qf = tr_frag16(Qs, KP, 16 * kb, 16 * ib, lane);
+                dk = F16::mma(tr_frag16(KKh, HP, 16 * rb, 16 * ib, lane), kf, dk);
+                dk2 = F16::mma(tr_frag16(KKl, HP, 16 * rb, 16 * ib, lane), kf, dk2);
+                dk = F16::mma(tr_frag16(QKh, HP, 16 * rb, 16 * ib, lane), qf, dk);
+                dk2 = F16::mma(tr_frag16(QKl, HP, 16 * rb, 16 * ib, lane), qf, dk2);
+            }
+            dq += dq2;
+            dk += dk2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t t = c0 + 16 * rb + 4 * lg + e;
+                if (t < T) {
+                    const int64_t o = ((b * T + t) * H + h) * DK + 16 * kb + ln;
+                    p.dq[o] = dq[e];
+                    p.dk[o] = dk[e];
+                }
+            }
+        }
+    }
+
+    // ---- G: dG per token, d ln alpha = suffix sums of dG, dalpha, dbeta
+    if (wave == 0) {
+        const int rr = C - 1 - lane;    // lane l carries token C-1-l (reversed for the scan)
+        const float GC = Gs[C - 1];
+        float g = 0.f, d3 = 0.f;
+        if (lane < C) {
+            const int rb = rr / 16, ri = rr % 16;
+            float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int tile = rb * NKB + kb;
+                s1 += sp[(0 * NTILE + tile) * 16 + ri];
+                s2 += sp[(1 * NTILE + tile) * 16 + ri];
+                s3 += sp[(2 * NTILE + tile) * 16 + ri];
+            }
+            const float br = __builtin_amdgcn_exp2f(Gs[rr]), dr = __builtin_amdgcn_exp2f(GC - Gs[rr]);
+            d3 = dr * s3;
+            g = br * s1 - br * Bs[rr] * s2 - d3;
+            for (int jb = 0; jb <= rb; ++jb)
+                g += rowE[(rb * NB + jb) * 16 + ri] + rowE[((NB + rb) * NB + jb) * 16 + ri];
+            for (int ib = rb; ib < NB; ++ib)
+                g -= colE[(ib * NB + rb) * 16 + ri] + colE[((NB + ib) * NB + rb) * 16 + ri];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) d3 += __shfl_xor(d3, off);
+        {
+            float ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWG; ++w) ss += red[w];
+            if (lane == 0) g += d3 + __builtin_amdgcn_exp2f(GC) * ss;
+        }
+        const float suf = wave_inclusive_sum(g, lane);
+        if (lane < C) {
+            const int64_t t = c0 + rr;
+            if (t < T) {
+                const int rb = rr / 16, ri = rr % 16;
+                float db = tokB[rr];
+                for (int jb = 0; jb <= rb; ++jb) db += rowB[(rb * NB + jb) * 16 + ri];
+                const int64_t o = (b * T + t) * H + h;
+                p.dalpha[o] = suf / Als[rr];
+                p.dbeta[o] = db;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
@@ -1373,7 +1752,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
         hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, false>), dim3(nslice), dim3(NT), 0, stream, kp);
         hipLaunchKernelGGL((bwd_carry_kernel<Tin, C, DK, true>), dim3(nslice), dim3(NT), 0, stream, kp);
     }
-    hipLaunchKernelGGL((bwd_chunk_kernel<Tin, C, DK>), dim3(nchunk), dim3(NTG), 0, stream, kp);
+    // the bf16 chunk-gradient kernel takes the value columns 32 at a time
+    if (std::is_same<Tin, __bf16>::value && a.Dv % 32 == 0)
+        hipLaunchKernelGGL((bwd_chunk16_kernel<C, DK>), dim3(nchunk), dim3(NTG), 0, stream, kp);
+    else
+        hipLaunchKernelGGL((bwd_chunk_kernel<Tin, C, DK>), dim3(nchunk), dim3(NTG), 0, stream, kp);
     return hipGetLastError();
 }
 
