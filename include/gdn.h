@@ -74,9 +74,15 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *                 per (sequence, head, chunk) -- the chunk quantities that do
  *                 not depend on the state (decay factors, (I + A)^-1 diag(beta)
  *                 and the masked Q K^T block, as bf16 hi/lo MFMA fragments;
- *                 21056 bytes at C = 64); GDN_F32 needs none (size 0, may be
- *                 NULL).  Too small or missing: GDN_ERR_WORKSPACE.  Its
- *                 contents are overwritten; nothing in it is kept between calls.
+ *                 21056 bytes at C = 64).  For GDN_F32 the workspace is
+ *                 optional: with one of gdn_prefill_workspace_bytes(...)
+ *                 bytes (per chunk, (I + A)^-1, P, the masked K K^T and the
+ *                 decay prefix in fp32: 49408 bytes at C = 64) the chunk
+ *                 quantities are computed once per chunk by a separate kernel
+ *                 before the recurrence; with NULL a single kernel computes
+ *                 them inside every 16-column value slice.  Too small (or
+ *                 missing for GDN_BF16): GDN_ERR_WORKSPACE.  Its contents are
+ *                 overwritten; nothing in it is kept between calls.
  * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
  */
 GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,

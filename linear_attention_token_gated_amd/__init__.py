@@ -135,11 +135,13 @@ def prefill_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype="bf16") -> int:
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_final_state: bool = True,
-            y=None, final_state=None, workspace=None):
+            y=None, final_state=None, workspace=None, single_kernel: bool = False):
     """Chunked prefill.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (float32 or bfloat16);
     alpha, beta: [B,T,H] float32; initial_state: [B,H,Dk,Dv] float32 or None.
     workspace: a device buffer of prefill_workspace_bytes(...) bytes, or None
-    to allocate one for this call.
+    to allocate one for this call.  For float32 inputs the workspace selects
+    the two-kernel path; single_kernel=True runs the single-kernel fp32 path
+    without one.
     Returns (y [B,T,H,Dv] float32, final_state or None)."""
     import torch
     B, T, H, Dk = q.shape
@@ -155,6 +157,10 @@ def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_fi
     _need(y, "y", torch.float32)
     _need(final_state, "final_state", torch.float32)
     need = int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _dtype_code(q)))
+    if single_kernel:
+        if _dtype_code(q) != GDN_F32:
+            raise ValueError("single_kernel applies to float32 inputs only")
+        workspace, need = None, 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

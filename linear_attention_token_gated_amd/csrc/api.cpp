@@ -93,10 +93,14 @@ const char *gdn_last_error(void) { return g_err; }
 size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                                    gdn_dtype dtype)
 {
-    if (B <= 0 || T <= 0 || H <= 0 || dtype != GDN_BF16 || !is_pow2_dim(Dk) || !is_pow2_dim(Dv) ||
-        (chunk != 16 && chunk != 32 && chunk != 64))
+    if (B <= 0 || T <= 0 || H <= 0 || (dtype != GDN_BF16 && dtype != GDN_F32) || !is_pow2_dim(Dk) ||
+        !is_pow2_dim(Dv) || (chunk != 16 && chunk != 32 && chunk != 64))
         return 0;
     int64_t n;
+    if (dtype == GDN_F32) {
+        if (!count(&n, {B, H, (T + chunk - 1) / chunk, gdn::bwd_record_floats(chunk), 4})) return 0;
+        return gdn::prefill_f32_workspace_bytes(B, T, H, chunk);
+    }
     if (!count(&n, {B, H, (T + chunk - 1) / chunk, (int64_t)gdn::prep_record_bytes(chunk)})) return 0;
     return gdn::prefill_workspace_bytes(B, T, H, chunk, true);
 }
@@ -158,7 +162,10 @@ gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k
         if (overlap(rs, inputs[i])) return fail(GDN_ERR_ALIAS, "%s: final_state overlaps %s", fn, inputs[i].name);
     if (final_state != initial_state && overlap(rs, inputs[5]))
         return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
-    const size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
+    // fp32: the workspace is optional; given (at least `need` bytes) it selects
+    // the two-kernel path, NULL the single-kernel one
+    size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
+    if (dtype == GDN_F32 && !workspace) need = 0;
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

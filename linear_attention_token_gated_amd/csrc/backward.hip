@@ -52,6 +52,8 @@ struct BwdParams {
     float *rec, *sc, *dsc;
     float *ub, *wb, *dxb;      // per chunk [C][Dv]: U, W~ = V - e^G K S (state pass), dX (adjoint pass)
     int64_t T, H, Dv, NC;
+    int64_t qs, ks, vs;        // elements between consecutive tokens of q, k, v (H * D when dense)
+    float *y, *sT;             // forward path: y [B, T, H, Dv], final state or null
     int64_t rec_floats;
     int xcd_map;               // state passes: the slices of one head on one XCD (B*H % 8 == 0)
 };
@@ -80,12 +82,13 @@ template <> struct Raw4<__bf16> {
 };
 
 // Rows t = c0 .. c0+C-1, columns n0 .. n0+W-1 of head h of a [B, T, H, ld]
-// tensor; zeros past T.  Stored with pitch P floats.
+// tensor whose consecutive tokens are `tok` elements apart (H * ld when dense);
+// zeros past T.  Stored with pitch P floats.
 template <typename Tin, int C, int W, int NTH = NT> struct RowsTile {
     using R = Raw4<Tin>;
     static constexpr int NU = C * W / 4, NV = (NU + NTH - 1) / NTH;
     typename R::type v[NV];
-    __device__ __forceinline__ void load(const Tin *src, int64_t b, int64_t h, int64_t c0, int64_t T, int64_t H,
+    __device__ __forceinline__ void load(const Tin *src, int64_t b, int64_t h, int64_t c0, int64_t T, int64_t tok,
                                          int64_t ld, int n0 = 0) {
 #pragma unroll
         for (int it = 0; it < NV; ++it) {
@@ -93,7 +96,7 @@ template <typename Tin, int C, int W, int NTH = NT> struct RowsTile {
             const int r = vi / (W / 4), col = (vi % (W / 4)) * 4;
             const int64_t t = c0 + r;
             v[it] = R::zero();
-            if ((NU % NTH == 0 || vi < NU) && t < T) v[it] = R::load(src + ((b * T + t) * H + h) * ld + n0 + col);
+            if ((NU % NTH == 0 || vi < NU) && t < T) v[it] = R::load(src + (b * T + t) * tok + h * ld + n0 + col);
         }
     }
     template <int P> __device__ __forceinline__ void store(float *dst) const {
@@ -200,8 +203,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     {
         using R = Raw4<Tin>;
         RowsTile<Tin, C, DK> tk, tq;
-        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
-        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, p.ks, DK);
+        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, p.qs, DK);
 #pragma unroll
         for (int it = 0; it < RowsTile<Tin, C, DK>::NV; ++it) {
             const int vi = tid + NT * it;
@@ -376,14 +379,14 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p)
     auto fetch = [&](int64_t c) {
         const int64_t c0 = c * C;
         const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
-        rk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
+        rk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H * DK, DK);
         rt.load(rec + Rec<C>::oT, C);
         if constexpr (ADJ) {
-            rq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+            rq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H * DK, DK);
             rp.load(rec + Rec<C>::oP, C);
-            ri.load(p.dy, b, h, c0, T, H, Dv, n0);
+            ri.load(p.dy, b, h, c0, T, H * Dv, Dv, n0);
         } else {
-            ri.load(static_cast<const Tin *>(p.v), b, h, c0, T, H, Dv, n0);
+            ri.load(static_cast<const Tin *>(p.v), b, h, c0, T, H * Dv, Dv, n0);
         }
         if (threadIdx.x < C) {
             const int64_t t = c0 + threadIdx.x;
@@ -1090,8 +1093,8 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
     {
         RowsTile<Tin, C, DK, NTG> tk, tq;
         DenseTile<C, C, NTG> tp;
-        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H, DK);
-        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H, DK);
+        tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, H * DK, DK);
+        tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, H * DK, DK);
         tp.load(rec + Rec<C>::oP, C);
         tk.template store<KP>(Ks);
         tq.template store<KP>(Qs);
@@ -1124,7 +1127,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk_kernel(BwdParams p)
         ru.load(Ug + n0, Dv);
         rx.load(Xg + n0, Dv);
         rw.load(Wg + n0, Dv);
-        rdy.load(p.dy, b, h, c0, T, H, Dv, n0);
+        rdy.load(p.dy, b, h, c0, T, H * Dv, Dv, n0);
     };
     fetch_slice(0);
 
@@ -1428,8 +1431,8 @@ __global__ __launch_bounds__(NTG) void bwd_chunk16_kernel(BwdParams p)
         using R = Raw4<__bf16>;
         RowsTile<__bf16, C, DK, NTG> tk, tq;
         DenseTile<C, C, NTG> tp;
-        tk.load(static_cast<const __bf16 *>(p.k), b, h, c0, T, H, DK);
-        tq.load(static_cast<const __bf16 *>(p.q), b, h, c0, T, H, DK);
+        tk.load(static_cast<const __bf16 *>(p.k), b, h, c0, T, H * DK, DK);
+        tq.load(static_cast<const __bf16 *>(p.q), b, h, c0, T, H * DK, DK);
         tp.load(rec + Rec<C>::oP, C);
 #pragma unroll
         for (int it = 0; it < RowsTile<__bf16, C, DK, NTG>::NV; ++it) {
@@ -1467,7 +1470,7 @@ __global__ __launch_bounds__(NTG) void bwd_chunk16_kernel(BwdParams p)
         ru.load(Ug + n0, Dv);
         rx.load(Xg + n0, Dv);
         rw.load(Wg + n0, Dv);
-        rdy.load(p.dy, b, h, c0, T, H, Dv, n0);
+        rdy.load(p.dy, b, h, c0, T, H * Dv, Dv, n0);
     };
     fetch_slice(0);
 
@@ -1721,6 +1724,193 @@ __global__ __launch_bounds__(NTG) void bwd_chunk16_kernel(BwdParams p)
     }
 }
 
+// ===========================================================================
+// Forward prefill for fp32 inputs in two kernels: bwd_prep_kernel<float> (T, P
+// and the decay prefix of every chunk, once per chunk) and fwd32_carry_kernel,
+// the state recurrence over 16-column slices that also writes y:
+//   X = diag(beta)(V - diag(e^G) K S),  U = T X,
+//   Y = diag(e^G) Q S + P U,  S' = e^{G_C} S + K^T diag(d) U.
+// q, k, v may be slices of a wider buffer (token strides).
+// ===========================================================================
+template <int C, int DK> struct Fwd32Lay {
+    static constexpr int KP = DK + 4, CP = C + 4;
+    static constexpr size_t oK = 0;
+    static constexpr size_t oQ = oK + 4 * C * KP;
+    static constexpr size_t oT = oQ + 4 * C * KP;
+    static constexpr size_t oP = oT + 4 * C * CP;
+    static constexpr size_t oST = oP + 4 * C * CP;
+    static constexpr size_t oIn = oST + 4 * BV * KP;
+    static constexpr size_t oX = oIn + 4 * C * VP;
+    static constexpr size_t oU = oX + 4 * C * VP;
+    static constexpr size_t oUd = oU + 4 * C * VP;
+    static constexpr size_t oG = oUd + 4 * BV * CP;
+    static constexpr size_t oB = oG + 4 * C;
+    static constexpr size_t BYTES = oB + 4 * C;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int C, int DK>
+__global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
+{
+    using L = Fwd32Lay<C, DK>;
+    constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4;
+    constexpr int KSD = DK % 32 == 0 ? 32 : 16, KSC = C % 32 == 0 ? 32 : 16;
+    using FD = Frag<float, KSD>;
+    using FC = Frag<float, KSC>;
+    using F16 = Frag<float, 16>;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    float *Ks = reinterpret_cast<float *>(smem + L::oK);
+    float *Qs = reinterpret_cast<float *>(smem + L::oQ);
+    float *Ts = reinterpret_cast<float *>(smem + L::oT);
+    float *Ps = reinterpret_cast<float *>(smem + L::oP);
+    float *STs = reinterpret_cast<float *>(smem + L::oST);
+    float *Ins = reinterpret_cast<float *>(smem + L::oIn);
+    float *Xs = reinterpret_cast<float *>(smem + L::oX);
+    float *Us = reinterpret_cast<float *>(smem + L::oU);
+    float *UdT = reinterpret_cast<float *>(smem + L::oUd);
+    float *Gs = reinterpret_cast<float *>(smem + L::oG);
+    float *Bs = reinterpret_cast<float *>(smem + L::oB);
+
+    const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
+    const int64_t NS = p.Dv / BV;
+    int64_t bh, sl;
+    slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
+    const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
+    const int n0 = (int)sl * BV;
+
+    f32x4 S[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        S[m] = zero4();
+        const int ib = wave + 4 * m;
+        if (ib < NKB && p.s0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = p.s0[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln];
+        }
+    }
+
+    RowsTile<float, C, DK> rk, rq;
+    DenseTile<C, C> rt, rp;
+    RowsTile<float, C, BV> ri;
+    float rg = 0.f, rbeta = 0.f;
+    auto fetch = [&](int64_t c) {
+        const int64_t c0 = c * C;
+        const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
+        rk.load(static_cast<const float *>(p.k), b, h, c0, T, p.ks, DK);
+        rq.load(static_cast<const float *>(p.q), b, h, c0, T, p.qs, DK);
+        rt.load(rec + Rec<C>::oT, C);
+        rp.load(rec + Rec<C>::oP, C);
+        ri.load(static_cast<const float *>(p.v), b, h, c0, T, p.vs, Dv, n0);
+        if (threadIdx.x < C) {
+            const int64_t t = c0 + threadIdx.x;
+            rg = rec[Rec<C>::oG + threadIdx.x];
+            rbeta = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
+        }
+    };
+    fetch(0);
+
+    for (int64_t c = 0; c < NC; ++c) {
+        const int64_t c0 = c * C;
+        rk.template store<KP>(Ks);
+        rq.template store<KP>(Qs);
+        rt.template store<CP>(Ts);
+        rp.template store<CP>(Ps);
+        ri.template store<VP>(Ins);
+        if (threadIdx.x < C) {
+            Gs[threadIdx.x] = rg;
+            Bs[threadIdx.x] = rbeta;
+        }
+        if (c + 1 < NC) fetch(c + 1);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) STs[ln * KP + 16 * ib + 4 * lg + e] = S[m][e];
+            }
+        }
+        lds_barrier();
+        const float GC = Gs[C - 1];
+
+        // step 1: K S -> X = diag(beta)(V - e^G K S); Q S kept for y
+        f32x4 qsv = zero4();
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 ks = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KSD) {
+                const FD sf = frag_rows<float, KSD>(STs, KP, 0, k0, lane);
+                ks = FD::mma(frag_rows<float, KSD>(Ks, KP, 16 * rb, k0, lane), sf, ks);
+                qsv = FD::mma(frag_rows<float, KSD>(Qs, KP, 16 * rb, k0, lane), sf, qsv);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                Xs[r * VP + ln] = Bs[r] * (Ins[r * VP + ln] - __builtin_amdgcn_exp2f(Gs[r]) * ks[e]);
+            }
+        }
+        lds_barrier();
+
+        // step 2: U = T X (row-major for P U, decayed and transposed for the update)
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 acc = zero4();
+            for (int kb = 0; kb <= rb; ++kb)
+                acc = F16::mma(frag_rows<float, 16>(Ts, CP, 16 * rb, 16 * kb, lane),
+                               frag_cols<float, 16>(Xs, VP, 0, 16 * kb, lane), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                Us[r * VP + ln] = acc[e];
+                UdT[ln * CP + r] = __builtin_amdgcn_exp2f(GC - Gs[r]) * acc[e];
+            }
+        }
+        lds_barrier();
+
+        // step 3: Y = diag(e^G) Q S + P U;  S <- e^{G_C} S + K^T (d o U)
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_exp2f(Gs[16 * rb + 4 * lg + e]) * qsv[e];
+            for (int jb = 0; jb <= rb; ++jb)
+                acc = F16::mma(frag_rows<float, 16>(Ps, CP, 16 * rb, 16 * jb, lane),
+                               frag_cols<float, 16>(Us, VP, 0, 16 * jb, lane), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t t = c0 + 16 * rb + 4 * lg + e;
+                if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e];
+            }
+        }
+        const float eGC = __builtin_amdgcn_exp2f(GC);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+                f32x4 acc = S[m] * eGC;
+#pragma unroll
+                for (int j0 = 0; j0 < C; j0 += KSC)
+                    acc = FC::mma(frag_cols<float, KSC>(Ks, KP, 16 * ib, j0, lane),
+                                  frag_rows<float, KSC>(UdT, CP, 0, j0, lane), acc);
+                S[m] = acc;
+            }
+        }
+        lds_barrier();
+    }
+
+    if (p.sT) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p.sT[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
@@ -1734,6 +1924,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     kp.T = a.T; kp.H = a.H; kp.Dv = a.Dv;
     kp.NC = (a.T + C - 1) / C;
     kp.rec_floats = bwd_record_floats(C);
+    kp.qs = a.H * DK; kp.ks = a.H * DK; kp.vs = a.H * a.Dv;
+    kp.y = nullptr; kp.sT = nullptr;
     kp.xcd_map = (a.B * a.H) % 8 == 0 ? 1 : 0;
     const int64_t bh = a.B * a.H;
     float *ws = static_cast<float *>(a.ws);
@@ -1783,6 +1975,38 @@ hipError_t launch_bwd_c(const BwdArgs &a, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+template <int C, int DK>
+hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
+{
+    BwdParams kp{};
+    kp.q = a.q; kp.k = a.k; kp.v = a.v;
+    kp.alpha = a.alpha; kp.beta = a.beta; kp.s0 = a.s0;
+    kp.y = a.y; kp.sT = a.sT;
+    kp.T = a.T; kp.H = a.H; kp.Dv = a.Dv;
+    kp.NC = (a.T + C - 1) / C;
+    kp.rec_floats = bwd_record_floats(C);
+    kp.xcd_map = (a.B * a.H) % 8 == 0 ? 1 : 0;
+    kp.qs = a.q_tok_stride; kp.ks = a.k_tok_stride; kp.vs = a.v_tok_stride;
+    kp.rec = static_cast<float *>(a.ws);
+    const int64_t bh = a.B * a.H;
+    const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
+    hipLaunchKernelGGL((bwd_prep_kernel<float, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
+    hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_fwd32_dk(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.Dk) {
+    case 16: return launch_fwd32_t<C, 16>(a, s);
+    case 32: return launch_fwd32_t<C, 32>(a, s);
+    case 64: return launch_fwd32_t<C, 64>(a, s);
+    case 128: return launch_fwd32_t<C, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 // T == 0: dL/dS_0 = dL/dS_T (or zero)
 __global__ void copy_or_zero(const float *__restrict__ src, float *__restrict__ dst, int64_t n)
 {
@@ -1798,6 +2022,21 @@ size_t prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, 
 {
     const int64_t nc = (T + C - 1) / C;
     return (size_t)(4 * B * H * nc * (bwd_record_floats(C) + 2 * Dk * Dv + 3 * C * Dv));
+}
+
+size_t prefill_f32_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t C)
+{
+    return (size_t)(4 * B * H * ((T + C - 1) / C) * bwd_record_floats(C));
+}
+
+hipError_t launch_prefill_f32_staged(const PrefillArgs &a, hipStream_t stream)
+{
+    switch (a.chunk) {
+    case 16: return launch_fwd32_dk<16>(a, stream);
+    case 32: return launch_fwd32_dk<32>(a, stream);
+    case 64: return launch_fwd32_dk<64>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)

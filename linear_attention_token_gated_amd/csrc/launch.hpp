@@ -71,6 +71,12 @@ int64_t bwd_record_floats(int64_t C);
 size_t prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C);
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
 
+// fp32 prefill in two kernels (backward.hip): per-chunk preparation into a
+// record workspace of prefill_f32_workspace_bytes(...) bytes (a.ws), then the
+// state recurrence writing y; q, k, v with token strides
+size_t prefill_f32_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t C);
+hipError_t launch_prefill_f32_staged(const PrefillArgs &a, hipStream_t stream);
+
 // Layer helpers (layer.hip)
 struct LayerArgs {
     const void *x;

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__
 constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-    size_t pre, post, z, ab, alpha, beta, y, g, total;
+    size_t pre, post, z, ab, alpha, beta, y, g, rec, total;
 };
 
 WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv)
@@ -403,6 +403,8 @@ WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv)
     w.beta = o;  o += al256(M * (size_t)H * 4);
     w.y = o;     o += al256(M * (size_t)(H * Dv) * 4);
     w.g = o;     o += al256(M * (size_t)(H * Dv) * 2);
+    // per-chunk records of the fp32 core; chunk 64 needs the most of {16, 32, 64}
+    w.rec = o;   o += al256(prefill_f32_workspace_bytes(B, T, H, 64));
     w.total = o;
     return w;
 }
@@ -490,6 +492,7 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     p.B = a.B; p.T = a.T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = a.chunk;
     p.q_tok_stride = nqkv; p.k_tok_stride = nqkv; p.v_tok_stride = nqkv;
     p.bf16 = false;
+    p.ws = ws + w.rec;        // per-chunk records: the two-kernel fp32 core
     if ((e = launch_prefill(p, s))) return e;
 
     switch (Dv) {

@@ -493,6 +493,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages)
         }
         return (stages & 2) ? launch_recurrence(a, stream) : hipSuccess;
     }
+    // fp32 with a record workspace: preparation once per chunk, then the
+    // recurrence (backward.hip); without one, the single kernel below
+    if (a.ws) return launch_prefill_f32_staged(a, stream);
     return launch_c<float>(a, stream);
 }
 

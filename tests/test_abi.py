@@ -100,6 +100,15 @@ def recurrence(L, q=A, k=A + 64 * MB, v=A + 128 * MB, s0=None, y=A + 256 * MB, s
     return L.gdn_prefill_recurrence(q, k, v, s0, y, sT, B, T, H, Dk, Dv, C, w, wb, None)
 
 
+def test_prefill_f32_optional_workspace(L):
+    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 0)
+    assert need == 4 * 2 * 4 * 832
+    ws = A + 512 * MB
+    assert prefill(L, w=ws, wb=need - 1) == WS          # given but too small
+    assert prefill(L, w=ws + 16, wb=need) == ALIGN      # given but misaligned
+    assert prefill(L, w=A + 256 * MB, wb=need) == ALIAS  # over y
+
+
 def test_stage_validation(L):
     # every case fails on the host before anything is launched
     assert prepare(L, q=None) == NULL
@@ -211,7 +220,8 @@ def test_workspace_queries(L):
     # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
     assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
     assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 0      # fp32 needs none
+    # fp32: optional records of the two-kernel path, 3*64*64+64 floats per chunk
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 4 * 32 * 512 * 12352
     assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
     assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
     assert L.gdn_layer_workspace_bytes(1, 0, 2048, 16, 128, 128, 4, 64) == 0

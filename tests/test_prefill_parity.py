@@ -191,3 +191,20 @@ def test_prefill_stages_equal_fused(oracle_mod, chunk):
     assert torch.equal(y_s, y_f) and torch.equal(s_s, s_f)
     y_ref, S_ref = oracle_prefill(oracle_mod, inp)
     assert rel_err(host(y_s), y_ref) <= TOL_BF16 and rel_err(host(s_s), S_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (64, 32), (128, 128), (16, 128)])
+def test_prefill_f32_single_kernel_and_two_kernel_paths(oracle_mod, chunk, Dk, Dv):
+    """fp32 inputs: with a workspace the two-kernel path (preparation, then the
+    recurrence) runs, without one the single-kernel path; both against the
+    oracle."""
+    T = 2 * chunk + 7
+    print(f"case: fp32 paths B=2 T={T} H=3 Dk={Dk} Dv={Dv} C={chunk}", flush=True)
+    inp = wl.prefill_inputs(2, T, 3, Dk, Dv, dtype="f32", s0_std=0.3, seed=5 * Dk + Dv + chunk)
+    y_ref, S_ref = oracle_prefill(oracle_mod, inp)
+    for single in (False, True):
+        y, sT = _gpu(inp, chunk, single_kernel=single)
+        ey, eS = rel_err(host(y), y_ref), rel_err(host(sT), S_ref)
+        print(f"  single_kernel={single} err y={ey:.3e} S={eS:.3e}", flush=True)
+        assert ey <= TOL_F32 and eS <= TOL_F32, (single, ey, eS)
