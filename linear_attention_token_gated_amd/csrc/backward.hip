@@ -1911,6 +1911,234 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
     }
 }
 
+// The same recurrence on bf16 MFMA: every fp32 operand (K, Q, the state, T, P,
+// X, U and the decayed U) enters as a bf16 pair hi + lo, and each product sums
+// hi*hi + hi*lo + lo*hi (about 16 bits of every operand).  Same LDS bytes as
+// the fp32 form; the MFMA chain per chunk is a quarter as long.
+template <int C, int DK> struct Fwd16Lay {
+    static constexpr int KP = DK + 8, CP = C + 8;   // bf16 pitches
+    static constexpr size_t KB = 2 * C * KP, CB = 2 * C * CP, SB = 2 * BV * KP, TB = 2 * BV * CP;
+    static constexpr size_t oKh = 0, oKl = oKh + KB, oQh = oKl + KB, oQl = oQh + KB;
+    static constexpr size_t oTh = oQl + KB, oTl = oTh + CB, oPh = oTl + CB, oPl = oPh + CB;
+    static constexpr size_t oSTh = oPl + CB, oSTl = oSTh + SB;
+    static constexpr size_t oXh = oSTl + SB, oXl = oXh + TB;       // X^T
+    static constexpr size_t oUh = oXl + TB, oUl = oUh + TB;        // U^T (for P U)
+    static constexpr size_t oDh = oUl + TB, oDl = oDh + TB;        // (d o U)^T (for the update)
+    static constexpr size_t oIn = oDl + TB;
+    static constexpr size_t oG = oIn + 4 * C * VP;
+    static constexpr size_t oB = oG + 4 * C;
+    static constexpr size_t BYTES = oB + 4 * C;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int C, int DK>
+__global__ __launch_bounds__(NT) void fwd16_carry_kernel(BwdParams p)
+{
+    using L = Fwd16Lay<C, DK>;
+    constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4;
+    using F16 = Frag<__bf16, 16>;
+    using F32 = Frag<__bf16, 32>;
+    static_assert(DK % 32 == 0 && C % 32 == 0, "32-deep fragments over Dk and C");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __bf16 *Kh = reinterpret_cast<__bf16 *>(smem + L::oKh), *Kl = reinterpret_cast<__bf16 *>(smem + L::oKl);
+    __bf16 *Qh = reinterpret_cast<__bf16 *>(smem + L::oQh), *Ql = reinterpret_cast<__bf16 *>(smem + L::oQl);
+    __bf16 *Th = reinterpret_cast<__bf16 *>(smem + L::oTh), *Tl = reinterpret_cast<__bf16 *>(smem + L::oTl);
+    __bf16 *Ph = reinterpret_cast<__bf16 *>(smem + L::oPh), *Pl = reinterpret_cast<__bf16 *>(smem + L::oPl);
+    __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh), *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
+    __bf16 *Xh = reinterpret_cast<__bf16 *>(smem + L::oXh), *Xl = reinterpret_cast<__bf16 *>(smem + L::oXl);
+    __bf16 *Uh = reinterpret_cast<__bf16 *>(smem + L::oUh), *Ul = reinterpret_cast<__bf16 *>(smem + L::oUl);
+    __bf16 *Dh = reinterpret_cast<__bf16 *>(smem + L::oDh), *Dl = reinterpret_cast<__bf16 *>(smem + L::oDl);
+    float *Ins = reinterpret_cast<float *>(smem + L::oIn);
+    float *Gs = reinterpret_cast<float *>(smem + L::oG);
+    float *Bs = reinterpret_cast<float *>(smem + L::oB);
+
+    const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
+    const int64_t NS = p.Dv / BV;
+    int64_t bh, sl;
+    slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
+    const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
+    const int n0 = (int)sl * BV;
+
+    f32x4 S[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        S[m] = zero4();
+        const int ib = wave + 4 * m;
+        if (ib < NKB && p.s0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = p.s0[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln];
+        }
+    }
+
+    RowsTile<float, C, DK> rk, rq;
+    DenseTile<C, C> rt, rp;
+    RowsTile<float, C, BV> ri;
+    float rg = 0.f, rbeta = 0.f;
+    auto fetch = [&](int64_t c) {
+        const int64_t c0 = c * C;
+        const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
+        rk.load(static_cast<const float *>(p.k), b, h, c0, T, p.ks, DK);
+        rq.load(static_cast<const float *>(p.q), b, h, c0, T, p.qs, DK);
+        rt.load(rec + Rec<C>::oT, C);
+        rp.load(rec + Rec<C>::oP, C);
+        ri.load(static_cast<const float *>(p.v), b, h, c0, T, p.vs, Dv, n0);
+        if (threadIdx.x < C) {
+            const int64_t t = c0 + threadIdx.x;
+            rg = rec[Rec<C>::oG + threadIdx.x];
+            rbeta = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
+        }
+    };
+    fetch(0);
+
+    for (int64_t c = 0; c < NC; ++c) {
+        const int64_t c0 = c * C;
+        // ---- stage the chunk as bf16 pairs; prefetch the next
+#pragma unroll
+        for (int it = 0; it < RowsTile<float, C, DK>::NV; ++it) {
+            const int vi = threadIdx.x + NT * it;
+            const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
+            if (RowsTile<float, C, DK>::NU % NT == 0 || vi < RowsTile<float, C, DK>::NU) {
+                store_split4(Kh + r * KP + col, Kl + r * KP + col, rk.v[it]);
+                store_split4(Qh + r * KP + col, Ql + r * KP + col, rq.v[it]);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < DenseTile<C, C>::NV; ++it) {
+            const int vi = threadIdx.x + NT * it;
+            const int r = vi / (C / 4), col = (vi % (C / 4)) * 4;
+            if (DenseTile<C, C>::NU % NT == 0 || vi < DenseTile<C, C>::NU) {
+                store_split4(Th + r * CP + col, Tl + r * CP + col, rt.v[it]);
+                store_split4(Ph + r * CP + col, Pl + r * CP + col, rp.v[it]);
+            }
+        }
+        ri.template store<VP>(Ins);
+        if (threadIdx.x < C) {
+            Gs[threadIdx.x] = rg;
+            Bs[threadIdx.x] = rbeta;
+        }
+        if (c + 1 < NC) fetch(c + 1);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+                const int row = 16 * ib + 4 * lg;
+                store_split4(STh + ln * KP + row, STl + ln * KP + row, S[m]);
+            }
+        }
+        lds_barrier();
+        const float GC = Gs[C - 1];
+
+        // ---- step 1: K S, Q S;  X = diag(beta)(V - e^G K S)
+        f32x4 qsv = zero4();
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 ks = zero4(), ks2 = zero4(), qs2 = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) {
+                const F32 sh = frag_rows<__bf16, 32>(STh, KP, 0, k0, lane);
+                const F32 sl2 = frag_rows<__bf16, 32>(STl, KP, 0, k0, lane);
+                const F32 kh = frag_rows<__bf16, 32>(Kh, KP, 16 * rb, k0, lane);
+                const F32 kl = frag_rows<__bf16, 32>(Kl, KP, 16 * rb, k0, lane);
+                const F32 qh = frag_rows<__bf16, 32>(Qh, KP, 16 * rb, k0, lane);
+                const F32 ql = frag_rows<__bf16, 32>(Ql, KP, 16 * rb, k0, lane);
+                ks = F32::mma(kh, sh, ks);
+                qsv = F32::mma(qh, sh, qsv);
+                ks2 = F32::mma(kh, sl2, ks2);
+                qs2 = F32::mma(qh, sl2, qs2);
+                ks2 = F32::mma(kl, sh, ks2);
+                qs2 = F32::mma(ql, sh, qs2);
+            }
+            ks += ks2;
+            qsv += qs2;
+            const int r0 = 16 * rb + 4 * lg;
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = Bs[r0 + e] * (Ins[(r0 + e) * VP + ln] - __builtin_amdgcn_exp2f(Gs[r0 + e]) * ks[e]);
+            store_split4(Xh + ln * CP + r0, Xl + ln * CP + r0, x);
+        }
+        lds_barrier();
+
+        // ---- step 2: U = T X, kept transposed (for P U) and decayed (for the update)
+        if (wave < NB) {
+            const int rb = wave;
+            const int r0 = 16 * rb + 4 * lg;
+            f32x4 acc = zero4(), acc2 = zero4();
+            for (int kb = 0; kb <= rb; ++kb) {
+                const F16 ah = frag_rows<__bf16, 16>(Th, CP, 16 * rb, 16 * kb, lane);
+                const F16 al = frag_rows<__bf16, 16>(Tl, CP, 16 * rb, 16 * kb, lane);
+                const F16 xh = frag_rows<__bf16, 16>(Xh, CP, 0, 16 * kb, lane);
+                const F16 xl = frag_rows<__bf16, 16>(Xl, CP, 0, 16 * kb, lane);
+                acc = F16::mma(ah, xh, acc);
+                acc2 = F16::mma(ah, xl, acc2);
+                acc2 = F16::mma(al, xh, acc2);
+            }
+            acc += acc2;
+            store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, acc);
+            f32x4 d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(GC - Gs[r0 + e]) * acc[e];
+            store_split4(Dh + ln * CP + r0, Dl + ln * CP + r0, d);
+        }
+        lds_barrier();
+
+        // ---- step 3: Y = diag(e^G) Q S + P U;  S <- e^{G_C} S + K^T (d o U)
+        if (wave < NB) {
+            const int rb = wave;
+            f32x4 acc, acc2 = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_exp2f(Gs[16 * rb + 4 * lg + e]) * qsv[e];
+            for (int jb = 0; jb <= rb; ++jb) {
+                const F16 ah = frag_rows<__bf16, 16>(Ph, CP, 16 * rb, 16 * jb, lane);
+                const F16 al = frag_rows<__bf16, 16>(Pl, CP, 16 * rb, 16 * jb, lane);
+                const F16 uh = frag_rows<__bf16, 16>(Uh, CP, 0, 16 * jb, lane);
+                const F16 ul = frag_rows<__bf16, 16>(Ul, CP, 0, 16 * jb, lane);
+                acc = F16::mma(ah, uh, acc);
+                acc2 = F16::mma(ah, ul, acc2);
+                acc2 = F16::mma(al, uh, acc2);
+            }
+            acc += acc2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t t = c0 + 16 * rb + 4 * lg + e;
+                if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e];
+            }
+        }
+        const float eGC = __builtin_amdgcn_exp2f(GC);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+                f32x4 acc = S[m] * eGC, acc2 = zero4();
+#pragma unroll
+                for (int j0 = 0; j0 < C; j0 += 32) {
+                    const F32 kh = tr_frag32(Kh, KP, 16 * ib, j0, lane);
+                    const F32 kl = tr_frag32(Kl, KP, 16 * ib, j0, lane);
+                    const F32 dh = pair_rows32(Dh, CP, 0, j0, lane);
+                    const F32 dl = pair_rows32(Dl, CP, 0, j0, lane);
+                    acc = F32::mma(kh, dh, acc);
+                    acc2 = F32::mma(kh, dl, acc2);
+                    acc2 = F32::mma(kl, dh, acc2);
+                }
+                S[m] = acc + acc2;
+            }
+        }
+        lds_barrier();
+    }
+
+    if (p.sT) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int ib = wave + 4 * m;
+            if (ib < NKB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p.sT[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
@@ -1991,7 +2219,10 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
     const int64_t bh = a.B * a.H;
     const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
     hipLaunchKernelGGL((bwd_prep_kernel<float, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
-    hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
+    if constexpr (DK % 32 == 0 && C % 32 == 0)
+        hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
+    else
+        hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
     return hipGetLastError();
 }
 
