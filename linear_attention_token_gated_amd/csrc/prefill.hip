@@ -36,9 +36,9 @@ namespace {
 
 constexpr int NTHREADS = 256;   // 4 wavefronts
 
-template <typename OpT, int C, int DK> struct Lay {
-    static constexpr bool SPLIT = sizeof(OpT) == 2;   // bf16 hi/lo state operand
-    static constexpr int PAD = sizeof(OpT) == 2 ? 8 : 4;
+template <int C, int DK> struct Lay {
+    using OpT = float;
+    static constexpr int PAD = 4;
     static constexpr int KP = DK + PAD;     // pitch of K, Q, S^T rows
     static constexpr int CP = C + PAD;      // pitch of C-wide operand rows
     static constexpr int TP = 16 + PAD;     // pitch of diagonal-inverse rows
@@ -52,18 +52,14 @@ template <typename OpT, int C, int DK> struct Lay {
     static constexpr size_t oK = 0;
     static constexpr size_t oQ = oK + align16(sizeof(OpT) * C * KP);
     static constexpr size_t oST = oQ + align16(sizeof(OpT) * C * KP);
-    static constexpr size_t oSTlo = oST + align16(sizeof(OpT) * BV * KP);
-    static constexpr size_t oAf = oSTlo + (SPLIT ? align16(sizeof(OpT) * BV * KP) : 0);
+    static constexpr size_t oAf = oST + align16(sizeof(OpT) * BV * KP);
     static constexpr size_t oAn = oAf + align16(4 * C * AFP);
     static constexpr size_t oP = oAn + align16(sizeof(OpT) * C * CP);
-    static constexpr size_t oPlo = oP + align16(sizeof(OpT) * C * CP);
-    static constexpr size_t oTd = oPlo + (SPLIT ? align16(sizeof(OpT) * C * CP) : 0);
+    static constexpr size_t oTd = oP + align16(sizeof(OpT) * C * CP);
     static constexpr size_t oRf = oTd + align16(sizeof(OpT) * C * TP);
     static constexpr size_t oUT = oRf + align16(4 * C * BV);
-    static constexpr size_t oUTlo = oUT + align16(sizeof(OpT) * BV * CP);
-    static constexpr size_t oUdT = oUTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
-    static constexpr size_t oUdTlo = oUdT + align16(sizeof(OpT) * BV * CP);
-    static constexpr size_t oV = oUdTlo + (SPLIT ? align16(sizeof(OpT) * BV * CP) : 0);
+    static constexpr size_t oUdT = oUT + align16(sizeof(OpT) * BV * CP);
+    static constexpr size_t oV = oUdT + align16(sizeof(OpT) * BV * CP);
     static constexpr size_t oBe = oV + align16(4 * C * BV);
     static constexpr size_t oG = oBe + align16(4 * C);
     static constexpr size_t oEG = oG + align16(4 * C);
@@ -84,9 +80,8 @@ struct KParams {
 template <typename Tin, int C, int DK>
 __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
 {
-    using OpT = Tin;
-    using L = Lay<OpT, C, DK>;
-    constexpr bool SPLIT = L::SPLIT;
+    using OpT = float;
+    using L = Lay<C, DK>;
     constexpr int KP = L::KP, CP = L::CP, TP = L::TP, AFP = L::AFP, NB = L::NB, NSB = L::NSB,
                   MS = L::MS, KS_DK = L::KS_DK, KS_C = L::KS_C;
     using FragDK = Frag<OpT, KS_DK>;
@@ -97,17 +92,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
     OpT *Ks = reinterpret_cast<OpT *>(smem + L::oK);
     OpT *Qs = reinterpret_cast<OpT *>(smem + L::oQ);
     OpT *STs = reinterpret_cast<OpT *>(smem + L::oST);
-    OpT *STlo = reinterpret_cast<OpT *>(smem + L::oSTlo);
     float *Af = reinterpret_cast<float *>(smem + L::oAf);
     OpT *An = reinterpret_cast<OpT *>(smem + L::oAn);
     OpT *Ps = reinterpret_cast<OpT *>(smem + L::oP);
-    OpT *Plo = reinterpret_cast<OpT *>(smem + L::oPlo);
     OpT *Td = reinterpret_cast<OpT *>(smem + L::oTd);
     float *Rf = reinterpret_cast<float *>(smem + L::oRf);
     OpT *UT = reinterpret_cast<OpT *>(smem + L::oUT);
-    OpT *UTlo = reinterpret_cast<OpT *>(smem + L::oUTlo);
     OpT *UdT = reinterpret_cast<OpT *>(smem + L::oUdT);
-    OpT *UdTlo = reinterpret_cast<OpT *>(smem + L::oUdTlo);
     float *Vs = reinterpret_cast<float *>(smem + L::oV);
     float *Be = reinterpret_cast<float *>(smem + L::oBe);
     float *Gs = reinterpret_cast<float *>(smem + L::oG);
@@ -154,11 +145,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
             const int ib = wave + 4 * m;
             if (ib < NSB) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const OpT hi = from_f32<OpT>(S[m][e]);
-                    STs[ln * KP + 16 * ib + 4 * lg + e] = hi;
-                    if constexpr (L::SPLIT) STlo[ln * KP + 16 * ib + 4 * lg + e] = from_f32<OpT>(S[m][e] - to_f32(hi));
-                }
+                for (int e = 0; e < 4; ++e) STs[ln * KP + 16 * ib + 4 * lg + e] = S[m][e];
             }
         }
     };
@@ -267,14 +254,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
                     const int r = 16 * rb + 4 * lg + e;
                     const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gj, 0.f));
                     if (isQ) {
-                        const float pvv = r >= j ? gam * acc[e] : 0.f;
-                        const OpT hi = from_f32<OpT>(pvv);
-                        Ps[r * CP + j] = hi;
-                        if constexpr (SPLIT) Plo[r * CP + j] = from_f32<OpT>(pvv - to_f32(hi));
+                        Ps[r * CP + j] = r >= j ? gam * acc[e] : 0.f;
                     } else {
                         const float val = r > j ? Be[r] * gam * acc[e] : 0.f;
                         if (rb == cb) Af[r * AFP + j] = val;
-                        else An[r * CP + j] = from_f32<OpT>(-val);
+                        else An[r * CP + j] = -val;
                     }
                 }
             }
@@ -292,11 +276,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
                 const FragDK sf = frag_rows<OpT, KS_DK>(STs, KP, 0, k0, lane);
                 ks_acc = FragDK::mma(kf, sf, ks_acc);
                 qs_acc = FragDK::mma(qf, sf, qs_acc);
-                if constexpr (L::SPLIT) {
-                    const FragDK sl2 = frag_rows<OpT, KS_DK>(STlo, KP, 0, k0, lane);
-                    ks_acc = FragDK::mma(kf, sl2, ks_acc);
-                    qs_acc = FragDK::mma(qf, sl2, qs_acc);
-                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -317,14 +296,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
             for (int i = 0; i < 4; ++i) X[i] = (ln == lg + 4 * i) ? 1.f : 0.f;
             tri_solve16(X, Lr, ln, std::make_integer_sequence<int, 15>{});
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Td[(16 * blk + ln) * TP + lg + 4 * i] = from_f32<OpT>(X[i]);
+            for (int i = 0; i < 4; ++i) Td[(16 * blk + ln) * TP + lg + 4 * i] = X[i];
         }
         __syncthreads();
 
         // ---------------- 4b. block forward substitution for U (wavefront 0) ----
         if (wave == 0) {
             // U blocks as B operands (accumulator layout == B layout for KS=16)
-            Frag16 Uh[NB], Ul[NB];
+            Frag16 Uf[NB];
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 f32x4 z;
@@ -333,34 +312,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
 #pragma unroll
                 for (int kb = 0; kb < i; ++kb) {
                     const Frag16 a = frag_rows<OpT, 16>(An, CP, 16 * i, 16 * kb, lane);
-                    z = Frag16::mma(a, Uh[kb], z);
-                    if constexpr (SPLIT) z = Frag16::mma(a, Ul[kb], z);
+                    z = Frag16::mma(a, Uf[kb], z);
                 }
-                Frag16 zh, zl;
+                Frag16 zf;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const OpT hi = from_f32<OpT>(z[e]);
-                    zh.set_raw(e, hi);
-                    if constexpr (SPLIT) zl.set(e, z[e] - to_f32(hi));
-                }
+                for (int e = 0; e < 4; ++e) zf.set_raw(e, z[e]);
                 const Frag16 ti = frag_rows<OpT, 16>(Td, TP, 16 * i, 0, lane);
-                f32x4 u = Frag16::mma(ti, zh, zero4());
-                if constexpr (SPLIT) u = Frag16::mma(ti, zl, u);
+                const f32x4 u = Frag16::mma(ti, zf, zero4());
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * i + 4 * lg + e;
-                    const OpT hi = from_f32<OpT>(u[e]);
-                    Uh[i].set_raw(e, hi);
-                    UT[ln * CP + r] = hi;
-                    const float ud = __builtin_amdgcn_exp2f(GC - Gs[r]) * u[e];
-                    const OpT dhi = from_f32<OpT>(ud);
-                    UdT[ln * CP + r] = dhi;
-                    if constexpr (SPLIT) {
-                        const OpT lo = from_f32<OpT>(u[e] - to_f32(hi));
-                        Ul[i].set_raw(e, lo);
-                        UTlo[ln * CP + r] = lo;
-                        UdTlo[ln * CP + r] = from_f32<OpT>(ud - to_f32(dhi));
-                    }
+                    Uf[i].set_raw(e, u[e]);
+                    UT[ln * CP + r] = u[e];
+                    UdT[ln * CP + r] = __builtin_amdgcn_exp2f(GC - Gs[r]) * u[e];
                 }
             }
         }
@@ -376,12 +340,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
                 const Frag16 a = frag_rows<OpT, 16>(Ps, CP, 16 * rb, 16 * jb, lane);
                 const Frag16 u = frag_rows<OpT, 16>(UT, CP, 0, 16 * jb, lane);
                 acc = Frag16::mma(a, u, acc);
-                if constexpr (SPLIT) {
-                    const Frag16 alo = frag_rows<OpT, 16>(Plo, CP, 16 * rb, 16 * jb, lane);
-                    const Frag16 ulo = frag_rows<OpT, 16>(UTlo, CP, 0, 16 * jb, lane);
-                    acc = Frag16::mma(alo, u, acc);
-                    acc = Frag16::mma(a, ulo, acc);
-                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -402,10 +360,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gdn_prefill_kernel(KParams p)
                     const FragC a = frag_cols<OpT, KS_C>(Ks, KP, 16 * ib, j0, lane);
                     const FragC u = frag_rows<OpT, KS_C>(UdT, CP, 0, j0, lane);
                     acc = FragC::mma(a, u, acc);
-                    if constexpr (SPLIT) {
-                        const FragC ulo = frag_rows<OpT, KS_C>(UdTlo, CP, 0, j0, lane);
-                        acc = FragC::mma(a, ulo, acc);
-                    }
                 }
                 S[m] = acc;
             }
