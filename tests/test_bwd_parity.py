@@ -110,3 +110,19 @@ def test_bwd_4k_bf16_sampled_heads(oracle_mod):
             e = rel_err(x, ref[r])
             print(f"  b={b} h={h} {n}={e:.2e}", flush=True)
             assert e <= TOL_F32, (b, h, n, e)
+
+
+@pytest.mark.parametrize("regime", ["strong_decay", "beta_near_one", "beta_near_zero"])
+def test_bwd_extreme_gates(oracle_mod, regime):
+    """Strong decay (alpha down to 1e-3, so e^G underflows inside a 64-token
+    chunk), write strength close to 1 (I + A far from identity) or close to 0."""
+    print(f"case: bwd extreme gates {regime}", flush=True)
+    inp = wl.bwd_inputs(1, 200, 2, 64, 64, dtype="f32", s0_std=0.3, seed=21, dst_std=1.0)
+    rng = np.random.default_rng(22)
+    if regime == "strong_decay":
+        inp["alpha"] = rng.uniform(1e-3, 0.5, inp["alpha"].shape).astype(np.float32)
+    elif regime == "beta_near_one":
+        inp["beta"] = rng.uniform(0.95, 1.0, inp["beta"].shape).astype(np.float32)
+    else:
+        inp["beta"] = rng.uniform(0.0, 1e-3, inp["beta"].shape).astype(np.float32)
+    _check(oracle_mod, inp, 64)
