@@ -225,7 +225,6 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
 {
     using L = RecLay<C, DK>;
     using Rec = PrepRecord<C>;
-    using F16 = Frag<__bf16, 16>;
     using FDK = Frag<__bf16, L::KS_DK>;
     using FC = Frag<__bf16, L::KS_C>;
     constexpr int KPS = L::KPS, CPU = L::CPU, CPD = L::CPD, NB = L::NB, NSB = L::NSB, MS = L::MS;
