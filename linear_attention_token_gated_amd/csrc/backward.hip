@@ -165,18 +165,6 @@ __device__ __forceinline__ float row16_total(float x) {
     return x;
 }
 
-// Workgroup barrier that orders LDS only: this wave's LDS accesses complete
-// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it carries no memory
-// fence, so global loads in flight (prefetch) and global stores (outputs) are
-// not waited for; every value these kernels pass between wavefronts goes
-// through LDS.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt and expcnt at their maximum, lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // ===========================================================================
 // 1. prep: G2, T = (I + A)^-1, P, Ak of one chunk
 // ===========================================================================

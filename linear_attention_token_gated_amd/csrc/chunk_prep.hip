@@ -166,9 +166,11 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
             if (lane < C) Ebs[rb * C + lane] = lane < 16 * rb ? __builtin_amdgcn_exp2f(gref - g2) : 0.f;
         }
     }
-    // the next item's rows (the registers of this one are consumed)
+    // the next item's rows (the registers of this one are consumed); the
+    // barriers below order LDS only, so these loads stay in flight until the
+    // next item stores them
     if (i + stride < mine) fetch(i + stride);
-    __syncthreads();
+    lds_barrier();
 
     // ---- 2. Gram blocks: A (NTRI blocks, fp32 into LDS) and P (NTRI blocks, bf16
     //         hi/lo fragments into the record).  Each is computed transposed, D =
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     case 2: gram_wave(std::integral_constant<int, 2>{}); break;
     default: gram_wave(std::integral_constant<int, 3>{}); break;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. diagonal blocks T_ii = (I + A_ii)^-1; lane (ln, lg) carries row ln,
     //         columns 4 lg + e
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         fsub16(X, Lr, std::make_integer_sequence<int, 15>{});
         *reinterpret_cast<f32x4 *>(Ts + (ii * 16 + ln) * AP + 4 * lg) = f32x4{X[0], X[1], X[2], X[3]};
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4. blocks below the diagonal, one distance d = i - k per level; wave i
     //         owns row block i.  M = sum_m A_im T_mk, then T_ik = -T_ii M.  The MFMA
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[(4 * lg + e) * AP + ln] = -tik[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- 5. T' = T diag(beta) as bf16 hi/lo fragments: lane (ln, lg) holds
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         tf[64 + lane] = lv;
     }
     // T reuses the K/Q rows: the next item's rows go there after this barrier
-    __syncthreads();
+    lds_barrier();
     }
 }
 

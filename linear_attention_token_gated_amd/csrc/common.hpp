@@ -201,4 +201,16 @@ __device__ __forceinline__ void tri_solve16(float (&X)[4], const float (&Lr)[16]
     (tri_step<S>(X, Lr, r), ...);
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it carries no memory
+// fence, so global loads in flight (prefetch) and global stores (outputs) are
+// not waited for; for kernels whose wavefronts pass values to each other only
+// through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt and expcnt at their maximum, lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace gdn
