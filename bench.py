@@ -373,7 +373,7 @@ def main():
                  "tokens_per_s": l_cfg.B * l_cfg.T / (l_ms * 1e-3),
                  "gemm_tflops_alg": gemm_f / 1e12, "core_tflops_alg": core_f / 1e12,
                  "tflops_achieved": (gemm_f + core_f) / (l_ms * 1e-3) / 1e12,
-                 "note": "core runs on fp32 q/k/v (fp32 MFMA); projections bf16 MFMA"}
+                 "note": "core runs on fp32 q/k/v (two kernels, bf16 MFMA with hi/lo operands); projections on hipBLASLt, bf16 operands, fp32 accumulation"}
 
     ld_cfg, ld_total, ld_per = bench_layer_decode(args, torch, gdn, wl)
     ld_ms = float(np.mean(ld_per))

@@ -3,8 +3,8 @@
     python -m linear_attention_token_gated_amd.build
 
 Every HIP translation unit is compiled in parallel, then linked into
-``linear_attention_token_gated_amd/libgdn.so`` with only the ``gdn_*`` C ABI
-symbols exported.
+``linear_attention_token_gated_amd/libgdn.so`` (with hipBLASLt for the layer's
+plain projections) with only the ``gdn_*`` C ABI symbols exported.
 """
 from __future__ import annotations
 
@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "chunk_prep.hip", "recurrence.hip", "layer.hip", "backward.hip"]
+SOURCES = ["api.cpp", "blas.cpp", "decode.hip", "prefill.hip", "chunk_prep.hip", "recurrence.hip", "layer.hip",
+           "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -48,7 +49,8 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

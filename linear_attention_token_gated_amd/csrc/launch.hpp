@@ -77,6 +77,12 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
 size_t prefill_f32_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t C);
 hipError_t launch_prefill_f32_staged(const PrefillArgs &a, hipStream_t stream);
 
+// C[M, N] = A[M, K] B[N, K]^T (row-major, bf16 operands, fp32 accumulation,
+// fp32 or bf16 C) through hipBLASLt (blas.cpp); hipErrorNotSupported when the
+// library has no algorithm for the shape
+hipError_t blas_gemm_nt(const void *A, const void *B, void *C, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream);
+
 // Layer helpers (layer.hip)
 struct LayerArgs {
     const void *x;

@@ -7,13 +7,16 @@
 // zero-centred RMSNorm.
 //
 // Steps (M = B*T tokens):
-//   1. gemm_nt: qkv_pre = x W_qkv^T (fp32), z = x W_gate^T (bf16), ab = x W_ab^T (fp32)
+//   1. projections: qkv_pre = x W_qkv^T (fp32), z = x W_gate^T (bf16), ab = x W_ab^T (fp32)
 //   2. prologue: depthwise causal conv over the q|k|v channels, L2 norm of
 //      every q and k head, alpha (eq (10)) and beta (eq (9)) per (token, head);
 //      q, k, v stay fp32
 //   3. the chunked core (prefill kernel, fp32 operands) reading q, k, v in place
 //   4. epilogue: g = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + gamma) (bf16)
-//   5. gemm_nt: out = g W_o^T (fp32)
+//   5. projection: out = g W_o^T (fp32)
+//
+// The projections are plain products: they go to hipBLASLt (blas.cpp), and to
+// this file's gemm_nt_kernel only for a shape the library has no algorithm for.
 //
 // Why q, k, v are not rounded to bf16 here: with unit-norm q and k in Dk
 // dimensions, y_t = S_t^T q_t is a small projection of the state (|q.k| ~
@@ -152,6 +155,16 @@ hipError_t gemm_nt(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_
     dim3 grid((unsigned)((N + GBN - 1) / GBN), (unsigned)((M + GBM - 1) / GBM));
     hipLaunchKernelGGL((gemm_nt_kernel<OutT>), grid, dim3(256), 0, s, A, Bm, C, (int)M, (int)N, (int)K, lda, ldb, ldc);
     return hipGetLastError();
+}
+
+// C[M, N] = A[M, K] B[N, K]^T: hipBLASLt, else gemm_nt_kernel
+template <typename OutT>
+hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                   int64_t ldb, int64_t ldc, hipStream_t s)
+{
+    const hipError_t e = blas_gemm_nt(A, Bm, C, std::is_same<OutT, __bf16>::value, M, N, K, lda, ldb, ldc, s);
+    if (e != hipErrorNotSupported) return e;
+    return gemm_nt<OutT>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
@@ -473,9 +486,9 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
-    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_qkv, pre, M, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
-    if ((e = gemm_nt<__bf16>(x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv, s))) return e;
-    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_ab, ab, M, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
+    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, M, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
+    if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv, s))) return e;
+    if ((e = project<float>(x, (const __bf16 *)a.W_ab, ab, M, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
 
     switch (Dk) {
     case 16: e = launch_prologue_dk<16>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
@@ -503,7 +516,7 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e) return e;
-    return gemm_nt<float>(g, (const __bf16 *)a.W_o, a.out, M, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+    return project<float>(g, (const __bf16 *)a.W_o, a.out, M, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
 }
 
 hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
@@ -524,10 +537,10 @@ hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
-    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
-    if ((e = gemm_nt<__bf16>(x, (const __bf16 *)a.W_gate, z, N, H * Dv, hidden, hidden, hidden, H * Dv, s)))
+    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
+    if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, N, H * Dv, hidden, hidden, hidden, H * Dv, s)))
         return e;
-    if ((e = gemm_nt<float>(x, (const __bf16 *)a.W_ab, ab, N, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
+    if ((e = project<float>(x, (const __bf16 *)a.W_ab, ab, N, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
 
     const __bf16 *cw = (const __bf16 *)a.conv_w;
     switch (Dk) {
@@ -554,7 +567,7 @@ hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e) return e;
-    return gemm_nt<float>(g, (const __bf16 *)a.W_o, a.out, N, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+    return project<float>(g, (const __bf16 *)a.W_o, a.out, N, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
 }
 
 }  // namespace gdn
