@@ -24,6 +24,8 @@
 // rounding) becomes several percent of max|err|/RMS in y and in the layer
 // output.  The inputs x and the weights are bf16 and the products accumulate in
 // fp32, so the projections themselves are exact up to fp32 summation.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -157,13 +159,18 @@ hipError_t gemm_nt(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_
     return hipGetLastError();
 }
 
-// C[M, N] = A[M, K] B[N, K]^T: hipBLASLt, else gemm_nt_kernel
+// C[M, N] = A[M, K] B[N, K]^T: hipBLASLt, else gemm_nt_kernel.  GDN_OWN_GEMM=1
+// in the environment selects gemm_nt_kernel for every shape (so that it stays
+// tested against the library's results).
 template <typename OutT>
 hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                    int64_t ldb, int64_t ldc, hipStream_t s)
 {
-    const hipError_t e = blas_gemm_nt(A, Bm, C, std::is_same<OutT, __bf16>::value, M, N, K, lda, ldb, ldc, s);
-    if (e != hipErrorNotSupported) return e;
+    const char *own = getenv("GDN_OWN_GEMM");
+    if (!(own && own[0] == '1')) {
+        const hipError_t e = blas_gemm_nt(A, Bm, C, std::is_same<OutT, __bf16>::value, M, N, K, lda, ldb, ldc, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     return gemm_nt<OutT>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
 }
 

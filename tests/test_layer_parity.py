@@ -75,3 +75,21 @@ def test_layer_full_config(oracle_mod):
     inp = wl.layer_config_inputs(cfg)
     eo, eS, _ = _run(oracle_mod, inp, cfg.B, cfg.T, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
     assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_layer_own_gemm_matches_library(oracle_mod, monkeypatch):
+    """The layer with the projections on this library's gemm_nt_kernel
+    (GDN_OWN_GEMM=1) against the same layer on hipBLASLt and the oracle."""
+    B, T, hidden, H, Dk, Dv, chunk = 1, 200, 256, 2, 64, 64, 64
+    print("case: layer own GEMM vs hipBLASLt", flush=True)
+    inp = wl.layer_inputs(B, T, hidden, H, Dk, Dv, conv_k=4, w_std=0.05, seed=31,
+                          gamma_std=0.1, A_val=0.3, b_alpha_val=-0.5)
+    monkeypatch.delenv("GDN_OWN_GEMM", raising=False)
+    eo1, eS1, o1 = _run(oracle_mod, inp, B, T, hidden, H, Dk, Dv, chunk)
+    monkeypatch.setenv("GDN_OWN_GEMM", "1")
+    eo2, eS2, o2 = _run(oracle_mod, inp, B, T, hidden, H, Dk, Dv, chunk)
+    d = rel_err(o2, o1)
+    print(f"  own vs library: {d:.3e}", flush=True)
+    assert max(eo1, eS1, eo2, eS2) <= TOL_BF16
+    # both accumulate the bf16 products in fp32 over k in order; they may agree bit for bit
+    assert d <= 1e-3
