@@ -228,6 +228,10 @@ GDN_API gdn_status gdn_decode_verify(const void *q, const void *k, const void *v
  * out[t,c] = sum_j conv_w[c,j] * in[t-(conv_k-1)+j, c] (zero history, no bias,
  * no activation).  RMSNorm runs per (token, head) over Dv.
  *
+ * The four projections are plain products on hipBLASLt (bf16 operands, fp32
+ * accumulation); this library's own GEMM kernel serves a shape the library
+ * has no algorithm for, or every shape with GDN_OWN_GEMM=1 in the environment.
+ *
  *   x     [B, T, hidden] bf16;  out [B, T, hidden] float32
  *   initial_state / final_state as in gdn_prefill_fwd (NULL allowed).
  *   hidden % 64 == 0; conv_k in [1, 4]; Dk, Dv, chunk as in gdn_prefill_fwd.
