@@ -165,23 +165,44 @@ __device__ __forceinline__ float row16_total(float x) {
     return x;
 }
 
+// four fp32 values as bf16 pairs hi (at hi) + lo (at lo)
+__device__ __forceinline__ void store_split4(__bf16 *hi, __bf16 *lo, const f32x4 x) {
+    bf16x4 h, l;
+    split4(x, h, l);
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+
 // ===========================================================================
 // 1. prep: G2, T = (I + A)^-1, P, Ak of one chunk
 // ===========================================================================
 template <typename Tin, int C, int DK>
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 {
-    // K and Q stay in the input type: bf16 inputs run the Gram on bf16 MFMA
-    // (exact products, fp32 sums), fp32 inputs on fp32 MFMA
-    constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
-    constexpr int KP = DK + PAD, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
+    // The Gram runs on bf16 MFMA with fp32 sums: bf16 inputs are exact
+    // operands; fp32 inputs are split into bf16 pairs hi + lo (hi = bf16(x),
+    // lo = bf16(x - hi)) and each product sums hi*hi + hi*lo + lo*hi.
+    constexpr bool F32IN = sizeof(Tin) == 4;
+    constexpr int NPART = F32IN ? 2 : 1;                 // bf16 parts per K or Q element
+    constexpr int KP = DK + 8, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
     constexpr int NTRI = NB * (NB + 1) / 2;
-    using FG = Frag<Tin, KSD>;
-    __shared__ __attribute__((aligned(16))) Tin Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) Tin Qs[C * KP];
-    __shared__ __attribute__((aligned(16))) float As[C * CP];
-    __shared__ __attribute__((aligned(16))) float Ts[C * CP];
-    __shared__ float Gs[C], Bs[C];
+    using FG = Frag<__bf16, KSD>;
+    // LDS: K parts, then a region holding the Q parts until the P tiles are
+    // done; for fp32 inputs A and T reuse it afterwards (two workgroups per CU)
+    constexpr size_t KQB = (size_t)2 * C * KP;           // one bf16 C x Dk part
+    constexpr size_t ATB = (size_t)4 * C * CP;           // one fp32 C x C matrix
+    constexpr size_t oQ = NPART * KQB;
+    constexpr size_t QREG = F32IN ? (NPART * KQB > 2 * ATB ? NPART * KQB : 2 * ATB) : NPART * KQB;
+    constexpr size_t oA = F32IN ? oQ : oQ + QREG, oT = oA + ATB;
+    constexpr size_t oG = F32IN ? oQ + QREG : oT + ATB, BYTES = oG + 8 * C;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) char smem[BYTES];
+    __bf16 *Ks = reinterpret_cast<__bf16 *>(smem);                 // part j at Ks + j * C * KP
+    __bf16 *Qs = reinterpret_cast<__bf16 *>(smem + oQ);
+    float *As = reinterpret_cast<float *>(smem + oA);
+    float *Ts = reinterpret_cast<float *>(smem + oT);
+    float *Gs = reinterpret_cast<float *>(smem + oG);
+    float *Bs = Gs + C;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
     const int64_t bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
@@ -189,7 +210,6 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
 
     {
-        using R = Raw4<Tin>;
         RowsTile<Tin, C, DK> tk, tq;
         tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, p.ks, DK);
         tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, p.qs, DK);
@@ -198,8 +218,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             const int vi = tid + NT * it;
             const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
             if (RowsTile<Tin, C, DK>::NU % NT == 0 || vi < RowsTile<Tin, C, DK>::NU) {
-                *reinterpret_cast<typename R::type *>(Ks + r * KP + col) = tk.v[it];
-                *reinterpret_cast<typename R::type *>(Qs + r * KP + col) = tq.v[it];
+                if constexpr (F32IN) {
+                    store_split4(Ks + r * KP + col, Ks + C * KP + r * KP + col, tk.v[it]);
+                    store_split4(Qs + r * KP + col, Qs + C * KP + r * KP + col, tq.v[it]);
+                } else {
+                    *reinterpret_cast<bf16x4 *>(Ks + r * KP + col) = tk.v[it];
+                    *reinterpret_cast<bf16x4 *>(Qs + r * KP + col) = tq.v[it];
+                }
             }
         }
     }
@@ -214,40 +239,62 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             rec[Rec<C>::oG + lane] = G2;
         }
     }
-    // blocks above the diagonal: zero in the record and in T
+    // blocks above the diagonal: zero in the record
     for (int i = tid; i < C * C; i += NT) {
         const int r = i / C, j = i % C;
         if (j / 16 > r / 16) {
             rec[Rec<C>::oP + i] = 0.f;
             rec[Rec<C>::oA + i] = 0.f;
-            Ts[r * CP + j] = 0.f;
         }
     }
     __syncthreads();
 
-    // Gram tiles on and below the diagonal: K K^T -> Ak, A;  Q K^T -> P
-    for (int tile = wave; tile < 2 * NTRI; tile += 4) {
-        const bool isQ = tile >= NTRI;
-        int rb, cb;
-        tri_block(isQ ? tile - NTRI : tile, rb, cb);
-        const Tin *src = isQ ? Qs : Ks;
-        f32x4 acc = zero4();
+    // one Gram tile D = X_rb K_cb^T (X = Q or K) on and below the diagonal
+    auto gram = [&](const __bf16 *Xs, int rb, int cb) {
+        f32x4 acc = zero4(), acc2 = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += KSD)
-            acc = FG::mma(frag_rows<Tin, KSD>(src, KP, 16 * rb, k0, lane),
-                          frag_rows<Tin, KSD>(Ks, KP, 16 * cb, k0, lane), acc);
+        for (int k0 = 0; k0 < DK; k0 += KSD) {
+            const FG xh = frag_rows<__bf16, KSD>(Xs, KP, 16 * rb, k0, lane);
+            const FG kh = frag_rows<__bf16, KSD>(Ks, KP, 16 * cb, k0, lane);
+            acc = FG::mma(xh, kh, acc);
+            if constexpr (F32IN) {
+                acc2 = FG::mma(xh, frag_rows<__bf16, KSD>(Ks + C * KP, KP, 16 * cb, k0, lane), acc2);
+                acc2 = FG::mma(frag_rows<__bf16, KSD>(Xs + C * KP, KP, 16 * rb, k0, lane), kh, acc2);
+            }
+        }
+        return acc + acc2;
+    };
+    // Q K^T -> P (the last use of Q)
+    for (int tile = wave; tile < NTRI; tile += 4) {
+        int rb, cb;
+        tri_block(tile, rb, cb);
+        const f32x4 acc = gram(Qs, rb, cb);
         const int j = 16 * cb + ln;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * lg + e;
             const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gs[j], 0.f));
-            if (isQ) {
-                rec[Rec<C>::oP + r * C + j] = r >= j ? gam * acc[e] : 0.f;
-            } else {
-                const float ak = r > j ? gam * acc[e] : 0.f;
-                rec[Rec<C>::oA + r * C + j] = ak;
-                As[r * CP + j] = Bs[r] * ak;
-            }
+            rec[Rec<C>::oP + r * C + j] = r >= j ? gam * acc[e] : 0.f;
+        }
+    }
+    if constexpr (F32IN) __syncthreads();        // A and T replace Q
+    for (int i = tid; i < C * C; i += NT) {
+        const int r = i / C, j = i % C;
+        if (j / 16 > r / 16) Ts[r * CP + j] = 0.f;
+    }
+    // K K^T -> Ak (record), A = diag(beta) Ak (LDS)
+    for (int tile = wave; tile < NTRI; tile += 4) {
+        int rb, cb;
+        tri_block(tile, rb, cb);
+        const f32x4 acc = gram(Ks, rb, cb);
+        const int j = 16 * cb + ln;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * lg + e;
+            const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gs[j], 0.f));
+            const float ak = r > j ? gam * acc[e] : 0.f;
+            rec[Rec<C>::oA + r * C + j] = ak;
+            As[r * CP + j] = Bs[r] * ak;
         }
     }
     __syncthreads();
@@ -570,13 +617,6 @@ __device__ __forceinline__ Frag<__bf16, 32> pair_rows32(const __bf16 *Bt, int P,
     Frag<__bf16, 32> f;
     f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return f;
-}
-
-__device__ __forceinline__ void store_split4(__bf16 *hi, __bf16 *lo, const f32x4 x) {
-    bf16x4 h, l;
-    split4(x, h, l);
-    *reinterpret_cast<bf16x4 *>(hi) = h;
-    *reinterpret_cast<bf16x4 *>(lo) = l;
 }
 
 template <int C, int DK, bool ADJ> struct Carry16Lay {
