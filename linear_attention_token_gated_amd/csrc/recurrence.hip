@@ -313,6 +313,10 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 const __bf16 *Vs = reinterpret_cast<const __bf16 *>(cb + L::cV);
                 const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * rb + 4 * lg);
+                // V[16 rb + 4 lg + e][ln], e = 0..3, in one transposing read issued
+                // ahead of the products (lane j of the group points at row j/4,
+                // columns 4 (j%4)..+3)
+                const bf16x4 vv = read_tr16(Vs + (16 * rb + 4 * lg + (ln >> 2)) * BV + 4 * (ln & 3));
                 // software-pipelined: the fragments of k-step kk + 2 are read while
                 // the MFMAs of step kk run (the scheduling barriers keep that order)
                 FDK kf[NK], qf[NK], sh[NK], slo[NK];
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 f32x4 rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    rv[e] = (float)Vs[(16 * rb + 4 * lg + e) * BV + ln] - eg[e] * (ks_h[e] + ks_l[e]);
+                    rv[e] = (float)vv[e] - eg[e] * (ks_h[e] + ks_l[e]);
                 bf16x4 hv, lv;
                 split4(rv, hv, lv);
                 Rh[rb * 64 + lane] = hv;
@@ -347,7 +351,19 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             }
             __syncthreads();
 
-            // ---- phase 2: U_rb = sum_{k <= rb} T'_rb,k R_k
+            // ---- phase 2: U_rb = sum_{k <= rb} T'_rb,k R_k.  The K^T operands of
+            // the phase-3 update are read first: K of the chunk is unchanged
+            // since the iteration began, so their latency overlaps this phase.
+            constexpr int NJ = C / KS_C;
+            FC ka[MS][NJ];
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = rb + 4 * m;
+                if (ib < NSB) {
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = k_cols_tr<KS_C, DK>(Ks, 16 * ib, jj * KS_C, lane);
+                }
+            }
             if constexpr (has_rb) {
                 f32x4 u = zero4(), u2 = zero4();
                 const int r0 = 16 * rb + 4 * lg;
@@ -378,21 +394,12 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
 
             // ---- phase 3: S <- EGC S + K^T (diag(Ed) U)
             {
-                constexpr int NJ = C / KS_C;
                 const float egc = dec[2 * C];
-                FC uh[NJ], ul[NJ], ka[MS][NJ];
+                FC uh[NJ], ul[NJ];
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) {
                     uh[jj] = frag_rows<__bf16, KS_C>(UdTh, CPD, 0, jj * KS_C, lane);
                     ul[jj] = frag_rows<__bf16, KS_C>(UdTl, CPD, 0, jj * KS_C, lane);
-                }
-#pragma unroll
-                for (int m = 0; m < MS; ++m) {
-                    const int ib = rb + 4 * m;
-                    if (ib < NSB) {
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) ka[m][jj] = k_cols_tr<KS_C, DK>(Ks, 16 * ib, jj * KS_C, lane);
-                    }
                 }
 #pragma unroll
                 for (int m = 0; m < MS; ++m) {
