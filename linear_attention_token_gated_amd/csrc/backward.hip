@@ -1953,20 +1953,35 @@ template <int C, int DK> struct Fwd16Lay {
     static constexpr size_t oUh = oXl + TB, oUl = oUh + TB;        // U^T (for P U)
     static constexpr size_t oDh = oUl + TB, oDl = oDh + TB;        // (d o U)^T (for the update)
     static constexpr size_t oIn = oDl + TB;
-    static constexpr size_t oG = oIn + 4 * C * VP;
-    static constexpr size_t oB = oG + 4 * C;
-    static constexpr size_t BYTES = oB + 4 * C;
+    static constexpr size_t oG = oIn + 4 * C * VP;                 // G2, two buffers
+    static constexpr size_t oB = oG + 2 * 4 * C;                   // beta, two buffers
+    static constexpr size_t BYTES = oB + 2 * 4 * C;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+// 8 wavefronts: waves 0-3 carry the chain of every chunk, waves 4-7 stage the
+// operands into LDS (as bf16 pairs) while it runs, each array in the window
+// after its last read, and prefetch the next chunk's into registers.  The
+// chain reads the K^T operands of the state update in step 1, so K (like Q
+// and V) is free after step 1.  Per chunk c (barriers B1, B2, B3):
+//   B1..B2  chain: step 1 (K S, Q S, X);    staging: P of chunk c
+//   B2..B3  chain: step 2 (U = T X);        staging: K, Q, V, G2, beta of chunk c+1
+//   B3..B1  chain: step 3 (y, update);      staging: T of chunk c+1
+constexpr int NTF = 512;
+
 template <int C, int DK>
-__global__ __launch_bounds__(NT) void fwd16_carry_kernel(BwdParams p)
+__global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
 {
     using L = Fwd16Lay<C, DK>;
-    constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4;
+    constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4, NJ = C / 32;
     using F16 = Frag<__bf16, 16>;
     using F32 = Frag<__bf16, 32>;
     static_assert(DK % 32 == 0 && C % 32 == 0, "32-deep fragments over Dk and C");
+    constexpr int NST = 256;                                       // staging threads
+    constexpr int NUK = C * DK / 4, NVK = (NUK + NST - 1) / NST;   // float4 units of K or Q
+    constexpr int NUT = C * C / 4, NVT = (NUT + NST - 1) / NST;    // of T or P
+    constexpr int NUV = C * BV / 4;                                // of the V slice
+    static_assert(NUV <= NST && C <= NST, "one V unit and one gate per staging thread");
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __bf16 *Kh = reinterpret_cast<__bf16 *>(smem + L::oKh), *Kl = reinterpret_cast<__bf16 *>(smem + L::oKl);
@@ -1978,190 +1993,259 @@ __global__ __launch_bounds__(NT) void fwd16_carry_kernel(BwdParams p)
     __bf16 *Uh = reinterpret_cast<__bf16 *>(smem + L::oUh), *Ul = reinterpret_cast<__bf16 *>(smem + L::oUl);
     __bf16 *Dh = reinterpret_cast<__bf16 *>(smem + L::oDh), *Dl = reinterpret_cast<__bf16 *>(smem + L::oDl);
     float *Ins = reinterpret_cast<float *>(smem + L::oIn);
-    float *Gs = reinterpret_cast<float *>(smem + L::oG);
-    float *Bs = reinterpret_cast<float *>(smem + L::oB);
+    float *Gb = reinterpret_cast<float *>(smem + L::oG);
+    float *Bb = reinterpret_cast<float *>(smem + L::oB);
 
     const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
+    const bool chain = wave < 4;
     const int64_t NS = p.Dv / BV;
     int64_t bh, sl;
     slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
     const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
     const int n0 = (int)sl * BV;
 
-    f32x4 S[MS];
+    // The two roles run separate loops with the same barrier sequence (one
+    // barrier after the prologue, three per chunk).
+    if (!chain) {
+        // ---- staging waves.  Every load is issued unconditionally (clamped
+        // unit and row indices, the zeros past T applied when the data is
+        // written), so the compiler waits on exact outstanding-load counts.
+        const int ts = threadIdx.x - 256;
+        const float *kg = static_cast<const float *>(p.k);
+        const float *qg = static_cast<const float *>(p.q);
+        const float *vg = static_cast<const float *>(p.v);
+        auto clampc = [&](int64_t c) { return c >= NC ? NC - 1 : c; };
+        auto rec_of = [&](int64_t c) { return p.rec + (bh * NC + c) * p.rec_floats; };
+        f32x4 rK[NVK], rQ[NVK], rT[NVT], rP[NVT], rV = zero4();
+        float rG = 0.f, rBe = 0.f;
+        int64_t cKQ = 0;                                   // chunk held by rK, rQ, rV, rG, rBe
+        const int uv = ts < NUV ? ts : NUV - 1, ug = ts < C ? ts : C - 1;
+        auto load_kqv = [&](int64_t c) {
+            cKQ = c;
+            const int64_t c0 = c * C;
 #pragma unroll
-    for (int m = 0; m < MS; ++m) {
-        S[m] = zero4();
-        const int ib = wave + 4 * m;
-        if (ib < NKB && p.s0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[m][e] = p.s0[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln];
-        }
-    }
-
-    RowsTile<float, C, DK> rk, rq;
-    DenseTile<C, C> rt, rp;
-    RowsTile<float, C, BV> ri;
-    float rg = 0.f, rbeta = 0.f;
-    auto fetch = [&](int64_t c) {
-        const int64_t c0 = c * C;
-        const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
-        rk.load(static_cast<const float *>(p.k), b, h, c0, T, p.ks, DK);
-        rq.load(static_cast<const float *>(p.q), b, h, c0, T, p.qs, DK);
-        rt.load(rec + Rec<C>::oT, C);
-        rp.load(rec + Rec<C>::oP, C);
-        ri.load(static_cast<const float *>(p.v), b, h, c0, T, p.vs, Dv, n0);
-        if (threadIdx.x < C) {
-            const int64_t t = c0 + threadIdx.x;
-            rg = rec[Rec<C>::oG + threadIdx.x];
-            rbeta = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
-        }
-    };
-    fetch(0);
-
-    for (int64_t c = 0; c < NC; ++c) {
-        const int64_t c0 = c * C;
-        // ---- stage the chunk as bf16 pairs; prefetch the next
-#pragma unroll
-        for (int it = 0; it < RowsTile<float, C, DK>::NV; ++it) {
-            const int vi = threadIdx.x + NT * it;
-            const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
-            if (RowsTile<float, C, DK>::NU % NT == 0 || vi < RowsTile<float, C, DK>::NU) {
-                store_split4(Kh + r * KP + col, Kl + r * KP + col, rk.v[it]);
-                store_split4(Qh + r * KP + col, Ql + r * KP + col, rq.v[it]);
+            for (int i = 0; i < NVK; ++i) {
+                int u = ts + NST * i;
+                u = (NUK % NST == 0 || u < NUK) ? u : NUK - 1;
+                const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+                const int64_t t = c0 + r < T ? c0 + r : T - 1;
+                rK[i] = *reinterpret_cast<const f32x4 *>(kg + (b * T + t) * p.ks + h * DK + col);
+                rQ[i] = *reinterpret_cast<const f32x4 *>(qg + (b * T + t) * p.qs + h * DK + col);
             }
-        }
+            const int rv = uv / (BV / 4), cv = (uv % (BV / 4)) * 4;
+            const int64_t tv = c0 + rv < T ? c0 + rv : T - 1;
+            rV = *reinterpret_cast<const f32x4 *>(vg + (b * T + tv) * p.vs + h * Dv + n0 + cv);
+            const int64_t tg = c0 + ug < T ? c0 + ug : T - 1;
+            rG = rec_of(c)[Rec<C>::oG + ug];
+            rBe = p.beta[(b * T + tg) * H + h];
+        };
+        auto load_cc = [&](f32x4 (&rr)[NVT], int64_t c, int off) {
+            const float *rec = rec_of(c) + off;
 #pragma unroll
-        for (int it = 0; it < DenseTile<C, C>::NV; ++it) {
-            const int vi = threadIdx.x + NT * it;
-            const int r = vi / (C / 4), col = (vi % (C / 4)) * 4;
-            if (DenseTile<C, C>::NU % NT == 0 || vi < DenseTile<C, C>::NU) {
-                store_split4(Th + r * CP + col, Tl + r * CP + col, rt.v[it]);
-                store_split4(Ph + r * CP + col, Pl + r * CP + col, rp.v[it]);
+            for (int i = 0; i < NVT; ++i) {
+                int u = ts + NST * i;
+                u = (NUT % NST == 0 || u < NUT) ? u : NUT - 1;
+                const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+                rr[i] = *reinterpret_cast<const f32x4 *>(rec + r * C + col);
             }
-        }
-        ri.template store<VP>(Ins);
-        if (threadIdx.x < C) {
-            Gs[threadIdx.x] = rg;
-            Bs[threadIdx.x] = rbeta;
-        }
-        if (c + 1 < NC) fetch(c + 1);
+        };
+        auto write_kqv = [&](int gb) {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int ib = wave + 4 * m;
-            if (ib < NKB) {
-                const int row = 16 * ib + 4 * lg;
-                store_split4(STh + ln * KP + row, STl + ln * KP + row, S[m]);
-            }
-        }
-        lds_barrier();
-        const float GC = Gs[C - 1];
-
-        // ---- step 1: K S, Q S;  X = diag(beta)(V - e^G K S)
-        f32x4 qsv = zero4();
-        if (wave < NB) {
-            const int rb = wave;
-            f32x4 ks = zero4(), ks2 = zero4(), qs2 = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32) {
-                const F32 sh = frag_rows<__bf16, 32>(STh, KP, 0, k0, lane);
-                const F32 sl2 = frag_rows<__bf16, 32>(STl, KP, 0, k0, lane);
-                const F32 kh = frag_rows<__bf16, 32>(Kh, KP, 16 * rb, k0, lane);
-                const F32 kl = frag_rows<__bf16, 32>(Kl, KP, 16 * rb, k0, lane);
-                const F32 qh = frag_rows<__bf16, 32>(Qh, KP, 16 * rb, k0, lane);
-                const F32 ql = frag_rows<__bf16, 32>(Ql, KP, 16 * rb, k0, lane);
-                ks = F32::mma(kh, sh, ks);
-                qsv = F32::mma(qh, sh, qsv);
-                ks2 = F32::mma(kh, sl2, ks2);
-                qs2 = F32::mma(qh, sl2, qs2);
-                ks2 = F32::mma(kl, sh, ks2);
-                qs2 = F32::mma(ql, sh, qs2);
-            }
-            ks += ks2;
-            qsv += qs2;
-            const int r0 = 16 * rb + 4 * lg;
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[e] = Bs[r0 + e] * (Ins[(r0 + e) * VP + ln] - __builtin_amdgcn_exp2f(Gs[r0 + e]) * ks[e]);
-            store_split4(Xh + ln * CP + r0, Xl + ln * CP + r0, x);
-        }
-        lds_barrier();
-
-        // ---- step 2: U = T X, kept transposed (for P U) and decayed (for the update)
-        if (wave < NB) {
-            const int rb = wave;
-            const int r0 = 16 * rb + 4 * lg;
-            f32x4 acc = zero4(), acc2 = zero4();
-            for (int kb = 0; kb <= rb; ++kb) {
-                const F16 ah = frag_rows<__bf16, 16>(Th, CP, 16 * rb, 16 * kb, lane);
-                const F16 al = frag_rows<__bf16, 16>(Tl, CP, 16 * rb, 16 * kb, lane);
-                const F16 xh = frag_rows<__bf16, 16>(Xh, CP, 0, 16 * kb, lane);
-                const F16 xl = frag_rows<__bf16, 16>(Xl, CP, 0, 16 * kb, lane);
-                acc = F16::mma(ah, xh, acc);
-                acc2 = F16::mma(ah, xl, acc2);
-                acc2 = F16::mma(al, xh, acc2);
-            }
-            acc += acc2;
-            store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, acc);
-            f32x4 d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(GC - Gs[r0 + e]) * acc[e];
-            store_split4(Dh + ln * CP + r0, Dl + ln * CP + r0, d);
-        }
-        lds_barrier();
-
-        // ---- step 3: Y = diag(e^G) Q S + P U;  S <- e^{G_C} S + K^T (d o U)
-        if (wave < NB) {
-            const int rb = wave;
-            f32x4 acc, acc2 = zero4();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_exp2f(Gs[16 * rb + 4 * lg + e]) * qsv[e];
-            for (int jb = 0; jb <= rb; ++jb) {
-                const F16 ah = frag_rows<__bf16, 16>(Ph, CP, 16 * rb, 16 * jb, lane);
-                const F16 al = frag_rows<__bf16, 16>(Pl, CP, 16 * rb, 16 * jb, lane);
-                const F16 uh = frag_rows<__bf16, 16>(Uh, CP, 0, 16 * jb, lane);
-                const F16 ul = frag_rows<__bf16, 16>(Ul, CP, 0, 16 * jb, lane);
-                acc = F16::mma(ah, uh, acc);
-                acc2 = F16::mma(ah, ul, acc2);
-                acc2 = F16::mma(al, uh, acc2);
-            }
-            acc += acc2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t t = c0 + 16 * rb + 4 * lg + e;
-                if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e];
-            }
-        }
-        const float eGC = __builtin_amdgcn_exp2f(GC);
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int ib = wave + 4 * m;
-            if (ib < NKB) {
-                f32x4 acc = S[m] * eGC, acc2 = zero4();
-#pragma unroll
-                for (int j0 = 0; j0 < C; j0 += 32) {
-                    const F32 kh = tr_frag32(Kh, KP, 16 * ib, j0, lane);
-                    const F32 kl = tr_frag32(Kl, KP, 16 * ib, j0, lane);
-                    const F32 dh = pair_rows32(Dh, CP, 0, j0, lane);
-                    const F32 dl = pair_rows32(Dl, CP, 0, j0, lane);
-                    acc = F32::mma(kh, dh, acc);
-                    acc2 = F32::mma(kh, dl, acc2);
-                    acc2 = F32::mma(kl, dh, acc2);
+            for (int i = 0; i < NVK; ++i) {
+                const int u = ts + NST * i;
+                const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+                if (NUK % NST == 0 || u < NUK) {
+                    const bool ok = cKQ * C + r < T;
+                    store_split4(Kh + r * KP + col, Kl + r * KP + col, ok ? rK[i] : zero4());
+                    store_split4(Qh + r * KP + col, Ql + r * KP + col, ok ? rQ[i] : zero4());
                 }
-                S[m] = acc + acc2;
             }
+            if (ts < NUV) {
+                const int r = ts / (BV / 4), col = (ts % (BV / 4)) * 4;
+                *reinterpret_cast<f32x4 *>(Ins + r * VP + col) = cKQ * C + r < T ? rV : zero4();
+            }
+            if (ts < C) {
+                Gb[gb * C + ts] = rG;
+                Bb[gb * C + ts] = cKQ * C + ts < T ? rBe : 0.f;
+            }
+        };
+        auto write_cc = [&](const f32x4 (&rr)[NVT], __bf16 *hi, __bf16 *lo) {
+#pragma unroll
+            for (int i = 0; i < NVT; ++i) {
+                const int u = ts + NST * i;
+                const int r = u / (C / 4), col = (u % (C / 4)) * 4;
+                if (NUT % NST == 0 || u < NUT) store_split4(hi + r * CP + col, lo + r * CP + col, rr[i]);
+            }
+        };
+        // chunk 0 into LDS (P(0) is written in the first window), then chunk 1
+        // in flight, in the issue order of the loop
+        load_kqv(0);
+        load_cc(rT, 0, Rec<C>::oT);
+        load_cc(rP, 0, Rec<C>::oP);
+        write_kqv(0);
+        write_cc(rT, Th, Tl);
+        load_kqv(clampc(1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_cc(rT, clampc(1), Rec<C>::oT);
+        lds_barrier();                                  // B1 of chunk 0
+        for (int64_t c = 0; c < NC; ++c) {
+            write_cc(rP, Ph, Pl);                       // P(c): P(c-1) last read in step 3
+            load_cc(rP, clampc(c + 1), Rec<C>::oP);
+            lds_barrier();                              // B2
+            write_kqv((int)((c + 1) & 1));              // chunk c+1: K, Q, V last read in step 1
+            load_kqv(clampc(c + 2));
+            lds_barrier();                              // B3
+            write_cc(rT, Th, Tl);                       // T(c+1): T(c) last read in step 2
+            load_cc(rT, clampc(c + 2), Rec<C>::oT);
+            lds_barrier();                              // B1 of chunk c+1
         }
-        lds_barrier();
-    }
-
-    if (p.sT) {
+    } else {
+        // ---- chain waves: the state slice in accumulators
+        f32x4 S[MS];
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
+            S[m] = zero4();
             const int ib = wave + 4 * m;
-            if (ib < NKB) {
+            if (ib < NKB && p.s0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p.sT[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+                for (int e = 0; e < 4; ++e) S[m][e] = p.s0[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln];
+            }
+        }
+        auto write_state_operand = [&]() {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+                    const int row = 16 * ib + 4 * lg;
+                    store_split4(STh + ln * KP + row, STl + ln * KP + row, S[m]);
+                }
+            }
+        };
+        write_state_operand();
+        lds_barrier();                                  // B1 of chunk 0
+        for (int64_t c = 0; c < NC; ++c) {
+            const int64_t c0 = c * C;
+            const float *Gs = Gb + (c & 1) * C, *Bs = Bb + (c & 1) * C;
+            const float GC = Gs[C - 1];
+
+            // ---- step 1: K S, Q S;  X = diag(beta)(V - e^G K S); the K^T
+            // operands of the update (K is restaged after this step)
+            F32 kth[MS][NJ], ktl[MS][NJ];
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) {
+                        kth[m][jj] = tr_frag32(Kh, KP, 16 * ib, 32 * jj, lane);
+                        ktl[m][jj] = tr_frag32(Kl, KP, 16 * ib, 32 * jj, lane);
+                    }
+                }
+            }
+            f32x4 qsv = zero4();
+            if (wave < NB) {
+                const int rb = wave;
+                f32x4 ks = zero4(), ks2 = zero4(), qs2 = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += 32) {
+                    const F32 sh = frag_rows<__bf16, 32>(STh, KP, 0, k0, lane);
+                    const F32 sl2 = frag_rows<__bf16, 32>(STl, KP, 0, k0, lane);
+                    const F32 kh = frag_rows<__bf16, 32>(Kh, KP, 16 * rb, k0, lane);
+                    const F32 kl = frag_rows<__bf16, 32>(Kl, KP, 16 * rb, k0, lane);
+                    const F32 qh = frag_rows<__bf16, 32>(Qh, KP, 16 * rb, k0, lane);
+                    const F32 ql = frag_rows<__bf16, 32>(Ql, KP, 16 * rb, k0, lane);
+                    ks = F32::mma(kh, sh, ks);
+                    qsv = F32::mma(qh, sh, qsv);
+                    ks2 = F32::mma(kh, sl2, ks2);
+                    qs2 = F32::mma(qh, sl2, qs2);
+                    ks2 = F32::mma(kl, sh, ks2);
+                    qs2 = F32::mma(ql, sh, qs2);
+                }
+                ks += ks2;
+                qsv += qs2;
+                const int r0 = 16 * rb + 4 * lg;
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = Bs[r0 + e] * (Ins[(r0 + e) * VP + ln] - __builtin_amdgcn_exp2f(Gs[r0 + e]) * ks[e]);
+                store_split4(Xh + ln * CP + r0, Xl + ln * CP + r0, x);
+            }
+            lds_barrier();                              // B2
+
+            // ---- step 2: U = T X, kept transposed (for P U) and decayed (for the update)
+            if (wave < NB) {
+                const int rb = wave;
+                const int r0 = 16 * rb + 4 * lg;
+                f32x4 acc = zero4(), acc2 = zero4();
+                for (int kb = 0; kb <= rb; ++kb) {
+                    const F16 ah = frag_rows<__bf16, 16>(Th, CP, 16 * rb, 16 * kb, lane);
+                    const F16 al = frag_rows<__bf16, 16>(Tl, CP, 16 * rb, 16 * kb, lane);
+                    const F16 xh = frag_rows<__bf16, 16>(Xh, CP, 0, 16 * kb, lane);
+                    const F16 xl = frag_rows<__bf16, 16>(Xl, CP, 0, 16 * kb, lane);
+                    acc = F16::mma(ah, xh, acc);
+                    acc2 = F16::mma(ah, xl, acc2);
+                    acc2 = F16::mma(al, xh, acc2);
+                }
+                acc += acc2;
+                store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, acc);
+                f32x4 d;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(GC - Gs[r0 + e]) * acc[e];
+                store_split4(Dh + ln * CP + r0, Dl + ln * CP + r0, d);
+            }
+            lds_barrier();                              // B3
+
+            // ---- step 3: Y = diag(e^G) Q S + P U;  S <- e^{G_C} S + K^T (d o U)
+            if (wave < NB) {
+                const int rb = wave;
+                f32x4 acc, acc2 = zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_exp2f(Gs[16 * rb + 4 * lg + e]) * qsv[e];
+                for (int jb = 0; jb <= rb; ++jb) {
+                    const F16 ah = frag_rows<__bf16, 16>(Ph, CP, 16 * rb, 16 * jb, lane);
+                    const F16 al = frag_rows<__bf16, 16>(Pl, CP, 16 * rb, 16 * jb, lane);
+                    const F16 uh = frag_rows<__bf16, 16>(Uh, CP, 0, 16 * jb, lane);
+                    const F16 ul = frag_rows<__bf16, 16>(Ul, CP, 0, 16 * jb, lane);
+                    acc = F16::mma(ah, uh, acc);
+                    acc2 = F16::mma(ah, ul, acc2);
+                    acc2 = F16::mma(al, uh, acc2);
+                }
+                acc += acc2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t t = c0 + 16 * rb + 4 * lg + e;
+                    if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = acc[e];
+                }
+            }
+            const float eGC = __builtin_amdgcn_exp2f(GC);
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+                    f32x4 acc = S[m] * eGC, acc2 = zero4();
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) {
+                        const F32 dh = pair_rows32(Dh, CP, 0, 32 * jj, lane);
+                        const F32 dl = pair_rows32(Dl, CP, 0, 32 * jj, lane);
+                        acc = F32::mma(kth[m][jj], dh, acc);
+                        acc2 = F32::mma(kth[m][jj], dl, acc2);
+                        acc2 = F32::mma(ktl[m][jj], dh, acc2);
+                    }
+                    S[m] = acc + acc2;
+                }
+            }
+            write_state_operand();                      // S^T of chunk c+1: last read in step 1
+            lds_barrier();                              // B1 of chunk c+1
+        }
+
+        if (p.sT) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = wave + 4 * m;
+                if (ib < NKB) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p.sT[(bh * DK + 16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+                }
             }
         }
     }
@@ -2248,7 +2332,7 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
     const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
     hipLaunchKernelGGL((bwd_prep_kernel<float, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
     if constexpr (DK % 32 == 0 && C % 32 == 0)
-        hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
+        hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
     else
         hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
     return hipGetLastError();
