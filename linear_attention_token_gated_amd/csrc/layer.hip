@@ -187,7 +187,7 @@ __device__ __forceinline__ float softplusf_(float x) { return x > 0.f ? x + log1
 // ---------------------------------------------------------------------------
 constexpr int PRO_TT = 32;
 
-template <int DK>
+template <int DK, int KC>
 __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__ pre, const __bf16 *__restrict__ conv_w,
                                                        const float *__restrict__ ab, const float *__restrict__ Aexp,
                                                        const float *__restrict__ b_alpha, float *__restrict__ post,
@@ -210,17 +210,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
         x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
         x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
     };
-    // taps: w[j] multiplies the input of token t - (conv_k - 1 - j)
-    float w[4][8];
+    // taps (KC = conv_k, a compile-time constant): w[j] multiplies the input
+    // of token t - (KC - 1 - j)
+    (void)conv_k;
+    float w[KC][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < KC; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[j][e] = j < conv_k ? (float)conv_w[(int64_t)(c0 + e) * conv_k + j] : 0.f;
-    // win[l - 1] = input of token t - l (zero before the sequence start)
-    float win[3][8];
+        for (int e = 0; e < 8; ++e) w[j][e] = (float)conv_w[(int64_t)(c0 + e) * KC + j];
+    // win[l - 1] = input of token t - l, zero before the sequence start, so a
+    // tap that reaches before it adds an exact zero
+    float win[KC > 1 ? KC - 1 : 1][8];
 #pragma unroll
-    for (int l = 1; l <= 3; ++l) {
-        if (l < conv_k && t0 - l >= 0) {
+    for (int l = 1; l < KC; ++l) {
+        if (t0 - l >= 0) {
             load8(t0 - l, win[l - 1]);
         } else {
 #pragma unroll
@@ -234,25 +237,21 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = xn[e];
         if (t + 1 < tend) load8(t + 1, xn);                // the next row is in flight meanwhile
-        // taps in the order j = 0 .. conv_k-1 (oldest input first); taps before the
-        // sequence start add nothing
+        // taps in the order j = 0 .. KC-1 (oldest input first)
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int lag = conv_k - 1 - j;
-            if (j < conv_k && t - lag >= 0) {
+        for (int j = 0; j < KC; ++j) {
+            const int lag = KC - 1 - j;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xv = lag == 0 ? x[e] : lag == 1 ? win[0][e] : lag == 2 ? win[1][e] : win[2][e];
-                    o[e] = fmaf(w[j][e], xv, o[e]);
-                }
-            }
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(w[j][e], lag == 0 ? x[e] : win[lag > 0 ? lag - 1 : 0][e], o[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            win[2][e] = win[1][e];
-            win[1][e] = win[0][e];
-            win[0][e] = x[e];
+        for (int l = KC - 2; l >= 1; --l)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[l][e] = win[l - 1][e];
+        if constexpr (KC > 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[0][e] = x[e];
         }
         // L2 normalisation of q and k heads (heads never straddle the q|k / v
         // boundary and vector groups are lane-aligned)
@@ -436,8 +435,17 @@ hipError_t launch_prologue_dk(const float *pre, const __bf16 *conv_w, const floa
 {
     const int64_t tiles = (M / T) * ((T + PRO_TT - 1) / PRO_TT);   // M = B * T, T > 0
     const unsigned slabs = (unsigned)((nqkv / 8 + 255) / 256);
-    hipLaunchKernelGGL((prologue_kernel<DK>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab, A,
-                       b_alpha, post, alpha, beta, T, H, nqkv, conv_k);
+    switch (conv_k) {
+    case 1: hipLaunchKernelGGL((prologue_kernel<DK, 1>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab,
+                               A, b_alpha, post, alpha, beta, T, H, nqkv, conv_k); break;
+    case 2: hipLaunchKernelGGL((prologue_kernel<DK, 2>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab,
+                               A, b_alpha, post, alpha, beta, T, H, nqkv, conv_k); break;
+    case 3: hipLaunchKernelGGL((prologue_kernel<DK, 3>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab,
+                               A, b_alpha, post, alpha, beta, T, H, nqkv, conv_k); break;
+    case 4: hipLaunchKernelGGL((prologue_kernel<DK, 4>), dim3((unsigned)tiles, slabs), dim3(256), 0, s, pre, conv_w, ab,
+                               A, b_alpha, post, alpha, beta, T, H, nqkv, conv_k); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
