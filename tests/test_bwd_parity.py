@@ -112,6 +112,27 @@ def test_bwd_4k_bf16_sampled_heads(oracle_mod):
             assert e <= TOL_F32, (b, h, n, e)
 
 
+def test_bwd_32k_bf16_sampled_heads(oracle_mod):
+    """The 32K-token workload the benchmark times (B=1, H=32, C=64, bf16), at
+    full size and in the same launch configuration; the oracle recomputes two
+    whole heads (every gradient of their 32768 tokens)."""
+    cfg = wl.PREFILL_32K
+    print(f"case: bwd {cfg.name} sampled heads", flush=True)
+    inp = wl.bwd_config_inputs(cfg)
+    g = _gpu(inp, cfg.chunk)
+    for b, h in ((0, 5), (0, cfg.H - 1)):
+        sub = {n: None if inp[n] is None else
+               inp[n][b:b + 1, h:h + 1] if n in ("S0", "dST") else inp[n][b:b + 1, :, h:h + 1]
+               for n in ("q", "k", "v", "alpha", "beta", "dy", "S0", "dST")}
+        ref = _oracle(oracle_mod, sub)
+        for n, r in GRADS:
+            x = host(g[n])
+            x = x[b:b + 1, :, h:h + 1] if n != "dinitial_state" else x[b:b + 1, h:h + 1]
+            e = rel_err(x, ref[r])
+            print(f"  b={b} h={h} {n}={e:.2e}", flush=True)
+            assert e <= TOL_F32, (b, h, n, e)
+
+
 @pytest.mark.parametrize("regime", ["strong_decay", "beta_near_one", "beta_near_zero"])
 def test_bwd_extreme_gates(oracle_mod, regime):
     """Strong decay (alpha down to 1e-3, so e^G underflows inside a 64-token
