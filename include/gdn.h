@@ -13,11 +13,14 @@
  * ---------------------------------------
  * - Every tensor pointer is a DEVICE pointer on the current HIP device, to a
  *   dense row-major (last index fastest) buffer, 16-byte aligned.
- * - The caller allocates and frees every buffer; the library keeps no device
- *   memory and no global mutable state other than a thread-local error string.
- *   It is reentrant.
+ * - The caller allocates and frees every buffer.  The library's own state is
+ *   a thread-local error string and, for the layer's projections, one
+ *   hipBLASLt handle per device with a cache of per-shape plans (created on
+ *   first use under a lock, kept until the process ends).  It is reentrant.
  * - Calls enqueue work on `stream` and return without synchronising.  A device
- *   fault shows up at the caller's next synchronisation.
+ *   fault shows up at the caller's next synchronisation.  With GDN_SYNC_CHECK=1
+ *   in the environment (a debugging aid) every call waits for its stream and
+ *   returns GDN_ERR_HIP, naming the entry point, if a kernel failed.
  * - Arguments are validated on the host before any HIP call: on a non-OK
  *   status nothing has been launched and no output has been touched.
  *   gdn_last_error() then holds a one-line description.

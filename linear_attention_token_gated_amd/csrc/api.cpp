@@ -2,6 +2,7 @@
 //
 // Every check runs on the host before any HIP call, so an invalid call
 // launches nothing and leaves every output untouched.
+#include <cstdlib>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -63,9 +64,18 @@ bool overlap(const Range &a, const Range &b)
     return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
-gdn_status hip_status(hipError_t e, const char *what)
+// The status of a launch.  With GDN_SYNC_CHECK=1 in the environment (a
+// debugging aid) the call also waits for the stream and reports any error the
+// kernels raised, naming the entry point; otherwise it returns at once.
+gdn_status hip_status(hipError_t e, const char *what, hipStream_t stream)
 {
-    if (e == hipSuccess) return ok();
+    if (e == hipSuccess) {
+        const char *sync = getenv("GDN_SYNC_CHECK");
+        if (!(sync && sync[0] == '1')) return ok();
+        e = hipStreamSynchronize(stream);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e == hipSuccess) return ok();
+    }
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -186,7 +196,7 @@ gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k
     a.q_tok_stride = H * Dk; a.k_tok_stride = H * Dk; a.v_tok_stride = H * Dv;
     a.bf16 = dtype == GDN_BF16;
     a.ws = need > 0 ? workspace : nullptr;
-    return hip_status(gdn::launch_prefill(a, stream, stages), fn);
+    return hip_status(gdn::launch_prefill(a, stream, stages), fn, stream);
 }
 
 }  // namespace
@@ -257,7 +267,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     gdn::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.y = y;
     a.N = N; a.H = H; a.Dk = Dk; a.Dv = Dv; a.bf16 = dtype == GDN_BF16;
-    return hip_status(gdn::launch_decode(a, stream), "gdn_decode_step launch");
+    return hip_status(gdn::launch_decode(a, stream), "gdn_decode_step launch", stream);
 }
 
 gdn_status gdn_decode_verify(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
@@ -300,7 +310,7 @@ gdn_status gdn_decode_verify(const void *q, const void *k, const void *v, const 
     gdn::VerifyArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s_in = state; a.s_out = states_out; a.y = y;
     a.N = N; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.bf16 = dtype == GDN_BF16;
-    return hip_status(gdn::launch_verify(a, stream), "gdn_decode_verify launch");
+    return hip_status(gdn::launch_verify(a, stream), "gdn_decode_verify launch", stream);
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk,
@@ -374,7 +384,7 @@ gdn_status gdn_layer_fwd(const void *x, const gdn_layer_params *p, const float *
     a.s0 = initial_state; a.sT = final_state; a.out = out;
     a.B = B; a.T = T; a.hidden = hidden; a.H = H; a.Dk = Dk; a.Dv = Dv; a.conv_k = conv_k; a.chunk = chunk;
     a.ws = workspace;
-    return hip_status(gdn::launch_layer(a, stream), "gdn_layer_fwd launch");
+    return hip_status(gdn::launch_layer(a, stream), "gdn_layer_fwd launch", stream);
 }
 
 size_t gdn_prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk)
@@ -452,7 +462,7 @@ gdn_status gdn_prefill_bwd(const void *q, const void *k, const void *v, const fl
     a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.chunk = chunk;
     a.bf16 = dtype == GDN_BF16;
     a.ws = need > 0 ? workspace : nullptr;
-    return hip_status(gdn::launch_prefill_bwd(a, stream), fn);
+    return hip_status(gdn::launch_prefill_bwd(a, stream), fn, stream);
 }
 
 size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
@@ -528,7 +538,7 @@ gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *p, float
     a.conv_state = conv_state; a.state = state; a.out = out;
     a.N = N; a.hidden = hidden; a.H = H; a.Dk = Dk; a.Dv = Dv; a.conv_k = conv_k;
     a.ws = workspace;
-    return hip_status(gdn::launch_layer_decode(a, stream), "gdn_layer_decode_step launch");
+    return hip_status(gdn::launch_layer_decode(a, stream), "gdn_layer_decode_step launch", stream);
 }
 
 }  // extern "C"

@@ -208,3 +208,19 @@ def test_prefill_f32_single_kernel_and_two_kernel_paths(oracle_mod, chunk, Dk, D
         ey, eS = rel_err(host(y), y_ref), rel_err(host(sT), S_ref)
         print(f"  single_kernel={single} err y={ey:.3e} S={eS:.3e}", flush=True)
         assert ey <= TOL_F32 and eS <= TOL_F32, (single, ey, eS)
+
+
+def test_sync_check_mode(oracle_mod, monkeypatch):
+    """GDN_SYNC_CHECK=1 makes every call wait for its stream and check for
+    kernel errors; results are the same bits as without it."""
+    import torch
+    import linear_attention_token_gated_amd as gdn
+    print("case: GDN_SYNC_CHECK", flush=True)
+    inp = wl.prefill_inputs(1, 130, 2, 64, 64, dtype="bf16", s0_std=0.1, seed=41)
+    args = [dev(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
+    monkeypatch.delenv("GDN_SYNC_CHECK", raising=False)
+    y1, s1 = gdn.prefill(*args, initial_state=dev(inp["S0"]), chunk=64)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("GDN_SYNC_CHECK", "1")
+    y2, s2 = gdn.prefill(*args, initial_state=dev(inp["S0"]), chunk=64)
+    assert np.array_equal(host(y1), host(y2)) and np.array_equal(host(s1), host(s2))
