@@ -3,22 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-A step is one chunked prefill on the 32K-token workload (B=1, T=32768,
-H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y) with every
-input already resident in HBM: gdn_prefill_prepare (the per-chunk
-preparation kernel) then gdn_prefill_recurrence (the state recurrence
-kernel), which together are exactly gdn_prefill_fwd.  The line printed also
-carries the decode step (256 sequences x 32 heads, fp32 128x128 states
-updated in place), the full layer (B=1, T=16384, hidden 2048, H=16) and the
-backward of the 32K prefill (every input gradient from dy and dS_T)
-measured the same way, the roofline of the recurrence kernel (the larger part
-of the step) with the preparation kernel beside it, and the fp64 oracle timed
-on the host cores on a bounded sample of the same workload.
+A step is one gdn_prefill_fwd on the 32K-token workload (B=1, T=32768, H=32,
+d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y) with every input
+already resident in HBM.  The JSON line carries that step's roofline (its
+algorithmic flops and bytes over the median step time, against the bf16 MFMA
+and HBM peaks), the 4K-context prefill (B=2, T=4096, H=16) measured the same
+way, the decode step (256 sequences x 32 heads, fp32 128x128 states updated in
+place), decode verify, the full layer (B=1, T=16384, hidden 2048, H=16) and
+its decode step, the backward of the 32K prefill, and the fp64 oracle timed on
+the host cores on a bounded sample of the same workload.
 
-Timing: HIP events recorded on the stream the kernels are launched on
-(torch's current stream), around every launch of the timed region (each of
-the two prefill kernels has its own pair); the region itself is bracketed by
-device synchronisations.
+Timing: HIP events recorded on torch's current stream, which is the stream the
+library launches on, around every timed step; a 512 MiB buffer is written
+before each timed step (outside the events) so that no step finds its inputs
+in the 256 MB Infinity Cache; the reported time is the median over the timed
+steps.  The region of all timed steps is bracketed by device synchronisations.
 """
 from __future__ import annotations
 
@@ -41,14 +40,22 @@ FP32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def prefill_alg(B, T, H, Dk, Dv, C, in_bytes=2, has_s0=False):
-    """Algorithmic bytes and flops of one prefill call (what the method must
-    move and compute, independent of the kernel): q, k, v read once, alpha and
-    beta read once, y (fp32) written once, final state written once."""
+def prefill_alg(B, T, H, Dk, Dv, C, has_s0=False):
+    """Algorithmic bytes and flops of one prefill (what the method must move and
+    compute, whatever the kernel).  Bytes per token-head: bf16 q, k, v, y and
+    fp32 alpha, beta = 2 (2 Dk + 2 Dv) + 8 (1032 at d = 128); plus the final
+    state written (and the initial state read, if given).  The outputs y here
+    are fp32, so the bytes with y at 4 bytes are returned too.  Flops per
+    token-head, triangle-exact: (3C - 1) Dk + 2 C Dv + 6 Dk Dv + C^2 / 3; with
+    full C x C tiles: 2 C (3 Dk + 2 Dv) + 6 Dk Dv + C^2 / 3.
+    Returns (bytes, bytes with fp32 y, F_alg, F_tile)."""
     tok = B * T * H
-    bytes_ = tok * ((2 * Dk + Dv) * in_bytes + 8 + 4 * Dv) + B * H * Dk * Dv * 4 * (2 if has_s0 else 1)
-    f_alg = (3 * C - 1) * Dk + 2 * C * Dv + 6 * Dk * Dv + C * C / 3.0     # per token-head
-    return bytes_, tok * f_alg
+    st = B * H * Dk * Dv * 4 * (2 if has_s0 else 1)
+    b_bf16_y = tok * (2 * (2 * Dk + 2 * Dv) + 8) + st
+    b_fp32_y = tok * (2 * (2 * Dk + Dv) + 4 * Dv + 8) + st
+    f_alg = (3 * C - 1) * Dk + 2 * C * Dv + 6 * Dk * Dv + C * C / 3.0
+    f_tile = 2 * C * (3 * Dk + 2 * Dv) + 6 * Dk * Dv + C * C / 3.0
+    return b_bf16_y, b_fp32_y, tok * f_alg, tok * f_tile
 
 
 def record_bytes(C):
@@ -157,25 +164,48 @@ PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/recurrence.hip",
 DECODE_SOURCES = ["linear_attention_token_gated_amd/csrc/decode.hip"]
 
 
-def measured_traffic(key="prefill_32k", sources=PREFILL_SOURCES):
-    """HBM bytes per launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE + WRITE_SIZE, each scaled by its reading for a copy of known
-    size), if they were taken on the current kernel source; else None."""
+# counter keys: the kernels whose FETCH_SIZE + WRITE_SIZE add up to one launch
+# of the workload, and the sources whose hash the stored counts were taken on
+TRAFFIC_KERNELS = {
+    "prefill_32k": (["gdn_chunk_prep_kernel", "gdn_recurrence_kernel"], PREFILL_SOURCES),
+    "decode_256x32": (["gdn_decode_kernel"], DECODE_SOURCES),
+}
+
+
+def measured_traffic(key="prefill_32k", sources=None):
+    """HBM bytes of one launch of a workload from the committed rocprofv3
+    counter runs (FETCH_SIZE + WRITE_SIZE, each scaled by its reading for a
+    copy of known size), if they were taken on the current kernel source;
+    else None."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             t = json.load(f)[key]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(sources):
+    if t.get("source_sha") != source_sha(sources or TRAFFIC_KERNELS[key][1]):
         return None
     return t.get("hbm_bytes_per_launch")
 
 
-def time_launches(fns, steps, warmup, torch):
-    """A step calls every function of `fns` in order.  Run `warmup` steps,
-    then `steps` steps with a HIP event pair around each call on the current
-    stream.  Returns (total ms of the bracketed region, per function a list of
-    per-call ms)."""
+class Flush:
+    """A 512 MiB device buffer written before every timed step: twice the
+    256 MB Infinity Cache, so no step finds its inputs left in it by the
+    previous one."""
+
+    def __init__(self, torch, nbytes=512 << 20):
+        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def time_steps(fns, steps, warmup, torch, flush=None):
+    """A step calls every function of `fns` in order on torch's current stream
+    (the stream the library launches on).  `warmup` untimed steps, then
+    `steps` timed ones, each preceded by `flush` (outside the timed events) and
+    bracketed by HIP events, with an event between consecutive functions.
+    The whole region is bracketed by device synchronisations.  Returns
+    (per-step ms list, per-function ms lists, ms of the whole region)."""
     if callable(fns):
         fns = [fns]
     for _ in range(warmup):
@@ -183,21 +213,26 @@ def time_launches(fns, steps, warmup, torch):
             fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
-          for _ in range(steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_all0.record(stream)
-    for step in ev:
-        for fn, (a, b) in zip(fns, step):
-            a.record(stream)
+    t0.record(stream)
+    for ev in evs:
+        if flush is not None:
+            flush()
+        ev[0].record(stream)
+        for i, fn in enumerate(fns):
             fn()
-            b.record(stream)
-    t_all1.record(stream)
+            ev[i + 1].record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
-    per = [[step[i][0].elapsed_time(step[i][1]) for step in ev] for i in range(len(fns))]
-    return t_all0.elapsed_time(t_all1), (per[0] if len(fns) == 1 else per)
+    per_step = [ev[0].elapsed_time(ev[-1]) for ev in evs]
+    per_fn = [[ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i in range(len(fns))]
+    return per_step, per_fn, t0.elapsed_time(t1)
+
+
+def median(x):
+    return float(np.median(np.asarray(x, dtype=np.float64)))
 
 
 def to_dev(a, torch):
@@ -208,33 +243,55 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def bench_prefill(args, torch, gdn, wl):
-    cfg = wl.PREFILL_32K
+def prefill_setup(cfg, torch, gdn, wl):
     inp = wl.prefill_config_inputs(cfg)
-    q, k, v = (to_dev(inp[n], torch) for n in ("q", "k", "v"))
-    al, be = to_dev(inp["alpha"], torch), to_dev(inp["beta"], torch)
+    t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "S0")}
     y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(gdn.prefill_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk, "bf16"),
-                     dtype=torch.uint8, device="cuda")
-    prep = lambda: gdn.prefill_prepare(q, k, al, be, ws, chunk=cfg.chunk)
-    rec = lambda: gdn.prefill_recurrence(q, k, v, ws, None, chunk=cfg.chunk, y=y, final_state=sT)
-    total_ms, (per_prep, per_rec) = time_launches([prep, rec], args.steps, args.warmup, torch)
-    return cfg, inp, total_ms, per_prep, per_rec
+    ws = torch.empty(max(1, gdn.prefill_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk,
+                                                        cfg.dtype)), dtype=torch.uint8, device="cuda")
+    fn = lambda: gdn.prefill(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["S0"], chunk=cfg.chunk, y=y,
+                             final_state=sT, workspace=ws)
+    return inp, fn
 
 
-def bench_decode(args, torch, gdn, wl):
+def prefill_report(cfg, per_step, region_ms, steps, peak_tflops):
+    ms = median(per_step)
+    b8, b32, f_alg, f_tile = prefill_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk,
+                                         has_s0=cfg.s0_std is not None)
+    t = ms * 1e-3
+    return {"workload": cfg.name, "ms_per_step": round(ms, 4), "ms_mean": round(float(np.mean(per_step)), 4),
+            "ms_min": round(float(np.min(per_step)), 4), "ms_back_to_back": round(region_ms / steps, 4),
+            "tokens_per_s": cfg.B * cfg.T / t,
+            "flops_alg": f_alg, "tflops_alg": f_alg / t / 1e12, "mfma_frac": f_alg / t / 1e12 / peak_tflops,
+            "mfma_frac_tile": f_tile / t / 1e12 / peak_tflops,
+            "alg_bytes": b8, "hbm_GBps": b8 / t / 1e9, "hbm_frac": b8 / t / 1e9 / HBM_PEAK_GBPS,
+            "alg_bytes_fp32_y": b32, "hbm_frac_fp32_y": b32 / t / 1e9 / HBM_PEAK_GBPS}
+
+
+def bench_simple(fn, args, torch, flush, steps=None, warmup=None):
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    per, _, region = time_steps(fn, steps, warmup, torch, flush)
+    return median(per), region / steps, steps
+
+
+def bench_decode(args, torch, gdn, wl, flush):
     cfg = wl.DECODE_256
     inp = wl.decode_config_inputs(cfg)
-    q, k, v = (to_dev(inp[n], torch) for n in ("q", "k", "v"))
-    al, be, S = (to_dev(inp[n], torch) for n in ("alpha", "beta", "S"))
+    q, k, v, al, be, S = (to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "S"))
     y = torch.empty((cfg.N, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     fn = lambda: gdn.decode_step(q, k, v, al, be, S, y=y)   # in place: each step is a valid next step
-    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
-    return cfg, total_ms, per
+    ms, hot, _ = bench_simple(fn, args, torch, flush)
+    b, _ = decode_alg(cfg.N, cfg.H, cfg.Dk, cfg.Dv)
+    state = 8 * cfg.N * cfg.H * cfg.Dk * cfg.Dv
+    return {"workload": cfg.name, "ms_per_step": round(ms, 4), "ms_back_to_back": round(hot, 4),
+            "GBps": b / (ms * 1e-3) / 1e9, "state_GBps": state / (ms * 1e-3) / 1e9,
+            "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "alg_bytes_per_launch": b,
+            "traffic": measured_traffic("decode_256x32", DECODE_SOURCES)}
 
 
-def bench_layer(args, torch, gdn, wl):
+def bench_layer(args, torch, gdn, wl, flush, peak):
     cfg = wl.LAYER_16K
     inp = wl.layer_config_inputs(cfg)
     names = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
@@ -246,23 +303,29 @@ def bench_layer(args, torch, gdn, wl):
                                                cfg.chunk), dtype=torch.uint8, device="cuda")
     fn = lambda: gdn.layer_fwd(x, params, cfg.H, cfg.Dk, cfg.Dv, chunk=cfg.chunk, out=out, final_state=sT,
                                workspace=ws)
-    steps = max(1, min(args.steps, 10))
-    total_ms, per = time_launches(fn, steps, max(1, min(args.warmup, 2)), torch)
-    return cfg, total_ms, per, steps
+    ms, hot, steps = bench_simple(fn, args, torch, flush, max(1, min(args.steps, 10)), max(1, min(args.warmup, 2)))
+    gemm_f, core_f = layer_flops(cfg.B, cfg.T, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
+    t = ms * 1e-3
+    return {"workload": cfg.name, "ms_per_step": round(ms, 4), "ms_back_to_back": round(hot, 4),
+            "tokens_per_s": cfg.B * cfg.T / t, "gemm_tflops_alg": gemm_f / 1e12, "core_tflops_alg": core_f / 1e12,
+            "tflops_achieved": (gemm_f + core_f) / t / 1e12,
+            "mfma_frac": (gemm_f + core_f) / t / 1e12 / peak}
 
 
-def bench_verify(args, torch, gdn, wl):
+def bench_verify(args, torch, gdn, wl, flush):
     cfg = wl.VERIFY_256x4
     inp = wl.prefill_config_inputs(cfg)
     q, k, v, al, be, S = (to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "S0"))
     y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     so = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
     fn = lambda: gdn.decode_verify(q, k, v, al, be, S, states_out=so, y=y)
-    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
-    return cfg, total_ms, per
+    ms, hot, _ = bench_simple(fn, args, torch, flush)
+    b = verify_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv)
+    return {"workload": cfg.name, "ms_per_step": round(ms, 4), "alg_bytes_per_step": b,
+            "GBps": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-def bench_layer_decode(args, torch, gdn, wl):
+def bench_layer_decode(args, torch, gdn, wl, flush):
     cfg = wl.LAYER_DECODE_256
     inp, cs0, S0 = wl.layer_decode_config_inputs(cfg)
     names = ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate", "norm_gamma", "W_o")
@@ -274,11 +337,14 @@ def bench_layer_decode(args, torch, gdn, wl):
                      dtype=torch.uint8, device="cuda")
     # in place: each step is a valid next step of the same sequences
     fn = lambda: gdn.layer_decode_step(x, params, cfg.H, cfg.Dk, cfg.Dv, cs, S, out=out, workspace=ws)
-    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
-    return cfg, total_ms, per
+    ms, hot, _ = bench_simple(fn, args, torch, flush)
+    b = layer_decode_alg(cfg.B, cfg.hidden, cfg.H, cfg.Dk, cfg.Dv, cfg.conv_k)
+    return {"workload": cfg.name, "ms_per_step": round(ms, 4), "tokens_per_s": cfg.B / (ms * 1e-3),
+            "alg_bytes_per_step": b, "GBps": b / (ms * 1e-3) / 1e9,
+            "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-def bench_bwd(args, torch, gdn, wl):
+def bench_bwd(args, torch, gdn, wl, flush, fwd_ms, peak):
     cfg = wl.PREFILL_32K
     inp = wl.bwd_config_inputs(cfg)
     t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "dy", "S0", "dST")}
@@ -290,23 +356,118 @@ def bench_bwd(args, torch, gdn, wl):
                      dtype=torch.uint8, device="cuda")
     fn = lambda: gdn.prefill_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["dy"], t["S0"], t["dST"],
                                  chunk=cfg.chunk, out=out, workspace=ws)
-    steps = max(1, min(args.steps, 10))
-    total_ms, per = time_launches(fn, steps, max(1, min(args.warmup, 2)), torch)
-    return cfg, total_ms, per, steps
+    ms, hot, steps = bench_simple(fn, args, torch, flush, max(1, min(args.steps, 10)), max(1, min(args.warmup, 2)))
+    f = bwd_flops(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
+    tf = f / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name + ", gradients of every input from dy and dS_T",
+            "ms_per_call": round(ms, 4), "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3),
+            "bwd_over_fwd": ms / fwd_ms, "flops_alg_per_call": f, "tflops_achieved": tf,
+            "peak_tflops": peak, "frac": tf / peak,
+            "alg_bytes_per_kernel": bwd_kernel_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk),
+            "note": "bf16 inputs: every product of the four kernels runs on bf16 MFMA (fp32 operands as hi/lo "
+                    "bf16 pairs), so frac is against the bf16 dense peak"}
 
 
-def cpu_baseline(inp, cfg, wl, sample_T):
-    """The oracle, untouched, on the first sample_T tokens of every head."""
+def cpu_baseline(wl, sample_T):
+    """The oracle, untouched, on the first sample_T tokens of every head of
+    the 32K workload (all host threads), plus single-thread runs of the tiny
+    workload and of a sample of the 4K workload."""
     import oracle
-    sl = slice(0, sample_T)
-    args = [wl.widen(inp[n][:, sl]) for n in ("q", "k", "v", "alpha", "beta")]
-    t0 = time.perf_counter()
-    oracle.gdn_recurrence(*args, None)
-    dt = time.perf_counter() - t0
-    return {"value": cfg.B * sample_T / dt, "unit": "tokens/s", "cores": oracle.last_threads_used,
-            "kind": "oracle",
-            "sample": f"fp64 sequential recurrence on the first {sample_T} tokens of all {cfg.B * cfg.H} "
-                      f"(batch, head) sequences of the 32K workload ({dt:.1f} s)"}
+
+    def rate(cfg, T, nthreads):
+        inp = wl.prefill_config_inputs(cfg)
+        sl = slice(0, T)
+        args = [wl.widen(inp[n][:, sl]) for n in ("q", "k", "v", "alpha", "beta")]
+        s0 = wl.widen(inp["S0"])
+        t0 = time.perf_counter()
+        oracle.gdn_recurrence(*args, s0, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        return cfg.B * T / dt, dt, oracle.last_threads_used
+
+    v, dt, cores = rate(wl.PREFILL_32K, sample_T, 0)
+    tiny, _, _ = rate(wl.TINY, wl.TINY.T, 1)
+    t4 = min(512, wl.PREFILL_4K.T)
+    one4k, dt4, _ = rate(wl.PREFILL_4K, t4, 1)
+    return {"value": v, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 sequential recurrence on the first {sample_T} tokens of all "
+                      f"{wl.PREFILL_32K.B * wl.PREFILL_32K.H} (batch, head) sequences of the 32K workload "
+                      f"({dt:.1f} s)",
+            "one_thread": {"tiny_tokens_per_s": tiny,
+                           "4k_tokens_per_s": one4k,
+                           "4k_sample": f"first {t4} tokens of all {wl.PREFILL_4K.B * wl.PREFILL_4K.H} sequences "
+                                        f"({dt4:.1f} s)"}}
+
+
+def device_info(torch):
+    """Name, CU count, the peak engine clock HIP reports and, where readable,
+    the current engine clock level from sysfs."""
+    import ctypes
+    import glob
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "peak_clock_mhz": None, "sclk_now_mhz": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, torch.cuda.current_device()) == 0:  # ClockRate, kHz
+            info["peak_clock_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if line.strip().endswith("*"):
+                    info["sclk_now_mhz"] = float(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                                 .replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+        if info["sclk_now_mhz"] is not None:
+            break
+    return info
+
+
+def pmc_summarize(fetch_csv, write_csv):
+    """Turn two rocprofv3 counter runs of `bench.py --pmc-run` (FETCH_SIZE,
+    then WRITE_SIZE, csv counter collections) into profiles/traffic.json: per
+    workload kernel, HBM bytes per launch, each counter scaled by its reading
+    for the 1 GiB copy of known size that --pmc-run ends with."""
+    import csv
+
+    def load(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            name = r["Kernel_Name"]
+            val = float(r["Counter_Value"])
+            rows.setdefault(name, []).append(val)
+        return rows
+
+    fr, wr = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = [n for n in fr if "copyBuffer" in n]
+    assert copy, "no calibration copy in the counter run"
+    gib = float(1 << 30)
+    f_fac = max(fr[copy[0]]) * 1024 / gib
+    w_fac = max(wr[copy[0]]) * 1024 / gib
+    out = {"calibration": {"kernel": copy[0] + " (torch copy_ of 1 GiB fp32)", "bytes_read": 1 << 30,
+                           "bytes_written": 1 << 30, "fetch_factor": f_fac, "write_factor": w_fac}}
+    for key, (needles, sources) in TRAFFIC_KERNELS.items():
+        names = [next((n for n in fr if nd in n), None) for nd in needles]
+        if None in names:
+            continue
+        # the largest dispatch of each kernel is the workload's (smaller ones are other shapes)
+        fk = sum(max(fr[n]) for n in names)
+        wk = sum(max(wr.get(n, [0.0])) for n in names)
+        rd, wb = fk * 1024 / f_fac, wk * 1024 / w_fac
+        out[key] = {"kernels": names, "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "hbm_read_bytes": rd,
+                    "hbm_write_bytes": wb, "hbm_bytes_per_launch": rd + wb, "source_sha": source_sha(sources)}
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(out, f, indent=1)
+    for key, t in out.items():
+        if key != "calibration":
+            print(f"| {key} | {t['FETCH_SIZE_KiB']:.0f} | {t['WRITE_SIZE_KiB']:.0f} | "
+                  f"{t['hbm_read_bytes'] / 1e6:.1f} MB | {t['hbm_write_bytes'] / 1e6:.1f} MB | "
+                  f"{t['hbm_bytes_per_launch'] / 1e6:.1f} MB |")
 
 
 def main():
@@ -317,30 +478,39 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-layer", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true", help="the 32K and 4K prefill objects only")
     ap.add_argument("--pmc-run", action="store_true",
-                    help="for hardware-counter passes: two prefill launches, two decode steps, two layer "
-                         "calls and a 1 GiB device copy of known size (the copy calibrates FETCH_SIZE / "
-                         "WRITE_SIZE)")
+                    help="for hardware-counter passes: each workload twice and a 1 GiB device copy of known size "
+                         "(the copy calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two --pmc-run counter collections")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
 
     import torch
     import linear_attention_token_gated_amd as gdn
     from linear_attention_token_gated_amd import workloads as wl
 
     gdn.lib()
-    props = torch.cuda.get_device_properties(0)
+    dev = device_info(torch)
+    clock = dev["peak_clock_mhz"] or 2400.0
+    peak_from_clock = dev["cus"] * 4096 * clock * 1e6 / 1e12          # bf16 dense: 4096 flop/clk per CU
 
     if args.pmc_run:
         pargs = argparse.Namespace(steps=1, warmup=1)
-        bench_prefill(pargs, torch, gdn, wl)
-        bench_decode(pargs, torch, gdn, wl)
-        bench_layer(pargs, torch, gdn, wl)
-        bench_layer_decode(pargs, torch, gdn, wl)
-        bench_verify(pargs, torch, gdn, wl)
-        bench_bwd(pargs, torch, gdn, wl)
+        for cfg in (wl.PREFILL_32K, wl.PREFILL_4K):
+            _, fn = prefill_setup(cfg, torch, gdn, wl)
+            fn(); fn()
+        bench_decode(pargs, torch, gdn, wl, None)
+        bench_layer(pargs, torch, gdn, wl, None, BF16_PEAK_TFLOPS)
+        bench_layer_decode(pargs, torch, gdn, wl, None)
+        bench_verify(pargs, torch, gdn, wl, None)
+        bench_bwd(pargs, torch, gdn, wl, None, 1.0, BF16_PEAK_TFLOPS)
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -349,107 +519,65 @@ def main():
                           "copy_bytes_written": dst.numel() * 4}))
         return
 
-    cfg, inp, p_total, p_prep, p_rec = bench_prefill(args, torch, gdn, wl)
-    alg_bytes, alg_flops = prefill_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
-    ms_step = p_total / args.steps
-    ms_prep, ms_rec = float(np.mean(p_prep)), float(np.mean(p_rec))
-    tok_s = cfg.B * cfg.T / (ms_step * 1e-3)
-    rec_bytes = recurrence_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk)
-    prep_bytes = prep_alg(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.chunk)
-    achieved_gbps = rec_bytes / (ms_rec * 1e-3) / 1e9
-    traffic = measured_traffic("prefill_32k_recurrence")
+    flush = Flush(torch)
+    cfg = wl.PREFILL_32K
+    inp, fn = prefill_setup(cfg, torch, gdn, wl)
+    per, _, region = time_steps(fn, args.steps, args.warmup, torch, flush)
+    head = prefill_report(cfg, per, region, args.steps, BF16_PEAK_TFLOPS)
+    print(f"prefill 32K: {head['ms_per_step']} ms", file=sys.stderr, flush=True)
+    _, fn4 = prefill_setup(wl.PREFILL_4K, torch, gdn, wl)
+    per4, _, region4 = time_steps(fn4, args.steps, args.warmup, torch, flush)
+    p4k = prefill_report(wl.PREFILL_4K, per4, region4, args.steps, BF16_PEAK_TFLOPS)
+    traffic = measured_traffic("prefill_32k")
+    ms_step = head["ms_per_step"]
 
-    d_cfg, d_total, d_per = bench_decode(args, torch, gdn, wl)
-    d_bytes, _ = decode_alg(d_cfg.N, d_cfg.H, d_cfg.Dk, d_cfg.Dv)
-    d_state = 8 * d_cfg.N * d_cfg.H * d_cfg.Dk * d_cfg.Dv
-    d_ms = float(np.mean(d_per))
-
-    layer = None
-    if not args.skip_layer:
-        l_cfg, l_total, l_per, l_steps = bench_layer(args, torch, gdn, wl)
-        gemm_f, core_f = layer_flops(l_cfg.B, l_cfg.T, l_cfg.hidden, l_cfg.H, l_cfg.Dk, l_cfg.Dv, l_cfg.chunk)
-        l_ms = l_total / l_steps
-        layer = {"workload": l_cfg.name, "ms_per_step": round(l_ms, 4),
-                 "tokens_per_s": l_cfg.B * l_cfg.T / (l_ms * 1e-3),
-                 "gemm_tflops_alg": gemm_f / 1e12, "core_tflops_alg": core_f / 1e12,
-                 "tflops_achieved": (gemm_f + core_f) / (l_ms * 1e-3) / 1e12,
-                 "note": "core runs on fp32 q/k/v (two kernels, bf16 MFMA with hi/lo operands); projections on hipBLASLt, bf16 operands, fp32 accumulation"}
-
-    ld_cfg, ld_total, ld_per = bench_layer_decode(args, torch, gdn, wl)
-    ld_ms = float(np.mean(ld_per))
-    ld_bytes = layer_decode_alg(ld_cfg.B, ld_cfg.hidden, ld_cfg.H, ld_cfg.Dk, ld_cfg.Dv, ld_cfg.conv_k)
-    layer_decode = {"workload": ld_cfg.name, "ms_per_step": round(ld_ms, 4),
-                    "tokens_per_s": ld_cfg.B / (ld_ms * 1e-3), "alg_bytes_per_step": ld_bytes,
-                    "GBps": ld_bytes / (ld_ms * 1e-3) / 1e9,
-                    "hbm_frac": ld_bytes / (ld_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-
-    v_cfg, v_total, v_per = bench_verify(args, torch, gdn, wl)
-    v_ms = float(np.mean(v_per))
-    v_bytes = verify_alg(v_cfg.B, v_cfg.T, v_cfg.H, v_cfg.Dk, v_cfg.Dv)
-    verify = {"workload": v_cfg.name, "ms_per_step": round(v_ms, 4), "alg_bytes_per_step": v_bytes,
-              "GBps": v_bytes / (v_ms * 1e-3) / 1e9, "hbm_frac": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-
-    b_cfg, b_total, b_per, b_steps = bench_bwd(args, torch, gdn, wl)
-    b_ms = float(np.mean(b_per))
-    b_flops = bwd_flops(b_cfg.B, b_cfg.T, b_cfg.H, b_cfg.Dk, b_cfg.Dv, b_cfg.chunk)
-    bwd = {"workload": b_cfg.name + ", gradients of every input from dy and dS_T",
-           "ms_per_call": round(b_ms, 4), "tokens_per_s": b_cfg.B * b_cfg.T / (b_ms * 1e-3),
-           "bwd_over_fwd": b_ms / ms_step, "flops_alg_per_call": b_flops,
-           "tflops_achieved": b_flops / (b_ms * 1e-3) / 1e12, "peak_tflops": FP32_PEAK_TFLOPS,
-           "frac": b_flops / (b_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
-           "alg_bytes_per_kernel": bwd_kernel_alg(b_cfg.B, b_cfg.T, b_cfg.H, b_cfg.Dk, b_cfg.Dv, b_cfg.chunk),
-           "note": "four kernels: preparation (Gram on bf16 MFMA), state pass and adjoint state pass (bf16 MFMA, "
-                   "hi/lo operands), chunk gradients (fp32 MFMA); frac is against the fp32 MFMA peak"}
+    extra = {}
+    if not args.only_prefill:
+        extra["decode"] = bench_decode(args, torch, gdn, wl, flush)
+        print(f"decode: {extra['decode']['ms_per_step']} ms", file=sys.stderr, flush=True)
+        extra["layer"] = None if args.skip_layer else bench_layer(args, torch, gdn, wl, flush, BF16_PEAK_TFLOPS)
+        extra["layer_decode"] = bench_layer_decode(args, torch, gdn, wl, flush)
+        extra["verify"] = bench_verify(args, torch, gdn, wl, flush)
+        extra["bwd"] = bench_bwd(args, torch, gdn, wl, flush, ms_step, BF16_PEAK_TFLOPS)
+        print(f"bwd: {extra['bwd']['ms_per_call']} ms", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, cfg, wl, min(args.cpu_sample_tokens, cfg.T))
+        cpu = cpu_baseline(wl, min(args.cpu_sample_tokens, cfg.T))
 
     line = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "Dk": cfg.Dk, "Dv": cfg.Dv,
-                   "chunk": cfg.chunk, "qkv": "bf16", "alpha_beta_state_y": "fp32",
-                   "initial_state": "none"},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "kernel": "gdn_recurrence_kernel<C=64, Dk=128>",
-                     "ms_per_launch": round(ms_rec, 4),
-                     "alg_bytes_per_launch": rec_bytes},
-        "prep_kernel": {"kernel": "gdn_chunk_prep_kernel<C=64, Dk=128>", "ms_per_launch": round(ms_prep, 4),
-                        "alg_bytes_per_launch": prep_bytes,
-                        "achieved_GBps": prep_bytes / (ms_prep * 1e-3) / 1e9,
-                        "hbm_frac": prep_bytes / (ms_prep * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                        "traffic": measured_traffic("prefill_32k_prep")},
-        "step_hbm": {"alg_bytes_per_step": alg_bytes, "achieved_GBps": alg_bytes / (ms_step * 1e-3) / 1e9,
-                     "frac": alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-        "mfma": {"flops_alg_per_step": alg_flops,
-                 "tflops_achieved": alg_flops / (ms_step * 1e-3) / 1e12,
-                 "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": alg_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
-        "decode": {"workload": d_cfg.name, "ms_per_step": round(d_ms, 4),
-                   "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
-                   "state_GBps": d_state / (d_ms * 1e-3) / 1e9,
-                   "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                   "alg_bytes_per_launch": d_bytes,
-                   "traffic": measured_traffic("decode_256x32", DECODE_SOURCES)},
-        "layer": layer,
-        "layer_decode": layer_decode,
-        "verify": verify,
-        "bwd": bwd,
+                   "chunk": cfg.chunk, "qkv": "bf16", "alpha_beta_state_y": "fp32", "initial_state": "none"},
+        "roofline": {"bound": "mfma", "achieved": head["tflops_alg"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": head["mfma_frac"], "traffic": traffic,
+                     "scope": "whole prefill step (every kernel gdn_prefill_fwd launches)",
+                     "flops_alg_per_step": head["flops_alg"],
+                     "frac_full_tile_flops": head["mfma_frac_tile"],
+                     "peak_from_clock_tflops": peak_from_clock,
+                     "alg_bytes_per_step": head["alg_bytes"],
+                     "traffic_over_alg_bytes": (traffic / head["alg_bytes"]) if traffic else None,
+                     "hbm": {"achieved_GBps": head["hbm_GBps"], "peak": HBM_PEAK_GBPS,
+                             "frac": head["hbm_frac"], "frac_with_fp32_y": head["hbm_frac_fp32_y"]}},
+        "prefill_32k": head,
+        "prefill_4k": p4k,
+        **extra,
         "cpu_baseline": cpu,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": dev,
+        "timing": {"protocol": "HIP events on the launch stream around each step; a 512 MiB buffer written "
+                               "before every timed step (outside the events); median over the timed steps",
+                   "mall_flush_bytes": 512 << 20},
     }
     print(json.dumps(line))
 

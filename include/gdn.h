@@ -25,8 +25,11 @@
  *   status nothing has been launched and no output has been touched.
  *   gdn_last_error() then holds a one-line description.
  * - Value domains are preconditions, not checked on the device:
- *   alpha in (0, 1] (the pages give the open interval (0,1); alpha = 1 is
- *   accepted as an exact identity decay), beta in [0, 1], all inputs finite.
+ *   alpha in [0, 1] for the forward entry points (the pages give the open
+ *   interval (0,1); alpha = 1 is accepted as an exact identity decay, and an
+ *   alpha below 2^-126 -- zero or subnormal -- acts as 2^-126, which leaves
+ *   less than 1.2e-38 of the state), alpha in (0, 1] for gdn_prefill_bwd,
+ *   beta in [0, 1], all inputs finite.
  * - Outputs y, out and final_state are always float32.
  */
 #ifndef GDN_H_
@@ -73,19 +76,16 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   chunk is padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
  *   workspace     device scratch of at least gdn_prefill_workspace_bytes(...)
  *                 bytes, 256-byte aligned, owned by the caller and not
- *                 overlapping any other argument.  GDN_BF16 needs one record
- *                 per (sequence, head, chunk) -- the chunk quantities that do
- *                 not depend on the state (decay factors, (I + A)^-1 diag(beta)
- *                 and the masked Q K^T block, as bf16 hi/lo MFMA fragments;
- *                 21056 bytes at C = 64).  For GDN_F32 the workspace is
- *                 optional: with one of gdn_prefill_workspace_bytes(...)
- *                 bytes (per chunk, (I + A)^-1, P, the masked K K^T and the
- *                 decay prefix in fp32: 49408 bytes at C = 64) the chunk
- *                 quantities are computed once per chunk by a separate kernel
- *                 before the recurrence; with NULL a single kernel computes
- *                 them inside every 16-column value slice.  Too small (or
- *                 missing for GDN_BF16): GDN_ERR_WORKSPACE.  Its contents are
- *                 overwritten; nothing in it is kept between calls.
+ *                 overlapping any other argument: one record per (sequence,
+ *                 head, chunk) of the chunk quantities that do not depend on
+ *                 the state, computed once per chunk by a separate kernel
+ *                 before the recurrence.  GDN_BF16: decay factors,
+ *                 (I + A)^-1 diag(beta) and the masked Q K^T block as bf16
+ *                 hi/lo MFMA fragments (21056 bytes at C = 64).  GDN_F32:
+ *                 (I + A)^-1, P, the masked K K^T and the decay prefix in fp32
+ *                 (49408 bytes at C = 64).  Missing or too small:
+ *                 GDN_ERR_WORKSPACE.  Its contents are overwritten; nothing in
+ *                 it is kept between calls.
  * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
  */
 GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
@@ -162,7 +162,10 @@ GDN_API gdn_status gdn_prefill_recurrence(const void *q, const void *k, const vo
  *                 T=32768, H=32.  Overwritten; nothing kept between calls.
  * Every output must not overlap any input, another output or the workspace.
  * T == 0 writes dinitial_state = dfinal_state (or zeros) and nothing else.
- * All arithmetic is float32 whatever the input dtype.
+ * Precision: every product accumulates in fp32.  For bf16 inputs all four
+ * kernels multiply on bf16 MFMA, with every operand that is not an input
+ * (states, T, P, the chunk matrices, the gradients) split into a bf16 pair
+ * hi + lo; for fp32 inputs the products run on fp32 MFMA.
  */
 GDN_API size_t gdn_prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                                int64_t Dv, int64_t chunk);

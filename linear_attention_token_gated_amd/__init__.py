@@ -129,19 +129,34 @@ def _need(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _same(ref, items):
+    """Every tensor of `items` ((tensor, name, shape) triples; None tensors
+    skipped) has exactly `shape` and lives on the device of `ref`."""
+    for t, name, shape in items:
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _same_device(ref, t, name):
+    if t is not None and t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def prefill_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype="bf16") -> int:
     code = {"f32": 0, "bf16": 1}[dtype]
     return int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), code))
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_final_state: bool = True,
-            y=None, final_state=None, workspace=None, single_kernel: bool = False):
+            y=None, final_state=None, workspace=None):
     """Chunked prefill.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (float32 or bfloat16);
     alpha, beta: [B,T,H] float32; initial_state: [B,H,Dk,Dv] float32 or None.
     workspace: a device buffer of prefill_workspace_bytes(...) bytes, or None
-    to allocate one for this call.  For float32 inputs the workspace selects
-    the two-kernel path; single_kernel=True runs the single-kernel fp32 path
-    without one.
+    to allocate one for this call.
     Returns (y [B,T,H,Dv] float32, final_state or None)."""
     import torch
     B, T, H, Dk = q.shape
@@ -156,11 +171,11 @@ def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_fi
         final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _need(y, "y", torch.float32)
     _need(final_state, "final_state", torch.float32)
+    _same(q, [(k, "k", (B, T, H, Dk)), (v, "v", (B, T, H, Dv)), (alpha, "alpha", (B, T, H)),
+              (beta, "beta", (B, T, H)), (initial_state, "initial_state", (B, H, Dk, Dv)),
+              (y, "y", (B, T, H, Dv)), (final_state, "final_state", (B, H, Dk, Dv))])
+    _same_device(q, workspace, "workspace")
     need = int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _dtype_code(q)))
-    if single_kernel:
-        if _dtype_code(q) != GDN_F32:
-            raise ValueError("single_kernel applies to float32 inputs only")
-        workspace, need = None, 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -180,6 +195,8 @@ def prefill_prepare(q, k, alpha, beta, workspace, chunk: int = 64):
     _need(alpha, "alpha", torch.float32)
     _need(beta, "beta", torch.float32)
     _need(workspace, "workspace")
+    _same(q, [(k, "k", (B, T, H, Dk)), (alpha, "alpha", (B, T, H)), (beta, "beta", (B, T, H))])
+    _same_device(q, workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().gdn_prefill_prepare(_ptr(q), _ptr(k), _ptr(alpha), _ptr(beta), B, T, H, Dk, int(chunk),
                                      _ptr(workspace), ws_bytes, _stream(q.device)))
@@ -202,6 +219,9 @@ def prefill_recurrence(q, k, v, workspace, initial_state=None, chunk: int = 64, 
     _need(y, "y", torch.float32)
     _need(final_state, "final_state", torch.float32)
     _need(workspace, "workspace")
+    _same(q, [(k, "k", (B, T, H, Dk)), (v, "v", (B, T, H, Dv)), (initial_state, "initial_state", (B, H, Dk, Dv)),
+              (y, "y", (B, T, H, Dv)), (final_state, "final_state", (B, H, Dk, Dv))])
+    _same_device(q, workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().gdn_prefill_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(initial_state), _ptr(y), _ptr(final_state),
                                         B, T, H, Dk, Dv, int(chunk), _ptr(workspace), ws_bytes,
@@ -238,6 +258,11 @@ def prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, dfinal_state=None,
         if res.get(n) is None:
             res[n] = torch.empty(shp, dtype=torch.float32, device=q.device)
         _need(res[n], n, torch.float32)
+    _same(q, [(k, "k", (B, T, H, Dk)), (v, "v", (B, T, H, Dv)), (alpha, "alpha", (B, T, H)),
+              (beta, "beta", (B, T, H)), (initial_state, "initial_state", (B, H, Dk, Dv)),
+              (dy, "dy", (B, T, H, Dv)), (dfinal_state, "dfinal_state", (B, H, Dk, Dv))]
+          + [(res[n], n, shp) for n, shp in shapes.items()])
+    _same_device(q, workspace, "workspace")
     need = prefill_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -263,6 +288,8 @@ def decode_step(q, k, v, alpha, beta, state, y=None):
     if y is None:
         y = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
     _need(y, "y", torch.float32)
+    _same(q, [(k, "k", (N, H, Dk)), (v, "v", (N, H, Dv)), (alpha, "alpha", (N, H)), (beta, "beta", (N, H)),
+              (state, "state", (N, H, Dk, Dv)), (y, "y", (N, H, Dv))])
     _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
                                  N, H, Dk, Dv, _dtype_code(q), _stream(q.device)))
     return y
@@ -286,9 +313,20 @@ def decode_verify(q, k, v, alpha, beta, state, states_out=None, y=None):
         states_out = torch.empty((N, T, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _need(y, "y", torch.float32)
     _need(states_out, "states_out", torch.float32)
+    _same(q, [(k, "k", (N, T, H, Dk)), (v, "v", (N, T, H, Dv)), (alpha, "alpha", (N, T, H)),
+              (beta, "beta", (N, T, H)), (state, "state", (N, H, Dk, Dv)), (y, "y", (N, T, H, Dv)),
+              (states_out, "states_out", (N, T, H, Dk, Dv))])
     _check(lib().gdn_decode_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
                                    _ptr(states_out), _ptr(y), N, T, H, Dk, Dv, _dtype_code(q), _stream(q.device)))
     return y, states_out
+
+
+def _layer_param_shapes(params, hidden, H, Dk, Dv, conv_k):
+    nqkv = H * (2 * Dk + Dv)
+    return [(params["W_qkv"], "W_qkv", (nqkv, hidden)), (params["conv_w"], "conv_w", (nqkv, conv_k)),
+            (params["W_ab"], "W_ab", (2 * H, hidden)), (params["A"], "A", (H,)),
+            (params["b_alpha"], "b_alpha", (H,)), (params["W_gate"], "W_gate", (H * Dv, hidden)),
+            (params["norm_gamma"], "norm_gamma", (Dv,)), (params["W_o"], "W_o", (hidden, H * Dv))]
 
 
 def layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k=4, chunk=64) -> int:
@@ -312,6 +350,12 @@ def layer_fwd(x, params: dict, H: int, Dk: int, Dv: int, initial_state=None, chu
         out = torch.empty((B, T, hidden), dtype=torch.float32, device=x.device)
     if final_state is None and return_final_state:
         final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32)
+    _need(final_state, "final_state", torch.float32)
+    _same(x, _layer_param_shapes(params, hidden, H, Dk, Dv, conv_k)
+          + [(initial_state, "initial_state", (B, H, Dk, Dv)), (final_state, "final_state", (B, H, Dk, Dv)),
+             (out, "out", (B, T, hidden))])
+    _same_device(x, workspace, "workspace")
     need = layer_workspace_bytes(B, T, hidden, H, Dk, Dv, conv_k, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -345,6 +389,11 @@ def layer_decode_step(x, params: dict, H: int, Dk: int, Dv: int, conv_state, sta
     if out is None:
         out = torch.empty((N, hidden), dtype=torch.float32, device=x.device)
     _need(out, "out", torch.float32)
+    nqkv = H * (2 * Dk + Dv)
+    _same(x, _layer_param_shapes(params, hidden, H, Dk, Dv, conv_k)
+          + [(conv_state, "conv_state", (N, conv_k - 1, nqkv)), (state, "state", (N, H, Dk, Dv)),
+             (out, "out", (N, hidden))])
+    _same_device(x, workspace, "workspace")
     need = layer_decode_workspace_bytes(N, hidden, H, Dk, Dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)

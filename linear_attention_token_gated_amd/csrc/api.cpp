@@ -172,10 +172,7 @@ gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k
         if (overlap(rs, inputs[i])) return fail(GDN_ERR_ALIAS, "%s: final_state overlaps %s", fn, inputs[i].name);
     if (final_state != initial_state && overlap(rs, inputs[5]))
         return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
-    // fp32: the workspace is optional; given (at least `need` bytes) it selects
-    // the two-kernel path, NULL the single-kernel one
-    size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
-    if (dtype == GDN_F32 && !workspace) need = 0;
+    const size_t need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

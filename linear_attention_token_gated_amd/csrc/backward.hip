@@ -31,8 +31,10 @@
 //             d ln alpha_i = sum_{r >= i} dG_r (within the chunk).
 //
 // Columns of S, dS', V, Y are independent in passes 2 and 3, so those carry a
-// 16-column slice of the state in MFMA accumulators, like the forward.  All
-// arithmetic is fp32 (16x16x4 fp32 MFMA); bf16 inputs are widened on load.
+// 16-column slice of the state in MFMA accumulators, like the forward.  Every
+// product accumulates in fp32.  bf16 inputs: products on bf16 MFMA, with the
+// operands that are not inputs (states, T, P, chunk matrices, gradients) split
+// into bf16 pairs hi + lo; fp32 inputs: fp32 MFMA (16x16x4).
 // Ragged tails are padded with identity tokens (alpha = 1, beta = 0, zeros),
 // whose gradients are never written.
 #include "common.hpp"
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     if (wave == 0) {
         const int64_t t = c0 + lane;
         const bool ok = lane < C && t < T;
-        const float g2 = ok ? __builtin_amdgcn_logf(p.alpha[(b * T + t) * H + h]) : 0.f;
+        const float g2 = ok ? log2_decay(p.alpha[(b * T + t) * H + h]) : 0.f;
         const float G2 = wave_inclusive_sum(g2, lane);
         if (lane < C) {
             Gs[lane] = G2;

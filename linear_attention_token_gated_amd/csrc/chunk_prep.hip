@@ -148,7 +148,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         const bool real = lane < C && t0 + lane < p.T;
         al = real ? al : 1.f;
         be = real ? be : 0.f;
-        const float g2 = wave_inclusive_sum(lane < C ? __builtin_amdgcn_logf(al) : 0.f, lane);
+        const float g2 = wave_inclusive_sum(lane < C ? log2_decay(al) : 0.f, lane);
         const float gC = lane_value(g2, C - 1);
         const float gblk = row_bcast<0>(g2);
         float *dec = reinterpret_cast<float *>(out + Rec::oDec);

@@ -132,6 +132,13 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// log2 of a decay alpha in [0, 1], floored at -126: alpha = 0 (or a subnormal
+// alpha) acts as 2^-126, a decay that leaves less than 1.2e-38 of the state,
+// instead of -inf, which would turn the decay ratios 2^(G_r - G_j) into NaN.
+__device__ __forceinline__ float log2_decay(float alpha) {
+    return fmaxf(__builtin_amdgcn_logf(alpha), -126.f);
+}
+
 // Broadcast lane S of every 16-lane row to the whole row (DPP row_newbcast).
 // Every lane has a valid source, so no old value is needed (bound_ctrl set):
 // the move then carries no extra copy and no wait state of its own.

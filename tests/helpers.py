@@ -40,3 +40,45 @@ def oracle_prefill(oracle, inp, S0=None):
     return oracle.gdn_recurrence(wl.widen(inp["q"]), wl.widen(inp["k"]), wl.widen(inp["v"]),
                                  wl.widen(inp["alpha"]), wl.widen(inp["beta"]),
                                  wl.widen(inp["S0"]) if S0 is None else S0)
+
+
+def gate_endpoint_inputs(case, B, T, H, Dk, Dv, dtype, seed):
+    """Prefill inputs of the recipe with the gates (and for some cases the keys)
+    moved to the ends of their ranges:
+
+    beta1_qk      beta = 1 and q = k: the read-out of each token is its own key
+    ortho         alpha = beta = 1 and, per (sequence, head), orthonormal keys
+                  (T <= Dk): key-to-value retrieval
+    beta_near1    beta ~ U(0.95, 1)
+    alpha1        alpha = 1 (no decay), beta of the recipe
+    alpha0        alpha of the recipe with every 7th token exactly 0 and every
+                  11th token subnormal (1e-40): the state is reset there
+    """
+    inp = wl.prefill_inputs(B, T, H, Dk, Dv, dtype="f32", s0_std=0.05, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    q, k = inp["q"], inp["k"]
+    if case == "beta1_qk":
+        inp["beta"] = np.ones_like(inp["beta"])
+        q = k.copy()
+    elif case == "ortho":
+        assert T <= Dk
+        inp["alpha"] = np.ones_like(inp["alpha"])
+        inp["beta"] = np.ones_like(inp["beta"])
+        for b in range(B):
+            for h in range(H):
+                m, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+                k[b, :, h] = m[:T].astype(np.float32)
+    elif case == "beta_near1":
+        inp["beta"] = rng.uniform(0.95, 1.0, inp["beta"].shape).astype(np.float32)
+    elif case == "alpha1":
+        inp["alpha"] = np.ones_like(inp["alpha"])
+    elif case == "alpha0":
+        a = inp["alpha"].copy()
+        a[:, ::7] = 0.0
+        a[:, 3::11] = np.float32(1e-40)
+        inp["alpha"] = a
+    else:
+        raise ValueError(case)
+    cast = (lambda x: wl.to_bf16_bits(x)) if dtype == "bf16" else (lambda x: np.ascontiguousarray(x, np.float32))
+    inp.update(q=cast(q), k=cast(k), v=cast(inp["v"]), dtype=dtype)
+    return inp

@@ -100,10 +100,11 @@ def recurrence(L, q=A, k=A + 64 * MB, v=A + 128 * MB, s0=None, y=A + 256 * MB, s
     return L.gdn_prefill_recurrence(q, k, v, s0, y, sT, B, T, H, Dk, Dv, C, w, wb, None)
 
 
-def test_prefill_f32_optional_workspace(L):
+def test_prefill_f32_workspace_required(L):
     need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 0)
     assert need == 4 * 2 * 4 * 832
     ws = A + 512 * MB
+    assert prefill(L) == WS                             # fp32 needs the record workspace too
     assert prefill(L, w=ws, wb=need - 1) == WS          # given but too small
     assert prefill(L, w=ws + 16, wb=need) == ALIGN      # given but misaligned
     assert prefill(L, w=A + 256 * MB, wb=need) == ALIAS  # over y
@@ -274,3 +275,24 @@ def test_prefill_bwd_validation(L):
     assert "gdn_prefill_bwd" in L.gdn_last_error().decode()
     # T == 0 needs no workspace and checks only what it writes
     assert prefill_bwd(L, T=0, w=None, wb=0, q=None, dq=None, ds0=A + 26 * MB) == ALIAS
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks every tensor's shape and device against the sizes it
+    derives from q (or x) before any C call: a mismatched tensor would
+    otherwise become an out-of-bounds device access."""
+    import torch
+    q = torch.zeros(1, 8, 2, 16)
+    ok = [(torch.zeros(1, 8, 2, 16), "k", (1, 8, 2, 16)), (None, "initial_state", (1, 2, 16, 16))]
+    gdn._same(q, ok)
+    with pytest.raises(ValueError, match="k has shape"):
+        gdn._same(q, [(torch.zeros(1, 8, 2, 32), "k", (1, 8, 2, 16))])
+    with pytest.raises(ValueError, match="alpha has shape"):
+        gdn._same(q, [(torch.zeros(1, 8, 3), "alpha", (1, 8, 2))])
+    params = {"W_qkv": torch.zeros(96, 64), "conv_w": torch.zeros(96, 4), "W_ab": torch.zeros(4, 64),
+              "A": torch.zeros(2), "b_alpha": torch.zeros(2), "W_gate": torch.zeros(32, 64),
+              "norm_gamma": torch.zeros(16), "W_o": torch.zeros(64, 32)}
+    gdn._same(q, gdn._layer_param_shapes(params, 64, 2, 16, 16, 4))
+    params["W_o"] = torch.zeros(32, 64)
+    with pytest.raises(ValueError, match="W_o has shape"):
+        gdn._same(q, gdn._layer_param_shapes(params, 64, 2, 16, 16, 4))

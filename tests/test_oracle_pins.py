@@ -6,7 +6,7 @@ and a hand-worked example; none of them re-types the oracle's loop.
 
 Source of the recurrence: "On the Design of Qwen3.8-Next Architecture", picx.dev
 summary, section "Theoretical foundations", eqs (1)-(4) (alpha, beta in (0,1);
-the delta term writes only the residual error).  Non-square d_k != d_v shapes
+eq (3) adds beta k e^T, where e is the prediction error of eq (2)).  Non-square d_k != d_v shapes
 are used throughout so that a transposed state cannot pass.
 """
 import numpy as np
