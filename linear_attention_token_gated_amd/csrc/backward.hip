@@ -60,9 +60,11 @@ struct BwdParams {
     int xcd_map;               // state passes: the slices of one head on one XCD (B*H % 8 == 0)
 };
 
-// ---- per-chunk record: T [C][C], P [C][C], Ak [C][C], G2 [C] (log2 cumulative decay)
+// ---- per-chunk record: T [C][C], P [C][C], Ak [C][C], G2 [C] (log2 cumulative
+// decay), Ed [C] = 2^(G2_{C-1} - G2_r) (formed from the fp64 prefix, so that it
+// keeps full precision when G2 itself is large)
 template <int C> struct Rec {
-    static constexpr int oT = 0, oP = C * C, oA = 2 * C * C, oG = 3 * C * C;
+    static constexpr int oT = 0, oP = C * C, oA = 2 * C * C, oG = 3 * C * C, oEd = 3 * C * C + C;
 };
 
 // Register-staged copies into LDS.  Every load of a tile is issued before any
@@ -196,15 +198,15 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     constexpr size_t oQ = NPART * KQB;
     constexpr size_t QREG = F32IN ? (NPART * KQB > 2 * ATB ? NPART * KQB : 2 * ATB) : NPART * KQB;
     constexpr size_t oA = F32IN ? oQ : oQ + QREG, oT = oA + ATB;
-    constexpr size_t oG = F32IN ? oQ + QREG : oT + ATB, BYTES = oG + 8 * C;
+    constexpr size_t oG = F32IN ? oQ + QREG : oT + ATB, BYTES = oG + 12 * C;   // G (fp64), beta
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char smem[BYTES];
     __bf16 *Ks = reinterpret_cast<__bf16 *>(smem);                 // part j at Ks + j * C * KP
     __bf16 *Qs = reinterpret_cast<__bf16 *>(smem + oQ);
     float *As = reinterpret_cast<float *>(smem + oA);
     float *Ts = reinterpret_cast<float *>(smem + oT);
-    float *Gs = reinterpret_cast<float *>(smem + oG);
-    float *Bs = Gs + C;
+    double *Gs = reinterpret_cast<double *>(smem + oG);
+    float *Bs = reinterpret_cast<float *>(Gs + C);
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
     const int64_t bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
@@ -234,11 +236,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
         const int64_t t = c0 + lane;
         const bool ok = lane < C && t < T;
         const float g2 = ok ? log2_decay(p.alpha[(b * T + t) * H + h]) : 0.f;
-        const float G2 = wave_inclusive_sum(g2, lane);
+        const double G2 = wave_inclusive_sum_f64((double)g2, lane);
+        const double GC = lane_value_f64(G2, C - 1);
         if (lane < C) {
             Gs[lane] = G2;
             Bs[lane] = ok ? p.beta[(b * T + t) * H + h] : 0.f;
-            rec[Rec<C>::oG + lane] = G2;
+            rec[Rec<C>::oG + lane] = (float)G2;
+            rec[Rec<C>::oEd + lane] = __builtin_amdgcn_exp2f((float)(GC - G2));
         }
     }
     // blocks above the diagonal: zero in the record
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * lg + e;
-            const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gs[j], 0.f));
+            const float gam = __builtin_amdgcn_exp2f((float)fmin(Gs[r] - Gs[j], 0.0));
             rec[Rec<C>::oP + r * C + j] = r >= j ? gam * acc[e] : 0.f;
         }
     }
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * lg + e;
-            const float gam = __builtin_amdgcn_exp2f(fminf(Gs[r] - Gs[j], 0.f));
+            const float gam = __builtin_amdgcn_exp2f((float)fmin(Gs[r] - Gs[j], 0.0));
             const float ak = r > j ? gam * acc[e] : 0.f;
             rec[Rec<C>::oA + r * C + j] = ak;
             As[r * CP + j] = Bs[r] * ak;
@@ -1775,7 +1779,8 @@ template <int C, int DK> struct Fwd32Lay {
     static constexpr size_t oUd = oU + 4 * C * VP;
     static constexpr size_t oG = oUd + 4 * BV * CP;
     static constexpr size_t oB = oG + 4 * C;
-    static constexpr size_t BYTES = oB + 4 * C;
+    static constexpr size_t oEd = oB + 4 * C;
+    static constexpr size_t BYTES = oEd + 4 * C;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -1801,6 +1806,7 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
     float *UdT = reinterpret_cast<float *>(smem + L::oUd);
     float *Gs = reinterpret_cast<float *>(smem + L::oG);
     float *Bs = reinterpret_cast<float *>(smem + L::oB);
+    float *Eds = reinterpret_cast<float *>(smem + L::oEd);
 
     const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
     const int64_t NS = p.Dv / BV;
@@ -1823,7 +1829,7 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
     RowsTile<float, C, DK> rk, rq;
     DenseTile<C, C> rt, rp;
     RowsTile<float, C, BV> ri;
-    float rg = 0.f, rbeta = 0.f;
+    float rg = 0.f, rbeta = 0.f, red = 0.f;
     auto fetch = [&](int64_t c) {
         const int64_t c0 = c * C;
         const float *rec = p.rec + (bh * NC + c) * p.rec_floats;
@@ -1835,6 +1841,7 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
         if (threadIdx.x < C) {
             const int64_t t = c0 + threadIdx.x;
             rg = rec[Rec<C>::oG + threadIdx.x];
+            red = rec[Rec<C>::oEd + threadIdx.x];
             rbeta = t < T ? p.beta[(b * T + t) * H + h] : 0.f;
         }
     };
@@ -1850,6 +1857,7 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
         if (threadIdx.x < C) {
             Gs[threadIdx.x] = rg;
             Bs[threadIdx.x] = rbeta;
+            Eds[threadIdx.x] = red;
         }
         if (c + 1 < NC) fetch(c + 1);
 #pragma unroll
@@ -1893,7 +1901,7 @@ __global__ __launch_bounds__(NT) void fwd32_carry_kernel(BwdParams p)
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * lg + e;
                 Us[r * VP + ln] = acc[e];
-                UdT[ln * CP + r] = __builtin_amdgcn_exp2f(GC - Gs[r]) * acc[e];
+                UdT[ln * CP + r] = Eds[r] * acc[e];
             }
         }
         lds_barrier();
@@ -1957,7 +1965,8 @@ template <int C, int DK> struct Fwd16Lay {
     static constexpr size_t oIn = oDl + TB;
     static constexpr size_t oG = oIn + 4 * C * VP;                 // G2, two buffers
     static constexpr size_t oB = oG + 2 * 4 * C;                   // beta, two buffers
-    static constexpr size_t BYTES = oB + 2 * 4 * C;
+    static constexpr size_t oEd = oB + 2 * 4 * C;                  // 2^(G2_{C-1} - G2), two buffers
+    static constexpr size_t BYTES = oEd + 2 * 4 * C;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -1997,6 +2006,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
     float *Ins = reinterpret_cast<float *>(smem + L::oIn);
     float *Gb = reinterpret_cast<float *>(smem + L::oG);
     float *Bb = reinterpret_cast<float *>(smem + L::oB);
+    float *Edb = reinterpret_cast<float *>(smem + L::oEd);
 
     const int lane = lane_id(), wave = wave_id(), ln = lane & 15, lg = lane >> 4;
     const bool chain = wave < 4;
@@ -2019,7 +2029,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
         auto clampc = [&](int64_t c) { return c >= NC ? NC - 1 : c; };
         auto rec_of = [&](int64_t c) { return p.rec + (bh * NC + c) * p.rec_floats; };
         f32x4 rK[NVK], rQ[NVK], rT[NVT], rP[NVT], rV = zero4();
-        float rG = 0.f, rBe = 0.f;
+        float rG = 0.f, rBe = 0.f, rEd = 0.f;
         int64_t cKQ = 0;                                   // chunk held by rK, rQ, rV, rG, rBe
         const int uv = ts < NUV ? ts : NUV - 1, ug = ts < C ? ts : C - 1;
         auto load_kqv = [&](int64_t c) {
@@ -2039,6 +2049,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
             rV = *reinterpret_cast<const f32x4 *>(vg + (b * T + tv) * p.vs + h * Dv + n0 + cv);
             const int64_t tg = c0 + ug < T ? c0 + ug : T - 1;
             rG = rec_of(c)[Rec<C>::oG + ug];
+            rEd = rec_of(c)[Rec<C>::oEd + ug];
             rBe = p.beta[(b * T + tg) * H + h];
         };
         auto load_cc = [&](f32x4 (&rr)[NVT], int64_t c, int off) {
@@ -2068,6 +2079,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
             }
             if (ts < C) {
                 Gb[gb * C + ts] = rG;
+                Edb[gb * C + ts] = rEd;
                 Bb[gb * C + ts] = cKQ * C + ts < T ? rBe : 0.f;
             }
         };
@@ -2127,7 +2139,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
         lds_barrier();                                  // B1 of chunk 0
         for (int64_t c = 0; c < NC; ++c) {
             const int64_t c0 = c * C;
-            const float *Gs = Gb + (c & 1) * C, *Bs = Bb + (c & 1) * C;
+            const float *Gs = Gb + (c & 1) * C, *Bs = Bb + (c & 1) * C, *Eds = Edb + (c & 1) * C;
             const float GC = Gs[C - 1];
 
             // ---- step 1: K S, Q S;  X = diag(beta)(V - e^G K S); the K^T
@@ -2192,7 +2204,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
                 store_split4(Uh + ln * CP + r0, Ul + ln * CP + r0, acc);
                 f32x4 d;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(GC - Gs[r0 + e]) * acc[e];
+                for (int e = 0; e < 4; ++e) d[e] = Eds[r0 + e] * acc[e];
                 store_split4(Dh + ln * CP + r0, Dl + ln * CP + r0, d);
             }
             lds_barrier();                              // B3
@@ -2361,7 +2373,7 @@ __global__ void copy_or_zero(const float *__restrict__ src, float *__restrict__ 
 
 }  // namespace
 
-int64_t bwd_record_floats(int64_t C) { return (3 * C * C + C + 63) / 64 * 64; }
+int64_t bwd_record_floats(int64_t C) { return (3 * C * C + 2 * C + 63) / 64 * 64; }
 
 size_t prefill_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C)
 {

@@ -187,6 +187,33 @@ __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 }
 
 
+// The same inclusive prefix sum in fp64.  The decay prefixes G_r of a chunk
+// are summed in fp64 so that differences G_r - G_j keep their precision when
+// the prefix itself is large (several alpha near 0 in one chunk); DPP moves
+// 32 bits, so each shift moves the two halves of the double.
+template <int N> __device__ __forceinline__ double row_shr_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x110 + N, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x110 + N, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double lane_value_f64(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_inclusive_sum_f64(double x, int lane) {
+    x += row_shr_f64<1>(x);
+    x += row_shr_f64<2>(x);
+    x += row_shr_f64<4>(x);
+    x += row_shr_f64<8>(x);
+    const double t0 = lane_value_f64(x, 15), t1 = lane_value_f64(x, 31), t2 = lane_value_f64(x, 47);
+    const int row = lane >> 4;
+    const double base = row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+    return x + base;
+}
+
 // Forward substitution of (I + L) X = I for a 16x16 strictly lower L, inside
 // one wavefront.  Lane (r = l%16, g = l/16) owns row r of X, columns g+4i.
 // Step s: row s is final; every row r > s subtracts L[r][s] * X[s][:].

@@ -222,7 +222,7 @@ def test_workspace_queries(L):
     assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
     assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
     # fp32: optional records of the two-kernel path, 3*64*64+64 floats per chunk
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 4 * 32 * 512 * 12352
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 4 * 32 * 512 * 12416
     assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
     assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
     assert L.gdn_layer_workspace_bytes(1, 0, 2048, 16, 128, 128, 4, 64) == 0
@@ -254,7 +254,7 @@ def test_prefill_bwd_validation(L):
     # per chunk: a record of 3*16*16+16 floats (rounded up to 64), two 16x16
     # states and three 16x16 chunk matrices
     assert need == 4 * 2 * 4 * (832 + 2 * 256 + 3 * 256)
-    assert L.gdn_prefill_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64) == 4 * 32 * 64 * (12352 + 2 * 16384 + 3 * 8192)
+    assert L.gdn_prefill_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64) == 4 * 32 * 64 * (12416 + 2 * 16384 + 3 * 8192)
     assert L.gdn_prefill_bwd_workspace_bytes(1, 0, 2, 16, 16, 16) == 0
     assert L.gdn_prefill_bwd_workspace_bytes(1, 64, 2, 48, 16, 16) == 0
     assert prefill_bwd(L, q=None) == NULL
