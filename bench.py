@@ -58,28 +58,6 @@ def prefill_alg(B, T, H, Dk, Dv, C, has_s0=False):
     return b_bf16_y, b_fp32_y, tok * f_alg, tok * f_tile
 
 
-def record_bytes(C):
-    """Bytes of one per-chunk record of the preparation kernel: T' and P as
-    bf16 hi/lo 16x16 blocks (C/16 (C/16 + 1) / 2 of each, 1 KB per block),
-    then the decay vectors (2C + 16 floats)."""
-    nb = C // 16
-    return 2 * (nb * (nb + 1) // 2) * 1024 + (2 * C + 16) * 4
-
-
-def prep_alg(B, T, H, Dk, C, in_bytes=2):
-    """Preparation kernel: q, k, alpha, beta read once, one record written per
-    (sequence, head, chunk)."""
-    return B * T * H * (2 * Dk * in_bytes + 8) + B * H * (-(-T // C)) * record_bytes(C)
-
-
-def recurrence_alg(B, T, H, Dk, Dv, C, in_bytes=2, has_s0=False):
-    """Recurrence kernel: q, k, v and the records read once, y (fp32) and the
-    final state written once."""
-    tok = B * T * H
-    return (tok * ((2 * Dk + Dv) * in_bytes + 4 * Dv) + B * H * (-(-T // C)) * record_bytes(C)
-            + B * H * Dk * Dv * 4 * (2 if has_s0 else 1))
-
-
 def decode_alg(N, H, Dk, Dv, in_bytes=2):
     """State read + written once, q/k/v/alpha/beta read, y (fp32) written."""
     per = 8 * Dk * Dv + (2 * Dk + Dv) * in_bytes + 8 + 4 * Dv
@@ -155,9 +133,7 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/recurrence.hip",
-                   "linear_attention_token_gated_amd/csrc/chunk_prep.hip",
-                   "linear_attention_token_gated_amd/csrc/prep_layout.hpp",
+PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill_fused.hip",
                    "linear_attention_token_gated_amd/csrc/common.hpp"]
 
 
@@ -167,7 +143,7 @@ DECODE_SOURCES = ["linear_attention_token_gated_amd/csrc/decode.hip"]
 # counter keys: the kernels whose FETCH_SIZE + WRITE_SIZE add up to one launch
 # of the workload, and the sources whose hash the stored counts were taken on
 TRAFFIC_KERNELS = {
-    "prefill_32k": (["gdn_chunk_prep_kernel", "gdn_recurrence_kernel"], PREFILL_SOURCES),
+    "prefill_32k": (["gdn_prefill_fused_kernel"], PREFILL_SOURCES),
     "decode_256x32": (["gdn_decode_kernel"], DECODE_SOURCES),
 }
 

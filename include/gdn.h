@@ -74,18 +74,16 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   B, H, T >= 0; B*H == 0 or T == 0 launch nothing except, for T == 0,
  *   final_state = initial_state (or zeros).  Any T is accepted: a ragged last
  *   chunk is padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
- *   workspace     device scratch of at least gdn_prefill_workspace_bytes(...)
- *                 bytes, 256-byte aligned, owned by the caller and not
- *                 overlapping any other argument: one record per (sequence,
- *                 head, chunk) of the chunk quantities that do not depend on
- *                 the state, computed once per chunk by a separate kernel
- *                 before the recurrence.  GDN_BF16: decay factors,
- *                 (I + A)^-1 diag(beta) and the masked Q K^T block as bf16
- *                 hi/lo MFMA fragments (21056 bytes at C = 64).  GDN_F32:
- *                 (I + A)^-1, P, the masked K K^T and the decay prefix in fp32
- *                 (49408 bytes at C = 64).  Missing or too small:
- *                 GDN_ERR_WORKSPACE.  Its contents are overwritten; nothing in
- *                 it is kept between calls.
+ *   workspace     GDN_BF16: none (NULL, 0): one kernel forms every chunk
+ *                 quantity on chip.  GDN_F32: device scratch of at least
+ *                 gdn_prefill_workspace_bytes(...) bytes, 256-byte aligned,
+ *                 owned by the caller and not overlapping any other argument:
+ *                 one record per (sequence, head, chunk) of the quantities that
+ *                 do not depend on the state ((I + A)^-1, P, the masked K K^T,
+ *                 the decay prefix and 2^(G_C - G); 49664 bytes at C = 64),
+ *                 computed by a separate kernel before the recurrence.
+ *                 Missing or too small: GDN_ERR_WORKSPACE.  Its contents are
+ *                 overwritten; nothing in it is kept between calls.
  * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
  */
 GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
@@ -98,40 +96,10 @@ GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
                            hipStream_t stream);
 
 /* Bytes of workspace gdn_prefill_fwd needs for these sizes: B*H*ceil(T/C)
- * records for GDN_BF16, 0 for GDN_F32, for empty problems and for arguments
+ * records for GDN_F32; 0 for GDN_BF16, for empty problems and for arguments
  * gdn_prefill_fwd would reject. */
 GDN_API size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                    int64_t Dv, int64_t chunk, gdn_dtype dtype);
-
-/*
- * The two stages of gdn_prefill_fwd for bf16 inputs, for callers that want to
- * schedule or time them apart (one after the other on a stream, they are
- * exactly gdn_prefill_fwd).  Arguments mean what they mean there.
- *
- * gdn_prefill_prepare -- the part of each chunk that depends on neither the
- * state nor v (decay prefix, (I + A)^-1 diag(beta), the masked Q K^T of the
- * chunk form of eqs (1)-(4)), for every (sequence, head, chunk) in parallel,
- * written into `workspace` (gdn_prefill_workspace_bytes(..., GDN_BF16) bytes,
- * 256-byte aligned).  q, k: [B, T, H, Dk] bf16; alpha, beta: [B, T, H].
- *
- * gdn_prefill_recurrence -- the state recurrence over the chunks, reading the
- * workspace written by gdn_prefill_prepare for the same q, k, alpha, beta and
- * sizes (not checked: other contents give meaningless output, never an
- * out-of-bounds access).  q, k, v, initial_state, y, final_state as in
- * gdn_prefill_fwd, bf16 inputs.
- *
- * Errors as gdn_prefill_fwd's; on a non-OK status nothing was launched.
- */
-GDN_API gdn_status gdn_prefill_prepare(const void *q, const void *k, const float *alpha,
-                                       const float *beta, int64_t B, int64_t T, int64_t H,
-                                       int64_t Dk, int64_t chunk, void *workspace,
-                                       size_t workspace_bytes, hipStream_t stream);
-GDN_API gdn_status gdn_prefill_recurrence(const void *q, const void *k, const void *v,
-                                          const float *initial_state, float *y,
-                                          float *final_state, int64_t B, int64_t T, int64_t H,
-                                          int64_t Dk, int64_t Dv, int64_t chunk,
-                                          const void *workspace, size_t workspace_bytes,
-                                          hipStream_t stream);
 
 /*
  * gdn_prefill_bwd -- gradients of gdn_prefill_fwd: the reverse mode of eqs

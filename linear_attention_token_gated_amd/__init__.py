@@ -28,8 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
-EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_prepare", "gdn_prefill_recurrence",
-            "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes",
+EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes",
             "gdn_decode_step", "gdn_decode_verify", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
             "gdn_layer_decode_workspace_bytes", "gdn_status_str", "gdn_last_error")
 
@@ -65,10 +64,6 @@ def lib():
     L.gdn_prefill_fwd.restype = ctypes.c_int
     L.gdn_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.gdn_prefill_workspace_bytes.restype = sz
-    L.gdn_prefill_prepare.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
-    L.gdn_prefill_prepare.restype = ctypes.c_int
-    L.gdn_prefill_recurrence.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
-    L.gdn_prefill_recurrence.restype = ctypes.c_int
     L.gdn_prefill_bwd.argtypes = [vp] * 14 + [i64] * 6 + [ctypes.c_int, vp, sz, vp]
     L.gdn_prefill_bwd.restype = ctypes.c_int
     L.gdn_prefill_bwd_workspace_bytes.argtypes = [i64] * 6
@@ -182,50 +177,6 @@ def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_fi
     _check(lib().gdn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
                                  _ptr(y), _ptr(final_state), B, T, H, Dk, Dv, int(chunk), _dtype_code(q),
                                  _ptr(workspace), ws_bytes, _stream(q.device)))
-    return y, final_state
-
-
-def prefill_prepare(q, k, alpha, beta, workspace, chunk: int = 64):
-    """First stage of the bf16 prefill: per-chunk records into `workspace`
-    (a uint8 device buffer of prefill_workspace_bytes(...) bytes)."""
-    import torch
-    B, T, H, Dk = q.shape
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(alpha, "alpha", torch.float32)
-    _need(beta, "beta", torch.float32)
-    _need(workspace, "workspace")
-    _same(q, [(k, "k", (B, T, H, Dk)), (alpha, "alpha", (B, T, H)), (beta, "beta", (B, T, H))])
-    _same_device(q, workspace, "workspace")
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().gdn_prefill_prepare(_ptr(q), _ptr(k), _ptr(alpha), _ptr(beta), B, T, H, Dk, int(chunk),
-                                     _ptr(workspace), ws_bytes, _stream(q.device)))
-
-
-def prefill_recurrence(q, k, v, workspace, initial_state=None, chunk: int = 64, y=None, final_state=None,
-                       return_final_state: bool = True):
-    """Second stage of the bf16 prefill, reading the records prefill_prepare
-    wrote for the same inputs.  Returns (y, final_state or None)."""
-    import torch
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16)
-    _need(initial_state, "initial_state", torch.float32)
-    if y is None:
-        y = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
-    if final_state is None and return_final_state:
-        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    _need(y, "y", torch.float32)
-    _need(final_state, "final_state", torch.float32)
-    _need(workspace, "workspace")
-    _same(q, [(k, "k", (B, T, H, Dk)), (v, "v", (B, T, H, Dv)), (initial_state, "initial_state", (B, H, Dk, Dv)),
-              (y, "y", (B, T, H, Dv)), (final_state, "final_state", (B, H, Dk, Dv))])
-    _same_device(q, workspace, "workspace")
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().gdn_prefill_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(initial_state), _ptr(y), _ptr(final_state),
-                                        B, T, H, Dk, Dv, int(chunk), _ptr(workspace), ws_bytes,
-                                        _stream(q.device)))
     return y, final_state
 
 

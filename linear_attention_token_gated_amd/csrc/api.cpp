@@ -9,7 +9,6 @@
 
 #include "../../include/gdn.h"
 #include "launch.hpp"
-#include "prep_layout.hpp"
 
 namespace {
 
@@ -103,25 +102,17 @@ const char *gdn_last_error(void) { return g_err; }
 size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                                    gdn_dtype dtype)
 {
-    if (B <= 0 || T <= 0 || H <= 0 || (dtype != GDN_BF16 && dtype != GDN_F32) || !is_pow2_dim(Dk) ||
-        !is_pow2_dim(Dv) || (chunk != 16 && chunk != 32 && chunk != 64))
-        return 0;
+    if (B <= 0 || T <= 0 || H <= 0 || dtype != GDN_F32 || !is_pow2_dim(Dk) || !is_pow2_dim(Dv) ||
+        (chunk != 16 && chunk != 32 && chunk != 64))
+        return 0;        // bf16 needs none; nothing for empty or rejected problems
     int64_t n;
-    if (dtype == GDN_F32) {
-        if (!count(&n, {B, H, (T + chunk - 1) / chunk, gdn::bwd_record_floats(chunk), 4})) return 0;
-        return gdn::prefill_f32_workspace_bytes(B, T, H, chunk);
-    }
-    if (!count(&n, {B, H, (T + chunk - 1) / chunk, (int64_t)gdn::prep_record_bytes(chunk)})) return 0;
-    return gdn::prefill_workspace_bytes(B, T, H, chunk, true);
+    if (!count(&n, {B, H, (T + chunk - 1) / chunk, gdn::bwd_record_floats(chunk), 4})) return 0;
+    return gdn::prefill_f32_workspace_bytes(B, T, H, chunk);
 }
 
 namespace {
 
-constexpr int STAGE_PREP = 1, STAGE_REC = 2;
-
-// gdn_prefill_fwd and its two stages: `stages` selects the chunk preparation
-// (bf16 only), the recurrence, or both; `fn` names the entry point in errors.
-gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k, const void *v,
+gdn_status prefill_impl(const char *fn, const void *q, const void *k, const void *v,
                         const float *alpha, const float *beta, const float *initial_state, float *y,
                         float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                         int64_t chunk, gdn_dtype dtype, void *workspace, size_t workspace_bytes,
@@ -147,13 +138,8 @@ gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k
     if (dtype == GDN_BF16 && chunk * H * (Dk > Dv ? Dk : Dv) * 2 >= ((int64_t)1 << 31))
         return fail(GDN_ERR_UNSUPPORTED, "%s: H=%lld too large for bf16 (chunk * H * max(Dk, Dv) * 2 must stay below 2^31)", fn,
                     (long long)H);
-    if (stages != (STAGE_PREP | STAGE_REC) && dtype != GDN_BF16)
-        return fail(GDN_ERR_UNSUPPORTED, "%s: the separate stages exist for bf16 inputs only", fn);
-    if (n_tok > 0) {
-        if (!q || !k) return fail(GDN_ERR_NULL, "%s: q and k are required", fn);
-        if ((stages & STAGE_PREP) && (!alpha || !beta)) return fail(GDN_ERR_NULL, "%s: alpha and beta are required", fn);
-        if ((stages & STAGE_REC) && (!v || !y)) return fail(GDN_ERR_NULL, "%s: v and y are required", fn);
-    }
+    if (n_tok > 0 && (!q || !k || !v || !alpha || !beta || !y))
+        return fail(GDN_ERR_NULL, "%s: q, k, v, alpha, beta and y are required", fn);
     const void *ptrs[] = {q, k, v, alpha, beta, initial_state, y, final_state};
     const char *names[] = {"q", "k", "v", "alpha", "beta", "initial_state", "y", "final_state"};
     for (int i = 0; i < 8; ++i)
@@ -193,7 +179,7 @@ gdn_status prefill_impl(const char *fn, int stages, const void *q, const void *k
     a.q_tok_stride = H * Dk; a.k_tok_stride = H * Dk; a.v_tok_stride = H * Dv;
     a.bf16 = dtype == GDN_BF16;
     a.ws = need > 0 ? workspace : nullptr;
-    return hip_status(gdn::launch_prefill(a, stream, stages), fn, stream);
+    return hip_status(gdn::launch_prefill(a, stream), fn, stream);
 }
 
 }  // namespace
@@ -204,26 +190,8 @@ gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v, const fl
                            int64_t Dv, int64_t chunk, gdn_dtype dtype, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
-    return prefill_impl("gdn_prefill_fwd", STAGE_PREP | STAGE_REC, q, k, v, alpha, beta, initial_state, y,
-                        final_state, B, T, H, Dk, Dv, chunk, dtype, workspace, workspace_bytes, stream);
-}
-
-gdn_status gdn_prefill_prepare(const void *q, const void *k, const float *alpha, const float *beta,
-                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t chunk,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream)
-{
-    return prefill_impl("gdn_prefill_prepare", STAGE_PREP, q, k, nullptr, alpha, beta, nullptr, nullptr, nullptr,
-                        B, T, H, Dk, Dk, chunk, GDN_BF16, workspace, workspace_bytes, stream);
-}
-
-gdn_status gdn_prefill_recurrence(const void *q, const void *k, const void *v, const float *initial_state,
-                                  float *y, float *final_state, int64_t B, int64_t T, int64_t H, int64_t Dk,
-                                  int64_t Dv, int64_t chunk, const void *workspace, size_t workspace_bytes,
-                                  hipStream_t stream)
-{
-    return prefill_impl("gdn_prefill_recurrence", STAGE_REC, q, k, v, nullptr, nullptr, initial_state, y,
-                        final_state, B, T, H, Dk, Dv, chunk, GDN_BF16, const_cast<void *>(workspace),
-                        workspace_bytes, stream);
+    return prefill_impl("gdn_prefill_fwd", q, k, v, alpha, beta, initial_state, y, final_state, B, T, H, Dk,
+                        Dv, chunk, dtype, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,

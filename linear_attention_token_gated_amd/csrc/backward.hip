@@ -2345,10 +2345,15 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
     const int64_t bh = a.B * a.H;
     const unsigned nchunk = (unsigned)(bh * kp.NC), nslice = (unsigned)(bh * (a.Dv / BV));
     hipLaunchKernelGGL((bwd_prep_kernel<float, C, DK>), dim3(nchunk), dim3(NT), 0, stream, kp);
-    if constexpr (DK % 32 == 0 && C % 32 == 0)
-        hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
-    else
-        hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
+    // fp32 MFMA unless the caller's bound is the bf16 one (hi/lo operands carry
+    // about 16 bits, which an fp32-input run with a small RMS(y) can exceed)
+    if constexpr (DK % 32 == 0 && C % 32 == 0) {
+        if (a.hilo_core) {
+            hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((fwd32_carry_kernel<C, DK>), dim3(nslice), dim3(NT), 0, stream, kp);
     return hipGetLastError();
 }
 

@@ -29,7 +29,11 @@ struct PrefillArgs {
     int64_t B, T, H, Dk, Dv, chunk;
     int64_t q_tok_stride, k_tok_stride, v_tok_stride;   // elements per token (all heads)
     bool bf16;
-    void *ws;                       // bf16: prefill_workspace_bytes(...) bytes, 256-byte aligned
+    void *ws;                       // fp32: prefill_f32_workspace_bytes(...) bytes, 256-byte aligned
+    // fp32 inputs: the caller's bound is the bf16 one (the layer's core), so the
+    // recurrence may run on bf16 MFMA with hi/lo operands (about 16 bits of each
+    // operand) instead of fp32 MFMA
+    bool hilo_core = false;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -45,13 +49,10 @@ struct VerifyArgs {
     bool bf16;
 };
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
-// stages: 1 = chunk preparation (bf16), 2 = recurrence, 3 = both
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages = 3);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
-// bf16 prefill: per-chunk preparation into the workspace, then the recurrence
-size_t prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t chunk, bool bf16);
-hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream);
-hipError_t launch_recurrence(const PrefillArgs &a, hipStream_t stream);
+// bf16 prefill in one kernel (prefill_fused.hip): chunk quantities formed on chip
+hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t stream);
 
 // Gradients of the prefill (backward.hip): dL/dq, dk, dv, dalpha, dbeta, dS_0
 // from dL/dy and dL/dS_T

@@ -521,6 +521,7 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     p.q_tok_stride = nqkv; p.k_tok_stride = nqkv; p.v_tok_stride = nqkv;
     p.bf16 = false;
     p.ws = ws + w.rec;        // per-chunk records: the two-kernel fp32 core
+    p.hilo_core = true;       // the layer's bound is the bf16 one
     if ((e = launch_prefill(p, s))) return e;
 
     switch (Dv) {

@@ -11,11 +11,11 @@
 //   Y = diag(2^G) Q S + P U,  P = lower_incl[ Gamma_rj (q_r . k_j) ]   (eq (4))
 //   S' = 2^{G_C} S + K^T diag(2^{G_C - G}) U                          (eqs (1),(3))
 //
-// bf16 inputs: chunk_prep.hip (the state-independent chunk quantities into a
-// record workspace) then recurrence.hip.  fp32 inputs (the layer's core):
-// the per-chunk preparation and the recurrence of backward.hip, also through a
-// record workspace.  Both need the caller's workspace.  Ragged tails are padded
-// with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
+// bf16 inputs: one kernel (prefill_fused.hip) that forms every chunk quantity
+// on chip.  fp32 inputs (and the layer's core): the per-chunk preparation of
+// backward.hip into a caller-provided record workspace, then the recurrence.
+// Ragged tails are padded with identity tokens (alpha = 1, beta = 0,
+// k = q = v = 0).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,24 +32,17 @@ __global__ void copy_or_zero_state(const float *__restrict__ s0, float *__restri
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int stages)
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
     if (a.B * a.H == 0) return hipSuccess;
     if (a.T == 0) {
-        if (!(stages & 2) || !a.sT || a.sT == a.s0) return hipSuccess;
+        if (!a.sT || a.sT == a.s0) return hipSuccess;
         const int64_t n = a.B * a.H * a.Dk * a.Dv;
         hipLaunchKernelGGL(copy_or_zero_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.s0, a.sT, n);
         return hipGetLastError();
     }
+    if (a.bf16) return launch_prefill_fused(a, stream);
     if (!a.ws) return hipErrorInvalidValue;   // the C ABI checks the workspace first
-    if (a.bf16) {
-        // per-chunk preparation of every (b, h, chunk), then the recurrence
-        if (stages & 1) {
-            const hipError_t e = launch_chunk_prep(a, stream);
-            if (e != hipSuccess) return e;
-        }
-        return (stages & 2) ? launch_recurrence(a, stream) : hipSuccess;
-    }
     return launch_prefill_f32_staged(a, stream);
 }
 

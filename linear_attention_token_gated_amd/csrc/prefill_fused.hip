@@ -1,0 +1,723 @@
+// prefill_fused.hip -- the chunked prefill of the gated delta rule for bf16
+// inputs in a single kernel: every chunk quantity is formed on chip, q, k and v
+// are read from HBM once, and y and the final state are written once.
+//
+// Source: "On the Design of Qwen3.8-Next Architecture", picx.dev summary,
+// "Theoretical foundations", eqs (1)-(4).  For one chunk of C tokens entering
+// with state S (G_r = sum_{i<=r} log2 alpha_i within the chunk):
+//
+//   A  = strict_lower[ beta_r 2^(G_r - G_j) (k_r . k_j) ],  T = (I + A)^-1
+//   T' = T diag(beta),  P = lower_incl[ 2^(G_r - G_j) (q_r . k_j) ]
+//   R  = V - diag(2^G) K S,   U = T' R          (u_r = beta_r e_r of eqs (2)-(3))
+//   Y  = diag(2^G) Q S + P U                     (eq (4))
+//   S' = 2^(G_C) S + K^T diag(2^(G_C - G)) U      (eqs (1), (3))
+//
+// Columns of S, V, U, Y are independent, so one workgroup carries one
+// 16-column slice of S of one (b, h) through every chunk; the slices of a head
+// are placed on one XCD, whose L2 then serves the eight reads of K and Q.
+// Eight wavefronts, two barriers (X, Y) per chunk c:
+//
+//   chain waves 0-3 (wave w owns state rows 16 (w + 4m))
+//     X-phase: K_w S (S as one bf16), Q_w S (S as bf16 hi + lo) for token block
+//              w; R_w = V_w - 2^G K_w S  -> LDS
+//     Y-phase: U = T' R for all token blocks (each chain wave, from LDS); its
+//              own state rows S <- 2^G_C S + K^T (2^(G_C-G) U); the S operand,
+//              U_w and 2^G Q_w S -> LDS
+//   preparation waves 4-7 (wave p = w - 4; chunk c + 1; outputs of chunk c - 1)
+//     X-phase: Y_p of chunk c-1 = 2^G Q_p S + P_p U (P_p kept in registers)
+//              -> y; decay prefix of chunk c+1 (fp64); Gram blocks (P row p,
+//              A_pp and some blocks of A below the diagonal); T_pp =
+//              (I + A_pp)^-1 by forward substitution -> LDS
+//     Y-phase: column p of T from the blocks of all waves,
+//              T_mp = -T_mm sum_{j=p}^{m-1} A_mj T_jp; T' column p -> LDS;
+//              the register-staged q, k, v, alpha, beta of chunk c + 2 -> LDS
+//
+// q, k and v tiles are loaded into registers by the preparation waves 1.5
+// chunks before they are written to LDS.  Rows past the end of the sequence
+// are zeros with alpha = 1 and beta = 0 (identity tokens).
+//
+// Precision: q, k, v are exact bf16 operands and every product accumulates in
+// fp32.  Operands computed in fp32 (S in Q S, R, U, T, T', P, the level
+// products of T) enter as bf16 pairs hi + lo, each product summing hi*hi +
+// hi*lo + lo*hi.  S enters K S as a single bf16 (the state recurrence damps
+// that rounding: 2e-3 of the bound-relevant max|err|/RMS at T = 32768 in a CPU
+// simulation of these rounding points, against 1e-2 for Q S).  Decay
+// prefixes are summed in fp64 so that 2^(G_r - G_j) keeps its precision after
+// decays near 0.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int FT = 512;   // 8 wavefronts
+
+struct FusedParams {
+    const __bf16 *q, *k, *v;
+    const float *alpha, *beta, *s0;
+    float *y, *sT;
+    int64_t T, H, Dv;
+    int64_t qs, ks, vs;      // token strides (elements)
+    int nslices;             // Dv / 16
+    int xcd_map;             // 1: the slices of a head on one XCD
+};
+
+template <int C, int DK> struct FL {
+    static constexpr int NB = C / 16, NSB = DK / 16, MS = (NSB + 3) / 4;
+    static constexpr int NTRI = NB * (NB + 1) / 2, NOFF = NB * (NB - 1) / 2;
+    static constexpr int KSD = DK % 32 == 0 ? 32 : 16, NK = DK / KSD;   // k-steps over Dk
+    static constexpr int KSC = C % 32 == 0 ? 32 : 16, NJ = C / KSC;     // k-steps over the chunk
+    static constexpr int KPS = frag_pitch<KSD>(DK);                     // S^T row pitch (bf16)
+    static constexpr size_t KQB = (size_t)2 * C * DK;                   // one K or Q chunk
+    static constexpr size_t VB = (size_t)2 * C * BV;                    // one V slice
+    static constexpr size_t ABB = (size_t)8 * C;                        // alpha[C] | beta[C]
+    static constexpr size_t oK = 0;                                     // [3] K chunks
+    static constexpr size_t oQ = oK + 3 * KQB;                          // [2] Q chunks
+    static constexpr size_t oV = oQ + 2 * KQB;                          // [2] V slices [C][16]
+    static constexpr size_t oAB = oV + 2 * VB;                          // [2] gates
+    static constexpr size_t oSTh = align16(oAB + 2 * ABB);              // S^T operand, hi
+    static constexpr size_t oSTl = oSTh + align16(2 * BV * KPS);        // S^T operand, lo
+    static constexpr size_t oR = oSTl + align16(2 * BV * KPS);          // R [NB][hi|lo][64] bf16x4
+    static constexpr size_t oTP = oR + (size_t)NB * 1024;               // [2][NTRI] T'^T blocks, hi|lo
+    static constexpr size_t TPB = (size_t)NTRI * 1024;
+    static constexpr size_t oDEC = oTP + 2 * TPB;                       // [2] EG[C] | Ed[C] | EGC
+    static constexpr size_t DECB = align16(4 * (2 * C + 4));
+    static constexpr size_t oXT = oDEC + 2 * DECB;                      // [NB] T_mm row-major, hi|lo
+    static constexpr size_t oXA = oXT + (size_t)NB * 1024;              // [NOFF] A_mj row-major, hi|lo
+    static constexpr size_t oUQ = oXA + (size_t)(NOFF > 0 ? NOFF : 1) * 1024;   // U_w [NB][hi|lo][64] bf16x4
+    static constexpr size_t oQS = oUQ + (size_t)NB * 1024;              // 2^G Q_w S [NB][64] f32x4
+    static constexpr size_t oGS = oQS + (size_t)NB * 1024;              // [4][C] decay prefix, fp64
+    static constexpr size_t BYTES = oGS + (size_t)4 * C * 8;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ int tri_idx(int i, int k) { return i * (i + 1) / 2 + k; }
+__device__ __forceinline__ int off_idx(int m, int j) { return m * (m - 1) / 2 + j; }
+constexpr int off_idx_c(int m, int j) { return m * (m - 1) / 2 + j; }
+
+// Which preparation wave forms the Gram block A_mj (m > j).  With four token
+// blocks the assignment evens out the X-phase: every wave forms five blocks
+// (its P row, A_pp and the ones listed here); otherwise the owner of column j.
+template <int NB> constexpr int a_owner(int m, int j) {
+    if constexpr (NB == 4) {
+        return (m == 1 && j == 0) || (m == 2 && j == 0) || (m == 3 && j == 2) ? 0
+             : (m == 3 && j == 0) || (m == 2 && j == 1) ? 1 : 2;
+    } else {
+        return j;
+    }
+}
+
+// Element (row, col) of a K or Q chunk in LDS: 16-byte granule col/8 of row r
+// sits at granule position (col/8) ^ (r mod G), which spreads fragment reads and
+// the column reads of the state update over distinct banks.
+template <int DK> __device__ __forceinline__ int kq_idx(int row, int col) {
+    constexpr int G = DK / 8;
+    return row * DK + ((((col >> 3) ^ row) & (G - 1)) << 3) + (col & 7);
+}
+
+template <int KS, int DK>
+__device__ __forceinline__ Frag<__bf16, KS> frag_kq(const __bf16 *base, int r0, int k0, int lane) {
+    Frag<__bf16, KS> f;
+    f.load(base + kq_idx<DK>(r0 + (lane & 15), k0 + (lane >> 4) * (KS / 4)));
+    return f;
+}
+
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4v *lds_i16x4;
+
+// Transposing LDS read of 16-bit elements (gfx950): lane j of each group of 16
+// supplies the address of 4 consecutive elements; lane i of the group receives
+// element i % 4 of the rows supplied by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.
+__device__ __forceinline__ bf16x4 read_tr16(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (lds_i16x4)(uintptr_t)(uint32_t)(uintptr_t)p));
+}
+
+// Column-ordered read of a row-major 16 x 16 bf16 block M: lane (n, g) receives
+// M[4g + s][n], s = 0..3 -- the MFMA accumulator layout of M, which is the B
+// operand of a 16-deep product with k = row.
+__device__ __forceinline__ bf16x4 read_cols16(const __bf16 *blk, int lane) {
+    const int ln = lane & 15, lg = lane >> 4;
+    return read_tr16(blk + (4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3));
+}
+// Row-ordered read: lane (r, g) receives M[r][4g + s] -- the A operand layout.
+__device__ __forceinline__ bf16x4 read_rows16(const __bf16 *blk, int lane) {
+    return *reinterpret_cast<const bf16x4 *>(blk + (lane & 15) * 16 + 4 * (lane >> 4));
+}
+// The lane's four values of a block held in accumulator layout (lane (n, g):
+// M[4g + s][n]) written row-major as the transpose: position n * 16 + 4g + s.
+__device__ __forceinline__ void write_acc_transposed(__bf16 *blk, bf16x4 v, int lane) {
+    *reinterpret_cast<bf16x4 *>(blk + (lane & 15) * 16 + 4 * (lane >> 4)) = v;
+}
+
+// A operand K^T[r0 + m][tokens k0 ..] of the state update from the row-major
+// (granule-permuted) K chunk: lane j of group g points at row k0 + 4g + j/4
+// (and 16 rows further for KS = 32), columns r0 + 4 (j % 4)..+3; lane m of the
+// group then holds column r0 + m at tokens k0 + 4g + s (and k0 + 16 + 4g + s).
+template <int KS, int DK>
+__device__ __forceinline__ Frag<__bf16, KS> k_cols_tr(const __bf16 *Ks, int r0, int k0, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const int row = k0 + 4 * g + (j >> 2), col = r0 + 4 * (j & 3);
+    Frag<__bf16, KS> f;
+    if constexpr (KS == 16) {
+        f.v = read_tr16(Ks + kq_idx<DK>(row, col));
+    } else {
+        const bf16x4 a = read_tr16(Ks + kq_idx<DK>(row, col));
+        const bf16x4 b = read_tr16(Ks + kq_idx<DK>(row + 16, col));
+        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    return f;
+}
+
+// Two 16-deep fragments (k-blocks a and b) as one 32-deep fragment.  Used on
+// both operands of a product, the pairing only reorders the terms of the k-sum.
+__device__ __forceinline__ Frag<__bf16, 32> pair16(bf16x4 a, bf16x4 b) {
+    Frag<__bf16, 32> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+// sum over the blocks k < N of A_k B_k, hi/lo pairs (three products each), two
+// blocks per 32-deep MFMA and a 16-deep one for an odd last block
+template <int N>
+__device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al, const bf16x4 *bh,
+                                              const bf16x4 *bl, f32x4 &acc, f32x4 &acc2) {
+    using F16 = Frag<__bf16, 16>;
+    using F32 = Frag<__bf16, 32>;
+    static_for<N / 2>([&](auto i_c) {
+        constexpr int k = 2 * decltype(i_c)::value;
+        const F32 a = pair16(ah[k], ah[k + 1]), a2 = pair16(al[k], al[k + 1]);
+        const F32 b = pair16(bh[k], bh[k + 1]), b2 = pair16(bl[k], bl[k + 1]);
+        acc = F32::mma(a, b, acc);
+        acc2 = F32::mma(a, b2, acc2);
+        acc2 = F32::mma(a2, b, acc2);
+    });
+    if constexpr (N % 2) {
+        F16 a, a2, b, b2;
+        a.v = ah[N - 1]; a2.v = al[N - 1]; b.v = bh[N - 1]; b2.v = bl[N - 1];
+        acc = F16::mma(a, b, acc);
+        acc2 = F16::mma(a, b2, acc2);
+        acc2 = F16::mma(a2, b, acc2);
+    }
+}
+
+// hi/lo product of one 16x16x16 pair (three products)
+__device__ __forceinline__ f32x4 mma_hilo16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl) {
+    using F16 = Frag<__bf16, 16>;
+    F16 a, a2, b, b2;
+    a.v = ah; a2.v = al; b.v = bh; b2.v = bl;
+    f32x4 acc = F16::mma(a, b, zero4());
+    f32x4 acc2 = F16::mma(a, b2, zero4());
+    acc2 = F16::mma(a2, b, acc2);
+    return acc + acc2;
+}
+
+template <int S> __device__ __forceinline__ void fsub_step(float (&X)[4], const float (&Lr)[16]) {
+    // rows r <= S have L[r][S] = 0 (strictly lower): the update is an exact no-op there
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[e] = fmaf(-Lr[S], row_bcast<S>(X[e]), X[e]);
+}
+template <int... S>
+__device__ __forceinline__ void fsub16(float (&X)[4], const float (&Lr)[16], std::integer_sequence<int, S...>) {
+    (fsub_step<S>(X, Lr), ...);
+}
+
+template <int C, int DK>
+__global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
+{
+    using L = FL<C, DK>;
+    using FDK = Frag<__bf16, L::KSD>;
+    using FC = Frag<__bf16, L::KSC>;
+    constexpr int NB = L::NB, NSB = L::NSB, MS = L::MS, NTRI = L::NTRI, KSD = L::KSD, NK = L::NK;
+    constexpr int KSC = L::KSC, NJ = L::NJ, KPS = L::KPS;
+
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+    auto Kb = [&](int i) { return reinterpret_cast<__bf16 *>(smem + L::oK + (size_t)i * L::KQB); };
+    auto Qb = [&](int i) { return reinterpret_cast<__bf16 *>(smem + L::oQ + (size_t)i * L::KQB); };
+    auto Vb = [&](int i) { return reinterpret_cast<__bf16 *>(smem + L::oV + (size_t)i * L::VB); };
+    auto ABb = [&](int i) { return reinterpret_cast<float *>(smem + L::oAB + (size_t)i * L::ABB); };
+    auto TPb = [&](int s, int blk) { return reinterpret_cast<__bf16 *>(smem + L::oTP + (size_t)s * L::TPB + (size_t)blk * 1024); };
+    auto DECb = [&](int s) { return reinterpret_cast<float *>(smem + L::oDEC + (size_t)s * L::DECB); };
+    auto XTb = [&](int m) { return reinterpret_cast<__bf16 *>(smem + L::oXT + (size_t)m * 1024); };
+    auto XAb = [&](int o) { return reinterpret_cast<__bf16 *>(smem + L::oXA + (size_t)o * 1024); };
+    __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
+    __bf16 *STl = reinterpret_cast<__bf16 *>(smem + L::oSTl);
+    bf16x4 *Rs = reinterpret_cast<bf16x4 *>(smem + L::oR);       // [NB][hi 64 | lo 64]
+    bf16x4 *UQs = reinterpret_cast<bf16x4 *>(smem + L::oUQ);     // [NB][hi 64 | lo 64]
+    f32x4 *QSs = reinterpret_cast<f32x4 *>(smem + L::oQS);       // [NB][64]
+
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const int ln = lane & 15, lg = lane >> 4;
+
+    const int64_t bid = blockIdx.x;
+    int64_t bh, sl;
+    if (p.xcd_map) {
+        const int64_t xcd = bid & 7, local = bid >> 3;
+        bh = (local / p.nslices) * 8 + xcd;
+        sl = local % p.nslices;
+    } else {
+        bh = bid / p.nslices;
+        sl = bid % p.nslices;
+    }
+    const int64_t H = p.H, T = p.T, Dv = p.Dv;
+    const int64_t b = bh / H, h = bh % H;
+    const int n0 = (int)sl * BV;
+    const int64_t NC = (T + C - 1) / C;
+
+    // ======================= chain waves =======================
+    auto chain_wave = [&](auto w_c) {
+        constexpr int w = decltype(w_c)::value;
+        constexpr bool has_rb = w < NB;
+        f32x4 S[MS];
+#pragma unroll
+        for (int m = 0; m < MS; ++m) S[m] = zero4();
+        if (p.s0) {
+            const float *s0 = p.s0 + bh * (int64_t)DK * Dv;
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = w + 4 * m;
+                if (ib < NSB) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[m][e] = s0[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln];
+                }
+            }
+        }
+        auto write_state_operand = [&]() {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = w + 4 * m;
+                if (ib < NSB) {
+                    bf16x4 hv, lv;
+                    split4(S[m], hv, lv);
+                    *reinterpret_cast<bf16x4 *>(STh + ln * KPS + 16 * ib + 4 * lg) = hv;
+                    *reinterpret_cast<bf16x4 *>(STl + ln * KPS + 16 * ib + 4 * lg) = lv;
+                }
+            }
+        };
+        lds_barrier();                              // chunk 0 staged
+        // iteration -1: nothing but the state operand
+        lds_barrier();
+        write_state_operand();
+        lds_barrier();
+        int kb = 0, qb = 0;                          // c % 3, c % 2
+        for (int64_t c = 0; c <= NC; ++c) {
+            if (c == NC) {                           // outputs of the last chunk: two more barriers
+                lds_barrier();
+                lds_barrier();
+                break;
+            }
+            const __bf16 *Ks = Kb(kb);
+            const float *dec = DECb(qb);
+            // ---- X-phase: K_w S, Q_w S -> R_w
+            f32x4 egqs = zero4();
+            if constexpr (has_rb) {
+                const __bf16 *Qs = Qb(qb);
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * w + 4 * lg);
+                const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
+                f32x4 ks = zero4(), qs = zero4(), qs2 = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const FDK kf = frag_kq<KSD, DK>(Ks, 16 * w, kk * KSD, lane);
+                    const FDK qf = frag_kq<KSD, DK>(Qs, 16 * w, kk * KSD, lane);
+                    const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
+                    const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
+                    ks = FDK::mma(kf, sh, ks);
+                    qs = FDK::mma(qf, sh, qs);
+                    qs2 = FDK::mma(qf, sl, qs2);
+                }
+                f32x4 rv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
+                bf16x4 hv, lv;
+                split4(rv, hv, lv);
+                Rs[w * 128 + lane] = hv;
+                Rs[w * 128 + 64 + lane] = lv;
+                egqs = eg * (qs + qs2);
+            }
+            lds_barrier();
+            // ---- Y-phase: U = T' R (every token block), state update
+            {
+                const int ts = (int)(c & 1);
+                bf16x4 rh[NB], rl[NB], udh[NB], udl[NB];
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    rh[k] = Rs[k * 128 + lane];
+                    rl[k] = Rs[k * 128 + 64 + lane];
+                }
+                static_for<NB>([&](auto i_c) {
+                    constexpr int i = decltype(i_c)::value;
+                    bf16x4 th[i + 1], tl[i + 1];
+#pragma unroll
+                    for (int k = 0; k <= i; ++k) {
+                        th[k] = read_cols16(TPb(ts, tri_idx(i, k)), lane);
+                        tl[k] = read_cols16(TPb(ts, tri_idx(i, k)) + 256, lane);
+                    }
+                    f32x4 u = zero4(), u2 = zero4();
+                    pair_products<i + 1>(th, tl, rh, rl, u, u2);
+                    u += u2;
+                    const f32x4 ed = *reinterpret_cast<const f32x4 *>(dec + C + 16 * i + 4 * lg);
+                    split4(ed * u, udh[i], udl[i]);
+                    if constexpr (i == w) {
+                        bf16x4 uh, ul;
+                        split4(u, uh, ul);
+                        UQs[w * 128 + lane] = uh;
+                        UQs[w * 128 + 64 + lane] = ul;
+                        QSs[w * 64 + lane] = egqs;
+                    }
+                });
+                const float egc = dec[2 * C];
+#pragma unroll
+                for (int m = 0; m < MS; ++m) {
+                    const int ib = w + 4 * m;
+                    if (ib < NSB) {
+                        f32x4 acc = S[m] * egc, acc2 = zero4();
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) {
+                            const FC ka = k_cols_tr<KSC, DK>(Ks, 16 * ib, jj * KSC, lane);
+                            FC bhf, blf;
+                            if constexpr (KSC == 32) {
+                                bhf = pair16(udh[2 * jj], udh[2 * jj + 1]);
+                                blf = pair16(udl[2 * jj], udl[2 * jj + 1]);
+                            } else {
+                                bhf.v = udh[jj];
+                                blf.v = udl[jj];
+                            }
+                            acc = FC::mma(ka, bhf, acc);
+                            acc2 = FC::mma(ka, blf, acc2);
+                        }
+                        S[m] = acc + acc2;
+                    }
+                }
+                write_state_operand();
+            }
+            lds_barrier();
+            kb = kb == 2 ? 0 : kb + 1;
+            qb ^= 1;
+        }
+        if (p.sT) {
+            float *sT = p.sT + bh * (int64_t)DK * Dv;
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int ib = w + 4 * m;
+                if (ib < NSB) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sT[(int64_t)(16 * ib + 4 * lg + e) * Dv + n0 + ln] = S[m][e];
+                }
+            }
+        }
+    };
+
+    // ======================= preparation waves =======================
+    auto prep_wave = [&](auto p_c) {
+        constexpr int pw = decltype(p_c)::value;
+        constexpr bool has_rb = pw < NB;
+        double *GS = reinterpret_cast<double *>(smem + L::oGS) + pw * C;
+
+        // register staging of the q, k, v rows of token block pw and of the gates
+        struct Stage {
+            FDK kf[NK], qf[NK];
+            bf16x8 vv;
+            float ab;
+        };
+        Stage st[2];
+        auto load_stage = [&](Stage &s, int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                const int64_t t = c0 + 16 * pw + ln;
+                const int64_t tc = t < T ? t : T - 1;
+                const __bf16 *kr = p.k + (b * T + tc) * p.ks + h * DK;
+                const __bf16 *qr = p.q + (b * T + tc) * p.qs + h * DK;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    s.kf[kk].load(kr + kk * KSD + lg * (KSD / 4));
+                    s.qf[kk].load(qr + kk * KSD + lg * (KSD / 4));
+                }
+                const int l32 = lane & 31;
+                const int64_t tv = c0 + 16 * pw + (l32 >> 1);
+                const int64_t tvc = tv < T ? tv : T - 1;
+                s.vv = *reinterpret_cast<const bf16x8 *>(p.v + (b * T + tvc) * p.vs + h * Dv + n0 + (l32 & 1) * 8);
+                const int64_t tg = c0 + 16 * pw + (lane & 15);
+                const int64_t tgc = tg < T ? tg : T - 1;
+                s.ab = (lane & 16) ? p.beta[(b * T + tgc) * H + h] : p.alpha[(b * T + tgc) * H + h];
+            }
+        };
+        auto write_stage = [&](const Stage &s, int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                __bf16 *Kd = Kb((int)(j % 3));
+                __bf16 *Qd = Qb((int)(j & 1));
+                const int row = 16 * pw + ln;
+                const bool ok = c0 + row < T;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    FDK kz = s.kf[kk], qz = s.qf[kk];
+                    if (!ok) {
+#pragma unroll
+                        for (int e = 0; e < KSD / 4; ++e) {
+                            kz.set(e, 0.f);
+                            qz.set(e, 0.f);
+                        }
+                    }
+                    *reinterpret_cast<decltype(kz.v) *>(Kd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = kz.v;
+                    *reinterpret_cast<decltype(qz.v) *>(Qd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = qz.v;
+                }
+                if (lane < 32) {
+                    const int r = 16 * pw + (lane >> 1);
+                    bf16x8 vz = s.vv;
+                    if (c0 + r >= T) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
+                    }
+                    *reinterpret_cast<bf16x8 *>(Vb((int)(j & 1)) + r * BV + (lane & 1) * 8) = vz;
+                    const int rg = 16 * pw + (lane & 15);
+                    const bool okg = c0 + rg < T;
+                    // alpha of a padding token is 1, beta 0
+                    ABb((int)(j & 1))[(lane & 16 ? C : 0) + rg] = okg ? s.ab : (lane & 16 ? 0.f : 1.f);
+                }
+            }
+        };
+
+        // P row pw of a chunk as bf16 hi/lo A operands (lane (r, g): P[r][4g + e]),
+        // kept from the chunk's preparation until its output is formed
+        bf16x4 Ph[2][NB > 0 ? NB : 1], Pl[2][NB > 0 ? NB : 1];
+        float Tdiag[4];                          // T_pp row ln, columns 4 lg + e
+
+        // Gram block D = X_r K_jb^T in row layout (lane (ln, g): D[ln][4g + e])
+        auto gram = [&](const __bf16 *Xs, int r, int jb, const __bf16 *Ks) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+                acc = FDK::mma(frag_kq<KSD, DK>(Ks, 16 * jb, kk * KSD, lane),
+                               frag_kq<KSD, DK>(Xs, 16 * r, kk * KSD, lane), acc);
+            return acc;
+        };
+        // 2^(G_r - G_j) on and below the diagonal (and strictly below for A), 0 above
+        auto decay_mask = [&](f32x4 d, int r, int jb, bool incl) {
+            const int rt = 16 * r + ln;
+            const double Gr = GS[rt];
+            f32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jt = 16 * jb + 4 * lg + e;
+                const bool keep = incl ? rt >= jt : rt > jt;
+                out[e] = keep ? __builtin_amdgcn_exp2f((float)(Gr - GS[jt])) * d[e] : 0.f;
+            }
+            return out;
+        };
+
+        // X-phase work of chunk j (set par of the P registers)
+        auto prep_x = [&](auto par_c, int64_t j) {
+            constexpr int par = decltype(par_c)::value;
+            const __bf16 *Ks = Kb((int)(j % 3));
+            const __bf16 *Qs = Qb((int)(j & 1));
+            const float *ab = ABb((int)(j & 1));
+            // decay prefix, one token per lane, in fp64
+            const float al = lane < C ? ab[lane] : 1.f;
+            const double G = wave_inclusive_sum_f64(lane < C ? (double)log2_decay(al) : 0.0, lane);
+            const double GC = lane_value_f64(G, C - 1);
+            if (lane < C) GS[lane] = G;
+            if constexpr (pw == 0) {
+                float *dec = DECb((int)(j & 1));
+                if (lane < C) {
+                    dec[lane] = __builtin_amdgcn_exp2f((float)G);
+                    dec[C + lane] = __builtin_amdgcn_exp2f((float)(GC - G));
+                }
+                if (lane == 0) dec[2 * C] = __builtin_amdgcn_exp2f((float)GC);
+            }
+            if constexpr (has_rb) {
+                // P row pw
+                static_for<pw + 1>([&](auto jb_c) {
+                    constexpr int jb = decltype(jb_c)::value;
+                    const f32x4 d = decay_mask(gram(Qs, pw, jb, Ks), pw, jb, true);
+                    split4(d, Ph[par][jb], Pl[par][jb]);
+                });
+                // A_pp: fp32 rows through the T_pp slot (scratch), then forward substitution
+                {
+                    const float bet = ab[C + 16 * pw + ln];
+                    const f32x4 d = decay_mask(gram(Ks, pw, pw, Ks), pw, pw, false) * bet;
+                    float *scr = reinterpret_cast<float *>(XTb(pw));
+                    *reinterpret_cast<f32x4 *>(scr + ln * 16 + 4 * lg) = d;
+                    float Lr[16];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(scr + ln * 16 + 4 * s4);
+                        Lr[4 * s4] = v4[0]; Lr[4 * s4 + 1] = v4[1]; Lr[4 * s4 + 2] = v4[2]; Lr[4 * s4 + 3] = v4[3];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Tdiag[e] = ln == 4 * lg + e ? 1.f : 0.f;
+                    fsub16(Tdiag, Lr, std::make_integer_sequence<int, 15>{});
+                    bf16x4 hv, lv;
+                    split4(f32x4{Tdiag[0], Tdiag[1], Tdiag[2], Tdiag[3]}, hv, lv);
+                    // the scratch rows were read above (same wavefront, LDS in order)
+                    *reinterpret_cast<bf16x4 *>(XTb(pw) + ln * 16 + 4 * lg) = hv;
+                    *reinterpret_cast<bf16x4 *>(XTb(pw) + 256 + ln * 16 + 4 * lg) = lv;
+                }
+                // blocks of A below the diagonal owned by this wave
+                static_for<NB>([&](auto m_c) {
+                    constexpr int m = decltype(m_c)::value;
+                    static_for<m>([&](auto jj_c) {
+                        constexpr int jj = decltype(jj_c)::value;
+                        if constexpr (a_owner<NB>(m, jj) == pw) {
+                            const float bet = ab[C + 16 * m + ln];
+                            const f32x4 d = decay_mask(gram(Ks, m, jj, Ks), m, jj, false) * bet;
+                            bf16x4 hv, lv;
+                            split4(d, hv, lv);
+                            constexpr int o = off_idx_c(m, jj);
+                            *reinterpret_cast<bf16x4 *>(XAb(o) + ln * 16 + 4 * lg) = hv;
+                            *reinterpret_cast<bf16x4 *>(XAb(o) + 256 + ln * 16 + 4 * lg) = lv;
+                        }
+                    });
+                });
+            }
+        };
+
+        // Y-phase work of chunk j: column pw of T, T' column pw into slot j % 2
+        auto prep_y = [&](int64_t j) {
+            if constexpr (has_rb) {
+                constexpr int k = pw;
+                const int ts = (int)(j & 1);
+                const float bcol = ABb((int)(j & 1))[C + 16 * k + ln];
+                bf16x4 bh[NB], bl[NB];                  // T_jk in accumulator layout, hi/lo
+                bh[k] = read_cols16(XTb(k), lane);
+                bl[k] = read_cols16(XTb(k) + 256, lane);
+                {
+                    f32x4 t;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t[e] = ((float)bh[k][e] + (float)bl[k][e]) * bcol;
+                    bf16x4 hv, lv;
+                    split4(t, hv, lv);
+                    write_acc_transposed(TPb(ts, tri_idx(k, k)), hv, lane);
+                    write_acc_transposed(TPb(ts, tri_idx(k, k)) + 256, lv, lane);
+                }
+                static_for<NB - k - 1>([&](auto i_c) {
+                    constexpr int m = k + 1 + decltype(i_c)::value;
+                    bf16x4 ah[m - k], al[m - k];
+#pragma unroll
+                    for (int jj = k; jj < m; ++jj) {
+                        ah[jj - k] = read_rows16(XAb(off_idx(m, jj)), lane);
+                        al[jj - k] = read_rows16(XAb(off_idx(m, jj)) + 256, lane);
+                    }
+                    f32x4 z = zero4(), z2 = zero4();
+                    pair_products<m - k>(ah, al, bh + k, bl + k, z, z2);
+                    bf16x4 zh, zl;
+                    split4(z + z2, zh, zl);
+                    const f32x4 t = -mma_hilo16(read_rows16(XTb(m), lane), read_rows16(XTb(m) + 256, lane), zh, zl);
+                    split4(t, bh[m], bl[m]);
+                    bf16x4 hv, lv;
+                    split4(t * bcol, hv, lv);
+                    write_acc_transposed(TPb(ts, tri_idx(m, k)), hv, lane);
+                    write_acc_transposed(TPb(ts, tri_idx(m, k)) + 256, lv, lane);
+                });
+            }
+        };
+
+        // output rows of token block pw of chunk j (P set par)
+        auto out_y = [&](auto par_c, int64_t j) {
+            constexpr int par = decltype(par_c)::value;
+            if constexpr (has_rb) {
+                f32x4 acc = QSs[pw * 64 + lane], acc2 = zero4();
+                bf16x4 uh[pw + 1], ul[pw + 1];
+#pragma unroll
+                for (int jb = 0; jb <= pw; ++jb) {
+                    uh[jb] = UQs[jb * 128 + lane];
+                    ul[jb] = UQs[jb * 128 + 64 + lane];
+                }
+                pair_products<pw + 1>(Ph[par], Pl[par], uh, ul, acc, acc2);
+                const f32x4 yv = acc + acc2;
+                const int64_t t0 = j * C + 16 * pw + 4 * lg;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t t = t0 + e;
+                    if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = yv[e];
+                }
+            }
+        };
+
+        // chunk 0 into LDS, chunk 1 in flight
+        load_stage(st[0], 0);
+        if (NC > 1) load_stage(st[1], 1);
+        write_stage(st[0], 0);
+        lds_barrier();
+
+        // iteration c: X-phase (outputs of c-1, loads of c+3, preparation of c+1),
+        // Y-phase (T' of c+1, chunk c+2 into LDS).  Register sets by parity:
+        // loads of chunk j and the P row of chunk j use set j & 1.
+        auto iter = [&](auto par_c, int64_t c) {
+            constexpr int par = decltype(par_c)::value;    // == (c + 1) & 1
+            using PAR = std::integral_constant<int, par>;
+            if (c >= 1) out_y(PAR{}, c - 1);
+            if (c + 3 < NC) load_stage(st[par], c + 3);
+            if (c + 1 < NC) prep_x(PAR{}, c + 1);
+            lds_barrier();
+            if (c + 1 < NC) prep_y(c + 1);
+            if (c + 2 < NC) write_stage(st[1 - par], c + 2);
+            lds_barrier();
+        };
+        for (int64_t c = -1; c <= NC; c += 2) {
+            iter(std::integral_constant<int, 0>{}, c);
+            if (c + 1 <= NC) iter(std::integral_constant<int, 1>{}, c + 1);
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    switch (wave) {
+    case 0: chain_wave(I0{}); break;
+    case 1: chain_wave(I1{}); break;
+    case 2: chain_wave(I2{}); break;
+    case 3: chain_wave(I3{}); break;
+    case 4: prep_wave(I0{}); break;
+    case 5: prep_wave(I1{}); break;
+    case 6: prep_wave(I2{}); break;
+    default: prep_wave(I3{}); break;
+    }
+}
+
+template <int C, int DK>
+hipError_t launch_fused_t(const PrefillArgs &a, hipStream_t stream)
+{
+    FusedParams fp;
+    fp.q = static_cast<const __bf16 *>(a.q);
+    fp.k = static_cast<const __bf16 *>(a.k);
+    fp.v = static_cast<const __bf16 *>(a.v);
+    fp.alpha = a.alpha; fp.beta = a.beta; fp.s0 = a.s0;
+    fp.y = a.y; fp.sT = a.sT;
+    fp.T = a.T; fp.H = a.H; fp.Dv = a.Dv;
+    fp.qs = a.q_tok_stride; fp.ks = a.k_tok_stride; fp.vs = a.v_tok_stride;
+    fp.nslices = (int)(a.Dv / BV);
+    const int64_t bh = a.B * a.H;
+    fp.xcd_map = (bh % 8 == 0) ? 1 : 0;
+    const int64_t grid = bh * fp.nslices;
+    hipLaunchKernelGGL((gdn_prefill_fused_kernel<C, DK>), dim3((unsigned)grid), dim3(FT), 0, stream, fp);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_fused_dk(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.Dk) {
+    case 16: return launch_fused_t<C, 16>(a, s);
+    case 32: return launch_fused_t<C, 32>(a, s);
+    case 64: return launch_fused_t<C, 64>(a, s);
+    case 128: return launch_fused_t<C, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t stream)
+{
+    switch (a.chunk) {
+    case 16: return launch_fused_dk<16>(a, stream);
+    case 32: return launch_fused_dk<32>(a, stream);
+    case 64: return launch_fused_dk<64>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -73,31 +73,17 @@ def test_prefill_validation(L):
 
 
 def test_prefill_workspace_validation(L):
-    # bf16 needs one record per (sequence, head, chunk); every case below fails
-    # on the host before anything is launched
-    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1)
-    assert need == 2 * 4 * 2240
+    # bf16 needs no workspace; fp32 needs one record per (sequence, head, chunk).
+    # Every failing case below fails on the host before anything is launched.
+    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1) == 0
+    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 0)
     W = A + 400 * MB
-    assert prefill(L, dt=1) == WS                                # missing
-    assert prefill(L, dt=1, w=W, wb=need - 1) == WS              # too small
-    assert prefill(L, dt=1, w=W + 16, wb=need) == ALIGN          # not 256-byte aligned
-    assert prefill(L, dt=1, w=A + 256 * MB, wb=need) == ALIAS    # workspace == y
-    assert prefill(L, dt=1, w=A + 64 * MB, wb=need) == ALIAS     # workspace == k
+    assert prefill(L, dt=0) == WS                                # missing
+    assert prefill(L, dt=0, w=W, wb=need - 1) == WS              # too small
+    assert prefill(L, dt=0, w=W + 16, wb=need) == ALIGN          # not 256-byte aligned
+    assert prefill(L, dt=0, w=A + 256 * MB, wb=need) == ALIAS    # workspace == y
+    assert prefill(L, dt=0, w=A + 64 * MB, wb=need) == ALIAS     # workspace == k
     assert "workspace" in L.gdn_last_error().decode()
-
-
-def prepare(L, q=A, k=A + 64 * MB, al=A + 192 * MB, be=A + 200 * MB, B=1, T=64, H=2, Dk=16, C=16,
-            w=A + 400 * MB, wb=None):
-    if wb is None:
-        wb = L.gdn_prefill_workspace_bytes(B, T, H, Dk, Dk, C, 1)
-    return L.gdn_prefill_prepare(q, k, al, be, B, T, H, Dk, C, w, wb, None)
-
-
-def recurrence(L, q=A, k=A + 64 * MB, v=A + 128 * MB, s0=None, y=A + 256 * MB, sT=None, B=1, T=64, H=2,
-               Dk=16, Dv=16, C=16, w=A + 400 * MB, wb=None):
-    if wb is None:
-        wb = L.gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, C, 1)
-    return L.gdn_prefill_recurrence(q, k, v, s0, y, sT, B, T, H, Dk, Dv, C, w, wb, None)
 
 
 def test_prefill_f32_workspace_required(L):
@@ -108,28 +94,6 @@ def test_prefill_f32_workspace_required(L):
     assert prefill(L, w=ws, wb=need - 1) == WS          # given but too small
     assert prefill(L, w=ws + 16, wb=need) == ALIGN      # given but misaligned
     assert prefill(L, w=A + 256 * MB, wb=need) == ALIAS  # over y
-
-
-def test_stage_validation(L):
-    # every case fails on the host before anything is launched
-    assert prepare(L, q=None) == NULL
-    assert prepare(L, al=None) == NULL
-    assert prepare(L, T=-1) == SHAPE
-    assert prepare(L, Dk=48) == UNSUP
-    assert prepare(L, C=128) == UNSUP
-    assert prepare(L, w=None) == WS
-    assert prepare(L, wb=100) == WS
-    assert prepare(L, w=A + 400 * MB + 16) == ALIGN
-    assert prepare(L, w=A) == ALIAS                                  # workspace == q
-    assert "gdn_prefill_prepare" in L.gdn_last_error().decode()
-    assert recurrence(L, v=None) == NULL
-    assert recurrence(L, y=None) == NULL
-    assert recurrence(L, Dv=256) == UNSUP
-    assert recurrence(L, w=None) == WS
-    assert recurrence(L, y=A + 16) == ALIAS                          # y inside q
-    assert recurrence(L, w=A + 256 * MB) == ALIAS                    # workspace == y
-    assert recurrence(L, s0=A + 300 * MB, sT=A + 300 * MB + 256) == ALIAS
-    assert "gdn_prefill_recurrence" in L.gdn_last_error().decode()
 
 
 def decode(L, q=A, k=A + MB, v=A + 2 * MB, al=A + 3 * MB, be=A + 4 * MB, S=A + 8 * MB, y=A + 64 * MB,
@@ -218,25 +182,15 @@ def test_layer_decode_validation(L):
 
 
 def test_workspace_queries(L):
-    # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
-    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
-    # fp32: optional records of the two-kernel path, 3*64*64+64 floats per chunk
+    # bf16 prefill: no workspace (every chunk quantity is formed on chip)
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 0
+    # fp32: records of the two-kernel path, 3*64*64 + 2*64 floats per 64-token chunk
     assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 4 * 32 * 512 * 12416
-    assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
-    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
+    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 0) == 4 * 2 * 3 * 4 * 3136
+    assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 0) == 0
+    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 0) == 0            # rejected shape
     assert L.gdn_layer_workspace_bytes(1, 0, 2048, 16, 128, 128, 4, 64) == 0
     assert L.gdn_layer_workspace_bytes(1, 16384, 2048, 16, 128, 128, 4, 64) > 16384 * 2048
-
-
-def test_bench_record_size_matches_library(L):
-    # the algorithmic-bytes accounting of bench.py uses the record size the
-    # library allocates per (sequence, head, chunk)
-    import sys
-    sys.path.insert(0, ROOT)
-    import bench
-    for C in (16, 32, 64):
-        assert bench.record_bytes(C) == L.gdn_prefill_workspace_bytes(1, C, 1, 128, 128, C, 1)
 
 
 def prefill_bwd(L, q=A, k=A + 8 * MB, v=A + 16 * MB, al=A + 24 * MB, be=A + 25 * MB, s0=A + 26 * MB,

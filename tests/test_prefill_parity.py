@@ -173,26 +173,6 @@ def test_prefill_strong_decay_no_nan(oracle_mod):
     _check(oracle_mod, inp, 64, TOL_BF16)
 
 
-@pytest.mark.parametrize("chunk", [16, 32, 64])
-def test_prefill_stages_equal_fused(oracle_mod, chunk):
-    """gdn_prefill_prepare then gdn_prefill_recurrence on one stream is exactly
-    gdn_prefill_fwd (same kernels, same workspace contents), and matches the oracle."""
-    import torch
-    import linear_attention_token_gated_amd as gdn
-    T = 5 * chunk + 3
-    print(f"case: stages B=2 T={T} H=3 Dk=64 Dv=32 C={chunk} bf16", flush=True)
-    inp = wl.prefill_inputs(2, T, 3, 64, 32, dtype="bf16", s0_std=0.3, seed=77 + chunk)
-    y_f, s_f = _gpu(inp, chunk)
-    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-    ws = torch.empty(gdn.prefill_workspace_bytes(2, T, 3, 64, 32, chunk), dtype=torch.uint8, device=q.device)
-    gdn.prefill_prepare(q, k, dev(inp["alpha"]), dev(inp["beta"]), ws, chunk=chunk)
-    y_s, s_s = gdn.prefill_recurrence(q, k, v, ws, dev(inp["S0"]), chunk=chunk)
-    torch.cuda.synchronize()
-    assert torch.equal(y_s, y_f) and torch.equal(s_s, s_f)
-    y_ref, S_ref = oracle_prefill(oracle_mod, inp)
-    assert rel_err(host(y_s), y_ref) <= TOL_BF16 and rel_err(host(s_s), S_ref) <= TOL_BF16
-
-
 def test_sync_check_mode(oracle_mod, monkeypatch):
     """GDN_SYNC_CHECK=1 makes every call wait for its stream and check for
     kernel errors; results are the same bits as without it."""
