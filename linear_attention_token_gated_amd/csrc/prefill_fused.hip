@@ -29,12 +29,12 @@
 //              A_pp and some blocks of A below the diagonal); T_pp =
 //              (I + A_pp)^-1 by forward substitution -> LDS
 //     Y-phase: column p of T from the blocks of all waves,
-//              T_mp = -T_mm sum_{j=p}^{m-1} A_mj T_jp; T' column p -> LDS;
-//              the register-staged q, k, v, alpha, beta of chunk c + 2 -> LDS
+//              T_mp = -T_mm sum_{j=p}^{m-1} A_mj T_jp; T' column p -> LDS
 //
-// q, k and v tiles are loaded into registers by the preparation waves 1.5
-// chunks before they are written to LDS.  Rows past the end of the sequence
-// are zeros with alpha = 1 and beta = 0 (identity tokens).
+// The chain waves also stage the inputs: the q, k, v rows and gates of token
+// block w of chunk c + 2 are loaded into registers at the start of iteration c
+// and written to LDS at its end.  Rows past the end of the sequence are zeros
+// with alpha = 1 and beta = 0 (identity tokens).
 //
 // Precision: q, k, v are exact bf16 operands and every product accumulates in
 // fp32.  Operands computed in fp32 (S in Q S, R, U, T, T', P, the level
@@ -179,7 +179,10 @@ __device__ __forceinline__ Frag<__bf16, 32> pair16(bf16x4 a, bf16x4 b) {
 }
 
 // sum over the blocks k < N of A_k B_k, hi/lo pairs (three products each), two
-// blocks per 32-deep MFMA and a 16-deep one for an odd last block
+// blocks per 32-deep MFMA and a 16-deep one for an odd last block.  The 16-deep
+// products accumulate apart and are added after: a 16x16x16 MFMA that takes the
+// result of a 16x16x32 one as its accumulator input straight away reads a stale
+// value on gfx950 (the compiler inserts no wait states between the two shapes).
 template <int N>
 __device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al, const bf16x4 *bh,
                                               const bf16x4 *bl, f32x4 &acc, f32x4 &acc2) {
@@ -196,9 +199,11 @@ __device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al
     if constexpr (N % 2) {
         F16 a, a2, b, b2;
         a.v = ah[N - 1]; a2.v = al[N - 1]; b.v = bh[N - 1]; b2.v = bl[N - 1];
-        acc = F16::mma(a, b, acc);
-        acc2 = F16::mma(a, b2, acc2);
-        acc2 = F16::mma(a2, b, acc2);
+        f32x4 t = F16::mma(a, b, zero4());
+        f32x4 t2 = F16::mma(a, b2, zero4());
+        t2 = F16::mma(a2, b, t2);
+        acc += t;
+        acc2 += t2;
     }
 }
 
@@ -284,6 +289,70 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
         }
+        // register staging of the q, k, v rows of token block w and of the gates
+        struct Stage {
+            FDK kf[NK], qf[NK];
+            bf16x8 vv;
+            float ab;
+        };
+        Stage st;
+        auto load_stage = [&](Stage &s, int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                const int64_t t = c0 + 16 * w + ln;
+                const int64_t tc = t < T ? t : T - 1;
+                const __bf16 *kr = p.k + (b * T + tc) * p.ks + h * DK;
+                const __bf16 *qr = p.q + (b * T + tc) * p.qs + h * DK;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    s.kf[kk].load(kr + kk * KSD + lg * (KSD / 4));
+                    s.qf[kk].load(qr + kk * KSD + lg * (KSD / 4));
+                }
+                const int l32 = lane & 31;
+                const int64_t tv = c0 + 16 * w + (l32 >> 1);
+                const int64_t tvc = tv < T ? tv : T - 1;
+                s.vv = *reinterpret_cast<const bf16x8 *>(p.v + (b * T + tvc) * p.vs + h * Dv + n0 + (l32 & 1) * 8);
+                const int64_t tg = c0 + 16 * w + (lane & 15);
+                const int64_t tgc = tg < T ? tg : T - 1;
+                s.ab = (lane & 16) ? p.beta[(b * T + tgc) * H + h] : p.alpha[(b * T + tgc) * H + h];
+            }
+        };
+        auto write_stage = [&](const Stage &s, int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                __bf16 *Kd = Kb((int)(j % 3));
+                __bf16 *Qd = Qb((int)(j & 1));
+                const int row = 16 * w + ln;
+                const bool ok = c0 + row < T;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    FDK kz = s.kf[kk], qz = s.qf[kk];
+                    if (!ok) {
+#pragma unroll
+                        for (int e = 0; e < KSD / 4; ++e) {
+                            kz.set(e, 0.f);
+                            qz.set(e, 0.f);
+                        }
+                    }
+                    *reinterpret_cast<decltype(kz.v) *>(Kd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = kz.v;
+                    *reinterpret_cast<decltype(qz.v) *>(Qd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = qz.v;
+                }
+                if (lane < 32) {
+                    const int r = 16 * w + (lane >> 1);
+                    bf16x8 vz = s.vv;
+                    if (c0 + r >= T) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
+                    }
+                    *reinterpret_cast<bf16x8 *>(Vb((int)(j & 1)) + r * BV + (lane & 1) * 8) = vz;
+                    const int rg = 16 * w + (lane & 15);
+                    const bool okg = c0 + rg < T;
+                    // alpha of a padding token is 1, beta 0
+                    ABb((int)(j & 1))[(lane & 16 ? C : 0) + rg] = okg ? s.ab : (lane & 16 ? 0.f : 1.f);
+                }
+            }
+        };
+
         auto write_state_operand = [&]() {
 #pragma unroll
             for (int m = 0; m < MS; ++m) {
@@ -296,50 +365,52 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
         };
+        // chunk 0 into LDS
+        load_stage(st, 0);
+        write_stage(st, 0);
         lds_barrier();                              // chunk 0 staged
-        // iteration -1: nothing but the state operand
-        lds_barrier();
-        write_state_operand();
-        lds_barrier();
-        int kb = 0, qb = 0;                          // c % 3, c % 2
-        for (int64_t c = 0; c <= NC; ++c) {
-            if (c == NC) {                           // outputs of the last chunk: two more barriers
-                lds_barrier();
-                lds_barrier();
-                break;
-            }
+
+        // iteration c (c = -1 .. NC): X-phase: loads of chunk c+2, K S, Q S, R of
+        // chunk c; Y-phase: U, the state update, then chunk c+2 into LDS
+        int kb = 0;                                  // c % 3 for c >= 0
+        for (int64_t c = -1; c <= NC; ++c) {
+            if (c + 2 < NC) load_stage(st, c + 2);
+            const bool work = c >= 0 && c < NC;
+            const int qb = (int)(c & 1);
             const __bf16 *Ks = Kb(kb);
             const float *dec = DECb(qb);
             // ---- X-phase: K_w S, Q_w S -> R_w
             f32x4 egqs = zero4();
             if constexpr (has_rb) {
-                const __bf16 *Qs = Qb(qb);
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * w + 4 * lg);
-                const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
-                f32x4 ks = zero4(), qs = zero4(), qs2 = zero4();
+                if (work) {
+                    const __bf16 *Qs = Qb(qb);
+                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * w + 4 * lg);
+                    const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
+                    f32x4 ks = zero4(), qs = zero4(), qs2 = zero4();
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const FDK kf = frag_kq<KSD, DK>(Ks, 16 * w, kk * KSD, lane);
-                    const FDK qf = frag_kq<KSD, DK>(Qs, 16 * w, kk * KSD, lane);
-                    const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
-                    const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
-                    ks = FDK::mma(kf, sh, ks);
-                    qs = FDK::mma(qf, sh, qs);
-                    qs2 = FDK::mma(qf, sl, qs2);
+                    for (int kk = 0; kk < NK; ++kk) {
+                        const FDK kf = frag_kq<KSD, DK>(Ks, 16 * w, kk * KSD, lane);
+                        const FDK qf = frag_kq<KSD, DK>(Qs, 16 * w, kk * KSD, lane);
+                        const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
+                        const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
+                        ks = FDK::mma(kf, sh, ks);
+                        qs = FDK::mma(qf, sh, qs);
+                        qs2 = FDK::mma(qf, sl, qs2);
+                    }
+                    f32x4 rv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
+                    bf16x4 hv, lv;
+                    split4(rv, hv, lv);
+                    Rs[w * 128 + lane] = hv;
+                    Rs[w * 128 + 64 + lane] = lv;
+                    egqs = eg * (qs + qs2);
                 }
-                f32x4 rv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
-                bf16x4 hv, lv;
-                split4(rv, hv, lv);
-                Rs[w * 128 + lane] = hv;
-                Rs[w * 128 + 64 + lane] = lv;
-                egqs = eg * (qs + qs2);
             }
             lds_barrier();
             // ---- Y-phase: U = T' R (every token block), state update
-            {
-                const int ts = (int)(c & 1);
+            if (work) {
+                const int ts = qb;
                 bf16x4 rh[NB], rl[NB], udh[NB], udl[NB];
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
@@ -390,11 +461,11 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                         S[m] = acc + acc2;
                     }
                 }
-                write_state_operand();
             }
+            if (c < NC) write_state_operand();       // c = -1: the initial state
+            if (c + 2 < NC) write_stage(st, c + 2);
             lds_barrier();
-            kb = kb == 2 ? 0 : kb + 1;
-            qb ^= 1;
+            if (c >= 0) kb = kb == 2 ? 0 : kb + 1;
         }
         if (p.sT) {
             float *sT = p.sT + bh * (int64_t)DK * Dv;
@@ -414,70 +485,6 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
         constexpr int pw = decltype(p_c)::value;
         constexpr bool has_rb = pw < NB;
         double *GS = reinterpret_cast<double *>(smem + L::oGS) + pw * C;
-
-        // register staging of the q, k, v rows of token block pw and of the gates
-        struct Stage {
-            FDK kf[NK], qf[NK];
-            bf16x8 vv;
-            float ab;
-        };
-        Stage st[2];
-        auto load_stage = [&](Stage &s, int64_t j) {
-            if constexpr (has_rb) {
-                const int64_t c0 = j * C;
-                const int64_t t = c0 + 16 * pw + ln;
-                const int64_t tc = t < T ? t : T - 1;
-                const __bf16 *kr = p.k + (b * T + tc) * p.ks + h * DK;
-                const __bf16 *qr = p.q + (b * T + tc) * p.qs + h * DK;
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    s.kf[kk].load(kr + kk * KSD + lg * (KSD / 4));
-                    s.qf[kk].load(qr + kk * KSD + lg * (KSD / 4));
-                }
-                const int l32 = lane & 31;
-                const int64_t tv = c0 + 16 * pw + (l32 >> 1);
-                const int64_t tvc = tv < T ? tv : T - 1;
-                s.vv = *reinterpret_cast<const bf16x8 *>(p.v + (b * T + tvc) * p.vs + h * Dv + n0 + (l32 & 1) * 8);
-                const int64_t tg = c0 + 16 * pw + (lane & 15);
-                const int64_t tgc = tg < T ? tg : T - 1;
-                s.ab = (lane & 16) ? p.beta[(b * T + tgc) * H + h] : p.alpha[(b * T + tgc) * H + h];
-            }
-        };
-        auto write_stage = [&](const Stage &s, int64_t j) {
-            if constexpr (has_rb) {
-                const int64_t c0 = j * C;
-                __bf16 *Kd = Kb((int)(j % 3));
-                __bf16 *Qd = Qb((int)(j & 1));
-                const int row = 16 * pw + ln;
-                const bool ok = c0 + row < T;
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    FDK kz = s.kf[kk], qz = s.qf[kk];
-                    if (!ok) {
-#pragma unroll
-                        for (int e = 0; e < KSD / 4; ++e) {
-                            kz.set(e, 0.f);
-                            qz.set(e, 0.f);
-                        }
-                    }
-                    *reinterpret_cast<decltype(kz.v) *>(Kd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = kz.v;
-                    *reinterpret_cast<decltype(qz.v) *>(Qd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = qz.v;
-                }
-                if (lane < 32) {
-                    const int r = 16 * pw + (lane >> 1);
-                    bf16x8 vz = s.vv;
-                    if (c0 + r >= T) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
-                    }
-                    *reinterpret_cast<bf16x8 *>(Vb((int)(j & 1)) + r * BV + (lane & 1) * 8) = vz;
-                    const int rg = 16 * pw + (lane & 15);
-                    const bool okg = c0 + rg < T;
-                    // alpha of a padding token is 1, beta 0
-                    ABb((int)(j & 1))[(lane & 16 ? C : 0) + rg] = okg ? s.ab : (lane & 16 ? 0.f : 1.f);
-                }
-            }
-        };
 
         // P row pw of a chunk as bf16 hi/lo A operands (lane (r, g): P[r][4g + e]),
         // kept from the chunk's preparation until its output is formed
@@ -635,24 +642,17 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             }
         };
 
-        // chunk 0 into LDS, chunk 1 in flight
-        load_stage(st[0], 0);
-        if (NC > 1) load_stage(st[1], 1);
-        write_stage(st[0], 0);
-        lds_barrier();
+        lds_barrier();                              // chunk 0 staged
 
-        // iteration c: X-phase (outputs of c-1, loads of c+3, preparation of c+1),
-        // Y-phase (T' of c+1, chunk c+2 into LDS).  Register sets by parity:
-        // loads of chunk j and the P row of chunk j use set j & 1.
+        // iteration c: X-phase (outputs of c-1, preparation of c+1), Y-phase
+        // (T' of c+1).  The P row of chunk j uses register set j & 1.
         auto iter = [&](auto par_c, int64_t c) {
             constexpr int par = decltype(par_c)::value;    // == (c + 1) & 1
             using PAR = std::integral_constant<int, par>;
             if (c >= 1) out_y(PAR{}, c - 1);
-            if (c + 3 < NC) load_stage(st[par], c + 3);
             if (c + 1 < NC) prep_x(PAR{}, c + 1);
             lds_barrier();
             if (c + 1 < NC) prep_y(c + 1);
-            if (c + 2 < NC) write_stage(st[1 - par], c + 2);
             lds_barrier();
         };
         for (int64_t c = -1; c <= NC; c += 2) {
