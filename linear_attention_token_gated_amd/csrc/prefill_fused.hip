@@ -72,23 +72,27 @@ template <int C, int DK> struct FL {
     static constexpr size_t KQB = (size_t)2 * C * DK;                   // one K or Q chunk
     static constexpr size_t VB = (size_t)2 * C * BV;                    // one V slice
     static constexpr size_t ABB = (size_t)8 * C;                        // alpha[C] | beta[C]
+    // decay table of one chunk: G[C] (fp64) | 2^G[C] | 2^(G_C - G)[C] | HC[C] |
+    // FR[NB - 1][C] | 2^G_C, with HC and FR the column and row factors of the
+    // decay ratios of the blocks below the diagonal
+    static constexpr size_t DT_EG = 8 * C, DT_ED = 12 * C, DT_HC = 16 * C, DT_FR = 20 * C;
+    static constexpr size_t DT_EGC = DT_FR + (size_t)4 * (NB - 1) * C;
+    static constexpr size_t DTB = align16(DT_EGC + 16);
     static constexpr size_t oK = 0;                                     // [3] K chunks
     static constexpr size_t oQ = oK + 3 * KQB;                          // [2] Q chunks
     static constexpr size_t oV = oQ + 2 * KQB;                          // [2] V slices [C][16]
-    static constexpr size_t oAB = oV + 2 * VB;                          // [2] gates
-    static constexpr size_t oSTh = align16(oAB + 2 * ABB);              // S^T operand, hi
+    static constexpr size_t oAB = oV + 2 * VB;                          // [4] gates
+    static constexpr size_t oSTh = align16(oAB + 4 * ABB);              // S^T operand, hi
     static constexpr size_t oSTl = oSTh + align16(2 * BV * KPS);        // S^T operand, lo
     static constexpr size_t oR = oSTl + align16(2 * BV * KPS);          // R [NB][hi|lo][64] bf16x4
     static constexpr size_t oTP = oR + (size_t)NB * 1024;               // [2][NTRI] T'^T blocks, hi|lo
     static constexpr size_t TPB = (size_t)NTRI * 1024;
-    static constexpr size_t oDEC = oTP + 2 * TPB;                       // [2] EG[C] | Ed[C] | EGC
-    static constexpr size_t DECB = align16(4 * (2 * C + 4));
-    static constexpr size_t oXT = oDEC + 2 * DECB;                      // [NB] T_mm row-major, hi|lo
+    static constexpr size_t oDT = oTP + 2 * TPB;                        // [4] decay tables
+    static constexpr size_t oXT = oDT + 4 * DTB;                        // [NB] T_mm row-major, hi|lo
     static constexpr size_t oXA = oXT + (size_t)NB * 1024;              // [NOFF] A_mj row-major, hi|lo
     static constexpr size_t oUQ = oXA + (size_t)(NOFF > 0 ? NOFF : 1) * 1024;   // U_w [NB][hi|lo][64] bf16x4
     static constexpr size_t oQS = oUQ + (size_t)NB * 1024;              // 2^G Q_w S [NB][64] f32x4
-    static constexpr size_t oGS = oQS + (size_t)NB * 1024;              // [4][C] decay prefix, fp64
-    static constexpr size_t BYTES = oGS + (size_t)4 * C * 8;
+    static constexpr size_t BYTES = oQS + (size_t)NB * 1024;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -178,55 +182,44 @@ __device__ __forceinline__ Frag<__bf16, 32> pair16(bf16x4 a, bf16x4 b) {
     return f;
 }
 
-// sum over the blocks k < N of A_k B_k, hi/lo pairs (three products each), two
-// blocks per 32-deep MFMA and a 16-deep one for an odd last block.  The 16-deep
-// products accumulate apart and are added after: a 16x16x16 MFMA that takes the
-// result of a 16x16x32 one as its accumulator input straight away reads a stale
-// value on gfx950 (the compiler inserts no wait states between the two shapes).
-template <int N>
-__device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al, const bf16x4 *bh,
-                                              const bf16x4 *bl, f32x4 &acc, f32x4 &acc2) {
-    using F16 = Frag<__bf16, 16>;
-    using F32 = Frag<__bf16, 32>;
-    static_for<N / 2>([&](auto i_c) {
-        constexpr int k = 2 * decltype(i_c)::value;
-        const F32 a = pair16(ah[k], ah[k + 1]), a2 = pair16(al[k], al[k + 1]);
-        const F32 b = pair16(bh[k], bh[k + 1]), b2 = pair16(bl[k], bl[k + 1]);
-        acc = F32::mma(a, b, acc);
-        acc2 = F32::mma(a, b2, acc2);
-        acc2 = F32::mma(a2, b, acc2);
-    });
-    if constexpr (N % 2) {
-        F16 a, a2, b, b2;
-        a.v = ah[N - 1]; a2.v = al[N - 1]; b.v = bh[N - 1]; b2.v = bl[N - 1];
-        f32x4 t = F16::mma(a, b, zero4());
-        f32x4 t2 = F16::mma(a, b2, zero4());
-        t2 = F16::mma(a2, b, t2);
-        acc += t;
-        acc2 += t2;
-    }
-}
-
-// hi/lo product of one 16x16x16 pair (three products)
-__device__ __forceinline__ f32x4 mma_hilo16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl) {
+// acc += A B for one 16 x 16 block pair held as bf16 hi/lo parts: the three
+// products hi*hi + hi*lo + lo*hi on 16-deep MFMAs into the one accumulator.
+// Accumulators that pass through here only ever meet 16x16x16 MFMAs: a 16x16x16
+// MFMA that takes the result of a 16x16x32 one as its accumulator input at once
+// reads a stale value on gfx950 (the compiler inserts no wait states between the
+// two shapes).
+__device__ __forceinline__ f32x4 mma_hl(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 acc) {
     using F16 = Frag<__bf16, 16>;
     F16 a, a2, b, b2;
     a.v = ah; a2.v = al; b.v = bh; b2.v = bl;
-    f32x4 acc = F16::mma(a, b, zero4());
-    f32x4 acc2 = F16::mma(a, b2, zero4());
-    acc2 = F16::mma(a2, b, acc2);
-    return acc + acc2;
+    acc = F16::mma(a, b, acc);
+    acc = F16::mma(a, b2, acc);
+    return F16::mma(a2, b, acc);
 }
 
-template <int S> __device__ __forceinline__ void fsub_step(float (&X)[4], const float (&Lr)[16]) {
-    // rows r <= S have L[r][S] = 0 (strictly lower): the update is an exact no-op there
-#pragma unroll
-    for (int e = 0; e < 4; ++e) X[e] = fmaf(-Lr[S], row_bcast<S>(X[e]), X[e]);
+// X <- (I - nL)^-1 X for a 16 x 16 block by forward substitution, lane (r, g)
+// holding X[r][4g + e] and nL[r][:] = -L[r][:] (strictly lower): step S adds
+// nL[r][S] X[S][:] to every row r (a no-op for r <= S).  X[S][:] sits in lane S
+// of the same 16-lane row and is read through a DPP row broadcast folded into
+// the multiply-add.  The fifteen steps are one asm statement, so nothing is
+// scheduled between them: a DPP read of a VGPR needs two wait states after a
+// VALU write of it, which the s_nop gives the writes before the first step;
+// inside, the other three columns of a step sit between a write and its read.
+#define GDN_FS1(S, E, N) "v_fmac_f32_dpp %" #E ", %" #E ", %" #N " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n"
+#define GDN_FS(S, N) GDN_FS1(S, 0, N) GDN_FS1(S, 1, N) GDN_FS1(S, 2, N) GDN_FS1(S, 3, N)
+__device__ __forceinline__ void fsub16(float (&X)[4], const float (&nL)[16]) {
+    asm volatile("s_nop 1\n"
+                 GDN_FS(0, 4) GDN_FS(1, 5) GDN_FS(2, 6) GDN_FS(3, 7) GDN_FS(4, 8)
+                 GDN_FS(5, 9) GDN_FS(6, 10) GDN_FS(7, 11) GDN_FS(8, 12) GDN_FS(9, 13)
+                 GDN_FS(10, 14) GDN_FS(11, 15) GDN_FS(12, 16) GDN_FS(13, 17) GDN_FS(14, 18)
+                 "s_nop 1"
+                 : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                 : "v"(nL[0]), "v"(nL[1]), "v"(nL[2]), "v"(nL[3]), "v"(nL[4]), "v"(nL[5]), "v"(nL[6]),
+                   "v"(nL[7]), "v"(nL[8]), "v"(nL[9]), "v"(nL[10]), "v"(nL[11]), "v"(nL[12]), "v"(nL[13]),
+                   "v"(nL[14]));
 }
-template <int... S>
-__device__ __forceinline__ void fsub16(float (&X)[4], const float (&Lr)[16], std::integer_sequence<int, S...>) {
-    (fsub_step<S>(X, Lr), ...);
-}
+#undef GDN_FS
+#undef GDN_FS1
 
 template <int C, int DK>
 __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
@@ -234,8 +227,11 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
     using L = FL<C, DK>;
     using FDK = Frag<__bf16, L::KSD>;
     using FC = Frag<__bf16, L::KSC>;
+    using F16 = Frag<__bf16, 16>;
     constexpr int NB = L::NB, NSB = L::NSB, MS = L::MS, NTRI = L::NTRI, KSD = L::KSD, NK = L::NK;
     constexpr int KSC = L::KSC, NJ = L::NJ, KPS = L::KPS;
+    constexpr int NBO = NB > 1 ? NB - 1 : 1;     // register blocks of P below the diagonal
+    static_assert(NTRI >= 1, "chunk");
 
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     auto Kb = [&](int i) { return reinterpret_cast<__bf16 *>(smem + L::oK + (size_t)i * L::KQB); };
@@ -243,7 +239,7 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
     auto Vb = [&](int i) { return reinterpret_cast<__bf16 *>(smem + L::oV + (size_t)i * L::VB); };
     auto ABb = [&](int i) { return reinterpret_cast<float *>(smem + L::oAB + (size_t)i * L::ABB); };
     auto TPb = [&](int s, int blk) { return reinterpret_cast<__bf16 *>(smem + L::oTP + (size_t)s * L::TPB + (size_t)blk * 1024); };
-    auto DECb = [&](int s) { return reinterpret_cast<float *>(smem + L::oDEC + (size_t)s * L::DECB); };
+    auto DTb = [&](int s) { return smem + L::oDT + (size_t)s * L::DTB; };
     auto XTb = [&](int m) { return reinterpret_cast<__bf16 *>(smem + L::oXT + (size_t)m * 1024); };
     auto XAb = [&](int o) { return reinterpret_cast<__bf16 *>(smem + L::oXA + (size_t)o * 1024); };
     __bf16 *STh = reinterpret_cast<__bf16 *>(smem + L::oSTh);
@@ -271,6 +267,17 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
     const int n0 = (int)sl * BV;
     const int64_t NC = (T + C - 1) / C;
 
+    // lane offsets (elements) of the K / Q fragments of block 0 of a chunk in LDS;
+    // block j adds 16 j DK, since 16 j leaves the granule permutation unchanged
+    int kqo[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kqo[kk] = kq_idx<DK>(ln, kk * KSD + lg * (KSD / 4));
+    auto frag_blk = [&](const __bf16 *X, int blk, int kk) {
+        FDK f;
+        f.load(X + blk * 16 * DK + kqo[kk]);
+        return f;
+    };
+
     // ======================= chain waves =======================
     auto chain_wave = [&](auto w_c) {
         constexpr int w = decltype(w_c)::value;
@@ -289,67 +296,103 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
         }
-        // register staging of the q, k, v rows of token block w and of the gates
+        // global bases of token 0 of this (b, h) and lane offsets within a chunk
+        const __bf16 *kg = p.k + b * T * p.ks + h * DK;
+        const __bf16 *qg = p.q + b * T * p.qs + h * DK;
+        const __bf16 *vg = p.v + b * T * p.vs + h * Dv + n0;
+        const float *ag = p.alpha + b * T * H + h;
+        const float *bg = p.beta + b * T * H + h;
+        const int rowk = 16 * w + ln;                        // K / Q row and gate token
+        const int l32 = lane & 31, rowv = 16 * w + (l32 >> 1);   // V row
+        const uint32_t ok0 = (uint32_t)(rowk * p.ks) + lg * (KSD / 4);
+        const uint32_t oq0 = (uint32_t)(rowk * p.qs) + lg * (KSD / 4);
+        const uint32_t ov0 = (uint32_t)(rowv * p.vs) + (l32 & 1) * 8;
+        const uint32_t og0 = (uint32_t)(rowk * H);
+
+        // register staging: q, k, v rows of token block w of one chunk, the
+        // gates of token block w of another
         struct Stage {
             FDK kf[NK], qf[NK];
             bf16x8 vv;
-            float ab;
+            float ga, gb;
         };
         Stage st;
-        auto load_stage = [&](Stage &s, int64_t j) {
-            if constexpr (has_rb) {
+        auto load_stage = [&](Stage &s, int64_t j, int64_t jg) {
+            if constexpr (!has_rb) return;
+            if (j < NC) {
                 const int64_t c0 = j * C;
-                const int64_t t = c0 + 16 * w + ln;
-                const int64_t tc = t < T ? t : T - 1;
-                const __bf16 *kr = p.k + (b * T + tc) * p.ks + h * DK;
-                const __bf16 *qr = p.q + (b * T + tc) * p.qs + h * DK;
+                uint32_t ok = ok0, oq = oq0, ov = ov0;
+                if (c0 + C > T) {                      // last chunk: rows past the end read token T-1
+                    const int64_t last = T - 1 - c0;
+                    const int64_t rk = rowk < last ? rowk : last, rv = rowv < last ? rowv : last;
+                    ok = (uint32_t)(rk * p.ks) + lg * (KSD / 4);
+                    oq = (uint32_t)(rk * p.qs) + lg * (KSD / 4);
+                    ov = (uint32_t)(rv * p.vs) + (l32 & 1) * 8;
+                }
+                const __bf16 *kc = kg + c0 * p.ks, *qc = qg + c0 * p.qs, *vc = vg + c0 * p.vs;
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
-                    s.kf[kk].load(kr + kk * KSD + lg * (KSD / 4));
-                    s.qf[kk].load(qr + kk * KSD + lg * (KSD / 4));
+                    s.kf[kk].load(kc + ok + kk * KSD);
+                    s.qf[kk].load(qc + oq + kk * KSD);
                 }
-                const int l32 = lane & 31;
-                const int64_t tv = c0 + 16 * w + (l32 >> 1);
-                const int64_t tvc = tv < T ? tv : T - 1;
-                s.vv = *reinterpret_cast<const bf16x8 *>(p.v + (b * T + tvc) * p.vs + h * Dv + n0 + (l32 & 1) * 8);
-                const int64_t tg = c0 + 16 * w + (lane & 15);
-                const int64_t tgc = tg < T ? tg : T - 1;
-                s.ab = (lane & 16) ? p.beta[(b * T + tgc) * H + h] : p.alpha[(b * T + tgc) * H + h];
+                s.vv = *reinterpret_cast<const bf16x8 *>(vc + ov);
+            }
+            if (jg < NC && lane < 16) {
+                const int64_t c0 = jg * C;
+                uint32_t og = og0;
+                if (c0 + C > T) {
+                    const int64_t last = T - 1 - c0;
+                    og = (uint32_t)((rowk < last ? rowk : last) * H);
+                }
+                s.ga = (ag + c0 * H)[og];
+                s.gb = (bg + c0 * H)[og];
             }
         };
-        auto write_stage = [&](const Stage &s, int64_t j) {
-            if constexpr (has_rb) {
+        auto write_stage = [&](const Stage &s, int64_t j, int64_t jg) {
+            if constexpr (!has_rb) return;
+            if (j < NC) {
                 const int64_t c0 = j * C;
-                __bf16 *Kd = Kb((int)(j % 3));
-                __bf16 *Qd = Qb((int)(j & 1));
-                const int row = 16 * w + ln;
-                const bool ok = c0 + row < T;
+                __bf16 *Kd = Kb((int)(j % 3)) + w * 16 * DK;
+                __bf16 *Qd = Qb((int)(j & 1)) + w * 16 * DK;
+                __bf16 *Vd = Vb((int)(j & 1)) + rowv * BV + (l32 & 1) * 8;
+                if (c0 + C <= T) {
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    FDK kz = s.kf[kk], qz = s.qf[kk];
-                    if (!ok) {
+                    for (int kk = 0; kk < NK; ++kk) {
+                        *reinterpret_cast<decltype(s.kf[kk].v) *>(Kd + kqo[kk]) = s.kf[kk].v;
+                        *reinterpret_cast<decltype(s.qf[kk].v) *>(Qd + kqo[kk]) = s.qf[kk].v;
+                    }
+                    if (lane < 32) *reinterpret_cast<bf16x8 *>(Vd) = s.vv;
+                } else {                               // rows past the end are zeros
+                    const bool ok = c0 + rowk < T;
 #pragma unroll
-                        for (int e = 0; e < KSD / 4; ++e) {
-                            kz.set(e, 0.f);
-                            qz.set(e, 0.f);
+                    for (int kk = 0; kk < NK; ++kk) {
+                        FDK kz = s.kf[kk], qz = s.qf[kk];
+                        if (!ok) {
+#pragma unroll
+                            for (int e = 0; e < KSD / 4; ++e) {
+                                kz.set(e, 0.f);
+                                qz.set(e, 0.f);
+                            }
                         }
+                        *reinterpret_cast<decltype(kz.v) *>(Kd + kqo[kk]) = kz.v;
+                        *reinterpret_cast<decltype(qz.v) *>(Qd + kqo[kk]) = qz.v;
                     }
-                    *reinterpret_cast<decltype(kz.v) *>(Kd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = kz.v;
-                    *reinterpret_cast<decltype(qz.v) *>(Qd + kq_idx<DK>(row, kk * KSD + lg * (KSD / 4))) = qz.v;
-                }
-                if (lane < 32) {
-                    const int r = 16 * w + (lane >> 1);
-                    bf16x8 vz = s.vv;
-                    if (c0 + r >= T) {
+                    if (lane < 32) {
+                        bf16x8 vz = s.vv;
+                        if (c0 + rowv >= T) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
+                            for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
+                        }
+                        *reinterpret_cast<bf16x8 *>(Vd) = vz;
                     }
-                    *reinterpret_cast<bf16x8 *>(Vb((int)(j & 1)) + r * BV + (lane & 1) * 8) = vz;
-                    const int rg = 16 * w + (lane & 15);
-                    const bool okg = c0 + rg < T;
-                    // alpha of a padding token is 1, beta 0
-                    ABb((int)(j & 1))[(lane & 16 ? C : 0) + rg] = okg ? s.ab : (lane & 16 ? 0.f : 1.f);
                 }
+            }
+            if (jg < NC && lane < 16) {
+                // alpha of a padding token is 1, beta 0
+                const bool okg = jg * C + rowk < T;
+                float *abd = ABb((int)(jg & 3));
+                abd[rowk] = okg ? s.ga : 1.f;
+                abd[C + rowk] = okg ? s.gb : 0.f;
             }
         };
 
@@ -365,47 +408,52 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
         };
-        // chunk 0 into LDS
-        load_stage(st, 0);
-        write_stage(st, 0);
-        lds_barrier();                              // chunk 0 staged
+        // chunk 0 and the gates of chunks 0 and 1 into LDS, then the decay table of
+        // chunk 0 (preparation wave 3)
+        load_stage(st, 0, 0);
+        write_stage(st, 0, 0);
+        load_stage(st, NC, 1);
+        write_stage(st, NC, 1);
+        lds_barrier();
+        lds_barrier();
 
-        // iteration c (c = -1 .. NC): X-phase: loads of chunk c+2, K S, Q S, R of
-        // chunk c; Y-phase: U, the state update, then chunk c+2 into LDS
+        // iteration c (c = -1 .. NC): X-phase: loads of chunk c+2 (gates of c+3),
+        // K S, Q S, R of chunk c; Y-phase: U, the state update, staging into LDS
         int kb = 0;                                  // c % 3 for c >= 0
+#pragma unroll 1
         for (int64_t c = -1; c <= NC; ++c) {
-            if (c + 2 < NC) load_stage(st, c + 2);
+            load_stage(st, c + 2, c + 3);
             const bool work = c >= 0 && c < NC;
             const int qb = (int)(c & 1);
             const __bf16 *Ks = Kb(kb);
-            const float *dec = DECb(qb);
+            const char *dt = DTb((int)(c & 3));
+            const float *EG = reinterpret_cast<const float *>(dt + L::DT_EG);
+            const float *Ed = reinterpret_cast<const float *>(dt + L::DT_ED);
             // ---- X-phase: K_w S, Q_w S -> R_w
             f32x4 egqs = zero4();
-            if constexpr (has_rb) {
-                if (work) {
-                    const __bf16 *Qs = Qb(qb);
-                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(dec + 16 * w + 4 * lg);
-                    const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
-                    f32x4 ks = zero4(), qs = zero4(), qs2 = zero4();
+            if (has_rb && work) {
+                const __bf16 *Qs = Qb(qb);
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(EG + 16 * w + 4 * lg);
+                const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
+                f32x4 ks = zero4(), qs = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < NK; ++kk) {
-                        const FDK kf = frag_kq<KSD, DK>(Ks, 16 * w, kk * KSD, lane);
-                        const FDK qf = frag_kq<KSD, DK>(Qs, 16 * w, kk * KSD, lane);
-                        const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
-                        const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
-                        ks = FDK::mma(kf, sh, ks);
-                        qs = FDK::mma(qf, sh, qs);
-                        qs2 = FDK::mma(qf, sl, qs2);
-                    }
-                    f32x4 rv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
-                    bf16x4 hv, lv;
-                    split4(rv, hv, lv);
-                    Rs[w * 128 + lane] = hv;
-                    Rs[w * 128 + 64 + lane] = lv;
-                    egqs = eg * (qs + qs2);
+                for (int kk = 0; kk < NK; ++kk) {
+                    const FDK kf = frag_blk(Ks, w, kk);
+                    const FDK qf = frag_blk(Qs, w, kk);
+                    const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
+                    const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
+                    ks = FDK::mma(kf, sh, ks);
+                    qs = FDK::mma(qf, sh, qs);
+                    qs = FDK::mma(qf, sl, qs);
                 }
+                f32x4 rv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
+                bf16x4 hv, lv;
+                split4(rv, hv, lv);
+                Rs[w * 128 + lane] = hv;
+                Rs[w * 128 + 64 + lane] = lv;
+                egqs = eg * qs;
             }
             lds_barrier();
             // ---- Y-phase: U = T' R (every token block), state update
@@ -419,16 +467,13 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
                 static_for<NB>([&](auto i_c) {
                     constexpr int i = decltype(i_c)::value;
-                    bf16x4 th[i + 1], tl[i + 1];
+                    f32x4 u = zero4();
 #pragma unroll
                     for (int k = 0; k <= i; ++k) {
-                        th[k] = read_cols16(TPb(ts, tri_idx(i, k)), lane);
-                        tl[k] = read_cols16(TPb(ts, tri_idx(i, k)) + 256, lane);
+                        const __bf16 *tb = TPb(ts, tri_idx(i, k));
+                        u = mma_hl(read_cols16(tb, lane), read_cols16(tb + 256, lane), rh[k], rl[k], u);
                     }
-                    f32x4 u = zero4(), u2 = zero4();
-                    pair_products<i + 1>(th, tl, rh, rl, u, u2);
-                    u += u2;
-                    const f32x4 ed = *reinterpret_cast<const f32x4 *>(dec + C + 16 * i + 4 * lg);
+                    const f32x4 ed = *reinterpret_cast<const f32x4 *>(Ed + 16 * i + 4 * lg);
                     split4(ed * u, udh[i], udl[i]);
                     if constexpr (i == w) {
                         bf16x4 uh, ul;
@@ -438,12 +483,12 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                         QSs[w * 64 + lane] = egqs;
                     }
                 });
-                const float egc = dec[2 * C];
+                const float egc = *reinterpret_cast<const float *>(dt + L::DT_EGC);
 #pragma unroll
                 for (int m = 0; m < MS; ++m) {
                     const int ib = w + 4 * m;
                     if (ib < NSB) {
-                        f32x4 acc = S[m] * egc, acc2 = zero4();
+                        f32x4 acc = S[m] * egc;
 #pragma unroll
                         for (int jj = 0; jj < NJ; ++jj) {
                             const FC ka = k_cols_tr<KSC, DK>(Ks, 16 * ib, jj * KSC, lane);
@@ -456,14 +501,14 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                                 blf.v = udl[jj];
                             }
                             acc = FC::mma(ka, bhf, acc);
-                            acc2 = FC::mma(ka, blf, acc2);
+                            acc = FC::mma(ka, blf, acc);
                         }
-                        S[m] = acc + acc2;
+                        S[m] = acc;
                     }
                 }
             }
             if (c < NC) write_state_operand();       // c = -1: the initial state
-            if (c + 2 < NC) write_stage(st, c + 2);
+            write_stage(st, c + 2, c + 3);
             lds_barrier();
             if (c >= 0) kb = kb == 2 ? 0 : kb + 1;
         }
@@ -484,177 +529,228 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
     auto prep_wave = [&](auto p_c) {
         constexpr int pw = decltype(p_c)::value;
         constexpr bool has_rb = pw < NB;
-        double *GS = reinterpret_cast<double *>(smem + L::oGS) + pw * C;
 
-        // P row pw of a chunk as bf16 hi/lo A operands (lane (r, g): P[r][4g + e]),
-        // kept from the chunk's preparation until its output is formed
-        bf16x4 Ph[2][NB > 0 ? NB : 1], Pl[2][NB > 0 ? NB : 1];
-        float Tdiag[4];                          // T_pp row ln, columns 4 lg + e
+        // P row pw of a chunk as bf16 hi/lo A operands (lane (r, g): P[r][4g + e]):
+        // the blocks left of the diagonal and the diagonal block, kept from the
+        // chunk's preparation until its output is formed; register set j & 1
+        // holds chunk j
+        bf16x4 Ph[2][NBO], Pl[2][NBO], Pdh[2], Pdl[2];
 
         // Gram block D = X_r K_jb^T in row layout (lane (ln, g): D[ln][4g + e])
         auto gram = [&](const __bf16 *Xs, int r, int jb, const __bf16 *Ks) {
+            FDK fa[NK], fb[NK];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                fa[kk] = frag_blk(Ks, jb, kk);
+                fb[kk] = frag_blk(Xs, r, kk);
+            }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk)
-                acc = FDK::mma(frag_kq<KSD, DK>(Ks, 16 * jb, kk * KSD, lane),
-                               frag_kq<KSD, DK>(Xs, 16 * r, kk * KSD, lane), acc);
+            for (int kk = 0; kk < NK; ++kk) acc = FDK::mma(fa[kk], fb[kk], acc);
             return acc;
         };
-        // 2^(G_r - G_j) on and below the diagonal (and strictly below for A), 0 above
-        auto decay_mask = [&](f32x4 d, int r, int jb, bool incl) {
-            const int rt = 16 * r + ln;
-            const double Gr = GS[rt];
+        // decay ratios 2^(G_r - G_j) on a diagonal block (r >= j, or r > j), 0 above
+        auto decay_diag = [&](f32x4 d, int blk, bool incl, const char *dt) {
+            const double *Gd = reinterpret_cast<const double *>(dt) + 16 * blk;
+            const double Gr = Gd[ln];
+            double Gc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gc[e] = Gd[4 * lg + e];
             f32x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int jt = 16 * jb + 4 * lg + e;
-                const bool keep = incl ? rt >= jt : rt > jt;
-                out[e] = keep ? __builtin_amdgcn_exp2f((float)(Gr - GS[jt])) * d[e] : 0.f;
+                const int jc = 4 * lg + e;
+                const bool keep = incl ? ln >= jc : ln > jc;
+                // above the diagonal the exponent is positive and the product discarded
+                const float g = __builtin_amdgcn_exp2f((float)fmin(Gr - Gc[e], 0.0)) * d[e];
+                out[e] = keep ? g : 0.f;
             }
             return out;
         };
+        // decay ratios on block (m, jb), m > jb: row factor f (of row 16 m + ln)
+        // times the column factors of block jb
+        auto decay_off = [&](f32x4 d, float f, int jb, const char *dt) {
+            const f32x4 hc = *reinterpret_cast<const f32x4 *>(dt + L::DT_HC + 4 * (16 * jb + 4 * lg));
+            return d * (hc * f);
+        };
+        auto row_factor = [&](const char *dt, int jb, int m) {
+            return reinterpret_cast<const float *>(dt + L::DT_FR)[jb * C + 16 * m + ln];
+        };
 
-        // X-phase work of chunk j (set par of the P registers)
-        auto prep_x = [&](auto par_c, int64_t j) {
-            constexpr int par = decltype(par_c)::value;
-            const __bf16 *Ks = Kb((int)(j % 3));
-            const __bf16 *Qs = Qb((int)(j & 1));
-            const float *ab = ABb((int)(j & 1));
-            // decay prefix, one token per lane, in fp64
+        // decay table of chunk j from its gates: fp64 prefix G of log2 alpha, then
+        // 2^G, 2^(G_C - G), 2^G_C; with anchor a_jb = G at the last token of block
+        // jb, HC_t = 2^(a_blk(t) - G_t) and FR_jb,t = 2^(G_t - a_jb) (used for
+        // t in later blocks), so that 2^(G_r - G_t) = FR_jb,r HC_t with both
+        // factors at most 1
+        auto decay_table = [&](int64_t j) {
+            const float *ab = ABb((int)(j & 3));
+            char *dt = DTb((int)(j & 3));
             const float al = lane < C ? ab[lane] : 1.f;
             const double G = wave_inclusive_sum_f64(lane < C ? (double)log2_decay(al) : 0.0, lane);
             const double GC = lane_value_f64(G, C - 1);
-            if (lane < C) GS[lane] = G;
-            if constexpr (pw == 0) {
-                float *dec = DECb((int)(j & 1));
-                if (lane < C) {
-                    dec[lane] = __builtin_amdgcn_exp2f((float)G);
-                    dec[C + lane] = __builtin_amdgcn_exp2f((float)(GC - G));
-                }
-                if (lane == 0) dec[2 * C] = __builtin_amdgcn_exp2f((float)GC);
-            }
-            if constexpr (has_rb) {
-                // P row pw
-                static_for<pw + 1>([&](auto jb_c) {
-                    constexpr int jb = decltype(jb_c)::value;
-                    const f32x4 d = decay_mask(gram(Qs, pw, jb, Ks), pw, jb, true);
-                    split4(d, Ph[par][jb], Pl[par][jb]);
-                });
-                // A_pp: fp32 rows through the T_pp slot (scratch), then forward substitution
-                {
-                    const float bet = ab[C + 16 * pw + ln];
-                    const f32x4 d = decay_mask(gram(Ks, pw, pw, Ks), pw, pw, false) * bet;
-                    float *scr = reinterpret_cast<float *>(XTb(pw));
-                    *reinterpret_cast<f32x4 *>(scr + ln * 16 + 4 * lg) = d;
-                    float Lr[16];
+            double anc[NB];
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(scr + ln * 16 + 4 * s4);
-                        Lr[4 * s4] = v4[0]; Lr[4 * s4 + 1] = v4[1]; Lr[4 * s4 + 2] = v4[2]; Lr[4 * s4 + 3] = v4[3];
-                    }
+            for (int jb = 0; jb < NB; ++jb) anc[jb] = lane_value_f64(G, 16 * jb + 15);
+            if (lane < C) {
+                float *f = reinterpret_cast<float *>(dt);
+                reinterpret_cast<double *>(dt)[lane] = G;
+                f[L::DT_EG / 4 + lane] = __builtin_amdgcn_exp2f((float)G);
+                f[L::DT_ED / 4 + lane] = __builtin_amdgcn_exp2f((float)(GC - G));
+                const int blk = lane >> 4;
+                double a = anc[0];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Tdiag[e] = ln == 4 * lg + e ? 1.f : 0.f;
-                    fsub16(Tdiag, Lr, std::make_integer_sequence<int, 15>{});
-                    bf16x4 hv, lv;
-                    split4(f32x4{Tdiag[0], Tdiag[1], Tdiag[2], Tdiag[3]}, hv, lv);
-                    // the scratch rows were read above (same wavefront, LDS in order)
-                    *reinterpret_cast<bf16x4 *>(XTb(pw) + ln * 16 + 4 * lg) = hv;
-                    *reinterpret_cast<bf16x4 *>(XTb(pw) + 256 + ln * 16 + 4 * lg) = lv;
-                }
-                // blocks of A below the diagonal owned by this wave
-                static_for<NB>([&](auto m_c) {
-                    constexpr int m = decltype(m_c)::value;
-                    static_for<m>([&](auto jj_c) {
-                        constexpr int jj = decltype(jj_c)::value;
-                        if constexpr (a_owner<NB>(m, jj) == pw) {
-                            const float bet = ab[C + 16 * m + ln];
-                            const f32x4 d = decay_mask(gram(Ks, m, jj, Ks), m, jj, false) * bet;
-                            bf16x4 hv, lv;
-                            split4(d, hv, lv);
-                            constexpr int o = off_idx_c(m, jj);
-                            *reinterpret_cast<bf16x4 *>(XAb(o) + ln * 16 + 4 * lg) = hv;
-                            *reinterpret_cast<bf16x4 *>(XAb(o) + 256 + ln * 16 + 4 * lg) = lv;
-                        }
-                    });
-                });
+                for (int jb = 1; jb < NB; ++jb) a = blk == jb ? anc[jb] : a;
+                f[L::DT_HC / 4 + lane] = __builtin_amdgcn_exp2f((float)(a - G));
+#pragma unroll
+                for (int jb = 0; jb < NB - 1; ++jb)
+                    f[L::DT_FR / 4 + jb * C + lane] = blk > jb ? __builtin_amdgcn_exp2f((float)(G - anc[jb])) : 0.f;
             }
+            if (lane == 0) *reinterpret_cast<float *>(dt + L::DT_EGC) = __builtin_amdgcn_exp2f((float)GC);
         };
 
-        // Y-phase work of chunk j: column pw of T, T' column pw into slot j % 2
-        auto prep_y = [&](int64_t j) {
-            if constexpr (has_rb) {
-                constexpr int k = pw;
-                const int ts = (int)(j & 1);
-                const float bcol = ABb((int)(j & 1))[C + 16 * k + ln];
-                bf16x4 bh[NB], bl[NB];                  // T_jk in accumulator layout, hi/lo
-                bh[k] = read_cols16(XTb(k), lane);
-                bl[k] = read_cols16(XTb(k) + 256, lane);
-                {
-                    f32x4 t;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) t[e] = ((float)bh[k][e] + (float)bl[k][e]) * bcol;
-                    bf16x4 hv, lv;
-                    split4(t, hv, lv);
-                    write_acc_transposed(TPb(ts, tri_idx(k, k)), hv, lane);
-                    write_acc_transposed(TPb(ts, tri_idx(k, k)) + 256, lv, lane);
+        // X-phase work of chunk j; its P row goes to register set par
+        auto prep_x = [&](auto par_c, int64_t j) {
+            constexpr int par = decltype(par_c)::value;
+            if constexpr (!has_rb) return;
+            const __bf16 *Ks = Kb((int)(j % 3));
+            const __bf16 *Qs = Qb((int)(j & 1));
+            const float *ab = ABb((int)(j & 3));
+            const char *dt = DTb((int)(j & 3));
+            // P row pw: blocks left of the diagonal, then the diagonal block
+            static_for<NB - 1>([&](auto jb_c) {
+                constexpr int jb = decltype(jb_c)::value;
+                if constexpr (jb < pw) {
+                    const f32x4 d = decay_off(gram(Qs, pw, jb, Ks), row_factor(dt, jb, pw), jb, dt);
+                    split4(d, Ph[par][jb], Pl[par][jb]);
                 }
-                static_for<NB - k - 1>([&](auto i_c) {
-                    constexpr int m = k + 1 + decltype(i_c)::value;
-                    bf16x4 ah[m - k], al[m - k];
+            });
+            split4(decay_diag(gram(Qs, pw, pw, Ks), pw, true, dt), Pdh[par], Pdl[par]);
+            // A_pp: -A_pp rows through the T_pp slot (scratch), then forward substitution
+            {
+                const float nbet = -ab[C + 16 * pw + ln];
+                const f32x4 d = decay_diag(gram(Ks, pw, pw, Ks), pw, false, dt) * nbet;
+                float *scr = reinterpret_cast<float *>(XTb(pw));
+                *reinterpret_cast<f32x4 *>(scr + ln * 16 + 4 * lg) = d;
+                float nL[16];
 #pragma unroll
-                    for (int jj = k; jj < m; ++jj) {
-                        ah[jj - k] = read_rows16(XAb(off_idx(m, jj)), lane);
-                        al[jj - k] = read_rows16(XAb(off_idx(m, jj)) + 256, lane);
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const f32x4 v4 = *reinterpret_cast<const f32x4 *>(scr + ln * 16 + 4 * s4);
+                    nL[4 * s4] = v4[0]; nL[4 * s4 + 1] = v4[1]; nL[4 * s4 + 2] = v4[2]; nL[4 * s4 + 3] = v4[3];
+                }
+                float X[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[e] = ln == 4 * lg + e ? 1.f : 0.f;
+                fsub16(X, nL);
+                bf16x4 hv, lv;
+                split4(f32x4{X[0], X[1], X[2], X[3]}, hv, lv);
+                // the scratch rows were read above (same wavefront, LDS in order)
+                *reinterpret_cast<bf16x4 *>(XTb(pw) + ln * 16 + 4 * lg) = hv;
+                *reinterpret_cast<bf16x4 *>(XTb(pw) + 256 + ln * 16 + 4 * lg) = lv;
+            }
+            // blocks of A below the diagonal owned by this wave
+            static_for<NB>([&](auto m_c) {
+                constexpr int m = decltype(m_c)::value;
+                static_for<m>([&](auto jj_c) {
+                    constexpr int jj = decltype(jj_c)::value;
+                    if constexpr (a_owner<NB>(m, jj) == pw) {
+                        const float f = row_factor(dt, jj, m) * ab[C + 16 * m + ln];
+                        const f32x4 d = decay_off(gram(Ks, m, jj, Ks), f, jj, dt);
+                        bf16x4 hv, lv;
+                        split4(d, hv, lv);
+                        constexpr int o = off_idx_c(m, jj);
+                        *reinterpret_cast<bf16x4 *>(XAb(o) + ln * 16 + 4 * lg) = hv;
+                        *reinterpret_cast<bf16x4 *>(XAb(o) + 256 + ln * 16 + 4 * lg) = lv;
                     }
-                    f32x4 z = zero4(), z2 = zero4();
-                    pair_products<m - k>(ah, al, bh + k, bl + k, z, z2);
+                });
+            });
+        };
+
+        // Y-phase work of chunk j: column k = pw of T, T' column k into slot j % 2.
+        // bh[d], bl[d] hold T_(k+d),k in accumulator layout, hi/lo.
+        auto prep_y = [&](int64_t j) {
+            if constexpr (!has_rb) return;
+            constexpr int k = pw;
+            const int ts = (int)(j & 1);
+            const float bcol = ABb((int)(j & 3))[C + 16 * k + ln];
+            bf16x4 bh[NB], bl[NB];
+            bh[0] = read_cols16(XTb(k), lane);
+            bl[0] = read_cols16(XTb(k) + 256, lane);
+            {
+                f32x4 t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = ((float)bh[0][e] + (float)bl[0][e]) * bcol;
+                bf16x4 hv, lv;
+                split4(t, hv, lv);
+                write_acc_transposed(TPb(ts, tri_idx(k, k)), hv, lane);
+                write_acc_transposed(TPb(ts, tri_idx(k, k)) + 256, lv, lane);
+            }
+            // T_mk = -T_mm sum_{i=k}^{m-1} A_mi T_ik, m = k + 1 + d
+            static_for<NB - 1>([&](auto d_c) {
+                constexpr int d = decltype(d_c)::value;
+                constexpr int m = k + 1 + d;
+                if constexpr (m < NB) {
+                    f32x4 z = zero4();
+#pragma unroll
+                    for (int t = 0; t <= d; ++t) {
+                        const __bf16 *xa = XAb(off_idx(m, k + t));
+                        z = mma_hl(read_rows16(xa, lane), read_rows16(xa + 256, lane), bh[t], bl[t], z);
+                    }
                     bf16x4 zh, zl;
-                    split4(z + z2, zh, zl);
-                    const f32x4 t = -mma_hilo16(read_rows16(XTb(m), lane), read_rows16(XTb(m) + 256, lane), zh, zl);
-                    split4(t, bh[m], bl[m]);
+                    split4(-z, zh, zl);
+                    const f32x4 t = mma_hl(read_rows16(XTb(m), lane), read_rows16(XTb(m) + 256, lane), zh, zl, zero4());
+                    split4(t, bh[d + 1], bl[d + 1]);
                     bf16x4 hv, lv;
                     split4(t * bcol, hv, lv);
                     write_acc_transposed(TPb(ts, tri_idx(m, k)), hv, lane);
                     write_acc_transposed(TPb(ts, tri_idx(m, k)) + 256, lv, lane);
-                });
-            }
+                }
+            });
         };
 
-        // output rows of token block pw of chunk j (P set par)
+        // output rows of token block pw of chunk j from P register set par
+        float *yg = p.y + ((b * T) * H + h) * Dv + n0;
+        uint32_t yo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yo[e] = (uint32_t)((16 * pw + 4 * lg + e) * H * Dv) + ln;
         auto out_y = [&](auto par_c, int64_t j) {
             constexpr int par = decltype(par_c)::value;
-            if constexpr (has_rb) {
-                f32x4 acc = QSs[pw * 64 + lane], acc2 = zero4();
-                bf16x4 uh[pw + 1], ul[pw + 1];
+            if constexpr (!has_rb) return;
+            f32x4 acc = QSs[pw * 64 + lane];
+            static_for<NB - 1>([&](auto jb_c) {
+                constexpr int jb = decltype(jb_c)::value;
+                if constexpr (jb < pw) acc = mma_hl(Ph[par][jb], Pl[par][jb], UQs[jb * 128 + lane], UQs[jb * 128 + 64 + lane], acc);
+            });
+            acc = mma_hl(Pdh[par], Pdl[par], UQs[pw * 128 + lane], UQs[pw * 128 + 64 + lane], acc);
+            const int64_t c0 = j * C;
+            float *yc = yg + c0 * H * Dv;
+            if (c0 + C <= T) {
 #pragma unroll
-                for (int jb = 0; jb <= pw; ++jb) {
-                    uh[jb] = UQs[jb * 128 + lane];
-                    ul[jb] = UQs[jb * 128 + 64 + lane];
-                }
-                pair_products<pw + 1>(Ph[par], Pl[par], uh, ul, acc, acc2);
-                const f32x4 yv = acc + acc2;
-                const int64_t t0 = j * C + 16 * pw + 4 * lg;
+                for (int e = 0; e < 4; ++e) yc[yo[e]] = acc[e];
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t t = t0 + e;
-                    if (t < T) p.y[((b * T + t) * H + h) * Dv + n0 + ln] = yv[e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + 16 * pw + 4 * lg + e < T) yc[yo[e]] = acc[e];
             }
         };
 
-        lds_barrier();                              // chunk 0 staged
+        lds_barrier();                              // chunk 0 and gates 0, 1 staged
+        if constexpr (pw == 3) decay_table(0);
+        lds_barrier();
 
         // iteration c: X-phase (outputs of c-1, preparation of c+1), Y-phase
-        // (T' of c+1).  The P row of chunk j uses register set j & 1.
+        // (T' of c+1, decay table of c+2).  Set (c+1) & 1 holds P of chunk c-1
+        // until its output is formed, then P of chunk c+1.
         auto iter = [&](auto par_c, int64_t c) {
-            constexpr int par = decltype(par_c)::value;    // == (c + 1) & 1
-            using PAR = std::integral_constant<int, par>;
-            if (c >= 1) out_y(PAR{}, c - 1);
-            if (c + 1 < NC) prep_x(PAR{}, c + 1);
+            if (c >= 1) out_y(par_c, c - 1);
+            if (c + 1 < NC) prep_x(par_c, c + 1);
             lds_barrier();
             if (c + 1 < NC) prep_y(c + 1);
+            if constexpr (pw == 3) {
+                if (c + 2 < NC) decay_table(c + 2);
+            }
             lds_barrier();
         };
+#pragma unroll 1
         for (int64_t c = -1; c <= NC; c += 2) {
             iter(std::integral_constant<int, 0>{}, c);
             if (c + 1 <= NC) iter(std::integral_constant<int, 1>{}, c + 1);
