@@ -127,6 +127,23 @@ __device__ __forceinline__ Frag<__bf16, KS> frag_kq(const __bf16 *base, int r0, 
     return f;
 }
 
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// Copy of 16 (4) bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds): lane L writes at l + 16 L (4 L); completion is tracked by
+// vmcnt.  The host pass of this file sees an empty body: the builtin exists only
+// for the device target.
+__device__ __forceinline__ void load_lds16(const void *g, lds_ptr l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void load_lds4(const void *g, lds_ptr l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+#endif
+}
+
 typedef short i16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4v *lds_i16x4;
 
@@ -296,104 +313,92 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
         }
-        // global bases of token 0 of this (b, h) and lane offsets within a chunk
+        // Inputs go straight from global memory into LDS (global_load_lds): lane L
+        // of a load writes the 16 bytes at the load's LDS base + 16 L, so each lane
+        // fetches the granule that the row permutation of kq_idx puts there.  Rows
+        // past the end of the sequence read token T-1 and are overwritten once the
+        // data has landed: zeros, alpha = 1, beta = 0 (identity tokens).
+        constexpr int G = DK / 8;                        // 16-byte granules per K / Q row
+        constexpr int NLD = (DK + 31) / 32;              // 1 KB loads per 16-row block
         const __bf16 *kg = p.k + b * T * p.ks + h * DK;
         const __bf16 *qg = p.q + b * T * p.qs + h * DK;
         const __bf16 *vg = p.v + b * T * p.vs + h * Dv + n0;
         const float *ag = p.alpha + b * T * H + h;
         const float *bg = p.beta + b * T * H + h;
-        const int rowk = 16 * w + ln;                        // K / Q row and gate token
-        const int l32 = lane & 31, rowv = 16 * w + (l32 >> 1);   // V row
-        const uint32_t ok0 = (uint32_t)(rowk * p.ks) + lg * (KSD / 4);
-        const uint32_t oq0 = (uint32_t)(rowk * p.qs) + lg * (KSD / 4);
-        const uint32_t ov0 = (uint32_t)(rowv * p.vs) + (l32 & 1) * 8;
-        const uint32_t og0 = (uint32_t)(rowk * H);
-
-        // register staging: q, k, v rows of token block w of one chunk, the
-        // gates of token block w of another
-        struct Stage {
-            FDK kf[NK], qf[NK];
-            bf16x8 vv;
-            float ga, gb;
-        };
-        Stage st;
-        auto load_stage = [&](Stage &s, int64_t j, int64_t jg) {
-            if constexpr (!has_rb) return;
-            if (j < NC) {
-                const int64_t c0 = j * C;
-                uint32_t ok = ok0, oq = oq0, ov = ov0;
-                if (c0 + C > T) {                      // last chunk: rows past the end read token T-1
-                    const int64_t last = T - 1 - c0;
-                    const int64_t rk = rowk < last ? rowk : last, rv = rowv < last ? rowv : last;
-                    ok = (uint32_t)(rk * p.ks) + lg * (KSD / 4);
-                    oq = (uint32_t)(rk * p.qs) + lg * (KSD / 4);
-                    ov = (uint32_t)(rv * p.vs) + (l32 & 1) * 8;
-                }
-                const __bf16 *kc = kg + c0 * p.ks, *qc = qg + c0 * p.qs, *vc = vg + c0 * p.vs;
+        int rbl[NLD], colg[NLD];                         // row in the block and column of lane's granule
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    s.kf[kk].load(kc + ok + kk * KSD);
-                    s.qf[kk].load(qc + oq + kk * KSD);
-                }
-                s.vv = *reinterpret_cast<const bf16x8 *>(vc + ov);
-            }
-            if (jg < NC && lane < 16) {
-                const int64_t c0 = jg * C;
-                uint32_t og = og0;
-                if (c0 + C > T) {
-                    const int64_t last = T - 1 - c0;
-                    og = (uint32_t)((rowk < last ? rowk : last) * H);
-                }
-                s.ga = (ag + c0 * H)[og];
-                s.gb = (bg + c0 * H)[og];
+        for (int i = 0; i < NLD; ++i) {
+            const int byte = i * 1024 + 16 * lane;
+            rbl[i] = byte / (2 * DK);
+            const int gp = (byte % (2 * DK)) / 16;
+            colg[i] = 8 * (gp ^ (rbl[i] & (G - 1)));
+        }
+        const int rv = lane >> 1;                        // V row of lane (lanes 0..31)
+        auto tok = [&](int64_t c0, int r) -> int64_t {   // token row r of the block, clamped
+            const int64_t t = c0 + 16 * w + r;
+            return t < T ? t : T - 1;
+        };
+        auto lds = [&](const void *x) { return (lds_ptr)(uintptr_t)(uint32_t)(uintptr_t)x; };
+        auto issue_k = [&](int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                __bf16 *dst = Kb((int)(j % 3)) + 16 * w * DK;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+                    if (rbl[i] < 16)
+                        load_lds16(kg + tok(c0, rbl[i]) * p.ks + colg[i], lds(dst + i * 512));
             }
         };
-        auto write_stage = [&](const Stage &s, int64_t j, int64_t jg) {
-            if constexpr (!has_rb) return;
-            if (j < NC) {
+        auto issue_qv = [&](int64_t j) {
+            if constexpr (has_rb) {
                 const int64_t c0 = j * C;
-                __bf16 *Kd = Kb((int)(j % 3)) + w * 16 * DK;
-                __bf16 *Qd = Qb((int)(j & 1)) + w * 16 * DK;
-                __bf16 *Vd = Vb((int)(j & 1)) + rowv * BV + (l32 & 1) * 8;
-                if (c0 + C <= T) {
+                __bf16 *dst = Qb((int)(j & 1)) + 16 * w * DK;
 #pragma unroll
-                    for (int kk = 0; kk < NK; ++kk) {
-                        *reinterpret_cast<decltype(s.kf[kk].v) *>(Kd + kqo[kk]) = s.kf[kk].v;
-                        *reinterpret_cast<decltype(s.qf[kk].v) *>(Qd + kqo[kk]) = s.qf[kk].v;
-                    }
-                    if (lane < 32) *reinterpret_cast<bf16x8 *>(Vd) = s.vv;
-                } else {                               // rows past the end are zeros
-                    const bool ok = c0 + rowk < T;
-#pragma unroll
-                    for (int kk = 0; kk < NK; ++kk) {
-                        FDK kz = s.kf[kk], qz = s.qf[kk];
-                        if (!ok) {
-#pragma unroll
-                            for (int e = 0; e < KSD / 4; ++e) {
-                                kz.set(e, 0.f);
-                                qz.set(e, 0.f);
-                            }
-                        }
-                        *reinterpret_cast<decltype(kz.v) *>(Kd + kqo[kk]) = kz.v;
-                        *reinterpret_cast<decltype(qz.v) *>(Qd + kqo[kk]) = qz.v;
-                    }
-                    if (lane < 32) {
-                        bf16x8 vz = s.vv;
-                        if (c0 + rowv >= T) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) vz[e] = (__bf16)0.f;
-                        }
-                        *reinterpret_cast<bf16x8 *>(Vd) = vz;
-                    }
+                for (int i = 0; i < NLD; ++i)
+                    if (rbl[i] < 16)
+                        load_lds16(qg + tok(c0, rbl[i]) * p.qs + colg[i], lds(dst + i * 512));
+                if (lane < 32)
+                    load_lds16(vg + tok(c0, rv) * p.vs + (lane & 1) * 8,
+                                                     lds(Vb((int)(j & 1)) + 16 * w * BV));
+            }
+        };
+        auto issue_gates = [&](int64_t j) {
+            if constexpr (has_rb) {
+                const int64_t c0 = j * C;
+                float *dst = ABb((int)(j & 3));
+                if (lane < 16) {
+                    const int64_t t = tok(c0, lane);
+                    load_lds4(ag + t * H, lds(dst + 16 * w));
+                    load_lds4(bg + t * H, lds(dst + C + 16 * w));
                 }
             }
-            if (jg < NC && lane < 16) {
-                // alpha of a padding token is 1, beta 0
-                const bool okg = jg * C + rowk < T;
-                float *abd = ABb((int)(jg & 3));
-                abd[rowk] = okg ? s.ga : 1.f;
-                abd[C + rowk] = okg ? s.gb : 0.f;
+        };
+        // after the loads of chunk j (inputs) and jg (gates) have landed
+        auto fill_tail = [&](int64_t j, int64_t jg) {
+            if constexpr (has_rb) {
+                if (j < NC && j * C + C > T) {
+                    const int64_t c0 = j * C;
+                    __bf16 *kd = Kb((int)(j % 3)) + 16 * w * DK, *qd = Qb((int)(j & 1)) + 16 * w * DK;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i)
+                        if (rbl[i] < 16 && c0 + 16 * w + rbl[i] >= T) {
+                            *reinterpret_cast<bf16x8 *>(kd + i * 512 + 8 * lane) = bf16x8{};
+                            *reinterpret_cast<bf16x8 *>(qd + i * 512 + 8 * lane) = bf16x8{};
+                        }
+                    if (lane < 32 && c0 + 16 * w + rv >= T)
+                        *reinterpret_cast<bf16x8 *>(Vb((int)(j & 1)) + 16 * w * BV + 8 * lane) = bf16x8{};
+                }
+                if (jg < NC && jg * C + C > T && lane < 16 && jg * C + 16 * w + lane >= T) {
+                    float *ab = ABb((int)(jg & 3));
+                    ab[16 * w + lane] = 1.f;
+                    ab[C + 16 * w + lane] = 0.f;
+                }
             }
+        };
+        auto wait_loads = [&]() {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+            asm volatile("" ::: "memory");
         };
 
         auto write_state_operand = [&]() {
@@ -410,10 +415,13 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
         };
         // chunk 0 and the gates of chunks 0 and 1 into LDS, then the decay table of
         // chunk 0 (preparation wave 3)
-        load_stage(st, 0, 0);
-        write_stage(st, 0, 0);
-        load_stage(st, NC, 1);
-        write_stage(st, NC, 1);
+        issue_k(0);
+        issue_qv(0);
+        issue_gates(0);
+        if (NC > 1) issue_gates(1);
+        wait_loads();
+        fill_tail(0, 0);
+        if (NC > 1) fill_tail(NC, 1);
         lds_barrier();
         lds_barrier();
 
@@ -422,7 +430,8 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
         int kb = 0;                                  // c % 3 for c >= 0
 #pragma unroll 1
         for (int64_t c = -1; c <= NC; ++c) {
-            load_stage(st, c + 2, c + 3);
+            if (c + 2 < NC) issue_k(c + 2);
+            if (c + 3 < NC) issue_gates(c + 3);
             const bool work = c >= 0 && c < NC;
             const int qb = (int)(c & 1);
             const __bf16 *Ks = Kb(kb);
@@ -456,6 +465,7 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 egqs = eg * qs;
             }
             lds_barrier();
+            if (c + 2 < NC) issue_qv(c + 2);           // Q(c), V(c) were last read above
             // ---- Y-phase: U = T' R (every token block), state update
             if (work) {
                 const int ts = qb;
@@ -508,7 +518,8 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 }
             }
             if (c < NC) write_state_operand();       // c = -1: the initial state
-            write_stage(st, c + 2, c + 3);
+            wait_loads();
+            fill_tail(c + 2, c + 3);
             lds_barrier();
             if (c >= 0) kb = kb == 2 ? 0 : kb + 1;
         }
