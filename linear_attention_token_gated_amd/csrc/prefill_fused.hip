@@ -92,7 +92,9 @@ template <int C, int DK> struct FL {
     static constexpr size_t oXA = oXT + (size_t)NB * 1024;              // [NOFF] A_mj row-major, hi|lo
     static constexpr size_t oUQ = oXA + (size_t)(NOFF > 0 ? NOFF : 1) * 1024;   // U_w [NB][hi|lo][64] bf16x4
     static constexpr size_t oQS = oUQ + (size_t)NB * 1024;              // 2^G Q_w S [NB][64] f32x4
-    static constexpr size_t BYTES = oQS + (size_t)NB * 1024;
+    static constexpr size_t oUD = oQS + (size_t)NB * 1024;              // 2^(G_C-G) U [hi|lo][64][NB] bf16x4
+    static constexpr size_t oTX = oUD + (size_t)NB * 1024;              // T_10 (accumulator layout) | T_32^T, hi|lo
+    static constexpr size_t BYTES = oTX + 2048;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -264,6 +266,8 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
     bf16x4 *Rs = reinterpret_cast<bf16x4 *>(smem + L::oR);       // [NB][hi 64 | lo 64]
     bf16x4 *UQs = reinterpret_cast<bf16x4 *>(smem + L::oUQ);     // [NB][hi 64 | lo 64]
     f32x4 *QSs = reinterpret_cast<f32x4 *>(smem + L::oQS);       // [NB][64]
+    bf16x4 *UDs = reinterpret_cast<bf16x4 *>(smem + L::oUD);     // [hi | lo][64][NB]
+    __bf16 *TX = reinterpret_cast<__bf16 *>(smem + L::oTX);
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
@@ -338,28 +342,41 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             const int64_t t = c0 + 16 * w + r;
             return t < T ? t : T - 1;
         };
+        // element offsets of the lane's data from token 0 of a chunk (no clamping)
+        uint32_t ofk[NLD], ofq[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            ofk[i] = (uint32_t)((16 * w + rbl[i]) * p.ks + colg[i]);
+            ofq[i] = (uint32_t)((16 * w + rbl[i]) * p.qs + colg[i]);
+        }
+        const uint32_t ofv = (uint32_t)((16 * w + rv) * p.vs + (lane & 1) * 8);
+        const uint32_t ofg = (uint32_t)((16 * w + (lane & 15)) * H);
         auto lds = [&](const void *x) { return (lds_ptr)(uintptr_t)(uint32_t)(uintptr_t)x; };
         auto issue_k = [&](int64_t j) {
             if constexpr (has_rb) {
                 const int64_t c0 = j * C;
                 __bf16 *dst = Kb((int)(j % 3)) + 16 * w * DK;
+                const __bf16 *kc = kg + c0 * p.ks;
+                const bool full = c0 + C <= T;
 #pragma unroll
                 for (int i = 0; i < NLD; ++i)
                     if (rbl[i] < 16)
-                        load_lds16(kg + tok(c0, rbl[i]) * p.ks + colg[i], lds(dst + i * 512));
+                        load_lds16(full ? kc + ofk[i] : kg + tok(c0, rbl[i]) * p.ks + colg[i], lds(dst + i * 512));
             }
         };
         auto issue_qv = [&](int64_t j) {
             if constexpr (has_rb) {
                 const int64_t c0 = j * C;
                 __bf16 *dst = Qb((int)(j & 1)) + 16 * w * DK;
+                const __bf16 *qc = qg + c0 * p.qs, *vc = vg + c0 * p.vs;
+                const bool full = c0 + C <= T;
 #pragma unroll
                 for (int i = 0; i < NLD; ++i)
                     if (rbl[i] < 16)
-                        load_lds16(qg + tok(c0, rbl[i]) * p.qs + colg[i], lds(dst + i * 512));
+                        load_lds16(full ? qc + ofq[i] : qg + tok(c0, rbl[i]) * p.qs + colg[i], lds(dst + i * 512));
                 if (lane < 32)
-                    load_lds16(vg + tok(c0, rv) * p.vs + (lane & 1) * 8,
-                                                     lds(Vb((int)(j & 1)) + 16 * w * BV));
+                    load_lds16(full ? vc + ofv : vg + tok(c0, rv) * p.vs + (lane & 1) * 8,
+                               lds(Vb((int)(j & 1)) + 16 * w * BV));
             }
         };
         auto issue_gates = [&](int64_t j) {
@@ -367,9 +384,11 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 const int64_t c0 = j * C;
                 float *dst = ABb((int)(j & 3));
                 if (lane < 16) {
-                    const int64_t t = tok(c0, lane);
-                    load_lds4(ag + t * H, lds(dst + 16 * w));
-                    load_lds4(bg + t * H, lds(dst + C + 16 * w));
+                    const bool full = c0 + C <= T;
+                    const float *ac = full ? ag + c0 * H + ofg : ag + tok(c0, lane) * H;
+                    const float *bc = full ? bg + c0 * H + ofg : bg + tok(c0, lane) * H;
+                    load_lds4(ac, lds(dst + 16 * w));
+                    load_lds4(bc, lds(dst + C + 16 * w));
                 }
             }
         };
@@ -425,13 +444,15 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
         lds_barrier();
         lds_barrier();
 
-        // iteration c (c = -1 .. NC): X-phase: loads of chunk c+2 (gates of c+3),
-        // K S, Q S, R of chunk c; Y-phase: U, the state update, staging into LDS
+        // iteration c (c = -1 .. NC), three barriers:
+        //   X:  K_w S, Q_w S, R_w of chunk c; copies of chunk c+2 (gates of c+3)
+        //       into LDS are issued once this wave has read its Q and V rows of
+        //       chunk c (no other wave reads those rows in this iteration)
+        //   Y1: U_w = sum_k T'_wk R_k; U_w, 2^(G_C-G) U_w and 2^G Q_w S -> LDS
+        //   Y2: state rows S <- 2^G_C S + K^T (2^(G_C-G) U), the S operand -> LDS
         int kb = 0;                                  // c % 3 for c >= 0
 #pragma unroll 1
         for (int64_t c = -1; c <= NC; ++c) {
-            if (c + 2 < NC) issue_k(c + 2);
-            if (c + 3 < NC) issue_gates(c + 3);
             const bool work = c >= 0 && c < NC;
             const int qb = (int)(c & 1);
             const __bf16 *Ks = Kb(kb);
@@ -442,19 +463,31 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             f32x4 egqs = zero4();
             if (has_rb && work) {
                 const __bf16 *Qs = Qb(qb);
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(EG + 16 * w + 4 * lg);
+                FDK kf[NK], qf[NK], sh[NK], sl[NK];
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    kf[kk] = frag_blk(Ks, w, kk);
+                    qf[kk] = frag_blk(Qs, w, kk);
+                    sh[kk] = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
+                    sl[kk] = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
+                }
                 const bf16x4 vv = read_cols16(Vb(qb) + 16 * w * BV, lane);
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(EG + 16 * w + 4 * lg);
                 f32x4 ks = zero4(), qs = zero4();
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
-                    const FDK kf = frag_blk(Ks, w, kk);
-                    const FDK qf = frag_blk(Qs, w, kk);
-                    const FDK sh = frag_rows<__bf16, KSD>(STh, KPS, 0, kk * KSD, lane);
-                    const FDK sl = frag_rows<__bf16, KSD>(STl, KPS, 0, kk * KSD, lane);
-                    ks = FDK::mma(kf, sh, ks);
-                    qs = FDK::mma(qf, sh, qs);
-                    qs = FDK::mma(qf, sl, qs);
+                    ks = FDK::mma(kf[kk], sh[kk], ks);
+                    qs = FDK::mma(qf[kk], sh[kk], qs);
+                    qs = FDK::mma(qf[kk], sl[kk], qs);
                 }
+                // the rows of Q_w and V_w of chunk c are in registers before the
+                // copies of chunk c+2 into the same rows are issued
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (c + 2 < NC) {
+                    issue_k(c + 2);
+                    issue_qv(c + 2);
+                }
+                if (c + 3 < NC) issue_gates(c + 3);
                 f32x4 rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
@@ -463,36 +496,37 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 Rs[w * 128 + lane] = hv;
                 Rs[w * 128 + 64 + lane] = lv;
                 egqs = eg * qs;
+            } else {
+                if (c + 2 < NC) {
+                    issue_k(c + 2);
+                    issue_qv(c + 2);
+                }
+                if (c + 3 < NC) issue_gates(c + 3);
             }
             lds_barrier();
-            if (c + 2 < NC) issue_qv(c + 2);           // Q(c), V(c) were last read above
-            // ---- Y-phase: U = T' R (every token block), state update
-            if (work) {
+            // ---- Y1: U_w = T'_w. R (token block w)
+            if (has_rb && work) {
                 const int ts = qb;
-                bf16x4 rh[NB], rl[NB], udh[NB], udl[NB];
+                f32x4 u = zero4();
 #pragma unroll
-                for (int k = 0; k < NB; ++k) {
-                    rh[k] = Rs[k * 128 + lane];
-                    rl[k] = Rs[k * 128 + 64 + lane];
+                for (int k = 0; k <= w; ++k) {
+                    const __bf16 *tb = TPb(ts, tri_idx(w, k));
+                    u = mma_hl(read_cols16(tb, lane), read_cols16(tb + 256, lane), Rs[k * 128 + lane],
+                               Rs[k * 128 + 64 + lane], u);
                 }
-                static_for<NB>([&](auto i_c) {
-                    constexpr int i = decltype(i_c)::value;
-                    f32x4 u = zero4();
-#pragma unroll
-                    for (int k = 0; k <= i; ++k) {
-                        const __bf16 *tb = TPb(ts, tri_idx(i, k));
-                        u = mma_hl(read_cols16(tb, lane), read_cols16(tb + 256, lane), rh[k], rl[k], u);
-                    }
-                    const f32x4 ed = *reinterpret_cast<const f32x4 *>(Ed + 16 * i + 4 * lg);
-                    split4(ed * u, udh[i], udl[i]);
-                    if constexpr (i == w) {
-                        bf16x4 uh, ul;
-                        split4(u, uh, ul);
-                        UQs[w * 128 + lane] = uh;
-                        UQs[w * 128 + 64 + lane] = ul;
-                        QSs[w * 64 + lane] = egqs;
-                    }
-                });
+                const f32x4 ed = *reinterpret_cast<const f32x4 *>(Ed + 16 * w + 4 * lg);
+                bf16x4 dh, dl, uh, ul;
+                split4(ed * u, dh, dl);
+                split4(u, uh, ul);
+                UDs[lane * NB + w] = dh;
+                UDs[64 * NB + lane * NB + w] = dl;
+                UQs[w * 128 + lane] = uh;
+                UQs[w * 128 + 64 + lane] = ul;
+                QSs[w * 64 + lane] = egqs;
+            }
+            lds_barrier();
+            // ---- Y2: state update
+            if (work) {
                 const float egc = *reinterpret_cast<const float *>(dt + L::DT_EGC);
 #pragma unroll
                 for (int m = 0; m < MS; ++m) {
@@ -504,11 +538,11 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                             const FC ka = k_cols_tr<KSC, DK>(Ks, 16 * ib, jj * KSC, lane);
                             FC bhf, blf;
                             if constexpr (KSC == 32) {
-                                bhf = pair16(udh[2 * jj], udh[2 * jj + 1]);
-                                blf = pair16(udl[2 * jj], udl[2 * jj + 1]);
+                                bhf.v = *reinterpret_cast<const bf16x8 *>(UDs + lane * NB + 2 * jj);
+                                blf.v = *reinterpret_cast<const bf16x8 *>(UDs + 64 * NB + lane * NB + 2 * jj);
                             } else {
-                                bhf.v = udh[jj];
-                                blf.v = udl[jj];
+                                bhf.v = UDs[lane * NB + jj];
+                                blf.v = UDs[64 * NB + lane * NB + jj];
                             }
                             acc = FC::mma(ka, bhf, acc);
                             acc = FC::mma(ka, blf, acc);
@@ -547,19 +581,6 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
         // holds chunk j
         bf16x4 Ph[2][NBO], Pl[2][NBO], Pdh[2], Pdl[2];
 
-        // Gram block D = X_r K_jb^T in row layout (lane (ln, g): D[ln][4g + e])
-        auto gram = [&](const __bf16 *Xs, int r, int jb, const __bf16 *Ks) {
-            FDK fa[NK], fb[NK];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                fa[kk] = frag_blk(Ks, jb, kk);
-                fb[kk] = frag_blk(Xs, r, kk);
-            }
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) acc = FDK::mma(fa[kk], fb[kk], acc);
-            return acc;
-        };
         // decay ratios 2^(G_r - G_j) on a diagonal block (r >= j, or r > j), 0 above
         auto decay_diag = [&](f32x4 d, int blk, bool incl, const char *dt) {
             const double *Gd = reinterpret_cast<const double *>(dt) + 16 * blk;
@@ -619,7 +640,9 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             if (lane == 0) *reinterpret_cast<float *>(dt + L::DT_EGC) = __builtin_amdgcn_exp2f((float)GC);
         };
 
-        // X-phase work of chunk j; its P row goes to register set par
+        // X-phase work of chunk j; its P row goes to register set par.  The
+        // fragments of every K block and of Q block pw are read once; the Gram
+        // blocks are formed from registers.
         auto prep_x = [&](auto par_c, int64_t j) {
             constexpr int par = decltype(par_c)::value;
             if constexpr (!has_rb) return;
@@ -627,19 +650,33 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             const __bf16 *Qs = Qb((int)(j & 1));
             const float *ab = ABb((int)(j & 3));
             const char *dt = DTb((int)(j & 3));
+            FDK kf[NB][NK], qf[NK];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) qf[kk] = frag_blk(Qs, pw, kk);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) kf[jb][kk] = frag_blk(Ks, jb, kk);
+            // X_r K_jb^T in row layout from fragments
+            auto gramr = [&](const FDK (&xr)[NK], int jb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) acc = FDK::mma(kf[jb][kk], xr[kk], acc);
+                return acc;
+            };
             // P row pw: blocks left of the diagonal, then the diagonal block
             static_for<NB - 1>([&](auto jb_c) {
                 constexpr int jb = decltype(jb_c)::value;
                 if constexpr (jb < pw) {
-                    const f32x4 d = decay_off(gram(Qs, pw, jb, Ks), row_factor(dt, jb, pw), jb, dt);
+                    const f32x4 d = decay_off(gramr(qf, jb), row_factor(dt, jb, pw), jb, dt);
                     split4(d, Ph[par][jb], Pl[par][jb]);
                 }
             });
-            split4(decay_diag(gram(Qs, pw, pw, Ks), pw, true, dt), Pdh[par], Pdl[par]);
+            split4(decay_diag(gramr(qf, pw), pw, true, dt), Pdh[par], Pdl[par]);
             // A_pp: -A_pp rows through the T_pp slot (scratch), then forward substitution
             {
                 const float nbet = -ab[C + 16 * pw + ln];
-                const f32x4 d = decay_diag(gram(Ks, pw, pw, Ks), pw, false, dt) * nbet;
+                const f32x4 d = decay_diag(gramr(kf[pw], pw), pw, false, dt) * nbet;
                 float *scr = reinterpret_cast<float *>(XTb(pw));
                 *reinterpret_cast<f32x4 *>(scr + ln * 16 + 4 * lg) = d;
                 float nL[16];
@@ -665,7 +702,7 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                     constexpr int jj = decltype(jj_c)::value;
                     if constexpr (a_owner<NB>(m, jj) == pw) {
                         const float f = row_factor(dt, jj, m) * ab[C + 16 * m + ln];
-                        const f32x4 d = decay_off(gram(Ks, m, jj, Ks), f, jj, dt);
+                        const f32x4 d = decay_off(gramr(kf[m], jj), f, jj, dt);
                         bf16x4 hv, lv;
                         split4(d, hv, lv);
                         constexpr int o = off_idx_c(m, jj);
@@ -676,46 +713,106 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             });
         };
 
-        // Y-phase work of chunk j: column k = pw of T, T' column k into slot j % 2.
-        // bh[d], bl[d] hold T_(k+d),k in accumulator layout, hi/lo.
-        auto prep_y = [&](int64_t j) {
+        // T = (I + A)^-1 from the diagonal inverses T_mm (in XT) by halves of the
+        // chunk: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (Y1), then the
+        // lower-left quarter -T_lower (A_lower-left T_upper) (Y2):
+        //   T_20 = -T_22 (A_20 T_00 + A_21 T_10),  T_21 = -T_22 A_21 T_11,
+        //   T_30 = -(T_32 W_20 + T_33 W_30),        T_31 = -(T_32 W_21 + T_33 W_31),
+        //   W_m0 = A_m0 T_00 + A_m1 T_10,  W_m1 = A_m1 T_11.
+        // Every block of T' = T diag(beta) goes to slot j % 2 as its transpose.
+        // B operands (right factors) are in accumulator layout, A operands in row
+        // layout; every product is hi/lo.
+        bf16x4 t10h = {}, t10l = {};                     // T_10 (wave 0, from Y1 to Y2)
+        auto xa_rows = [&](int m, int jj, bf16x4 &h, bf16x4 &l) {
+            const __bf16 *x = XAb(off_idx(m, jj));
+            h = read_rows16(x, lane);
+            l = read_rows16(x + 256, lane);
+        };
+        auto write_tp = [&](int ts, int m, int k, f32x4 t, float bk) {
+            bf16x4 hv, lv;
+            split4(t * bk, hv, lv);
+            write_acc_transposed(TPb(ts, tri_idx(m, k)), hv, lane);
+            write_acc_transposed(TPb(ts, tri_idx(m, k)) + 256, lv, lane);
+        };
+        // -T_mm Z for Z in accumulator layout
+        auto neg_tmm = [&](int m, f32x4 z) {
+            bf16x4 zh, zl;
+            split4(-z, zh, zl);
+            return mma_hl(read_rows16(XTb(m), lane), read_rows16(XTb(m) + 256, lane), zh, zl, zero4());
+        };
+        auto prep_y1 = [&](int64_t j) {
             if constexpr (!has_rb) return;
-            constexpr int k = pw;
             const int ts = (int)(j & 1);
-            const float bcol = ABb((int)(j & 3))[C + 16 * k + ln];
-            bf16x4 bh[NB], bl[NB];
-            bh[0] = read_cols16(XTb(k), lane);
-            bl[0] = read_cols16(XTb(k) + 256, lane);
+            const float bk = ABb((int)(j & 3))[C + 16 * pw + ln];     // beta of column block pw
+            const bf16x4 dh = read_cols16(XTb(pw), lane), dl = read_cols16(XTb(pw) + 256, lane);
             {
                 f32x4 t;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = ((float)bh[0][e] + (float)bl[0][e]) * bcol;
-                bf16x4 hv, lv;
-                split4(t, hv, lv);
-                write_acc_transposed(TPb(ts, tri_idx(k, k)), hv, lane);
-                write_acc_transposed(TPb(ts, tri_idx(k, k)) + 256, lv, lane);
+                for (int e = 0; e < 4; ++e) t[e] = (float)dh[e] + (float)dl[e];
+                write_tp(ts, pw, pw, t, bk);
             }
-            // T_mk = -T_mm sum_{i=k}^{m-1} A_mi T_ik, m = k + 1 + d
-            static_for<NB - 1>([&](auto d_c) {
-                constexpr int d = decltype(d_c)::value;
-                constexpr int m = k + 1 + d;
-                if constexpr (m < NB) {
-                    f32x4 z = zero4();
-#pragma unroll
-                    for (int t = 0; t <= d; ++t) {
-                        const __bf16 *xa = XAb(off_idx(m, k + t));
-                        z = mma_hl(read_rows16(xa, lane), read_rows16(xa + 256, lane), bh[t], bl[t], z);
+            if constexpr (NB >= 2 && (pw == 0 || (NB == 4 && pw == 2))) {
+                bf16x4 ah, al;
+                xa_rows(pw + 1, pw, ah, al);
+                const f32x4 t = neg_tmm(pw + 1, mma_hl(ah, al, dh, dl, zero4()));
+                write_tp(ts, pw + 1, pw, t, bk);
+                if constexpr (NB == 4) {
+                    bf16x4 h, l;
+                    split4(t, h, l);
+                    if constexpr (pw == 0) {
+                        t10h = h;
+                        t10l = l;
+                        reinterpret_cast<bf16x4 *>(TX)[lane] = h;
+                        reinterpret_cast<bf16x4 *>(TX)[64 + lane] = l;
+                    } else {
+                        write_acc_transposed(TX + 512, h, lane);
+                        write_acc_transposed(TX + 768, l, lane);
                     }
-                    bf16x4 zh, zl;
-                    split4(-z, zh, zl);
-                    const f32x4 t = mma_hl(read_rows16(XTb(m), lane), read_rows16(XTb(m) + 256, lane), zh, zl, zero4());
-                    split4(t, bh[d + 1], bl[d + 1]);
-                    bf16x4 hv, lv;
-                    split4(t * bcol, hv, lv);
-                    write_acc_transposed(TPb(ts, tri_idx(m, k)), hv, lane);
-                    write_acc_transposed(TPb(ts, tri_idx(m, k)) + 256, lv, lane);
                 }
-            });
+            }
+        };
+        auto prep_y2 = [&](int64_t j) {
+            if constexpr (NB == 4 && has_rb) {
+                const int ts = (int)(j & 1);
+                constexpr int k = pw & 1;                 // column block of this wave's result
+                const float bk = ABb((int)(j & 3))[C + 16 * k + ln];
+                // T_kk (B operand) and, for column 0, T_10
+                const bf16x4 th = read_cols16(XTb(k), lane), tl = read_cols16(XTb(k) + 256, lane);
+                bf16x4 a1h, a1l, a2h, a2l;
+                if constexpr (pw == 0) {                  // T_20
+                    xa_rows(2, 0, a1h, a1l);
+                    xa_rows(2, 1, a2h, a2l);
+                    f32x4 z = mma_hl(a1h, a1l, th, tl, zero4());
+                    z = mma_hl(a2h, a2l, t10h, t10l, z);
+                    write_tp(ts, 2, 0, neg_tmm(2, z), bk);
+                } else if constexpr (pw == 1) {           // T_21
+                    xa_rows(2, 1, a1h, a1l);
+                    write_tp(ts, 2, 1, neg_tmm(2, mma_hl(a1h, a1l, th, tl, zero4())), bk);
+                } else {                                  // T_3k
+                    f32x4 wa, wb;                         // W_2k, W_3k
+                    if constexpr (k == 0) {
+                        const bf16x4 uh = reinterpret_cast<const bf16x4 *>(TX)[lane];
+                        const bf16x4 ul = reinterpret_cast<const bf16x4 *>(TX)[64 + lane];
+                        xa_rows(2, 0, a1h, a1l);
+                        xa_rows(2, 1, a2h, a2l);
+                        wa = mma_hl(a2h, a2l, uh, ul, mma_hl(a1h, a1l, th, tl, zero4()));
+                        xa_rows(3, 0, a1h, a1l);
+                        xa_rows(3, 1, a2h, a2l);
+                        wb = mma_hl(a2h, a2l, uh, ul, mma_hl(a1h, a1l, th, tl, zero4()));
+                    } else {
+                        xa_rows(2, 1, a1h, a1l);
+                        xa_rows(3, 1, a2h, a2l);
+                        wa = mma_hl(a1h, a1l, th, tl, zero4());
+                        wb = mma_hl(a2h, a2l, th, tl, zero4());
+                    }
+                    bf16x4 wah, wal, wbh, wbl;
+                    split4(-wa, wah, wal);
+                    split4(-wb, wbh, wbl);
+                    f32x4 t = mma_hl(read_cols16(TX + 512, lane), read_cols16(TX + 768, lane), wah, wal, zero4());
+                    t = mma_hl(read_rows16(XTb(3), lane), read_rows16(XTb(3) + 256, lane), wbh, wbl, t);
+                    write_tp(ts, 3, k, t, bk);
+                }
+            }
         };
 
         // output rows of token block pw of chunk j from P register set par
@@ -744,21 +841,24 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             }
         };
 
+        constexpr int TBL = NB == 4 ? 1 : 3;        // the wave that builds the decay tables
         lds_barrier();                              // chunk 0 and gates 0, 1 staged
-        if constexpr (pw == 3) decay_table(0);
+        if constexpr (pw == TBL) decay_table(0);
         lds_barrier();
 
-        // iteration c: X-phase (outputs of c-1, preparation of c+1), Y-phase
-        // (T' of c+1, decay table of c+2).  Set (c+1) & 1 holds P of chunk c-1
-        // until its output is formed, then P of chunk c+1.
+        // iteration c: X (outputs of c-1, preparation of c+1), Y1 and Y2 (T' of
+        // c+1, decay table of c+2).  Set (c+1) & 1 holds P of chunk c-1 until its
+        // output is formed, then P of chunk c+1.
         auto iter = [&](auto par_c, int64_t c) {
             if (c >= 1) out_y(par_c, c - 1);
             if (c + 1 < NC) prep_x(par_c, c + 1);
             lds_barrier();
-            if (c + 1 < NC) prep_y(c + 1);
-            if constexpr (pw == 3) {
+            if (c + 1 < NC) prep_y1(c + 1);
+            if constexpr (pw == TBL) {
                 if (c + 2 < NC) decay_table(c + 2);
             }
+            lds_barrier();
+            if (c + 1 < NC) prep_y2(c + 1);
             lds_barrier();
         };
 #pragma unroll 1
