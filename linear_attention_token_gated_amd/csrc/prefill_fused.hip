@@ -461,6 +461,8 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
             const float *Ed = reinterpret_cast<const float *>(dt + L::DT_ED);
             // ---- X-phase: K_w S, Q_w S -> R_w
             f32x4 egqs = zero4();
+            if (c + 2 < NC) issue_k(c + 2);
+            if (c + 3 < NC) issue_gates(c + 3);
             if (has_rb && work) {
                 const __bf16 *Qs = Qb(qb);
                 FDK kf[NK], qf[NK], sh[NK], sl[NK];
@@ -483,11 +485,7 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 // the rows of Q_w and V_w of chunk c are in registers before the
                 // copies of chunk c+2 into the same rows are issued
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (c + 2 < NC) {
-                    issue_k(c + 2);
-                    issue_qv(c + 2);
-                }
-                if (c + 3 < NC) issue_gates(c + 3);
+                if (c + 2 < NC) issue_qv(c + 2);
                 f32x4 rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rv[e] = (float)vv[e] - eg[e] * ks[e];
@@ -497,11 +495,7 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 Rs[w * 128 + 64 + lane] = lv;
                 egqs = eg * qs;
             } else {
-                if (c + 2 < NC) {
-                    issue_k(c + 2);
-                    issue_qv(c + 2);
-                }
-                if (c + 3 < NC) issue_gates(c + 3);
+                if (c + 2 < NC) issue_qv(c + 2);
             }
             lds_barrier();
             // ---- Y1: U_w = T'_w. R (token block w)
