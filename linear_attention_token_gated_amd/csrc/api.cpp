@@ -433,7 +433,7 @@ gdn_status gdn_prefill_bwd(const void *q, const void *k, const void *v, const fl
 size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv)
 {
     if (N < 0 || hidden < 0 || H < 0 || Dk < 0 || Dv < 0) return 0;
-    return gdn::layer_workspace_bytes(N, 1, hidden, H, Dk, Dv);
+    return gdn::layer_decode_workspace_bytes(N, H, Dk, Dv);
 }
 
 gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *p, float *conv_state, float *state,
@@ -472,7 +472,7 @@ gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *p, float
     for (int i = 0; i < 13; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GDN_ERR_ALIGN, "gdn_layer_decode_step: %s is not 16-byte aligned", names[i]);
-    const size_t need = gdn::layer_workspace_bytes(N, 1, hidden, H, Dk, Dv);
+    const size_t need = gdn::layer_decode_workspace_bytes(N, H, Dk, Dv);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GDN_ERR_WORKSPACE, "gdn_layer_decode_step: workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);

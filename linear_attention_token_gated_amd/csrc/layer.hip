@@ -15,8 +15,7 @@
 //   4. epilogue: g = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + gamma) (bf16)
 //   5. projection: out = g W_o^T (fp32)
 //
-// The projections are plain products: they go to hipBLASLt (blas.cpp), and to
-// this file's gemm_nt_kernel only for a shape the library has no algorithm for.
+// The projections are plain products on this file's gemm_nt_kernel.
 //
 // Why q, k, v are not rounded to bf16 here: with unit-norm q and k in Dk
 // dimensions, y_t = S_t^T q_t is a small projection of the state (|q.k| ~
@@ -38,17 +37,20 @@ constexpr float kRmsEps = 1e-6f;
 
 // ---------------------------------------------------------------------------
 // C[M, N] = A[M, K] * B[N, K]^T, bf16 operands, fp32 accumulation.
-// 128 x 128 workgroup tile, 4 wavefronts in a 2 x 2 grid of 64 x 64, K steps
-// of 64.  The tiles of A and B reach LDS through buffer loads that write LDS
-// directly, two K steps ahead into three stages; one barrier per K step.
-// Rows (128 bytes, two to a 256-byte line of the 64 banks) are stored
-// unpadded, 16-byte granule g of row r at position g ^ ((r / 2) mod 8): the
-// 16 rows of a fragment read then hit all 64 banks once.  Rows past M / N
-// lie outside the buffer range of the load and k past K gets an offset
-// outside it: both read as zeros.  K must be a multiple of 8.
+// A BM x BN workgroup tile, four wavefronts in a 2 x 2 grid of (BM/2) x (BN/2),
+// K steps of 32 on 16x16x32 MFMAs.  The K-step tiles of A and B reach LDS
+// through buffer loads that write LDS directly, three steps ahead into four
+// stages; the fragments of step k+1 are read while the MFMAs of step k run.
+// Every output element sums its K in the same order (32-wide steps, ascending)
+// whatever the tile size, so a product of a few rows equals, bit for bit, the
+// same rows of a taller product.
+// Rows (64 bytes, four to a 256-byte line of the 64 banks) are stored unpadded,
+// 16-byte granule g of row r at position g ^ ((r / 4) mod 4): the 16 rows of a
+// fragment read then hit all 64 banks once.  Rows past M / N lie outside the
+// buffer range of the load and k past K gets an offset outside it: both read
+// as zeros.  K must be a multiple of 8.
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 64, GSTAGES = 3;
-constexpr int GTILE = GBM * GBK * 2;                 // bytes of one A (or B) tile
+constexpr int GBK = 32, GSTAGES = 4;
 constexpr uint32_t G_OOB = 0x7FFFFFF0u;
 
 typedef __attribute__((address_space(3))) void *glds_ptr;
@@ -58,120 +60,179 @@ __device__ __forceinline__ void gload_lds(const void *base, uint32_t nrec, uint3
         (glds_ptr)(uintptr_t)(uint32_t)(uintptr_t)dst, 16, voff, 0, 0, 0);
 }
 
-// position of element (r, k) of a [rows][64] tile with permuted granules
-__device__ __forceinline__ int gsw(int r, int k) { return r * GBK + ((((k >> 3) ^ (r >> 1)) & 7) << 3) + (k & 7); }
+template <int BM, int BN> struct GemmTile {
+    static constexpr int MI = BM / 32, NJ = BN / 32;          // 16 x 16 tiles per wave
+    static constexpr int ATILE = BM * GBK * 2, BTILE = BN * GBK * 2;
+    static constexpr int STAGE = ATILE + BTILE;
+    static constexpr int LA = BM / 64, LB = BN / 64;          // 1 KB loads per thread per stage
+    static constexpr int LOADS = LA + LB;
+};
 
-template <typename OutT>
-__global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
+template <typename OutT, int BM, int BN>
+__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
                                                          OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
-                                                         int64_t ldb, int64_t ldc)
+                                                         int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int bn_log)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[GSTAGES * 2 * GTILE];
+    using G = GemmTile<BM, BN>;
+    constexpr int MI = G::MI, NJ = G::NJ, LA = G::LA, LB = G::LB;
+    __shared__ __attribute__((aligned(1024))) char smem[GSTAGES * G::STAGE];
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
-    const int64_t mrows = M - m0 < GBM ? M - m0 : GBM, nrows = N - n0 < GBN ? N - n0 : GBN;
+
+    // Tile order: workgroups are dispatched to the 8 XCDs in turn, so workgroup
+    // 8 j + x runs on XCD x; XCD x takes blocks of 32 / bn x bn tiles (rows x
+    // columns, bn = 2^bn_log <= 8), block 8 (j / 32) + x, tile j % 32 of it.  The
+    // 32 workgroups of an XCD then share a few rows of A tiles and columns of B
+    // tiles in its L2.  Tiles past the grid (blocks padded to a multiple of 8)
+    // end at once.
+    int tm, tn;
+    {
+        const int pid = blockIdx.x, x = pid & 7, j = pid >> 3;
+        const int blk = 8 * (j >> 5) + x, t = j & 31;
+        const int bn = 1 << bn_log, bm = 32 >> bn_log;
+        const int bpr = (tiles_n + bn - 1) / bn;                // blocks per block-row
+        tm = (blk / bpr) * bm + (t >> bn_log);
+        tn = (blk % bpr) * bn + (t & (bn - 1));
+        if (tm >= tiles_m || tn >= tiles_n) return;
+    }
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t mrows = M - m0 < BM ? M - m0 : BM, nrows = N - n0 < BN ? N - n0 : BN;
     const int ntk = (K + GBK - 1) / GBK;
 
-    // load t (t = 0..3) of this wave moves rows 8 i .. 8 i + 7 (i = wave + 4 t) of
-    // the A tile and of the B tile: lane -> row 8 i + lane / 8, stored granule lane % 8
-    uint32_t roff_a[4], roff_b[4];
-    int lgk[4];
+    // load t of this wave moves tile rows 16 i .. 16 i + 15 (i = wave + 4 t): lane
+    // -> row 16 i + lane / 4, LDS granule position lane % 4, which holds granule
+    // (lane % 4) ^ ((lane / 16) % 4) of the row
+    const int gk = 8 * ((lane & 3) ^ ((lane >> 4) & 3));     // k offset of the lane's granule
+    uint32_t roff_a[LA], roff_b[LB];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int r = 8 * (wave + 4 * t) + (lane >> 3);
-        lgk[t] = 8 * ((lane ^ (r >> 1)) & 7);                           // k offset of this lane's granule
-        roff_a[t] = (uint32_t)(r * lda * 2 + lgk[t] * 2);
-        roff_b[t] = (uint32_t)(r * ldb * 2 + lgk[t] * 2);
-    }
+    for (int t = 0; t < LA; ++t) roff_a[t] = (uint32_t)((16 * (wave + 4 * t) + (lane >> 2)) * lda * 2 + gk * 2);
+#pragma unroll
+    for (int t = 0; t < LB; ++t) roff_b[t] = (uint32_t)((16 * (wave + 4 * t) + (lane >> 2)) * ldb * 2 + gk * 2);
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * GBK;
-        char *sa = smem + stage * 2 * GTILE, *sb = sa + GTILE;
+        char *sa = smem + stage * G::STAGE, *sb = sa + G::ATILE;
         const __bf16 *ba = A + m0 * lda + k0, *bb = Bm + n0 * ldb + k0;
         const uint32_t na = (uint32_t)((mrows * lda - k0) * 2), nb = (uint32_t)((nrows * ldb - k0) * 2);
+        // granules past K: an offset outside the range (a select, not a branch)
+        const uint32_t oob = k0 + gk < K ? 0u : G_OOB;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool kin = k0 + lgk[t] < K;
-            gload_lds(ba, na, kin ? roff_a[t] : G_OOB, sa + (wave + 4 * t) * 1024);
-            gload_lds(bb, nb, kin ? roff_b[t] : G_OOB, sb + (wave + 4 * t) * 1024);
-        }
+        for (int t = 0; t < LA; ++t) gload_lds(ba, na, roff_a[t] | oob, sa + (wave + 4 * t) * 1024);
+#pragma unroll
+        for (int t = 0; t < LB; ++t) gload_lds(bb, nb, roff_b[t] | oob, sb + (wave + 4 * t) * 1024);
+    };
+    // fragment of rows r0 + ln, k 8 lg .. 8 lg + 7 (r0 a multiple of 16)
+    const int fpos = 8 * (lg ^ ((ln >> 2) & 3));
+    using F = Frag<__bf16, 32>;
+    auto read_frags = [&](int stage, F (&af)[MI], F (&bf)[NJ]) {
+        const __bf16 *As = reinterpret_cast<const __bf16 *>(smem + stage * G::STAGE);
+        const __bf16 *Bs = reinterpret_cast<const __bf16 *>(smem + stage * G::STAGE + G::ATILE);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i].load(As + (wm * (BM / 2) + 16 * i + ln) * GBK + fpos);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bf[j].load(Bs + (wn * (BN / 2) + 16 * j + ln) * GBK + fpos);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-    issue(0, 0);
-    issue(ntk > 1 ? 1 : 0, 1);
-    int st = 0;
-    for (int kt = 0; kt < ntk; ++kt) {
-        // tile kt complete (tile kt+1 may still be in flight), for every wave after
-        // the barrier, which also finds every wave done with tile kt-1
-        __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+        for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
+    auto mmas = [&](const F (&af)[MI], const F (&bf)[NJ]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = F::mma(af[i], bf[j], acc[i][j]);
+    };
+    // vmcnt(n) with expcnt and lgkmcnt left alone
+    auto wait_vm = [&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    };
+    auto barrier = [&]() {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // tile kt+2 into the stage of tile kt-1 (past the end, the last tile again:
-        // that stage is never read)
-        issue(kt + 2 < ntk ? kt + 2 : ntk - 1, st == 0 ? 2 : st - 1);
-        const __bf16 *As = reinterpret_cast<const __bf16 *>(smem + st * 2 * GTILE);
-        const __bf16 *Bs = As + GBM * GBK;
-#pragma unroll
-        for (int kk = 0; kk < GBK; kk += 32) {
-            Frag<__bf16, 32> af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i].load(As + gsw(wm * 64 + 16 * i + ln, kk + 8 * lg));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j].load(Bs + gsw(wn * 64 + 16 * j + ln, kk + 8 * lg));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = Frag<__bf16, 32>::mma(af[i], bf[j], acc[i][j]);
-        }
-        st = st == GSTAGES - 1 ? 0 : st + 1;
+    };
+    constexpr int L = G::LOADS;
+    auto last = [&](int kt) { return kt < ntk ? kt : ntk - 1; };   // past the end: the last tile again
+
+    // tiles 0, 1, 2 in flight; tile 0 landed for every wave, its fragments read
+    issue(0, 0);
+    issue(last(1), 1);
+    issue(last(2), 2);
+    wait_vm(std::integral_constant<int, 2 * L>{});
+    barrier();
+    F fa[2][MI], fb[2][NJ];
+    read_frags(0, fa[0], fb[0]);
+    // step kt: tile kt+1 landed for every wave (tile kt+2 may be in flight);
+    // tile kt+3 goes to the stage of tile kt-1, read before the barrier of step
+    // kt-1; the fragments of kt+1 are read while the MFMAs of kt run
+    auto step = [&](int kt, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        wait_vm(std::integral_constant<int, L>{});
+        barrier();
+        issue(last(kt + 3), (kt + 3) & 3);
+        if (kt + 1 < ntk) read_frags((kt + 1) & 3, fa[cur ^ 1], fb[cur ^ 1]);
+        mmas(fa[cur], fb[cur]);
+        // interleave: the loads into LDS and the fragment reads between the MFMAs
+        static_for<L>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        });
+        static_for<MI + NJ>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, (MI * NJ - L) / (MI + NJ), 0);
+        });
+    };
+    int kt = 0;
+    for (; kt + 1 < ntk; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        step(kt + 1, std::integral_constant<int, 1>{});
     }
+    if (kt < ntk) step(kt, std::integral_constant<int, 0>{});
     // no LDS write may land after the workgroup ends
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    wait_vm(std::integral_constant<int, 0>{});
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + 16 * j + ln;
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t col = n0 + wn * (BN / 2) + 16 * j + ln;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + wm * 64 + 16 * i + 4 * lg + e;
+                const int64_t row = m0 + wm * (BM / 2) + 16 * i + 4 * lg + e;
                 if (row < M && col < N) Cm[row * ldc + col] = from_f32<OutT>(acc[i][j][e]);
             }
         }
 }
 
-template <typename OutT>
-hipError_t gemm_nt(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                   int64_t ldb, int64_t ldc, hipStream_t s)
+template <typename OutT, int BM, int BN>
+hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                        int64_t ldb, int64_t ldc, hipStream_t s)
 {
-    if (M == 0 || N == 0) return hipSuccess;
-    dim3 grid((unsigned)((N + GBN - 1) / GBN), (unsigned)((M + GBM - 1) / GBM));
-    hipLaunchKernelGGL((gemm_nt_kernel<OutT>), grid, dim3(256), 0, s, A, Bm, C, (int)M, (int)N, (int)K, lda, ldb, ldc);
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    int bn_log = 0;
+    while (bn_log < 3 && (2 << bn_log) <= tiles_n) ++bn_log;
+    const int bn = 1 << bn_log, bm = 32 >> bn_log;
+    const int64_t blocks = (int64_t)((tiles_m + bm - 1) / bm) * ((tiles_n + bn - 1) / bn);
+    const int64_t grid = (blocks + 7) / 8 * 8 * 32;                 // 32 tiles a block, blocks a multiple of 8
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN>), dim3((unsigned)grid), dim3(256), 0, s, A, Bm, C, (int)M,
+                       (int)N, (int)K, lda, ldb, ldc, tiles_m, tiles_n, bn_log);
     return hipGetLastError();
 }
 
-// C[M, N] = A[M, K] B[N, K]^T: hipBLASLt, else gemm_nt_kernel.  GDN_OWN_GEMM=1
-// in the environment selects gemm_nt_kernel for every shape (so that it stays
-// tested against the library's results).
+// C[M, N] = A[M, K] B[N, K]^T.  The tile is the largest that still gives every
+// compute unit a workgroup (256 x 256, 128 x 128, else 64 x 64).
 template <typename OutT>
 hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                    int64_t ldb, int64_t ldc, hipStream_t s)
 {
-    const char *own = getenv("GDN_OWN_GEMM");
-    if (!(own && own[0] == '1')) {
-        const hipError_t e = blas_gemm_nt(A, Bm, C, std::is_same<OutT, __bf16>::value, M, N, K, lda, ldb, ldc, s);
-        if (e != hipErrorNotSupported) return e;
-    }
-    return gemm_nt<OutT>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    if (M == 0 || N == 0) return hipSuccess;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 256) >= 256) return gemm_nt_tile<OutT, 256, 256>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    if (tiles(128, 128) >= 256) return gemm_nt_tile<OutT, 128, 128>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    return gemm_nt_tile<OutT, 64, 64>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
@@ -408,7 +469,9 @@ struct WsLayout {
     size_t pre, post, z, ab, alpha, beta, y, g, rec, total;
 };
 
-WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv)
+// with_core: room for the per-chunk records of the chunked core (the decode
+// step runs the token-by-token kernel, which needs none)
+WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool with_core = true)
 {
     const size_t M = (size_t)(B * T);
     const size_t nqkv = (size_t)(H * (2 * Dk + Dv));
@@ -423,7 +486,7 @@ WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv)
     w.y = o;     o += al256(M * (size_t)(H * Dv) * 4);
     w.g = o;     o += al256(M * (size_t)(H * Dv) * 2);
     // per-chunk records of the fp32 core; chunk 64 needs the most of {16, 32, 64}
-    w.rec = o;   o += al256(prefill_f32_workspace_bytes(B, T, H, 64));
+    w.rec = o;   o += with_core ? al256(prefill_f32_workspace_bytes(B, T, H, 64)) : 0;
     w.total = o;
     return w;
 }
@@ -476,6 +539,13 @@ size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, in
     if (B * T == 0 || H == 0) return 0;
     return ws_layout(B, T, H, Dk, Dv).total;
 }
+
+size_t layer_decode_workspace_bytes(int64_t N, int64_t H, int64_t Dk, int64_t Dv)
+{
+    if (N == 0 || H == 0) return 0;
+    return ws_layout(N, 1, H, Dk, Dv, false).total;
+}
+
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
 {
@@ -539,7 +609,7 @@ hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
 {
     const int64_t N = a.N, H = a.H, Dk = a.Dk, Dv = a.Dv, hidden = a.hidden;
     if (N == 0 || H == 0) return hipSuccess;
-    const WsLayout w = ws_layout(N, 1, H, Dk, Dv);
+    const WsLayout w = ws_layout(N, 1, H, Dk, Dv, false);
     char *ws = static_cast<char *>(a.ws);
     float *pre = reinterpret_cast<float *>(ws + w.pre);
     float *post = reinterpret_cast<float *>(ws + w.post);
