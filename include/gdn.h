@@ -260,6 +260,25 @@ GDN_API gdn_status gdn_layer_decode_step(const void *x, const gdn_layer_params *
 GDN_API size_t gdn_layer_decode_workspace_bytes(int64_t N, int64_t hidden, int64_t H,
                                                 int64_t Dk, int64_t Dv);
 
+/*
+ * gdn_layer_decode_step_noalloc -- gdn_layer_decode_step without a workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * layouts, in-place updates, results and errors are those of
+ * gdn_layer_decode_step; the call allocates nothing, in the library or in HIP.
+ * The intermediates live in one 32 MiB scratch array that the library holds on
+ * each GPU it runs on until the process ends; a size for which
+ * gdn_layer_decode_workspace_bytes() exceeds 32 MiB fails with
+ * GDN_ERR_WORKSPACE.  Every call on a GPU shares that GPU's array and writes
+ * all of it that it reads, so nothing needs clearing between calls, but two
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race on it and give undefined results.
+ */
+GDN_API gdn_status gdn_layer_decode_step_noalloc(const void *x, const gdn_layer_params *p,
+                                                 float *conv_state, float *state, float *out,
+                                                 int64_t N, int64_t hidden, int64_t H, int64_t Dk,
+                                                 int64_t Dv, int64_t conv_k, hipStream_t stream);
+
 /* Static description of a status code. */
 GDN_API const char *gdn_status_str(gdn_status s);
 

@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
                 4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes",
             "gdn_decode_step", "gdn_decode_verify", "gdn_layer_fwd", "gdn_layer_workspace_bytes", "gdn_layer_decode_step",
-            "gdn_layer_decode_workspace_bytes", "gdn_status_str", "gdn_last_error")
+            "gdn_layer_decode_workspace_bytes", "gdn_layer_decode_step_noalloc", "gdn_status_str",
+            "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -82,6 +83,9 @@ def lib():
     L.gdn_layer_decode_step.restype = ctypes.c_int
     L.gdn_layer_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     L.gdn_layer_decode_workspace_bytes.restype = sz
+    L.gdn_layer_decode_step_noalloc.argtypes = [vp, ctypes.POINTER(gdn_layer_params), vp, vp, vp, i64, i64, i64,
+                                                i64, i64, i64, vp]
+    L.gdn_layer_decode_step_noalloc.restype = ctypes.c_int
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_last_error.argtypes = []
@@ -353,4 +357,29 @@ def layer_decode_step(x, params: dict, H: int, Dk: int, Dv: int, conv_state, sta
     _check(lib().gdn_layer_decode_step(_ptr(x), ctypes.byref(p), _ptr(conv_state), _ptr(state), _ptr(out),
                                        N, hidden, H, Dk, Dv, conv_k, _ptr(workspace), workspace.numel(),
                                        _stream(x.device)))
+    return out
+
+
+def layer_decode_step_noalloc(x, params: dict, H: int, Dk: int, Dv: int, conv_state, state, out):
+    """layer_decode_step on the library's own scratch memory: no workspace, and
+    out must be given, so that the call allocates nothing."""
+    import torch
+    N, hidden = x.shape
+    conv_k = params["conv_w"].shape[1]
+    _need(x, "x", torch.bfloat16)
+    for n in ("W_qkv", "conv_w", "W_ab", "W_gate", "W_o"):
+        _need(params[n], n, torch.bfloat16)
+    for n in ("A", "b_alpha", "norm_gamma"):
+        _need(params[n], n, torch.float32)
+    _need(conv_state, "conv_state", torch.float32)
+    _need(state, "state", torch.float32)
+    _need(out, "out", torch.float32)
+    nqkv = H * (2 * Dk + Dv)
+    _same(x, _layer_param_shapes(params, hidden, H, Dk, Dv, conv_k)
+          + [(conv_state, "conv_state", (N, conv_k - 1, nqkv)), (state, "state", (N, H, Dk, Dv)),
+             (out, "out", (N, hidden))])
+    p = gdn_layer_params(*(_ptr(params[n]) for n in ("W_qkv", "conv_w", "W_ab", "A", "b_alpha", "W_gate",
+                                                      "norm_gamma", "W_o")))
+    _check(lib().gdn_layer_decode_step_noalloc(_ptr(x), ctypes.byref(p), _ptr(conv_state), _ptr(state), _ptr(out),
+                                               N, hidden, H, Dk, Dv, conv_k, _stream(x.device)))
     return out

@@ -91,6 +91,9 @@ struct LayerArgs {
 };
 size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t Dk, int64_t Dv);
 size_t layer_decode_workspace_bytes(int64_t N, int64_t H, int64_t Dk, int64_t Dv);
+// the library's own scratch for the allocation-free decode step (layer.hip)
+size_t layer_decode_scratch_bytes();
+hipError_t layer_decode_scratch(void **out);
 hipError_t launch_layer(const LayerArgs &a, hipStream_t stream);
 
 // One token of the layer for N sequences: x [N, hidden]; conv_state [N, conv_k-1,

@@ -24,6 +24,7 @@
 // output.  The inputs x and the weights are bf16 and the products accumulate in
 // fp32, so the projections themselves are exact up to fp32 summation.
 #include <cstdlib>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -546,6 +547,36 @@ size_t layer_decode_workspace_bytes(int64_t N, int64_t H, int64_t Dk, int64_t Dv
     return ws_layout(N, 1, H, Dk, Dv, false).total;
 }
 
+// Scratch memory of the allocation-free layer decode step: the intermediates
+// of one call (in-projections, gates, core output, gated norm), each written in
+// full before it is read, so no call needs it cleared.  One copy per GPU, held
+// until the process ends and shared by every call on that GPU.
+constexpr size_t kLayerDecodeScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kLayerDecodeScratchBytes];
+
+size_t layer_decode_scratch_bytes() { return kLayerDecodeScratchBytes; }
+
+// Device address of this GPU's scratch (the current device), looked up once per
+// device: in host code the array's name is only a host-side stand-in.
+hipError_t layer_decode_scratch(void **out)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
 {
