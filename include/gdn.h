@@ -14,9 +14,10 @@
  * - Every tensor pointer is a DEVICE pointer on the current HIP device, to a
  *   dense row-major (last index fastest) buffer, 16-byte aligned.
  * - The caller allocates and frees every buffer.  The library's own state is
- *   a thread-local error string and, for the layer's projections, one
- *   hipBLASLt handle per device with a cache of per-shape plans (created on
- *   first use under a lock, kept until the process ends).  It is reentrant.
+ *   a thread-local error string and the scratch array of
+ *   gdn_layer_decode_step_noalloc (32 MiB per GPU, part of the code object,
+ *   its address looked up once per device under a lock).  Every entry point
+ *   other than that one is reentrant.
  * - Calls enqueue work on `stream` and return without synchronising.  A device
  *   fault shows up at the caller's next synchronisation.  With GDN_SYNC_CHECK=1
  *   in the environment (a debugging aid) every call waits for its stream and
@@ -202,9 +203,9 @@ GDN_API gdn_status gdn_decode_verify(const void *q, const void *k, const void *v
  * out[t,c] = sum_j conv_w[c,j] * in[t-(conv_k-1)+j, c] (zero history, no bias,
  * no activation).  RMSNorm runs per (token, head) over Dv.
  *
- * The four projections are plain products on hipBLASLt (bf16 operands, fp32
- * accumulation); this library's own GEMM kernel serves a shape the library
- * has no algorithm for, or every shape with GDN_OWN_GEMM=1 in the environment.
+ * The four projections are plain products on this library's GEMM kernel
+ * (bf16 operands, fp32 accumulation, every output summed over K in one order
+ * whatever the number of rows).
  *
  *   x     [B, T, hidden] bf16;  out [B, T, hidden] float32
  *   initial_state / final_state as in gdn_prefill_fwd (NULL allowed).
