@@ -1975,9 +1975,11 @@ template <int C, int DK> struct Fwd16Lay {
 // after its last read, and prefetch the next chunk's into registers.  The
 // chain reads the K^T operands of the state update in step 1, so K (like Q
 // and V) is free after step 1.  Per chunk c (barriers B1, B2, B3):
-//   B1..B2  chain: step 1 (K S, Q S, X);    staging: P of chunk c
-//   B2..B3  chain: step 2 (U = T X);        staging: K, Q, V, G2, beta of chunk c+1
-//   B3..B1  chain: step 3 (y, update);      staging: T of chunk c+1
+//   B1..B2  chain: step 1 (K S, Q S, X);    staging: P and T of chunk c
+//   B2..B3  chain: step 2 (U = T X);        staging: 3/4 of K, V, G2, beta of chunk c+1
+//   B3..B1  chain: step 3 (y, update);      staging: the rest of K, Q of chunk c+1
+// (the K and Q conversions to bf16 pairs are the staging's largest part, so
+// they are spread over the two windows after step 1)
 constexpr int NTF = 512;
 
 template <int C, int DK>
@@ -2030,20 +2032,34 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
         auto rec_of = [&](int64_t c) { return p.rec + (bh * NC + c) * p.rec_floats; };
         f32x4 rK[NVK], rQ[NVK], rT[NVT], rP[NVT], rV = zero4();
         float rG = 0.f, rBe = 0.f, rEd = 0.f;
-        int64_t cKQ = 0;                                   // chunk held by rK, rQ, rV, rG, rBe
+        int64_t cK = 0;                                    // chunk held by rV, rG, rBe
         const int uv = ts < NUV ? ts : NUV - 1, ug = ts < C ? ts : C - 1;
-        auto load_kqv = [&](int64_t c) {
-            cKQ = c;
+        // unit u = ts + NST i of a K or Q tile: row ts / (DK/4) + i NST / (DK/4),
+        // columns 4 (ts mod DK/4) ..; byte offsets inside a chunk's rows, 32-bit
+        constexpr int RPI = NST / (DK / 4);                 // rows between units i and i+1
+        static_assert(NUK % NST == 0, "whole K/Q tiles per staging pass");
+        const int kr0 = ts / (DK / 4), kc0 = (ts % (DK / 4)) * 4;
+        const uint32_t kstep = (uint32_t)(RPI * p.ks * 4), qstep = (uint32_t)(RPI * p.qs * 4);
+        const uint32_t koff0 = (uint32_t)((kr0 * p.ks + kc0) * 4), qoff0 = (uint32_t)((kr0 * p.qs + kc0) * 4);
+        // rows of a K or Q tile at or past T (the last chunk only) read token
+        // T-1: their beta is 0 and their outputs are not stored, so the rows
+        // need no zeros (finite values suffice)
+        auto tile_off = [&](int64_t c0, int i, int64_t stride, uint32_t off0, uint32_t step) {
+            if (c0 + C <= T) return off0 + (uint32_t)i * step;
+            const int64_t r = kr0 + (int64_t)i * RPI;
+            return (uint32_t)(((c0 + r < T ? r : T - 1 - c0) * stride + kc0) * 4);
+        };
+        // K units [i0, i1) of chunk c
+        auto load_k = [&](int64_t c, int i0, int i1) {
             const int64_t c0 = c * C;
+            const char *kb = reinterpret_cast<const char *>(kg + (b * T + c0) * p.ks + h * DK);
 #pragma unroll
-            for (int i = 0; i < NVK; ++i) {
-                int u = ts + NST * i;
-                u = (NUK % NST == 0 || u < NUK) ? u : NUK - 1;
-                const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
-                const int64_t t = c0 + r < T ? c0 + r : T - 1;
-                rK[i] = *reinterpret_cast<const f32x4 *>(kg + (b * T + t) * p.ks + h * DK + col);
-                rQ[i] = *reinterpret_cast<const f32x4 *>(qg + (b * T + t) * p.qs + h * DK + col);
-            }
+            for (int i = i0; i < i1; ++i)
+                rK[i] = *reinterpret_cast<const f32x4 *>(kb + tile_off(c0, i, p.ks, koff0, kstep));
+        };
+        auto load_vg = [&](int64_t c) {
+            cK = c;
+            const int64_t c0 = c * C;
             const int rv = uv / (BV / 4), cv = (uv % (BV / 4)) * 4;
             const int64_t tv = c0 + rv < T ? c0 + rv : T - 1;
             rV = *reinterpret_cast<const f32x4 *>(vg + (b * T + tv) * p.vs + h * Dv + n0 + cv);
@@ -2051,6 +2067,13 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
             rG = rec_of(c)[Rec<C>::oG + ug];
             rEd = rec_of(c)[Rec<C>::oEd + ug];
             rBe = p.beta[(b * T + tg) * H + h];
+        };
+        auto load_q = [&](int64_t c) {
+            const int64_t c0 = c * C;
+            const char *qb = reinterpret_cast<const char *>(qg + (b * T + c0) * p.qs + h * DK);
+#pragma unroll
+            for (int i = 0; i < NVK; ++i)
+                rQ[i] = *reinterpret_cast<const f32x4 *>(qb + tile_off(c0, i, p.qs, qoff0, qstep));
         };
         auto load_cc = [&](f32x4 (&rr)[NVT], int64_t c, int off) {
             const float *rec = rec_of(c) + off;
@@ -2062,25 +2085,29 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
                 rr[i] = *reinterpret_cast<const f32x4 *>(rec + r * C + col);
             }
         };
-        auto write_kqv = [&](int gb) {
+        auto write_k = [&](int i0, int i1) {
 #pragma unroll
-            for (int i = 0; i < NVK; ++i) {
-                const int u = ts + NST * i;
-                const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
-                if (NUK % NST == 0 || u < NUK) {
-                    const bool ok = cKQ * C + r < T;
-                    store_split4(Kh + r * KP + col, Kl + r * KP + col, ok ? rK[i] : zero4());
-                    store_split4(Qh + r * KP + col, Ql + r * KP + col, ok ? rQ[i] : zero4());
-                }
+            for (int i = i0; i < i1; ++i) {
+                const int r = kr0 + RPI * i;
+                store_split4(Kh + r * KP + kc0, Kl + r * KP + kc0, rK[i]);
             }
+        };
+        auto write_vg = [&](int gb) {
             if (ts < NUV) {
                 const int r = ts / (BV / 4), col = (ts % (BV / 4)) * 4;
-                *reinterpret_cast<f32x4 *>(Ins + r * VP + col) = cKQ * C + r < T ? rV : zero4();
+                *reinterpret_cast<f32x4 *>(Ins + r * VP + col) = cK * C + r < T ? rV : zero4();
             }
             if (ts < C) {
                 Gb[gb * C + ts] = rG;
                 Edb[gb * C + ts] = rEd;
-                Bb[gb * C + ts] = cKQ * C + ts < T ? rBe : 0.f;
+                Bb[gb * C + ts] = cK * C + ts < T ? rBe : 0.f;
+            }
+        };
+        auto write_q = [&]() {
+#pragma unroll
+            for (int i = 0; i < NVK; ++i) {
+                const int r = kr0 + RPI * i;
+                store_split4(Qh + r * KP + kc0, Ql + r * KP + kc0, rQ[i]);
             }
         };
         auto write_cc = [&](const f32x4 (&rr)[NVT], __bf16 *hi, __bf16 *lo) {
@@ -2091,26 +2118,38 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
                 if (NUT % NST == 0 || u < NUT) store_split4(hi + r * CP + col, lo + r * CP + col, rr[i]);
             }
         };
-        // chunk 0 into LDS (P(0) is written in the first window), then chunk 1
-        // in flight, in the issue order of the loop
-        load_kqv(0);
-        load_cc(rT, 0, Rec<C>::oT);
+        // chunk 0 into LDS (P(0) and T(0) are written in its first window),
+        // then chunk 1 in flight, in the issue order of the loop
+        constexpr int NK1 = (3 * NVK + 2) / 4;          // K units staged in B2..B3, the rest in B3..B1
+        load_k(0, 0, NVK);
+        load_vg(0);
+        load_q(0);
         load_cc(rP, 0, Rec<C>::oP);
-        write_kqv(0);
-        write_cc(rT, Th, Tl);
-        load_kqv(clampc(1));
+        load_cc(rT, 0, Rec<C>::oT);
+        write_k(0, NVK);
+        write_vg(0);
+        write_q();
+        load_k(clampc(1), 0, NK1);
+        load_vg(clampc(1));
         __builtin_amdgcn_sched_barrier(0);
-        load_cc(rT, clampc(1), Rec<C>::oT);
+        load_k(clampc(1), NK1, NVK);
+        load_q(clampc(1));
         lds_barrier();                                  // B1 of chunk 0
         for (int64_t c = 0; c < NC; ++c) {
             write_cc(rP, Ph, Pl);                       // P(c): P(c-1) last read in step 3
+            write_cc(rT, Th, Tl);                       // T(c): T(c-1) last read in step 2
             load_cc(rP, clampc(c + 1), Rec<C>::oP);
+            load_cc(rT, clampc(c + 1), Rec<C>::oT);
             lds_barrier();                              // B2
-            write_kqv((int)((c + 1) & 1));              // chunk c+1: K, Q, V last read in step 1
-            load_kqv(clampc(c + 2));
+            write_k(0, NK1);                            // chunk c+1: K and V last read in step 1
+            write_vg((int)((c + 1) & 1));
+            load_k(clampc(c + 2), 0, NK1);
+            load_vg(clampc(c + 2));
             lds_barrier();                              // B3
-            write_cc(rT, Th, Tl);                       // T(c+1): T(c) last read in step 2
-            load_cc(rT, clampc(c + 2), Rec<C>::oT);
+            write_k(NK1, NVK);
+            write_q();                                  // Q(c+1): Q(c) last read in step 1
+            load_k(clampc(c + 2), NK1, NVK);
+            load_q(clampc(c + 2));
             lds_barrier();                              // B1 of chunk c+1
         }
     } else {
@@ -2348,7 +2387,9 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
     // fp32 MFMA unless the caller's bound is the bf16 one (hi/lo operands carry
     // about 16 bits, which an fp32-input run with a small RMS(y) can exceed)
     if constexpr (DK % 32 == 0 && C % 32 == 0) {
-        if (a.hilo_core) {
+        // (its staging addresses a chunk's q and k rows by 32-bit byte offsets)
+        const int64_t wide = a.q_tok_stride > a.k_tok_stride ? a.q_tok_stride : a.k_tok_stride;
+        if (a.hilo_core && (int64_t)C * wide * 4 < ((int64_t)1 << 32)) {
             hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
             return hipGetLastError();
         }
