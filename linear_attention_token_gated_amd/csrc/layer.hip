@@ -51,7 +51,7 @@ constexpr float kRmsEps = 1e-6f;
 // buffer range of the load and k past K gets an offset outside it: both read
 // as zeros.  K must be a multiple of 8.
 // ---------------------------------------------------------------------------
-constexpr int GBK = 32, GSTAGES = 4;
+constexpr int GBK = 32;
 constexpr uint32_t G_OOB = 0x7FFFFFF0u;
 
 typedef __attribute__((address_space(3))) void *glds_ptr;
@@ -69,14 +69,16 @@ template <int BM, int BN> struct GemmTile {
     static constexpr int LOADS = LA + LB;
 };
 
-template <typename OutT, int BM, int BN>
+// ST stages of K steps in LDS (a power of two >= 4), ST - 1 of them in flight
+template <typename OutT, int BM, int BN, int ST>
 __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
                                                          OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
                                                          int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int bn_log)
 {
     using G = GemmTile<BM, BN>;
     constexpr int MI = G::MI, NJ = G::NJ, LA = G::LA, LB = G::LB;
-    __shared__ __attribute__((aligned(1024))) char smem[GSTAGES * G::STAGE];
+    static_assert(ST >= 4 && (ST & (ST - 1)) == 0 && (ST - 2) * G::LOADS < 64, "stages");
+    __shared__ __attribute__((aligned(1024))) char smem[ST * G::STAGE];
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
@@ -158,23 +160,25 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
     constexpr int L = G::LOADS;
     auto last = [&](int kt) { return kt < ntk ? kt : ntk - 1; };   // past the end: the last tile again
 
-    // tiles 0, 1, 2 in flight; tile 0 landed for every wave, its fragments read
-    issue(0, 0);
-    issue(last(1), 1);
-    issue(last(2), 2);
-    wait_vm(std::integral_constant<int, 2 * L>{});
+    // tiles 0 .. ST-2 in flight; tile 0 landed for every wave, its fragments read
+    static_for<ST - 1>([&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        issue(last(t), t);
+    });
+    wait_vm(std::integral_constant<int, (ST - 2) * L>{});
     barrier();
     F fa[2][MI], fb[2][NJ];
     read_frags(0, fa[0], fb[0]);
-    // step kt: tile kt+1 landed for every wave (tile kt+2 may be in flight);
-    // tile kt+3 goes to the stage of tile kt-1, read before the barrier of step
-    // kt-1; the fragments of kt+1 are read while the MFMAs of kt run
+    // step kt: tile kt+1 landed for every wave (tiles kt+2 .. kt+ST-2 may be in
+    // flight); tile kt+ST-1 goes to the stage of tile kt-1, read before the
+    // barrier of step kt-1; the fragments of kt+1 are read while the MFMAs of
+    // kt run
     auto step = [&](int kt, auto cur_c) {
         constexpr int cur = decltype(cur_c)::value;
-        wait_vm(std::integral_constant<int, L>{});
+        wait_vm(std::integral_constant<int, (ST - 3) * L>{});
         barrier();
-        issue(last(kt + 3), (kt + 3) & 3);
-        if (kt + 1 < ntk) read_frags((kt + 1) & 3, fa[cur ^ 1], fb[cur ^ 1]);
+        issue(last(kt + ST - 1), (kt + ST - 1) & (ST - 1));
+        if (kt + 1 < ntk) read_frags((kt + 1) & (ST - 1), fa[cur ^ 1], fb[cur ^ 1]);
         mmas(fa[cur], fb[cur]);
         // interleave: the loads into LDS and the fragment reads between the MFMAs
         static_for<L>([&](auto) {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
         }
 }
 
-template <typename OutT, int BM, int BN>
+template <typename OutT, int BM, int BN, int ST>
 hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, int64_t ldc, hipStream_t s)
 {
@@ -218,22 +222,24 @@ hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, i
     const int bn = 1 << bn_log, bm = 32 >> bn_log;
     const int64_t blocks = (int64_t)((tiles_m + bm - 1) / bm) * ((tiles_n + bn - 1) / bn);
     const int64_t grid = (blocks + 7) / 8 * 8 * 32;                 // 32 tiles a block, blocks a multiple of 8
-    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN>), dim3((unsigned)grid), dim3(256), 0, s, A, Bm, C, (int)M,
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST>), dim3((unsigned)grid), dim3(256), 0, s, A, Bm, C, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, tiles_m, tiles_n, bn_log);
     return hipGetLastError();
 }
 
 // C[M, N] = A[M, K] B[N, K]^T.  The tile is the largest that still gives every
-// compute unit a workgroup (256 x 256, 128 x 128, else 64 x 64).
+// compute unit a workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles
+// do little MFMA work per K step, so they keep 7 steps in flight (8 stages,
+// 64 KB of LDS) against the memory latency; the larger ones 3.
 template <typename OutT>
 hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                    int64_t ldb, int64_t ldc, hipStream_t s)
 {
     if (M == 0 || N == 0) return hipSuccess;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 256) return gemm_nt_tile<OutT, 256, 256>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
-    if (tiles(128, 128) >= 256) return gemm_nt_tile<OutT, 128, 128>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
-    return gemm_nt_tile<OutT, 64, 64>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    if (tiles(256, 256) >= 256) return gemm_nt_tile<OutT, 256, 256, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    if (tiles(128, 128) >= 256) return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
