@@ -45,9 +45,11 @@ constexpr float kRmsEps = 1e-6f;
 // Every output element sums its K in the same order (32-wide steps, ascending)
 // whatever the tile size, so a product of a few rows equals, bit for bit, the
 // same rows of a taller product.
-// Rows (64 bytes, four to a 256-byte line of the 64 banks) are stored unpadded,
-// 16-byte granule g of row r at position g ^ ((r / 4) mod 4): the 16 rows of a
-// fragment read then hit all 64 banks once.  Rows past M / N lie outside the
+// Rows (64 bytes) are stored unpadded, 16-byte granule g of row r at position
+// g ^ s(r), s(r) = ((r / 2) ^ (r / 4)) mod 4: any 8 consecutive rows of a
+// fragment read then cover 128 bytes of banks once and the 16 rows of it 256
+// bytes once, so the read is conflict-free whether the LDS serves 8 or 16
+// lanes of a 16-byte read per pass.  Rows past M / N lie outside the
 // buffer range of the load and k past K gets an offset outside it: both read
 // as zeros.  K must be a multiple of 8.
 // ---------------------------------------------------------------------------
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
 
     // load t of this wave moves tile rows 16 i .. 16 i + 15 (i = wave + 4 t): lane
     // -> row 16 i + lane / 4, LDS granule position lane % 4, which holds granule
-    // (lane % 4) ^ ((lane / 16) % 4) of the row
-    const int gk = 8 * ((lane & 3) ^ ((lane >> 4) & 3));     // k offset of the lane's granule
+    // (lane % 4) ^ s(lane / 4) of the row
+    const int gk = 8 * ((lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3));   // k offset of the lane's granule
     uint32_t roff_a[LA], roff_b[LB];
 #pragma unroll
     for (int t = 0; t < LA; ++t) roff_a[t] = (uint32_t)((16 * (wave + 4 * t) + (lane >> 2)) * lda * 2 + gk * 2);
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
         for (int t = 0; t < LB; ++t) gload_lds(bb, nb, roff_b[t] | oob, sb + (wave + 4 * t) * 1024);
     };
     // fragment of rows r0 + ln, k 8 lg .. 8 lg + 7 (r0 a multiple of 16)
-    const int fpos = 8 * (lg ^ ((ln >> 2) & 3));
+    const int fpos = 8 * (lg ^ (((ln >> 1) ^ (ln >> 2)) & 3));
     using F = Frag<__bf16, 32>;
     auto read_frags = [&](int stage, F (&af)[MI], F (&bf)[NJ]) {
         const __bf16 *As = reinterpret_cast<const __bf16 *>(smem + stage * G::STAGE);
