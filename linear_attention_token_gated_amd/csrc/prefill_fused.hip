@@ -216,29 +216,42 @@ __device__ __forceinline__ f32x4 mma_hl(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 
     return F16::mma(a2, b, acc);
 }
 
-// X <- (I - nL)^-1 X for a 16 x 16 block by forward substitution, lane (r, g)
-// holding X[r][4g + e] and nL[r][:] = -L[r][:] (strictly lower): step S adds
-// nL[r][S] X[S][:] to every row r (a no-op for r <= S).  X[S][:] sits in lane S
-// of the same 16-lane row and is read through a DPP row broadcast folded into
-// the multiply-add.  The fifteen steps are one asm statement, so nothing is
-// scheduled between them: a DPP read of a VGPR needs two wait states after a
-// VALU write of it, which the s_nop gives the writes before the first step;
-// inside, the other three columns of a step sit between a write and its read.
-#define GDN_FS1(S, E, N) "v_fmac_f32_dpp %" #E ", %" #E ", %" #N " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n"
-#define GDN_FS(S, N) GDN_FS1(S, 0, N) GDN_FS1(S, 1, N) GDN_FS1(S, 2, N) GDN_FS1(S, 3, N)
-__device__ __forceinline__ void fsub16(float (&X)[4], const float (&nL)[16]) {
-    asm volatile("s_nop 1\n"
-                 GDN_FS(0, 4) GDN_FS(1, 5) GDN_FS(2, 6) GDN_FS(3, 7) GDN_FS(4, 8)
-                 GDN_FS(5, 9) GDN_FS(6, 10) GDN_FS(7, 11) GDN_FS(8, 12) GDN_FS(9, 13)
-                 GDN_FS(10, 14) GDN_FS(11, 15) GDN_FS(12, 16) GDN_FS(13, 17) GDN_FS(14, 18)
-                 "s_nop 1"
-                 : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
-                 : "v"(nL[0]), "v"(nL[1]), "v"(nL[2]), "v"(nL[3]), "v"(nL[4]), "v"(nL[5]), "v"(nL[6]),
-                   "v"(nL[7]), "v"(nL[8]), "v"(nL[9]), "v"(nL[10]), "v"(nL[11]), "v"(nL[12]), "v"(nL[13]),
-                   "v"(nL[14]));
-}
-#undef GDN_FS
+// One step of X <- (I - nL)^-1 X for a 16 x 16 block by forward substitution,
+// lane (r, g) holding X[r][4g + e] and nL[r][:] = -L[r][:] (strictly lower):
+// step S adds nL[r][S] X[S][:] to every row r (a no-op for r <= S), with n =
+// nL[r][S].  X[S][:] sits in lane S of the same 16-lane row and is read
+// through a DPP row broadcast folded into the multiply-add.  Each step is one
+// asm statement led by s_nop 1: a DPP read of a VGPR needs two wait states
+// after a VALU write of it, and the compiler may place its own instructions (a
+// copy of X among them) between the steps; inside a step the four columns are
+// independent.  The compiler schedules nothing across an asm statement, so
+// what the caller writes between two steps runs between them.
+template <int S> __device__ __forceinline__ void fsub_step(float (&X)[4], float n);
+#define GDN_FS1(S, E) "v_fmac_f32_dpp %" #E ", %" #E ", %4 row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n"
+#define GDN_FSTEP(S)                                                                                   \
+    template <> __device__ __forceinline__ void fsub_step<S>(float (&X)[4], float n) {               \
+        asm volatile("s_nop 1\n" GDN_FS1(S, 0) GDN_FS1(S, 1) GDN_FS1(S, 2) GDN_FS1(S, 3)              \
+                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])                                 \
+                     : "v"(n));                                                                       \
+    }
+GDN_FSTEP(0) GDN_FSTEP(1) GDN_FSTEP(2) GDN_FSTEP(3) GDN_FSTEP(4) GDN_FSTEP(5) GDN_FSTEP(6) GDN_FSTEP(7)
+GDN_FSTEP(8) GDN_FSTEP(9) GDN_FSTEP(10) GDN_FSTEP(11) GDN_FSTEP(12) GDN_FSTEP(13) GDN_FSTEP(14)
+#undef GDN_FSTEP
 #undef GDN_FS1
+
+// Blocks A_mj (m > j) that preparation wave pw forms in X, in order (m, then j)
+template <int NB> constexpr int own_count(int pw) {
+    int n = 0;
+    for (int m = 1; m < NB; ++m)
+        for (int j = 0; j < m; ++j) n += a_owner<NB>(m, j) == pw;
+    return n;
+}
+template <int NB> constexpr int own_blk(int pw, int k, bool row) {
+    for (int m = 1; m < NB; ++m)
+        for (int j = 0; j < m; ++j)
+            if (a_owner<NB>(m, j) == pw && k-- == 0) return row ? m : j;
+    return 0;
+}
 
 template <int C, int DK>
 __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
@@ -658,53 +671,78 @@ __global__ __launch_bounds__(FT, 1) void gdn_prefill_fused_kernel(FusedParams p)
                 for (int kk = 0; kk < NK; ++kk) acc = FDK::mma(kf[jb][kk], xr[kk], acc);
                 return acc;
             };
-            // P row pw: blocks left of the diagonal, then the diagonal block
-            static_for<NB - 1>([&](auto jb_c) {
+            // every Gram block at once (A_pp first: its substitution is the long
+            // chain), then the decay factors, so that the substitution steps
+            // below have only registers to wait for
+            constexpr int NOWN = own_count<NB>(pw);
+            const f32x4 gpp = gramr(kf[pw], pw);
+            f32x4 gp[NB], ga[NOWN > 0 ? NOWN : 1], fp[NB], fa[NOWN > 0 ? NOWN : 1];
+            static_for<NB>([&](auto jb_c) {
                 constexpr int jb = decltype(jb_c)::value;
-                if constexpr (jb < pw) {
-                    const f32x4 d = decay_off(gramr(qf, jb), row_factor(dt, jb, pw), jb, dt);
-                    split4(d, Ph[par][jb], Pl[par][jb]);
-                }
+                if constexpr (jb <= pw) gp[jb] = gramr(qf, jb);
             });
-            split4(decay_diag(gramr(qf, pw), pw, true, dt), Pdh[par], Pdl[par]);
-            // A_pp: -A_pp rows through the T_pp slot (scratch), then forward substitution
+            static_for<NOWN>([&](auto k_c) {
+                constexpr int k = decltype(k_c)::value;
+                ga[k] = gramr(kf[own_blk<NB>(pw, k, true)], own_blk<NB>(pw, k, false));
+            });
+            const float nbet = -ab[C + 16 * pw + ln];
+            const f32x4 one4 = {1.f, 1.f, 1.f, 1.f};
+            static_for<NB>([&](auto jb_c) {
+                constexpr int jb = decltype(jb_c)::value;
+                if constexpr (jb < pw) fp[jb] = decay_off(one4, row_factor(dt, jb, pw), jb, dt);
+                else if constexpr (jb == pw) fp[jb] = decay_diag(one4, pw, true, dt);
+            });
+            static_for<NOWN>([&](auto k_c) {
+                constexpr int k = decltype(k_c)::value;
+                constexpr int m = own_blk<NB>(pw, k, true), jj = own_blk<NB>(pw, k, false);
+                fa[k] = decay_off(one4, row_factor(dt, jj, m) * ab[C + 16 * m + ln], jj, dt);
+            });
+            // A_pp: -A_pp rows through the T_pp slot (scratch)
+            float nL[16];
             {
-                const float nbet = -ab[C + 16 * pw + ln];
-                const f32x4 d = decay_diag(gramr(kf[pw], pw), pw, false, dt) * nbet;
+                const f32x4 d = decay_diag(gpp, pw, false, dt) * nbet;
                 float *scr = reinterpret_cast<float *>(XTb(pw));
                 *reinterpret_cast<f32x4 *>(scr + ln * 16 + 4 * lg) = d;
-                float nL[16];
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const f32x4 v4 = *reinterpret_cast<const f32x4 *>(scr + ln * 16 + 4 * s4);
                     nL[4 * s4] = v4[0]; nL[4 * s4 + 1] = v4[1]; nL[4 * s4 + 2] = v4[2]; nL[4 * s4 + 3] = v4[3];
                 }
-                float X[4];
+            }
+            // the other blocks, one between each pair of substitution steps: P
+            // row pw (left of the diagonal, then the diagonal block), then the
+            // owned blocks of A below the diagonal
+            auto task = [&](auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                if constexpr (t < pw) {
+                    split4(gp[t] * fp[t], Ph[par][t], Pl[par][t]);
+                } else if constexpr (t == pw) {
+                    split4(gp[pw] * fp[pw], Pdh[par], Pdl[par]);
+                } else if constexpr (t - pw - 1 < NOWN) {
+                    constexpr int k = t - pw - 1;
+                    constexpr int o = off_idx_c(own_blk<NB>(pw, k, true), own_blk<NB>(pw, k, false));
+                    bf16x4 hv, lv;
+                    split4(ga[k] * fa[k], hv, lv);
+                    *reinterpret_cast<bf16x4 *>(XAb(o) + ln * 16 + 4 * lg) = hv;
+                    *reinterpret_cast<bf16x4 *>(XAb(o) + 256 + ln * 16 + 4 * lg) = lv;
+                }
+            };
+            static_assert(NB + NOWN <= 15, "one block a step");
+            float X[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) X[e] = ln == 4 * lg + e ? 1.f : 0.f;
-                fsub16(X, nL);
+            for (int e = 0; e < 4; ++e) X[e] = ln == 4 * lg + e ? 1.f : 0.f;
+            static_for<15>([&](auto s_c) {
+                constexpr int S = decltype(s_c)::value;
+                fsub_step<S>(X, nL[S]);
+                task(s_c);
+            });
+            {
                 bf16x4 hv, lv;
                 split4(f32x4{X[0], X[1], X[2], X[3]}, hv, lv);
                 // the scratch rows were read above (same wavefront, LDS in order)
                 *reinterpret_cast<bf16x4 *>(XTb(pw) + ln * 16 + 4 * lg) = hv;
                 *reinterpret_cast<bf16x4 *>(XTb(pw) + 256 + ln * 16 + 4 * lg) = lv;
             }
-            // blocks of A below the diagonal owned by this wave
-            static_for<NB>([&](auto m_c) {
-                constexpr int m = decltype(m_c)::value;
-                static_for<m>([&](auto jj_c) {
-                    constexpr int jj = decltype(jj_c)::value;
-                    if constexpr (a_owner<NB>(m, jj) == pw) {
-                        const float f = row_factor(dt, jj, m) * ab[C + 16 * m + ln];
-                        const f32x4 d = decay_off(gramr(kf[m], jj), f, jj, dt);
-                        bf16x4 hv, lv;
-                        split4(d, hv, lv);
-                        constexpr int o = off_idx_c(m, jj);
-                        *reinterpret_cast<bf16x4 *>(XAb(o) + ln * 16 + 4 * lg) = hv;
-                        *reinterpret_cast<bf16x4 *>(XAb(o) + 256 + ln * 16 + 4 * lg) = lv;
-                    }
-                });
-            });
         };
 
         // T = (I + A)^-1 from the diagonal inverses T_mm (in XT) by halves of the
