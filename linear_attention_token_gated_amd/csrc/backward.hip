@@ -670,7 +670,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry16_kernel(BwdParams p)
     using F32 = Frag<__bf16, 32>;
     static_assert(DK % 32 == 0 || DK == 16, "Dk");
     constexpr int NST = 256;                                   // staging threads
-    constexpr int NUK = C * DK / 4, NVK = (NUK + NST - 1) / NST;
+    constexpr int NUK = C * DK / 8, NVK = (NUK + NST - 1) / NST;   // 8-element units of K or Q
     constexpr int NUT = C * C / 4, NVT = (NUT + NST - 1) / NST;
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry16_kernel(BwdParams p)
     // zeros past T applied when the data is written), so the compiler can wait
     // on exact outstanding-load counts instead of draining the prefetch.
     f32x4 rP[NVT], rT[NVT];
-    bf16x4 rK[NVK], rQ[NVK];
+    bf16x8 rK[NVK], rQ[NVK];
     f32x4 rY = zero4();                      // dY piece (adjoint)
     bf16x4 rV = Raw4<__bf16>::zero();        // V piece (state pass)
     float rG = 0.f, rBe = 0.f, rGa = 0.f;    // rGa: G2 of this thread's set-A token (e^G o dY)
@@ -748,10 +748,10 @@ __global__ __launch_bounds__(NTC) void bwd_carry16_kernel(BwdParams p)
         for (int i = 0; i < NVK; ++i) {
             int u = ts + NST * i;
             u = (NUK % NST == 0 || u < NUK) ? u : NUK - 1;
-            const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+            const int r = u / (DK / 8), col = (u % (DK / 8)) * 8;
             const int64_t t = c0 + r < T ? c0 + r : T - 1;
-            rK[i] = *reinterpret_cast<const bf16x4 *>(kg + ((b * T + t) * H + h) * DK + col);
-            if constexpr (ADJ) rQ[i] = *reinterpret_cast<const bf16x4 *>(qg + ((b * T + t) * H + h) * DK + col);
+            rK[i] = *reinterpret_cast<const bf16x8 *>(kg + ((b * T + t) * H + h) * DK + col);
+            if constexpr (ADJ) rQ[i] = *reinterpret_cast<const bf16x8 *>(qg + ((b * T + t) * H + h) * DK + col);
         }
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
@@ -802,11 +802,11 @@ __global__ __launch_bounds__(NTC) void bwd_carry16_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < NVK; ++i) {
             const int u = ts + NST * i;
-            const int r = u / (DK / 4), col = (u % (DK / 4)) * 4;
+            const int r = u / (DK / 8), col = (u % (DK / 8)) * 8;
             if (NUK % NST == 0 || u < NUK) {
                 const bool ok = cB * C + r < T;
-                *reinterpret_cast<bf16x4 *>(Kd + r * KP + col) = ok ? rK[i] : Raw4<__bf16>::zero();
-                if constexpr (ADJ) *reinterpret_cast<bf16x4 *>(Qd + r * KP + col) = ok ? rQ[i] : Raw4<__bf16>::zero();
+                *reinterpret_cast<bf16x8 *>(Kd + r * KP + col) = ok ? rK[i] : bf16x8{};
+                if constexpr (ADJ) *reinterpret_cast<bf16x8 *>(Qd + r * KP + col) = ok ? rQ[i] : bf16x8{};
             }
         }
 #pragma unroll
