@@ -72,10 +72,15 @@ template <int BM, int BN> struct GemmTile {
 };
 
 // ST stages of K steps in LDS (a power of two >= 4), ST - 1 of them in flight
+// Two products of one A may share a launch: column tiles from tiles_n1 on
+// belong to the second (B2, C2, N2, ldb2, ldc2); a single product passes
+// tiles_n1 = tiles_n.
 template <typename OutT, int BM, int BN, int ST>
-__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ Bm,
-                                                         OutT *__restrict__ Cm, int M, int N, int K, int64_t lda,
-                                                         int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int bn_log)
+__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ B1,
+                                                         OutT *__restrict__ C1, int M, int N1, int K, int64_t lda,
+                                                         int64_t ldb1, int64_t ldc1, int tiles_m, int tiles_n, int bn_log,
+                                                         const __bf16 *__restrict__ B2, OutT *__restrict__ C2, int N2,
+                                                         int64_t ldb2, int64_t ldc2, int tiles_n1)
 {
     using G = GemmTile<BM, BN>;
     constexpr int MI = G::MI, NJ = G::NJ, LA = G::LA, LB = G::LB;
@@ -101,6 +106,12 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
         tn = (blk % bpr) * bn + (t & (bn - 1));
         if (tm >= tiles_m || tn >= tiles_n) return;
     }
+    const bool second = tn >= tiles_n1;
+    const __bf16 *Bm = second ? B2 : B1;
+    OutT *Cm = second ? C2 : C1;
+    const int N = second ? N2 : N1;
+    const int64_t ldb = second ? ldb2 : ldb1, ldc = second ? ldc2 : ldc1;
+    if (second) tn -= tiles_n1;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t mrows = M - m0 < BM ? M - m0 : BM, nrows = N - n0 < BN ? N - n0 : BN;
     const int ntk = (K + GBK - 1) / GBK;
@@ -216,32 +227,39 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
 
 template <typename OutT, int BM, int BN, int ST>
 hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                        int64_t ldb, int64_t ldc, hipStream_t s)
+                        int64_t ldb, int64_t ldc, const __bf16 *B2, OutT *C2, int64_t N2, int64_t ldb2, int64_t ldc2,
+                        hipStream_t s)
 {
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n1 = (int)((N + BN - 1) / BN);
+    const int tiles_n = tiles_n1 + (int)((N2 + BN - 1) / BN);
     int bn_log = 0;
     while (bn_log < 3 && (2 << bn_log) <= tiles_n) ++bn_log;
     const int bn = 1 << bn_log, bm = 32 >> bn_log;
     const int64_t blocks = (int64_t)((tiles_m + bm - 1) / bm) * ((tiles_n + bn - 1) / bn);
     const int64_t grid = (blocks + 7) / 8 * 8 * 32;                 // 32 tiles a block, blocks a multiple of 8
     hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST>), dim3((unsigned)grid), dim3(256), 0, s, A, Bm, C, (int)M,
-                       (int)N, (int)K, lda, ldb, ldc, tiles_m, tiles_n, bn_log);
+                       (int)N, (int)K, lda, ldb, ldc, tiles_m, tiles_n, bn_log, B2 ? B2 : Bm, C2 ? C2 : C,
+                       (int)N2, ldb2, ldc2, tiles_n1);
     return hipGetLastError();
 }
 
-// C[M, N] = A[M, K] B[N, K]^T.  The tile is the largest that still gives every
-// compute unit a workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles
-// do little MFMA work per K step, so they keep 7 steps in flight (8 stages,
-// 64 KB of LDS) against the memory latency; the larger ones 3.
+// C[M, N] = A[M, K] B[N, K]^T, and optionally C2[M, N2] = A B2^T in the same
+// launch.  The tile is the largest that still gives every compute unit a
+// workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles do little MFMA
+// work per K step, so they keep 7 steps in flight (8 stages, 64 KB of LDS)
+// against the memory latency; the larger ones 3.
 template <typename OutT>
 hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                   int64_t ldb, int64_t ldc, hipStream_t s)
+                   int64_t ldb, int64_t ldc, hipStream_t s, const __bf16 *B2 = nullptr, OutT *C2 = nullptr,
+                   int64_t N2 = 0, int64_t ldb2 = 0, int64_t ldc2 = 0)
 {
-    if (M == 0 || N == 0) return hipSuccess;
-    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 256) return gemm_nt_tile<OutT, 256, 256, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
-    if (tiles(128, 128) >= 256) return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
-    return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, s);
+    if (M == 0 || N + N2 == 0) return hipSuccess;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn + (N2 + bn - 1) / bn); };
+    if (tiles(256, 256) >= 256)
+        return gemm_nt_tile<OutT, 256, 256, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
+    if (tiles(128, 128) >= 256)
+        return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
+    return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
@@ -610,6 +628,8 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
+    // (separate launches: at M = B*T the q|k|v tiles fill whole rounds of the
+    // compute units, and the a|b tiles added to that launch would start one more)
     if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, M, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
     if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv, s))) return e;
     if ((e = project<float>(x, (const __bf16 *)a.W_ab, ab, M, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
@@ -662,10 +682,13 @@ hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
-    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
+    // q|k|v and a|b in one launch (the same x, fp32 out): at M = N the launch is
+    // one round of small tiles, bound by its K steps, so a|b comes at no cost
+    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s,
+                            (const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H)))
+        return e;
     if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, N, H * Dv, hidden, hidden, hidden, H * Dv, s)))
         return e;
-    if ((e = project<float>(x, (const __bf16 *)a.W_ab, ab, N, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
 
     const __bf16 *cw = (const __bf16 *)a.conv_w;
     switch (Dk) {
