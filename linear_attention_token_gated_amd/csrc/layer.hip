@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
 // rows are then shifted by one, in place: each thread reads and writes only
 // its own 8 channels.  L2 norm and gates as in the prologue.
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK, int KC>
 __global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__restrict__ pre,
                                                               const __bf16 *__restrict__ conv_w,
                                                               const float *__restrict__ ab,
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__res
                                                               const float *__restrict__ b_alpha,
                                                               float *__restrict__ conv_state, float *__restrict__ post,
                                                               float *__restrict__ alpha, float *__restrict__ beta,
-                                                              int H, int nqkv, int conv_k)
+                                                              int H, int nqkv)
 {
     const int64_t n = blockIdx.x;
     const int nvec = nqkv / 8;
@@ -400,23 +400,23 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__res
         x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
         x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
     };
-    float rows[4][8];                        // taps 0 .. conv_k-1: history rows, then the current token
+    float rows[KC][8];                       // taps 0 .. KC-1: history rows, then the current token
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < conv_k - 1) {
-            ld8(conv_state + (n * (conv_k - 1) + j) * nqkv + c0, rows[j]);
-        } else if (j == conv_k - 1) {
-            ld8(pre + n * nqkv + c0, rows[j]);
-        }
+    for (int j = 0; j < KC - 1; ++j) ld8(conv_state + (n * (KC - 1) + j) * nqkv + c0, rows[j]);
+    ld8(pre + n * nqkv + c0, rows[KC - 1]);
+    // the thread's taps: 8 KC consecutive bf16 (channel-major), in 16-byte pieces
+    __bf16 w[8 * KC];
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(conv_w + (int64_t)c0 * KC + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[8 * q + e] = v[e];
     }
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < conv_k) {
+    for (int j = 0; j < KC; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf((float)conv_w[(int64_t)(c0 + e) * conv_k + j], rows[j][e], o[e]);
-        }
-    }
+        for (int e = 0; e < 8; ++e) o[e] = fmaf((float)w[e * KC + j], rows[j][e], o[e]);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
@@ -431,9 +431,9 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__res
         *reinterpret_cast<f32x4 *>(post + n * nqkv + c0 + 4) = o1;
         // history shifted by one token: row r <- tap r + 1
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            if (r < conv_k - 1) {
-                float *dst = conv_state + (n * (conv_k - 1) + r) * nqkv + c0;
+        for (int r = 0; r < KC - 1; ++r) {
+            {
+                float *dst = conv_state + (n * (KC - 1) + r) * nqkv + c0;
                 *reinterpret_cast<f32x4 *>(dst) = f32x4{rows[r + 1][0], rows[r + 1][1], rows[r + 1][2], rows[r + 1][3]};
                 *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{rows[r + 1][4], rows[r + 1][5], rows[r + 1][6], rows[r + 1][7]};
             }
@@ -553,8 +553,18 @@ hipError_t launch_decode_prologue_dk(const float *pre, const __bf16 *conv_w, con
                                      int64_t N, int H, int nqkv, int conv_k, hipStream_t s)
 {
     const unsigned slabs = (unsigned)((nqkv / 8 + 255) / 256);
-    hipLaunchKernelGGL((decode_prologue_kernel<DK>), dim3((unsigned)N, slabs), dim3(256), 0, s, pre, conv_w, ab, A,
-                       b_alpha, conv_state, post, alpha, beta, H, nqkv, conv_k);
+    const dim3 grid((unsigned)N, slabs);
+    switch (conv_k) {
+    case 1: hipLaunchKernelGGL((decode_prologue_kernel<DK, 1>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
+                               conv_state, post, alpha, beta, H, nqkv); break;
+    case 2: hipLaunchKernelGGL((decode_prologue_kernel<DK, 2>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
+                               conv_state, post, alpha, beta, H, nqkv); break;
+    case 3: hipLaunchKernelGGL((decode_prologue_kernel<DK, 3>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
+                               conv_state, post, alpha, beta, H, nqkv); break;
+    case 4: hipLaunchKernelGGL((decode_prologue_kernel<DK, 4>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
+                               conv_state, post, alpha, beta, H, nqkv); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
