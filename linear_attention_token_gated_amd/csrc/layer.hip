@@ -318,44 +318,60 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
             for (int e = 0; e < 8; ++e) win[l - 1][e] = 0.f;
         }
     }
-    float xn[8];
-    load8(t0, xn);
-    for (int64_t t = t0; t < tend; ++t) {
-        float x[8];
+    // tokens in groups of PG: the rows of the next group are in flight while
+    // the current group is computed (rows past the tile are not read)
+    constexpr int PG = 4;
+    static_assert(PRO_TT % PG == 0, "whole groups per tile");
+    float cur[PG][8], nxt[PG][8];
+    auto load_group = [&](int64_t tg, float (&g)[PG][8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = xn[e];
-        if (t + 1 < tend) load8(t + 1, xn);                // the next row is in flight meanwhile
-        // taps in the order j = 0 .. KC-1 (oldest input first)
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < PG; ++i)
+            if (tg + i < tend) load8(tg + i, g[i]);
+    };
+    load_group(t0, cur);
+    for (int64_t tg = t0; tg < tend; tg += PG) {
+        if (tg + PG < tend) load_group(tg + PG, nxt);
 #pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            const int lag = KC - 1 - j;
+        for (int i = 0; i < PG; ++i) {
+            const int64_t t = tg + i;
+            if (t >= tend) break;
+            const float (&x)[8] = cur[i];
+            // taps in the order j = 0 .. KC-1 (oldest input first)
+            float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(w[j][e], lag == 0 ? x[e] : win[lag > 0 ? lag - 1 : 0][e], o[e]);
+            for (int j = 0; j < KC; ++j) {
+                const int lag = KC - 1 - j;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = fmaf(w[j][e], lag == 0 ? x[e] : win[lag > 0 ? lag - 1 : 0][e], o[e]);
+            }
+#pragma unroll
+            for (int l = KC - 2; l >= 1; --l)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[l][e] = win[l - 1][e];
+            if constexpr (KC > 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[0][e] = x[e];
+            }
+            // L2 normalisation of q and k heads (heads never straddle the q|k / v
+            // boundary and vector groups are lane-aligned)
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
+#pragma unroll
+            for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
+            if (active) {
+                const float scale = scale_qk ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
+                f32x4 o0, o1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
+                *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0) = o0;
+                *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0 + 4) = o1;
+            }
         }
 #pragma unroll
-        for (int l = KC - 2; l >= 1; --l)
+        for (int i = 0; i < PG; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) win[l][e] = win[l - 1][e];
-        if constexpr (KC > 1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) win[0][e] = x[e];
-        }
-        // L2 normalisation of q and k heads (heads never straddle the q|k / v
-        // boundary and vector groups are lane-aligned)
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
-#pragma unroll
-        for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
-        if (active) {
-            const float scale = scale_qk ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
-            f32x4 o0, o1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
-            *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0) = o0;
-            *reinterpret_cast<f32x4 *>(post + (b * T + t) * nqkv + c0 + 4) = o1;
-        }
+            for (int e = 0; e < 8; ++e) cur[i][e] = nxt[i][e];
     }
     // eq (10) decay and eq (9) write strength for every head of the tile's tokens
     if (blockIdx.y == 0) {
