@@ -63,26 +63,30 @@ __device__ __forceinline__ void gload_lds(const void *base, uint32_t nrec, uint3
         (glds_ptr)(uintptr_t)(uint32_t)(uintptr_t)dst, 16, voff, 0, 0, 0);
 }
 
-template <int BM, int BN> struct GemmTile {
-    static constexpr int MI = BM / 32, NJ = BN / 32;          // 16 x 16 tiles per wave
+// NW wavefronts in a (NW / 2) x 2 grid over the BM x BN tile
+template <int BM, int BN, int NW> struct GemmTile {
+    static constexpr int WGM = NW / 2;
+    static constexpr int MI = BM / (16 * WGM), NJ = BN / 32;  // 16 x 16 tiles per wave
     static constexpr int ATILE = BM * GBK * 2, BTILE = BN * GBK * 2;
     static constexpr int STAGE = ATILE + BTILE;
-    static constexpr int LA = BM / 64, LB = BN / 64;          // 1 KB loads per thread per stage
+    static constexpr int LA = BM / (16 * NW), LB = BN / (16 * NW);   // 1 KB loads per thread per stage
     static constexpr int LOADS = LA + LB;
+    static_assert(LA >= 1 && LB >= 1, "every wave loads rows of both tiles");
 };
 
-// ST stages of K steps in LDS (a power of two >= 4), ST - 1 of them in flight
-// Two products of one A may share a launch: column tiles from tiles_n1 on
-// belong to the second (B2, C2, N2, ldb2, ldc2); a single product passes
-// tiles_n1 = tiles_n.
-template <typename OutT, int BM, int BN, int ST>
-__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ B1,
+// ST stages of K steps in LDS (a power of two >= 4), ST - 1 of them in flight;
+// NW wavefronts.  Two products of one A may share a launch: column tiles from
+// tiles_n1 on belong to the second (B2, C2, N2, ldb2, ldc2); a single product
+// passes tiles_n1 = tiles_n.
+template <typename OutT, int BM, int BN, int ST, int NW>
+__global__ __launch_bounds__(64 * NW, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ B1,
                                                          OutT *__restrict__ C1, int M, int N1, int K, int64_t lda,
                                                          int64_t ldb1, int64_t ldc1, int tiles_m, int tiles_n, int bn_log,
                                                          const __bf16 *__restrict__ B2, OutT *__restrict__ C2, int N2,
                                                          int64_t ldb2, int64_t ldc2, int tiles_n1)
 {
-    using G = GemmTile<BM, BN>;
+    using G = GemmTile<BM, BN, NW>;
+    constexpr int WGM = G::WGM;
     constexpr int MI = G::MI, NJ = G::NJ, LA = G::LA, LB = G::LB;
     static_assert(ST >= 4 && (ST & (ST - 1)) == 0 && (ST - 2) * G::LOADS < 64, "stages");
     __shared__ __attribute__((aligned(1024))) char smem[ST * G::STAGE];
@@ -122,9 +126,9 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
     const int gk = 8 * ((lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3));   // k offset of the lane's granule
     uint32_t roff_a[LA], roff_b[LB];
 #pragma unroll
-    for (int t = 0; t < LA; ++t) roff_a[t] = (uint32_t)((16 * (wave + 4 * t) + (lane >> 2)) * lda * 2 + gk * 2);
+    for (int t = 0; t < LA; ++t) roff_a[t] = (uint32_t)((16 * (wave + NW * t) + (lane >> 2)) * lda * 2 + gk * 2);
 #pragma unroll
-    for (int t = 0; t < LB; ++t) roff_b[t] = (uint32_t)((16 * (wave + 4 * t) + (lane >> 2)) * ldb * 2 + gk * 2);
+    for (int t = 0; t < LB; ++t) roff_b[t] = (uint32_t)((16 * (wave + NW * t) + (lane >> 2)) * ldb * 2 + gk * 2);
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * GBK;
         char *sa = smem + stage * G::STAGE, *sb = sa + G::ATILE;
@@ -133,9 +137,9 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
         // granules past K: an offset outside the range (a select, not a branch)
         const uint32_t oob = k0 + gk < K ? 0u : G_OOB;
 #pragma unroll
-        for (int t = 0; t < LA; ++t) gload_lds(ba, na, roff_a[t] | oob, sa + (wave + 4 * t) * 1024);
+        for (int t = 0; t < LA; ++t) gload_lds(ba, na, roff_a[t] | oob, sa + (wave + NW * t) * 1024);
 #pragma unroll
-        for (int t = 0; t < LB; ++t) gload_lds(bb, nb, roff_b[t] | oob, sb + (wave + 4 * t) * 1024);
+        for (int t = 0; t < LB; ++t) gload_lds(bb, nb, roff_b[t] | oob, sb + (wave + NW * t) * 1024);
     };
     // fragment of rows r0 + ln, k 8 lg .. 8 lg + 7 (r0 a multiple of 16)
     const int fpos = 8 * (lg ^ (((ln >> 1) ^ (ln >> 2)) & 3));
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
         const __bf16 *As = reinterpret_cast<const __bf16 *>(smem + stage * G::STAGE);
         const __bf16 *Bs = reinterpret_cast<const __bf16 *>(smem + stage * G::STAGE + G::ATILE);
 #pragma unroll
-        for (int i = 0; i < MI; ++i) af[i].load(As + (wm * (BM / 2) + 16 * i + ln) * GBK + fpos);
+        for (int i = 0; i < MI; ++i) af[i].load(As + (wm * (BM / WGM) + 16 * i + ln) * GBK + fpos);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bf[j].load(Bs + (wn * (BN / 2) + 16 * j + ln) * GBK + fpos);
     };
@@ -219,13 +223,13 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nt_kernel(const _
             const int64_t col = n0 + wn * (BN / 2) + 16 * j + ln;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + wm * (BM / 2) + 16 * i + 4 * lg + e;
+                const int64_t row = m0 + wm * (BM / WGM) + 16 * i + 4 * lg + e;
                 if (row < M && col < N) Cm[row * ldc + col] = from_f32<OutT>(acc[i][j][e]);
             }
         }
 }
 
-template <typename OutT, int BM, int BN, int ST>
+template <typename OutT, int BM, int BN, int ST, int NW = 4>
 hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, int64_t ldc, const __bf16 *B2, OutT *C2, int64_t N2, int64_t ldb2, int64_t ldc2,
                         hipStream_t s)
@@ -237,7 +241,7 @@ hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, i
     const int bn = 1 << bn_log, bm = 32 >> bn_log;
     const int64_t blocks = (int64_t)((tiles_m + bm - 1) / bm) * ((tiles_n + bn - 1) / bn);
     const int64_t grid = (blocks + 7) / 8 * 8 * 32;                 // 32 tiles a block, blocks a multiple of 8
-    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST>), dim3((unsigned)grid), dim3(256), 0, s, A, Bm, C, (int)M,
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, A, Bm, C, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, tiles_m, tiles_n, bn_log, B2 ? B2 : Bm, C2 ? C2 : C,
                        (int)N2, ldb2, ldc2, tiles_n1);
     return hipGetLastError();
@@ -256,7 +260,7 @@ hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_
     if (M == 0 || N + N2 == 0) return hipSuccess;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn + (N2 + bn - 1) / bn); };
     if (tiles(256, 256) >= 256)
-        return gemm_nt_tile<OutT, 256, 256, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
+        return gemm_nt_tile<OutT, 256, 256, 4, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
     if (tiles(128, 128) >= 256)
         return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
     return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
