@@ -198,11 +198,12 @@ __global__ __launch_bounds__(64 * NW, BM == 256 ? 1 : 2) void gemm_nt_kernel(con
         if (kt + 1 < ntk) read_frags((kt + 1) & (ST - 1), fa[cur ^ 1], fb[cur ^ 1]);
         mmas(fa[cur], fb[cur]);
         // interleave: the loads into LDS and the fragment reads between the MFMAs
-        static_for<L>([&](auto) {
+        // (with one wavefront per SIMD; with two the SIMD interleaves them)
+        if constexpr (NW == 4) static_for<L>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         });
-        static_for<MI + NJ>([&](auto) {
+        if constexpr (NW == 4) static_for<MI + NJ>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
             __builtin_amdgcn_sched_group_barrier(0x008, (MI * NJ - L) / (MI + NJ), 0);
         });
