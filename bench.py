@@ -18,6 +18,8 @@ library launches on, around every timed step; a 512 MiB buffer is written
 before each timed step (outside the events) so that no step finds its inputs
 in the 256 MB Infinity Cache; the reported time is the median over the timed
 steps.  The region of all timed steps is bracketed by device synchronisations.
+`ms_back_to_back` is a second region of as many steps run back to back with
+no flush in between (inputs may then sit in the Infinity Cache).
 """
 from __future__ import annotations
 
@@ -180,8 +182,9 @@ def time_steps(fns, steps, warmup, torch, flush=None):
     (the stream the library launches on).  `warmup` untimed steps, then
     `steps` timed ones, each preceded by `flush` (outside the timed events) and
     bracketed by HIP events, with an event between consecutive functions.
-    The whole region is bracketed by device synchronisations.  Returns
-    (per-step ms list, per-function ms lists, ms of the whole region)."""
+    Then `steps` more steps back to back, without the flush, between two
+    events.  Each region is bracketed by device synchronisations.  Returns
+    (per-step ms list, per-function ms lists, ms of the back-to-back region)."""
     if callable(fns):
         fns = [fns]
     for _ in range(warmup):
@@ -192,7 +195,6 @@ def time_steps(fns, steps, warmup, torch, flush=None):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record(stream)
     for ev in evs:
         if flush is not None:
             flush()
@@ -200,6 +202,11 @@ def time_steps(fns, steps, warmup, torch, flush=None):
         for i, fn in enumerate(fns):
             fn()
             ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        for fn in fns:
+            fn()
     t1.record(stream)
     torch.cuda.synchronize()
     per_step = [ev[0].elapsed_time(ev[-1]) for ev in evs]
