@@ -5,7 +5,8 @@
 
 A step is one gdn_prefill_fwd on the 32K-token workload (B=1, T=32768, H=32,
 d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, state and y) with every input
-already resident in HBM.  The JSON line carries that step's roofline (its
+and its record workspace already resident in HBM; the single-kernel form
+(no workspace) is timed the same way as `prefill_32k_fused`.  The JSON line carries that step's roofline (its
 algorithmic flops and bytes over the median step time, against the bf16 MFMA
 and HBM peaks), the 4K-context prefill (B=2, T=4096, H=16) measured the same
 way, the decode step (256 sequences x 32 heads, fp32 128x128 states updated in
@@ -135,8 +136,12 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill_fused.hip",
+PREFILL_SOURCES = ["linear_attention_token_gated_amd/csrc/recurrence.hip",
+                   "linear_attention_token_gated_amd/csrc/chunk_prep.hip",
+                   "linear_attention_token_gated_amd/csrc/prep_layout.hpp",
                    "linear_attention_token_gated_amd/csrc/common.hpp"]
+FUSED_SOURCES = ["linear_attention_token_gated_amd/csrc/prefill_fused.hip",
+                 "linear_attention_token_gated_amd/csrc/common.hpp"]
 
 
 DECODE_SOURCES = ["linear_attention_token_gated_amd/csrc/decode.hip"]
@@ -145,7 +150,8 @@ DECODE_SOURCES = ["linear_attention_token_gated_amd/csrc/decode.hip"]
 # counter keys: the kernels whose FETCH_SIZE + WRITE_SIZE add up to one launch
 # of the workload, and the sources whose hash the stored counts were taken on
 TRAFFIC_KERNELS = {
-    "prefill_32k": (["gdn_prefill_fused_kernel"], PREFILL_SOURCES),
+    "prefill_32k": (["gdn_chunk_prep_kernel", "gdn_recurrence_kernel"], PREFILL_SOURCES),
+    "prefill_32k_fused": (["gdn_prefill_fused_kernel"], FUSED_SOURCES),
     "decode_256x32": (["gdn_decode_kernel"], DECODE_SOURCES),
 }
 
@@ -226,15 +232,18 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def prefill_setup(cfg, torch, gdn, wl):
+def prefill_setup(cfg, torch, gdn, wl, fused=False):
+    """The prefill of a workload: with the record workspace (per-chunk
+    preparation, then the recurrence), or with fused=True the single-kernel
+    form that takes none."""
     inp = wl.prefill_config_inputs(cfg)
     t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "alpha", "beta", "S0")}
     y = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     sT = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, gdn.prefill_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk,
-                                                        cfg.dtype)), dtype=torch.uint8, device="cuda")
+    ws = None if fused else torch.empty(max(1, gdn.prefill_workspace_bytes(
+        cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, cfg.chunk, cfg.dtype)), dtype=torch.uint8, device="cuda")
     fn = lambda: gdn.prefill(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["S0"], chunk=cfg.chunk, y=y,
-                             final_state=sT, workspace=ws)
+                             final_state=sT, workspace=ws, fused=fused)
     return inp, fn
 
 
@@ -487,8 +496,11 @@ def main():
     if args.pmc_run:
         pargs = argparse.Namespace(steps=1, warmup=1)
         for cfg in (wl.PREFILL_32K, wl.PREFILL_4K):
-            _, fn = prefill_setup(cfg, torch, gdn, wl)
-            fn(); fn()
+            for fused in (False, True):
+                _, fn = prefill_setup(cfg, torch, gdn, wl, fused)
+                fn(); fn()
+                del fn
+                torch.cuda.synchronize()
         bench_decode(pargs, torch, gdn, wl, None)
         bench_layer(pargs, torch, gdn, wl, None, BF16_PEAK_TFLOPS)
         bench_layer_decode(pargs, torch, gdn, wl, None)
@@ -511,7 +523,16 @@ def main():
     _, fn4 = prefill_setup(wl.PREFILL_4K, torch, gdn, wl)
     per4, _, region4 = time_steps(fn4, args.steps, args.warmup, torch, flush)
     p4k = prefill_report(wl.PREFILL_4K, per4, region4, args.steps, BF16_PEAK_TFLOPS)
+    del fn4
+    _, fnf = prefill_setup(cfg, torch, gdn, wl, fused=True)
+    perf, _, regionf = time_steps(fnf, args.steps, args.warmup, torch, flush)
+    pfused = prefill_report(cfg, perf, regionf, args.steps, BF16_PEAK_TFLOPS)
+    pfused["form"] = "one fused kernel, no workspace (q, k, v read once)"
+    pfused["traffic"] = measured_traffic("prefill_32k_fused")
+    del fnf
+    print(f"prefill 32K fused: {pfused['ms_per_step']} ms", file=sys.stderr, flush=True)
     traffic = measured_traffic("prefill_32k")
+    head["form"] = "per-chunk records (preparation kernel), then the recurrence"
     ms_step = head["ms_per_step"]
 
     extra = {}
@@ -555,6 +576,7 @@ def main():
                              "frac": head["hbm_frac"], "frac_with_fp32_y": head["hbm_frac_fp32_y"]}},
         "prefill_32k": head,
         "prefill_4k": p4k,
+        "prefill_32k_fused": pfused,
         **extra,
         "cpu_baseline": cpu,
         "device": dev,

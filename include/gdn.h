@@ -75,16 +75,22 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   B, H, T >= 0; B*H == 0 or T == 0 launch nothing except, for T == 0,
  *   final_state = initial_state (or zeros).  Any T is accepted: a ragged last
  *   chunk is padded with identity tokens (alpha = 1, beta = 0, k = q = v = 0).
- *   workspace     GDN_BF16: none (NULL, 0): one kernel forms every chunk
- *                 quantity on chip.  GDN_F32: device scratch of at least
- *                 gdn_prefill_workspace_bytes(...) bytes, 256-byte aligned,
- *                 owned by the caller and not overlapping any other argument:
- *                 one record per (sequence, head, chunk) of the quantities that
- *                 do not depend on the state ((I + A)^-1, P, the masked K K^T,
- *                 the decay prefix and 2^(G_C - G); 49664 bytes at C = 64),
- *                 computed by a separate kernel before the recurrence.
- *                 Missing or too small: GDN_ERR_WORKSPACE.  Its contents are
- *                 overwritten; nothing in it is kept between calls.
+ *   workspace     device scratch of at least gdn_prefill_workspace_bytes(...)
+ *                 bytes, 256-byte aligned, owned by the caller and not
+ *                 overlapping any other argument: one record per (sequence,
+ *                 head, chunk) of the quantities that do not depend on the
+ *                 state, computed for every chunk in parallel by a separate
+ *                 kernel before the recurrence.  GDN_BF16: decay factors,
+ *                 (I + A)^-1 diag(beta) and the masked Q K^T block as bf16
+ *                 hi/lo MFMA fragments (21056 bytes at C = 64); optional:
+ *                 NULL selects one kernel that forms every chunk quantity on
+ *                 chip and reads q, k, v from memory once (no scratch, less
+ *                 memory traffic, longer per-chunk period).  GDN_F32:
+ *                 required; (I + A)^-1, P, the masked K K^T, the decay prefix
+ *                 and 2^(G_C - G) (49664 bytes at C = 64).  Given but too
+ *                 small, or missing where required: GDN_ERR_WORKSPACE.  Its
+ *                 contents are overwritten; nothing in it is kept between
+ *                 calls.
  * y must not overlap q, k, v, alpha, beta, initial_state or final_state.
  */
 GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
@@ -96,8 +102,8 @@ GDN_API gdn_status gdn_prefill_fwd(const void *q, const void *k, const void *v,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Bytes of workspace gdn_prefill_fwd needs for these sizes: B*H*ceil(T/C)
- * records for GDN_F32; 0 for GDN_BF16, for empty problems and for arguments
+/* Bytes of workspace gdn_prefill_fwd takes for these sizes: B*H*ceil(T/C)
+ * records of the dtype's layout; 0 for empty problems and for arguments
  * gdn_prefill_fwd would reject. */
 GDN_API size_t gdn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                    int64_t Dv, int64_t chunk, gdn_dtype dtype);

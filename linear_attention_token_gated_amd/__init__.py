@@ -151,11 +151,12 @@ def prefill_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype="bf16") -> int:
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_final_state: bool = True,
-            y=None, final_state=None, workspace=None):
+            y=None, final_state=None, workspace=None, fused: bool = False):
     """Chunked prefill.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (float32 or bfloat16);
     alpha, beta: [B,T,H] float32; initial_state: [B,H,Dk,Dv] float32 or None.
     workspace: a device buffer of prefill_workspace_bytes(...) bytes, or None
-    to allocate one for this call.
+    to allocate one for this call.  fused (bfloat16 only): pass no workspace,
+    which selects the library's single-kernel form.
     Returns (y [B,T,H,Dv] float32, final_state or None)."""
     import torch
     B, T, H, Dk = q.shape
@@ -174,7 +175,12 @@ def prefill(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, return_fi
               (beta, "beta", (B, T, H)), (initial_state, "initial_state", (B, H, Dk, Dv)),
               (y, "y", (B, T, H, Dv)), (final_state, "final_state", (B, H, Dk, Dv))])
     _same_device(q, workspace, "workspace")
-    need = int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _dtype_code(q)))
+    if fused:
+        if q.dtype != torch.bfloat16 or workspace is not None:
+            raise ValueError("prefill: fused=True takes bfloat16 inputs and no workspace")
+        need = 0
+    else:
+        need = int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _dtype_code(q)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

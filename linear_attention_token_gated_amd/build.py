@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_fused.hip", "layer.hip", "backward.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_fused.hip", "chunk_prep.hip", "recurrence.hip",
+           "layer.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

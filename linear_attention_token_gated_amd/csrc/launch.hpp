@@ -29,7 +29,10 @@ struct PrefillArgs {
     int64_t B, T, H, Dk, Dv, chunk;
     int64_t q_tok_stride, k_tok_stride, v_tok_stride;   // elements per token (all heads)
     bool bf16;
-    void *ws;                       // fp32: prefill_f32_workspace_bytes(...) bytes, 256-byte aligned
+    // fp32: prefill_f32_workspace_bytes(...) bytes, 256-byte aligned; bf16:
+    // prefill_bf16_workspace_bytes(...) bytes for the two-kernel form, or null
+    // for the single fused kernel
+    void *ws;
     // fp32 inputs: the caller's bound is the bf16 one (the layer's core), so the
     // recurrence may run on bf16 MFMA with hi/lo operands (about 16 bits of each
     // operand) instead of fp32 MFMA
@@ -53,6 +56,13 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 // bf16 prefill in one kernel (prefill_fused.hip): chunk quantities formed on chip
 hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t stream);
+
+// bf16 prefill in two kernels: the state-independent chunk quantities of every
+// (b, h, chunk) into per-chunk records (chunk_prep.hip, prep_layout.hpp), then
+// the recurrence over 16-column slices reading them (recurrence.hip)
+size_t prefill_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t chunk);
+hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_recurrence(const PrefillArgs &a, hipStream_t stream);
 
 // Gradients of the prefill (backward.hip): dL/dq, dk, dv, dalpha, dbeta, dS_0
 // from dL/dy and dL/dS_T

@@ -11,8 +11,11 @@
 //   Y = diag(2^G) Q S + P U,  P = lower_incl[ Gamma_rj (q_r . k_j) ]   (eq (4))
 //   S' = 2^{G_C} S + K^T diag(2^{G_C - G}) U                          (eqs (1),(3))
 //
-// bf16 inputs: one kernel (prefill_fused.hip) that forms every chunk quantity
-// on chip.  fp32 inputs (and the layer's core): the per-chunk preparation of
+// bf16 inputs with a workspace: the chunk quantities of every (b, h, chunk) in
+// parallel into per-chunk records (chunk_prep.hip), then the recurrence
+// reading them (recurrence.hip).  bf16 inputs without one: a single kernel
+// (prefill_fused.hip) that forms every chunk quantity on chip and reads q, k,
+// v once.  fp32 inputs (and the layer's core): the per-chunk preparation of
 // backward.hip into a caller-provided record workspace, then the recurrence.
 // Ragged tails are padded with identity tokens (alpha = 1, beta = 0,
 // k = q = v = 0).
@@ -41,7 +44,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
         hipLaunchKernelGGL(copy_or_zero_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.s0, a.sT, n);
         return hipGetLastError();
     }
-    if (a.bf16) return launch_prefill_fused(a, stream);
+    if (a.bf16) {
+        if (!a.ws) return launch_prefill_fused(a, stream);
+        const hipError_t e = launch_chunk_prep(a, stream);
+        return e != hipSuccess ? e : launch_recurrence(a, stream);
+    }
     if (!a.ws) return hipErrorInvalidValue;   // the C ABI checks the workspace first
     return launch_prefill_f32_staged(a, stream);
 }

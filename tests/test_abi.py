@@ -73,11 +73,17 @@ def test_prefill_validation(L):
 
 
 def test_prefill_workspace_validation(L):
-    # bf16 needs no workspace; fp32 needs one record per (sequence, head, chunk).
-    # Every failing case below fails on the host before anything is launched.
-    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1) == 0
-    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 0)
+    # one record per (sequence, head, chunk): optional for bf16 (none selects
+    # the fused kernel), required for fp32.  Every failing case below fails on
+    # the host before anything is launched.
+    need16 = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1)
+    assert need16 == 2 * 4 * 2240
     W = A + 400 * MB
+    assert prefill(L, dt=1, w=W, wb=need16 - 1) == WS            # given but too small
+    assert prefill(L, dt=1, w=W + 16, wb=need16) == ALIGN        # not 256-byte aligned
+    assert prefill(L, dt=1, w=A + 256 * MB, wb=need16) == ALIAS  # workspace == y
+    assert prefill(L, dt=1, w=A + 64 * MB, wb=need16) == ALIAS   # workspace == k
+    need = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 0)
     assert prefill(L, dt=0) == WS                                # missing
     assert prefill(L, dt=0, w=W, wb=need - 1) == WS              # too small
     assert prefill(L, dt=0, w=W + 16, wb=need) == ALIGN          # not 256-byte aligned
@@ -182,8 +188,11 @@ def test_layer_decode_validation(L):
 
 
 def test_workspace_queries(L):
-    # bf16 prefill: no workspace (every chunk quantity is formed on chip)
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 0
+    # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
+    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
+    assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
+    assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
     # fp32: records of the two-kernel path, 3*64*64 + 2*64 floats per 64-token chunk
     assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 0) == 4 * 32 * 512 * 12416
     assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 0) == 4 * 2 * 3 * 4 * 3136

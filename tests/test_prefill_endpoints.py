@@ -13,8 +13,9 @@ from linear_attention_token_gated_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 CASES = ["beta1_qk", "ortho", "beta_near1", "alpha1", "alpha0"]
-# the bf16 headline shape (C = 64, d = 128) and two fp32 instances
-PATHS = [("bf16", 64, 128, 128), ("f32", 64, 128, 128), ("f32", 16, 32, 16)]
+# the bf16 headline shape (C = 64, d = 128) in both bf16 forms (records +
+# recurrence, one fused kernel) and two fp32 instances
+PATHS = [("bf16", 64, 128, 128), ("bf16-fused", 64, 128, 128), ("f32", 64, 128, 128), ("f32", 16, 32, 16)]
 
 
 @pytest.mark.parametrize("dtype,chunk,Dk,Dv", PATHS)
@@ -25,9 +26,11 @@ def test_prefill_gate_endpoints(oracle_mod, case, dtype, chunk, Dk, Dv):
     T = min(Dk, 100) if case == "ortho" else 2 * chunk + 37
     B, H = 2, 2
     print(f"case: endpoints {case} B={B} T={T} H={H} Dk={Dk} Dv={Dv} C={chunk} {dtype}", flush=True)
+    fused = dtype == "bf16-fused"
+    dtype = "bf16" if fused else dtype
     inp = gate_endpoint_inputs(case, B, T, H, Dk, Dv, dtype, seed=100 + Dk + chunk)
     y, sT = gdn.prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["alpha"]), dev(inp["beta"]),
-                        dev(inp["S0"]), chunk=chunk)
+                        dev(inp["S0"]), chunk=chunk, fused=fused)
     torch.cuda.synchronize()
     y_ref, S_ref = oracle_prefill(oracle_mod, inp)
     ey, eS = rel_err(host(y), y_ref), rel_err(host(sT), S_ref)

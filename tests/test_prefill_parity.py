@@ -19,8 +19,8 @@ def _gpu(inp, chunk, S0=None, **kw):
     return y, sT
 
 
-def _check(oracle, inp, chunk, tol):
-    y, sT = _gpu(inp, chunk)
+def _check(oracle, inp, chunk, tol, **kw):
+    y, sT = _gpu(inp, chunk, **kw)
     y_ref, S_ref = oracle_prefill(oracle, inp)
     ey, eS = rel_err(host(y), y_ref), rel_err(host(sT), S_ref)
     print(f"  err y={ey:.3e} S={eS:.3e}", flush=True)
@@ -33,27 +33,34 @@ def test_prefill_tiny_f32(oracle_mod):
     _check(oracle_mod, wl.prefill_config_inputs(cfg), cfg.chunk, TOL_F32)
 
 
-def test_prefill_4k_bf16(oracle_mod):
+# the two bf16 forms: records + recurrence (a workspace), one fused kernel (none)
+FORMS = [pytest.param(False, id="records"), pytest.param(True, id="fused")]
+
+
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_4k_bf16(oracle_mod, fused):
     cfg = wl.PREFILL_4K
-    print(f"case: {cfg.name}", flush=True)
-    _check(oracle_mod, wl.prefill_config_inputs(cfg), cfg.chunk, TOL_BF16)
+    print(f"case: {cfg.name} fused={fused}", flush=True)
+    _check(oracle_mod, wl.prefill_config_inputs(cfg), cfg.chunk, TOL_BF16, fused=fused)
 
 
 @pytest.mark.slow
-def test_prefill_32k_bf16(oracle_mod):
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_32k_bf16(oracle_mod, fused):
     cfg = wl.PREFILL_32K
-    print(f"case: {cfg.name}", flush=True)
-    _check(oracle_mod, wl.prefill_config_inputs(cfg), cfg.chunk, TOL_BF16)
+    print(f"case: {cfg.name} fused={fused}", flush=True)
+    _check(oracle_mod, wl.prefill_config_inputs(cfg), cfg.chunk, TOL_BF16, fused=fused)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "bf16-fused"])
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("Dk,Dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
 def test_prefill_shapes_chunks_ragged(oracle_mod, dtype, chunk, Dk, Dv):
     T = 3 * chunk + 5            # several chunks and a ragged tail
     print(f"case: prefill B=2 T={T} H=3 Dk={Dk} Dv={Dv} C={chunk} {dtype}", flush=True)
-    inp = wl.prefill_inputs(2, T, 3, Dk, Dv, dtype=dtype, s0_std=0.3, seed=Dk + 3 * Dv + chunk)
-    _check(oracle_mod, inp, chunk, TOL_F32 if dtype == "f32" else TOL_BF16)
+    inp = wl.prefill_inputs(2, T, 3, Dk, Dv, dtype=dtype[:4].rstrip("-"), s0_std=0.3, seed=Dk + 3 * Dv + chunk)
+    kw = {"fused": True} if dtype == "bf16-fused" else {}
+    _check(oracle_mod, inp, chunk, TOL_F32 if dtype == "f32" else TOL_BF16, **kw)
 
 
 @pytest.mark.parametrize("T", [1, 2, 15, 17, 63, 64, 65])
@@ -63,30 +70,32 @@ def test_prefill_short_sequences(oracle_mod, T):
     _check(oracle_mod, inp, 64, TOL_F32)
 
 
-def test_prefill_chunk_size_invariance(oracle_mod):
-    print("case: chunk invariance C=16/32/64", flush=True)
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_chunk_size_invariance(oracle_mod, fused):
+    print(f"case: chunk invariance C=16/32/64 fused={fused}", flush=True)
     inp = wl.prefill_inputs(1, 200, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=11)
     y_ref, S_ref = oracle_prefill(oracle_mod, inp)
     ys = []
     for C in (16, 32, 64):
-        y, sT = _gpu(inp, C)
+        y, sT = _gpu(inp, C, fused=fused)
         assert rel_err(host(y), y_ref) <= TOL_BF16 and rel_err(host(sT), S_ref) <= TOL_BF16
         ys.append(host(y))
     assert rel_err(ys[0], ys[2]) <= TOL_BF16
 
 
-def test_prefill_split_resume(oracle_mod):
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_split_resume(oracle_mod, fused):
     """prefill(0:T1) -> S; prefill(T1:T, S) == prefill(0:T) (state hand-off)."""
     import torch
     import linear_attention_token_gated_amd as gdn
-    print("case: split/resume", flush=True)
+    print(f"case: split/resume fused={fused}", flush=True)
     inp = wl.prefill_inputs(2, 300, 2, 64, 64, dtype="bf16", s0_std=0.02, seed=12)
-    y_full, S_full = _gpu(inp, 64)
+    y_full, S_full = _gpu(inp, 64, fused=fused)
     T1 = 131
     part = {n: (inp[n][:, :T1] if inp[n] is not None and n != "S0" and n != "dtype" else inp[n]) for n in inp}
     rest = {n: (inp[n][:, T1:] if inp[n] is not None and n != "S0" and n != "dtype" else inp[n]) for n in inp}
-    y1, S1 = _gpu(part, 64)
-    y2, S2 = _gpu(rest, 64, S0=S1)
+    y1, S1 = _gpu(part, 64, fused=fused)
+    y2, S2 = _gpu(rest, 64, S0=S1, fused=fused)
     # chunk boundaries move, so rounding differs: both runs meet the oracle bound
     y_ref, S_ref = oracle_prefill(oracle_mod, inp)
     assert rel_err(host(torch.cat([y1, y2], 1)), y_ref) <= TOL_BF16
@@ -141,36 +150,39 @@ def test_prefill_identity_tokens_and_pure_decay(oracle_mod):
     _check(oracle_mod, inp2, 32, TOL_F32)
 
 
-def test_prefill_column_slices_independent(oracle_mod):
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_column_slices_independent(oracle_mod, fused):
     """Column separability: the first 32 value columns computed alone equal the
     same columns of the full-width run (same kernel, different slice count)."""
-    print("case: column slices", flush=True)
+    print(f"case: column slices fused={fused}", flush=True)
     inp = wl.prefill_inputs(1, 150, 2, 64, 128, dtype="bf16", s0_std=0.02, seed=16)
-    y, sT = _gpu(inp, 64)
+    y, sT = _gpu(inp, 64, fused=fused)
     sub = dict(inp)
     sub["v"] = np.ascontiguousarray(inp["v"][..., :32])
     sub["S0"] = np.ascontiguousarray(inp["S0"][..., :32])
-    y2, s2 = _gpu(sub, 64)
+    y2, s2 = _gpu(sub, 64, fused=fused)
     np.testing.assert_array_equal(host(y2), host(y)[..., :32])
     np.testing.assert_array_equal(host(s2), host(sT)[..., :32])
 
 
-def test_prefill_deterministic(oracle_mod):
-    print("case: determinism", flush=True)
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_deterministic(oracle_mod, fused):
+    print(f"case: determinism fused={fused}", flush=True)
     inp = wl.prefill_inputs(2, 500, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=17)
-    y1, s1 = _gpu(inp, 64)
-    y2, s2 = _gpu(inp, 64)
+    y1, s1 = _gpu(inp, 64, fused=fused)
+    y2, s2 = _gpu(inp, 64, fused=fused)
     np.testing.assert_array_equal(host(y1), host(y2))
     np.testing.assert_array_equal(host(s1), host(s2))
 
 
-def test_prefill_strong_decay_no_nan(oracle_mod):
+@pytest.mark.parametrize("fused", FORMS)
+def test_prefill_strong_decay_no_nan(oracle_mod, fused):
     """alpha down to 1e-3 per token (log-decay prefix far below fp32 range over a chunk)."""
-    print("case: strong decay", flush=True)
+    print(f"case: strong decay fused={fused}", flush=True)
     inp = wl.prefill_inputs(1, 256, 2, 128, 128, dtype="bf16", s0_std=0.02, seed=18)
     rng = np.random.default_rng(0)
     inp["alpha"] = rng.uniform(1e-3, 0.2, inp["alpha"].shape).astype(np.float32)
-    _check(oracle_mod, inp, 64, TOL_BF16)
+    _check(oracle_mod, inp, 64, TOL_BF16, fused=fused)
 
 
 def test_sync_check_mode(oracle_mod, monkeypatch):
