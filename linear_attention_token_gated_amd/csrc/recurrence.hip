@@ -191,7 +191,10 @@ __device__ __forceinline__ Frag<__bf16, 32> pair16(bf16x4 a, bf16x4 b) {
 }
 
 // sum over the blocks k < NK2 of A_k B_k (hi/lo pairs, three products each),
-// two blocks per 32-deep MFMA and a 16-deep one for an odd last block
+// two blocks per 32-deep MFMA and a 16-deep one for an odd last block.  The
+// 16-deep products of an odd last block after pairs accumulate apart and are
+// added at the end: a 32-deep result is never the accumulator input of a
+// 16-deep MFMA.
 template <int NK2>
 __device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al, const bf16x4 *bh, const bf16x4 *bl,
                                               f32x4 &acc, f32x4 &acc2) {
@@ -208,9 +211,16 @@ __device__ __forceinline__ void pair_products(const bf16x4 *ah, const bf16x4 *al
     if constexpr (NK2 % 2) {
         F16 a, a2, b, b2;
         a.v = ah[NK2 - 1]; a2.v = al[NK2 - 1]; b.v = bh[NK2 - 1]; b2.v = bl[NK2 - 1];
-        acc = F16::mma(a, b, acc);
-        acc2 = F16::mma(a, b2, acc2);
-        acc2 = F16::mma(a2, b, acc2);
+        if constexpr (NK2 == 1) {
+            acc = F16::mma(a, b, acc);
+            acc2 = F16::mma(a, b2, acc2);
+            acc2 = F16::mma(a2, b, acc2);
+        } else {
+            f32x4 o = F16::mma(a, b, zero4()), o2 = F16::mma(a, b2, zero4());
+            o2 = F16::mma(a2, b, o2);
+            acc += o;
+            acc2 += o2;
+        }
     }
 }
 
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         };
         write_state_operand();
 
-        __syncthreads();                        // chunk 0 staged, S^T written
+        lds_barrier();                        // chunk 0 staged, S^T written
 
         auto iter = [&](auto set_c, int64_t c, int cbi) {
             constexpr int s_ = decltype(set_c)::value;
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 Rl[rb * 64 + lane] = lv;
                 reinterpret_cast<f32x4 *>(smem + L::oEq)[rb * 64 + lane] = eg * (qs_h + qs_l);
             }
-            __syncthreads();
+            lds_barrier();
 
             // ---- phase 2: U_rb = sum_{k <= rb} T'_rb,k R_k.  The K^T operands of
             // the phase-3 update are read first: K of the chunk is unchanged
@@ -390,7 +400,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 *reinterpret_cast<bf16x4 *>(UdTh + pd) = dh;
                 *reinterpret_cast<bf16x4 *>(UdTl + pd) = dl;
             }
-            __syncthreads();
+            lds_barrier();
 
             // ---- phase 3: S <- EGC S + K^T (diag(Ed) U)
             {
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 }
                 write_state_operand();
             }
-            __syncthreads();
+            lds_barrier();
         };
         int64_t c = 0;
         int cbi = 0;
@@ -473,13 +483,13 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
             }
         };
         load_p(0);
-        __syncthreads();
+        lds_barrier();
 
         for (int64_t c = 0; c < NC; ++c) {
             // ---- phase 1: rows of chunk c - 1
             if (c > 0) store_y(c - 1);
-            __syncthreads();
-            __syncthreads();
+            lds_barrier();
+            lds_barrier();
             // ---- phase 3: Y = diag(EG) Q S + P U; then the next chunk's P (the
             // last chunk's again at the end: no branch)
             if constexpr (has_rb) {
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 asm volatile("" : "+v"(yv));
             }
             load_p(clampc(c + 1));
-            __syncthreads();
+            lds_barrier();
         }
         if (NC > 0) store_y(NC - 1);
     };
