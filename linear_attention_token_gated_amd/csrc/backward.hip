@@ -38,6 +38,7 @@
 // Ragged tails are padded with identity tokens (alpha = 1, beta = 0, zeros),
 // whose gradients are never written.
 #include "common.hpp"
+#include "gemm_nt.hpp"
 #include "launch.hpp"
 
 namespace gdn {
@@ -1982,8 +1983,10 @@ template <int C, int DK> struct Fwd16Lay {
 // they are spread over the two windows after step 1)
 constexpr int NTF = 512;
 
+// One workgroup of the recurrence: slice bid of the grid, LDS of
+// Fwd16Lay<C, DK>::BYTES at smem.
 template <int C, int DK>
-__global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
+__device__ __forceinline__ void fwd16_carry_block(const BwdParams &p, int64_t bid, char *smem)
 {
     using L = Fwd16Lay<C, DK>;
     constexpr int KP = L::KP, CP = L::CP, NB = C / 16, NKB = DK / 16, MS = (NKB + 3) / 4, NJ = C / 32;
@@ -1996,7 +1999,6 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
     constexpr int NUV = C * BV / 4;                                // of the V slice
     static_assert(NUV <= NST && C <= NST, "one V unit and one gate per staging thread");
 
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __bf16 *Kh = reinterpret_cast<__bf16 *>(smem + L::oKh), *Kl = reinterpret_cast<__bf16 *>(smem + L::oKl);
     __bf16 *Qh = reinterpret_cast<__bf16 *>(smem + L::oQh), *Ql = reinterpret_cast<__bf16 *>(smem + L::oQl);
     __bf16 *Th = reinterpret_cast<__bf16 *>(smem + L::oTh), *Tl = reinterpret_cast<__bf16 *>(smem + L::oTl);
@@ -2014,7 +2016,7 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
     const bool chain = wave < 4;
     const int64_t NS = p.Dv / BV;
     int64_t bh, sl;
-    slice_of(blockIdx.x, NS, p.xcd_map, bh, sl);
+    slice_of(bid, NS, p.xcd_map, bh, sl);
     const int64_t H = p.H, T = p.T, Dv = p.Dv, NC = p.NC, b = bh / H, h = bh % H;
     const int n0 = (int)sl * BV;
 
@@ -2304,6 +2306,47 @@ __global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
     }
 }
 
+template <int C, int DK>
+__global__ __launch_bounds__(NTF) void fwd16_carry_kernel(BwdParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[Fwd16Lay<C, DK>::BYTES];
+    fwd16_carry_block<C, DK>(p, blockIdx.x, smem);
+}
+
+// The recurrence and an independent bf16 product in one launch: workgroups
+// below nslice are the recurrence's slices (placed as in fwd16_carry_kernel),
+// those from ncore (nslice rounded up to a multiple of 8; the ones between end
+// at once) the product's 256 x 256 tiles, which the hardware then places on
+// the compute units the slices leave free.  Every output of the product sums its K in the
+// same order as in a launch of its own, so it is the same bits.
+constexpr int SIDE_BM = 256, SIDE_BN = 256, SIDE_ST = 4, SIDE_NW = 8;
+static_assert(SIDE_NW * 64 == NTF, "one block size for both roles");
+
+struct SideArgs {
+    const __bf16 *A, *B;
+    __bf16 *C;
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+    int tiles_m, tiles_n, bn_log;
+    int64_t nslice, ncore;
+};
+
+template <int C, int DK>
+__global__ __launch_bounds__(NTF, 1) void fwd16_carry_side_kernel(BwdParams p, SideArgs g)
+{
+    constexpr size_t GB = (size_t)SIDE_ST * GemmTile<SIDE_BM, SIDE_BN, SIDE_NW>::STAGE;
+    constexpr size_t FB = Fwd16Lay<C, DK>::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[FB > GB ? FB : GB];
+    const int64_t bid = blockIdx.x;
+    if (bid < g.nslice) {
+        fwd16_carry_block<C, DK>(p, bid, smem);
+    } else if (bid >= g.ncore) {
+        gemm_nt_block<__bf16, SIDE_BM, SIDE_BN, SIDE_ST, SIDE_NW>(
+            (int)(bid - g.ncore), smem, g.A, g.B, g.C, g.M, g.N, g.K, g.lda, g.ldb, g.ldc, g.tiles_m, g.tiles_n,
+            g.bn_log, g.B, g.C, 0, g.ldb, g.ldc, g.tiles_n);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
@@ -2390,7 +2433,23 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
         // (its staging addresses a chunk's q and k rows by 32-bit byte offsets)
         const int64_t wide = a.q_tok_stride > a.k_tok_stride ? a.q_tok_stride : a.k_tok_stride;
         if (a.hilo_core && (int64_t)C * wide * 4 < ((int64_t)1 << 32)) {
-            hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
+            if (!a.side) {
+                hipLaunchKernelGGL((fwd16_carry_kernel<C, DK>), dim3(nslice), dim3(NTF), 0, stream, kp);
+                return hipGetLastError();
+            }
+            const PrefillArgs::SideGemm &sg = *a.side;
+            const GemmGrid<SIDE_BM, SIDE_BN> gg(sg.M, sg.N, 0);
+            SideArgs g;
+            g.A = sg.A; g.B = sg.B; g.C = sg.C;
+            g.M = (int)sg.M; g.N = (int)sg.N; g.K = (int)sg.K;
+            g.lda = sg.lda; g.ldb = sg.ldb; g.ldc = sg.ldc;
+            g.tiles_m = gg.tiles_m; g.tiles_n = gg.tiles_n; g.bn_log = gg.bn_log;
+            // the product's workgroups start on a multiple of 8, so its XCD
+            // placement is the one of a launch of its own
+            g.nslice = nslice;
+            g.ncore = ((int64_t)nslice + 7) / 8 * 8;
+            hipLaunchKernelGGL((fwd16_carry_side_kernel<C, DK>), dim3((unsigned)(g.ncore + gg.grid)), dim3(NTF), 0,
+                               stream, kp, g);
             return hipGetLastError();
         }
     }
@@ -2440,6 +2499,16 @@ hipError_t launch_prefill_f32_staged(const PrefillArgs &a, hipStream_t stream)
     case 64: return launch_fwd32_dk<64>(a, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// Whether launch_prefill_f32_staged runs the hi/lo recurrence for these
+// arguments (and with it a.side): the same conditions as launch_fwd32_t, after
+// launch_prefill's early returns.
+bool prefill_f32_takes_side(const PrefillArgs &a)
+{
+    const int64_t wide = a.q_tok_stride > a.k_tok_stride ? a.q_tok_stride : a.k_tok_stride;
+    return !a.bf16 && a.ws && a.hilo_core && a.B * a.H > 0 && a.T > 0 && a.Dk % 32 == 0 && a.Dk <= 128 &&
+           a.chunk % 32 == 0 && a.chunk <= 64 && a.chunk * wide * 4 < ((int64_t)1 << 32);
 }
 
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)

@@ -37,6 +37,16 @@ struct PrefillArgs {
     // recurrence may run on bf16 MFMA with hi/lo operands (about 16 bits of each
     // operand) instead of fp32 MFMA
     bool hilo_core = false;
+    // An independent product C = A B^T (bf16, [M, K] x [N, K] -> [M, N] bf16)
+    // that the hi/lo recurrence runs in its own launch, on the compute units its
+    // slices leave free; null: none.  prefill_f32_takes_side() says whether the
+    // recurrence will take it; if not, the caller runs it itself.
+    struct SideGemm {
+        const __bf16 *A, *B;
+        __bf16 *C;
+        int64_t M, N, K, lda, ldb, ldc;
+    };
+    const SideGemm *side = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -87,6 +97,7 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
 // state recurrence writing y; q, k, v with token strides
 size_t prefill_f32_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t C);
 hipError_t launch_prefill_f32_staged(const PrefillArgs &a, hipStream_t stream);
+bool prefill_f32_takes_side(const PrefillArgs &a);
 
 // Layer helpers (layer.hip)
 struct LayerArgs {
