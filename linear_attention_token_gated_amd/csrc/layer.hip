@@ -68,7 +68,11 @@ hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, i
 // launch.  The tile is the largest that still gives every compute unit a
 // workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles do little MFMA
 // work per K step, so they keep 7 steps in flight (8 stages, 64 KB of LDS)
-// against the memory latency; the larger ones 3.
+// against the memory latency; the larger ones 3.  Where 64 x 64 tiles would
+// outnumber the compute units but 64 x 128 tiles would not (a few hundred
+// rows, thousands of columns: the decode step's in-projection), the wider
+// tile runs the product in one round, one workgroup per CU: its K steps are
+// latency-bound, so two workgroups sharing a CU take twice as long.
 template <typename OutT>
 hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
                    int64_t ldb, int64_t ldc, hipStream_t s, const __bf16 *B2 = nullptr, OutT *C2 = nullptr,
@@ -80,6 +84,8 @@ hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_
         return gemm_nt_tile<OutT, 256, 256, 4, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
     if (tiles(128, 128) >= 256)
         return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
+    if (tiles(64, 64) > 256 && tiles(64, 128) <= 256)
+        return gemm_nt_tile<OutT, 64, 128, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
     return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
 }
 
