@@ -187,19 +187,28 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     // The Gram runs on bf16 MFMA with fp32 sums: bf16 inputs are exact
     // operands; fp32 inputs are split into bf16 pairs hi + lo (hi = bf16(x),
     // lo = bf16(x - hi)) and each product sums hi*hi + hi*lo + lo*hi.
+    // The wavefronts pass values to each other only through LDS, and nothing
+    // here reads the record back, so the barriers order LDS only: the record's
+    // stores stay in flight across them.
     constexpr bool F32IN = sizeof(Tin) == 4;
     constexpr int NPART = F32IN ? 2 : 1;                 // bf16 parts per K or Q element
     constexpr int KP = DK + 8, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
     constexpr int NTRI = NB * (NB + 1) / 2;
     using FG = Frag<__bf16, KSD>;
     // LDS: K parts, then a region holding the Q parts until the P tiles are
-    // done; for fp32 inputs A and T reuse it afterwards (two workgroups per CU)
+    // done, which A reuses afterwards; T reuses the rest of that region for
+    // fp32 inputs (whose Q parts take twice the room), and for bf16 inputs K's
+    // rows once the K K^T tiles are done, where they hold it (Dk >= 2 C):
+    // two workgroups per CU for fp32 inputs at C = 64, Dk = 128, four for bf16
     constexpr size_t KQB = (size_t)2 * C * KP;           // one bf16 C x Dk part
     constexpr size_t ATB = (size_t)4 * C * CP;           // one fp32 C x C matrix
+    constexpr bool T_IN_K = !F32IN && ATB <= KQB;
     constexpr size_t oQ = NPART * KQB;
-    constexpr size_t QREG = F32IN ? (NPART * KQB > 2 * ATB ? NPART * KQB : 2 * ATB) : NPART * KQB;
-    constexpr size_t oA = F32IN ? oQ : oQ + QREG, oT = oA + ATB;
-    constexpr size_t oG = F32IN ? oQ + QREG : oT + ATB, BYTES = oG + 12 * C;   // G (fp64), beta
+    constexpr size_t QREG = F32IN ? (NPART * KQB > 2 * ATB ? NPART * KQB : 2 * ATB)
+                                  : (NPART * KQB > ATB ? NPART * KQB : ATB);
+    constexpr size_t oA = oQ;
+    constexpr size_t oT = F32IN ? oA + ATB : T_IN_K ? 0 : oQ + QREG;
+    constexpr size_t oG = oQ + QREG + (F32IN || T_IN_K ? 0 : ATB), BYTES = oG + 12 * C;   // G (fp64), beta
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char smem[BYTES];
     __bf16 *Ks = reinterpret_cast<__bf16 *>(smem);                 // part j at Ks + j * C * KP
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             rec[Rec<C>::oA + i] = 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // one Gram tile D = X_rb K_cb^T (X = Q or K) on and below the diagonal
     auto gram = [&](const __bf16 *Xs, int rb, int cb) {
@@ -284,11 +293,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             rec[Rec<C>::oP + r * C + j] = r >= j ? gam * acc[e] : 0.f;
         }
     }
-    if constexpr (F32IN) __syncthreads();        // A and T replace Q
-    for (int i = tid; i < C * C; i += NT) {
-        const int r = i / C, j = i % C;
-        if (j / 16 > r / 16) Ts[r * CP + j] = 0.f;
-    }
+    lds_barrier();                               // A (and for fp32 inputs T) replace Q
     // K K^T -> Ak (record), A = diag(beta) Ak (LDS)
     for (int tile = wave; tile < NTRI; tile += 4) {
         int rb, cb;
@@ -304,7 +309,11 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             As[r * CP + j] = Bs[r] * ak;
         }
     }
-    __syncthreads();
+    lds_barrier();                               // T may replace K
+    for (int i = tid; i < C * C; i += NT) {
+        const int r = i / C, j = i % C;
+        if (j / 16 > r / 16) Ts[r * CP + j] = 0.f;
+    }
 
     // diagonal blocks of T by forward substitution
     if (wave < NB) {
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ts[(16 * blk + ln) * CP + 16 * blk + lg + 4 * i] = X[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // blocks below the diagonal, one block row at a time:
     // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
@@ -341,7 +350,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ts[(16 * i + 4 * lg + e) * CP + 16 * j + ln] = -o[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     for (int i = tid; i < C * C / 4; i += NT) {

@@ -149,7 +149,9 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void gdn_verify_kernel(
 
     for (int t = 0; t < T; ++t) {
         const int64_t tok = (n * T + t) * H + hh;          // (n, t, h)
-        __syncthreads();                                   // the previous token's k, q, v are consumed
+        // barriers order LDS only: the previous token's state and y stores
+        // stay in flight across them (no wavefront reads what another stored)
+        lds_barrier();                                     // the previous token's k, q, v are consumed
         for (int i = tid; i < DK; i += NT) {
             sk[i] = to_f32(k[tok * DK + i]);
             sq[i] = to_f32(q[tok * DK + i]);
@@ -157,7 +159,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void gdn_verify_kernel(
         for (int i = tid; i < DV; i += NT) sv[i] = to_f32(v[tok * DV + i]);
         const float a_t = alpha[tok];
         const float b_t = beta[tok];
-        __syncthreads();
+        lds_barrier();
 
         f32x4 pa = zero4(), pb = zero4();
         float pkq = 0.f;
@@ -183,7 +185,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void gdn_verify_kernel(
             red_b[wave][lane] = pb;
             if (lane == 0) red_kq[wave] = pkq;
         }
-        __syncthreads();
+        lds_barrier();
         f32x4 A = zero4(), Bq = zero4();
         float kq = 0.f;
 #pragma unroll

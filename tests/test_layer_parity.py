@@ -31,6 +31,9 @@ def _run(oracle, inp, B, T, hidden, H, Dk, Dv, chunk, S0=None, nthreads=0):
     (2, 150, 256, 2, 64, 64, 64),
     (1, 77, 192, 4, 16, 32, 32),
     (1, 300, 512, 4, 128, 128, 64),
+    # 3 slices: the core's launch shared with the gate projection starts the
+    # projection's tiles at 8, so 5 workgroups between them end at once
+    (1, 100, 256, 3, 32, 16, 32),
 ])
 def test_layer_small(oracle_mod, B, T, hidden, H, Dk, Dv, chunk):
     print(f"case: layer B={B} T={T} hidden={hidden} H={H} Dk={Dk} Dv={Dv} C={chunk}", flush=True)
@@ -79,8 +82,9 @@ def test_layer_full_config(oracle_mod):
 
 def test_layer_every_gemm_tile(oracle_mod):
     """A layer whose projections take each tile size of gemm_nt_kernel: the
-    in-projection (4096 x 6144) 256 x 256, the gate and out-projections
-    (4096 x 2048) 128 x 128, the gate pair a|b (4096 x 32) 64 x 64."""
+    in-projection (4096 x 6144) 256 x 256, the out-projection (4096 x 2048)
+    128 x 128, the gate pair a|b (4096 x 32) 64 x 64; the gate projection
+    (4096 x 2048) runs in the core's launch on 256 x 256 tiles."""
     B, T, hidden, H, Dk, Dv, chunk = 1, 4096, 2048, 16, 128, 128, 64
     print("case: layer with every GEMM tile", flush=True)
     inp = wl.layer_inputs(B, T, hidden, H, Dk, Dv, conv_k=4, w_std=0.02, seed=33)
