@@ -195,20 +195,18 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     constexpr int KP = DK + 8, CP = C + 4, NB = C / 16, KSD = DK % 32 == 0 ? 32 : 16;
     constexpr int NTRI = NB * (NB + 1) / 2;
     using FG = Frag<__bf16, KSD>;
-    // LDS: K parts, then a region holding the Q parts until the P tiles are
-    // done, which A reuses afterwards; T reuses the rest of that region for
-    // fp32 inputs (whose Q parts take twice the room), and for bf16 inputs K's
-    // rows once the K K^T tiles are done, where they hold it (Dk >= 2 C):
-    // two workgroups per CU for fp32 inputs at C = 64, Dk = 128, four for bf16
+    // LDS: the K parts; a region holding one Q part at a time (fp32 inputs:
+    // the hi part, then the lo part) until the P tiles are done, which A
+    // reuses afterwards; T in K's rows once the K K^T tiles are done, where
+    // they hold it: three workgroups per CU for fp32 inputs, four for bf16 at
+    // C = 64, Dk = 128
     constexpr size_t KQB = (size_t)2 * C * KP;           // one bf16 C x Dk part
     constexpr size_t ATB = (size_t)4 * C * CP;           // one fp32 C x C matrix
-    constexpr bool T_IN_K = !F32IN && ATB <= KQB;
+    constexpr bool T_IN_K = ATB <= NPART * KQB;
     constexpr size_t oQ = NPART * KQB;
-    constexpr size_t QREG = F32IN ? (NPART * KQB > 2 * ATB ? NPART * KQB : 2 * ATB)
-                                  : (NPART * KQB > ATB ? NPART * KQB : ATB);
-    constexpr size_t oA = oQ;
-    constexpr size_t oT = F32IN ? oA + ATB : T_IN_K ? 0 : oQ + QREG;
-    constexpr size_t oG = oQ + QREG + (F32IN || T_IN_K ? 0 : ATB), BYTES = oG + 12 * C;   // G (fp64), beta
+    constexpr size_t QREG = KQB > ATB ? KQB : ATB;
+    constexpr size_t oA = oQ, oT = T_IN_K ? 0 : oQ + QREG;
+    constexpr size_t oG = oQ + QREG + (T_IN_K ? 0 : ATB), BYTES = oG + 12 * C;   // G (fp64), beta
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char smem[BYTES];
     __bf16 *Ks = reinterpret_cast<__bf16 *>(smem);                 // part j at Ks + j * C * KP
@@ -223,8 +221,26 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     const int64_t H = p.H, T = p.T, b = bh / H, h = bh % H, c0 = c * C;
     float *rec = p.rec + (bh * p.NC + c) * p.rec_floats;
 
+    RowsTile<Tin, C, DK> tq;         // fp32 inputs: kept until the lo part of Q goes to LDS
+    // the Q part `lo` (fp32 inputs; 0 = hi) into LDS
+    auto write_q = [&](bool lo) {
+#pragma unroll
+        for (int it = 0; it < RowsTile<Tin, C, DK>::NV; ++it) {
+            const int vi = tid + NT * it;
+            const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
+            if (RowsTile<Tin, C, DK>::NU % NT == 0 || vi < RowsTile<Tin, C, DK>::NU) {
+                if constexpr (F32IN) {
+                    bf16x4 hv, lv;
+                    split4(tq.v[it], hv, lv);
+                    *reinterpret_cast<bf16x4 *>(Qs + r * KP + col) = lo ? lv : hv;
+                } else {
+                    *reinterpret_cast<bf16x4 *>(Qs + r * KP + col) = tq.v[it];
+                }
+            }
+        }
+    };
     {
-        RowsTile<Tin, C, DK> tk, tq;
+        RowsTile<Tin, C, DK> tk;
         tk.load(static_cast<const Tin *>(p.k), b, h, c0, T, p.ks, DK);
         tq.load(static_cast<const Tin *>(p.q), b, h, c0, T, p.qs, DK);
 #pragma unroll
@@ -232,15 +248,11 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             const int vi = tid + NT * it;
             const int r = vi / (DK / 4), col = (vi % (DK / 4)) * 4;
             if (RowsTile<Tin, C, DK>::NU % NT == 0 || vi < RowsTile<Tin, C, DK>::NU) {
-                if constexpr (F32IN) {
-                    store_split4(Ks + r * KP + col, Ks + C * KP + r * KP + col, tk.v[it]);
-                    store_split4(Qs + r * KP + col, Qs + C * KP + r * KP + col, tq.v[it]);
-                } else {
-                    *reinterpret_cast<bf16x4 *>(Ks + r * KP + col) = tk.v[it];
-                    *reinterpret_cast<bf16x4 *>(Qs + r * KP + col) = tq.v[it];
-                }
+                if constexpr (F32IN) store_split4(Ks + r * KP + col, Ks + C * KP + r * KP + col, tk.v[it]);
+                else *reinterpret_cast<bf16x4 *>(Ks + r * KP + col) = tk.v[it];
             }
         }
+        write_q(false);
     }
     if (wave == 0) {
         const int64_t t = c0 + lane;
@@ -265,7 +277,14 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
     }
     lds_barrier();
 
-    // one Gram tile D = X_rb K_cb^T (X = Q or K) on and below the diagonal
+    // sum over Dk of X_rb Kp_cb^T for one bf16 part of each, added to acc
+    auto gram_part = [&](const __bf16 *Xs, const __bf16 *Kp, int rb, int cb, f32x4 acc) {
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += KSD)
+            acc = FG::mma(frag_rows<__bf16, KSD>(Xs, KP, 16 * rb, k0, lane), frag_rows<__bf16, KSD>(Kp, KP, 16 * cb, k0, lane), acc);
+        return acc;
+    };
+    // one Gram tile D = X_rb K_cb^T (X = K, all its parts in LDS) on and below the diagonal
     auto gram = [&](const __bf16 *Xs, int rb, int cb) {
         f32x4 acc = zero4(), acc2 = zero4();
 #pragma unroll
@@ -280,11 +299,41 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
         }
         return acc + acc2;
     };
-    // Q K^T -> P (the last use of Q)
-    for (int tile = wave; tile < NTRI; tile += 4) {
+    // Q K^T -> P (the last use of Q).  fp32 inputs: Qh Kh and Qh Kl with the hi
+    // part of Q in LDS, then Ql Kh once the lo part has replaced it
+    constexpr int NPT = (NTRI + 3) / 4;                  // P tiles per wave
+    f32x4 pa[NPT], pb[NPT];
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+        const int tile = wave + 4 * t;
+        int rb = 0, cb = 0;
+        if (tile < NTRI) tri_block(tile, rb, cb);
+        pa[t] = zero4();
+        pb[t] = zero4();
+        if (tile < NTRI) {
+            pa[t] = gram_part(Qs, Ks, rb, cb, pa[t]);
+            if constexpr (F32IN) pb[t] = gram_part(Qs, Ks + C * KP, rb, cb, pb[t]);
+        }
+    }
+    if constexpr (F32IN) {
+        lds_barrier();                               // every wave is done with Qh
+        write_q(true);
+        lds_barrier();
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) {
+            const int tile = wave + 4 * t;
+            int rb = 0, cb = 0;
+            if (tile < NTRI) tri_block(tile, rb, cb);
+            if (tile < NTRI) pb[t] = gram_part(Qs, Ks, rb, cb, pb[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+        const int tile = wave + 4 * t;
+        if (tile >= NTRI) continue;
         int rb, cb;
         tri_block(tile, rb, cb);
-        const f32x4 acc = gram(Qs, rb, cb);
+        const f32x4 acc = pa[t] + pb[t];
         const int j = 16 * cb + ln;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -293,7 +342,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdParams p)
             rec[Rec<C>::oP + r * C + j] = r >= j ? gam * acc[e] : 0.f;
         }
     }
-    lds_barrier();                               // A (and for fp32 inputs T) replace Q
+    lds_barrier();                               // A replaces Q
     // K K^T -> Ak (record), A = diag(beta) Ak (LDS)
     for (int tile = wave; tile < NTRI; tile += 4) {
         int rb, cb;
