@@ -2381,10 +2381,10 @@ constexpr int SIDE_BM = 256, SIDE_BN = 256, SIDE_ST = 4, SIDE_NW = 8;
 static_assert(SIDE_NW * 64 == NTF, "one block size for both roles");
 
 struct SideArgs {
-    const __bf16 *A, *B;
-    __bf16 *C;
-    int M, N, K;
-    int64_t lda, ldb, ldc;
+    const __bf16 *A;
+    GemmProducts<__bf16> P;
+    int M, K;
+    int64_t lda;
     int tiles_m, tiles_n, bn_log;
     int64_t nslice, ncore;
 };
@@ -2399,9 +2399,8 @@ __global__ __launch_bounds__(NTF, 1) void fwd16_carry_side_kernel(BwdParams p, S
     if (bid < g.nslice) {
         fwd16_carry_block<C, DK>(p, bid, smem);
     } else if (bid >= g.ncore) {
-        gemm_nt_block<__bf16, SIDE_BM, SIDE_BN, SIDE_ST, SIDE_NW>(
-            (int)(bid - g.ncore), smem, g.A, g.B, g.C, g.M, g.N, g.K, g.lda, g.ldb, g.ldc, g.tiles_m, g.tiles_n,
-            g.bn_log, g.B, g.C, 0, g.ldb, g.ldc, g.tiles_n);
+        gemm_nt_block<__bf16, SIDE_BM, SIDE_BN, SIDE_ST, SIDE_NW>((int)(bid - g.ncore), smem, g.A, g.M, g.K, g.lda,
+                                                                  g.P, g.tiles_m, g.tiles_n, g.bn_log);
     }
 }
 
@@ -2498,9 +2497,9 @@ hipError_t launch_fwd32_t(const PrefillArgs &a, hipStream_t stream)
             const PrefillArgs::SideGemm &sg = *a.side;
             const GemmGrid<SIDE_BM, SIDE_BN> gg(sg.M, sg.N, 0);
             SideArgs g;
-            g.A = sg.A; g.B = sg.B; g.C = sg.C;
-            g.M = (int)sg.M; g.N = (int)sg.N; g.K = (int)sg.K;
-            g.lda = sg.lda; g.ldb = sg.ldb; g.ldc = sg.ldc;
+            g.A = sg.A;
+            g.P = gemm_products(gg, GemmOp<__bf16>{sg.B, sg.C, sg.N, sg.ldb, sg.ldc});
+            g.M = (int)sg.M; g.K = (int)sg.K; g.lda = sg.lda;
             g.tiles_m = gg.tiles_m; g.tiles_n = gg.tiles_n; g.bn_log = gg.bn_log;
             // the product's workgroups start on a multiple of 8, so its XCD
             // placement is the one of a launch of its own

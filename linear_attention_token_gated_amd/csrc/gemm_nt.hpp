@@ -49,18 +49,25 @@ template <int BM, int BN, int NW> struct GemmTile {
     static_assert(LA >= 1 && LB >= 1, "every wave loads rows of both tiles");
 };
 
+// Up to three products of one A in one launch, C_p = A B_p^T: column tiles
+// [0, tile_end[0]) belong to product 0, [tile_end[0], tile_end[1]) to product
+// 1, [tile_end[1], tile_end[2]) to product 2 (an absent product has no tiles).
+template <typename OutT> struct GemmProducts {
+    const __bf16 *B[3];
+    OutT *C[3];
+    int N[3];
+    int64_t ldb[3], ldc[3];
+    int tile_end[3];
+};
+
 // One workgroup's tile (pid: its index in the GEMM's grid, smem: ST * STAGE
 // bytes of LDS, 1024-byte aligned).  ST stages of K steps in LDS (a power of
-// two >= 4), ST - 1 of them in flight; NW wavefronts.  Two products of one A may share a launch: column tiles from
-// tiles_n1 on belong to the second (B2, C2, N2, ldb2, ldc2); a single product
-// passes tiles_n1 = tiles_n.
+// two >= 4), ST - 1 of them in flight; NW wavefronts.  tiles_n: column tiles of
+// every product together.
 template <typename OutT, int BM, int BN, int ST, int NW>
-__device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 *__restrict__ A,
-                                              const __bf16 *__restrict__ B1, OutT *__restrict__ C1, int M, int N1,
-                                              int K, int64_t lda, int64_t ldb1, int64_t ldc1, int tiles_m,
-                                              int tiles_n, int bn_log, const __bf16 *__restrict__ B2,
-                                              OutT *__restrict__ C2, int N2, int64_t ldb2, int64_t ldc2,
-                                              int tiles_n1)
+__device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 *__restrict__ A, int M, int K,
+                                              int64_t lda, const GemmProducts<OutT> &P, int tiles_m, int tiles_n,
+                                              int bn_log)
 {
     using G = GemmTile<BM, BN, NW>;
     constexpr int WGM = G::WGM;
@@ -86,12 +93,12 @@ __device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 
         tn = (blk % bpr) * bn + (t & (bn - 1));
         if (tm >= tiles_m || tn >= tiles_n) return;
     }
-    const bool second = tn >= tiles_n1;
-    const __bf16 *Bm = second ? B2 : B1;
-    OutT *Cm = second ? C2 : C1;
-    const int N = second ? N2 : N1;
-    const int64_t ldb = second ? ldb2 : ldb1, ldc = second ? ldc2 : ldc1;
-    if (second) tn -= tiles_n1;
+    const int pi = tn < P.tile_end[0] ? 0 : (tn < P.tile_end[1] ? 1 : 2);
+    const __bf16 *Bm = P.B[pi];
+    OutT *Cm = P.C[pi];
+    const int N = P.N[pi];
+    const int64_t ldb = P.ldb[pi], ldc = P.ldc[pi];
+    if (pi > 0) tn -= P.tile_end[pi - 1];
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t mrows = M - m0 < BM ? M - m0 : BM, nrows = N - n0 < BN ? N - n0 : BN;
     const int ntk = (K + GBK - 1) / GBK;
@@ -209,12 +216,15 @@ __device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 
 // Grid of a GEMM launch: tiles_m x tiles_n tiles of BM x BN, XCD blocks of
 // 32 tiles (bn_log: log2 of the columns of a block), a multiple of 8 blocks.
 template <int BM, int BN> struct GemmGrid {
-    int tiles_m, tiles_n1, tiles_n, bn_log;
+    int tiles_m, tiles_n, bn_log;
+    int tile_end[3];
     int64_t grid;
-    GemmGrid(int64_t M, int64_t N, int64_t N2) {
+    GemmGrid(int64_t M, int64_t N, int64_t N2 = 0, int64_t N3 = 0) {
         tiles_m = (int)((M + BM - 1) / BM);
-        tiles_n1 = (int)((N + BN - 1) / BN);
-        tiles_n = tiles_n1 + (int)((N2 + BN - 1) / BN);
+        tile_end[0] = (int)((N + BN - 1) / BN);
+        tile_end[1] = tile_end[0] + (int)((N2 + BN - 1) / BN);
+        tile_end[2] = tile_end[1] + (int)((N3 + BN - 1) / BN);
+        tiles_n = tile_end[2];
         bn_log = 0;
         while (bn_log < 3 && (2 << bn_log) <= tiles_n) ++bn_log;
         const int bn = 1 << bn_log, bm = 32 >> bn_log;
@@ -222,6 +232,31 @@ template <int BM, int BN> struct GemmGrid {
         grid = (blocks + 7) / 8 * 8 * 32;                 // 32 tiles a block, blocks a multiple of 8
     }
 };
+
+// One product of a launch: C[M, N] = A B^T with B [N, K] (rows ldb apart)
+// and C rows ldc apart
+template <typename OutT> struct GemmOp {
+    const __bf16 *B = nullptr;
+    OutT *C = nullptr;
+    int64_t N = 0, ldb = 0, ldc = 0;
+};
+
+// The products of a launch on grid g (built with the same N, N2, N3); an
+// absent product keeps the first one's pointers and has no tiles.
+template <typename OutT, int BM, int BN>
+GemmProducts<OutT> gemm_products(const GemmGrid<BM, BN> &g, const GemmOp<OutT> &p0, GemmOp<OutT> p1 = {},
+                                 GemmOp<OutT> p2 = {})
+{
+    if (!p1.B) { p1 = p0; p1.N = 0; }
+    if (!p2.B) { p2 = p0; p2.N = 0; }
+    const GemmOp<OutT> *ops[3] = {&p0, &p1, &p2};
+    GemmProducts<OutT> P;
+    for (int i = 0; i < 3; ++i) {
+        P.B[i] = ops[i]->B; P.C[i] = ops[i]->C; P.N[i] = (int)ops[i]->N;
+        P.ldb[i] = ops[i]->ldb; P.ldc[i] = ops[i]->ldc; P.tile_end[i] = g.tile_end[i];
+    }
+    return P;
+}
 
 }  // namespace
 

@@ -41,52 +41,53 @@ constexpr float kRmsEps = 1e-6f;
 
 
 template <typename OutT, int BM, int BN, int ST, int NW>
-__global__ __launch_bounds__(64 * NW, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, const __bf16 *__restrict__ B1,
-                                                         OutT *__restrict__ C1, int M, int N1, int K, int64_t lda,
-                                                         int64_t ldb1, int64_t ldc1, int tiles_m, int tiles_n, int bn_log,
-                                                         const __bf16 *__restrict__ B2, OutT *__restrict__ C2, int N2,
-                                                         int64_t ldb2, int64_t ldc2, int tiles_n1)
+__global__ __launch_bounds__(64 * NW, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, int M,
+                                                                              int K, int64_t lda,
+                                                                              GemmProducts<OutT> P, int tiles_m,
+                                                                              int tiles_n, int bn_log)
 {
     __shared__ __attribute__((aligned(1024))) char smem[ST * GemmTile<BM, BN, NW>::STAGE];
-    gemm_nt_block<OutT, BM, BN, ST, NW>((int)blockIdx.x, smem, A, B1, C1, M, N1, K, lda, ldb1, ldc1, tiles_m, tiles_n,
-                                        bn_log, B2, C2, N2, ldb2, ldc2, tiles_n1);
+    gemm_nt_block<OutT, BM, BN, ST, NW>((int)blockIdx.x, smem, A, M, K, lda, P, tiles_m, tiles_n, bn_log);
 }
 
+// C_p = A B_p^T for up to three products of one A [M, K] in one launch
 template <typename OutT, int BM, int BN, int ST, int NW = 4>
-hipError_t gemm_nt_tile(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                        int64_t ldb, int64_t ldc, const __bf16 *B2, OutT *C2, int64_t N2, int64_t ldb2, int64_t ldc2,
-                        hipStream_t s)
+hipError_t gemm_nt_tile(const __bf16 *A, int64_t M, int64_t K, int64_t lda, const GemmOp<OutT> &p0,
+                        const GemmOp<OutT> &p1, const GemmOp<OutT> &p2, hipStream_t s)
 {
-    const GemmGrid<BM, BN> g(M, N, N2);
-    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST, NW>), dim3((unsigned)g.grid), dim3(64 * NW), 0, s, A, Bm, C,
-                       (int)M, (int)N, (int)K, lda, ldb, ldc, g.tiles_m, g.tiles_n, g.bn_log, B2 ? B2 : Bm,
-                       C2 ? C2 : C, (int)N2, ldb2, ldc2, g.tiles_n1);
+    const GemmGrid<BM, BN> g(M, p0.N, p1.B ? p1.N : 0, p2.B ? p2.N : 0);
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST, NW>), dim3((unsigned)g.grid), dim3(64 * NW), 0, s, A, (int)M,
+                       (int)K, lda, gemm_products(g, p0, p1, p2), g.tiles_m, g.tiles_n, g.bn_log);
     return hipGetLastError();
 }
 
-// C[M, N] = A[M, K] B[N, K]^T, and optionally C2[M, N2] = A B2^T in the same
-// launch.  The tile is the largest that still gives every compute unit a
-// workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles do little MFMA
-// work per K step, so they keep 7 steps in flight (8 stages, 64 KB of LDS)
+// C[M, N] = A[M, K] B[N, K]^T, with up to two more products of the same A in
+// the same launch.  The tile is the largest that still gives every compute
+// unit a workgroup (256 x 256, 128 x 128, else 64 x 64).  Small tiles do little
+// MFMA work per K step, so they keep 7 steps in flight (8 stages, 64 KB of LDS)
 // against the memory latency; the larger ones 3.  Where 64 x 64 tiles would
 // outnumber the compute units but 64 x 128 tiles would not (a few hundred
-// rows, thousands of columns: the decode step's in-projection), the wider
-// tile runs the product in one round, one workgroup per CU: its K steps are
-// latency-bound, so two workgroups sharing a CU take twice as long.
+// rows, thousands of columns), the wider tile runs the product in one round,
+// one workgroup per CU: its K steps are latency-bound, so two workgroups
+// sharing a CU take twice as long.  Where even 64 x 128 tiles outnumber the
+// compute units (the decode step's three in-projections at once, 260 tiles),
+// they keep 3 steps in flight in 48 KB, so three fit on a CU and the launch
+// is still one round.
 template <typename OutT>
-hipError_t project(const __bf16 *A, const __bf16 *Bm, OutT *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                   int64_t ldb, int64_t ldc, hipStream_t s, const __bf16 *B2 = nullptr, OutT *C2 = nullptr,
-                   int64_t N2 = 0, int64_t ldb2 = 0, int64_t ldc2 = 0)
+hipError_t project(const __bf16 *A, int64_t M, int64_t K, int64_t lda, const GemmOp<OutT> &p0, hipStream_t s,
+                   const GemmOp<OutT> &p1 = {}, const GemmOp<OutT> &p2 = {})
 {
-    if (M == 0 || N + N2 == 0) return hipSuccess;
-    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn + (N2 + bn - 1) / bn); };
-    if (tiles(256, 256) >= 256)
-        return gemm_nt_tile<OutT, 256, 256, 4, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
-    if (tiles(128, 128) >= 256)
-        return gemm_nt_tile<OutT, 128, 128, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
-    if (tiles(64, 64) > 256 && tiles(64, 128) <= 256)
-        return gemm_nt_tile<OutT, 64, 128, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
-    return gemm_nt_tile<OutT, 64, 64, 8>(A, Bm, C, M, N, K, lda, ldb, ldc, B2, C2, N2, ldb2, ldc2, s);
+    const int64_t N1 = p0.N, N2 = p1.B ? p1.N : 0, N3 = p2.B ? p2.N : 0;
+    if (M == 0 || N1 + N2 + N3 == 0) return hipSuccess;
+    auto tiles = [&](int64_t bm, int64_t bn) {
+        return ((M + bm - 1) / bm) * ((N1 + bn - 1) / bn + (N2 + bn - 1) / bn + (N3 + bn - 1) / bn);
+    };
+    if (tiles(256, 256) >= 256) return gemm_nt_tile<OutT, 256, 256, 4, 8>(A, M, K, lda, p0, p1, p2, s);
+    if (tiles(128, 128) >= 256) return gemm_nt_tile<OutT, 128, 128, 4>(A, M, K, lda, p0, p1, p2, s);
+    if (tiles(64, 64) > 256 && tiles(64, 128) <= 256) return gemm_nt_tile<OutT, 64, 128, 8>(A, M, K, lda, p0, p1, p2, s);
+    if (tiles(64, 128) > 256 && tiles(64, 128) <= 3 * 256)
+        return gemm_nt_tile<OutT, 64, 128, 4>(A, M, K, lda, p0, p1, p2, s);
+    return gemm_nt_tile<OutT, 64, 64, 8>(A, M, K, lda, p0, p1, p2, s);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
@@ -214,80 +215,173 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Decode prologue: one token per sequence.  conv_state row r of sequence n
-// holds the in-projection of token t - (conv_k - 1 - r), oldest first; tap j
-// (j < conv_k - 1) reads row j and tap conv_k - 1 the current token.  The
-// rows are then shifted by one, in place: each thread reads and writes only
-// its own 8 channels.  L2 norm and gates as in the prologue.
+// Layer decode step, everything between the in-projections and the
+// out-projection for one (sequence n, head h) in one workgroup:
+//   1. causal conv of this head's q, k, v channels over the conv history and
+//      this token's in-projection row; the history (conv_state row r of
+//      sequence n holds the in-projection of token t - (conv_k - 1 - r), oldest
+//      first) shifted by one row in place; L2 norm of q and k; alpha by eq (10)
+//      and beta by eq (9)
+//   2. eqs (1)-(4) for one token on the stored fp32 state (read once, written
+//      once; the same arithmetic as the decode kernel)
+//   3. zero-centred RMSNorm of y over Dv with gain (1 + gamma), times
+//      sigmoid(z), written as the bf16 operand of W_o (eq (11))
+// The state's loads are issued first and land while steps 1 and 2 begin.
+// The first (2 Dk + Dv) / 4 threads own 4 channels each (q, then k, then v; a
+// q or k head is Dk / 4 aligned lanes of one wavefront, reduced with
+// xor-shuffles).
 // ---------------------------------------------------------------------------
-template <int DK, int KC>
-__global__ __launch_bounds__(256) void decode_prologue_kernel(const float *__restrict__ pre,
-                                                              const __bf16 *__restrict__ conv_w,
-                                                              const float *__restrict__ ab,
-                                                              const float *__restrict__ Aexp,
-                                                              const float *__restrict__ b_alpha,
-                                                              float *__restrict__ conv_state, float *__restrict__ post,
-                                                              float *__restrict__ alpha, float *__restrict__ beta,
-                                                              int H, int nqkv)
+// waves per SIMD that two resident workgroups need (the register budget that
+// keeps two on a CU, so one's loads stream while the other computes)
+template <int DK, int DV> struct LayerDecodeWaves {
+    static constexpr int NT = DecodeShape<DK, DV>::NT;
+    static constexpr int value = NT >= 1024 ? 8 : (NT >= 256 ? NT / 128 : 1);
+};
+
+template <int DK, int DV, int KC>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT), (LayerDecodeWaves<DK, DV>::value)) void layer_decode_kernel(
+    const float *__restrict__ pre, const float *__restrict__ ab, const float *__restrict__ zf,
+    const __bf16 *__restrict__ conv_w, const float *__restrict__ Aexp, const float *__restrict__ b_alpha,
+    const float *__restrict__ gamma, float *__restrict__ conv_state, float *__restrict__ state,
+    __bf16 *__restrict__ g, int H, int nqkv)
 {
-    const int64_t n = blockIdx.x;
-    const int nvec = nqkv / 8;
-    const int nqk_vec = 2 * H * DK / 8;
-    constexpr int HV = DK / 8;
-    const int vi = blockIdx.y * 256 + threadIdx.x;
-    const bool active = vi < nvec;
-    const int c0 = active ? vi * 8 : 0;
-    auto ld8 = [&](const float *src, float (&x)[8]) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
-        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
-        x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
-        x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
-    };
-    float rows[KC][8];                       // taps 0 .. KC-1: history rows, then the current token
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+    // prologue threads: 4 channels each, in whole wavefronts (PW of them)
+    constexpr int HVK = DK / 4, NV = (2 * DK + DV) / 4, PW = (NV + 63) / 64;
+    static_assert(64 * PW <= NT && HVK <= 64 && CG <= 64, "prologue threads and y columns");
+    const int64_t nh = blockIdx.x, n = nh / H;
+    const int hh = (int)(nh % H);
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+
+    __shared__ __attribute__((aligned(16))) float sk[DK], sq[DK], sv[DV];
+    __shared__ f32x4 red_a[Sh::NWAVE][CG], red_b[Sh::NWAVE][CG];
+    __shared__ float red_kq[Sh::NWAVE];
+    __shared__ float s_ab[2];
+
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(state + nh * (int64_t)(DK * DV));
+    f32x4 s[RPT];
 #pragma unroll
-    for (int j = 0; j < KC - 1; ++j) ld8(conv_state + (n * (KC - 1) + j) * nqkv + c0, rows[j]);
-    ld8(pre + n * nqkv + c0, rows[KC - 1]);
-    // the thread's taps: 8 KC consecutive bf16 (channel-major), in 16-byte pieces
-    __bf16 w[8 * KC];
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(S4 + (rg + RG * i) * CG + cg);
+    f32x4 zv = zero4();
+    if (rg == 0) zv = *reinterpret_cast<const f32x4 *>(zf + nh * DV + 4 * cg);
+
+    if (tid < 64 * PW) {
+        // step 1: thread tid < NV owns channels c0 .. c0 + 3 of the q|k|v row
+        const bool active = tid < NV;
+        const int part = tid < HVK ? 0 : (tid < 2 * HVK ? 1 : 2);
+        const int local = 4 * (tid - part * HVK);             // channel within this head's q, k or v
+        const int c0 = active ? (part < 2 ? part * H * DK + hh * DK : 2 * H * DK + hh * DV) + local : 0;
+        f32x4 rows[KC];                                       // taps 0 .. KC-1: history, then this token
 #pragma unroll
-    for (int q = 0; q < KC; ++q) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(conv_w + (int64_t)c0 * KC + 8 * q);
+        for (int j = 0; j < KC - 1; ++j) rows[j] = *reinterpret_cast<const f32x4 *>(conv_state + (n * (KC - 1) + j) * nqkv + c0);
+        rows[KC - 1] = *reinterpret_cast<const f32x4 *>(pre + n * nqkv + c0);
+        __bf16 w[4 * KC];                                     // 4 KC consecutive taps, channel-major
+        if constexpr (KC % 2 == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[8 * q + e] = v[e];
-    }
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < KC / 2; ++q) {
+                const bf16x8 v = *reinterpret_cast<const bf16x8 *>(conv_w + (int64_t)c0 * KC + 8 * q);
 #pragma unroll
-    for (int j = 0; j < KC; ++j)
+                for (int e = 0; e < 8; ++e) w[8 * q + e] = v[e];
+            }
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf((float)w[e * KC + j], rows[j][e], o[e]);
-    float ss = 0.f;
+            for (int q = 0; q < KC; ++q) {
+                const bf16x4 v = *reinterpret_cast<const bf16x4 *>(conv_w + (int64_t)c0 * KC + 4 * q);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
-#pragma unroll
-    for (int off = 1; off < HV; off <<= 1) ss += __shfl_xor(ss, off);
-    if (active) {
-        const float scale = vi < nqk_vec ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
-        f32x4 o0, o1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { o0[e] = o[e] * scale; o1[e] = o[4 + e] * scale; }
-        *reinterpret_cast<f32x4 *>(post + n * nqkv + c0) = o0;
-        *reinterpret_cast<f32x4 *>(post + n * nqkv + c0 + 4) = o1;
-        // history shifted by one token: row r <- tap r + 1
-#pragma unroll
-        for (int r = 0; r < KC - 1; ++r) {
-            {
-                float *dst = conv_state + (n * (KC - 1) + r) * nqkv + c0;
-                *reinterpret_cast<f32x4 *>(dst) = f32x4{rows[r + 1][0], rows[r + 1][1], rows[r + 1][2], rows[r + 1][3]};
-                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{rows[r + 1][4], rows[r + 1][5], rows[r + 1][6], rows[r + 1][7]};
+                for (int e = 0; e < 4; ++e) w[4 * q + e] = v[e];
             }
         }
+        f32x4 o = zero4();
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = fmaf((float)w[e * KC + j], rows[j][e], o[e]);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(o[e], o[e], ss);
+#pragma unroll
+        for (int off = 1; off < HVK; off <<= 1) ss += __shfl_xor(ss, off);
+        if (active) {
+            const float scale = part < 2 ? 1.f / sqrtf(ss + kL2Eps) : 1.f;
+            float *dst = part == 0 ? sq : (part == 1 ? sk : sv);
+            *reinterpret_cast<f32x4 *>(dst + local) = o * scale;
+#pragma unroll
+            for (int r = 0; r < KC - 1; ++r)
+                *reinterpret_cast<f32x4 *>(conv_state + (n * (KC - 1) + r) * nqkv + c0) = rows[r + 1];
+        }
+        if (tid == 63) {
+            const float a = ab[n * 2 * H + hh], bb = ab[n * 2 * H + H + hh];
+            s_ab[0] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
+            s_ab[1] = sigmoidf_(bb);
+        }
     }
-    if (blockIdx.y == 0) {
-        for (int hh = threadIdx.x; hh < H; hh += 256) {
-            const float a = ab[n * 2 * H + hh];
-            const float bb = ab[n * 2 * H + H + hh];
-            alpha[n * H + hh] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
-            beta[n * H + hh] = sigmoidf_(bb);
+    __syncthreads();
+
+    // step 2: a = S^T k, b = S^T q, kq = k . q over this thread's rows, reduced
+    // inside the wavefront (lanes CG apart), then across wavefronts through LDS
+    f32x4 pa = zero4(), pb = zero4();
+    float pkq = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + RG * i;
+        const float kr = sk[r], qr = sq[r];
+        pa += s[i] * kr;
+        pb += s[i] * qr;
+        if (cg == 0) pkq += kr * qr;
+    }
+#pragma unroll
+    for (int off = CG; off < 64 && off < NT; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pa[c] += __shfl_xor(pa[c], off);
+            pb[c] += __shfl_xor(pb[c], off);
+        }
+        pkq += __shfl_xor(pkq, off);
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < CG) {
+        red_a[wave][lane] = pa;
+        red_b[wave][lane] = pb;
+        if (lane == 0) red_kq[wave] = pkq;
+    }
+    __syncthreads();
+    f32x4 Av = zero4(), Bq = zero4();
+    float kq = 0.f;
+#pragma unroll
+    for (int w = 0; w < Sh::NWAVE; ++w) {
+        Av += red_a[w][cg];
+        Bq += red_b[w][cg];
+        kq += red_kq[w];
+    }
+    const float a_t = s_ab[0], b_t = s_ab[1];
+    const f32x4 vv = *reinterpret_cast<const f32x4 *>(&sv[4 * cg]);
+    const f32x4 e = vv - a_t * Av;                 // eq (2) on the decayed state
+    const f32x4 yv = a_t * Bq + (b_t * kq) * e;   // eq (4) on the updated state
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + RG * i;
+        const f32x4 sn = a_t * s[i] + (b_t * sk[r]) * e;   // eqs (1), (3)
+        __builtin_nontemporal_store(sn, S4 + r * CG + cg);
+    }
+
+    // step 3: lanes 0 .. CG-1 of wavefront 0 hold y's columns 4 cg .. 4 cg + 3
+    if (tid < 64) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ss = fmaf(yv[c], yv[c], ss);
+#pragma unroll
+        for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
+        if (rg == 0) {
+            const float inv = 1.f / sqrtf(ss / (float)DV + kRmsEps);
+            bf16x4 outv;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // z as the layer's gate projection stores it (bf16)
+                const float zb = (float)(__bf16)zv[c];
+                outv[c] = (__bf16)(sigmoidf_(zb) * yv[c] * inv * (1.f + gamma[4 * cg + c]));
+            }
+            *reinterpret_cast<bf16x4 *>(g + nh * DV + 4 * cg) = outv;
         }
     }
 }
@@ -390,25 +484,56 @@ hipError_t launch_epilogue_dv(const float *y, const __bf16 *z, const float *gamm
     return hipGetLastError();
 }
 
-template <int DK>
-hipError_t launch_decode_prologue_dk(const float *pre, const __bf16 *conv_w, const float *ab, const float *A,
-                                     const float *b_alpha, float *conv_state, float *post, float *alpha, float *beta,
-                                     int64_t N, int H, int nqkv, int conv_k, hipStream_t s)
+template <int DK, int DV>
+hipError_t launch_layer_decode_dv(const LayerDecodeArgs &a, const float *pre, const float *ab, const float *zf,
+                                  __bf16 *g, int nqkv, hipStream_t s)
 {
-    const unsigned slabs = (unsigned)((nqkv / 8 + 255) / 256);
-    const dim3 grid((unsigned)N, slabs);
-    switch (conv_k) {
-    case 1: hipLaunchKernelGGL((decode_prologue_kernel<DK, 1>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
-                               conv_state, post, alpha, beta, H, nqkv); break;
-    case 2: hipLaunchKernelGGL((decode_prologue_kernel<DK, 2>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
-                               conv_state, post, alpha, beta, H, nqkv); break;
-    case 3: hipLaunchKernelGGL((decode_prologue_kernel<DK, 3>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
-                               conv_state, post, alpha, beta, H, nqkv); break;
-    case 4: hipLaunchKernelGGL((decode_prologue_kernel<DK, 4>), grid, dim3(256), 0, s, pre, conv_w, ab, A, b_alpha,
-                               conv_state, post, alpha, beta, H, nqkv); break;
+    const dim3 grid((unsigned)(a.N * a.H)), block(DecodeShape<DK, DV>::NT);
+    const __bf16 *cw = (const __bf16 *)a.conv_w;
+    const int H = (int)a.H;
+    switch (a.conv_k) {
+    case 1: hipLaunchKernelGGL((layer_decode_kernel<DK, DV, 1>), grid, block, 0, s, pre, ab, zf, cw, a.A, a.b_alpha,
+                               a.norm_gamma, a.conv_state, a.state, g, H, nqkv); break;
+    case 2: hipLaunchKernelGGL((layer_decode_kernel<DK, DV, 2>), grid, block, 0, s, pre, ab, zf, cw, a.A, a.b_alpha,
+                               a.norm_gamma, a.conv_state, a.state, g, H, nqkv); break;
+    case 3: hipLaunchKernelGGL((layer_decode_kernel<DK, DV, 3>), grid, block, 0, s, pre, ab, zf, cw, a.A, a.b_alpha,
+                               a.norm_gamma, a.conv_state, a.state, g, H, nqkv); break;
+    case 4: hipLaunchKernelGGL((layer_decode_kernel<DK, DV, 4>), grid, block, 0, s, pre, ab, zf, cw, a.A, a.b_alpha,
+                               a.norm_gamma, a.conv_state, a.state, g, H, nqkv); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_layer_decode_dk(const LayerDecodeArgs &a, const float *pre, const float *ab, const float *zf,
+                                  __bf16 *g, int nqkv, hipStream_t s)
+{
+    switch (a.Dv) {
+    case 16: return launch_layer_decode_dv<DK, 16>(a, pre, ab, zf, g, nqkv, s);
+    case 32: return launch_layer_decode_dv<DK, 32>(a, pre, ab, zf, g, nqkv, s);
+    case 64: return launch_layer_decode_dv<DK, 64>(a, pre, ab, zf, g, nqkv, s);
+    case 128: return launch_layer_decode_dv<DK, 128>(a, pre, ab, zf, g, nqkv, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Workspace of the decode step: the three in-projections (fp32) and the gated
+// norm (bf16, the out-projection's operand)
+struct DecodeWs {
+    size_t pre, ab, z, g, total;
+};
+DecodeWs decode_ws_layout(int64_t N, int64_t H, int64_t Dk, int64_t Dv)
+{
+    const size_t n = (size_t)N, nqkv = (size_t)(H * (2 * Dk + Dv));
+    DecodeWs w;
+    size_t o = 0;
+    w.pre = o; o += al256(n * nqkv * 4);
+    w.ab = o;  o += al256(n * (size_t)(2 * H) * 4);
+    w.z = o;   o += al256(n * (size_t)(H * Dv) * 4);
+    w.g = o;   o += al256(n * (size_t)(H * Dv) * 2);
+    w.total = o;
+    return w;
 }
 
 }  // namespace
@@ -423,7 +548,7 @@ size_t layer_workspace_bytes(int64_t B, int64_t T, int64_t hidden, int64_t H, in
 size_t layer_decode_workspace_bytes(int64_t N, int64_t H, int64_t Dk, int64_t Dv)
 {
     if (N == 0 || H == 0) return 0;
-    return ws_layout(N, 1, H, Dk, Dv, false).total;
+    return decode_ws_layout(N, H, Dk, Dv).total;
 }
 
 // Scratch memory of the allocation-free layer decode step: the intermediates
@@ -483,8 +608,10 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
 
     // (separate launches: at M = B*T the q|k|v tiles fill whole rounds of the
     // compute units, and the a|b tiles added to that launch would start one more)
-    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, M, nqkv, hidden, hidden, hidden, nqkv, s))) return e;
-    if ((e = project<float>(x, (const __bf16 *)a.W_ab, ab, M, 2 * H, hidden, hidden, hidden, 2 * H, s))) return e;
+    if ((e = project<float>(x, M, hidden, hidden, GemmOp<float>{(const __bf16 *)a.W_qkv, pre, nqkv, hidden, nqkv}, s)))
+        return e;
+    if ((e = project<float>(x, M, hidden, hidden, GemmOp<float>{(const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H}, s)))
+        return e;
 
     switch (Dk) {
     case 16: e = launch_prologue_dk<16>(pre, (const __bf16 *)a.conv_w, ab, a.A, a.b_alpha, post, alpha, beta, M, a.T, (int)H, (int)nqkv, (int)a.conv_k, s); break;
@@ -509,7 +636,8 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     const PrefillArgs::SideGemm gate{x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv};
     if (prefill_f32_takes_side(p)) {
         p.side = &gate;
-    } else if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, M, H * Dv, hidden, hidden, hidden, H * Dv, s))) {
+    } else if ((e = project<__bf16>(x, M, hidden, hidden,
+                                    GemmOp<__bf16>{(const __bf16 *)a.W_gate, z, H * Dv, hidden, H * Dv}, s))) {
         return e;
     }
     if ((e = launch_prefill(p, s))) return e;
@@ -522,61 +650,39 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e) return e;
-    return project<float>(g, (const __bf16 *)a.W_o, a.out, M, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+    return project<float>(g, M, H * Dv, H * Dv, GemmOp<float>{(const __bf16 *)a.W_o, a.out, hidden, H * Dv, hidden}, s);
 }
 
 hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
 {
     const int64_t N = a.N, H = a.H, Dk = a.Dk, Dv = a.Dv, hidden = a.hidden;
     if (N == 0 || H == 0) return hipSuccess;
-    const WsLayout w = ws_layout(N, 1, H, Dk, Dv, false);
+    const DecodeWs w = decode_ws_layout(N, H, Dk, Dv);
     char *ws = static_cast<char *>(a.ws);
     float *pre = reinterpret_cast<float *>(ws + w.pre);
-    float *post = reinterpret_cast<float *>(ws + w.post);
-    __bf16 *z = reinterpret_cast<__bf16 *>(ws + w.z);
     float *ab = reinterpret_cast<float *>(ws + w.ab);
-    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
-    float *beta = reinterpret_cast<float *>(ws + w.beta);
-    float *y = reinterpret_cast<float *>(ws + w.y);
+    float *zf = reinterpret_cast<float *>(ws + w.z);
     __bf16 *g = reinterpret_cast<__bf16 *>(ws + w.g);
     const __bf16 *x = static_cast<const __bf16 *>(a.x);
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
-    // q|k|v and a|b in one launch (the same x, fp32 out): at M = N the launch is
-    // one round of small tiles, bound by its K steps, so a|b comes at no cost
-    if ((e = project<float>(x, (const __bf16 *)a.W_qkv, pre, N, nqkv, hidden, hidden, hidden, nqkv, s,
-                            (const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H)))
+    // q|k|v, a|b and the gate z in one launch (the same x, fp32 out): at M = N
+    // each product is a few rows of small tiles bound by its K steps, so they
+    // run side by side in one round of the compute units
+    if ((e = project<float>(x, N, hidden, hidden, GemmOp<float>{(const __bf16 *)a.W_qkv, pre, nqkv, hidden, nqkv}, s,
+                            GemmOp<float>{(const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H},
+                            GemmOp<float>{(const __bf16 *)a.W_gate, zf, H * Dv, hidden, H * Dv})))
         return e;
-    if ((e = project<__bf16>(x, (const __bf16 *)a.W_gate, z, N, H * Dv, hidden, hidden, hidden, H * Dv, s)))
-        return e;
-
-    const __bf16 *cw = (const __bf16 *)a.conv_w;
     switch (Dk) {
-    case 16: e = launch_decode_prologue_dk<16>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
-    case 32: e = launch_decode_prologue_dk<32>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
-    case 64: e = launch_decode_prologue_dk<64>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
-    case 128: e = launch_decode_prologue_dk<128>(pre, cw, ab, a.A, a.b_alpha, a.conv_state, post, alpha, beta, N, (int)H, (int)nqkv, (int)a.conv_k, s); break;
+    case 16: e = launch_layer_decode_dk<16>(a, pre, ab, zf, g, (int)nqkv, s); break;
+    case 32: e = launch_layer_decode_dk<32>(a, pre, ab, zf, g, (int)nqkv, s); break;
+    case 64: e = launch_layer_decode_dk<64>(a, pre, ab, zf, g, (int)nqkv, s); break;
+    case 128: e = launch_layer_decode_dk<128>(a, pre, ab, zf, g, (int)nqkv, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e) return e;
-
-    DecodeArgs d{};
-    d.q = post; d.k = post + H * Dk; d.v = post + 2 * H * Dk;
-    d.alpha = alpha; d.beta = beta; d.state = a.state; d.y = y;
-    d.N = N; d.H = H; d.Dk = Dk; d.Dv = Dv; d.bf16 = false;
-    d.q_seq_stride = nqkv; d.k_seq_stride = nqkv; d.v_seq_stride = nqkv;
-    if ((e = launch_decode(d, s))) return e;
-
-    switch (Dv) {
-    case 16: e = launch_epilogue_dv<16>(y, z, a.norm_gamma, g, N, (int)H, s); break;
-    case 32: e = launch_epilogue_dv<32>(y, z, a.norm_gamma, g, N, (int)H, s); break;
-    case 64: e = launch_epilogue_dv<64>(y, z, a.norm_gamma, g, N, (int)H, s); break;
-    case 128: e = launch_epilogue_dv<128>(y, z, a.norm_gamma, g, N, (int)H, s); break;
-    default: return hipErrorInvalidValue;
-    }
-    if (e) return e;
-    return project<float>(g, (const __bf16 *)a.W_o, a.out, N, hidden, H * Dv, H * Dv, H * Dv, hidden, s);
+    return project<float>(g, N, H * Dv, H * Dv, GemmOp<float>{(const __bf16 *)a.W_o, a.out, hidden, H * Dv, hidden}, s);
 }
 
 }  // namespace gdn
