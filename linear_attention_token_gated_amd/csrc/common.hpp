@@ -146,21 +146,6 @@ template <int S> __device__ __forceinline__ float row_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + S, 0xF, 0xF, true));
 }
 
-// Threads of a single-token state update of a DK x DV fp32 state: each owns
-// 4 consecutive columns (one float4) of RPT rows, so a wavefront reads and
-// writes whole contiguous rows.
-template <int DK, int DV> struct DecodeShape {
-    static constexpr int CG = DV / 4;                       // float4 columns per row
-    static constexpr int TOTAL4 = DK * DV / 4;              // float4 per state
-    // four float4 rows per thread: measured fastest for 128x128 states on
-    // MI355X (1024 threads, 5.8 TB/s of state traffic vs 5.6 at 256 threads)
-    static constexpr int NT = TOTAL4 / 4 >= 1024 ? 1024 : (TOTAL4 / 4 < 64 ? (TOTAL4 < 64 ? TOTAL4 : 64) : TOTAL4 / 4);
-    static constexpr int RG = NT / CG;                      // row groups
-    static constexpr int RPT = DK / RG;                     // rows per thread
-    static constexpr int NWAVE = (NT + 63) / 64;
-    static_assert(NT % CG == 0 && DK % RG == 0, "decode tiling");
-};
-
 constexpr int BV = 16;   // value columns carried by one prefill workgroup
 
 constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }

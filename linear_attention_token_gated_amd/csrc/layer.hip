@@ -231,21 +231,28 @@ __global__ __launch_bounds__(256) void prologue_kernel(const float *__restrict__
 // q or k head is Dk / 4 aligned lanes of one wavefront, reduced with
 // xor-shuffles).
 // ---------------------------------------------------------------------------
-// waves per SIMD that two resident workgroups need (the register budget that
-// keeps two on a CU, so one's loads stream while the other computes)
-template <int DK, int DV> struct LayerDecodeWaves {
-    static constexpr int NT = DecodeShape<DK, DV>::NT;
-    static constexpr int value = NT >= 1024 ? 8 : (NT >= 256 ? NT / 128 : 1);
+// Threads of the step: each owns 4 consecutive columns (one float4) of RPT
+// rows of the Dk x Dv state, four rows each up to 1024 threads, so a wavefront
+// reads and writes whole contiguous rows (the decode kernel's tiling).  WPE:
+// waves per SIMD that two resident workgroups need, i.e. the register budget
+// that keeps two on a CU, so one's loads stream while the other computes.
+template <int DK, int DV> struct LayerDecodeShape {
+    static constexpr int CG = DV / 4;
+    static constexpr int TOTAL4 = DK * DV / 4;
+    static constexpr int NT = TOTAL4 / 4 >= 1024 ? 1024 : (TOTAL4 / 4 < 64 ? (TOTAL4 < 64 ? TOTAL4 : 64) : TOTAL4 / 4);
+    static constexpr int RG = NT / CG, RPT = DK / RG, NWAVE = (NT + 63) / 64;
+    static constexpr int WPE = NT >= 1024 ? 8 : (NT >= 256 ? NT / 128 : 1);
+    static_assert(NT % CG == 0 && DK % RG == 0, "decode tiling");
 };
 
 template <int DK, int DV, int KC>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::NT), (LayerDecodeWaves<DK, DV>::value)) void layer_decode_kernel(
+__global__ __launch_bounds__((LayerDecodeShape<DK, DV>::NT), (LayerDecodeShape<DK, DV>::WPE)) void layer_decode_kernel(
     const float *__restrict__ pre, const float *__restrict__ ab, const float *__restrict__ zf,
     const __bf16 *__restrict__ conv_w, const float *__restrict__ Aexp, const float *__restrict__ b_alpha,
     const float *__restrict__ gamma, float *__restrict__ conv_state, float *__restrict__ state,
     __bf16 *__restrict__ g, int H, int nqkv)
 {
-    using Sh = DecodeShape<DK, DV>;
+    using Sh = LayerDecodeShape<DK, DV>;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
     // prologue threads: 4 channels each, in whole wavefronts (PW of them)
     constexpr int HVK = DK / 4, NV = (2 * DK + DV) / 4, PW = (NV + 63) / 64;
@@ -488,7 +495,7 @@ template <int DK, int DV>
 hipError_t launch_layer_decode_dv(const LayerDecodeArgs &a, const float *pre, const float *ab, const float *zf,
                                   __bf16 *g, int nqkv, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.N * a.H)), block(DecodeShape<DK, DV>::NT);
+    const dim3 grid((unsigned)(a.N * a.H)), block(LayerDecodeShape<DK, DV>::NT);
     const __bf16 *cw = (const __bf16 *)a.conv_w;
     const int H = (int)a.H;
     switch (a.conv_k) {
