@@ -80,9 +80,10 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *                 overlapping any other argument: one record per (sequence,
  *                 head, chunk) of the quantities that do not depend on the
  *                 state, computed for every chunk in parallel by a separate
- *                 kernel before the recurrence.  GDN_BF16: decay factors,
- *                 (I + A)^-1 diag(beta) and the masked Q K^T block as bf16
- *                 hi/lo MFMA fragments (21056 bytes at C = 64); optional:
+ *                 kernel before the recurrence.  GDN_BF16: the decay prefix,
+ *                 decay factors and (I + A)^-1 diag(beta) as bf16 hi/lo MFMA
+ *                 fragments (11072 bytes at C = 64; the recurrence forms the
+ *                 masked Q K^T block itself); optional:
  *                 NULL selects one kernel that forms every chunk quantity on
  *                 chip and reads q, k, v from memory once (no scratch, less
  *                 memory traffic, longer per-chunk period).  GDN_F32:

@@ -10,12 +10,13 @@
 //   EG_r = 2^G_r,  Ed_r = 2^(G_{C-1} - G_r),  EGC = 2^G_{C-1}
 //   A    = strict_lower[ beta_r 2^(G_r - G_j) (k_r . k_j) ]
 //   T'   = (I + A)^-1 diag(beta)        (so that U = T' (V - diag(EG) K S))
-//   P    = lower_incl[ 2^(G_r - G_j) (q_r . k_j) ]
 //
-// The recurrence kernel then only needs K S, one dense product U = T' R per
-// chunk, the state update and the output.  T' and P are written as bf16 hi/lo
-// pairs in MFMA operand order (one 8-byte fragment per lane and 16x16 block),
-// so the recurrence loads them straight into registers.
+// The recurrence kernel then needs K S, one dense product U = T' R per chunk,
+// the state update and the output; it forms the output's causal scores P =
+// lower_incl[ 2^(G_r - G_j) (q_r . k_j) ] itself from the K and Q rows it
+// stages anyway, so this kernel reads only K and the gates.  T' is written as
+// bf16 hi/lo pairs in MFMA operand order (one 8-byte fragment per lane and
+// 16x16 block), and G beside the decay vectors.
 //
 // (I + A)^-1 is formed in fp32: each diagonal block by forward substitution
 // inside one wavefront (DPP row broadcast), the blocks below it level by level
@@ -31,6 +32,9 @@ namespace gdn {
 namespace {
 
 constexpr int PREP_THREADS = 256;   // 4 wavefronts
+// resident workgroups per CU: four fit the LDS (33 KB each at C = 64, d = 128)
+// and the register file (one wavefront per SIMD each, at most 128 VGPRs)
+constexpr int PREP_PER_CU = 4;
 
 template <int C, int DK> struct PrepLds {
     using R = PrepRecord<C>;
@@ -39,11 +43,10 @@ template <int C, int DK> struct PrepLds {
     static constexpr int KP = frag_pitch<KS_DK>(DK);
     static constexpr int AP = 20;                               // fp32 block row pitch
     static constexpr size_t oK = 0;
-    static constexpr size_t oQ = oK + align16(2 * C * KP);
-    static constexpr size_t oA = oQ + align16(2 * C * KP);      // A blocks [NTRI][16][AP], row-major
+    static constexpr size_t oA = oK + align16(2 * C * KP);      // A blocks [NTRI][16][AP], row-major
     // (I + A)^-1 blocks, row-major: written only after the Gram blocks are done,
-    // so they reuse the space of the K and Q rows where that is large enough
-    static constexpr bool T_IN_KQ = 4 * NTRI * 16 * AP <= 2 * 2 * C * KP;
+    // so they reuse the space of the K rows where that is large enough
+    static constexpr bool T_IN_KQ = 4 * NTRI * 16 * AP <= 2 * C * KP;
     static constexpr size_t oT = T_IN_KQ ? oK : oA + align16(4 * NTRI * 16 * AP);
     static constexpr size_t oG = (T_IN_KQ ? oA : oT) + align16(4 * NTRI * 16 * AP);
     static constexpr size_t oBe = oG + align16(4 * C);
@@ -67,7 +70,7 @@ __device__ __forceinline__ void fsub16(float (&X)[4], const float (&Lr)[16], std
 }
 
 template <int C, int DK>
-__global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepParams p)
+__global__ __launch_bounds__(PREP_THREADS, PREP_PER_CU) void gdn_chunk_prep_kernel(PrepParams p)
 {
     using L = PrepLds<C, DK>;
     using Rec = PrepRecord<C>;
@@ -78,7 +81,6 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __bf16 *Ks = reinterpret_cast<__bf16 *>(smem + L::oK);
-    __bf16 *Qs = reinterpret_cast<__bf16 *>(smem + L::oQ);
     float *As = reinterpret_cast<float *>(smem + L::oA);
     float *Ts = reinterpret_cast<float *>(smem + L::oT);
     float *Gs = reinterpret_cast<float *>(smem + L::oG);
@@ -90,12 +92,11 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int ln = lane & 15, lg = lane >> 4;
     const __bf16 *kg = static_cast<const __bf16 *>(p.k);
-    const __bf16 *qg = static_cast<const __bf16 *>(p.q);
     const int64_t NC = (p.T + C - 1) / C;
     const int64_t BH = p.BH, nwork = BH * NC;
 
     // Work items are taken chunk-major, so the workgroups running at one time
-    // share the rows of K, Q and the gates.  With a grid that is a multiple of
+    // share the rows of K and the gates.  With a grid that is a multiple of
     // 8, the items of chunk c go to the workgroups with id = c mod 8, which the
     // hardware places on one XCD: every gate row is then fetched into one L2.
     // The rows of the next item are loaded into registers while the current
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     // item i of this residue -> (chunk, bh)
     auto item_c = [&](int64_t i) { return xcd ? gx + 8 * (i / BH) : i / BH; };
     constexpr int NLD = (C * VPR + PREP_THREADS - 1) / PREP_THREADS;
-    f32x4 kv[NLD], qv[NLD];
+    f32x4 kv[NLD];
     float al = 1.f, be = 0.f;
     auto fetch = [&](int64_t i) {
         const int64_t c = item_c(i), bh = i % BH, b = bh / p.H, h = bh % p.H, t0 = c * C;
@@ -117,7 +118,6 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
             const int r = (vi < C * VPR ? vi : 0) / VPR, col = (vi % VPR) * 8;
             const int64_t tok = b * p.T + (t0 + r < p.T ? t0 + r : p.T - 1);   // rows past the end: zeroed later
             kv[i] = *reinterpret_cast<const f32x4 *>(kg + tok * p.ks + h * DK + col);
-            qv[i] = *reinterpret_cast<const f32x4 *>(qg + tok * p.qs + h * DK + col);
         }
         if (wave == 0) {
             const int64_t gi = (b * p.T + (lane < C && t0 + lane < p.T ? t0 + lane : 0)) * p.H + h;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     const int64_t t0 = c * C;
     char *out = static_cast<char *>(p.ws) + (bh * NC + c) * Rec::BYTES;
 
-    // ---- 1. K and Q rows of the chunk (zero past the end), gates and decay scan
+    // ---- 1. K rows of the chunk (zero past the end), gates and decay scan
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int vi = tid + i * PREP_THREADS;
@@ -141,7 +141,6 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
         if (vi < C * VPR) {
             const bool in = t0 + r < p.T;
             *reinterpret_cast<f32x4 *>(Ks + r * KP + col) = in ? kv[i] : zero4();
-            *reinterpret_cast<f32x4 *>(Qs + r * KP + col) = in ? qv[i] : zero4();
         }
     }
     if (wave == 0) {
@@ -158,6 +157,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
             Eas[lane] = __builtin_amdgcn_exp2f(g2 - gblk);
             dec[lane] = __builtin_amdgcn_exp2f(g2);                 // EG
             dec[C + lane] = __builtin_amdgcn_exp2f(gC - g2);        // Ed
+            dec[Rec::DEC_G + lane] = g2;                            // G
         }
         if (lane == 0) dec[2 * C] = __builtin_amdgcn_exp2f(gC);     // EGC
 #pragma unroll
@@ -172,20 +172,15 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     if (i + stride < mine) fetch(i + stride);
     lds_barrier();
 
-    // ---- 2. Gram blocks: A (NTRI blocks, fp32 into LDS) and P (NTRI blocks, bf16
-    //         hi/lo fragments into the record).  Each is computed transposed, D =
-    //         K_cb X_rb^T, so lane (ln, lg) holds row r = 16 rb + ln, columns
-    //         j = 16 cb + 4 lg + e: the A-operand fragment of that block.  A wave
-    //         takes whole block rows (the X_rb fragments are loaded once per row):
-    //         A row NB-1-m with P row m, or P row NB-1-m with A row m, so that
-    //         every wave has NB + 1 blocks.
-    auto gram_row = [&](auto isP_c, auto rb_c) {
-        constexpr bool isP = decltype(isP_c)::value;
+    // ---- 2. Gram blocks of A (NTRI blocks, fp32 into LDS), computed transposed,
+    //         D = K_cb K_rb^T, so lane (ln, lg) holds row r = 16 rb + ln, columns
+    //         j = 16 cb + 4 lg + e: the A-operand fragment of that block.  Wave w
+    //         takes block row w (its K_rb fragments are loaded once).
+    auto gram_row = [&](auto rb_c) {
         constexpr int rb = decltype(rb_c)::value;
-        const __bf16 *Xs = isP ? Qs : Ks;
         FDK fb[NK];
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) fb[kk] = frag_rows<__bf16, KS_DK>(Xs, KP, 16 * rb, kk * KS_DK, lane);
+        for (int kk = 0; kk < NK; ++kk) fb[kk] = frag_rows<__bf16, KS_DK>(Ks, KP, 16 * rb, kk * KS_DK, lane);
         const int r = 16 * rb + ln;
         const float Gr = Gs[r], Ear = Eas[r], ber = Bes[r];
         static_for<rb + 1>([&](auto cb_c) {
@@ -199,50 +194,21 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
             if constexpr (rb == cb) {
                 const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gs + j0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool keep = r > j0 + e || (isP && r == j0 + e);
-                    val[e] = keep ? __builtin_amdgcn_exp2f(Gr - Gj[e]) * acc[e] : 0.f;
-                }
+                for (int e = 0; e < 4; ++e) val[e] = r > j0 + e ? __builtin_amdgcn_exp2f(Gr - Gj[e]) * acc[e] : 0.f;
             } else {
                 // r > j: 2^(G_r - G_j) = 2^(G_r - G_{16 rb}) 2^(G_{16 rb} - G_j), both factors <= 1
                 const f32x4 eb = *reinterpret_cast<const f32x4 *>(Ebs + rb * C + j0);
                 val = acc * eb * Ear;
             }
             constexpr int idx = rb * (rb + 1) / 2 + cb;
-            if constexpr (isP) {
-                bf16x4 hv, lv;
-                split4(val, hv, lv);
-                bf16x4 *pf = reinterpret_cast<bf16x4 *>(out + Rec::oP) + idx * 128;
-                pf[lane] = hv;
-                pf[64 + lane] = lv;
-            } else {
-                *reinterpret_cast<f32x4 *>(As + (idx * 16 + ln) * AP + 4 * lg) = val * ber;
-            }
+            *reinterpret_cast<f32x4 *>(As + (idx * 16 + ln) * AP + 4 * lg) = val * ber;
         });
     };
-    using TF = std::true_type;
-    using FF = std::false_type;
-    auto gram_wave = [&](auto w_c) {
-        constexpr int w = decltype(w_c)::value, m = w / 2, hi = NB - 1 - m;
-        constexpr bool odd = w % 2;
-        if constexpr (m < (NB + 1) / 2) {
-            if constexpr (hi == m) {
-                if constexpr (odd) gram_row(TF{}, std::integral_constant<int, m>{});
-                else gram_row(FF{}, std::integral_constant<int, m>{});
-            } else if constexpr (odd) {
-                gram_row(TF{}, std::integral_constant<int, hi>{});
-                gram_row(FF{}, std::integral_constant<int, m>{});
-            } else {
-                gram_row(FF{}, std::integral_constant<int, hi>{});
-                gram_row(TF{}, std::integral_constant<int, m>{});
-            }
-        }
-    };
     switch (wave) {
-    case 0: gram_wave(std::integral_constant<int, 0>{}); break;
-    case 1: gram_wave(std::integral_constant<int, 1>{}); break;
-    case 2: gram_wave(std::integral_constant<int, 2>{}); break;
-    default: gram_wave(std::integral_constant<int, 3>{}); break;
+    case 0: gram_row(std::integral_constant<int, 0>{}); break;
+    case 1: if constexpr (NB > 1) gram_row(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (NB > 2) gram_row(std::integral_constant<int, 2>{}); break;
+    default: if constexpr (NB > 3) gram_row(std::integral_constant<int, 3>{}); break;
     }
     lds_barrier();
 
@@ -313,15 +279,15 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void gdn_chunk_prep_kernel(PrepPar
     }
 }
 
-// Workgroups of the persistent preparation grid: three per CU (the LDS of
-// one workgroup allows three), never more than there are records.
+// Workgroups of the persistent preparation grid: PREP_PER_CU per CU, never
+// more than there are records.
 int prep_grid(int64_t nrec)
 {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    const int64_t g = (int64_t)cus * 3;
+    const int64_t g = (int64_t)cus * PREP_PER_CU;
     return (int)(nrec < g ? nrec : g);
 }
 
@@ -350,9 +316,9 @@ hipError_t launch_prep_dk(const PrepParams &p, int64_t Dk, int64_t nrec, hipStre
 hipError_t launch_chunk_prep(const PrefillArgs &a, hipStream_t stream)
 {
     PrepParams p;
-    p.q = a.q; p.k = a.k; p.alpha = a.alpha; p.beta = a.beta; p.ws = a.ws;
+    p.k = a.k; p.alpha = a.alpha; p.beta = a.beta; p.ws = a.ws;
     p.T = a.T; p.H = a.H; p.BH = a.B * a.H;
-    p.qs = a.q_tok_stride; p.ks = a.k_tok_stride;
+    p.ks = a.k_tok_stride;
     const int64_t nrec = a.B * a.H * ((a.T + a.chunk - 1) / a.chunk);
     switch (a.chunk) {
     case 16: return launch_prep_dk<16>(p, a.Dk, nrec, stream);

@@ -6,9 +6,10 @@
 // blocks (row block i, column block k <= i) at index i (i + 1) / 2 + k:
 //   oT   [NTRI][hi, lo][64 lanes] bf16x4   T' = (I + A)^-1 diag(beta):
 //                                           lane (ln, lg) holds T'_ik[ln][4 lg + e]
-//   oP   [NTRI][hi, lo][64 lanes] bf16x4   P: lane (ln, lg) holds P_ik[ln][4 lg + e]
-//   oDec float EG[C], Ed[C], EGC, 15 floats of padding
-// Both block arrays hold the A-operand fragments of 16x16x16 bf16 MFMAs.
+//                                           (the A-operand fragments of 16x16x16
+//                                           bf16 MFMAs)
+//   oDec float EG[C], Ed[C], EGC, 15 floats of padding, G[C] (the base-2 decay
+//        prefix itself, from which the recurrence forms the decay ratios of P)
 #pragma once
 
 #include <stddef.h>
@@ -19,10 +20,11 @@ namespace gdn {
 template <int C> struct PrepRecord {
     static constexpr int NB = C / 16;
     static constexpr int NTRI = NB * (NB + 1) / 2;
+    static constexpr int DEC = 3 * C + 16;          // floats of the decay block
+    static constexpr int DEC_G = 2 * C + 16;        // offset of G in it
     static constexpr size_t oT = 0;
-    static constexpr size_t oP = oT + (size_t)NTRI * 2 * 64 * 8;
-    static constexpr size_t oDec = oP + (size_t)NTRI * 2 * 64 * 8;
-    static constexpr size_t BYTES = oDec + (size_t)(2 * C + 16) * 4;
+    static constexpr size_t oDec = oT + (size_t)NTRI * 2 * 64 * 8;
+    static constexpr size_t BYTES = oDec + (size_t)DEC * 4;
     static_assert(BYTES % 64 == 0, "records stay 64-byte aligned");
 };
 
@@ -36,12 +38,12 @@ inline size_t prep_record_bytes(int64_t chunk) {
 }
 
 struct PrepParams {
-    const void *q, *k;
+    const void *k;
     const float *alpha, *beta;
     void *ws;
     int64_t T, H;
     int64_t BH;              // B * H
-    int64_t qs, ks;          // token strides (elements)
+    int64_t ks;              // token stride (elements)
 };
 
 }  // namespace gdn

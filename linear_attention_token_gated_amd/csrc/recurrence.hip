@@ -87,7 +87,7 @@ template <int C, int DK> struct RecLay {
     static constexpr int KPS = frag_pitch<KS_DK>(DK);  // S^T rows (bf16)
     static constexpr int CPU = C + 4;                  // U^T rows: 64-bit stores and reads
     static constexpr int CPD = frag_pitch<KS_C>(C);    // e^{G_C-G} U^T rows
-    static constexpr int DEC = 2 * C + 16;             // floats of EG, Ed, EGC (+ padding)
+    static constexpr int DEC = PrepRecord<C>::DEC;     // floats of EG, Ed, EGC (+ padding), G
     // one chunk buffer; every region a whole number of 1 KB blocks (one wave's load)
     static constexpr size_t cK = 0;                    // [C][DK] bf16, granules permuted
     static constexpr size_t cQ = cK + round1k(2 * C * DK);
@@ -451,24 +451,54 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
         }
     };
 
-    // Y-waves: row block rb = w - 4, compile-time in each copy.  The output
-    // of a chunk is off the critical path of the recurrence: P U in phase 3
-    // (U is complete; diag(EG) Q S comes from the S-wave of the row block),
-    // then the loads of the next chunk's P fragments, and the stores of the
-    // rows in phase 1 of the next iteration.
+    // Y-waves: row block rb = 7 - w, compile-time in each copy (the wave of the
+    // largest row block of P and of P U shares its SIMD with the S-wave that has
+    // the smallest U product).  The output of a chunk is off the critical path
+    // of the recurrence: the causal scores P of the row block in phase 2, from
+    // the chunk's K and Q rows already in LDS (D = K_cb Q_rb^T, so that lane
+    // (ln, lg) holds P[16 rb + ln][16 cb + 4 lg + e], the A operand of P U),
+    // decayed by 2^(G_r - G_j) and kept in registers as hi/lo pairs; then P U in
+    // phase 3 (U is complete; diag(EG) Q S comes from the S-wave of the row
+    // block), and the stores of the rows in phase 1 of the next iteration.
     auto y_wave = [&](auto rb_c) {
         constexpr int rb = decltype(rb_c)::value;
         constexpr bool has_rb = rb < NB;
         constexpr int NP = has_rb ? rb + 1 : 1;     // P blocks of this row block
         bf16x4 pfh[NP], pfl[NP];                    // P fragments of this row block
-        auto load_p = [&](int64_t c) {
+        auto form_p = [&](int cbi) {
             if constexpr (has_rb) {
-                const bf16x4 *pf = reinterpret_cast<const bf16x4 *>(recs + c * (int64_t)Rec::BYTES + Rec::oP);
+                const char *cb = cbuf(cbi);
+                const __bf16 *Ks = reinterpret_cast<const __bf16 *>(cb + L::cK);
+                const __bf16 *Qs = reinterpret_cast<const __bf16 *>(cb + L::cQ);
+                const float *Gv = reinterpret_cast<const float *>(cb + L::cDec) + Rec::DEC_G;
+                FDK qf[NK];
 #pragma unroll
-                for (int k = 0; k <= rb; ++k) {
-                    pfh[k] = pf[tri_idx(rb, k) * 128 + lane];
-                    pfl[k] = pf[tri_idx(rb, k) * 128 + 64 + lane];
-                }
+                for (int kk = 0; kk < NK; ++kk) qf[kk] = frag_kq<KS_DK, DK>(Qs, 16 * rb, kk * KS_DK, lane);
+                const int r = 16 * rb + ln;
+                const float Gr = Gv[r], Grb = Gv[16 * rb];
+                const float Ear = __builtin_amdgcn_exp2f(Gr - Grb);
+                static_for<NP>([&](auto cb_c) {
+                    constexpr int cbk = decltype(cb_c)::value;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < NK; ++kk)
+                        acc = FDK::mma(frag_kq<KS_DK, DK>(Ks, 16 * cbk, kk * KS_DK, lane), qf[kk], acc);
+                    const int j0 = 16 * cbk + 4 * lg;
+                    const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gv + j0);
+                    f32x4 val;
+                    if constexpr (cbk == rb) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            val[e] = r >= j0 + e ? __builtin_amdgcn_exp2f(Gr - Gj[e]) * acc[e] : 0.f;
+                    } else {
+                        // r > j: 2^(G_r - G_j) = 2^(G_r - G_{16 rb}) 2^(G_{16 rb} - G_j), both <= 1
+                        f32x4 eb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) eb[e] = __builtin_amdgcn_exp2f(Grb - Gj[e]);
+                        val = acc * eb * Ear;
+                    }
+                    split4(val, pfh[cbk], pfl[cbk]);
+                });
             }
         };
         f32x4 yv = zero4();                         // output rows waiting to be stored
@@ -482,16 +512,17 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 }
             }
         };
-        load_p(0);
         lds_barrier();
 
+        int cbi = 0;
         for (int64_t c = 0; c < NC; ++c) {
             // ---- phase 1: rows of chunk c - 1
             if (c > 0) store_y(c - 1);
             lds_barrier();
+            // ---- phase 2: P of chunk c
+            form_p(cbi);
             lds_barrier();
-            // ---- phase 3: Y = diag(EG) Q S + P U; then the next chunk's P (the
-            // last chunk's again at the end: no branch)
+            // ---- phase 3: Y = diag(EG) Q S + P U
             if constexpr (has_rb) {
                 f32x4 acc = reinterpret_cast<const f32x4 *>(smem + L::oEq)[rb * 64 + lane], acc2 = zero4();
                 bf16x4 uh[NP], ul[NP];
@@ -506,8 +537,8 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
                 // a branch can miss its wait states
                 asm volatile("" : "+v"(yv));
             }
-            load_p(clampc(c + 1));
             lds_barrier();
+            cbi = next_buf(cbi);
         }
         if (NC > 0) store_y(NC - 1);
     };
@@ -641,10 +672,10 @@ __global__ __launch_bounds__(REC_THREADS, 1) void gdn_recurrence_kernel(RecParam
     case 1: s_wave(I1{}); break;
     case 2: s_wave(I2{}); break;
     case 3: s_wave(I3{}); break;
-    case 4: y_wave(I0{}); break;
-    case 5: y_wave(I1{}); break;
-    case 6: y_wave(I2{}); break;
-    case 7: y_wave(I3{}); break;
+    case 4: y_wave(I3{}); break;
+    case 5: y_wave(I2{}); break;
+    case 6: y_wave(I1{}); break;
+    case 7: y_wave(I0{}); break;
     case 8: l_wave(I0{}); break;
     case 9: l_wave(I1{}); break;
     case 10: l_wave(I2{}); break;

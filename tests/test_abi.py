@@ -77,7 +77,7 @@ def test_prefill_workspace_validation(L):
     # the fused kernel), required for fp32.  Every failing case below fails on
     # the host before anything is launched.
     need16 = L.gdn_prefill_workspace_bytes(1, 64, 2, 16, 16, 16, 1)
-    assert need16 == 2 * 4 * 2240
+    assert need16 == 2 * 4 * 1280          # 16-token chunks: one T' block (1024 bytes), 64 decay floats
     W = A + 400 * MB
     assert prefill(L, dt=1, w=W, wb=need16 - 1) == WS            # given but too small
     assert prefill(L, dt=1, w=W + 16, wb=need16) == ALIGN        # not 256-byte aligned
@@ -188,9 +188,11 @@ def test_layer_decode_validation(L):
 
 
 def test_workspace_queries(L):
-    # bf16 prefill: one 21056-byte record per (sequence, head, 64-token chunk)
-    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 21056
-    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 6464
+    # bf16 prefill: one 11072-byte record per (sequence, head, 64-token chunk):
+    # T' as 10 blocks of hi/lo fragments (10240 bytes) and 208 floats of decay
+    # vectors; 3520 bytes at 32-token chunks (3 blocks, 112 floats)
+    assert L.gdn_prefill_workspace_bytes(1, 32768, 32, 128, 128, 64, 1) == 32 * 512 * 11072
+    assert L.gdn_prefill_workspace_bytes(2, 100, 3, 64, 32, 32, 1) == 2 * 3 * 4 * 3520
     assert L.gdn_prefill_workspace_bytes(1, 0, 32, 128, 128, 64, 1) == 0
     assert L.gdn_prefill_workspace_bytes(1, 64, 2, 48, 16, 64, 1) == 0            # rejected shape
     # fp32: records of the two-kernel path, 3*64*64 + 2*64 floats per 64-token chunk
