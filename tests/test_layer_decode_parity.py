@@ -18,7 +18,10 @@ def _params(inp):
 
 
 @pytest.mark.parametrize("conv_k", [1, 2, 3, 4])
-@pytest.mark.parametrize("N,hidden,H,Dk,Dv", [(3, 128, 2, 32, 64), (2, 192, 4, 16, 32), (5, 128, 1, 128, 128)])
+# (16, 128): 128 threads a (sequence, head), 40 of them on the conv step;
+# (128, 16): 128 threads, the conv step on two wavefronts (68 threads)
+@pytest.mark.parametrize("N,hidden,H,Dk,Dv", [(3, 128, 2, 32, 64), (2, 192, 4, 16, 32), (5, 128, 1, 128, 128),
+                                              (2, 128, 2, 16, 128), (3, 64, 2, 128, 16)])
 def test_steps_equal_layer(oracle_mod, conv_k, N, hidden, H, Dk, Dv):
     import torch
     import linear_attention_token_gated_amd as gdn
