@@ -60,6 +60,14 @@ template <typename OutT> struct GemmProducts {
     int tile_end[3];
 };
 
+// K cut into splits of whole K steps: split s sums K steps s * steps ..
+// s * steps + steps - 1 and writes its partial product at C_p + s * M * ldc_p
+// (steps = 0: one split, all of K).  The consumer adds the partials in split
+// order.
+struct GemmSplit {
+    int steps = 0, split = 0;
+};
+
 // One workgroup's tile (pid: its index in the GEMM's grid, smem: ST * STAGE
 // bytes of LDS, 1024-byte aligned).  ST stages of K steps in LDS (a power of
 // two >= 4), ST - 1 of them in flight; NW wavefronts.  tiles_n: column tiles of
@@ -67,7 +75,7 @@ template <typename OutT> struct GemmProducts {
 template <typename OutT, int BM, int BN, int ST, int NW>
 __device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 *__restrict__ A, int M, int K,
                                               int64_t lda, const GemmProducts<OutT> &P, int tiles_m, int tiles_n,
-                                              int bn_log)
+                                              int bn_log, GemmSplit sp = GemmSplit{})
 {
     using G = GemmTile<BM, BN, NW>;
     constexpr int WGM = G::WGM;
@@ -101,7 +109,11 @@ __device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 
     if (pi > 0) tn -= P.tile_end[pi - 1];
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t mrows = M - m0 < BM ? M - m0 : BM, nrows = N - n0 < BN ? N - n0 : BN;
-    const int ntk = (K + GBK - 1) / GBK;
+    // this split's K steps: kbase .. kbase + ntk - 1
+    const int ntk_all = (K + GBK - 1) / GBK;
+    const int kbase = sp.steps ? sp.split * sp.steps : 0;
+    const int ntk = sp.steps ? (ntk_all - kbase < sp.steps ? ntk_all - kbase : sp.steps) : ntk_all;
+    Cm += (int64_t)sp.split * M * ldc;
 
     // load t of this wave moves tile rows 16 i .. 16 i + 15 (i = wave + 4 t): lane
     // -> row 16 i + lane / 4, LDS granule position lane % 4, which holds granule
@@ -113,7 +125,7 @@ __device__ __forceinline__ void gemm_nt_block(int pid, char *smem, const __bf16 
 #pragma unroll
     for (int t = 0; t < LB; ++t) roff_b[t] = (uint32_t)((16 * (wave + NW * t) + (lane >> 2)) * ldb * 2 + gk * 2);
     auto issue = [&](int kt, int stage) {
-        const int k0 = kt * GBK;
+        const int k0 = (kbase + kt) * GBK;
         char *sa = smem + stage * G::STAGE, *sb = sa + G::ATILE;
         const __bf16 *ba = A + m0 * lda + k0, *bb = Bm + n0 * ldb + k0;
         const uint32_t na = (uint32_t)((mrows * lda - k0) * 2), nb = (uint32_t)((nrows * ldb - k0) * 2);

@@ -44,20 +44,30 @@ template <typename OutT, int BM, int BN, int ST, int NW>
 __global__ __launch_bounds__(64 * NW, BM == 256 ? 1 : 2) void gemm_nt_kernel(const __bf16 *__restrict__ A, int M,
                                                                               int K, int64_t lda,
                                                                               GemmProducts<OutT> P, int tiles_m,
-                                                                              int tiles_n, int bn_log)
+                                                                              int tiles_n, int bn_log, int ksteps)
 {
     __shared__ __attribute__((aligned(1024))) char smem[ST * GemmTile<BM, BN, NW>::STAGE];
-    gemm_nt_block<OutT, BM, BN, ST, NW>((int)blockIdx.x, smem, A, M, K, lda, P, tiles_m, tiles_n, bn_log);
+    GemmSplit sp;
+    sp.steps = ksteps;
+    sp.split = (int)blockIdx.y;
+    gemm_nt_block<OutT, BM, BN, ST, NW>((int)blockIdx.x, smem, A, M, K, lda, P, tiles_m, tiles_n, bn_log, sp);
 }
 
-// C_p = A B_p^T for up to three products of one A [M, K] in one launch
+// C_p = A B_p^T for up to three products of one A [M, K] in one launch.
+// nsplit = 2: K in two halves of whole K steps (K of at least two steps),
+// each writing a partial product, the second at C_p + M * ldc_p; the caller
+// adds them (first + second).
 template <typename OutT, int BM, int BN, int ST, int NW = 4>
 hipError_t gemm_nt_tile(const __bf16 *A, int64_t M, int64_t K, int64_t lda, const GemmOp<OutT> &p0,
-                        const GemmOp<OutT> &p1, const GemmOp<OutT> &p2, hipStream_t s)
+                        const GemmOp<OutT> &p1, const GemmOp<OutT> &p2, hipStream_t s, int nsplit = 1)
 {
     const GemmGrid<BM, BN> g(M, p0.N, p1.B ? p1.N : 0, p2.B ? p2.N : 0);
-    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST, NW>), dim3((unsigned)g.grid), dim3(64 * NW), 0, s, A, (int)M,
-                       (int)K, lda, gemm_products(g, p0, p1, p2), g.tiles_m, g.tiles_n, g.bn_log);
+    const int ntk = (int)((K + GBK - 1) / GBK);
+    const int steps = nsplit == 2 ? (ntk + 1) / 2 : 0;
+    if (nsplit == 2 && ntk < 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_nt_kernel<OutT, BM, BN, ST, NW>), dim3((unsigned)g.grid, nsplit == 2 ? 2u : 1u),
+                       dim3(64 * NW), 0, s, A, (int)M, (int)K, lda, gemm_products(g, p0, p1, p2), g.tiles_m,
+                       g.tiles_n, g.bn_log, steps);
     return hipGetLastError();
 }
 
@@ -271,7 +281,12 @@ __global__ __launch_bounds__((LayerDecodeShape<DK, DV>::NT), (LayerDecodeShape<D
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(S4 + (rg + RG * i) * CG + cg);
     f32x4 zv = zero4();
-    if (rg == 0) zv = *reinterpret_cast<const f32x4 *>(zf + nh * DV + 4 * cg);
+    // the projections arrive as two partial products over halves of K (the
+    // second NH rows further on), added first + second
+    const int64_t NH = (int64_t)gridDim.x * DV;
+    if (rg == 0)
+        zv = *reinterpret_cast<const f32x4 *>(zf + nh * DV + 4 * cg) +
+             *reinterpret_cast<const f32x4 *>(zf + NH + nh * DV + 4 * cg);
 
     if (tid < 64 * PW) {
         // step 1: thread tid < NV owns channels c0 .. c0 + 3 of the q|k|v row
@@ -282,7 +297,9 @@ __global__ __launch_bounds__((LayerDecodeShape<DK, DV>::NT), (LayerDecodeShape<D
         f32x4 rows[KC];                                       // taps 0 .. KC-1: history, then this token
 #pragma unroll
         for (int j = 0; j < KC - 1; ++j) rows[j] = *reinterpret_cast<const f32x4 *>(conv_state + (n * (KC - 1) + j) * nqkv + c0);
-        rows[KC - 1] = *reinterpret_cast<const f32x4 *>(pre + n * nqkv + c0);
+        const int64_t npre = (int64_t)(gridDim.x / H) * nqkv;           // partial stride
+        rows[KC - 1] = *reinterpret_cast<const f32x4 *>(pre + n * nqkv + c0) +
+                       *reinterpret_cast<const f32x4 *>(pre + npre + n * nqkv + c0);
         __bf16 w[4 * KC];                                     // 4 KC consecutive taps, channel-major
         if constexpr (KC % 2 == 0) {
 #pragma unroll
@@ -318,7 +335,9 @@ __global__ __launch_bounds__((LayerDecodeShape<DK, DV>::NT), (LayerDecodeShape<D
                 *reinterpret_cast<f32x4 *>(conv_state + (n * (KC - 1) + r) * nqkv + c0) = rows[r + 1];
         }
         if (tid == 63) {
-            const float a = ab[n * 2 * H + hh], bb = ab[n * 2 * H + H + hh];
+            const int64_t nab = (int64_t)(gridDim.x / H) * 2 * H;
+            const float a = ab[n * 2 * H + hh] + ab[nab + n * 2 * H + hh];
+            const float bb = ab[n * 2 * H + H + hh] + ab[nab + n * 2 * H + H + hh];
             s_ab[0] = expf(-expf(Aexp[hh]) * softplusf_(a + b_alpha[hh]));
             s_ab[1] = sigmoidf_(bb);
         }
@@ -525,8 +544,9 @@ hipError_t launch_layer_decode_dk(const LayerDecodeArgs &a, const float *pre, co
     return hipErrorInvalidValue;
 }
 
-// Workspace of the decode step: the three in-projections (fp32) and the gated
-// norm (bf16, the out-projection's operand)
+// Workspace of the decode step: the three in-projections (fp32, two partial
+// products each over halves of K) and the gated norm (bf16, the
+// out-projection's operand)
 struct DecodeWs {
     size_t pre, ab, z, g, total;
 };
@@ -535,9 +555,9 @@ DecodeWs decode_ws_layout(int64_t N, int64_t H, int64_t Dk, int64_t Dv)
     const size_t n = (size_t)N, nqkv = (size_t)(H * (2 * Dk + Dv));
     DecodeWs w;
     size_t o = 0;
-    w.pre = o; o += al256(n * nqkv * 4);
-    w.ab = o;  o += al256(n * (size_t)(2 * H) * 4);
-    w.z = o;   o += al256(n * (size_t)(H * Dv) * 4);
+    w.pre = o; o += al256(2 * n * nqkv * 4);
+    w.ab = o;  o += al256(2 * n * (size_t)(2 * H) * 4);
+    w.z = o;   o += al256(2 * n * (size_t)(H * Dv) * 4);
     w.g = o;   o += al256(n * (size_t)(H * Dv) * 2);
     w.total = o;
     return w;
@@ -674,12 +694,16 @@ hipError_t launch_layer_decode(const LayerDecodeArgs &a, hipStream_t s)
     const int64_t nqkv = H * (2 * Dk + Dv);
     hipError_t e;
 
-    // q|k|v, a|b and the gate z in one launch (the same x, fp32 out): at M = N
-    // each product is a few rows of small tiles bound by its K steps, so they
-    // run side by side in one round of the compute units
-    if ((e = project<float>(x, N, hidden, hidden, GemmOp<float>{(const __bf16 *)a.W_qkv, pre, nqkv, hidden, nqkv}, s,
-                            GemmOp<float>{(const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H},
-                            GemmOp<float>{(const __bf16 *)a.W_gate, zf, H * Dv, hidden, H * Dv})))
+    // q|k|v, a|b and the gate z in one launch (the same x, fp32 out), K in two
+    // halves: at M = N each product is a few rows of tiles bound by the
+    // latency of their K steps (the weights arrive cold from HBM), so halving
+    // the steps per workgroup and doubling the workgroups (128 x 128 tiles,
+    // two per CU) shortens it; the decode kernel adds the two halves
+    if ((e = gemm_nt_tile<float, 128, 128, 4>(x, N, hidden, hidden,
+                                              GemmOp<float>{(const __bf16 *)a.W_qkv, pre, nqkv, hidden, nqkv},
+                                              GemmOp<float>{(const __bf16 *)a.W_ab, ab, 2 * H, hidden, 2 * H},
+                                              GemmOp<float>{(const __bf16 *)a.W_gate, zf, H * Dv, hidden, H * Dv},
+                                              s, 2)))
         return e;
     switch (Dk) {
     case 16: e = launch_layer_decode_dk<16>(a, pre, ab, zf, g, (int)nqkv, s); break;

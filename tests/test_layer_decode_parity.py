@@ -92,13 +92,14 @@ def test_decode_matches_gpu_layer(oracle_mod):
     eS = rel_err(host(S), host(S_l))
     print(f"  decode vs layer: out {eo:.3e} S {eS:.3e}", flush=True)
     assert eS <= 1e-3
-    # The projections of T tokens at once and of one token per step sum every
-    # output over k in the same order, so they agree bit for bit, and the states
-    # agree to ~1e-6.  The two cores (chunked, token by token) still differ in
-    # the last bits of y; where that crosses a rounding boundary of the gated
-    # norm's bf16 output g, one g element steps by one bf16 ulp (2^-8 to 2^-7 of
-    # it), which moves its token's outputs by up to that much of |g_i W_o[:, i]|:
-    # about 2e-3 of RMS(out) here.  The output is held to such a step.
+    # The projections of T tokens at once and of one token per step agree to
+    # fp32 rounding (the decode step sums each in-projection over two halves of
+    # k, the layer over all of k in one pass), and the states to ~1e-6.  The
+    # two cores (chunked, token by token) differ in the last bits of y; where
+    # that crosses a rounding boundary of the gated norm's bf16 output g, one g
+    # element steps by one bf16 ulp (2^-8 to 2^-7 of it), which moves its
+    # token's outputs by up to that much of |g_i W_o[:, i]|: about 2e-3 of
+    # RMS(out) here.  The output is held to such a step.
     assert eo <= 5e-3
 
 
